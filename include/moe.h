@@ -1,0 +1,274 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) decode-time MoE expert FFN.
+ *
+ * The library computes one Mixture-of-Experts FFN layer for a small decode
+ * batch (T <= 32 tokens) whose experts are stored as GGUF-style quantized
+ * blocks: router GEMV, softmax top-k with renormalised weights, grouping of
+ * (token, expert) pairs, gate/up quantized matvecs with SiLU(gate)*up, the
+ * down matvec and the weighted combine (plus always-active shared experts
+ * and the residual add).  Beside it sits a slot-pool expert cache that keeps
+ * hot experts in HBM and uploads misses from pinned host memory.
+ *
+ * Sources (pages on the method): the gating step and its softmax top-k are
+ * described in the MoE offload blog (mhpn.cn, sections 3.1 and 5.2); the
+ * slot-pool cache, its grouping of experts by tensor type and shape, the LRU
+ * eviction, the 32-token batch limit and the budget planner are described in
+ * the T4 MoE-cache report (kongchang.com, sections "What the MoE cache
+ * caches" and "Size your experts before configuring"); a GPU matvec that
+ * keeps weights in their quantized blocks is described in the GPU-offload
+ * research notes (kwkr.cn, section 1.2).
+ *
+ * Conventions for every call:
+ *  - Pointers documented as "device" must point to GPU memory of the current
+ *    HIP device; "host" pointers to host memory; "pinned" to memory from
+ *    hipHostMalloc.  The caller owns every buffer it passes in.
+ *  - GPU work is enqueued on the given stream and the call returns at once.
+ *    Argument and shape errors are detected on the host before anything is
+ *    enqueued and returned synchronously; nothing is enqueued then.  Launch
+ *    failures return MOE_ERR_HIP.  No exception crosses the ABI.
+ *  - On any error, moe_last_error() returns a message (thread-local).
+ *  - Layouts are row-major and tightly packed unless stated otherwise.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_ARG = -1,      /* null pointer, negative size, k > E, ... */
+    MOE_ERR_SHAPE = -2,    /* row length not a whole number of tiles/blocks */
+    MOE_ERR_QTYPE = -3,    /* unknown quantization type */
+    MOE_ERR_BUDGET = -4,   /* cache budget below the floor for some group */
+    MOE_ERR_CAPACITY = -5, /* more distinct experts in one layer-step than slots */
+    MOE_ERR_HIP = -6,      /* a HIP runtime call failed */
+    MOE_ERR_BATCH = -7,    /* T outside [1, 32] */
+    MOE_ERR_STATE = -8     /* call out of order (e.g. upload before lookup) */
+} moe_status;
+
+/* Block formats (public GGUF layouts; the pages name them but print no bit
+ * packing -- T4 MoE-cache report, section "What the MoE cache caches", names
+ * Q4_K/Q6_K; the GPU-offload research notes, section 1.2, give the 34-byte
+ * q8_0 block):
+ *   MOE_Q8_0: 32 weights / 34 B: fp16 d, int8 q[32];            w = d*q
+ *   MOE_Q4_K: 256 weights / 144 B: fp16 d, fp16 dmin, 12 B of packed 6-bit
+ *             scales and mins of 8 sub-blocks, 128 B of 4-bit q;  w = d*sc*q - dmin*m
+ *   MOE_Q6_K: 256 weights / 210 B: 128 B low 4 bits, 64 B high 2 bits,
+ *             int8 sc[16] (one per 16 weights), fp16 d;         w = d*sc*(q-32) */
+typedef enum { MOE_Q8_0 = 1, MOE_Q4_K = 2, MOE_Q6_K = 3 } moe_qtype;
+
+/* One expert's shape: gate and up are [I, H] (rows of H weights), down is
+ * [H, Ipad] with Ipad = I rounded up to a multiple of 256 (the tile width,
+ * for every type; the padded columns multiply zeros).  Requirements: H a
+ * multiple of 256, I a multiple of 64, the three qtypes valid. */
+typedef struct {
+    int32_t gate, up, down; /* moe_qtype of each matrix */
+    int32_t H, I;
+} moe_expert_desc;
+
+/* Thread-local text of the last error (never NULL). */
+const char *moe_last_error(void);
+
+/* ---------------------------------------------------------------------- */
+/* Expert storage.                                                         */
+
+/* Bytes of one expert (gate + up + down) in either layout; the slot layout
+ * permutes the canonical bytes and adds nothing.  Returns -1 on a bad desc. */
+int64_t moe_expert_bytes(const moe_expert_desc *d);
+
+/* Padded down-row length Ipad of the desc (see moe_expert_desc), -1 on error. */
+int32_t moe_down_k(const moe_expert_desc *d);
+
+/* Repack one expert from canonical GGUF blocks (row-major rows of whole
+ * blocks: gate [I,H], up [I,H], down [H,Ipad]; host memory) into the slot
+ * layout read by moe_expert_ffn (host memory, moe_expert_bytes(d) bytes).
+ * The slot layout groups 64 rows x 256 columns into one contiguous tile and
+ * inside a tile stores each 16-byte piece of a block for all 64 rows side by
+ * side, so that 64 lanes reading the same piece of 64 rows read 1 KiB of
+ * consecutive bytes.  Pure host function, no GPU. */
+moe_status moe_repack_expert(const moe_expert_desc *d, const void *gate, const void *up,
+                             const void *down, void *slot, size_t slot_bytes);
+
+/* ---------------------------------------------------------------------- */
+/* Steps of the decode path.                                               */
+
+/* xhat[t] = h[t] / sqrt(mean(h[t]^2) + eps), per token.  h, xhat: device
+ * fp32 [T, H].  (Weightless pre-norm of the layer stack; the pages give no
+ * stack composition, so the residual pre-norm block is this library's
+ * reading.) */
+moe_status moe_rmsnorm(const float *h, int32_t T, int32_t H, float eps, float *xhat, hipStream_t s);
+
+/* Router and top-k (MoE offload blog, section 3.1: router logits, softmax,
+ * pick the k best experts; the batched form is section 5.2).
+ *   x        device fp32 [T, H], the normalised token states
+ *   w_router device fp32 [E, H]
+ *   bias     device fp32 [E] or NULL (added to the logits)
+ *   idx      device int32 [T, k]: expert ids by descending logit, ties to
+ *            the lower id
+ *   w        device fp32 [T, k]: softmax over the k selected logits (equal
+ *            to the full softmax renormalised over the k winners)
+ *   logits   device fp32 [T, E] or NULL
+ * 1 <= T <= 32, 1 <= k <= E <= 1024, H a multiple of 256. */
+moe_status moe_route_topk(const float *x, int32_t T, int32_t H, const float *w_router,
+                          const float *bias, int32_t E, int32_t k, int32_t *idx, float *w,
+                          float *logits, hipStream_t s);
+
+/* Stable counting sort of the T*k (token, slot) pairs by expert.
+ *   idx    device int32 [T, k], values in [0, E)
+ *   count  device int32 [E]
+ *   offset device int32 [E+1], exclusive prefix sum of count
+ *   pairs  device int32 [T*k], entries t*k+j ordered by (expert, token, slot) */
+moe_status moe_group_tokens(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *count,
+                            int32_t *offset, int32_t *pairs, hipStream_t s);
+
+/* Device scratch needed by moe_expert_ffn / moe_layer_forward for batches
+ * of up to T tokens (counters, grouped pairs, activation encodings,
+ * per-pair outputs).  Returns 0 on a bad argument. */
+size_t moe_workspace_bytes(const moe_expert_desc *d, int32_t T, int32_t k, int32_t E, int32_t n_shared);
+
+/* Zero a workspace (a fill kernel on stream s, no hipMemset) before its
+ * first use.  The kernels leave their counters at zero when they finish, so
+ * a workspace is reusable by any later call of the same or smaller sizes.
+ * Calls that share one workspace must be ordered (same stream or events). */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s);
+
+/* Expert FFN and weighted combine for one layer:
+ *   y[t] = (accumulate ? y[t] : 0) + sum_j w[t,j] * FFN_{idx[t,j]}(x[t]) + sum_s FFN_shared_s(x[t])
+ *   FFN_e(x) = down_e( SiLU(gate_e x) * (up_e x) )
+ * (gate/up/down expert tensors: T4 MoE-cache report, section "What the MoE
+ * cache caches"; shared experts of weight one: laptop 16B MoE post, lpnh.cn,
+ * section 2.1.)
+ *   d           expert shape, shared by all experts of the layer
+ *   x           device fp32 [T, H] normalised states
+ *   idx, w      device int32 / fp32 [T, k] routing (ids distinct per token)
+ *   expert_ptrs device array [E] of device addresses of each expert in the
+ *               slot layout (only the selected entries are read)
+ *   shared_ptrs device array [n_shared] of slot-layout addresses, or NULL
+ *               when n_shared == 0
+ *   y           device fp32 [T, H]
+ *   act_out     NULL, or device fp32 [T*(k+n_shared), Ipad]: SiLU(g)*u of
+ *               every pair, in grouped order (routed experts by ascending
+ *               id then token; then each shared expert by token); columns
+ *               [I, Ipad) are not written
+ *   ws          workspace from moe_workspace_bytes(d, >=T, >=k, >=E, >=n_shared),
+ *               initialised once with moe_workspace_init
+ * 1 <= T <= 32. */
+moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, int32_t k,
+                          int32_t E, const int32_t *idx, const float *w,
+                          const void *const *expert_ptrs, const void *const *shared_ptrs,
+                          int32_t n_shared, float *y, int32_t accumulate, float *act_out,
+                          void *ws, size_t ws_bytes, hipStream_t s);
+
+/* First half of moe_layer_forward (one kernel): RMSNorm of h, router
+ * logits (+ bias), softmax top-k, grouping of the (token, expert) pairs and
+ * the encoding of the normalised states, all left in the workspace for the
+ * moe_layer_ffn that follows on the same stream and workspace.  idx_out /
+ * w_out as in moe_layer_forward. */
+moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, const float *w_router,
+                           const float *bias, int32_t E, int32_t k, int32_t n_shared, float eps,
+                           int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes, hipStream_t s);
+
+/* Second half (two kernels): the expert FFN of the pairs grouped by the
+ * preceding moe_layer_route in `ws`, weighted combine, h += result.  T, E,
+ * k and n_shared must equal those of that moe_layer_route. */
+moe_status moe_layer_ffn(const moe_expert_desc *d, float *h, int32_t T, int32_t E, int32_t k,
+                         const void *const *expert_ptrs, const void *const *shared_ptrs, int32_t n_shared,
+                         void *ws, size_t ws_bytes, hipStream_t s);
+
+/* One whole pre-norm residual MoE layer, fused into three kernels:
+ *   xhat = RMSNorm(h); idx, w = top-k(router(xhat) + bias); h += MoE(xhat)
+ *   h           device fp32 [T, H], updated in place
+ *   idx_out     NULL or device int32 [T, k]; w_out NULL or device fp32 [T, k]
+ * Other arguments as for moe_route_topk and moe_expert_ffn. */
+moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, const float *w_router,
+                             const float *bias, int32_t E, int32_t k,
+                             const void *const *expert_ptrs, const void *const *shared_ptrs,
+                             int32_t n_shared, float eps, int32_t *idx_out, float *w_out,
+                             void *ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------- */
+/* Expert slot-pool cache (T4 MoE-cache report, sections "What the MoE cache
+ * caches" and "Size your experts before configuring").  Experts are grouped
+ * by (type, shape) -- one moe_expert_desc per group -- and each group owns
+ * one pool of fixed-size slots in HBM shared by all of its layers.  A
+ * lookup of a layer-step's distinct experts hits (the expert is in a slot)
+ * or misses (the least recently used key of the group is evicted and its
+ * slot reassigned); misses are then uploaded from pinned host memory with
+ * hipMemcpyAsync on a copy stream.  Only batches of up to 32 tokens use the
+ * cache. */
+
+/* Slots per group for a byte budget: each group gets the same share of its
+ * (layer, expert) keys,
+ *     slots[g] = floor(budget * layers[g] / sum_h layers[h] * bytes[h]) - 1,
+ * and a group below top_k slots is disabled (0).  This reproduces the
+ * report's printed figures (1,834 slots per group at 10,000 MiB for
+ * Qwen3-30B-A3B Q4_K_M; 50 MiB accepted, 49 MiB refused).
+ *   groups [n_groups] host, layers_per_group [n_groups] host, slots_out
+ *   [n_groups] host.  Returns MOE_ERR_BUDGET when every group is disabled
+ *   (slots_out still filled). */
+moe_status moe_cache_plan(const moe_expert_desc *groups, const int32_t *layers_per_group,
+                          int32_t n_groups, uint64_t budget_bytes, int32_t top_k,
+                          int32_t *slots_out);
+
+typedef struct moe_cache moe_cache;
+
+/* Create a cache.
+ *   groups [n_groups], slots [n_groups] (all >= 1; a disabled group is
+ *   refused with MOE_ERR_BUDGET because this library has no host fallback
+ *   for its experts), layer_group [n_layers] (group of each layer),
+ *   host_experts [n_layers * E] pinned host addresses of each expert in the
+ *   slot layout (the pinned memory stays owned by the caller and must
+ *   outlive the cache).  Allocates one device pool per group (hipMalloc) and
+ *   one device pointer table per layer. */
+moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
+                            const int32_t *layer_group, int32_t n_layers, int32_t E,
+                            const void *const *host_experts, moe_cache **out);
+
+/* Look up the distinct experts of one layer-step (host int32 [n], strictly
+ * ascending ids in [0, E)).  T is the batch size of the step (for the
+ * per-batch-size hit statistics).  Updates the LRU state and records the
+ * misses for the next moe_cache_upload of this layer.  Per expert: slot_out
+ * (host int32 [n]), hit_out (host uint8 [n]), victim_layer/victim_expert
+ * (host int32 [n], -1 when nothing was evicted; either may be NULL).
+ * Returns MOE_ERR_CAPACITY when n exceeds the group's slots and
+ * MOE_ERR_BATCH when T > 32 (state unchanged in both cases). */
+moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, const int32_t *experts, int32_t n,
+                            int32_t *slot_out, uint8_t *hit_out, int32_t *victim_layer,
+                            int32_t *victim_expert);
+
+/* Enqueue the misses recorded by the last lookup of `layer` as
+ * hipMemcpyAsync host->device copies on copy_stream, then record `done` (may
+ * be NULL) on copy_stream.  The compute stream waits on `done` before the
+ * FFN reads the slots.  The layer's device pointer table is also refreshed
+ * on copy_stream. */
+moe_status moe_cache_upload(moe_cache *c, int32_t layer, hipStream_t copy_stream, hipEvent_t done);
+
+/* Device array [E] of slot addresses of `layer` (entries of experts not
+ * resident are NULL).  The array is owned by the cache and is valid after
+ * the upload of the layer completes.  Pass it as expert_ptrs. */
+const void *const *moe_cache_expert_ptrs(moe_cache *c, int32_t layer);
+
+typedef struct {
+    uint64_t lookups, hits, misses, evictions, upload_bytes;
+    uint64_t lookups_le8, hits_le8;     /* steps with T <= 8 */
+    uint64_t lookups_9_32, hits_9_32;   /* steps with 9 <= T <= 32 */
+} moe_cache_stats_t;
+
+moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out);
+
+/* Reset statistics (not the cache contents). */
+moe_status moe_cache_reset_stats(moe_cache *c);
+
+/* Drain outstanding copies and free the pools and tables. */
+void moe_cache_destroy(moe_cache *c);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

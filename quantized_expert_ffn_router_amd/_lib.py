@@ -1,0 +1,280 @@
+"""ctypes binding of libmoe.so (include/moe.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_Q8_0, MOE_Q4_K, MOE_Q6_K = 1, 2, 3
+
+EXPORTED = [
+    "moe_last_error", "moe_expert_bytes", "moe_down_k", "moe_repack_expert",
+    "moe_rmsnorm", "moe_route_topk", "moe_group_tokens", "moe_workspace_bytes",
+    "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
+    "moe_cache_plan", "moe_cache_create", "moe_cache_lookup", "moe_cache_upload",
+    "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
+]
+
+_STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_QTYPE",
+           -4: "MOE_ERR_BUDGET", -5: "MOE_ERR_CAPACITY", -6: "MOE_ERR_HIP", -7: "MOE_ERR_BATCH",
+           -8: "MOE_ERR_STATE"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+
+
+class ExpertDesc(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_int32), ("up", ctypes.c_int32), ("down", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, qtypes, H: int, I: int) -> "ExpertDesc":
+        return cls(int(qtypes[0]), int(qtypes[1]), int(qtypes[2]), int(H), int(I))
+
+
+class CacheStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "lookups", "hits", "misses", "evictions", "upload_bytes",
+        "lookups_le8", "hits_le8", "lookups_9_32", "hits_9_32")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with quantized_expert_ffn_router_amd/build.py")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i32, u64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(ExpertDesc)
+    sig = {
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_expert_bytes": (ctypes.c_int64, [D]),
+        "moe_down_k": (i32, [D]),
+        "moe_repack_expert": (i32, [D, P, P, P, P, sz]),
+        "moe_rmsnorm": (i32, [P, i32, i32, f32, P, P]),
+        "moe_route_topk": (i32, [P, i32, i32, P, P, i32, i32, P, P, P, P]),
+        "moe_group_tokens": (i32, [P, i32, i32, i32, P, P, P, P]),
+        "moe_workspace_bytes": (sz, [D, i32, i32, i32, i32]),
+        "moe_workspace_init": (i32, [P, sz, P]),
+        "moe_expert_ffn": (i32, [D, P, i32, i32, i32, P, P, P, P, i32, P, i32, P, P, sz, P]),
+        "moe_layer_route": (i32, [D, P, i32, P, P, i32, i32, i32, f32, P, P, P, sz, P]),
+        "moe_layer_ffn": (i32, [D, P, i32, i32, i32, P, P, i32, P, sz, P]),
+        "moe_layer_forward": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
+        "moe_cache_plan": (i32, [D, P, i32, u64, i32, P]),
+        "moe_cache_create": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(P)]),
+        "moe_cache_lookup": (i32, [P, i32, i32, P, i32, P, P, P, P]),
+        "moe_cache_upload": (i32, [P, i32, P, P]),
+        "moe_cache_expert_ptrs": (P, [P, i32]),
+        "moe_cache_stats": (i32, [P, ctypes.POINTER(CacheStats)]),
+        "moe_cache_reset_stats": (i32, [P]),
+        "moe_cache_destroy": (None, [P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(st: int):
+    if st != 0:
+        raise MoeError(st, lib().moe_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    """Device/host address of a torch tensor or numpy array (None passes NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _desc(d) -> ExpertDesc:
+    return d if isinstance(d, ExpertDesc) else ExpertDesc.of(*d)
+
+
+# ---------------------------------------------------------------- layout
+
+def moe_expert_bytes(desc) -> int:
+    n = lib().moe_expert_bytes(ctypes.byref(_desc(desc)))
+    if n < 0:
+        raise MoeError(-2, "bad expert desc")
+    return n
+
+
+def moe_down_k(desc) -> int:
+    n = lib().moe_down_k(ctypes.byref(_desc(desc)))
+    if n < 0:
+        raise MoeError(-2, "bad expert desc")
+    return n
+
+
+def moe_repack_expert(desc, gate: np.ndarray, up: np.ndarray, down: np.ndarray, out: Optional[np.ndarray] = None
+                      ) -> np.ndarray:
+    """Host repack of one expert (canonical blocks -> slot layout)."""
+    d = _desc(desc)
+    n = moe_expert_bytes(d)
+    if out is None:
+        out = np.empty(n, np.uint8)
+    g, u, dn = (np.ascontiguousarray(a, np.uint8) for a in (gate, up, down))
+    _check(lib().moe_repack_expert(ctypes.byref(d), g.ctypes.data, u.ctypes.data, dn.ctypes.data,
+                                   out.ctypes.data, out.nbytes))
+    return out
+
+
+# ---------------------------------------------------------------- steps
+
+def moe_rmsnorm(h, T: int, H: int, eps: float, xhat, stream=None):
+    _check(lib().moe_rmsnorm(_ptr(h), T, H, eps, _ptr(xhat), _stream(stream)))
+
+
+def moe_route_topk(x, T: int, H: int, w_router, bias, E: int, k: int, idx, w, logits=None, stream=None):
+    _check(lib().moe_route_topk(_ptr(x), T, H, _ptr(w_router), _ptr(bias), E, k, _ptr(idx), _ptr(w),
+                                _ptr(logits), _stream(stream)))
+
+
+def moe_group_tokens(idx, T: int, k: int, E: int, count, offset, pairs, stream=None):
+    _check(lib().moe_group_tokens(_ptr(idx), T, k, E, _ptr(count), _ptr(offset), _ptr(pairs), _stream(stream)))
+
+
+def moe_workspace_bytes(desc, T: int, k: int, E: int, n_shared: int = 0) -> int:
+    n = lib().moe_workspace_bytes(ctypes.byref(_desc(desc)), T, k, E, n_shared)
+    if n == 0:
+        raise MoeError(-1, "bad workspace arguments")
+    return n
+
+
+def moe_workspace_init(ws, nbytes: int, stream=None):
+    _check(lib().moe_workspace_init(_ptr(ws), nbytes, _stream(stream)))
+
+
+def moe_expert_ffn(desc, x, T: int, k: int, E: int, idx, w, expert_ptrs, shared_ptrs, n_shared: int, y,
+                   accumulate: int, act_out, ws, ws_bytes: int, stream=None):
+    _check(lib().moe_expert_ffn(ctypes.byref(_desc(desc)), _ptr(x), T, k, E, _ptr(idx), _ptr(w), _ptr(expert_ptrs),
+                                _ptr(shared_ptrs), n_shared, _ptr(y), accumulate, _ptr(act_out), _ptr(ws),
+                                ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward(desc, h, T: int, w_router, bias, E: int, k: int, expert_ptrs, shared_ptrs, n_shared: int,
+                      eps: float, idx_out, w_out, ws, ws_bytes: int, stream=None):
+    _check(lib().moe_layer_forward(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k,
+                                   _ptr(expert_ptrs), _ptr(shared_ptrs), n_shared, eps, _ptr(idx_out),
+                                   _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_route(desc, h, T: int, w_router, bias, E: int, k: int, n_shared: int, eps: float, idx_out, w_out,
+                    ws, ws_bytes: int, stream=None):
+    _check(lib().moe_layer_route(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k, n_shared,
+                                 eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_ffn(desc, h, T: int, E: int, k: int, expert_ptrs, shared_ptrs, n_shared: int, ws, ws_bytes: int,
+                  stream=None):
+    _check(lib().moe_layer_ffn(ctypes.byref(_desc(desc)), _ptr(h), T, E, k, _ptr(expert_ptrs), _ptr(shared_ptrs),
+                               n_shared, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------- cache
+
+def moe_cache_plan(descs: Sequence, layers_per_group: Sequence[int], budget_bytes: int, top_k: int):
+    """Returns (status, slots).  status is 0 or the MOE_ERR_BUDGET code."""
+    n = len(descs)
+    arr = (ExpertDesc * n)(*[_desc(d) for d in descs])
+    lay = np.asarray(layers_per_group, np.int32)
+    slots = np.zeros(n, np.int32)
+    st = lib().moe_cache_plan(arr, lay.ctypes.data, n, int(budget_bytes), top_k, slots.ctypes.data)
+    if st not in (0, -4):
+        _check(st)
+    return st, slots
+
+
+class Cache:
+    """Owner of a moe_cache* (moe_cache_create / moe_cache_destroy)."""
+
+    def __init__(self, descs: Sequence, slots: Sequence[int], layer_group: Sequence[int], E: int,
+                 host_expert_ptrs: Sequence[int]):
+        n = len(descs)
+        self._descs = (ExpertDesc * n)(*[_desc(d) for d in descs])
+        self._slots = np.asarray(slots, np.int32)
+        self._lg = np.asarray(layer_group, np.int32)
+        self._hp = np.asarray(host_expert_ptrs, np.uint64)
+        self.n_layers = len(self._lg)
+        self.E = E
+        h = ctypes.c_void_p()
+        _check(lib().moe_cache_create(self._descs, n, self._slots.ctypes.data, self._lg.ctypes.data,
+                                      self.n_layers, E, self._hp.ctypes.data, ctypes.byref(h)))
+        self.h = h
+
+    def lookup(self, layer: int, T: int, experts: np.ndarray):
+        ex = np.ascontiguousarray(experts, np.int32)
+        n = ex.shape[0]
+        slot = np.empty(n, np.int32)
+        hit = np.empty(n, np.uint8)
+        vl = np.empty(n, np.int32)
+        ve = np.empty(n, np.int32)
+        _check(lib().moe_cache_lookup(self.h, layer, T, ex.ctypes.data, n, slot.ctypes.data, hit.ctypes.data,
+                                      vl.ctypes.data, ve.ctypes.data))
+        return slot, hit, vl, ve
+
+    def upload(self, layer: int, copy_stream, done_event=None):
+        ev = None if done_event is None else done_event.cuda_event if hasattr(done_event, "cuda_event") else done_event
+        _check(lib().moe_cache_upload(self.h, layer, _stream(copy_stream), ev))
+
+    def expert_ptrs(self, layer: int) -> int:
+        p = lib().moe_cache_expert_ptrs(self.h, layer)
+        if not p:
+            _check(-1)
+        return p
+
+    def stats(self) -> dict:
+        s = CacheStats()
+        _check(lib().moe_cache_stats(self.h, ctypes.byref(s)))
+        return s.as_dict()
+
+    def reset_stats(self):
+        _check(lib().moe_cache_reset_stats(self.h))
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,390 @@
+// moe_host.cpp -- host half of libmoe: errors, expert sizes, the repacker
+// into the slot layout, and the expert slot-pool cache.
+//
+// Slot-pool cache (T4 MoE-cache report, kongchang.com, sections "What the
+// MoE cache caches" and "Size your experts before configuring"): experts
+// are grouped by (type, shape); each group owns one pool of fixed-size slots
+// in HBM shared by all of its layers, so a hot expert of one layer can push
+// out a cold expert of another; hits are read from HBM, misses are uploaded
+// over PCIe; eviction is least-recently-used.  One hipMalloc per pool (one
+// large allocation instead of one per tensor, as the GPU-offload research
+// notes, kwkr.cn, section 3, recommend).  Uploads are hipMemcpyAsync from
+// pinned host memory on a caller-given copy stream (pinned memory and
+// asynchronous copies: laptop 16B MoE post, lpnh.cn, section 5.2).
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "no error";
+
+void set_error(const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+namespace {
+
+// Copy one canonical matrix [n, k] into tiles.
+void repack_matrix(int qt, const uint8_t *src, int n, int k, uint8_t *dst)
+{
+    const int S = k / kTileCols;
+    const size_t TB = (size_t)tile_bytes(qt);
+    const size_t row_bytes = (size_t)(k / block_weights(qt)) * block_bytes(qt);
+    for (int r = 0; r < n; r++) {
+        const int rt = r / kTileRows, lt = r % kTileRows;
+        const uint8_t *row = src + row_bytes * r;
+        for (int s = 0; s < S; s++) {
+            uint8_t *tile = dst + ((size_t)rt * S + s) * TB;
+            if (qt == MOE_Q4_K) {
+                const uint8_t *b = row + (size_t)s * 144;
+                memcpy(tile + lt * 16, b, 16);  // d, dmin, scales[12]
+                for (int j = 0; j < 8; j++) memcpy(tile + 1024 + j * 1024 + lt * 16, b + 16 + 16 * j, 16);
+            } else if (qt == MOE_Q6_K) {
+                const uint8_t *b = row + (size_t)s * 210;
+                for (int j = 0; j < 8; j++) memcpy(tile + j * 1024 + lt * 16, b + 16 * j, 16);        // ql
+                for (int j = 0; j < 4; j++) memcpy(tile + 8192 + j * 1024 + lt * 16, b + 128 + 16 * j, 16);  // qh
+                memcpy(tile + 12288 + lt * 16, b + 192, 16);  // sc
+                memcpy(tile + 13312 + lt * 2, b + 208, 2);    // d
+            } else {
+                for (int bb = 0; bb < 8; bb++) {
+                    const uint8_t *b = row + (size_t)(8 * s + bb) * 34;
+                    memcpy(tile + (2 * bb) * 1024 + lt * 16, b + 2, 16);
+                    memcpy(tile + (2 * bb + 1) * 1024 + lt * 16, b + 18, 16);
+                    memcpy(tile + 16384 + lt * 16 + bb * 2, b, 2);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err; }
+
+int64_t moe_expert_bytes(const moe_expert_desc *d)
+{
+    ExpertGeom g;
+    if (!d || !geom(*d, &g)) return -1;
+    return (int64_t)g.bytes;
+}
+
+int32_t moe_down_k(const moe_expert_desc *d)
+{
+    ExpertGeom g;
+    if (!d || !geom(*d, &g)) return -1;
+    return g.kd;
+}
+
+moe_status moe_repack_expert(const moe_expert_desc *d, const void *gate, const void *up, const void *down,
+                             void *slot, size_t slot_bytes)
+{
+    ExpertGeom g;
+    if (!d || !gate || !up || !down || !slot) { set_error("moe_repack_expert: null argument"); return MOE_ERR_ARG; }
+    if (!qtype_ok(d->gate) || !qtype_ok(d->up) || !qtype_ok(d->down)) { set_error("moe_repack_expert: bad qtype"); return MOE_ERR_QTYPE; }
+    if (!geom(*d, &g)) { set_error("moe_repack_expert: bad shape H=%d I=%d", d->H, d->I); return MOE_ERR_SHAPE; }
+    if (slot_bytes < g.bytes) { set_error("moe_repack_expert: slot of %zu bytes < %zu", slot_bytes, g.bytes); return MOE_ERR_ARG; }
+    uint8_t *dst = (uint8_t *)slot;
+    repack_matrix(d->gate, (const uint8_t *)gate, d->I, d->H, dst + g.gate_off);
+    repack_matrix(d->up, (const uint8_t *)up, d->I, d->H, dst + g.up_off);
+    repack_matrix(d->down, (const uint8_t *)down, d->H, g.kd, dst + g.down_off);
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// slot-pool cache
+
+moe_status moe_cache_plan(const moe_expert_desc *groups, const int32_t *layers_per_group, int32_t n_groups,
+                          uint64_t budget_bytes, int32_t top_k, int32_t *slots_out)
+{
+    if (!groups || !layers_per_group || !slots_out || n_groups < 1 || top_k < 1) {
+        set_error("moe_cache_plan: bad argument");
+        return MOE_ERR_ARG;
+    }
+    unsigned __int128 denom = 0;
+    for (int g = 0; g < n_groups; g++) {
+        ExpertGeom eg;
+        if (!geom(groups[g], &eg) || layers_per_group[g] < 1) {
+            set_error("moe_cache_plan: bad group %d", g);
+            return MOE_ERR_SHAPE;
+        }
+        denom += (unsigned __int128)eg.bytes * (uint64_t)layers_per_group[g];
+    }
+    bool any = false;
+    for (int g = 0; g < n_groups; g++) {
+        unsigned __int128 q = ((unsigned __int128)budget_bytes * (uint64_t)layers_per_group[g]) / denom;
+        long long s = (long long)q - 1;
+        if (s < top_k) s = 0;
+        if (s > 0x7fffffff) s = 0x7fffffff;
+        slots_out[g] = (int32_t)s;
+        any = any || s > 0;
+    }
+    if (!any) {
+        set_error("cache budget of %llu bytes leaves every group below %d slots", (unsigned long long)budget_bytes, top_k);
+        return MOE_ERR_BUDGET;
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"
+
+struct moe_cache {
+    struct Group {
+        moe_expert_desc desc;
+        size_t slot_bytes = 0;
+        int n_slots = 0;
+        uint8_t *pool = nullptr;
+        std::vector<int64_t> slot_key;  // key = layer*E + expert, -1 free
+        std::vector<int> prev, next;    // recency list over slots, head = most recent
+        int head = -1, tail = -1, next_free = 0;
+    };
+    int n_layers = 0, E = 0, device = 0;
+    std::vector<Group> groups;
+    std::vector<int> layer_group;
+    std::vector<const void *> host;      // [L*E] pinned sources
+    std::vector<int> where;              // [L*E] slot of a key, -1 absent
+    const void **htab = nullptr;         // pinned [L*E] slot addresses
+    void **dtab = nullptr;               // device [L*E]
+    std::vector<hipEvent_t> table_done;  // per layer: last table copy
+    std::vector<char> table_pending;
+    struct Pending { int slot; const void *src; };
+    std::vector<std::vector<Pending>> pending;  // per layer
+    std::vector<char> looked_up;
+    moe_cache_stats_t st{};
+};
+
+namespace {
+
+void unlink(moe_cache::Group &g, int s)
+{
+    int p = g.prev[s], n = g.next[s];
+    if (p >= 0) g.next[p] = n; else g.head = n;
+    if (n >= 0) g.prev[n] = p; else g.tail = p;
+    g.prev[s] = g.next[s] = -1;
+}
+
+void push_front(moe_cache::Group &g, int s)
+{
+    g.prev[s] = -1;
+    g.next[s] = g.head;
+    if (g.head >= 0) g.prev[g.head] = s;
+    g.head = s;
+    if (g.tail < 0) g.tail = s;
+}
+
+void destroy(moe_cache *c)
+{
+    if (!c) return;
+    (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    for (auto &g : c->groups)
+        if (g.pool) (void)hipFree(g.pool);
+    if (c->dtab) (void)hipFree(c->dtab);
+    if (c->htab) (void)hipHostFree((void *)c->htab);
+    for (auto ev : c->table_done)
+        if (ev) (void)hipEventDestroy(ev);
+    delete c;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
+                            const int32_t *layer_group, int32_t n_layers, int32_t E,
+                            const void *const *host_experts, moe_cache **out)
+{
+    if (!groups || !slots || !layer_group || !host_experts || !out || n_groups < 1 || n_layers < 1 || E < 1) {
+        set_error("moe_cache_create: bad argument");
+        return MOE_ERR_ARG;
+    }
+    *out = nullptr;
+    for (int g = 0; g < n_groups; g++) {
+        if (slots[g] < 1) {
+            set_error("group %d has no slots (below the budget floor); its experts would have nowhere to run", g);
+            return MOE_ERR_BUDGET;
+        }
+    }
+    for (int l = 0; l < n_layers; l++) {
+        if (layer_group[l] < 0 || layer_group[l] >= n_groups) { set_error("layer %d: bad group", l); return MOE_ERR_ARG; }
+    }
+    for (size_t i = 0; i < (size_t)n_layers * E; i++) {
+        if (!host_experts[i]) { set_error("host expert %zu is null", i); return MOE_ERR_ARG; }
+    }
+    moe_cache *c = new moe_cache();
+    c->n_layers = n_layers;
+    c->E = E;
+    if (hipGetDevice(&c->device) != hipSuccess) { delete c; set_error("hipGetDevice failed"); return MOE_ERR_HIP; }
+    c->groups.resize(n_groups);
+    for (int g = 0; g < n_groups; g++) {
+        ExpertGeom eg;
+        if (!geom(groups[g], &eg)) { destroy(c); set_error("group %d: bad expert desc", g); return MOE_ERR_SHAPE; }
+        auto &G = c->groups[g];
+        G.desc = groups[g];
+        G.slot_bytes = eg.bytes;
+        G.n_slots = slots[g];
+        G.slot_key.assign(G.n_slots, -1);
+        G.prev.assign(G.n_slots, -1);
+        G.next.assign(G.n_slots, -1);
+        hipError_t e = hipMalloc((void **)&G.pool, G.slot_bytes * (size_t)G.n_slots);
+        if (e != hipSuccess) {
+            G.pool = nullptr;
+            destroy(c);
+            set_error("hipMalloc of %zu bytes for pool %d failed: %s", G.slot_bytes * (size_t)G.n_slots, g,
+                      hipGetErrorString(e));
+            return MOE_ERR_HIP;
+        }
+    }
+    c->layer_group.assign(layer_group, layer_group + n_layers);
+    c->host.assign(host_experts, host_experts + (size_t)n_layers * E);
+    c->where.assign((size_t)n_layers * E, -1);
+    size_t tb = sizeof(void *) * (size_t)n_layers * E;
+    if (hipHostMalloc((void **)&c->htab, tb, hipHostMallocDefault) != hipSuccess ||
+        hipMalloc((void **)&c->dtab, tb) != hipSuccess || hipMemset(c->dtab, 0, tb) != hipSuccess) {
+        destroy(c);
+        set_error("allocation of the slot tables failed");
+        return MOE_ERR_HIP;
+    }
+    memset((void *)c->htab, 0, tb);
+    c->table_done.assign(n_layers, nullptr);
+    for (int l = 0; l < n_layers; l++) {
+        if (hipEventCreateWithFlags(&c->table_done[l], hipEventDisableTiming) != hipSuccess) {
+            destroy(c);
+            set_error("hipEventCreate failed");
+            return MOE_ERR_HIP;
+        }
+    }
+    c->table_pending.assign(n_layers, 0);
+    c->pending.assign(n_layers, {});
+    c->looked_up.assign(n_layers, 0);
+    *out = c;
+    return MOE_OK;
+}
+
+moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, const int32_t *experts, int32_t n,
+                            int32_t *slot_out, uint8_t *hit_out, int32_t *victim_layer, int32_t *victim_expert)
+{
+    if (!c || !experts || !slot_out || !hit_out || n < 0 || layer < 0 || layer >= c->n_layers) {
+        set_error("moe_cache_lookup: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (T < 1 || T > kMaxT) { set_error("moe_cache_lookup: T=%d outside [1, 32]; larger batches bypass the cache", T); return MOE_ERR_BATCH; }
+    for (int i = 0; i < n; i++) {
+        if (experts[i] < 0 || experts[i] >= c->E || (i > 0 && experts[i] <= experts[i - 1])) {
+            set_error("moe_cache_lookup: experts must be distinct, ascending and in [0, %d)", c->E);
+            return MOE_ERR_ARG;
+        }
+    }
+    auto &G = c->groups[c->layer_group[layer]];
+    if (n > G.n_slots) {
+        set_error("moe_cache_lookup: %d distinct experts exceed the %d slots of the group", n, G.n_slots);
+        return MOE_ERR_CAPACITY;
+    }
+    if (c->pending[layer].size()) { set_error("moe_cache_lookup: previous misses of layer %d not uploaded", layer); return MOE_ERR_STATE; }
+    // the previous table copy of this layer must have read the pinned table
+    if (c->table_pending[layer]) {
+        if (hipEventSynchronize(c->table_done[layer]) != hipSuccess) { set_error("hipEventSynchronize failed"); return MOE_ERR_HIP; }
+        c->table_pending[layer] = 0;
+    }
+    const int64_t E = c->E;
+    for (int i = 0; i < n; i++) {
+        const int64_t key = layer * E + experts[i];
+        int s = c->where[key];
+        int vl = -1, ve = -1;
+        c->st.lookups++;
+        if (T <= 8) c->st.lookups_le8++; else c->st.lookups_9_32++;
+        if (s >= 0) {
+            hit_out[i] = 1;
+            c->st.hits++;
+            if (T <= 8) c->st.hits_le8++; else c->st.hits_9_32++;
+            unlink(G, s);
+            push_front(G, s);
+        } else {
+            hit_out[i] = 0;
+            c->st.misses++;
+            if (G.next_free < G.n_slots) {
+                s = G.next_free++;
+            } else {
+                s = G.tail;
+                const int64_t vk = G.slot_key[s];
+                vl = (int)(vk / E);
+                ve = (int)(vk % E);
+                c->where[vk] = -1;
+                unlink(G, s);
+                c->st.evictions++;
+            }
+            G.slot_key[s] = key;
+            c->where[key] = s;
+            push_front(G, s);
+            c->pending[layer].push_back({s, c->host[key]});
+        }
+        c->htab[key] = G.pool + (size_t)s * G.slot_bytes;
+        slot_out[i] = s;
+        if (victim_layer) victim_layer[i] = vl;
+        if (victim_expert) victim_expert[i] = ve;
+    }
+    c->looked_up[layer] = 1;
+    return MOE_OK;
+}
+
+moe_status moe_cache_upload(moe_cache *c, int32_t layer, hipStream_t copy_stream, hipEvent_t done)
+{
+    if (!c || layer < 0 || layer >= c->n_layers) { set_error("moe_cache_upload: bad argument"); return MOE_ERR_ARG; }
+    if (!c->looked_up[layer]) { set_error("moe_cache_upload: layer %d has no lookup", layer); return MOE_ERR_STATE; }
+    auto &G = c->groups[c->layer_group[layer]];
+    for (const auto &p : c->pending[layer]) {
+        hipError_t e = hipMemcpyAsync(G.pool + (size_t)p.slot * G.slot_bytes, p.src, G.slot_bytes,
+                                      hipMemcpyHostToDevice, copy_stream);
+        if (e != hipSuccess) { set_error("expert upload failed: %s", hipGetErrorString(e)); return MOE_ERR_HIP; }
+        c->st.upload_bytes += G.slot_bytes;
+    }
+    c->pending[layer].clear();
+    const size_t off = (size_t)layer * c->E;
+    hipError_t e = hipMemcpyAsync(c->dtab + off, c->htab + off, sizeof(void *) * (size_t)c->E,
+                                  hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(c->table_done[layer], copy_stream);
+    if (e == hipSuccess && done) e = hipEventRecord(done, copy_stream);
+    if (e != hipSuccess) { set_error("slot table upload failed: %s", hipGetErrorString(e)); return MOE_ERR_HIP; }
+    c->table_pending[layer] = 1;
+    c->looked_up[layer] = 0;
+    return MOE_OK;
+}
+
+const void *const *moe_cache_expert_ptrs(moe_cache *c, int32_t layer)
+{
+    if (!c || layer < 0 || layer >= c->n_layers) { set_error("moe_cache_expert_ptrs: bad argument"); return nullptr; }
+    return (const void *const *)(c->dtab + (size_t)layer * c->E);
+}
+
+moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out)
+{
+    if (!c || !out) { set_error("moe_cache_stats: null argument"); return MOE_ERR_ARG; }
+    *out = c->st;
+    return MOE_OK;
+}
+
+moe_status moe_cache_reset_stats(moe_cache *c)
+{
+    if (!c) { set_error("moe_cache_reset_stats: null cache"); return MOE_ERR_ARG; }
+    c->st = moe_cache_stats_t{};
+    return MOE_OK;
+}
+
+void moe_cache_destroy(moe_cache *c) { destroy(c); }
+
+}  // extern "C"

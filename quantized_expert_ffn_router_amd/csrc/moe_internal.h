@@ -1,0 +1,130 @@
+// moe_internal.h -- private definitions shared by the libmoe sources.
+//
+// Slot layout.  A quantized matrix [N, K] (N a multiple of 64, K a multiple
+// of 256) is cut into tiles of 64 rows x 256 columns, stored tile after tile
+// with the column index fastest: tile (rt, s) starts at (rt*S + s)*tile_bytes,
+// S = K/256.  Inside a tile each 16-byte piece ("granule") of the 64 rows'
+// blocks is stored side by side (row 0's granule, row 1's, ...), so that a
+// wavefront in which lane r owns row r reads each granule of the tile as
+// 1 KiB of consecutive bytes.  The bytes are the canonical block bytes,
+// permuted; no byte is added or dropped.
+//
+//   Q4_K tile (9216 B):  [meta 64x16: d,dmin,scales[12]] [qs granule j=0..7: 64x16]
+//   Q6_K tile (13440 B): [ql granule j=0..7: 64x16] [qh granule j=0..3: 64x16]
+//                        [sc 64x16] [d 64x2]
+//   Q8_0 tile (17408 B): [q granule j=0..15: 64x16 (block j/2, half j%2)] [d 64x16 (8 fp16)]
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kTileRows = 64;
+constexpr int kTileCols = 256;
+constexpr int kMaxT = 32;
+constexpr int kMaxE = 1024;
+constexpr int kMaxShared = 8;
+constexpr int kMaxH = 16384;
+constexpr int kPieces = 3;  // activations are encoded as 3 int8 pieces
+
+inline int tile_bytes(int qtype)
+{
+    switch (qtype) {
+    case MOE_Q4_K: return 64 * 144;
+    case MOE_Q6_K: return 64 * 210;
+    case MOE_Q8_0: return 64 * 8 * 34;
+    default: return 0;
+    }
+}
+
+inline int block_weights(int qtype) { return qtype == MOE_Q8_0 ? 32 : 256; }
+inline int block_bytes(int qtype)
+{
+    return qtype == MOE_Q8_0 ? 34 : qtype == MOE_Q4_K ? 144 : qtype == MOE_Q6_K ? 210 : 0;
+}
+inline bool qtype_ok(int q) { return q == MOE_Q8_0 || q == MOE_Q4_K || q == MOE_Q6_K; }
+
+// Down-row length after padding to whole 256-column tiles.
+inline int down_k(const moe_expert_desc &d) { return (d.I + kTileCols - 1) / kTileCols * kTileCols; }
+
+inline size_t mat_bytes(int qtype, int n, int k)
+{
+    return (size_t)(n / kTileRows) * (size_t)(k / kTileCols) * (size_t)tile_bytes(qtype);
+}
+
+struct ExpertGeom {
+    size_t gate_off, up_off, down_off, bytes;
+    int kd;  // padded down row length
+};
+
+inline bool geom(const moe_expert_desc &d, ExpertGeom *g)
+{
+    if (!qtype_ok(d.gate) || !qtype_ok(d.up) || !qtype_ok(d.down)) return false;
+    if (d.H <= 0 || d.I <= 0 || d.H % kTileCols || d.H % kTileRows || d.I % kTileRows) return false;
+    if (d.H > kMaxH || d.I > kMaxH) return false;
+    g->kd = down_k(d);
+    g->gate_off = 0;
+    g->up_off = mat_bytes(d.gate, d.I, d.H);
+    g->down_off = g->up_off + mat_bytes(d.up, d.I, d.H);
+    g->bytes = g->down_off + mat_bytes(d.down, d.H, g->kd);
+    return true;
+}
+
+
+// Self-resetting counters sit at fixed offsets at the start of every
+// workspace, whatever the batch size, so that calls of different sizes can
+// share one workspace: [0] route, [1, 1+kMaxE+kMaxShared) gate/up per
+// distinct expert, then one per 64-row tile of the down matrices.
+constexpr size_t kCntRoute = 0;
+constexpr size_t kCntGU = 4;
+constexpr size_t kCntDn = kCntGU + 4 * (kMaxE + kMaxShared);
+constexpr size_t kCntBytes = (kCntDn + 4 * (kMaxH / 64) + 255) & ~(size_t)255;
+
+// Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
+struct WsLayout {
+    int T, k, E, ns, H, kd, P, U;
+    size_t xq, xs, xsum, logits, idx, w, nuniq, uniq, uoff, ptok, pw, inv,
+        hact, hq, hs, hsum, osc, cnt_route, cnt_gu, cnt_dn, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
+{
+    WsLayout L{};
+    L.T = T; L.k = k; L.E = E; L.ns = ns; L.H = d.H; L.kd = down_k(d);
+    L.P = T * (k + ns);
+    int ur = E < T * k ? E : T * k;
+    L.U = ur + ns;
+    size_t o = kCntBytes;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+    L.xq = take((size_t)T * kPieces * d.H);
+    L.xs = take((size_t)T * 4);
+    L.xsum = take((size_t)T * kPieces * (d.H / 16) * 4);
+    L.logits = take((size_t)T * E * 4);
+    L.idx = take((size_t)T * k * 4);
+    L.w = take((size_t)T * k * 4);
+    L.nuniq = take(4);
+    L.uniq = take((size_t)L.U * 4);
+    L.uoff = take((size_t)(L.U + 1) * 4);
+    L.ptok = take((size_t)L.P * 4);
+    L.pw = take((size_t)L.P * 4);
+    L.inv = take((size_t)L.P * 4);
+    L.hact = take((size_t)L.P * L.kd * 4);
+    L.hq = take((size_t)L.P * kPieces * L.kd);
+    L.hs = take((size_t)L.P * 4);
+    L.hsum = take((size_t)L.P * kPieces * (L.kd / 16) * 4);
+    L.osc = take((size_t)L.P * d.H * 4);
+    L.cnt_route = kCntRoute;
+    L.cnt_gu = kCntGU;
+    L.cnt_dn = kCntDn;
+    L.total = o;
+    return L;
+}
+
+// Error reporting (thread-local message).
+void set_error(const char *fmt, ...);
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+"""Host-side checks of the C ABI (no GPU calls): the library loads, exports
+every function include/moe.h declares, validates arguments before touching
+the GPU, plans cache slots as the T4 MoE-cache report prints, and repacks
+experts by pure byte permutation into the documented tile layout."""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+import quantized_expert_ffn_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = moe.lib()
+    decl = _declared()
+    assert len(decl) >= 19
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(moe.EXPORTED) == decl
+
+
+def test_argument_errors_are_host_side():
+    L = moe.lib()
+    d = moe.ExpertDesc.of((W.Q4_K,) * 3, 2048, 768)
+    fake = 0x1000
+    ws_need = moe.moe_workspace_bytes(d, 8, 8, 128, 0)
+
+    def st(**kw):
+        a = dict(desc=d, h=fake, T=8, wr=fake, bias=None, E=128, k=8, ep=fake, sp=None, ns=0, ws=fake, wsb=ws_need)
+        a.update(kw)
+        import ctypes
+        return L.moe_layer_forward(ctypes.byref(a["desc"]), a["h"], a["T"], a["wr"], a["bias"], a["E"], a["k"],
+                                   a["ep"], a["sp"], a["ns"], 1e-6, None, None, a["ws"], a["wsb"], 0)
+
+    assert st(T=33) == -7 and st(T=0) == -7
+    assert st(k=129) == -1 and st(k=0) == -1 and st(E=2000) == -1
+    assert st(desc=moe.ExpertDesc.of((7, 2, 2), 2048, 768)) == -3
+    assert st(desc=moe.ExpertDesc.of((W.Q4_K,) * 3, 2000, 768)) == -2
+    assert st(desc=moe.ExpertDesc.of((W.Q4_K,) * 3, 2048, 700)) == -2
+    assert st(h=None) == -1 and st(ns=1) == -1
+    assert st(wsb=ws_need - 1) == -1
+    assert b"workspace too small" in L.moe_last_error()
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_topk(fake, 40, 2048, fake, None, 128, 8, fake, fake, None, stream=0)
+    assert ei.value.name == "MOE_ERR_BATCH"
+    with pytest.raises(moe.MoeError):
+        moe.moe_group_tokens(fake, 4, 9, 8, fake, fake, fake, stream=0)
+
+
+def test_cache_plan_through_abi_reproduces_page_example():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "t4_cache_plan_example.json")))
+    pr = g["printed"]
+    descs = [moe.ExpertDesc.of((W.Q4_K,) * 3, g["H"], g["I"]),
+             moe.ExpertDesc.of((W.Q4_K, W.Q4_K, W.Q6_K), g["H"], g["I"])]
+    assert moe.moe_expert_bytes(descs[0]) == 2_654_208
+    assert moe.moe_expert_bytes(descs[1]) == 3_059_712
+    st, slots = moe.moe_cache_plan(descs, [24, 24], pr["budget_mib"] << 20, g["top_k"])
+    assert st == 0 and list(slots) == [pr["slots_per_group"]] * 2
+    st, slots = moe.moe_cache_plan(descs, [24, 24], pr["floor_ok_mib"] << 20, g["top_k"])
+    assert st == 0 and min(slots) >= g["top_k"]
+    st, slots = moe.moe_cache_plan(descs, [24, 24], pr["floor_fail_mib"] << 20, g["top_k"])
+    assert st == -4 and max(slots) == 0
+
+
+@pytest.mark.parametrize("qt", [W.Q8_0, W.Q4_K, W.Q6_K])
+def test_repack_is_a_byte_permutation_with_documented_tiles(qt):
+    cfg = W.MoEConfig("repack", 1, 512, 2, 1, 128, ((qt,) * 3,), seed=9)
+    ex = W.expert(cfg, 0, 1)
+    d = moe.ExpertDesc.of(cfg.qtypes(0), cfg.H, cfg.I)
+    out = moe.moe_repack_expert(d, ex.gate, ex.up, ex.down)
+    assert out.nbytes == cfg.expert_bytes(0) == moe.moe_expert_bytes(d)
+    assert np.array_equal(np.sort(out), np.sort(ex.concat()))
+    # row 5, K-group 1 of the gate matrix: its first 16 canonical bytes sit at
+    # tile (0, 1), lane 5 of the first 16-byte plane
+    S = cfg.H // 256
+    tb = {W.Q8_0: 17408, W.Q4_K: 9216, W.Q6_K: 13440}[qt]
+    row = ex.gate[5]
+    if qt == W.Q4_K:
+        first16 = row[144:160]
+        at = 1 * tb + 5 * 16
+    elif qt == W.Q6_K:
+        first16 = row[210:226]
+        at = 1 * tb + 5 * 16
+    else:
+        first16 = row[8 * 34 + 2:8 * 34 + 18]   # block 8 (K-group 1) quant bytes 0-15
+        at = 1 * tb + 5 * 16
+    assert np.array_equal(out[at:at + 16], first16)
+    assert S == 2

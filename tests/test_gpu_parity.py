@@ -1,0 +1,280 @@
+"""GPU parity of every step of the decode path against the CPU oracle.
+
+Each test prints the case it runs (shape, seed, entry point) before any GPU
+work, so a failing run names its case.  Inputs are seeded; routing inputs
+are redrawn until the oracle's k-th/(k+1)-th logit gap is at least 1e-4.
+Bars: exact for ids, counts, offsets and grouped order; rel 1e-5 on the
+renormalised weights; rel-L2 <= 1e-3 on fp32 outputs (also after removing
+each vector's mean, and on zero-mean weight variants, so that the common
+offset of Q4_K weights cannot hide an error).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads as W
+import quantized_expert_ffn_router_amd as moe
+from quantized_expert_ffn_router_amd.stack import ResidentStack
+
+from helpers import (REL_L2_BAR, TIE_GAP, ExpertCache, centered_rel_l2, chain_min_gap, layer_specs,
+                     oracle_layers, sets_equal, weights_close)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+# ---------------------------------------------------------------- rmsnorm
+@pytest.mark.parametrize("T,H", [(1, 256), (7, 2048), (32, 4096)])
+def test_rmsnorm(T, H):
+    _say("moe_rmsnorm", T, H)
+    h = np.random.default_rng(T).standard_normal((T, H)).astype(np.float32) * 3
+    out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    moe.moe_rmsnorm(_dev(h), T, H, 1e-6, out)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(h)
+    assert oracle.rel_l2(out.cpu().numpy(), ref) < 1e-6
+
+
+# ---------------------------------------------------------------- router / top-k
+ROUTE_CASES = [
+    # (T, H, E, k, zipf, seed)
+    (1, 256, 8, 2, False, 1),
+    (8, 2048, 128, 8, False, 2),
+    (32, 2048, 128, 8, True, 3),
+    (5, 512, 5, 5, False, 4),        # k == E, E not a multiple of 4
+    (3, 768, 61, 7, False, 5),
+    (2, 1024, 1000, 16, False, 6),
+]
+
+
+def _tie_free_route_inputs(T, H, E, k, zipf, seed):
+    rng = np.random.default_rng(seed)
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    bias = None
+    if zipf:
+        p = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+        bias = np.log(p / p.sum())[rng.permutation(E)].astype(np.float32)
+    xs = []
+    while len(xs) < T:
+        x = oracle.rmsnorm(rng.standard_normal(H).astype(np.float32)).astype(np.float32)
+        r = oracle.route(x[None].astype(np.float64), wr, bias, k)
+        if r.gap[0] >= TIE_GAP:
+            xs.append(x)
+    return np.stack(xs), wr, bias
+
+
+@pytest.mark.parametrize("T,H,E,k,zipf,seed", ROUTE_CASES)
+def test_route_topk(T, H, E, k, zipf, seed):
+    _say("moe_route_topk", dict(T=T, H=H, E=E, k=k, zipf=zipf, seed=seed))
+    x, wr, bias = _tie_free_route_inputs(T, H, E, k, zipf, seed)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.moe_route_topk(_dev(x), T, H, _dev(wr), None if bias is None else _dev(bias), E, k, idx, w, lg)
+    torch.cuda.synchronize()
+    ref = oracle.route(x.astype(np.float64), wr, bias, k)
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+    assert sets_equal(gi, ref.idx)
+    assert weights_close(gi, gw, ref.idx, ref.w)
+    assert np.max(np.abs(lg.cpu().numpy() - ref.logits)) < 2e-5
+    # ids come out by descending logit
+    glg = lg.cpu().numpy()
+    for t in range(T):
+        vals = glg[t, gi[t]]
+        assert np.all(vals[:-1] >= vals[1:])
+
+
+# ---------------------------------------------------------------- grouping
+@pytest.mark.parametrize("T,k,E,seed", [(1, 2, 8, 0), (5, 3, 7, 1), (8, 8, 128, 2), (32, 8, 128, 3),
+                                        (32, 1, 1000, 4), (17, 64, 64, 5)])
+def test_group_tokens(T, k, E, seed):
+    _say("moe_group_tokens", T, k, E, seed)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    count = torch.empty(E, dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    pairs = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    moe.moe_group_tokens(_dev(idx), T, k, E, count, off, pairs)
+    torch.cuda.synchronize()
+    ref = oracle.group(idx, E)
+    assert np.array_equal(count.cpu().numpy(), ref.count)
+    assert np.array_equal(off.cpu().numpy(), ref.offset)
+    assert np.array_equal(pairs.cpu().numpy(), ref.pairs)
+
+
+# ---------------------------------------------------------------- expert FFN
+def _upload_experts(cfg, layer, experts: ExpertCache, n):
+    d = moe.ExpertDesc.of(cfg.qtypes(layer), cfg.H, cfg.I)
+    eb = moe.moe_expert_bytes(d)
+    host = np.empty(n * eb, np.uint8)
+    for e in range(n):
+        ex = experts(layer, e)
+        moe.moe_repack_expert(d, ex.gate, ex.up, ex.down, host[e * eb:(e + 1) * eb])
+    buf = _dev(host)
+    tab = torch.tensor([buf.data_ptr() + e * eb for e in range(n)], dtype=torch.int64, device=DEV)
+    return d, buf, tab
+
+
+FFN_CASES = [
+    # (qtypes, H, I, E, k, ns, T, zero_mean)
+    ((W.Q8_0,) * 3, 256, 512, 8, 2, 0, 1, False),
+    ((W.Q4_K,) * 3, 512, 192, 6, 2, 0, 3, False),
+    ((W.Q4_K,) * 3, 512, 192, 6, 2, 0, 3, True),
+    ((W.Q6_K,) * 3, 512, 320, 5, 3, 1, 8, False),     # I=320: down rows padded to 512
+    ((W.Q4_K, W.Q4_K, W.Q6_K), 768, 256, 9, 4, 2, 11, False),
+    ((W.Q8_0, W.Q8_0, W.Q4_K), 1024, 128, 4, 4, 0, 32, False),
+    ((W.Q4_K,) * 3, 2048, 768, 16, 8, 0, 8, True),
+]
+
+
+@pytest.mark.parametrize("qt,H,I,E,k,ns,T,zm", FFN_CASES)
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_expert_ffn(qt, H, I, E, k, ns, T, zm, accumulate):
+    _say("moe_expert_ffn", dict(qt=qt, H=H, I=I, E=E, k=k, ns=ns, T=T, zero_mean=zm, acc=accumulate))
+    cfg = W.MoEConfig("ffn-case", 1, H, E, k, I, (qt,), n_shared=ns, zero_mean=zm, seed=100 + T)
+    experts = ExpertCache(cfg)
+    d, buf, tab = _upload_experts(cfg, 0, experts, E + ns)
+    rng = np.random.default_rng(T)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    wts = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    wts /= wts.sum(axis=1, keepdims=True)
+    y0 = rng.standard_normal((T, H)).astype(np.float32)
+    kd = moe.moe_down_k(d)
+    P = T * (k + ns)
+    ws_bytes = moe.moe_workspace_bytes(d, T, k, E, ns)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    moe.moe_workspace_init(ws, ws_bytes)
+    y = _dev(y0)
+    act = torch.full((P, kd), float("nan"), dtype=torch.float32, device=DEV)
+    moe.moe_expert_ffn(d, _dev(x), T, k, E, _dev(idx), _dev(wts), tab, tab[E:] if ns else None, ns, y, accumulate,
+                       act, ws, ws_bytes)
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy()
+    ag = act.cpu().numpy()
+    # oracle
+    grp = oracle.group(idx, E)
+    yref = y0.astype(np.float64) * accumulate
+    per = {}
+    for t in range(T):
+        for e in list(idx[t]) + [E + s for s in range(ns)]:
+            ex = experts(0, int(e))
+            per[(t, int(e))] = oracle.expert_ffn(qt, H, I, kd, ex.gate, ex.up, ex.down, x[t].astype(np.float64))
+        yref[t] += sum(float(wts[t, j]) * per[(t, int(idx[t, j]))].o for j in range(k))
+        yref[t] += sum(per[(t, E + s)].o for s in range(ns))
+    # activations in grouped order: routed pairs by (expert, token), then shared experts by token
+    order = [divmod(int(p), k) for p in grp.pairs]
+    aref = [per[(t, int(idx[t, j]))].a for t, j in order]
+    aref += [per[(t, E + s)].a for s in range(ns) for t in range(T)]
+    aref = np.stack(aref)
+    ag = ag[:, :I]
+    aref = aref[:, :I]
+    assert np.all(np.isfinite(ag))
+    assert oracle.rel_l2(ag, aref) <= REL_L2_BAR
+    assert centered_rel_l2(ag, aref) <= REL_L2_BAR
+    assert oracle.rel_l2(yg, yref) <= REL_L2_BAR
+    assert centered_rel_l2(yg - y0 * accumulate, yref - y0 * accumulate) <= REL_L2_BAR
+    print("rel-L2 act %.3g y %.3g" % (oracle.rel_l2(ag, aref), oracle.rel_l2(yg, yref)))
+
+
+# ---------------------------------------------------------------- fused layer and stack
+def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None):
+    experts = ExpertCache(cfg)
+    olayers = oracle_layers(cfg, experts, n_layers)
+    x, att = W.tie_free_tokens(cfg, step, T, chain_min_gap(olayers))
+    _say("stack", cfg.name, dict(layers=n_layers, T=T, step=step, attempts=att))
+    st = ResidentStack(layer_specs(cfg, n_layers), experts, T_max=T_max or T)
+    h = _dev(x)
+    idx = torch.empty((n_layers, T, cfg.k), dtype=torch.int32, device=DEV)
+    wts = torch.empty((n_layers, T, cfg.k), dtype=torch.float32, device=DEV)
+    st.step(h, idx, wts)
+    torch.cuda.synchronize()
+    hg, ig, wg = h.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy()
+    href = []
+    for t in range(T):
+        outs = oracle.stack_token(olayers, x[t])
+        for l, o in enumerate(outs):
+            assert sets_equal(ig[l, t][None], o.route.idx), f"layer {l} token {t}"
+            assert weights_close(ig[l, t][None], wg[l, t][None], o.route.idx, o.route.w), f"layer {l} token {t}"
+        href.append(outs[-1].h_next)
+    href = np.stack(href)
+    e1 = oracle.rel_l2(hg, href)
+    e2 = centered_rel_l2(hg - x, href - x)
+    print("rel-L2 h %.3g, centered update %.3g" % (e1, e2))
+    assert e1 <= REL_L2_BAR and e2 <= REL_L2_BAR
+    return st
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+def test_layer_tiny_q8_0(seed):
+    _run_stack_and_compare(W.tiny_q8_0(seed=seed), 1, 1)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_layer_qwen3_shape_q4k(T):
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T), 1, T)
+
+
+def test_layer_qwen3_shape_q4k_zero_mean():
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=4).with_(zero_mean=True, seed=7), 1, 4)
+
+
+def test_layer_qwen3_shape_zipf_t32():
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k_zipf(T=32), 1, 32)
+
+
+@pytest.mark.parametrize("T,first", [(1, 0), (4, 12)])
+def test_layer_mixed_shared_q6k(T, first):
+    cfg = W.mixed_shared_q4k_q6k(T=T)
+    # layer `first` of the mixed stack (0: Q4_K group, 12: Q6_K group)
+    sub = cfg.with_(n_layers=1, layer_qtypes=(cfg.qtypes(first),), seed=cfg.seed + first)
+    _run_stack_and_compare(sub, 1, T)
+
+
+def test_stack_qwen3_shape_4_layers_t8():
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=8, n_layers=4), 4, 8)
+
+
+def test_zero_state_stays_zero():
+    cfg = W.tiny_q8_0(seed=3)
+    experts = ExpertCache(cfg)
+    _say("zero state", cfg.name)
+    st = ResidentStack(layer_specs(cfg), experts, T_max=2)
+    h = torch.zeros((2, cfg.H), dtype=torch.float32, device=DEV)
+    idx = torch.empty((1, 2, cfg.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((1, 2, cfg.k), dtype=torch.float32, device=DEV)
+    st.step(h, idx, w)
+    torch.cuda.synchronize()
+    assert torch.all(h == 0).item()
+    # all logits equal: the lowest ids win, weights uniform
+    assert np.array_equal(idx.cpu().numpy()[0], np.tile(np.arange(cfg.k, dtype=np.int32), (2, 1)))
+    assert np.allclose(w.cpu().numpy(), 1.0 / cfg.k)
+
+
+def test_workspace_reuse_across_sizes():
+    """Counters are left at zero: one workspace serves calls of different T."""
+    cfg = W.qwen3_30b_a3b_q4k(T=8, n_layers=1).with_(seed=11)
+    experts = ExpertCache(cfg)
+    olayers = oracle_layers(cfg, experts, 1)
+    _say("workspace reuse", cfg.name)
+    st = ResidentStack(layer_specs(cfg, 1), experts, T_max=8)
+    for T in (8, 1, 5, 8):
+        x, _ = W.tie_free_tokens(cfg, T, T, chain_min_gap(olayers))
+        h = _dev(x)
+        st.step(h)
+        torch.cuda.synchronize()
+        href = np.stack([oracle.stack_token(olayers, x[t])[-1].h_next for t in range(T)])
+        assert oracle.rel_l2(h.cpu().numpy(), href) <= REL_L2_BAR

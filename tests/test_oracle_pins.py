@@ -287,8 +287,10 @@ def test_expert_ffn_composition_matches_dense_numpy():
     Wd = oracle.dequant_matrix(qd, ex.down, cfg.H, cfg.down_k(0))
     g = Wg @ x
     u = Wu @ x
-    a = g / (1 + np.exp(-g)) * u
+    a = np.zeros(cfg.down_k(0))
+    a[:cfg.I] = g / (1 + np.exp(-g)) * u
     assert np.allclose(f.g, g, rtol=1e-12) and np.allclose(f.u, u, rtol=1e-12)
+    assert np.array_equal(f.a, a) or np.allclose(f.a, a, rtol=1e-14)
     assert np.allclose(f.o, Wd @ a, rtol=1e-11)
     z = oracle.expert_ffn(cfg.qtypes(0), cfg.H, cfg.I, cfg.down_k(0), ex.gate, ex.up, ex.down, np.zeros(cfg.H))
     assert np.all(z.o == 0.0)

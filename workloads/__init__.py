@@ -74,13 +74,14 @@ class MoEConfig:
         return self.layer_qtypes[layer]
 
     def down_k(self, layer: int) -> int:
-        """Row length of the down matrix after block padding."""
-        return padded_k(self.qtypes(layer)[2], self.I)
+        """Row length of the down matrix: I padded to whole 256-weight groups
+        (the padded columns multiply a zero tail of the activation)."""
+        return (self.I + 255) // 256 * 256
 
     def expert_bytes(self, layer: int) -> int:
         qg, qu, qd = self.qtypes(layer)
         return (matrix_bytes(qg, self.I, self.H) + matrix_bytes(qu, self.I, self.H)
-                + matrix_bytes(qd, self.H, self.I))
+                + matrix_bytes(qd, self.H, self.down_k(layer)))
 
     def with_(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -191,7 +192,7 @@ def expert(cfg: MoEConfig, layer: int, e: int) -> ExpertBytes:
     """Expert e of a layer; e in [E, E+n_shared) are the shared experts."""
     qg, qu, qd = cfg.qtypes(layer)
     mats = []
-    for m, (q, n, kk) in enumerate(((qg, cfg.I, cfg.H), (qu, cfg.I, cfg.H), (qd, cfg.H, cfg.I))):
+    for m, (q, n, kk) in enumerate(((qg, cfg.I, cfg.H), (qu, cfg.I, cfg.H), (qd, cfg.H, cfg.down_k(layer)))):
         mats.append(quant_matrix(q, _rng(cfg.seed, layer, e, m), n, kk, cfg.zero_mean))
     return ExpertBytes(*mats)
 
