@@ -75,18 +75,22 @@ inline bool geom(const moe_expert_desc &d, ExpertGeom *g)
 
 // Self-resetting counters sit at fixed offsets at the start of every
 // workspace, whatever the batch size, so that calls of different sizes can
-// share one workspace: [0] route, [1, 1+kMaxE+kMaxShared) gate/up per
-// distinct expert, then one per 64-row tile of the down matrices.
+// share one workspace: [0] route, then one per 64-row tile of the down
+// matrices.
 constexpr size_t kCntRoute = 0;
-constexpr size_t kCntGU = 4;
-constexpr size_t kCntDn = kCntGU + 4 * (kMaxE + kMaxShared);
+constexpr size_t kCntDn = 256;
 constexpr size_t kCntBytes = (kCntDn + 4 * (kMaxH / 64) + 255) & ~(size_t)255;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
+//
+// Activations are stored encoded: per vector of K positions, pieces q[3][K]
+// (int8, piece-major), per-32-position block scales bs[K/32] and exact fp32
+// block sums bsum[K/32], and per-16-position integer sums of each piece
+// ps[3][K/16].
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U;
-    size_t xq, xs, xsum, logits, idx, w, nuniq, uniq, uoff, ptok, pw, inv,
-        hact, hq, hs, hsum, osc, cnt_route, cnt_gu, cnt_dn, total;
+    size_t xq, xbs, xbsum, xps, logits, idx, w, nuniq, wt, ptok, inv,
+        hq, hbs, hbsum, hps, osc, cnt_route, cnt_dn, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -101,24 +105,22 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     size_t o = kCntBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xq = take((size_t)T * kPieces * d.H);
-    L.xs = take((size_t)T * 4);
-    L.xsum = take((size_t)T * kPieces * (d.H / 16) * 4);
+    L.xbs = take((size_t)T * (d.H / 32) * 4);
+    L.xbsum = take((size_t)T * (d.H / 32) * 4);
+    L.xps = take((size_t)T * kPieces * (d.H / 16) * 4);
     L.logits = take((size_t)T * E * 4);
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
     L.nuniq = take(4);
-    L.uniq = take((size_t)L.U * 4);
-    L.uoff = take((size_t)(L.U + 1) * 4);
+    L.wt = take((size_t)L.U * 16);
     L.ptok = take((size_t)L.P * 4);
-    L.pw = take((size_t)L.P * 4);
     L.inv = take((size_t)L.P * 4);
-    L.hact = take((size_t)L.P * L.kd * 4);
     L.hq = take((size_t)L.P * kPieces * L.kd);
-    L.hs = take((size_t)L.P * 4);
-    L.hsum = take((size_t)L.P * kPieces * (L.kd / 16) * 4);
+    L.hbs = take((size_t)L.P * (L.kd / 32) * 4);
+    L.hbsum = take((size_t)L.P * (L.kd / 32) * 4);
+    L.hps = take((size_t)L.P * kPieces * (L.kd / 16) * 4);
     L.osc = take((size_t)L.P * d.H * 4);
     L.cnt_route = kCntRoute;
-    L.cnt_gu = kCntGU;
     L.cnt_dn = kCntDn;
     L.total = o;
     return L;
