@@ -138,8 +138,8 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
         for l in range(nl):
             sp = st.layers[l]
             ev[l][0].record()
-            moe.moe_layer_route(st.descs[l], h, T, st.routers[l], st.biases[l], sp.E, sp.k, sp.n_shared, st.eps,
-                                idx[l], None, st.ws, st.ws_bytes)
+            moe.moe_layer_route(st.descs[l], h, T, st.routers[l], st.biases[l], sp.E, sp.k, st.expert_ptrs(l),
+                                st.shared_ptrs(l), sp.n_shared, st.eps, idx[l], None, st.ws, st.ws_bytes)
             ev[l][1].record()
             moe.moe_layer_ffn(st.descs[l], h, T, sp.E, sp.k, st.expert_ptrs(l), st.shared_ptrs(l), sp.n_shared,
                               st.ws, st.ws_bytes)

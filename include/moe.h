@@ -168,10 +168,16 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
 /* First half of moe_layer_forward (one kernel): RMSNorm of h, router
  * logits (+ bias), softmax top-k, grouping of the (token, expert) pairs and
  * the encoding of the normalised states, all left in the workspace for the
- * moe_layer_ffn that follows on the same stream and workspace.  idx_out /
- * w_out as in moe_layer_forward. */
+ * moe_layer_ffn that follows on the same stream and workspace.
+ *   expert_ptrs / shared_ptrs  NULL, or the expert address tables when their
+ *       entries are final when this kernel runs (resident experts): the
+ *       grouping then records each selected expert's address and the FFN
+ *       kernels skip one dependent load.  With a slot cache, whose table is
+ *       refreshed after the routing is known, pass NULL.
+ *   idx_out / w_out as in moe_layer_forward. */
 moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, const float *w_router,
-                           const float *bias, int32_t E, int32_t k, int32_t n_shared, float eps,
+                           const float *bias, int32_t E, int32_t k, const void *const *expert_ptrs,
+                           const void *const *shared_ptrs, int32_t n_shared, float eps,
                            int32_t *idx_out, float *w_out, void *ws, size_t ws_bytes, hipStream_t s);
 
 /* Second half (two kernels): the expert FFN of the pairs grouped by the

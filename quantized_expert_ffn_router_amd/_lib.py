@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
         "moe_workspace_bytes": (sz, [D, i32, i32, i32, i32]),
         "moe_workspace_init": (i32, [P, sz, P]),
         "moe_expert_ffn": (i32, [D, P, i32, i32, i32, P, P, P, P, i32, P, i32, P, P, sz, P]),
-        "moe_layer_route": (i32, [D, P, i32, P, P, i32, i32, i32, f32, P, P, P, sz, P]),
+        "moe_layer_route": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_layer_ffn": (i32, [D, P, i32, i32, i32, P, P, i32, P, sz, P]),
         "moe_layer_forward": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_cache_plan": (i32, [D, P, i32, u64, i32, P]),
@@ -196,10 +196,11 @@ def moe_layer_forward(desc, h, T: int, w_router, bias, E: int, k: int, expert_pt
                                    _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def moe_layer_route(desc, h, T: int, w_router, bias, E: int, k: int, n_shared: int, eps: float, idx_out, w_out,
-                    ws, ws_bytes: int, stream=None):
-    _check(lib().moe_layer_route(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k, n_shared,
-                                 eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
+def moe_layer_route(desc, h, T: int, w_router, bias, E: int, k: int, expert_ptrs, shared_ptrs, n_shared: int,
+                    eps: float, idx_out, w_out, ws, ws_bytes: int, stream=None):
+    _check(lib().moe_layer_route(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k,
+                                 _ptr(expert_ptrs), _ptr(shared_ptrs), n_shared, eps, _ptr(idx_out), _ptr(w_out),
+                                 _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_layer_ffn(desc, h, T: int, E: int, k: int, expert_ptrs, shared_ptrs, n_shared: int, ws, ws_bytes: int,

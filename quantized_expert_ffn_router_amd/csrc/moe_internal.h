@@ -112,7 +112,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
     L.nuniq = take(4);
-    L.wt = take((size_t)L.U * 16);
+    L.wt = take((size_t)L.U * 32);
     L.ptok = take((size_t)L.P * 4);
     L.inv = take((size_t)L.P * 4);
     L.hq = take((size_t)L.P * kPieces * L.kd);

@@ -51,19 +51,63 @@ namespace {
 constexpr float kC1 = 1.0f / 254.0f;
 constexpr float kC2 = 1.0f / 64516.0f;
 constexpr int kChunk = 8;  // tokens per pass of the matvec kernels
-constexpr int kRouteThreads = 512;
+constexpr int kRouteThreads = 256;
 constexpr int kRouteRows = kRouteThreads / 64;  // router rows per workgroup
+constexpr int kEncThreads = 256;                // positions encoded per workgroup
 constexpr int kMaxK = 64;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
-__device__ __forceinline__ float wave_sum(float v)
+// Cross-lane exchanges without LDS: DPP quad permutes and row mirrors move
+// data inside 16-lane rows, v_permlane16_swap / v_permlane32_swap (gfx950)
+// between rows.  xchg_*(v) returns the value of a partner lane such that a
+// symmetric reduction over (v, partner) pairs at steps 1, 2, 4, 8, 16, 32
+// reduces 2, 4, 8, 16, 32, 64 lanes; every lane of a group ends with the
+// same result.
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int STEP> __device__ __forceinline__ int xchg(int v)
+{
+    if constexpr (STEP == 1) return dpp_i<0xB1>(v);        // quad_perm [1,0,3,2]
+    else if constexpr (STEP == 2) return dpp_i<0x4E>(v);   // quad_perm [2,3,0,1]
+    else if constexpr (STEP == 4) return dpp_i<0x141>(v);  // row_half_mirror
+    else if constexpr (STEP == 8) return dpp_i<0x140>(v);  // row_mirror
+    else if constexpr (STEP == 16) {
+        auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (int)((threadIdx.x & 16) ? r[0] : r[1]);
+    } else {
+        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+    }
+}
+template <int STEP> __device__ __forceinline__ float xchg(float v) { return __int_as_float(xchg<STEP>(__float_as_int(v))); }
+
+template <int N, class T> __device__ __forceinline__ T group_sum(T v)
+{
+    v += xchg<1>(v);
+    v += xchg<2>(v);
+    if constexpr (N > 4) v += xchg<4>(v);
+    if constexpr (N > 8) v += xchg<8>(v);
+    if constexpr (N > 16) v += xchg<16>(v);
+    if constexpr (N > 32) v += xchg<32>(v);
     return v;
 }
+
+template <int N> __device__ __forceinline__ float group_max(float v)
+{
+    v = fmaxf(v, xchg<1>(v));
+    v = fmaxf(v, xchg<2>(v));
+    if constexpr (N > 4) v = fmaxf(v, xchg<4>(v));
+    if constexpr (N > 8) v = fmaxf(v, xchg<8>(v));
+    if constexpr (N > 16) v = fmaxf(v, xchg<16>(v));
+    if constexpr (N > 32) v = fmaxf(v, xchg<32>(v));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 __device__ __forceinline__ uint32_t comp(const uint4 &v, int i)
 {
@@ -120,33 +164,19 @@ struct Enc {
 
 __device__ __forceinline__ void encode32(float v, int r, const Enc &e, int vec, int K, int pos0)
 {
-    float a = fabsf(v), sm = v;
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) {
-        a = fmaxf(a, __shfl_xor(a, o, 32));
-        sm += __shfl_xor(sm, o, 32);
-    }
+    const float a = group_max<32>(fabsf(v));
+    const float sm = group_sum<32>(v);
     const float inv = a > 0.f ? 127.0f / a : 0.f;
     const float r0 = v * inv, f0 = rintf(r0);
     const float r1 = (r0 - f0) * 254.0f, f1 = rintf(r1);
     const float r2 = (r1 - f1) * 254.0f, f2 = rintf(r2);
     const int i0 = (int)f0, i1 = (int)f1, i2 = (int)f2;
     const int sh = 8 * (r & 3);
-    int w0 = (int)((uint32_t)(i0 & 0xff) << sh), w1 = (int)((uint32_t)(i1 & 0xff) << sh),
-        w2 = (int)((uint32_t)(i2 & 0xff) << sh);
-    int s0 = i0, s1 = i1, s2 = i2;
-#pragma unroll
-    for (int o = 1; o < 4; o <<= 1) {  // bytes are disjoint: add == or
-        w0 += __shfl_xor(w0, o, 32);
-        w1 += __shfl_xor(w1, o, 32);
-        w2 += __shfl_xor(w2, o, 32);
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-        s0 += __shfl_xor(s0, o, 32);
-        s1 += __shfl_xor(s1, o, 32);
-        s2 += __shfl_xor(s2, o, 32);
-    }
+    // bytes of 4 lanes are disjoint, so their sum is their concatenation
+    const int w0 = group_sum<4>((int)((uint32_t)(i0 & 0xff) << sh));
+    const int w1 = group_sum<4>((int)((uint32_t)(i1 & 0xff) << sh));
+    const int w2 = group_sum<4>((int)((uint32_t)(i2 & 0xff) << sh));
+    const int s0 = group_sum<16>(i0), s1 = group_sum<16>(i1), s2 = group_sum<16>(i2);
     const size_t qb = (size_t)vec * kPieces * K + pos0 + r;
     if ((r & 3) == 0) {
         *(int *)(e.q + qb) = w0;
@@ -185,77 +215,157 @@ __device__ void zero_blocks(const Enc &e, int vec, int K, int b0, int b1, int ti
 // pairs, run by one workgroup.  Routed pairs of expert e come first in
 // ascending e, each expert's pairs by ascending token; shared expert s is
 // pseudo-expert E+s with one pair per token.  Ids outside [0, E) are dropped.
+struct WorkEntry {
+    int e, p0, p1, pad;   // expert (E+s for shared s), grouped pairs [p0, p1)
+    const void *ptr;      // expert's slot address, or null: read it from the pointer table
+    const void *pad2;
+};
+
 struct GroupOut {
-    int *nuniq;    // distinct experts (workspace)
-    int4 *wt;      // [Umax] {expert, first pair, end pair, 0}; empty past nuniq
+    int *nuniq;           // distinct experts (workspace)
+    WorkEntry *wt;        // [Umax]; entries past nuniq are empty (p0 == p1)
     int Umax;
-    int *ptok;     // [P] token of each grouped pair
-    int *inv;      // [T][k+ns] grouped position of (t, j), -1 if dropped
+    int *ptok;            // [P] token of each grouped pair
+    int *inv;             // [T][k+ns] grouped position of (t, j), -1 if dropped
+    const void *const *eptr, *const *sptr;  // pointer tables to resolve, or null
     int *count, *offset, *pairs;  // moe_group_tokens outputs (may be null)
 };
 
-__device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupOut g, int *lstart /* LDS [E+ns] */)
+// Branch-free counting formulation over the P = T*k routed pairs q (in
+// (token, slot) order; ids are distinct within a token, so that is also
+// (token) order per expert):
+//   count(e)  = #{q : e_q == e},   below(e) = #{q : e_q < e},
+//   rank(p)   = #{q < p : e_q == e_p}       (stable position inside e_p)
+//   pos(p)    = below(e_p) + rank(p)
+//   u(p)      = #{q : e_q < e_p and rank(q) == 0}   (distinct-expert index)
+// Shared expert s follows as pseudo-expert E+s with pair T*k + s*T + t.
+__device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupOut g, int *lrank /* LDS [T*k] */)
 {
-    const int ne = E + ns;
-    for (int e = threadIdx.x; e < ne; e += blockDim.x) lstart[e] = e < E ? 0 : T;
-    __syncthreads();
-    for (int p = threadIdx.x; p < T * k; p += blockDim.x)
-        if ((unsigned)sidx[p] < (unsigned)E) atomicAdd(&lstart[sidx[p]], 1);
-    __syncthreads();
-    // exclusive scan of counts and compaction of non-empty experts (wave 0)
-    if (threadIdx.x < 64) {
-        const int lane = lane_id();
-        int run = 0, nu = 0;
-        for (int base = 0; base < ne; base += 64) {
-            const int e = base + lane;
-            const int c = e < ne ? lstart[e] : 0;
-            int x = c, f = c > 0 ? 1 : 0;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o, 64);
-                const int z = __shfl_up(f, o, 64);
-                if (lane >= o) { x += y; f += z; }
-            }
-            const int excl = run + x - c;
-            const int uidx = nu + f - (c > 0 ? 1 : 0);
-            if (e < ne) {
-                if (g.count && e < E) g.count[e] = c;
-                if (g.offset && e < E) g.offset[e] = excl;
-                if (c > 0 && g.wt) g.wt[uidx] = make_int4(e, excl, excl + c, 0);
-                lstart[e] = excl;
-            }
-            run += __shfl(x, 63, 64);
-            nu += __shfl(f, 63, 64);
-        }
-        if (g.offset && lane == 0) g.offset[E] = run - T * ns;
-        if (g.wt) {
-            for (int u = nu + lane; u < g.Umax; u += 64) g.wt[u] = make_int4(0, 0, 0, 0);
-            if (lane == 0) *g.nuniq = nu;
-        }
+    const int P = T * k;
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const int ep = sidx[p];
+        int rank = 0;
+        for (int q = 0; q < p; q++) rank += sidx[q] == ep;
+        lrank[p] = (unsigned)ep < (unsigned)E ? rank : -1;
     }
     __syncthreads();
-    const int kk = k + ns;
-    for (int p = threadIdx.x; p < T * kk; p += blockDim.x) {
-        const int t = p / kk, j = p - t * kk;
-        int pos;
-        if (j < k) {
-            const int e = sidx[t * k + j];
-            if ((unsigned)e >= (unsigned)E) {
-                if (g.inv) g.inv[p] = -1;
-                continue;
-            }
-            int rank = 0;
-            for (int t2 = 0; t2 < t; t2++)
-                for (int j2 = 0; j2 < k; j2++) rank += sidx[t2 * k + j2] == e;
-            pos = lstart[e] + rank;
-            if (g.pairs) g.pairs[pos] = t * k + j;
-        } else {
-            pos = lstart[E + (j - k)] + t;
+    int nu_local = 0;
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const int ep = sidx[p];
+        const int t = p / k, j = p - t * k;
+        if ((unsigned)ep >= (unsigned)E) {
+            if (g.inv) g.inv[t * (k + ns) + j] = -1;
+            continue;
         }
+        int below = 0, cnt = 0, ubelow = 0;
+        for (int q = 0; q < P; q++) {
+            const int eq = sidx[q];
+            const bool valid = (unsigned)eq < (unsigned)E;
+            below += valid && eq < ep;
+            cnt += eq == ep;
+            ubelow += valid && eq < ep && lrank[q] == 0;
+        }
+        const int pos = below + lrank[p];
+        if (g.pairs) g.pairs[pos] = p;
         if (g.ptok) {
             g.ptok[pos] = t;
-            g.inv[p] = pos;
+            g.inv[t * (k + ns) + j] = pos;
         }
+        if (lrank[p] == 0) {
+            nu_local++;
+            if (g.count) g.count[ep] = cnt;
+            if (g.wt) {
+                WorkEntry we;
+                we.e = ep; we.p0 = below; we.p1 = below + cnt; we.pad = 0; we.pad2 = nullptr;
+                we.ptr = g.eptr ? g.eptr[ep] : nullptr;
+                g.wt[ubelow] = we;
+            }
+        }
+    }
+    // number of distinct routed experts, and the API's per-expert arrays
+    __shared__ int s_nu, s_valid;
+    if (threadIdx.x == 0) { s_nu = 0; s_valid = 0; }
+    __syncthreads();
+    if (nu_local) atomicAdd(&s_nu, nu_local);
+    for (int p = threadIdx.x; p < P; p += blockDim.x)
+        if (lrank[p] >= 0) atomicAdd(&s_valid, 1);
+    __syncthreads();
+    const int nu = s_nu, nvalid = s_valid;
+    if (g.count || g.offset) {
+        for (int e = threadIdx.x; e < E; e += blockDim.x) {
+            int below = 0, cnt = 0;
+            for (int q = 0; q < P; q++) {
+                const int eq = sidx[q];
+                below += (unsigned)eq < (unsigned)e;
+                cnt += eq == e;
+            }
+            if (g.count && cnt == 0) g.count[e] = 0;
+            if (g.offset) g.offset[e] = below;
+        }
+        if (g.offset && threadIdx.x == 0) g.offset[E] = nvalid;
+    }
+    if (g.wt) {
+        for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x) {
+            WorkEntry we;
+            we.e = E + s2; we.p0 = nvalid + s2 * T; we.p1 = nvalid + (s2 + 1) * T; we.pad = 0; we.pad2 = nullptr;
+            we.ptr = g.eptr ? g.sptr[s2] : nullptr;
+            g.wt[nu + s2] = we;
+        }
+        for (int u = nu + ns + threadIdx.x; u < g.Umax; u += blockDim.x) g.wt[u] = WorkEntry{0, 0, 0, 0, nullptr, nullptr};
+        if (threadIdx.x == 0) *g.nuniq = nu + ns;
+    }
+    if (g.ptok) {
+        for (int i = threadIdx.x; i < ns * T; i += blockDim.x) {
+            const int s2 = i / T, t = i - s2 * T;
+            const int pos = nvalid + s2 * T + t;
+            g.ptok[pos] = t;
+            g.inv[t * (k + ns) + k + s2] = pos;
+        }
+    }
+}
+
+// Top-k of one token by one wave.  Each candidate is a 64-bit key: the
+// logit's bits mapped to an unsigned order (high word) and the inverted
+// expert id (low word), so the unsigned maximum is the largest logit and,
+// among equal logits, the lowest id.  Lane j receives the j-th selection.
+__device__ __forceinline__ uint32_t ord_bits(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_bits(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+template <int S> __device__ __forceinline__ uint64_t max_step(uint64_t b)
+{
+    const uint32_t hi = xchg<S>((int)(uint32_t)(b >> 32));
+    const uint32_t lo = xchg<S>((int)(uint32_t)b);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > b ? o : b;
+}
+
+template <int NVL>
+__device__ __forceinline__ void topk_wave(const float *lg, int E, int k, float *mine, int *myid, float *top)
+{
+    const int lane = lane_id();
+    uint64_t key[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; i++) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? ((uint64_t)ord_bits(ld_coh(lg + e)) << 32) | (uint32_t)~e : 0ull;
+    }
+    for (int j = 0; j < k; j++) {
+        uint64_t b = key[0];
+#pragma unroll
+        for (int i = 1; i < NVL; i++) b = key[i] > b ? key[i] : b;
+        b = max_step<1>(b); b = max_step<2>(b); b = max_step<4>(b);
+        b = max_step<8>(b); b = max_step<16>(b); b = max_step<32>(b);
+#pragma unroll
+        for (int i = 0; i < NVL; i++) key[i] = key[i] == b ? 0ull : key[i];
+        const float v = unord_bits((uint32_t)(b >> 32));
+        if (j == 0) *top = v;
+        if (lane == j) { *mine = v; *myid = (int)~(uint32_t)b; }
     }
 }
 
@@ -276,7 +386,6 @@ struct RouteArgs {
     int *idx2;              // optional copies
     float *w2;
     float *logits2;
-    int encode;             // encode normalised h for the matvecs
     Enc x;                  // [T] vectors of H
     int group;
     int ns;
@@ -284,71 +393,84 @@ struct RouteArgs {
     Enc hpad;               // [P] vectors of kd: padding blocks zeroed here
     int P, I, kd;
     unsigned *counter;
-    int n_expert_blocks;
+    int n_expert_blocks;    // router workgroups; the rest encode (T * H/256)
 };
 
+// Router workgroup: 4 router rows, one per wave, against all T tokens.
+// Encoding workgroup (t, c): RMS of token t, then positions [256c, 256c+256).
+// The last router workgroup to finish does top-k and grouping.
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
 {
-    __shared__ float red[16];
+    __shared__ float red[8];
     __shared__ int sidx[kMaxT * kMaxK];
     __shared__ float sw[kMaxT * kMaxK];
-    __shared__ int lstart[kMaxE + kMaxShared];
+    __shared__ int lstart[kMaxT * kMaxK];
     __shared__ int flag;
 
     const int H = a.H, T = a.T, E = a.E;
     const int blk = blockIdx.x;
     const int lane = lane_id();
+    const int nv = H >> 8;  // float4 per lane per row
     if (blk >= a.n_expert_blocks) {
-        // encode token t and zero the padding blocks of some pairs' h encodings
-        const int t = blk - a.n_expert_blocks;
-        const float *ht = a.h + (size_t)t * H;
+        const int g = blk - a.n_expert_blocks;
+        const int t = g / nv, c = g - t * nv;
+        const float4 *hr = (const float4 *)(a.h + (size_t)t * H);
         float ss = 0.f;
-        for (int i = threadIdx.x; i < H; i += blockDim.x) ss += ht[i] * ht[i];
-        ss = block_sum(ss, red);
+        for (int i = threadIdx.x; i < H / 4; i += blockDim.x) {
+            const float4 v = hr[i];
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave_id()] = ss;
+        __syncthreads();
+        ss = 0.f;
+        for (int i = 0; i < kRouteThreads / 64; i++) ss += red[i];
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
-        for (int pos = threadIdx.x; pos < H; pos += blockDim.x)
-            encode32(ht[pos] * r, threadIdx.x & 31, a.x, t, H, pos & ~31);
-        if (a.kd > a.I)
-            for (int p = t; p < a.P; p += T) zero_blocks(a.hpad, p, a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
+        const int pos = c * 256 + threadIdx.x;
+        encode32(a.h[(size_t)t * H + pos] * r, threadIdx.x & 31, a.x, t, H, pos & ~31);
+        if (a.kd > a.I) {
+            const int nenc = T * nv;
+            for (int p = g; p < a.P; p += nenc) zero_blocks(a.hpad, p, a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
+        }
         return;
     }
 
     const int e = blk * kRouteRows + wave_id();
     if (e < E) {
         const float4 *wrow = (const float4 *)(a.wr + (size_t)e * H);
-        const int nv = H >> 8;  // float4 per lane
-        for (int t0 = 0; t0 < T; t0 += kChunk) {
-            float acc[kChunk], ss[kChunk];
-#pragma unroll
-            for (int tt = 0; tt < kChunk; tt++) { acc[tt] = 0.f; ss[tt] = 0.f; }
+        const float b = a.bias ? a.bias[e] : 0.f;
+        for (int t0 = 0; t0 < T; t0 += 4) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f}, ss[4] = {0.f, 0.f, 0.f, 0.f};
             for (int i0 = 0; i0 < nv; i0 += 8) {
-                float4 wv[8];
+                // issue the router row chunk and 4 tokens' state chunks together
+                float4 wv[8], hv[4][8];
 #pragma unroll
                 for (int i = 0; i < 8; i++)
                     if (i0 + i < nv) wv[i] = wrow[(i0 + i) * 64 + lane];
 #pragma unroll
-                for (int tt = 0; tt < kChunk; tt++) {
-                    if (t0 + tt < T) {
-                        const float4 *hrow = (const float4 *)(a.h + (size_t)(t0 + tt) * H);
+                for (int tt = 0; tt < 4; tt++)
 #pragma unroll
-                        for (int i = 0; i < 8; i++) {
-                            if (i0 + i < nv) {
-                                const float4 hv = hrow[(i0 + i) * 64 + lane];
-                                acc[tt] += wv[i].x * hv.x + wv[i].y * hv.y + wv[i].z * hv.z + wv[i].w * hv.w;
-                                ss[tt] += hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
-                            }
+                    for (int i = 0; i < 8; i++)
+                        if (t0 + tt < T && i0 + i < nv)
+                            hv[tt][i] = ((const float4 *)(a.h + (size_t)(t0 + tt) * H))[(i0 + i) * 64 + lane];
+#pragma unroll
+                for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+                    for (int i = 0; i < 8; i++)
+                        if (t0 + tt < T && i0 + i < nv) {
+                            const float4 x = hv[tt][i];
+                            acc[tt] += wv[i].x * x.x + wv[i].y * x.y + wv[i].z * x.z + wv[i].w * x.w;
+                            ss[tt] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
                         }
-                    }
-                }
             }
 #pragma unroll
-            for (int tt = 0; tt < kChunk; tt++) {
+            for (int tt = 0; tt < 4; tt++) {
                 if (t0 + tt < T) {
                     const float d = wave_sum(acc[tt]);
                     const float q = wave_sum(ss[tt]);
                     if (lane == 0) {
-                        const float r = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
-                        const float lg = d * r + (a.bias ? a.bias[e] : 0.f);
+                        const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
+                        const float lg = d * rr + b;
                         st_coh(a.logits + (size_t)(t0 + tt) * E + e, lg);
                         if (a.logits2) a.logits2[(size_t)(t0 + tt) * E + e] = lg;
                     }
@@ -358,45 +480,28 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
     }
     if (!arrive(a.counter, (unsigned)a.n_expert_blocks, &flag)) return;
 
-    // last workgroup: softmax top-k of every token (one wave per token)
+    // last router workgroup: softmax top-k of every token (one wave per token)
     const int k = a.k;
     for (int t = wave_id(); t < T; t += kRouteThreads / 64) {
-        float v[kMaxE / 64];
-        uint32_t taken = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxE / 64; i++) {
-            const int ee = lane + 64 * i;
-            v[i] = ee < E ? ld_coh(a.logits + (size_t)t * E + ee) : -INFINITY;
-        }
-        float top = 0.f;
-        for (int j = 0; j < k; j++) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < kMaxE / 64; i++) {
-                const int ee = lane + 64 * i;
-                if (ee < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && ee < bi))) { bv = v[i]; bi = ee; }
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-            }
-            if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
-            if (j == 0) top = bv;
-            if (lane == 0) { sidx[t * k + j] = bi; sw[t * k + j] = bv; }
-        }
-        float s = 0.f;
-        for (int j = lane; j < k; j += 64) s += expf(sw[t * k + j] - top);
-        s = wave_sum(s);
-        for (int j = lane; j < k; j += 64) {
-            const float wj = expf(sw[t * k + j] - top) / s;
-            const int id = sidx[t * k + j];
-            a.idx[t * k + j] = id;
-            a.w[t * k + j] = wj;
-            if (a.idx2) a.idx2[t * k + j] = id;
-            if (a.w2) a.w2[t * k + j] = wj;
+        float top = 0.f, mine = 0.f;
+        int myid = 0;
+        const float *lg = a.logits + (size_t)t * E;
+        if (E <= 64) topk_wave<1>(lg, E, k, &mine, &myid, &top);
+        else if (E <= 128) topk_wave<2>(lg, E, k, &mine, &myid, &top);
+        else if (E <= 256) topk_wave<4>(lg, E, k, &mine, &myid, &top);
+        else if (E <= 512) topk_wave<8>(lg, E, k, &mine, &myid, &top);
+        else topk_wave<16>(lg, E, k, &mine, &myid, &top);
+        // softmax over the k selected logits, lane j holding selection j
+        const float ex = lane < k ? expf(mine - top) : 0.f;
+        const float s = wave_sum(ex);
+        if (lane < k) {
+            const float wj = ex / s;
+            sidx[t * k + lane] = myid;
+            sw[t * k + lane] = wj;
+            a.idx[t * k + lane] = myid;
+            a.w[t * k + lane] = wj;
+            if (a.idx2) a.idx2[t * k + lane] = myid;
+            if (a.w2) a.w2[t * k + lane] = wj;
         }
     }
     __syncthreads();
@@ -419,7 +524,7 @@ struct PrepArgs {
 __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
 {
     __shared__ int sidx[kMaxT * kMaxK];
-    __shared__ int lstart[kMaxE + kMaxShared];
+    __shared__ int lstart[kMaxT * kMaxK];
     const int t = blockIdx.x;
     for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x)
         encode32(a.x[(size_t)t * a.H + pos], threadIdx.x & 31, a.xe, t, a.H, pos & ~31);
@@ -435,7 +540,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
 __global__ __launch_bounds__(kRouteThreads) void k_group(const int *idx, int T, int k, int E, GroupOut go)
 {
     __shared__ int sidx[kMaxT * kMaxK];
-    __shared__ int lstart[kMaxE + kMaxShared];
+    __shared__ int lstart[kMaxT * kMaxK];
     for (int p = threadIdx.x; p < T * k; p += blockDim.x) sidx[p] = idx[p];
     __syncthreads();
     group_block(sidx, T, k, E, 0, go, lstart);
@@ -638,7 +743,7 @@ struct GateUpArgs {
     const void *const *eptr;
     const void *const *sptr;
     int E;
-    const int4 *wt;
+    const WorkEntry *wt;
     const int *ptok;
     Enc x;            // token encodings, K = H
     int H, I, kd;
@@ -658,10 +763,10 @@ __global__ __launch_bounds__(kGUThreads) void k_gate_up(GateUpArgs a)
 
     const int u = blockIdx.x / a.ntile;
     const int rt = blockIdx.x - u * a.ntile;
-    const int4 wt = a.wt[u];
-    const int e = wt.x, p0 = wt.y, p1 = wt.z;
+    const WorkEntry we = a.wt[u];
+    const int e = we.e, p0 = we.p0, p1 = we.p1;
     if (p0 >= p1) return;
-    const uint8_t *base = (const uint8_t *)(e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
+    const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
     const int H = a.H, S = H >> 8;
     const int wv = wave_id(), lane = lane_id();
     const int row = rt * 32 + (lane & 31);
@@ -713,7 +818,7 @@ struct DownArgs {
     const void *const *sptr;
     int E;
     const int *nuniq;
-    const int4 *wt;
+    const WorkEntry *wt;
     Enc h;           // pair encodings, K = kd
     int H, kd;
     unsigned long long down_off;
@@ -731,15 +836,18 @@ template <int QT>
 __global__ __launch_bounds__(512) void k_down(DownArgs a)
 {
     __shared__ float part[8][kChunk][64];
+    __shared__ int sinv[kMaxT * (kMaxK + kMaxShared)];
+    __shared__ float swt[kMaxT * kMaxK];
     __shared__ int flag;
 
     const int u = blockIdx.x / a.nrt;
     const int rt = blockIdx.x - u * a.nrt;
-    const int4 wt = a.wt[u];
-    const int e = wt.x, p0 = wt.y, p1 = wt.z;
+    const WorkEntry we = a.wt[u];
+    const int e = we.e, p0 = we.p0, p1 = we.p1;
     if (p0 >= p1) return;
     const int nu = *a.nuniq;
-    const uint8_t *base = (const uint8_t *)(e < a.E ? a.eptr[e] : a.sptr[e - a.E]) + a.down_off;
+    const uint8_t *base =
+        (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]) + a.down_off;
     const int kd = a.kd, S = kd >> 8;
     const int nwv = (int)(blockDim.x >> 6);
     const int wv = wave_id(), lane = lane_id();
@@ -766,17 +874,21 @@ __global__ __launch_bounds__(512) void k_down(DownArgs a)
         __syncthreads();
     }
 
-    if (!arrive(&a.cnt[rt], (unsigned)nu, &flag)) return;
+    // routing of every token, staged before the arrival so that the last
+    // workgroup only waits for the hand-over loads
     const int kk = a.k + a.ns;
+    for (int i = threadIdx.x; i < a.T * kk; i += blockDim.x) sinv[i] = a.inv[i];
+    for (int i = threadIdx.x; i < a.T * a.k; i += blockDim.x) swt[i] = a.w[i];
+    if (!arrive(&a.cnt[rt], (unsigned)nu, &flag)) return;
     for (int i = threadIdx.x; i < a.T * 64; i += blockDim.x) {
         const int t = i >> 6, ln = i & 63;
         const size_t row = (size_t)rt * 64 + ln;
         float acc = a.accumulate ? a.y[(size_t)t * a.H + row] : 0.f;
         for (int j = 0; j < a.k; j++) {
-            const int pj = a.inv[t * kk + j];
-            if (pj >= 0) acc += a.w[t * a.k + j] * ld_coh(a.osc + (size_t)pj * a.H + row);
+            const int pj = sinv[t * kk + j];
+            if (pj >= 0) acc += swt[t * a.k + j] * ld_coh(a.osc + (size_t)pj * a.H + row);
         }
-        for (int s = 0; s < a.ns; s++) acc += ld_coh(a.osc + (size_t)a.inv[t * kk + a.k + s] * a.H + row);
+        for (int s = 0; s < a.ns; s++) acc += ld_coh(a.osc + (size_t)sinv[t * kk + a.k + s] * a.H + row);
         a.y[(size_t)t * a.H + row] = acc;
     }
 }
@@ -818,7 +930,7 @@ struct Ws {
     {
         GroupOut g{};
         g.nuniq = at<int>(L.nuniq);
-        g.wt = at<int4>(L.wt);
+        g.wt = at<WorkEntry>(L.wt);
         g.Umax = L.U;
         g.ptok = at<int>(L.ptok);
         g.inv = at<int>(L.inv);
@@ -869,7 +981,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
-    ga.wt = ws.at<int4>(L.wt); ga.ptok = ws.at<int>(L.ptok);
+    ga.wt = ws.at<WorkEntry>(L.wt); ga.ptok = ws.at<int>(L.ptok);
     ga.x = ws.x();
     ga.H = d.H; ga.I = d.I; ga.kd = g.kd; ga.up_off = g.up_off;
     ga.h = ws.h();
@@ -995,13 +1107,15 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     PrepArgs pa{};
     pa.x = x; pa.T = T; pa.H = d->H; pa.k = k; pa.E = E; pa.ns = n_shared; pa.idx = idx;
     pa.xe = W.x(); pa.go = W.group(); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
+    pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
     return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, w, y, accumulate, act_out, s);
 }
 
 moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, const float *w_router,
-                           const float *bias, int32_t E, int32_t k, int32_t n_shared, float eps, int32_t *idx_out,
+                           const float *bias, int32_t E, int32_t k, const void *const *expert_ptrs,
+                           const void *const *shared_ptrs, int32_t n_shared, float eps, int32_t *idx_out,
                            float *w_out, void *ws, size_t ws_bytes, hipStream_t s)
 {
     ExpertGeom g;
@@ -1009,18 +1123,20 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     if (st != MOE_OK) return st;
     if ((st = check_tke(T, k, E, n_shared)) != MOE_OK) return st;
     if (!h || !w_router) { set_error("moe_layer_route: null pointer"); return MOE_ERR_ARG; }
+    if (expert_ptrs && n_shared > 0 && !shared_ptrs) { set_error("moe_layer_route: shared_ptrs missing"); return MOE_ERR_ARG; }
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
     RouteArgs a{};
     a.h = h; a.T = T; a.H = d->H; a.wr = w_router; a.bias = bias; a.E = E; a.k = k; a.eps = eps; a.normalize = 1;
     a.logits = W.at<float>(W.L.logits); a.idx = W.at<int>(W.L.idx); a.w = W.at<float>(W.L.w);
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
-    a.encode = 1; a.x = W.x();
+    a.x = W.x();
     a.group = 1; a.ns = n_shared; a.go = W.group();
+    a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
     a.counter = W.at<unsigned>(W.L.cnt_route);
     a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows;
-    k_route<<<a.n_expert_blocks + T, kRouteThreads, 0, s>>>(a);
+    k_route<<<a.n_expert_blocks + T * (d->H / kEncThreads), kRouteThreads, 0, s>>>(a);
     LAUNCH_OK("k_route");
     return MOE_OK;
 }
@@ -1046,7 +1162,8 @@ moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, cons
                              hipStream_t s)
 {
     if (!expert_ptrs || (n_shared > 0 && !shared_ptrs)) { set_error("moe_layer_forward: null pointer"); return MOE_ERR_ARG; }
-    moe_status st = moe_layer_route(d, h, T, w_router, bias, E, k, n_shared, eps, idx_out, w_out, ws, ws_bytes, s);
+    moe_status st = moe_layer_route(d, h, T, w_router, bias, E, k, expert_ptrs, shared_ptrs, n_shared, eps, idx_out,
+                                    w_out, ws, ws_bytes, s);
     if (st != MOE_OK) return st;
     return moe_layer_ffn(d, h, T, E, k, expert_ptrs, shared_ptrs, n_shared, ws, ws_bytes, s);
 }
