@@ -26,7 +26,7 @@ constexpr int kTileCols = 256;
 constexpr int kMaxT = 32;
 constexpr int kMaxE = 1024;
 constexpr int kMaxShared = 8;
-constexpr int kMaxH = 16384;
+constexpr int kMaxH = 8192;
 constexpr int kPieces = 3;  // activations are encoded as 3 int8 pieces
 
 inline int tile_bytes(int qtype)
@@ -83,14 +83,15 @@ constexpr size_t kCntBytes = (kCntDn + 4 * (kMaxH / 64) + 255) & ~(size_t)255;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
-// Activations are stored encoded: per vector of K positions, pieces q[3][K]
-// (int8, piece-major), per-32-position block scales bs[K/32] and exact fp32
-// block sums bsum[K/32], and per-16-position integer sums of each piece
-// ps[3][K/16].
+// Activations are stored encoded, one contiguous record of 4K bytes per
+// vector of K positions: pieces q[3][K] (int8, piece-major), per-32-position
+// block scales bs[K/32] and exact fp32 block sums bsum[K/32] (float), and
+// per-16-position integer sums of each piece ps[3][K/16] (int32).
+constexpr size_t enc_bytes(int K) { return (size_t)4 * K; }
+
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U;
-    size_t xq, xbs, xbsum, xps, logits, idx, w, nuniq, wt, ptok, inv,
-        hq, hbs, hbsum, hps, osc, cnt_route, cnt_dn, total;
+    size_t xenc, logits, idx, w, nuniq, wt, ptok, inv, henc, osc, cnt_route, cnt_dn, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -104,10 +105,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.U = ur + ns;
     size_t o = kCntBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-    L.xq = take((size_t)T * kPieces * d.H);
-    L.xbs = take((size_t)T * (d.H / 32) * 4);
-    L.xbsum = take((size_t)T * (d.H / 32) * 4);
-    L.xps = take((size_t)T * kPieces * (d.H / 16) * 4);
+    L.xenc = take((size_t)T * enc_bytes(d.H));
     L.logits = take((size_t)T * E * 4);
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
@@ -115,10 +113,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.wt = take((size_t)L.U * 32);
     L.ptok = take((size_t)L.P * 4);
     L.inv = take((size_t)L.P * 4);
-    L.hq = take((size_t)L.P * kPieces * L.kd);
-    L.hbs = take((size_t)L.P * (L.kd / 32) * 4);
-    L.hbsum = take((size_t)L.P * (L.kd / 32) * 4);
-    L.hps = take((size_t)L.P * kPieces * (L.kd / 16) * 4);
+    L.henc = take((size_t)L.P * enc_bytes(L.kd));
     L.osc = take((size_t)L.P * d.H * 4);
     L.cnt_route = kCntRoute;
     L.cnt_dn = kCntDn;

@@ -109,6 +109,20 @@ template <int N> __device__ __forceinline__ float group_max(float v)
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
+// inside 16-lane rows (row_shr 1, 2, 4, 8), then the row totals carried
+// across rows with row_bcast:15 and row_bcast:31.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 __device__ __forceinline__ uint32_t comp(const uint4 &v, int i)
 {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -153,16 +167,20 @@ __device__ float block_sum(float v, float *red)
 }
 
 // ---------------------------------------------------------------------------
-// Activation encoding of one 32-value block held by 32 consecutive lanes
-// (lane r of the group holds position pos0 + r of a vector of K positions).
+// Encoded activation records, one per vector of K positions (4K bytes):
+//   [0, 3K)          pieces q[3][K], int8, piece-major
+//   [3K, 3K+K/8)     block scales bs[K/32], fp32
+//   [3K+K/8, 3K+K/4) exact block sums bsum[K/32], fp32
+//   [3K+K/4, 4K)     per-16 sums of each piece ps[3][K/16], int32
 struct Enc {
-    int8_t *q;     // [n][3][K]
-    float *bs;     // [n][K/32]
-    float *bsum;   // [n][K/32]
-    int *ps;       // [n][3][K/16]
+    uint8_t *base;  // records back to back
 };
 
-__device__ __forceinline__ void encode32(float v, int r, const Enc &e, int vec, int K, int pos0)
+__device__ __forceinline__ uint8_t *rec_at(const Enc &e, int vec, int K) { return e.base + (size_t)vec * 4 * K; }
+
+// Encode one 32-value block held by 32 consecutive lanes (lane r of the
+// group holds position pos0 + r) into record `rec`.
+__device__ __forceinline__ void encode32(float v, int r, uint8_t *rec, int K, int pos0)
 {
     const float a = group_max<32>(fabsf(v));
     const float sm = group_sum<32>(v);
@@ -177,36 +195,38 @@ __device__ __forceinline__ void encode32(float v, int r, const Enc &e, int vec, 
     const int w1 = group_sum<4>((int)((uint32_t)(i1 & 0xff) << sh));
     const int w2 = group_sum<4>((int)((uint32_t)(i2 & 0xff) << sh));
     const int s0 = group_sum<16>(i0), s1 = group_sum<16>(i1), s2 = group_sum<16>(i2);
-    const size_t qb = (size_t)vec * kPieces * K + pos0 + r;
     if ((r & 3) == 0) {
-        *(int *)(e.q + qb) = w0;
-        *(int *)(e.q + qb + K) = w1;
-        *(int *)(e.q + qb + 2 * (size_t)K) = w2;
+        *(int *)(rec + pos0 + r) = w0;
+        *(int *)(rec + K + pos0 + r) = w1;
+        *(int *)(rec + 2 * K + pos0 + r) = w2;
     }
     if ((r & 15) == 0) {
-        const size_t pb = (size_t)vec * kPieces * (K / 16) + (pos0 + r) / 16;
-        e.ps[pb] = s0;
-        e.ps[pb + K / 16] = s1;
-        e.ps[pb + 2 * (K / 16)] = s2;
+        int *ps = (int *)(rec + 3 * K + K / 4) + (pos0 + r) / 16;
+        ps[0] = s0;
+        ps[K / 16] = s1;
+        ps[K / 8] = s2;
     }
     if (r == 0) {
-        e.bs[(size_t)vec * (K / 32) + pos0 / 32] = a / 127.0f;
-        e.bsum[(size_t)vec * (K / 32) + pos0 / 32] = sm;
+        float *bs = (float *)(rec + 3 * K);
+        bs[pos0 / 32] = a / 127.0f;
+        bs[K / 32 + pos0 / 32] = sm;
     }
 }
 
-// Zero blocks [b0, b1) of vector `vec` (padding columns of the down rows).
-__device__ void zero_blocks(const Enc &e, int vec, int K, int b0, int b1, int tid, int nthr)
+// Zero blocks [b0, b1) of a record (padding columns of the down rows).
+__device__ void zero_blocks(uint8_t *rec, int K, int b0, int b1, int tid, int nthr)
 {
     for (int b = b0 + tid; b < b1; b += nthr) {
+        float *bs = (float *)(rec + 3 * K);
+        int *ps = (int *)(rec + 3 * K + K / 4);
         for (int p = 0; p < kPieces; p++) {
-            int *q = (int *)(e.q + (size_t)vec * kPieces * K + (size_t)p * K + 32 * b);
+            int *q = (int *)(rec + (size_t)p * K + 32 * b);
             for (int i = 0; i < 8; i++) q[i] = 0;
-            e.ps[(size_t)vec * kPieces * (K / 16) + (size_t)p * (K / 16) + 2 * b] = 0;
-            e.ps[(size_t)vec * kPieces * (K / 16) + (size_t)p * (K / 16) + 2 * b + 1] = 0;
+            ps[p * (K / 16) + 2 * b] = 0;
+            ps[p * (K / 16) + 2 * b + 1] = 0;
         }
-        e.bs[(size_t)vec * (K / 32) + b] = 0.f;
-        e.bsum[(size_t)vec * (K / 32) + b] = 0.f;
+        bs[b] = 0.f;
+        bs[K / 32 + b] = 0.f;
     }
 }
 
@@ -215,10 +235,11 @@ __device__ void zero_blocks(const Enc &e, int vec, int K, int b0, int b1, int ti
 // pairs, run by one workgroup.  Routed pairs of expert e come first in
 // ascending e, each expert's pairs by ascending token; shared expert s is
 // pseudo-expert E+s with one pair per token.  Ids outside [0, E) are dropped.
+constexpr int kInlineTok = 8;
 struct WorkEntry {
-    int e, p0, p1, pad;   // expert (E+s for shared s), grouped pairs [p0, p1)
-    const void *ptr;      // expert's slot address, or null: read it from the pointer table
-    const void *pad2;
+    int e, p0, p1, pad;          // expert (E+s for shared s), grouped pairs [p0, p1)
+    const void *ptr;             // expert's slot address, or null: read it from the pointer table
+    uint8_t tok[kInlineTok];     // tokens of the first kInlineTok pairs
 };
 
 struct GroupOut {
@@ -231,25 +252,70 @@ struct GroupOut {
     int *count, *offset, *pairs;  // moe_group_tokens outputs (may be null)
 };
 
-// Branch-free counting formulation over the P = T*k routed pairs q (in
-// (token, slot) order; ids are distinct within a token, so that is also
-// (token) order per expert):
-//   count(e)  = #{q : e_q == e},   below(e) = #{q : e_q < e},
-//   rank(p)   = #{q < p : e_q == e_p}       (stable position inside e_p)
-//   pos(p)    = below(e_p) + rank(p)
-//   u(p)      = #{q : e_q < e_p and rank(q) == 0}   (distinct-expert index)
-// Shared expert s follows as pseudo-expert E+s with pair T*k + s*T + t.
-__device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupOut g, int *lrank /* LDS [T*k] */)
+// Expert-table entries lane and 64 + lane, which the router's wave 0 loads
+// before the top-k so that the grouping does not wait on them.
+struct PrePtr { const void *p0, *p1; bool valid; };
+
+// Grouping by token masks.  Ids are distinct within a token, so an expert
+// is chosen at most once per token and its pairs, in (token, slot) order,
+// are described by a T-bit mask (T <= 32) of the tokens that chose it:
+//   count(e) = popc(mask_e),  rank of token t's pair = popc(mask_e & ((1<<t)-1)),
+//   offset(e) = sum of counts of experts below e (wave scan),
+//   distinct-expert index = number of non-empty experts below e (wave scan).
+// Shared expert s follows as pseudo-expert E+s with pair nvalid + s*T + t.
+// A token that names one expert in two slots gets one pair, which both slots
+// point at (its output then carries the sum of their weights).
+// `lmask` is LDS of at least E ints; wave 0 scans.
+__device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupOut g, int *lmask,
+                            PrePtr pre /* this lane's table entries lane and 64 + lane, if valid */)
 {
+    __shared__ int s_nu, s_valid;
     const int P = T * k;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) lmask[e] = 0;
+    __syncthreads();
     for (int p = threadIdx.x; p < P; p += blockDim.x) {
         const int ep = sidx[p];
-        int rank = 0;
-        for (int q = 0; q < p; q++) rank += sidx[q] == ep;
-        lrank[p] = (unsigned)ep < (unsigned)E ? rank : -1;
+        if ((unsigned)ep < (unsigned)E) atomicOr((unsigned *)&lmask[ep], 1u << (p / k));
     }
     __syncthreads();
-    int nu_local = 0;
+    if (threadIdx.x < 64) {
+        const int lane = lane_id();
+        int run = 0, nu = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + lane;
+            const uint32_t m = e < E ? (uint32_t)lmask[e] : 0u;
+            const int cnt = __popc(m);
+            const int incl = wave_incl_scan(cnt);
+            const int uincl = wave_incl_scan(cnt > 0);
+            const int off = run + incl - cnt;
+            const int ui = nu + uincl - (cnt > 0);
+            if (g.count && e < E) g.count[e] = cnt;
+            if (g.offset && e < E) g.offset[e] = off;
+            if (cnt > 0 && g.wt) {
+                WorkEntry we{};
+                we.e = e; we.p0 = off; we.p1 = off + cnt;
+                we.ptr = !g.eptr                     ? nullptr
+                         : (pre.valid && base == 0)  ? pre.p0
+                         : (pre.valid && base == 64) ? pre.p1
+                                                     : g.eptr[e];
+                uint64_t toks = 0;
+                uint32_t mm = m;
+                for (int i = 0; i < kInlineTok && mm; i++) {
+                    const int t = __ffs(mm) - 1;
+                    toks |= (uint64_t)t << (8 * i);
+                    mm &= mm - 1;
+                }
+                __builtin_memcpy(we.tok, &toks, sizeof(toks));
+                g.wt[ui] = we;
+            }
+            run += __shfl(incl, 63, 64);
+            nu += __shfl(uincl, 63, 64);
+            if (e < E) lmask[E + e] = off;
+        }
+        if (lane == 0) { s_nu = nu; s_valid = run; }
+    }
+    __syncthreads();
+    const int nu = s_nu, nvalid = s_valid;
     for (int p = threadIdx.x; p < P; p += blockDim.x) {
         const int ep = sidx[p];
         const int t = p / k, j = p - t * k;
@@ -257,61 +323,23 @@ __device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupO
             if (g.inv) g.inv[t * (k + ns) + j] = -1;
             continue;
         }
-        int below = 0, cnt = 0, ubelow = 0;
-        for (int q = 0; q < P; q++) {
-            const int eq = sidx[q];
-            const bool valid = (unsigned)eq < (unsigned)E;
-            below += valid && eq < ep;
-            cnt += eq == ep;
-            ubelow += valid && eq < ep && lrank[q] == 0;
-        }
-        const int pos = below + lrank[p];
+        const int pos = lmask[E + ep] + __popc((uint32_t)lmask[ep] & ((1u << t) - 1u));
         if (g.pairs) g.pairs[pos] = p;
         if (g.ptok) {
             g.ptok[pos] = t;
             g.inv[t * (k + ns) + j] = pos;
         }
-        if (lrank[p] == 0) {
-            nu_local++;
-            if (g.count) g.count[ep] = cnt;
-            if (g.wt) {
-                WorkEntry we;
-                we.e = ep; we.p0 = below; we.p1 = below + cnt; we.pad = 0; we.pad2 = nullptr;
-                we.ptr = g.eptr ? g.eptr[ep] : nullptr;
-                g.wt[ubelow] = we;
-            }
-        }
     }
-    // number of distinct routed experts, and the API's per-expert arrays
-    __shared__ int s_nu, s_valid;
-    if (threadIdx.x == 0) { s_nu = 0; s_valid = 0; }
-    __syncthreads();
-    if (nu_local) atomicAdd(&s_nu, nu_local);
-    for (int p = threadIdx.x; p < P; p += blockDim.x)
-        if (lrank[p] >= 0) atomicAdd(&s_valid, 1);
-    __syncthreads();
-    const int nu = s_nu, nvalid = s_valid;
-    if (g.count || g.offset) {
-        for (int e = threadIdx.x; e < E; e += blockDim.x) {
-            int below = 0, cnt = 0;
-            for (int q = 0; q < P; q++) {
-                const int eq = sidx[q];
-                below += (unsigned)eq < (unsigned)e;
-                cnt += eq == e;
-            }
-            if (g.count && cnt == 0) g.count[e] = 0;
-            if (g.offset) g.offset[e] = below;
-        }
-        if (g.offset && threadIdx.x == 0) g.offset[E] = nvalid;
-    }
+    if (g.offset && threadIdx.x == 0) g.offset[E] = nvalid;
     if (g.wt) {
         for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x) {
-            WorkEntry we;
-            we.e = E + s2; we.p0 = nvalid + s2 * T; we.p1 = nvalid + (s2 + 1) * T; we.pad = 0; we.pad2 = nullptr;
+            WorkEntry we{};
+            we.e = E + s2; we.p0 = nvalid + s2 * T; we.p1 = nvalid + (s2 + 1) * T;
             we.ptr = g.eptr ? g.sptr[s2] : nullptr;
+            for (int i = 0; i < kInlineTok; i++) we.tok[i] = (uint8_t)i;
             g.wt[nu + s2] = we;
         }
-        for (int u = nu + ns + threadIdx.x; u < g.Umax; u += blockDim.x) g.wt[u] = WorkEntry{0, 0, 0, 0, nullptr, nullptr};
+        for (int u = nu + ns + threadIdx.x; u < g.Umax; u += blockDim.x) g.wt[u] = WorkEntry{};
         if (threadIdx.x == 0) *g.nuniq = nu + ns;
     }
     if (g.ptok) {
@@ -321,6 +349,36 @@ __device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupO
             g.ptok[pos] = t;
             g.inv[t * (k + ns) + k + s2] = pos;
         }
+    }
+}
+
+// Stable counting sort of the T*k (token, slot) pairs by expert, for the
+// stand-alone grouping entry point (which also admits repeated ids in a
+// token): pair p goes to (valid ids below idx[p]) + (earlier pairs with the
+// same id).
+__device__ void group_sort(const int *sidx, int T, int k, int E, int *count, int *offset, int *pairs)
+{
+    const int P = T * k;
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const int ep = sidx[p];
+        if ((unsigned)ep >= (unsigned)E) continue;
+        int below = 0, rank = 0;
+        for (int q = 0; q < P; q++) {
+            const int eq = sidx[q];
+            below += (unsigned)eq < (unsigned)ep;
+            rank += q < p && eq == ep;
+        }
+        pairs[below + rank] = p;
+    }
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+        int below = 0, cnt = 0;
+        for (int q = 0; q < P; q++) {
+            const int eq = sidx[q];
+            below += (unsigned)eq < (unsigned)e;
+            cnt += eq == e;
+        }
+        if (e < E) count[e] = cnt;
+        offset[e] = below;
     }
 }
 
@@ -404,7 +462,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
     __shared__ float red[8];
     __shared__ int sidx[kMaxT * kMaxK];
     __shared__ float sw[kMaxT * kMaxK];
-    __shared__ int lstart[kMaxT * kMaxK];
+    __shared__ int lstart[2 * kMaxE];
     __shared__ int flag;
 
     const int H = a.H, T = a.T, E = a.E;
@@ -427,20 +485,28 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         for (int i = 0; i < kRouteThreads / 64; i++) ss += red[i];
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
         const int pos = c * 256 + threadIdx.x;
-        encode32(a.h[(size_t)t * H + pos] * r, threadIdx.x & 31, a.x, t, H, pos & ~31);
+        encode32(a.h[(size_t)t * H + pos] * r, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
         if (a.kd > a.I) {
             const int nenc = T * nv;
-            for (int p = g; p < a.P; p += nenc) zero_blocks(a.hpad, p, a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
+            for (int p = g; p < a.P; p += nenc)
+                zero_blocks(rec_at(a.hpad, p, a.kd), a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
         }
         return;
     }
 
+    // pointer table entries lane + 64i, loaded early in case this workgroup ends last
+    PrePtr pre{nullptr, nullptr, a.go.eptr != nullptr};
+    if (a.go.eptr && wave_id() == 0) {
+        if (lane < E) pre.p0 = a.go.eptr[lane];
+        if (64 + lane < E) pre.p1 = a.go.eptr[64 + lane];
+    }
     const int e = blk * kRouteRows + wave_id();
     if (e < E) {
         const float4 *wrow = (const float4 *)(a.wr + (size_t)e * H);
         const float b = a.bias ? a.bias[e] : 0.f;
         for (int t0 = 0; t0 < T; t0 += 4) {
             float acc[4] = {0.f, 0.f, 0.f, 0.f}, ss[4] = {0.f, 0.f, 0.f, 0.f};
+            // (T=1 issues one row chunk and one state chunk; larger T four states per batch)
             for (int i0 = 0; i0 < nv; i0 += 8) {
                 // issue the router row chunk and 4 tokens' state chunks together
                 float4 wv[8], hv[4][8];
@@ -505,7 +571,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         }
     }
     __syncthreads();
-    if (a.group) group_block(sidx, T, k, E, a.ns, a.go, lstart);
+    if (a.group) group_block(sidx, T, k, E, a.ns, a.go, lstart, pre);
 }
 
 // ---------------------------------------------------------------------------
@@ -524,26 +590,27 @@ struct PrepArgs {
 __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
 {
     __shared__ int sidx[kMaxT * kMaxK];
-    __shared__ int lstart[kMaxT * kMaxK];
+    __shared__ int lstart[2 * kMaxE];
     const int t = blockIdx.x;
     for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x)
-        encode32(a.x[(size_t)t * a.H + pos], threadIdx.x & 31, a.xe, t, a.H, pos & ~31);
+        encode32(a.x[(size_t)t * a.H + pos], threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31);
     if (a.kd > a.I)
-        for (int p = t; p < a.P; p += a.T) zero_blocks(a.hpad, p, a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
+        for (int p = t; p < a.P; p += a.T)
+            zero_blocks(rec_at(a.hpad, p, a.kd), a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
     if (t != 0) return;
     for (int p = threadIdx.x; p < a.T * a.k; p += blockDim.x) sidx[p] = a.idx[p];
     __syncthreads();
-    group_block(sidx, a.T, a.k, a.E, a.ns, a.go, lstart);
+    group_block(sidx, a.T, a.k, a.E, a.ns, a.go, lstart, PrePtr{nullptr, nullptr, false});
 }
 
 // k_group: moe_group_tokens (one workgroup).
-__global__ __launch_bounds__(kRouteThreads) void k_group(const int *idx, int T, int k, int E, GroupOut go)
+__global__ __launch_bounds__(kRouteThreads) void k_group(const int *idx, int T, int k, int E, int *count,
+                                                          int *offset, int *pairs)
 {
     __shared__ int sidx[kMaxT * kMaxK];
-    __shared__ int lstart[kMaxT * kMaxK];
     for (int p = threadIdx.x; p < T * k; p += blockDim.x) sidx[p] = idx[p];
     __syncthreads();
-    group_block(sidx, T, k, E, 0, go, lstart);
+    group_sort(sidx, T, k, E, count, offset, pairs);
 }
 
 // k_rmsnorm: one workgroup per token.
@@ -559,16 +626,34 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *h, int H, float ep
 }
 
 // ---------------------------------------------------------------------------
-// Per-lane K-group dot products.  A lane owns one row of a 64-row tile and
-// one 256-column K-group.  X points at the token's encoding of that K-group:
-// w0..w2 its three pieces (64 int32 words each), bs / bsum its 8 block
-// scales and sums, p0..p2 the per-16 sums of each piece (16 each).
+// Per-lane K-group dot products.  A lane owns one row of a 64-row tile (two
+// rows, of two matrices sharing the activation, in k_gate_up) and one
+// 256-column K-group.  The token's encoded record is staged in LDS; every
+// lane of a half-wave reads the same 16-byte words (broadcast ds_read_b128),
+// which feed v_dot4 directly.
 
-struct XGroup {
-    const int *__restrict__ w0, *__restrict__ w1, *__restrict__ w2;
-    const float *__restrict__ bs, *__restrict__ bsum;
-    const int *__restrict__ p0, *__restrict__ p1, *__restrict__ p2;
+struct XL {  // one encoded K-group in LDS
+    const int4 *q0, *q1, *q2;        // 16 int4 (64 words) of each piece
+    const float *bs, *bsum;          // 8 block scales, 8 block sums
+    const int *p0, *p1, *p2;         // 16 per-16 sums of each piece
 };
+
+__device__ __forceinline__ XL xl(const uint8_t *rec, int K, int s)
+{
+    XL X;
+    X.q0 = (const int4 *)(rec + s * 256);
+    X.q1 = (const int4 *)(rec + K + s * 256);
+    X.q2 = (const int4 *)(rec + 2 * K + s * 256);
+    X.bs = (const float *)(rec + 3 * K) + s * 8;
+    X.bsum = X.bs + K / 32;
+    const int *ps = (const int *)(rec + 3 * K + K / 4) + s * 16;
+    X.p0 = ps;
+    X.p1 = ps + K / 16;
+    X.p2 = ps + K / 8;
+    return X;
+}
+
+__device__ __forceinline__ int w4(const int4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 struct Q4KRegs { uint4 meta; uint4 q[8]; };
 struct Q6KRegs { uint4 ql[8]; uint4 qh[4]; uint4 sc; uint32_t d; };
@@ -604,111 +689,159 @@ __device__ __forceinline__ float fpieces(int a0, int a1, int a2)
 }
 
 // Q4_K: sum_b bs_b*(d*sc_b*D_b) - dmin*m_b*bsum_b, D_b = piece dots of sub-block b.
-__device__ __forceinline__ float kgroup_dot(const Q4KRegs &r, const XGroup &X)
+template <int NM>
+__device__ __forceinline__ void kgroup_dot(const Q4KRegs (&r)[NM], const XL &X, float (&out)[NM])
 {
-    const uint32_t W0 = r.meta.y, W1 = r.meta.z, W2 = r.meta.w;
-    const uint32_t sclo = W0 & 0x3F3F3F3Fu, mlo = W1 & 0x3F3F3F3Fu;
-    const uint32_t schi = (W2 & 0x0F0F0F0Fu) | ((W0 >> 2) & 0x30303030u);
-    const uint32_t mhi = ((W2 >> 4) & 0x0F0F0F0Fu) | ((W1 >> 2) & 0x30303030u);
-    float acc = 0.f, accm = 0.f;
+    uint32_t sclo[NM], mlo[NM], schi[NM], mhi[NM];
+    float acc[NM], accm[NM];
+#pragma unroll
+    for (int m = 0; m < NM; m++) {
+        const uint32_t W0 = r[m].meta.y, W1 = r[m].meta.z, W2 = r[m].meta.w;
+        sclo[m] = W0 & 0x3F3F3F3Fu;
+        mlo[m] = W1 & 0x3F3F3F3Fu;
+        schi[m] = (W2 & 0x0F0F0F0Fu) | ((W0 >> 2) & 0x30303030u);
+        mhi[m] = ((W2 >> 4) & 0x0F0F0F0Fu) | ((W1 >> 2) & 0x30303030u);
+        acc[m] = 0.f;
+        accm[m] = 0.f;
+    }
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-        const uint32_t scw = c < 2 ? sclo : schi;
-        const uint32_t mw = c < 2 ? mlo : mhi;
-        const int sh0 = 8 * ((2 * c) & 3), sh1 = 8 * ((2 * c + 1) & 3);
-        const int sc0 = (scw >> sh0) & 0xff, sc1 = (scw >> sh1) & 0xff;
-        const int m0 = (mw >> sh0) & 0xff, m1 = (mw >> sh1) & 0xff;
-        int a0 = 0, a1 = 0, a2 = 0, b0 = 0, b1 = 0, b2 = 0;
+        // words 16c..16c+7 (sub-block 2c) and 16c+8..16c+15 (sub-block 2c+1) of each piece
+        const int4 x0a = X.q0[4 * c], x0b = X.q0[4 * c + 1], x0c = X.q0[4 * c + 2], x0d = X.q0[4 * c + 3];
+        const int4 x1a = X.q1[4 * c], x1b = X.q1[4 * c + 1], x1c = X.q1[4 * c + 2], x1d = X.q1[4 * c + 3];
+        const int4 x2a = X.q2[4 * c], x2b = X.q2[4 * c + 1], x2c = X.q2[4 * c + 2], x2d = X.q2[4 * c + 3];
+        const float bs0 = X.bs[2 * c], bs1 = X.bs[2 * c + 1];
+        const float bm0 = X.bsum[2 * c], bm1 = X.bsum[2 * c + 1];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t qd = comp(r.q[2 * c + (i >> 2)], i & 3);
-            const uint32_t lo = qd & 0x0F0F0F0Fu;
-            const uint32_t hi = (qd >> 4) & 0x0F0F0F0Fu;
-            a0 = dot4(lo, X.w0[16 * c + i], a0);
-            a1 = dot4(lo, X.w1[16 * c + i], a1);
-            a2 = dot4(lo, X.w2[16 * c + i], a2);
-            b0 = dot4(hi, X.w0[16 * c + 8 + i], b0);
-            b1 = dot4(hi, X.w1[16 * c + 8 + i], b1);
-            b2 = dot4(hi, X.w2[16 * c + 8 + i], b2);
+        for (int m = 0; m < NM; m++) {
+            const uint32_t scw = c < 2 ? sclo[m] : schi[m];
+            const uint32_t mw = c < 2 ? mlo[m] : mhi[m];
+            const int sh0 = 8 * ((2 * c) & 3), sh1 = 8 * ((2 * c + 1) & 3);
+            const int sc0 = (scw >> sh0) & 0xff, sc1 = (scw >> sh1) & 0xff;
+            const int m0 = (mw >> sh0) & 0xff, m1 = (mw >> sh1) & 0xff;
+            int a0 = 0, a1 = 0, a2 = 0, b0 = 0, b1 = 0, b2 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t qd = comp(r[m].q[2 * c + (i >> 2)], i & 3);
+                const uint32_t lo = qd & 0x0F0F0F0Fu;
+                const uint32_t hi = (qd >> 4) & 0x0F0F0F0Fu;
+                const int xl0 = i < 4 ? w4(x0a, i) : w4(x0b, i - 4), xh0 = i < 4 ? w4(x0c, i) : w4(x0d, i - 4);
+                const int xl1 = i < 4 ? w4(x1a, i) : w4(x1b, i - 4), xh1 = i < 4 ? w4(x1c, i) : w4(x1d, i - 4);
+                const int xl2 = i < 4 ? w4(x2a, i) : w4(x2b, i - 4), xh2 = i < 4 ? w4(x2c, i) : w4(x2d, i - 4);
+                a0 = dot4(lo, xl0, a0);
+                a1 = dot4(lo, xl1, a1);
+                a2 = dot4(lo, xl2, a2);
+                b0 = dot4(hi, xh0, b0);
+                b1 = dot4(hi, xh1, b1);
+                b2 = dot4(hi, xh2, b2);
+            }
+            acc[m] += (float)sc0 * (bs0 * fpieces(a0, a1, a2)) + (float)sc1 * (bs1 * fpieces(b0, b1, b2));
+            accm[m] += (float)m0 * bm0 + (float)m1 * bm1;
         }
-        acc += (float)sc0 * (X.bs[2 * c] * fpieces(a0, a1, a2)) + (float)sc1 * (X.bs[2 * c + 1] * fpieces(b0, b1, b2));
-        accm += (float)m0 * X.bsum[2 * c] + (float)m1 * X.bsum[2 * c + 1];
     }
-    return half_lo(r.meta.x) * acc - half_hi(r.meta.x) * accm;
+#pragma unroll
+    for (int m = 0; m < NM; m++) out[m] = half_lo(r[m].meta.x) * acc[m] - half_hi(r[m].meta.x) * accm[m];
 }
 
-// Q6_K: d * sum_b bs_b * sum_{j in b} sc_j * (Q_j - 32*S_j), Q_j, S_j piece dots / sums of sub-block j.
-__device__ __forceinline__ float kgroup_dot(const Q6KRegs &r, const XGroup &X)
+// Q6_K: d * sum_b bs_b * sum_{j in b} sc_j * (Q_j - 32*S_j), Q_j / S_j piece dots / sums of sub-block j.
+template <int NM>
+__device__ __forceinline__ void kgroup_dot(const Q6KRegs (&r)[NM], const XL &X, float (&out)[NM])
 {
-    float acc = 0.f;
+    float acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; m++) acc[m] = 0.f;
 #pragma unroll
     for (int n = 0; n < 2; n++) {
-        int A[4][2][3];
 #pragma unroll
-        for (int ih = 0; ih < 2; ih++) {
-            uint32_t qv[4][4];
+        for (int mq = 0; mq < 4; mq++) {
+            // activation block b = 4n+mq: words 32n+8mq .. +8 of each piece (sub-blocks 2b, 2b+1)
+            const int b = 4 * n + mq;
+            const int4 x0a = X.q0[(32 * n + 8 * mq) / 4], x0b = X.q0[(32 * n + 8 * mq) / 4 + 1];
+            const int4 x1a = X.q1[(32 * n + 8 * mq) / 4], x1b = X.q1[(32 * n + 8 * mq) / 4 + 1];
+            const int4 x2a = X.q2[(32 * n + 8 * mq) / 4], x2b = X.q2[(32 * n + 8 * mq) / 4 + 1];
+            const int s00 = X.p0[2 * b], s01 = X.p0[2 * b + 1];
+            const int s10 = X.p1[2 * b], s11 = X.p1[2 * b + 1];
+            const int s20 = X.p2[2 * b], s21 = X.p2[2 * b + 1];
+            const float bsb = X.bs[b];
 #pragma unroll
-            for (int i4 = 0; i4 < 4; i4++) {
-                const int i = 4 * ih + i4;
-                const uint32_t qlA = comp(r.ql[4 * n + (i >> 2)], i & 3);
-                const uint32_t qlB = comp(r.ql[4 * n + 2 + (i >> 2)], i & 3);
-                const uint32_t qhw = comp(r.qh[2 * n + (i >> 2)], i & 3);
-                qv[0][i4] = (qlA & 0x0F0F0F0Fu) | ((qhw << 4) & 0x30303030u);
-                qv[1][i4] = (qlB & 0x0F0F0F0Fu) | ((qhw << 2) & 0x30303030u);
-                qv[2][i4] = ((qlA >> 4) & 0x0F0F0F0Fu) | (qhw & 0x30303030u);
-                qv[3][i4] = ((qlB >> 4) & 0x0F0F0F0Fu) | ((qhw >> 2) & 0x30303030u);
-            }
+            for (int m = 0; m < NM; m++) {
+                int I0 = 0, I1 = 0, I2 = 0;
 #pragma unroll
-            for (int m = 0; m < 4; m++) {
-                const int wb = 32 * n + 8 * m + 4 * ih;
-                int a0 = 0, a1 = 0, a2 = 0;
+                for (int ih = 0; ih < 2; ih++) {
+                    int a0 = 0, a1 = 0, a2 = 0;
 #pragma unroll
-                for (int i4 = 0; i4 < 4; i4++) {
-                    a0 = dot4(qv[m][i4], X.w0[wb + i4], a0);
-                    a1 = dot4(qv[m][i4], X.w1[wb + i4], a1);
-                    a2 = dot4(qv[m][i4], X.w2[wb + i4], a2);
+                    for (int i4 = 0; i4 < 4; i4++) {
+                        const int i = 4 * ih + i4;
+                        const uint32_t qlA = comp(r[m].ql[4 * n + (i >> 2)], i & 3);
+                        const uint32_t qlB = comp(r[m].ql[4 * n + 2 + (i >> 2)], i & 3);
+                        const uint32_t qhw = comp(r[m].qh[2 * n + (i >> 2)], i & 3);
+                        uint32_t qv;
+                        if (mq == 0) qv = (qlA & 0x0F0F0F0Fu) | ((qhw << 4) & 0x30303030u);
+                        else if (mq == 1) qv = (qlB & 0x0F0F0F0Fu) | ((qhw << 2) & 0x30303030u);
+                        else if (mq == 2) qv = ((qlA >> 4) & 0x0F0F0F0Fu) | (qhw & 0x30303030u);
+                        else qv = ((qlB >> 4) & 0x0F0F0F0Fu) | ((qhw >> 2) & 0x30303030u);
+                        const int xw0 = ih ? w4(x0b, i4) : w4(x0a, i4);
+                        const int xw1 = ih ? w4(x1b, i4) : w4(x1a, i4);
+                        const int xw2 = ih ? w4(x2b, i4) : w4(x2a, i4);
+                        a0 = dot4(qv, xw0, a0);
+                        a1 = dot4(qv, xw1, a1);
+                        a2 = dot4(qv, xw2, a2);
+                    }
+                    const int j = 2 * b + ih;
+                    const int sc = (int)(int8_t)((comp(r[m].sc, j >> 2) >> (8 * (j & 3))) & 0xff);
+                    I0 += __mul24(sc, a0 - 32 * (ih ? s01 : s00));
+                    I1 += __mul24(sc, a1 - 32 * (ih ? s11 : s10));
+                    I2 += __mul24(sc, a2 - 32 * (ih ? s21 : s20));
                 }
-                A[m][ih][0] = a0; A[m][ih][1] = a1; A[m][ih][2] = a2;
+                acc[m] += bsb * fpieces(I0, I1, I2);
             }
-        }
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const int b = 4 * n + m;  // 32-position activation block = sub-blocks 2b, 2b+1
-            int I0 = 0, I1 = 0, I2 = 0;
-#pragma unroll
-            for (int ih = 0; ih < 2; ih++) {
-                const int j = 2 * b + ih;
-                const int sc = (int)(int8_t)((comp(r.sc, j >> 2) >> (8 * (j & 3))) & 0xff);
-                I0 += __mul24(sc, A[m][ih][0] - 32 * X.p0[j]);
-                I1 += __mul24(sc, A[m][ih][1] - 32 * X.p1[j]);
-                I2 += __mul24(sc, A[m][ih][2] - 32 * X.p2[j]);
-            }
-            acc += X.bs[b] * fpieces(I0, I1, I2);
         }
     }
-    return half_lo(r.d) * acc;
+#pragma unroll
+    for (int m = 0; m < NM; m++) out[m] = half_lo(r[m].d) * acc[m];
 }
 
 // Q8_0: sum_b d_b * bs_b * D_b over the 8 blocks of 32.
-__device__ __forceinline__ float kgroup_dot(const Q80Regs &r, const XGroup &X)
+template <int NM>
+__device__ __forceinline__ void kgroup_dot(const Q80Regs (&r)[NM], const XL &X, float (&out)[NM])
 {
-    float acc = 0.f;
+    float acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; m++) acc[m] = 0.f;
 #pragma unroll
     for (int b = 0; b < 8; b++) {
-        int a0 = 0, a1 = 0, a2 = 0;
+        const int4 x0a = X.q0[2 * b], x0b = X.q0[2 * b + 1];
+        const int4 x1a = X.q1[2 * b], x1b = X.q1[2 * b + 1];
+        const int4 x2a = X.q2[2 * b], x2b = X.q2[2 * b + 1];
+        const float bsb = X.bs[b];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int D = 8 * b + i;
-            const uint32_t qd = comp(r.q[D >> 2], D & 3);
-            a0 = dot4(qd, X.w0[D], a0);
-            a1 = dot4(qd, X.w1[D], a1);
-            a2 = dot4(qd, X.w2[D], a2);
+        for (int m = 0; m < NM; m++) {
+            int a0 = 0, a1 = 0, a2 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int D = 8 * b + i;
+                const uint32_t qd = comp(r[m].q[D >> 2], D & 3);
+                a0 = dot4(qd, i < 4 ? w4(x0a, i) : w4(x0b, i - 4), a0);
+                a1 = dot4(qd, i < 4 ? w4(x1a, i) : w4(x1b, i - 4), a1);
+                a2 = dot4(qd, i < 4 ? w4(x2a, i) : w4(x2b, i - 4), a2);
+            }
+            const uint32_t dw = comp(r[m].d, b >> 1);
+            const float db = (b & 1) ? half_hi(dw) : half_lo(dw);
+            acc[m] += db * (bsb * fpieces(a0, a1, a2));
         }
-        const uint32_t dw = comp(r.d, b >> 1);
-        const float db = (b & 1) ? half_hi(dw) : half_lo(dw);
-        acc += db * (X.bs[b] * fpieces(a0, a1, a2));
     }
-    return acc;
+#pragma unroll
+    for (int m = 0; m < NM; m++) out[m] = acc[m];
+}
+
+// An empty asm that claims to modify the weight registers: the nibble
+// unpacking then stays inside each dot product instead of being hoisted out
+// of the token loop, where its unpacked copies would not fit in registers.
+template <class R> __device__ __forceinline__ void opaque(R &r)
+{
+    uint32_t *w = reinterpret_cast<uint32_t *>(&r);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(R) / 4); i++) asm volatile("" : "+v"(w[i]));
 }
 
 template <int QT> struct RegsOf;
@@ -718,26 +851,27 @@ template <> struct RegsOf<MOE_Q8_0> { using T = Q80Regs; };
 
 template <int QT> constexpr int kTileBytes = QT == MOE_Q4_K ? 9216 : QT == MOE_Q6_K ? 13440 : 17408;
 
-// Encoding of vector `vec` (K positions), K-group s.
-__device__ __forceinline__ XGroup xgroup(const Enc &e, int vec, int K, int s)
+// Copy n bytes (multiple of 16) from global to LDS with the whole workgroup.
+__device__ __forceinline__ void stage16(uint8_t *dst, const uint8_t *src, size_t n)
 {
-    XGroup X;
-    const int *q = (const int *)(e.q + (size_t)vec * kPieces * K) + s * 64;
-    X.w0 = q;
-    X.w1 = q + K / 4;
-    X.w2 = q + K / 2;
-    X.bs = e.bs + (size_t)vec * (K / 32) + s * 8;
-    X.bsum = e.bsum + (size_t)vec * (K / 32) + s * 8;
-    const int *ps = e.ps + (size_t)vec * kPieces * (K / 16) + s * 16;
-    X.p0 = ps;
-    X.p1 = ps + K / 16;
-    X.p2 = ps + K / 8;
-    return X;
+    const uint4 *s4 = (const uint4 *)src;
+    uint4 *d4 = (uint4 *)dst;
+    for (size_t i = threadIdx.x; i < n / 16; i += blockDim.x) d4[i] = s4[i];
+}
+
+__device__ __forceinline__ int token_of(const WorkEntry &we, const int *ptok, int p)
+{
+    const int i = p - we.p0;
+    uint64_t toks;
+    __builtin_memcpy(&toks, we.tok, sizeof(toks));
+    return i < kInlineTok ? (int)((toks >> (8 * i)) & 0xff) : ptok[p];
 }
 
 // ---------------------------------------------------------------------------
 // k_gate_up: workgroup (u, rt) = distinct expert u, rows [32rt, 32rt+32) of
-// gate (lanes 0-31) and up (lanes 32-63); wave w takes K-groups w, w+8, ...
+// gate and up.  Lane (half, r) of wave w owns gate row 32rt+r and up row
+// 32rt+r for K-groups 2w+half, 2w+half+8, ...; the expert's tokens are
+// staged in LDS `tpass` at a time.
 
 struct GateUpArgs {
     const void *const *eptr;
@@ -745,21 +879,26 @@ struct GateUpArgs {
     int E;
     const WorkEntry *wt;
     const int *ptok;
-    Enc x;            // token encodings, K = H
+    Enc x;            // token records, K = H
     int H, I, kd;
     unsigned long long up_off;
-    Enc h;            // pair encodings, K = kd
+    Enc h;            // pair records, K = kd
     float *act_out;   // [P][kd] or null
     int ntile;        // I/32
+    int tpass;        // tokens staged per pass
 };
 
-constexpr int kGUThreads = 512;
+constexpr int kGUThreads = 256;
+constexpr int kTokPass = 4;
+constexpr int kGULds = 32768;   // staged token records per pass
+constexpr int kDnLds = 24576;   // staged pair records per pass
+constexpr int kDnPass = 8;
 
 template <int QT>
-__global__ __launch_bounds__(kGUThreads) void k_gate_up(GateUpArgs a)
+__global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gate_up(GateUpArgs a)
 {
-    __shared__ float part[8][kChunk][64];
-    __shared__ float redv[kChunk][64];
+    extern __shared__ __align__(16) uint8_t xs[];
+    __shared__ float part[8][kTokPass][32][2];
 
     const int u = blockIdx.x / a.ntile;
     const int rt = blockIdx.x - u * a.ntile;
@@ -768,50 +907,70 @@ __global__ __launch_bounds__(kGUThreads) void k_gate_up(GateUpArgs a)
     if (p0 >= p1) return;
     const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
     const int H = a.H, S = H >> 8;
+    const size_t RB = enc_bytes(H);
     const int wv = wave_id(), lane = lane_id();
-    const int row = rt * 32 + (lane & 31);
+    const int slot = 2 * wv + (lane >> 5), r = lane & 31;
+    const int row = rt * 32 + r;
     const int tile64 = row >> 6, lt = row & 63;
-    const uint8_t *mbase = base + ((lane >> 5) ? a.up_off : 0ull);
-    const int nwv = S < 8 ? S : 8;
 
-    for (int c0 = p0; c0 < p1; c0 += kChunk) {
-        const int nt = p1 - c0 < kChunk ? p1 - c0 : kChunk;
-        if (wv < nwv) {
-            for (int s = wv; s < S; s += 8) {
-                typename RegsOf<QT>::T r;
-                load_regs(r, mbase + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
-                for (int tt = 0; tt < nt; tt++) {
-                    const XGroup X = xgroup(a.x, a.ptok[c0 + tt], H, s);
-                    const float v = kgroup_dot(r, X);
-                    if (s == wv) part[wv][tt][lane] = v;
-                    else part[wv][tt][lane] += v;
+    typename RegsOf<QT>::T rg[2];
+    int loaded = -1;
+    if (slot < S) {  // issue the first K-group's weights before staging the tokens
+        load_regs(rg[0], base + ((size_t)tile64 * S + slot) * kTileBytes<QT>, lt);
+        load_regs(rg[1], base + a.up_off + ((size_t)tile64 * S + slot) * kTileBytes<QT>, lt);
+        loaded = slot;
+    }
+    for (int c0 = p0; c0 < p1; c0 += a.tpass) {
+        const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
+        if (c0 != p0) __syncthreads();  // the previous pass is done with xs
+        for (int tt = 0; tt < nt; tt++) stage16(xs + tt * RB, rec_at(a.x, token_of(we, a.ptok, c0 + tt), H), RB);
+        __syncthreads();
+        // each lane owns part[slot][*][r]: plain writes for its first K-group, sums after
+        for (int s = slot; s < S; s += 8) {
+            if (s != loaded) {
+                load_regs(rg[0], base + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
+                load_regs(rg[1], base + a.up_off + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
+                loaded = s;
+            }
+#pragma unroll 1
+            for (int tt = 0; tt < nt; tt++) {
+                float o[2];
+                opaque(rg[0]);
+                opaque(rg[1]);
+                kgroup_dot<2>(rg, xl(xs + tt * RB, H, s), o);
+                if (s == slot) {
+                    part[slot][tt][r][0] = o[0];
+                    part[slot][tt][r][1] = o[1];
+                } else {
+                    part[slot][tt][r][0] += o[0];
+                    part[slot][tt][r][1] += o[1];
                 }
             }
         }
-        __syncthreads();
-        for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
-            const int tt = i >> 6, ln = i & 63;
-            float s = 0.f;
-            for (int w = 0; w < nwv; w++) s += part[w][tt][ln];
-            redv[tt][ln] = s;
-        }
+        if (slot >= S)
+            for (int tt = 0; tt < nt; tt++) part[slot][tt][r][0] = part[slot][tt][r][1] = 0.f;
         __syncthreads();
         // SiLU(g)*u of rows [32rt, 32rt+32) and their encoding as block rt
         for (int i = threadIdx.x; i < nt * 32; i += blockDim.x) {
-            const int tt = i >> 5, r = i & 31;
-            const float g = redv[tt][r], up = redv[tt][32 + r];
-            const float hv = g / (1.0f + expf(-g)) * up;
-            encode32(hv, r, a.h, c0 + tt, a.kd, rt * 32);
-            if (a.act_out) a.act_out[(size_t)(c0 + tt) * a.kd + rt * 32 + r] = hv;
+            const int tt = i >> 5, rr = i & 31;
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < 8; sl++) {
+                gs += part[sl][tt][rr][0];
+                us += part[sl][tt][rr][1];
+            }
+            const float hv = gs / (1.0f + expf(-gs)) * us;
+            encode32(hv, rr, rec_at(a.h, c0 + tt, a.kd), a.kd, rt * 32);
+            if (a.act_out) a.act_out[(size_t)(c0 + tt) * a.kd + rt * 32 + rr] = hv;
         }
-        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
 // k_down: workgroup (u, rt) = distinct expert u, down rows [64rt, 64rt+64);
-// wave w takes K-groups w, w+nw, ...  The last expert to finish row tile rt
-// writes y for every token.
+// wave w takes K-groups w, w+nw, ...  The expert's pair records are staged
+// in LDS `tpass` at a time.  The last expert to finish row tile rt writes y
+// for every token.
 
 struct DownArgs {
     const void *const *eptr;
@@ -819,7 +978,7 @@ struct DownArgs {
     int E;
     const int *nuniq;
     const WorkEntry *wt;
-    Enc h;           // pair encodings, K = kd
+    Enc h;           // pair records, K = kd
     int H, kd;
     unsigned long long down_off;
     float *osc;      // [P][H] hand-over buffer
@@ -830,12 +989,14 @@ struct DownArgs {
     const float *w;  // [T][k]
     float *y;        // [T][H]
     int accumulate;
+    int tpass;
 };
 
 template <int QT>
-__global__ __launch_bounds__(512) void k_down(DownArgs a)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_down(DownArgs a)
 {
-    __shared__ float part[8][kChunk][64];
+    extern __shared__ __align__(16) uint8_t hsl[];
+    __shared__ float part[8][kDnPass][64];
     __shared__ int sinv[kMaxT * (kMaxK + kMaxShared)];
     __shared__ float swt[kMaxT * kMaxK];
     __shared__ int flag;
@@ -849,29 +1010,42 @@ __global__ __launch_bounds__(512) void k_down(DownArgs a)
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]) + a.down_off;
     const int kd = a.kd, S = kd >> 8;
+    const size_t RB = enc_bytes(kd);
     const int nwv = (int)(blockDim.x >> 6);
     const int wv = wave_id(), lane = lane_id();
 
-    for (int c0 = p0; c0 < p1; c0 += kChunk) {
-        const int nt = p1 - c0 < kChunk ? p1 - c0 : kChunk;
+    typename RegsOf<QT>::T rg[1];
+    int loaded = -1;
+    if (wv < S) {
+        load_regs(rg[0], base + ((size_t)rt * S + wv) * kTileBytes<QT>, lane);
+        loaded = wv;
+    }
+    for (int c0 = p0; c0 < p1; c0 += a.tpass) {
+        const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
+        if (c0 != p0) __syncthreads();
+        stage16(hsl, rec_at(a.h, c0, kd), nt * RB);  // the expert's pairs are contiguous
+        __syncthreads();
         for (int s = wv; s < S; s += nwv) {
-            typename RegsOf<QT>::T r;
-            load_regs(r, base + ((size_t)rt * S + s) * kTileBytes<QT>, lane);
+            if (s != loaded) {
+                load_regs(rg[0], base + ((size_t)rt * S + s) * kTileBytes<QT>, lane);
+                loaded = s;
+            }
+#pragma unroll 1
             for (int tt = 0; tt < nt; tt++) {
-                const XGroup X = xgroup(a.h, c0 + tt, kd, s);
-                const float v = kgroup_dot(r, X);
-                if (s == wv) part[wv][tt][lane] = v;
-                else part[wv][tt][lane] += v;
+                float v[1];
+                opaque(rg[0]);
+                kgroup_dot<1>(rg, xl(hsl + tt * RB, kd, s), v);
+                if (s == wv) part[wv][tt][lane] = v[0];
+                else part[wv][tt][lane] += v[0];
             }
         }
         __syncthreads();
         for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
             const int tt = i >> 6, ln = i & 63;
-            float s = 0.f;
-            for (int w = 0; w < nwv && w < S; w++) s += part[w][tt][ln];
-            st_coh(a.osc + (size_t)(c0 + tt) * a.H + rt * 64 + ln, s);
+            float sum = 0.f;
+            for (int w = 0; w < nwv; w++) sum += part[w][tt][ln];
+            st_coh(a.osc + (size_t)(c0 + tt) * a.H + rt * 64 + ln, sum);
         }
-        __syncthreads();
     }
 
     // routing of every token, staged before the arrival so that the last
@@ -885,8 +1059,9 @@ __global__ __launch_bounds__(512) void k_down(DownArgs a)
         const size_t row = (size_t)rt * 64 + ln;
         float acc = a.accumulate ? a.y[(size_t)t * a.H + row] : 0.f;
         for (int j = 0; j < a.k; j++) {
-            const int pj = sinv[t * kk + j];
-            if (pj >= 0) acc += swt[t * a.k + j] * ld_coh(a.osc + (size_t)pj * a.H + row);
+            const int pj = sinv[t * kk + j];  // -1: dropped id, contributes zero
+            const float v = ld_coh(a.osc + (size_t)(pj < 0 ? 0 : pj) * a.H + row);
+            acc += (pj < 0 ? 0.f : swt[t * a.k + j]) * v;
         }
         for (int s = 0; s < a.ns; s++) acc += ld_coh(a.osc + (size_t)sinv[t * kk + a.k + s] * a.H + row);
         a.y[(size_t)t * a.H + row] = acc;
@@ -924,8 +1099,8 @@ struct Ws {
     WsLayout L;
     uint8_t *b;
     template <class T> T *at(size_t off) const { return (T *)(b + off); }
-    Enc x() const { return Enc{at<int8_t>(L.xq), at<float>(L.xbs), at<float>(L.xbsum), at<int>(L.xps)}; }
-    Enc h() const { return Enc{at<int8_t>(L.hq), at<float>(L.hbs), at<float>(L.hbsum), at<int>(L.hps)}; }
+    Enc x() const { return Enc{at<uint8_t>(L.xenc)}; }
+    Enc h() const { return Enc{at<uint8_t>(L.henc)}; }
     GroupOut group() const
     {
         GroupOut g{};
@@ -946,8 +1121,9 @@ moe_status check_desc(const moe_expert_desc *d, ExpertGeom *g)
         return MOE_ERR_QTYPE;
     }
     if (d->gate != d->up) { set_error("gate and up must share one qtype"); return MOE_ERR_QTYPE; }
-    if (!geom(*d, g)) {
-        set_error("bad shape H=%d I=%d: H must be a multiple of 256 and I of 64, both <= %d", d->H, d->I, kMaxH);
+    if (!geom(*d, g) || enc_bytes(g->kd) > (size_t)kDnLds) {
+        set_error("bad shape H=%d I=%d: H must be a multiple of 256 up to %d, I a multiple of 64 up to %d",
+                  d->H, d->I, kMaxH, kDnLds / 4);
         return MOE_ERR_SHAPE;
     }
     return MOE_OK;
@@ -987,11 +1163,14 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     ga.h = ws.h();
     ga.act_out = act_out;
     ga.ntile = d.I / 32;
+    ga.tpass = (int)(kGULds / enc_bytes(d.H));
+    if (ga.tpass > kTokPass) ga.tpass = kTokPass;
+    const size_t glds = (size_t)ga.tpass * enc_bytes(d.H);
     dim3 ggrid(L.U * ga.ntile);
     switch (d.gate) {
-    case MOE_Q4_K: k_gate_up<MOE_Q4_K><<<ggrid, kGUThreads, 0, s>>>(ga); break;
-    case MOE_Q6_K: k_gate_up<MOE_Q6_K><<<ggrid, kGUThreads, 0, s>>>(ga); break;
-    case MOE_Q8_0: k_gate_up<MOE_Q8_0><<<ggrid, kGUThreads, 0, s>>>(ga); break;
+    case MOE_Q4_K: k_gate_up<MOE_Q4_K><<<ggrid, kGUThreads, glds, s>>>(ga); break;
+    case MOE_Q6_K: k_gate_up<MOE_Q6_K><<<ggrid, kGUThreads, glds, s>>>(ga); break;
+    case MOE_Q8_0: k_gate_up<MOE_Q8_0><<<ggrid, kGUThreads, glds, s>>>(ga); break;
     }
     LAUNCH_OK("k_gate_up");
 
@@ -1004,11 +1183,14 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     da.nrt = d.H / 64;
     da.T = T; da.k = k; da.ns = ns; da.inv = ws.at<int>(L.inv); da.w = wts; da.y = y; da.accumulate = accumulate;
     const int S = g.kd / 256;
+    da.tpass = (int)(kDnLds / enc_bytes(g.kd));
+    if (da.tpass > kDnPass) da.tpass = kDnPass;
+    const size_t dlds = (size_t)da.tpass * enc_bytes(g.kd);
     dim3 dgrid(L.U * da.nrt), dblock(64 * (S < 8 ? S : 8));
     switch (d.down) {
-    case MOE_Q4_K: k_down<MOE_Q4_K><<<dgrid, dblock, 0, s>>>(da); break;
-    case MOE_Q6_K: k_down<MOE_Q6_K><<<dgrid, dblock, 0, s>>>(da); break;
-    case MOE_Q8_0: k_down<MOE_Q8_0><<<dgrid, dblock, 0, s>>>(da); break;
+    case MOE_Q4_K: k_down<MOE_Q4_K><<<dgrid, dblock, dlds, s>>>(da); break;
+    case MOE_Q6_K: k_down<MOE_Q6_K><<<dgrid, dblock, dlds, s>>>(da); break;
+    case MOE_Q8_0: k_down<MOE_Q8_0><<<dgrid, dblock, dlds, s>>>(da); break;
     }
     LAUNCH_OK("k_down");
     return MOE_OK;
@@ -1063,9 +1245,7 @@ moe_status moe_group_tokens(const int32_t *idx, int32_t T, int32_t k, int32_t E,
     moe_status st = check_tke(T, k, E, 0);
     if (st != MOE_OK) return st;
     if (!idx || !count || !offset || !pairs) { set_error("moe_group_tokens: null pointer"); return MOE_ERR_ARG; }
-    GroupOut go{};
-    go.count = count; go.offset = offset; go.pairs = pairs;
-    k_group<<<1, kRouteThreads, 0, s>>>(idx, T, k, E, go);
+    k_group<<<1, kRouteThreads, 0, s>>>(idx, T, k, E, count, offset, pairs);
     LAUNCH_OK("k_group");
     return MOE_OK;
 }
