@@ -15,10 +15,14 @@ device copy of that step's input into the graph's state buffer), bracketed
 by synchronisation; value = T*K / elapsed.
 
 Roofline: the expert FFN (the gate/up and down kernels of moe_layer_ffn,
-which read the selected experts' bytes) timed with HIP events on its own
+which read the selected experts' bytes) timed with HIP events on the launch
 stream, layer by layer, in steps launched behind a delay kernel so that they
 run back to back.  achieved = sum over layer-steps of U * expert_bytes /
-sum of FFN durations, U = distinct experts of the layer-step.
+sum of FFN durations, U = distinct experts of the layer-step.  traffic =
+HBM bytes per FFN launch measured with the FETCH_SIZE and WRITE_SIZE
+counters (scaled by a copy kernel of known size), read from the committed
+counter summary under profiles/ and reported only while the kernel sources
+hash to the values recorded there.
 
 cpu_baseline: the fp64 oracle on the host, on a bounded sample (a few tokens
 through a few layers), scaled to tokens/s of the whole stack.
@@ -39,6 +43,31 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE decode tokens/s (layer stack) + achieved HBM GB/s on expert bytes read"
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_ffn_qwen3_30b_q4k_hbm_traffic.md")
+KERNEL_SOURCES = ("moe_kernels.hip", "moe_internal.h")
+
+
+def measured_traffic(T: int):
+    """HBM bytes per FFN launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a copy kernel), or None when that summary has no
+    figure for T or was taken on kernel sources other than the current ones."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"kernel_sources_sha256:(.*)", text)
+    if not m:
+        return None
+    recorded = dict(zip(m.group(1).split()[0::2], m.group(1).split()[1::2]))
+    csrc = os.path.join(ROOT, "quantized_expert_ffn_router_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != recorded.get(name):
+                return None
+    m = re.search(rf"traffic_bytes_per_launch T={T}: (\d+)", text)
+    return int(m.group(1)) if m else None
 
 
 def log(*a):
@@ -188,18 +217,31 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=10)
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB three times (reads and writes MIB MiB "
+                         "each), the reference dispatch for scaling HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build runs the decode path on a single MI355X "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); the multi-GPU expert-parallel "
-              f"layout is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the decode path runs on a single MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); an expert-parallel layout over "
+              f"several GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18  # fp32 elements in MIB MiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "elementwise copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                          "dispatches": 3}), flush=True)
+        return
     import workloads as W
     import quantized_expert_ffn_router_amd as moe
     moe.lib()
@@ -224,9 +266,9 @@ def main():
         cpu = cpu_baseline(cfg, kept, args.cpu_tokens, args.cpu_layers)
         log(f"cpu baseline {cpu['value']:.4f} tok/s ({cpu['sample']})")
 
-    def roof(tm):
+    def roof(tm, T):
         return {"bound": "hbm", "achieved": round(tm["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(tm["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(tm["gbps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(T),
                 "kernel": "expert FFN (k_gate_up + k_down of moe_layer_ffn)",
                 "bytes_per_launch": round(tm["bytes_per_launch"]), "us_per_launch": round(tm["ffn_us"], 3),
                 "launches": tm["launches"]}
@@ -241,14 +283,15 @@ def main():
         "config": {"workload": f"qwen3-30b-a3b-shaped Q4_K MoE stack: {cfg.n_layers} layers, H=2048, E=128, "
                                f"top-8, I=768, T={T}, all experts resident",
                    "layers": cfg.n_layers, "batch": T, "expert_bytes": cfg.expert_bytes(0)},
-        "roofline": roof(tm),
+        "roofline": roof(tm, T),
         "route_us_per_layer": round(tm["route_us"], 3),
         "cpu_baseline": cpu,
     }
     if args.also_batch and args.also_batch in res and args.also_batch != T:
         t2, m2, tm2 = res[args.also_batch]
         out[f"batch{args.also_batch}"] = {"value": round(t2, 2), "unit": "tokens/s", "ms_per_step": round(m2, 4),
-                                          "roofline": roof(tm2), "route_us_per_layer": round(tm2["route_us"], 3)}
+                                          "roofline": roof(tm2, args.also_batch),
+                                          "route_us_per_layer": round(tm2["route_us"], 3)}
     print(json.dumps(out), flush=True)
 
 

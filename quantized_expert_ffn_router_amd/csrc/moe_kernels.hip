@@ -403,7 +403,7 @@ template <int S> __device__ __forceinline__ uint64_t max_step(uint64_t b)
     return o > b ? o : b;
 }
 
-template <int NVL>
+template <int NVL, bool LDS = false>
 __device__ __forceinline__ void topk_wave(const float *lg, int E, int k, float *mine, int *myid, float *top)
 {
     const int lane = lane_id();
@@ -411,7 +411,8 @@ __device__ __forceinline__ void topk_wave(const float *lg, int E, int k, float *
 #pragma unroll
     for (int i = 0; i < NVL; i++) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? ((uint64_t)ord_bits(ld_coh(lg + e)) << 32) | (uint32_t)~e : 0ull;
+        const float v = e < E ? (LDS ? lg[e] : ld_coh(lg + e)) : 0.f;
+        key[i] = e < E ? ((uint64_t)ord_bits(v) << 32) | (uint32_t)~e : 0ull;
     }
     for (int j = 0; j < k; j++) {
         uint64_t b = key[0];
@@ -572,6 +573,49 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
     }
     __syncthreads();
     if (a.group) group_block(sidx, T, k, E, a.ns, a.go, lstart, pre);
+}
+
+// k_route_token: stand-alone routing, one workgroup per token (16 waves
+// share the E router rows; the logits stay in LDS).
+constexpr int kRouteTokThreads = 1024;
+__global__ __launch_bounds__(kRouteTokThreads) void k_route_token(const float *x, int H, const float *wr,
+                                                                  const float *bias, int E, int k, int *idx,
+                                                                  float *w, float *logits)
+{
+    __shared__ float lg[kMaxE];
+    const int t = blockIdx.x, lane = lane_id();
+    const float4 *xr = (const float4 *)(x + (size_t)t * H);
+    const int nv = H >> 8;
+    for (int e = wave_id(); e < E; e += kRouteTokThreads / 64) {
+        const float4 *wrow = (const float4 *)(wr + (size_t)e * H);
+        float acc = 0.f;
+        for (int i = 0; i < nv; i++) {
+            const float4 a = wrow[i * 64 + lane], b = xr[i * 64 + lane];
+            acc += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) {
+            const float l = acc + (bias ? bias[e] : 0.f);
+            lg[e] = l;
+            if (logits) logits[(size_t)t * E + e] = l;
+        }
+    }
+    __syncthreads();
+    if (wave_id() != 0) return;
+    float top = 0.f, mine = 0.f;
+    int myid = 0;
+    if (E <= 64) topk_wave<1, true>(lg, E, k, &mine, &myid, &top);
+    else if (E <= 128) topk_wave<2, true>(lg, E, k, &mine, &myid, &top);
+    else if (E <= 256) topk_wave<4, true>(lg, E, k, &mine, &myid, &top);
+    else if (E <= 512) topk_wave<8, true>(lg, E, k, &mine, &myid, &top);
+    else topk_wave<16, true>(lg, E, k, &mine, &myid, &top);
+    // softmax over the k selected logits, lane j holding selection j
+    const float ex = lane < k ? expf(mine - top) : 0.f;
+    const float sum = wave_sum(ex);
+    if (lane < k) {
+        idx[t * k + lane] = myid;
+        w[t * k + lane] = ex / sum;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1218,24 +1262,8 @@ moe_status moe_route_topk(const float *x, int32_t T, int32_t H, const float *w_r
     if (st != MOE_OK) return st;
     if (!x || !w_router || !idx || !w) { set_error("moe_route_topk: null pointer"); return MOE_ERR_ARG; }
     if (H < 256 || H % 256 || H > kMaxH) { set_error("moe_route_topk: H=%d must be a multiple of 256 up to %d", H, kMaxH); return MOE_ERR_SHAPE; }
-    // small private scratch per thread and device: logits and the arrival counter
-    static thread_local struct { void *p = nullptr; int dev = -1; } scr;
-    int dev = 0;
-    HIP_OK(hipGetDevice(&dev));
-    const size_t cap = (size_t)kMaxT * kMaxE * 4 + 256;
-    if (!scr.p || scr.dev != dev) {
-        scr.p = nullptr;
-        HIP_OK(hipMalloc(&scr.p, cap));
-        HIP_OK(hipMemset(scr.p, 0, cap));
-        scr.dev = dev;
-    }
-    RouteArgs a{};
-    a.h = x; a.T = T; a.H = H; a.wr = w_router; a.bias = bias; a.E = E; a.k = k; a.eps = 0.f; a.normalize = 0;
-    a.logits = (float *)scr.p; a.idx = idx; a.w = w; a.logits2 = logits;
-    a.counter = (unsigned *)((uint8_t *)scr.p + (size_t)kMaxT * kMaxE * 4);
-    a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows;
-    k_route<<<a.n_expert_blocks, kRouteThreads, 0, s>>>(a);
-    LAUNCH_OK("k_route");
+    k_route_token<<<T, kRouteTokThreads, 0, s>>>(x, H, w_router, bias, E, k, idx, w, logits);
+    LAUNCH_OK("k_route_token");
     return MOE_OK;
 }
 

@@ -74,17 +74,26 @@ class ResidentStack:
         s = self.layers[layer]
         return self.tables[layer].data_ptr() + 8 * s.E if s.n_shared else None
 
-    def layer_forward(self, layer: int, h: torch.Tensor, idx_out=None, w_out=None, stream=None):
+    def layer_forward(self, layer: int, h: torch.Tensor, idx_out=None, w_out=None, stream=None, split=False):
+        """One layer through moe_layer_forward or, with split=True, through its
+        two halves moe_layer_route and moe_layer_ffn."""
         s = self.layers[layer]
         T = h.shape[0]
+        if split:
+            L.moe_layer_route(self.descs[layer], h, T, self.routers[layer], self.biases[layer], s.E, s.k,
+                              self.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared, self.eps,
+                              idx_out, w_out, self.ws, self.ws_bytes, stream)
+            L.moe_layer_ffn(self.descs[layer], h, T, s.E, s.k, self.expert_ptrs(layer), self.shared_ptrs(layer),
+                            s.n_shared, self.ws, self.ws_bytes, stream)
+            return
         L.moe_layer_forward(self.descs[layer], h, T, self.routers[layer], self.biases[layer], s.E, s.k,
                             self.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared, self.eps,
                             idx_out, w_out, self.ws, self.ws_bytes, stream)
 
     def step(self, h: torch.Tensor, idx_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None,
-             stream=None):
+             stream=None, split=False):
         """One decode step through every layer; h [T, H] fp32 is updated in place.
         idx_out / w_out, if given, are [L, T, k] and receive each layer's routing."""
         for li in range(len(self.layers)):
             self.layer_forward(li, h, None if idx_out is None else idx_out[li],
-                               None if w_out is None else w_out[li], stream)
+                               None if w_out is None else w_out[li], stream, split)

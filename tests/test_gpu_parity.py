@@ -191,7 +191,7 @@ def test_expert_ffn(qt, H, I, E, k, ns, T, zm, accumulate):
 
 
 # ---------------------------------------------------------------- fused layer and stack
-def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None):
+def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False):
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts, n_layers)
     x, att = W.tie_free_tokens(cfg, step, T, chain_min_gap(olayers))
@@ -200,7 +200,7 @@ def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None):
     h = _dev(x)
     idx = torch.empty((n_layers, T, cfg.k), dtype=torch.int32, device=DEV)
     wts = torch.empty((n_layers, T, cfg.k), dtype=torch.float32, device=DEV)
-    st.step(h, idx, wts)
+    st.step(h, idx, wts, split=split)
     torch.cuda.synchronize()
     hg, ig, wg = h.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy()
     href = []
@@ -246,6 +246,18 @@ def test_layer_mixed_shared_q6k(T, first):
 
 def test_stack_qwen3_shape_4_layers_t8():
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=8, n_layers=4), 4, 8)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_stack_split_route_then_ffn(T):
+    """moe_layer_route followed by moe_layer_ffn, the two halves of a layer."""
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T, n_layers=2).with_(seed=5), 2, T, split=True)
+
+
+def test_mixed_shared_split():
+    cfg = W.mixed_shared_q4k_q6k(T=4)
+    sub = cfg.with_(n_layers=1, layer_qtypes=(cfg.qtypes(12),), seed=cfg.seed + 3)
+    _run_stack_and_compare(sub, 1, 4, split=True)
 
 
 def test_zero_state_stays_zero():
