@@ -382,10 +382,8 @@ __device__ void group_sort(const int *sidx, int T, int k, int E, int *count, int
     }
 }
 
-// Top-k of one token by one wave.  Each candidate is a 64-bit key: the
-// logit's bits mapped to an unsigned order (high word) and the inverted
-// expert id (low word), so the unsigned maximum is the largest logit and,
-// among equal logits, the lowest id.  Lane j receives the j-th selection.
+// A float's bits mapped to an unsigned integer of the same order (every
+// non-NaN value maps above 0).
 __device__ __forceinline__ uint32_t ord_bits(float v)
 {
     const uint32_t u = __float_as_uint(v);
@@ -395,37 +393,71 @@ __device__ __forceinline__ float unord_bits(uint32_t o)
 {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
-template <int S> __device__ __forceinline__ uint64_t max_step(uint64_t b)
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ int below(uint64_t m)
 {
-    const uint32_t hi = xchg<S>((int)(uint32_t)(b >> 32));
-    const uint32_t lo = xchg<S>((int)(uint32_t)b);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > b ? o : b;
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+__device__ __forceinline__ int ballot_count(bool p) { return __popcll(__ballot(p)); }
 
+// Top-k of one token by one wave, E <= 64*NVL logits (lane l holds experts
+// l + 64i).  Order-preserving keys make the comparisons integer.  A radix
+// select finds the k-th largest key v from the most significant bit down
+// (bit b is kept when at least k keys are >= the candidate); the keys above
+// v and, among those equal to v, the lowest ids make up the selection.  A
+// selected key's rank is the number of keys above it plus the equal keys of
+// lower id (logit descending, ties to the lower id).  Lane j < k receives
+// selection j; *top is the largest logit.
 template <int NVL, bool LDS = false>
 __device__ __forceinline__ void topk_wave(const float *lg, int E, int k, float *mine, int *myid, float *top)
 {
     const int lane = lane_id();
-    uint64_t key[NVL];
+    uint32_t key[NVL];
 #pragma unroll
     for (int i = 0; i < NVL; i++) {
         const int e = lane + 64 * i;
         const float v = e < E ? (LDS ? lg[e] : ld_coh(lg + e)) : 0.f;
-        key[i] = e < E ? ((uint64_t)ord_bits(v) << 32) | (uint32_t)~e : 0ull;
+        key[i] = e < E ? ord_bits(v) : 0u;  // every valid key is above 0
     }
-    for (int j = 0; j < k; j++) {
-        uint64_t b = key[0];
+    uint32_t thr = 0;
+    for (int b = 31; b >= 0; b--) {
+        const uint32_t cand = thr | (1u << b);
+        int cnt = 0;
 #pragma unroll
-        for (int i = 1; i < NVL; i++) b = key[i] > b ? key[i] : b;
-        b = max_step<1>(b); b = max_step<2>(b); b = max_step<4>(b);
-        b = max_step<8>(b); b = max_step<16>(b); b = max_step<32>(b);
-#pragma unroll
-        for (int i = 0; i < NVL; i++) key[i] = key[i] == b ? 0ull : key[i];
-        const float v = unord_bits((uint32_t)(b >> 32));
-        if (j == 0) *top = v;
-        if (lane == j) { *mine = v; *myid = (int)~(uint32_t)b; }
+        for (int i = 0; i < NVL; i++) cnt += ballot_count(key[i] >= cand);
+        if (cnt >= k) thr = cand;
     }
+    int need = k;  // keys equal to thr taken, lowest ids first
+#pragma unroll
+    for (int i = 0; i < NVL; i++) need -= ballot_count(key[i] > thr);
+    uint64_t sel[NVL];
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; i++) {
+        const uint64_t eq = __ballot(key[i] == thr && lane + 64 * i < E);
+        const bool take = key[i] > thr || ((eq >> lane) & 1ull && before + below(eq) < need);
+        sel[i] = __ballot(take);
+        before += __popcll(eq);
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; i++) {
+        uint64_t m = sel[i];
+        while (m) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t kx = (uint32_t)__builtin_amdgcn_readlane((int)key[i], l);
+            const int id = l + 64 * i;
+            int r = 0;
+#pragma unroll
+            for (int i2 = 0; i2 < NVL; i2++)
+                r += ballot_count(key[i2] > kx || (key[i2] == kx && lane + 64 * i2 < id));
+            if (lane == r) {
+                *mine = unord_bits(kx);
+                *myid = id;
+            }
+        }
+    }
+    *top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(*mine), 0));
 }
 
 // ---------------------------------------------------------------------------
