@@ -32,9 +32,26 @@ class LayerSpec:
     bias: Optional[np.ndarray]    # fp32 [E] or None
 
 
+def pack_layer(spec: LayerSpec, layer: int, expert_fn: Callable[[int, int], object]) -> torch.Tensor:
+    """Pinned host buffer of one layer's experts (routed, then shared) in the
+    slot layout, back to back."""
+    desc = L.ExpertDesc.of(spec.qtypes, spec.H, spec.I)
+    eb = L.moe_expert_bytes(desc)
+    n = spec.E + spec.n_shared
+    host = torch.empty(n * eb, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy()
+    for e in range(n):
+        ex = expert_fn(layer, e)
+        L.moe_repack_expert(desc, ex.gate, ex.up, ex.down, hv[e * eb:(e + 1) * eb])
+    return host
+
+
 class ResidentStack:
-    def __init__(self, layers: Sequence[LayerSpec], expert_fn: Callable[[int, int], object],
-                 T_max: int = 8, device: str = "cuda", eps: float = 1e-6, threads: int = 8):
+    def __init__(self, layers: Sequence[LayerSpec], expert_fn: Optional[Callable[[int, int], object]],
+                 T_max: int = 8, device: str = "cuda", eps: float = 1e-6, threads: int = 8,
+                 packed: Optional[Sequence[torch.Tensor]] = None):
+        """Experts come from expert_fn(layer, e) (canonical blocks) or, when
+        `packed` is given, from pinned per-layer buffers made by pack_layer."""
         self.layers = list(layers)
         self.device = torch.device(device)
         self.eps = eps
@@ -48,11 +65,7 @@ class ResidentStack:
         for li, spec in enumerate(self.layers):
             n = spec.E + spec.n_shared
             eb = self.expert_bytes[li]
-            host = torch.empty(n * eb, dtype=torch.uint8, pin_memory=True)
-            hv = host.numpy()
-            for e in range(n):
-                ex = expert_fn(li, e)
-                L.moe_repack_expert(self.descs[li], ex.gate, ex.up, ex.down, hv[e * eb:(e + 1) * eb])
+            host = packed[li] if packed is not None else pack_layer(spec, li, expert_fn)
             dev = torch.empty(n * eb, dtype=torch.uint8, device=self.device)
             dev.copy_(host, non_blocking=False)
             base = dev.data_ptr()
@@ -97,3 +110,103 @@ class ResidentStack:
         for li in range(len(self.layers)):
             self.layer_forward(li, h, None if idx_out is None else idx_out[li],
                                None if w_out is None else w_out[li], stream, split)
+
+
+class CachedStack:
+    """A decode-time MoE stack whose routed experts live in pinned host memory
+    behind an HBM slot-pool cache (moe_cache_*); shared experts and routers
+    stay resident.  Layers are grouped by expert shape and type, one slot
+    pool per group.  Per layer of a step: moe_layer_route; the ids are copied
+    to the host; the step's distinct experts are looked up in ascending id
+    (hits refresh their recency, misses take a free or the least recently
+    used slot); the misses are uploaded on a side stream, which the compute
+    stream then waits for; moe_layer_ffn reads the experts through the
+    cache's slot table of the layer.
+    """
+
+    def __init__(self, layers: Sequence[LayerSpec], packed: Sequence[torch.Tensor], slots: Sequence[int],
+                 T_max: int = 8, device: str = "cuda", eps: float = 1e-6):
+        self.layers = list(layers)
+        self.device = torch.device(device)
+        self.eps = eps
+        self.T_max = T_max
+        self.packed = list(packed)
+        self.descs = [L.ExpertDesc.of(s.qtypes, s.H, s.I) for s in self.layers]
+        self.expert_bytes = [L.moe_expert_bytes(d) for d in self.descs]
+        keys = []
+        self.layer_group = []
+        for s in self.layers:
+            key = (tuple(s.qtypes), s.H, s.I)
+            if key not in keys:
+                keys.append(key)
+            self.layer_group.append(keys.index(key))
+        self.group_descs = [L.ExpertDesc.of(q, H, I) for q, H, I in keys]
+        Es = {s.E for s in self.layers}
+        if len(Es) != 1:
+            raise ValueError("all layers of a cached stack need the same expert count")
+        self.E = Es.pop()
+        host_ptrs = []
+        for li, s in enumerate(self.layers):
+            base = self.packed[li].data_ptr()
+            host_ptrs += [base + e * self.expert_bytes[li] for e in range(s.E)]
+        self.slots = list(slots)
+        self.cache = L.Cache(self.group_descs, self.slots, self.layer_group, self.E, host_ptrs)
+        # shared experts, routers and biases resident
+        self.shared: List[Optional[torch.Tensor]] = []
+        self.shared_tabs: List[Optional[torch.Tensor]] = []
+        self.routers: List[torch.Tensor] = []
+        self.biases: List[Optional[torch.Tensor]] = []
+        for li, s in enumerate(self.layers):
+            eb = self.expert_bytes[li]
+            if s.n_shared:
+                dev = self.packed[li][s.E * eb:(s.E + s.n_shared) * eb].to(self.device)
+                self.shared.append(dev)
+                self.shared_tabs.append(torch.tensor([dev.data_ptr() + j * eb for j in range(s.n_shared)],
+                                                     dtype=torch.int64).to(self.device))
+            else:
+                self.shared.append(None)
+                self.shared_tabs.append(None)
+            self.routers.append(torch.from_numpy(np.ascontiguousarray(s.router, np.float32)).to(self.device))
+            self.biases.append(None if s.bias is None else
+                               torch.from_numpy(np.ascontiguousarray(s.bias, np.float32)).to(self.device))
+        self.ws_bytes = max(L.moe_workspace_bytes(d, T_max, s.k, s.E, s.n_shared)
+                            for d, s in zip(self.descs, self.layers))
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        L.moe_workspace_init(self.ws, self.ws_bytes)
+        kmax = max(s.k for s in self.layers)
+        self.idx_dev = torch.empty((T_max, kmax), dtype=torch.int32, device=self.device)
+        self.idx_host = torch.empty((T_max, kmax), dtype=torch.int32, pin_memory=True)
+        self.copy_stream = torch.cuda.Stream(device=self.device)
+        self.trace: Optional[list] = None
+
+    def shared_ptrs(self, layer: int) -> Optional[int]:
+        t = self.shared_tabs[layer]
+        return None if t is None else t.data_ptr()
+
+    def layer_forward(self, layer: int, h: torch.Tensor):
+        s = self.layers[layer]
+        T = h.shape[0]
+        d = self.descs[layer]
+        idx = self.idx_dev[:T, :s.k]
+        L.moe_layer_route(d, h, T, self.routers[layer], self.biases[layer], s.E, s.k, None, self.shared_ptrs(layer),
+                          s.n_shared, self.eps, idx, None, self.ws, self.ws_bytes)
+        ih = self.idx_host[:T, :s.k]
+        ih.copy_(idx, non_blocking=True)
+        torch.cuda.current_stream(self.device).synchronize()
+        experts = np.unique(ih.numpy())
+        slot, hit, vl, ve = self.cache.lookup(layer, T, experts)
+        if self.trace is not None:
+            self.trace.append((layer, experts.copy(), hit.copy(), vl.copy(), ve.copy()))
+        self.cache.upload(layer, self.copy_stream)
+        torch.cuda.current_stream(self.device).wait_stream(self.copy_stream)
+        L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
+                        self.ws, self.ws_bytes)
+
+    def step(self, h: torch.Tensor):
+        """One decode step through every layer; h [T, H] fp32 is updated in place."""
+        for li in range(len(self.layers)):
+            self.layer_forward(li, h)
+
+    def close(self):
+        torch.cuda.synchronize(self.device)
+        self.cache.close()

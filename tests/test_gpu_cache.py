@@ -1,0 +1,127 @@
+"""GPU tests of the expert slot-pool cache (moe_cache_* through CachedStack).
+
+A decode loop runs with the routed experts in pinned host memory behind an
+HBM slot pool.  Each step's output is compared with the oracle's layer stack,
+and the cache's hit/miss/victim trace with the oracle's LRU simulation fed
+the oracle's own routing (slot plan from the oracle planner, lookup order:
+step, layer, then the layer-step's distinct experts in ascending id).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import quantized_expert_ffn_router_amd as moe
+from helpers import ExpertCache, REL_L2_BAR, centered_rel_l2, chain_min_gap, layer_specs, oracle_layers, sets_equal
+from quantized_expert_ffn_router_amd.stack import CachedStack, pack_layer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[cache]", *a, flush=True)
+
+
+def _groups(cfg, n_layers):
+    keys, layer_group = [], []
+    for l in range(n_layers):
+        key = cfg.qtypes(l)
+        if key not in keys:
+            keys.append(key)
+        layer_group.append(keys.index(key))
+    descs = [moe.ExpertDesc.of(q, cfg.H, cfg.I) for q in keys]
+    ebytes = [moe.moe_expert_bytes(d) for d in descs]
+    per_group = [layer_group.count(g) for g in range(len(keys))]
+    return descs, ebytes, per_group, layer_group
+
+
+def _run(cfg, n_layers, steps, fraction, T):
+    experts = ExpertCache(cfg)
+    olayers = oracle_layers(cfg, experts, n_layers)
+    specs = layer_specs(cfg, n_layers)
+    descs, ebytes, per_group, layer_group = _groups(cfg, n_layers)
+    total = sum(cfg.E * ebytes[g] for g in layer_group)
+    budget = int(fraction * total)
+    st, slots = moe.moe_cache_plan(descs, per_group, budget, cfg.k)
+    rc, oslots = oracle.cache_plan(ebytes, per_group, budget, cfg.k)
+    assert st == 0 and rc == 0 and np.array_equal(slots, oslots), (slots, oslots)
+    _say(cfg.name, dict(layers=n_layers, steps=steps, T=T, fraction=fraction, slots=list(slots)))
+    packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
+    cs = CachedStack(specs, packed, slots, T_max=T)
+    cs.trace = []
+    ids = np.empty((steps, n_layers, T * cfg.k), np.int32)
+    try:
+        for step in range(steps):
+            x, _ = W.tie_free_tokens(cfg, step, T, chain_min_gap(olayers))
+            h = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+            cs.step(h)
+            torch.cuda.synchronize()
+            outs = [oracle.stack_token(olayers, x[t]) for t in range(T)]
+            for l in range(n_layers):
+                ids[step, l] = np.concatenate([outs[t][l].route.idx.ravel() for t in range(T)])
+            href = np.stack([outs[t][-1].h_next for t in range(T)])
+            hg = h.cpu().numpy()
+            assert oracle.rel_l2(hg, href) <= REL_L2_BAR, f"step {step}"
+            assert centered_rel_l2(hg - x, href - x) <= REL_L2_BAR, f"step {step}"
+        # the GPU's lookups are the oracle routing's distinct experts ...
+        LL, EE = oracle.lookup_sequence(ids)
+        gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in cs.trace])
+        ge = np.concatenate([e for _, e, *_ in cs.trace]).astype(np.int32)
+        assert np.array_equal(gl, LL) and np.array_equal(ge, EE)
+        # ... and its hit/miss/victim trace is the oracle LRU's, bit for bit
+        ref = oracle.lru(slots, layer_group, LL, EE)
+        hit = np.concatenate([t[2] for t in cs.trace])
+        vl = np.concatenate([t[3] for t in cs.trace])
+        ve = np.concatenate([t[4] for t in cs.trace])
+        assert np.array_equal(hit, ref.hit)
+        assert np.array_equal(vl, ref.victim_layer)
+        assert np.array_equal(ve, ref.victim_expert)
+        s = cs.cache.stats()
+        n_hit = int(ref.hit.sum())
+        assert s["lookups"] == len(LL) and s["hits"] == n_hit and s["misses"] == len(LL) - n_hit
+        assert s["evictions"] == int((ref.victim_layer >= 0).sum())
+        assert s["upload_bytes"] == sum(ebytes[layer_group[l]] for l, m in zip(LL, ref.hit) if not m)
+        _say("hit rate %.3f over %d lookups, %d evictions" % (n_hit / len(LL), len(LL), s["evictions"]))
+        return s
+    finally:
+        cs.close()
+
+
+@pytest.mark.parametrize("fraction", [0.1, 0.6])
+def test_cache_zipf_qwen3_shape(fraction):
+    """Zipf-biased routing over a 4-layer Qwen3-30B-A3B-shaped Q4_K stack,
+    pool at 10 % / 60 % of the routed expert bytes, 24 decode steps."""
+    _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1)
+
+
+def test_cache_two_groups_mixed_shared():
+    """Q4_K and Q6_K layers (two pools), 2 shared experts kept resident, T=4."""
+    cfg = W.mixed_shared_q4k_q6k(T=4)
+    Q4, Q6 = W.Q4_K, W.Q6_K
+    sub = cfg.with_(n_layers=4, layer_qtypes=((Q4,) * 3, (Q4,) * 3, (Q6,) * 3, (Q6,) * 3))
+    s = _run(sub, 4, 6, 0.25, 4)
+    assert s["lookups_le8"] == s["lookups"] and s["lookups_9_32"] == 0
+
+
+def test_cache_errors():
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=1).with_(E=16, k=4, seed=9)
+    experts = ExpertCache(cfg)
+    specs = layer_specs(cfg, 1)
+    packed = [pack_layer(specs[0], 0, experts)]
+    cs = CachedStack(specs, packed, [5], T_max=1)
+    try:
+        with pytest.raises(moe.MoeError):  # 6 distinct experts > 5 slots
+            cs.cache.lookup(0, 1, np.arange(6, dtype=np.int32))
+        with pytest.raises(moe.MoeError):  # batches over 32 tokens bypass the cache
+            cs.cache.lookup(0, 33, np.arange(2, dtype=np.int32))
+        with pytest.raises(moe.MoeError):  # not ascending
+            cs.cache.lookup(0, 1, np.array([3, 1], np.int32))
+        assert cs.cache.stats()["lookups"] == 0  # refused lookups leave the state unchanged
+        slot, hit, vl, ve = cs.cache.lookup(0, 1, np.array([1, 2, 3], np.int32))
+        assert not hit.any() and (vl == -1).all() and sorted(slot.tolist()) == [0, 1, 2]
+        cs.cache.upload(0, cs.copy_stream)
+        torch.cuda.synchronize()
+    finally:
+        cs.close()
