@@ -24,6 +24,12 @@ counters (scaled by a copy kernel of known size), read from the committed
 counter summary under profiles/ and reported only while the kernel sources
 hash to the values recorded there.
 
+cache: the same stack with its routed experts in pinned host memory behind
+an HBM slot pool of 10 % and of 60 % of the routed expert bytes (LRU, misses
+uploaded on a side stream), Zipf(1.1)-biased routing, 512 single-token
+steps from a cold pool: tokens/s, hit rates, misses per token and the
+upload rate over PCIe (upload bytes / summed copy intervals).
+
 cpu_baseline: the fp64 oracle on the host, on a bounded sample (a few tokens
 through a few layers), scaled to tokens/s of the whole stack.
 """
@@ -74,34 +80,29 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def build_stack(cfg, threads: int, keep_layers: int = 0):
-    """Generate, repack and upload every expert; keep the canonical bytes of
-    the first `keep_layers` layers for the CPU baseline."""
+def build_stack(cfg, threads: int, keep_layers: int = 0, T_max: int = 8):
+    """Generate and repack every expert into pinned per-layer host buffers,
+    upload them as a resident stack, and keep the canonical bytes of the
+    first `keep_layers` layers for the CPU baseline."""
     import workloads as W
-    from quantized_expert_ffn_router_amd.stack import LayerSpec, ResidentStack
+    from quantized_expert_ffn_router_amd.stack import LayerSpec, ResidentStack, pack_layer
 
     specs = [LayerSpec(cfg.qtypes(l), cfg.H, cfg.I, cfg.E, cfg.k, cfg.n_shared, W.router(cfg, l),
                        W.zipf_bias(cfg, l)) for l in range(cfg.n_layers)]
     pool = ThreadPoolExecutor(threads)
-    cache = {}
     kept = {}
-
-    def expert_fn(l, e):
-        # generate a whole layer at a time on the thread pool
-        if (l, e) not in cache:
-            cache.clear()
-            n = cfg.E + cfg.n_shared
-            for ee, ex in zip(range(n), pool.map(lambda x: W.expert(cfg, l, x), range(n))):
-                cache[(l, ee)] = ex
-                if l < keep_layers:
-                    kept[(l, ee)] = ex
-            if l % 8 == 0:
-                log(f"generated layer {l}/{cfg.n_layers}")
-        return cache[(l, e)]
-
-    st = ResidentStack(specs, expert_fn, T_max=8)
+    packed = []
+    n = cfg.E + cfg.n_shared
+    for l in range(cfg.n_layers):
+        exs = list(pool.map(lambda e: W.expert(cfg, l, e), range(n)))
+        if l < keep_layers:
+            kept.update({(l, e): exs[e] for e in range(n)})
+        packed.append(pack_layer(specs[l], l, lambda _l, e: exs[e]))
+        if l % 8 == 0:
+            log(f"generated layer {l}/{cfg.n_layers}")
     pool.shutdown()
-    return st, kept
+    st = ResidentStack(specs, None, T_max=T_max, packed=packed)
+    return st, kept, specs, packed
 
 
 def throughput(st, T: int, K: int, Wm: int, H: int, seed: int):
@@ -185,6 +186,60 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
                 bytes_per_launch=tot_bytes / n_ffn, gbps=tot_bytes / (tot_ffn_ms * 1e-3) / 1e9, launches=n_ffn)
 
 
+def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int):
+    """The same stack with its routed experts in pinned host memory behind an
+    HBM slot pool of `fraction` of the routed expert bytes, Zipf(1.1)-biased
+    routing, `steps` single-token decode steps from a cold pool."""
+    import torch
+    import workloads as W
+    import quantized_expert_ffn_router_amd as moe
+    from quantized_expert_ffn_router_amd.stack import CachedStack, LayerSpec
+
+    zcfg = cfg.with_(zipf_s=1.1)
+    zspecs = [LayerSpec(s.qtypes, s.H, s.I, s.E, s.k, s.n_shared, s.router, W.zipf_bias(zcfg, l))
+              for l, s in enumerate(specs)]
+    desc = moe.ExpertDesc.of(cfg.qtypes(0), cfg.H, cfg.I)
+    eb = moe.moe_expert_bytes(desc)
+    total = cfg.n_layers * cfg.E * eb
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    xs = torch.randn((steps + 2, 1, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+    legs = []
+    for f in fractions:
+        st, slots = moe.moe_cache_plan([desc], [cfg.n_layers], int(f * total), cfg.k)
+        if st != 0:
+            legs.append({"pool_fraction": f, "error": "budget below the floor"})
+            continue
+        # warm the kernels on a pool that is then discarded, so the timed trace starts cold
+        cs = CachedStack(zspecs, packed, slots, T_max=1)
+        for s_ in range(2):
+            cs.step(xs[steps + s_].clone())
+        cs.close()
+        del cs
+        cs = CachedStack(zspecs, packed, slots, T_max=1)
+        cs.time_copies = True
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            cs.step(xs[s_].clone())
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        stats = cs.cache.stats()
+        copy_s = cs.copy_ms() * 1e-3
+        cs.close()
+        legs.append({
+            "pool_fraction": f, "slots": int(slots[0]), "tokens_per_s": round(steps / el, 2),
+            "hit_rate": round(stats["hits"] / stats["lookups"], 4),
+            "hit_rate_le8": round(stats["hits_le8"] / max(1, stats["lookups_le8"]), 4),
+            "misses_per_token": round(stats["misses"] / steps, 2),
+            "upload_bytes": int(stats["upload_bytes"]),
+            "upload_GBps": round(stats["upload_bytes"] / copy_s / 1e9, 2) if copy_s > 0 else None,
+        })
+        log(f"cache {f:.0%}: {legs[-1]}")
+    return {"workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
+                        f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K)",
+            "legs": legs}
+
+
 def cpu_baseline(cfg, experts: dict, n_tokens: int, n_layers: int):
     """The oracle as it stands, on a bounded sample (n_tokens single-token
     decodes through the first n_layers layers), scaled to the whole stack."""
@@ -219,6 +274,9 @@ def main():
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--cache-steps", type=int, default=512, help="decode steps of each slot-pool leg (0: none)")
+    ap.add_argument("--zipf", action="store_true", help="Zipf(1.1) router bias on the resident stack "
+                                                         "(the skewed T=32 workload)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB three times (reads and writes MIB MiB "
                          "each), the reference dispatch for scaling HBM byte counters")
@@ -248,9 +306,12 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     cfg = W.qwen3_30b_a3b_q4k(T=args.batch, n_layers=args.layers)
+    if args.zipf:
+        cfg = cfg.with_(zipf_s=1.1)
     log(f"building {cfg.name}: {cfg.n_layers} layers x {cfg.E} experts x {cfg.expert_bytes(0)} B")
     t0 = time.time()
-    st, kept = build_stack(cfg, args.threads, args.cpu_layers if args.cpu_baseline else 0)
+    st, kept, specs, packed = build_stack(cfg, args.threads, args.cpu_layers if args.cpu_baseline else 0,
+                                          T_max=max(8, args.batch, args.also_batch))
     log(f"stack resident in {time.time() - t0:.1f} s")
 
     res = {}
@@ -260,6 +321,10 @@ def main():
         res[T] = (tps, ms, tm)
         log(f"T={T}: {tps:.1f} tok/s, {ms:.3f} ms/step; FFN {tm['ffn_us']:.2f} us/launch "
             f"{tm['gbps']:.0f} GB/s ({tm['bytes_per_launch'] / 1e6:.2f} MB), route {tm['route_us']:.2f} us")
+
+    cache = None
+    if args.cache_steps:
+        cache = cache_leg(cfg, specs, packed, (0.1, 0.6), args.cache_steps, seed=4)
 
     cpu = None
     if args.cpu_baseline:
@@ -286,6 +351,7 @@ def main():
         "roofline": roof(tm, T),
         "route_us_per_layer": round(tm["route_us"], 3),
         "cpu_baseline": cpu,
+        "cache": cache,
     }
     if args.also_batch and args.also_batch in res and args.also_batch != T:
         t2, m2, tm2 = res[args.also_batch]

@@ -178,6 +178,8 @@ class CachedStack:
         self.idx_host = torch.empty((T_max, kmax), dtype=torch.int32, pin_memory=True)
         self.copy_stream = torch.cuda.Stream(device=self.device)
         self.trace: Optional[list] = None
+        self.time_copies = False       # record events around each layer's uploads
+        self.copy_events: list = []
 
     def shared_ptrs(self, layer: int) -> Optional[int]:
         t = self.shared_tabs[layer]
@@ -197,7 +199,15 @@ class CachedStack:
         slot, hit, vl, ve = self.cache.lookup(layer, T, experts)
         if self.trace is not None:
             self.trace.append((layer, experts.copy(), hit.copy(), vl.copy(), ve.copy()))
+        timed = self.time_copies and not hit.all()
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.copy_stream)
         self.cache.upload(layer, self.copy_stream)
+        if timed:
+            e1.record(self.copy_stream)
+            self.copy_events.append((e0, e1))
         torch.cuda.current_stream(self.device).wait_stream(self.copy_stream)
         L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
                         self.ws, self.ws_bytes)
@@ -206,6 +216,10 @@ class CachedStack:
         """One decode step through every layer; h [T, H] fp32 is updated in place."""
         for li in range(len(self.layers)):
             self.layer_forward(li, h)
+
+    def copy_ms(self) -> float:
+        """Sum of the timed upload intervals (after a synchronisation)."""
+        return sum(a.elapsed_time(b) for a, b in self.copy_events)
 
     def close(self):
         torch.cuda.synchronize(self.device)
