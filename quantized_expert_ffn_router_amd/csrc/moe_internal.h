@@ -91,7 +91,7 @@ constexpr size_t enc_bytes(int K) { return (size_t)4 * K; }
 
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U;
-    size_t xenc, logits, idx, w, nuniq, wt, ptok, inv, henc, osc, cnt_route, cnt_dn, total;
+    size_t xenc, xhat, logits, idx, w, nuniq, wt, ptok, inv, henc, hf, osc, cnt_route, cnt_dn, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -106,6 +106,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     size_t o = kCntBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
+    L.xhat = take((size_t)T * d.H * 4);
     L.logits = take((size_t)T * E * 4);
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
@@ -114,6 +115,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.ptok = take((size_t)L.P * 4);
     L.inv = take((size_t)L.P * 4);
     L.henc = take((size_t)L.P * enc_bytes(L.kd));
+    L.hf = take((size_t)L.P * L.kd * 4);
     L.osc = take((size_t)L.P * d.H * 4);
     L.cnt_route = kCntRoute;
     L.cnt_dn = kCntDn;

@@ -39,6 +39,7 @@
 // the XCDs' L2 caches without whole-cache write-back or invalidation), a
 // wait for their completion, and a relaxed arrival counter.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <hip/hip_fp16.h>
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +59,8 @@ constexpr int kMaxK = 64;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Cross-lane exchanges without LDS: DPP quad permutes and row mirrors move
 // data inside 16-lane rows, v_permlane16_swap / v_permlane32_swap (gfx950)
@@ -478,6 +481,7 @@ struct RouteArgs {
     float *w2;
     float *logits2;
     Enc x;                  // [T] vectors of H
+    float *xhat;            // [T][H] normalised states (fp32), or null
     int group;
     int ns;
     GroupOut go;
@@ -518,7 +522,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         for (int i = 0; i < kRouteThreads / 64; i++) ss += red[i];
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
         const int pos = c * 256 + threadIdx.x;
-        encode32(a.h[(size_t)t * H + pos] * r, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
+        const float xv = a.h[(size_t)t * H + pos] * r;
+        encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
+        if (a.xhat) a.xhat[(size_t)t * H + pos] = xv;
         if (a.kd > a.I) {
             const int nenc = T * nv;
             for (int p = g; p < a.P; p += nenc)
@@ -1144,6 +1150,400 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA path for Q4_K experts with many tokens (the batched form of the
+// expert FFN, T4 MoE-cache report, "What the MoE cache caches": batches of
+// up to 32 tokens).  Per 256-wide super-block of a weight row the Q4_K value
+// is  d * sc_b * q - dmin * m_b  (b = 32-wide sub-block), so
+//     row . x = d * sum_b sc_b (q . x)_b  -  dmin * sum_b m_b S_b,
+// S_b the block sums of x.  sc_b * q <= 63 * 15 = 945 and m_b <= 63 are
+// integers exact in fp16; x is split into fp16 hi + lo parts (22 bits) after
+// scaling the column's super-block by a power of two.  One super-block of
+// one 32-row block against up to 32 columns is then 16 v_mfma_f32_32x32x16_f16
+// per part for the first term and one v_mfma_f32_32x32x8_f16 per part for
+// the second, both accumulated in fp32 (products exact), and an epilogue
+//     acc[t][r] += 2^-e_t * (d_r * C1[t][r] - dmin_r * C2[t][r]).
+// MFMA operand layouts (v_mfma_f32_32x32x16_f16): A lane l holds row l%32,
+// K (l/32)*8 + [0,8); B lane l holds column l%32, the same K; D lane l holds
+// column l%32, rows 8j + 4*(l/32) + i in element 4j+i.  Here A = activations
+// (rows = the expert's columns, i.e. tokens or pairs), B = weights (columns
+// = weight rows), so each lane owns one weight row of the output.
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMfmaCols = 32;  // columns (tokens or pairs) per expert
+// LDS of one staged super-block: hi and lo [16 K-steps][2 halves][32 cols][8],
+// block sums hi and lo [2][32][4], column scales [32].
+constexpr int kStageHalf = 16 * 2 * kMfmaCols * 8;       // halves per part
+constexpr int kStageSum = 2 * kMfmaCols * 4;            // halves per part
+constexpr size_t kStageBytes = (size_t)(2 * kStageHalf + 2 * kStageSum) * 2 + kMfmaCols * 4;
+
+struct Stage {
+    _Float16 *hi, *lo, *shi, *slo;
+    float *esc;
+};
+__device__ __forceinline__ Stage stage_at(uint8_t *base)
+{
+    Stage st;
+    st.hi = (_Float16 *)base;
+    st.lo = st.hi + kStageHalf;
+    st.shi = st.lo + kStageHalf;
+    st.slo = st.shi + kStageSum;
+    st.esc = (float *)(st.slo + kStageSum);
+    return st;
+}
+
+// Staging of super-block sb of n columns (column c = row rowof(c) of src,
+// fp32, row length K, positions >= valid read as zero), in two halves so
+// that the loads of the next super-block are in flight during the MFMAs of
+// the current one: stage_load fills the registers, stage_store converts them
+// into LDS.  The 256 items (column c, 32-wide block b) go to the NT threads
+// in turn, NI = 256/NT each.  A column's scale is a power of two bringing its
+// largest magnitude in the super-block to [0.5, 1).
+template <int NT> struct StageRegs {
+    float v[256 / NT][32];
+};
+
+template <int NT, class RowOf>
+__device__ __forceinline__ void stage_load(StageRegs<NT> &r, const float *src, int K, int valid, int sb, int n,
+                                           RowOf rowof)
+{
+    constexpr int NI = 256 / NT;
+#pragma unroll
+    for (int it = 0; it < NI; it++) {
+        const int item = threadIdx.x + it * NT, c = item >> 3, b = item & 7;
+        const int pos0 = sb * 256 + b * 32;
+        if (c < n) {
+            const float *row = src + (size_t)rowof(c) * K;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int p = pos0 + 4 * i;
+                float4 q;
+                if (p + 3 < valid) {
+                    q = *(const float4 *)(row + p);
+                } else {  // ragged end of the valid positions
+                    q.x = p < valid ? row[p] : 0.f;
+                    q.y = p + 1 < valid ? row[p + 1] : 0.f;
+                    q.z = p + 2 < valid ? row[p + 2] : 0.f;
+                    q.w = 0.f;
+                }
+                r.v[it][4 * i] = q.x; r.v[it][4 * i + 1] = q.y; r.v[it][4 * i + 2] = q.z; r.v[it][4 * i + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; i++) r.v[it][i] = 0.f;
+        }
+    }
+}
+
+// lmax: LDS [kMfmaCols] ints, zero on entry and left zero on exit.  Every
+// thread of the workgroup calls this (it holds barriers).
+template <int NT>
+__device__ __forceinline__ void stage_store(const StageRegs<NT> &r, Stage st, int *lmax)
+{
+    constexpr int NI = 256 / NT;
+#pragma unroll
+    for (int it = 0; it < NI; it++) {
+        const int c = (threadIdx.x + it * NT) >> 3;
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; i++) m = fmaxf(m, fabsf(r.v[it][i]));
+        if (m > 0.f) atomicMax(&lmax[c], __float_as_int(m));  // order of magnitudes = order of their bits
+    }
+    __syncthreads();
+    int cms[NI];
+#pragma unroll
+    for (int it = 0; it < NI; it++) cms[it] = lmax[(threadIdx.x + it * NT) >> 3];
+    __syncthreads();
+    if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;  // for the next call
+#pragma unroll
+    for (int it = 0; it < NI; it++) {
+        const int item = threadIdx.x + it * NT, c = item >> 3, b = item & 7;
+        const float cm = __int_as_float(cms[it]);
+        const int e = cm > 0.f ? -ilogbf(cm) - 1 : 0;  // cm * 2^e in [0.5, 1)
+        const float sc = ldexpf(1.0f, e);
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {  // 8 positions: K-step 2b + j/2, half j%2
+            f16x8 h, l;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float x = r.v[it][8 * j + i] * sc;  // exact (power of two)
+                const _Float16 xh = (_Float16)x;
+                h[i] = xh;
+                l[i] = (_Float16)(x - (float)xh);
+                sum += x;
+            }
+            const int s = 2 * b + (j >> 1), kh = j & 1;
+            *(f16x8 *)(st.hi + ((s * 2 + kh) * kMfmaCols + c) * 8) = h;
+            *(f16x8 *)(st.lo + ((s * 2 + kh) * kMfmaCols + c) * 8) = l;
+        }
+        // block sums: A'' lane l holds column l%32, blocks (l/32)*4 + [0,4)
+        const _Float16 sh = (_Float16)sum;
+        st.shi[((b >> 2) * kMfmaCols + c) * 4 + (b & 3)] = sh;
+        st.slo[((b >> 2) * kMfmaCols + c) * 4 + (b & 3)] = (_Float16)(sum - (float)sh);
+        if (b == 0) st.esc[c] = ldexpf(1.0f, -e);
+    }
+}
+
+// Weight operand of one 32-row block: lane l owns row r (tile row64) of the
+// 64-row tile holding it; per super-block it loads the row's meta and, for
+// each of the 4 qs chunks and 2 position halves, the 8 bytes of K positions
+// 16*half + 8*(l/32) + [0,8) (low nibbles: sub-block 2c, high: 2c+1).
+struct Q4KRow {
+    uint4 meta;
+    uint2 q[8];  // [chunk c][half]
+};
+__device__ __forceinline__ void load_q4k_row(Q4KRow &w, const uint8_t *tile, int row64, int kh)
+{
+    w.meta = *(const uint4 *)(tile + row64 * 16);
+#pragma unroll
+    for (int g = 0; g < 8; g++) w.q[g] = *(const uint2 *)(tile + 1024 + g * 1024 + row64 * 16 + kh * 8);
+}
+
+// 4 bytes of quants -> 4 fp16 (sc * q), q the low (HI=false) or high nibbles.
+template <bool HI>
+__device__ __forceinline__ void quant_f16(uint32_t w, f16x2 scv, f16x2 &o0, f16x2 &o1)
+{
+    const uint32_t q = HI ? (w >> 4) & 0x0F0F0F0Fu : w & 0x0F0F0F0Fu;
+    // bytes q0 q1 q2 q3 -> halves 1024+q0, 1024+q1 | 1024+q2, 1024+q3
+    const uint32_t a = __builtin_amdgcn_perm(0u, q, 0x0c010c00u) | 0x64006400u;
+    const uint32_t b = __builtin_amdgcn_perm(0u, q, 0x0c030c02u) | 0x64006400u;
+    const f16x2 k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+    o0 = (__builtin_bit_cast(f16x2, a) - k1024) * scv;
+    o1 = (__builtin_bit_cast(f16x2, b) - k1024) * scv;
+}
+
+// One super-block of one 32-row block: acc[j] += 2^-e_t (d C1 - dmin C2).
+__device__ __forceinline__ void mfma_super(const Q4KRow &w, Stage st, int lane, float (&acc)[16])
+{
+    const int kh = lane >> 5, col = lane & 31;
+    const uint32_t W0 = w.meta.y, W1 = w.meta.z, W2 = w.meta.w;
+    const uint32_t sclo = W0 & 0x3F3F3F3Fu, mlo = W1 & 0x3F3F3F3Fu;
+    const uint32_t schi = (W2 & 0x0F0F0F0Fu) | ((W0 >> 2) & 0x30303030u);
+    const uint32_t mhi = ((W2 >> 4) & 0x0F0F0F0Fu) | ((W1 >> 2) & 0x30303030u);
+    f32x16 c1 = {};
+#pragma unroll
+    for (int cch = 0; cch < 4; cch++) {
+#pragma unroll
+        for (int nib = 0; nib < 2; nib++) {
+            const int b = 2 * cch + nib;
+            const uint32_t scw = b < 4 ? sclo : schi;
+            const _Float16 scb = (_Float16)(float)((scw >> (8 * (b & 3))) & 0xff);
+            const f16x2 scv = {scb, scb};
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+                const uint2 qw = w.q[cch * 2 + half];
+                f16x2 p0, p1, p2, p3;
+                if (nib) {
+                    quant_f16<true>(qw.x, scv, p0, p1);
+                    quant_f16<true>(qw.y, scv, p2, p3);
+                } else {
+                    quant_f16<false>(qw.x, scv, p0, p1);
+                    quant_f16<false>(qw.y, scv, p2, p3);
+                }
+                const f16x8 bw = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                const int s = 2 * b + half;
+                const f16x8 ah = *(const f16x8 *)(st.hi + ((s * 2 + kh) * kMfmaCols + col) * 8);
+                const f16x8 al = *(const f16x8 *)(st.lo + ((s * 2 + kh) * kMfmaCols + col) * 8);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bw, c1, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bw, c1, 0, 0, 0);
+            }
+        }
+    }
+    // min term: A'' = block sums (columns x 8 blocks), B'' = m_b (blocks x rows)
+    const uint32_t mw = kh ? mhi : mlo;
+    const f16x4 bm = {(_Float16)(float)(mw & 0xff), (_Float16)(float)((mw >> 8) & 0xff),
+                      (_Float16)(float)((mw >> 16) & 0xff), (_Float16)(float)(mw >> 24)};
+    const f16x4 sh = *(const f16x4 *)(st.shi + (kh * kMfmaCols + col) * 4);
+    const f16x4 sl = *(const f16x4 *)(st.slo + (kh * kMfmaCols + col) * 4);
+    f32x16 c2 = {};
+    c2 = __builtin_amdgcn_mfma_f32_32x32x8f16(sh, bm, c2, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x8f16(sl, bm, c2, 0, 0, 0);
+    const float d = half_lo(w.meta.x), dmin = half_hi(w.meta.x);
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int t = 8 * (j >> 2) + 4 * kh + (j & 3);
+        acc[j] += st.esc[t] * (d * c1[j] - dmin * c2[j]);
+    }
+}
+
+// k_gate_up_mfma: workgroup (u, rb) = distinct expert u, rows [64rb, 64rb+64)
+// of gate (waves 0, 1: 32 rows each) and up (waves 2, 3) against the
+// expert's tokens (<= 32); super-blocks staged double-buffered.  Writes
+// SiLU(g)*u (fp32) per pair.
+struct GateUpMfmaArgs {
+    const void *const *eptr;
+    const void *const *sptr;
+    int E;
+    const WorkEntry *wt;
+    const int *nuniq;
+    const int *ptok;
+    const float *x;     // [T][H] normalised states
+    int H, I, kd;
+    unsigned long long up_off;
+    float *hf;          // [P][kd] SiLU(g)*u
+    float *act_out;     // [P][kd] or null
+    int nrb;            // I/64
+};
+
+constexpr int kGUMfmaThreads = 256;
+constexpr int kDnMfmaThreads = 128;
+
+__global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs a)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int lmax[kMfmaCols];
+    __shared__ float xg[2][kMfmaCols][33];
+    if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;
+    const int nitems = uni(*a.nuniq) * a.nrb;
+    const int wv = wave_id(), lane = lane_id();
+    const int hr = wv & 1;  // 32-row half of the 64-row block
+    const int kh = lane >> 5;
+    const int S = a.H >> 8;
+    // one workgroup per item (u, rb); the grid covers the largest possible
+    // number of distinct experts, and workgroups past the actual ones leave
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int u = item / a.nrb, rb = item - u * a.nrb;
+        const WorkEntry we = a.wt[u];
+        const int p0 = we.p0, n = we.p1 - we.p0;
+        const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]);
+        const int row64 = hr * 32 + (lane & 31), row = rb * 64 + row64;
+        const uint8_t *mat = base + (wv >= 2 ? a.up_off : 0);
+        auto rowof = [&](int c) { return token_of(we, a.ptok, p0 + c); };
+        float acc[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc[j] = 0.f;
+        StageRegs<kGUMfmaThreads> sr;
+        stage_load<kGUMfmaThreads>(sr, a.x, a.H, a.H, 0, n, rowof);
+        Q4KRow w;
+        load_q4k_row(w, mat + ((size_t)rb * S) * kTileBytes<MOE_Q4_K>, row64, kh);
+        __syncthreads();  // the previous item is done with the staging buffers and xg
+        stage_store<kGUMfmaThreads>(sr, stage_at(smem), lmax);
+        for (int sb = 0; sb < S; sb++) {
+            Q4KRow wn;
+            if (sb + 1 < S) load_q4k_row(wn, mat + ((size_t)rb * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
+            __syncthreads();  // stage sb is complete
+            opaque(w);
+            mfma_super(w, stage_at(smem + (sb & 1) * kStageBytes), lane, acc);
+            if (sb + 1 < S) {  // stage the next super-block while the other buffer is in use
+                stage_load<kGUMfmaThreads>(sr, a.x, a.H, a.H, sb + 1, n, rowof);
+                stage_store<kGUMfmaThreads>(sr, stage_at(smem + ((sb + 1) & 1) * kStageBytes), lmax);
+                w = wn;
+            }
+        }
+        // SiLU(g) * u: the gate waves hand their values over through LDS
+        if (wv < 2) {
+#pragma unroll
+            for (int j = 0; j < 16; j++) xg[hr][8 * (j >> 2) + 4 * kh + (j & 3)][lane & 31] = acc[j];
+        }
+        __syncthreads();
+        if (wv >= 2) {
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                const int t = 8 * (j >> 2) + 4 * kh + (j & 3);
+                if (t < n) {
+                    const float g = xg[hr][t][lane & 31];
+                    const float hv = g / (1.0f + expf(-g)) * acc[j];
+                    a.hf[(size_t)(p0 + t) * a.kd + row] = hv;
+                    if (a.act_out) a.act_out[(size_t)(p0 + t) * a.kd + row] = hv;
+                }
+            }
+        }
+    }
+}
+
+// k_down_mfma: workgroup (u, rt) = distinct expert u, down rows
+// [64rt, 64rt+64) (wave w: rows 32w..32w+31) against the expert's pairs'
+// SiLU(g)*u; hands each pair's rows over and the last expert of the tile
+// writes y, as k_down does.
+struct DownMfmaArgs {
+    const void *const *eptr;
+    const void *const *sptr;
+    int E;
+    const int *nuniq;
+    const WorkEntry *wt;
+    const float *hf;   // [P][kd]
+    int H, I, kd;
+    unsigned long long down_off;
+    float *osc;
+    unsigned *cnt;
+    int nrt;
+    int T, k, ns;
+    const int *inv;
+    const float *w;
+    float *y;
+    int accumulate;
+};
+
+__global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int lmax[kMfmaCols];
+    __shared__ int sinv[kMaxT * (kMaxK + kMaxShared)];
+    __shared__ float swt[kMaxT * kMaxK];
+    __shared__ int flag;
+    const int u = blockIdx.x / a.nrt, rt = blockIdx.x - u * a.nrt;
+    const int nu = uni(*a.nuniq);
+    if (u >= nu) return;
+    const WorkEntry we = a.wt[u];
+    const int p0 = we.p0, n = we.p1 - we.p0;
+    const uint8_t *base =
+        (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]) + a.down_off;
+    const int wv = wave_id(), lane = lane_id();
+    const int row64 = wv * 32 + (lane & 31), kh = lane >> 5;
+    const int S = a.kd >> 8;
+    const int kk = a.k + a.ns;
+    auto rowof = [&](int c) { return p0 + c; };
+    if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) acc[j] = 0.f;
+    StageRegs<kDnMfmaThreads> sr;
+    stage_load<kDnMfmaThreads>(sr, a.hf, a.kd, a.I, 0, n, rowof);
+    Q4KRow w;
+    load_q4k_row(w, base + ((size_t)rt * S) * kTileBytes<MOE_Q4_K>, row64, kh);
+    __syncthreads();  // lmax cleared
+    stage_store<kDnMfmaThreads>(sr, stage_at(smem), lmax);
+    for (int sb = 0; sb < S; sb++) {
+        Q4KRow wn;
+        if (sb + 1 < S) load_q4k_row(wn, base + ((size_t)rt * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
+        __syncthreads();  // stage sb is complete
+        opaque(w);
+        mfma_super(w, stage_at(smem + (sb & 1) * kStageBytes), lane, acc);
+        if (sb + 1 < S) {  // stage the next super-block while the other buffer is in use
+            stage_load<kDnMfmaThreads>(sr, a.hf, a.kd, a.I, sb + 1, n, rowof);
+            stage_store<kDnMfmaThreads>(sr, stage_at(smem + ((sb + 1) & 1) * kStageBytes), lmax);
+            w = wn;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        const int t = 8 * (j >> 2) + 4 * kh + (j & 3);
+        if (t < n) st_coh(a.osc + (size_t)(p0 + t) * a.H + rt * 64 + row64, acc[j]);
+    }
+    // routing of every token, staged before the arrival
+    for (int i = threadIdx.x; i < a.T * kk; i += blockDim.x) sinv[i] = a.inv[i];
+    for (int i = threadIdx.x; i < a.T * a.k; i += blockDim.x) swt[i] = a.w[i];
+    if (!arrive(&a.cnt[rt], (unsigned)nu, &flag)) return;
+    // the last expert of row tile rt: weighted sum of every token's outputs
+    for (int i = threadIdx.x; i < a.T * 64; i += blockDim.x) {
+        const int t = i >> 6, ln = i & 63;
+        const size_t r = (size_t)rt * 64 + ln;
+        float acc2 = a.accumulate ? a.y[(size_t)t * a.H + r] : 0.f;
+        for (int j = 0; j < a.k; j++) {
+            const int pj = sinv[t * kk + j];
+            const float v = ld_coh(a.osc + (size_t)(pj < 0 ? 0 : pj) * a.H + r);
+            acc2 += (pj < 0 ? 0.f : swt[t * a.k + j]) * v;
+        }
+        for (int s2 = 0; s2 < a.ns; s2++) acc2 += ld_coh(a.osc + (size_t)sinv[t * kk + a.k + s2] * a.H + r);
+        a.y[(size_t)t * a.H + r] = acc2;
+    }
+}
+
 __global__ void k_fill_zero(uint4 *p, size_t n16)
 {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
@@ -1226,10 +1626,52 @@ moe_status check_ws(const moe_expert_desc &d, void *ws, size_t ws_bytes, int T, 
     return MOE_OK;
 }
 
-moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int k, int E,
-                              int ns, const void *const *eptr, const void *const *sptr, const float *wts, float *y,
-                              int accumulate, float *act_out, hipStream_t s)
+// The MFMA path takes batches of more than kMfmaMinT tokens whose expert
+// matrices are all Q4_K.
+constexpr int kMfmaMinT = 8;
+bool use_mfma(const moe_expert_desc &d, int T)
 {
+    return T > kMfmaMinT && d.gate == MOE_Q4_K && d.up == MOE_Q4_K && d.down == MOE_Q4_K;
+}
+
+moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int k, int E, int ns,
+                           const void *const *eptr, const void *const *sptr, const float *src, const float *wts,
+                           float *y, int accumulate, float *act_out, hipStream_t s)
+{
+    const WsLayout &L = ws.L;
+    const size_t lds = 2 * kStageBytes;
+    static bool attr = false;
+    if (!attr) {
+        HIP_OK(hipFuncSetAttribute((const void *)k_gate_up_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        HIP_OK(hipFuncSetAttribute((const void *)k_down_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        attr = true;
+    }
+    GateUpMfmaArgs ga;
+    ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
+    ga.wt = ws.at<WorkEntry>(L.wt); ga.ptok = ws.at<int>(L.ptok);
+    ga.x = src; ga.H = d.H; ga.I = d.I; ga.kd = g.kd; ga.up_off = g.up_off;
+    ga.hf = ws.at<float>(L.hf); ga.act_out = act_out;
+    ga.nrb = d.I / 64;
+    ga.nuniq = ws.at<int>(L.nuniq);
+    k_gate_up_mfma<<<L.U * ga.nrb, kGUMfmaThreads, lds, s>>>(ga);
+    LAUNCH_OK("k_gate_up_mfma");
+    DownMfmaArgs da;
+    da.eptr = eptr; da.sptr = sptr; da.E = E;
+    da.nuniq = ws.at<int>(L.nuniq); da.wt = ga.wt; da.hf = ga.hf;
+    da.H = d.H; da.I = d.I; da.kd = g.kd; da.down_off = g.down_off;
+    da.osc = ws.at<float>(L.osc); da.cnt = ws.at<unsigned>(L.cnt_dn); da.nrt = d.H / 64;
+    da.T = T; da.k = k; da.ns = ns; da.inv = ws.at<int>(L.inv); da.w = wts; da.y = y; da.accumulate = accumulate;
+    k_down_mfma<<<L.U * da.nrt, kDnMfmaThreads, lds, s>>>(da);
+    LAUNCH_OK("k_down_mfma");
+    return MOE_OK;
+}
+
+moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int k, int E,
+                              int ns, const void *const *eptr, const void *const *sptr, const float *src,
+                              const float *wts, float *y, int accumulate, float *act_out, hipStream_t s)
+{
+    if (use_mfma(d, T))
+        return launch_ffn_mfma(d, g, ws, T, k, E, ns, eptr, sptr, src, wts, y, accumulate, act_out, s);
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -1350,7 +1792,8 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
-    return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, w, y, accumulate, act_out, s);
+    return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, x, w, y, accumulate, act_out,
+                              s);
 }
 
 moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, const float *w_router,
@@ -1371,6 +1814,7 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.logits = W.at<float>(W.L.logits); a.idx = W.at<int>(W.L.idx); a.w = W.at<float>(W.L.w);
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
     a.x = W.x();
+    a.xhat = use_mfma(*d, T) ? W.at<float>(W.L.xhat) : nullptr;
     a.group = 1; a.ns = n_shared; a.go = W.group();
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
@@ -1392,8 +1836,8 @@ moe_status moe_layer_ffn(const moe_expert_desc *d, float *h, int32_t T, int32_t 
     if (!h || !expert_ptrs || (n_shared > 0 && !shared_ptrs)) { set_error("moe_layer_ffn: null pointer"); return MOE_ERR_ARG; }
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
-    return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, W.at<float>(W.L.w), h, 1,
-                              nullptr, s);
+    return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, W.at<float>(W.L.xhat),
+                              W.at<float>(W.L.w), h, 1, nullptr, s);
 }
 
 moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, const float *w_router, const float *bias,

@@ -137,6 +137,11 @@ FFN_CASES = [
     ((W.Q4_K, W.Q4_K, W.Q6_K), 768, 256, 9, 4, 2, 11, False),
     ((W.Q8_0, W.Q8_0, W.Q4_K), 1024, 128, 4, 4, 0, 32, False),
     ((W.Q4_K,) * 3, 2048, 768, 16, 8, 0, 8, True),
+    # all-Q4_K experts with more than 8 tokens take the MFMA path
+    ((W.Q4_K,) * 3, 512, 192, 6, 2, 0, 9, False),       # just above the threshold; down rows padded
+    ((W.Q4_K,) * 3, 1024, 320, 8, 8, 0, 32, False),     # every token on every expert: 32 columns; ragged I
+    ((W.Q4_K,) * 3, 2048, 768, 128, 8, 2, 16, True),    # shared experts, zero-mean weights
+    ((W.Q4_K,) * 3, 2048, 768, 16, 8, 0, 32, False),    # the Qwen3-30B-A3B shape at T=32
 ]
 
 
