@@ -253,6 +253,15 @@ def test_stack_qwen3_shape_4_layers_t8():
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=8, n_layers=4), 4, 8)
 
 
+def test_stack_mixed_shared_6_layers_t4():
+    """Three Q4_K layers then three Q6_K layers, 64 routed (top-2) + 2 shared
+    experts, I=1408 (down rows padded to 1536), T=4, through the whole stack."""
+    cfg = W.mixed_shared_q4k_q6k(T=4)
+    Q4, Q6 = W.Q4_K, W.Q6_K
+    sub = cfg.with_(n_layers=6, layer_qtypes=((Q4,) * 3,) * 3 + ((Q6,) * 3,) * 3, seed=cfg.seed + 21)
+    _run_stack_and_compare(sub, 6, 4)
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_stack_split_route_then_ffn(T):
     """moe_layer_route followed by moe_layer_ffn, the two halves of a layer."""
