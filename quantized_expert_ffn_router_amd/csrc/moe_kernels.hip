@@ -951,9 +951,9 @@ __device__ __forceinline__ int token_of(const WorkEntry &we, const int *ptok, in
 
 // ---------------------------------------------------------------------------
 // k_gate_up: workgroup (u, rt) = distinct expert u, rows [32rt, 32rt+32) of
-// gate and up.  Lane (half, r) of wave w owns gate row 32rt+r and up row
-// 32rt+r for K-groups 2w+half, 2w+half+8, ...; the expert's tokens are
-// staged in LDS `tpass` at a time.
+// gate and up.  Thread 256m + 32j + r owns row 32rt+r of matrix m (0: gate,
+// 1: up) for K-groups j, j+8, ...; the expert's tokens are staged in LDS
+// `tpass` at a time.
 
 struct GateUpArgs {
     const void *const *eptr;
@@ -970,7 +970,7 @@ struct GateUpArgs {
     int tpass;        // tokens staged per pass
 };
 
-constexpr int kGUThreads = 256;
+constexpr int kGUThreads = 512;
 constexpr int kTokPass = 4;
 constexpr int kGULds = 32768;   // staged token records per pass
 constexpr int kDnLds = 24576;   // staged pair records per pass
@@ -990,16 +990,17 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
     const int H = a.H, S = H >> 8;
     const size_t RB = enc_bytes(H);
-    const int wv = wave_id(), lane = lane_id();
-    const int slot = 2 * wv + (lane >> 5), r = lane & 31;
+    const int lane = lane_id();
+    const int m = (int)(threadIdx.x >> 8);              // 0: gate, 1: up
+    const int slot = (int)((threadIdx.x >> 5) & 7), r = lane & 31;
     const int row = rt * 32 + r;
     const int tile64 = row >> 6, lt = row & 63;
+    const uint8_t *mat = base + (m ? a.up_off : 0);
 
-    typename RegsOf<QT>::T rg[2];
+    typename RegsOf<QT>::T rg[1];
     int loaded = -1;
     if (slot < S) {  // issue the first K-group's weights before staging the tokens
-        load_regs(rg[0], base + ((size_t)tile64 * S + slot) * kTileBytes<QT>, lt);
-        load_regs(rg[1], base + a.up_off + ((size_t)tile64 * S + slot) * kTileBytes<QT>, lt);
+        load_regs(rg[0], mat + ((size_t)tile64 * S + slot) * kTileBytes<QT>, lt);
         loaded = slot;
     }
     for (int c0 = p0; c0 < p1; c0 += a.tpass) {
@@ -1010,27 +1011,20 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2)))
         // each lane owns part[slot][*][r]: plain writes for its first K-group, sums after
         for (int s = slot; s < S; s += 8) {
             if (s != loaded) {
-                load_regs(rg[0], base + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
-                load_regs(rg[1], base + a.up_off + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
+                load_regs(rg[0], mat + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
                 loaded = s;
             }
 #pragma unroll 1
             for (int tt = 0; tt < nt; tt++) {
-                float o[2];
+                float o[1];
                 opaque(rg[0]);
-                opaque(rg[1]);
-                kgroup_dot<2>(rg, xl(xs + tt * RB, H, s), o);
-                if (s == slot) {
-                    part[slot][tt][r][0] = o[0];
-                    part[slot][tt][r][1] = o[1];
-                } else {
-                    part[slot][tt][r][0] += o[0];
-                    part[slot][tt][r][1] += o[1];
-                }
+                kgroup_dot<1>(rg, xl(xs + tt * RB, H, s), o);
+                if (s == slot) part[slot][tt][r][m] = o[0];
+                else part[slot][tt][r][m] += o[0];
             }
         }
         if (slot >= S)
-            for (int tt = 0; tt < nt; tt++) part[slot][tt][r][0] = part[slot][tt][r][1] = 0.f;
+            for (int tt = 0; tt < nt; tt++) part[slot][tt][r][m] = 0.f;
         __syncthreads();
         // SiLU(g)*u of rows [32rt, 32rt+32) and their encoding as block rt
         for (int i = threadIdx.x; i < nt * 32; i += blockDim.x) {
