@@ -124,12 +124,14 @@ def throughput(st, T: int, K: int, Wm: int, H: int, seed: int):
         with torch.cuda.graph(graph, stream=stream):
             st.step(h)
     torch.cuda.synchronize()
-    for rep in range(3):  # graph replays must equal the eager step
+    for rep in range(3):  # graph replays must match the eager step
         h.copy_(xs[0])
         graph.replay()
         torch.cuda.synchronize()
-        if not torch.equal(h, ref):
-            raise RuntimeError("graph replay differs from the eager step")
+        # the experts' outputs are summed with float atomics: equal up to rounding order
+        err = (torch.linalg.vector_norm(h - ref) / torch.linalg.vector_norm(ref)).item()
+        if not err <= 1e-5:
+            raise RuntimeError(f"graph replay differs from the eager step (rel-L2 {err:.3g})")
         st.step(h)  # eager work between replays
         torch.cuda.synchronize()
     for s in range(Wm):

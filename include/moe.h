@@ -158,7 +158,13 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s);
  *               [I, Ipad) are not written
  *   ws          workspace from moe_workspace_bytes(d, >=T, >=k, >=E, >=n_shared),
  *               initialised once with moe_workspace_init
- * 1 <= T <= 32. */
+ * 1 <= T <= 32.  The experts' contributions are added into y with float
+ * atomics, so the order of the sum over a token's experts follows the
+ * order in which workgroups finish: results agree with any fixed order to
+ * fp32 rounding, but their last bits can differ from run to run.  The same
+ * holds for moe_layer_ffn and moe_layer_forward.  All-Q4_K experts with
+ * T > 8 run on matrix cores (fp16 MFMA with fp32 accumulation of exact
+ * integer weights and a two-part activation split). */
 moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, int32_t k,
                           int32_t E, const int32_t *idx, const float *w,
                           const void *const *expert_ptrs, const void *const *shared_ptrs,

@@ -73,13 +73,11 @@ inline bool geom(const moe_expert_desc &d, ExpertGeom *g)
 }
 
 
-// Self-resetting counters sit at fixed offsets at the start of every
-// workspace, whatever the batch size, so that calls of different sizes can
-// share one workspace: [0] route, then one per 64-row tile of the down
-// matrices.
+// The router's self-resetting arrival counter sits at a fixed offset at the
+// start of every workspace, whatever the batch size, so that calls of
+// different sizes can share one workspace.
 constexpr size_t kCntRoute = 0;
-constexpr size_t kCntDn = 256;
-constexpr size_t kCntBytes = (kCntDn + 4 * (kMaxH / 64) + 255) & ~(size_t)255;
+constexpr size_t kCntBytes = 256;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
@@ -91,7 +89,7 @@ constexpr size_t enc_bytes(int K) { return (size_t)4 * K; }
 
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U;
-    size_t xenc, xhat, logits, idx, w, nuniq, wt, ptok, inv, henc, hf, osc, cnt_route, cnt_dn, total;
+    size_t xenc, xhat, logits, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, cnt_route, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -114,11 +112,10 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.wt = take((size_t)L.U * 32);
     L.ptok = take((size_t)L.P * 4);
     L.inv = take((size_t)L.P * 4);
+    L.pw = take((size_t)L.P * 4);
     L.henc = take((size_t)L.P * enc_bytes(L.kd));
     L.hf = take((size_t)L.P * L.kd * 4);
-    L.osc = take((size_t)L.P * d.H * 4);
     L.cnt_route = kCntRoute;
-    L.cnt_dn = kCntDn;
     L.total = o;
     return L;
 }

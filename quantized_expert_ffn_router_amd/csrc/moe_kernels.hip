@@ -253,6 +253,8 @@ struct GroupOut {
     int *inv;             // [T][k+ns] grouped position of (t, j), -1 if dropped
     const void *const *eptr, *const *sptr;  // pointer tables to resolve, or null
     int *count, *offset, *pairs;  // moe_group_tokens outputs (may be null)
+    float *pw;            // [P] combine weight of each grouped pair, or null
+    const float *wsrc;    // [T][k] routing weights the pair weights are taken from
 };
 
 // Expert-table entries lane and 64 + lane, which the router's wave 0 loads
@@ -332,6 +334,7 @@ __device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupO
             g.ptok[pos] = t;
             g.inv[t * (k + ns) + j] = pos;
         }
+        if (g.pw) g.pw[pos] = g.wsrc[p];
     }
     if (g.offset && threadIdx.x == 0) g.offset[E] = nvalid;
     if (g.wt) {
@@ -349,6 +352,7 @@ __device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupO
         for (int i = threadIdx.x; i < ns * T; i += blockDim.x) {
             const int s2 = i / T, t = i - s2 * T;
             const int pos = nvalid + s2 * T + t;
+            if (g.pw) g.pw[pos] = 1.0f;  // shared experts have weight one
             g.ptok[pos] = t;
             g.inv[t * (k + ns) + k + s2] = pos;
         }
@@ -610,7 +614,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         }
     }
     __syncthreads();
-    if (a.group) group_block(sidx, T, k, E, a.ns, a.go, lstart, pre);
+    if (a.group) {
+        GroupOut go = a.go;
+        go.wsrc = sw;
+        group_block(sidx, T, k, E, a.ns, go, lstart, pre);
+    }
 }
 
 // k_route_token: stand-alone routing, one workgroup per token (16 waves
@@ -663,6 +671,8 @@ struct PrepArgs {
     const float *x;
     int T, H, k, E, ns;
     const int *idx;
+    const float *w;  // [T][k] routing weights
+    float *yzero;    // [T][H] cleared here (the FFN adds into it), or null
     Enc xe;
     GroupOut go;
     Enc hpad;
@@ -674,15 +684,19 @@ __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
     __shared__ int sidx[kMaxT * kMaxK];
     __shared__ int lstart[2 * kMaxE];
     const int t = blockIdx.x;
-    for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x)
+    for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x) {
         encode32(a.x[(size_t)t * a.H + pos], threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31);
+        if (a.yzero) a.yzero[(size_t)t * a.H + pos] = 0.f;
+    }
     if (a.kd > a.I)
         for (int p = t; p < a.P; p += a.T)
             zero_blocks(rec_at(a.hpad, p, a.kd), a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
     if (t != 0) return;
     for (int p = threadIdx.x; p < a.T * a.k; p += blockDim.x) sidx[p] = a.idx[p];
     __syncthreads();
-    group_block(sidx, a.T, a.k, a.E, a.ns, a.go, lstart, PrePtr{nullptr, nullptr, false});
+    GroupOut go = a.go;
+    go.wsrc = a.w;
+    group_block(sidx, a.T, a.k, a.E, a.ns, go, lstart, PrePtr{nullptr, nullptr, false});
 }
 
 // k_group: moe_group_tokens (one workgroup).
@@ -1045,8 +1059,11 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // ---------------------------------------------------------------------------
 // k_down: workgroup (u, rt) = distinct expert u, down rows [64rt, 64rt+64);
 // wave w takes K-groups w, w+nw, ...  The expert's pair records are staged
-// in LDS `tpass` at a time.  The last expert to finish row tile rt writes y
-// for every token.
+// in LDS `tpass` at a time.  Each pair's rows, times the pair's combine
+// weight, are added to its token's rows of y with float atomics, so the
+// experts of a token are summed in whatever order their workgroups finish
+// (the sum is exact up to fp32 rounding; its last bits can vary from run to
+// run).
 
 struct DownArgs {
     const void *const *eptr;
@@ -1057,32 +1074,30 @@ struct DownArgs {
     Enc h;           // pair records, K = kd
     int H, kd;
     unsigned long long down_off;
-    float *osc;      // [P][H] hand-over buffer
-    unsigned *cnt;   // [H/64]
     int nrt;
-    int T, k, ns;
-    const int *inv;  // [T][k+ns]
-    const float *w;  // [T][k]
-    float *y;        // [T][H]
-    int accumulate;
+    const int *ptok; // [P] token of each grouped pair
+    const float *pw; // [P] combine weight of each grouped pair
+    float *y;        // [T][H], added into
     int tpass;
 };
+
+// y[t][row] += v, relaxed agent-scope float atomic (no return value).
+__device__ __forceinline__ void add_to(float *p, float v)
+{
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int QT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_down(DownArgs a)
 {
     extern __shared__ __align__(16) uint8_t hsl[];
     __shared__ float part[8][kDnPass][64];
-    __shared__ int sinv[kMaxT * (kMaxK + kMaxShared)];
-    __shared__ float swt[kMaxT * kMaxK];
-    __shared__ int flag;
 
     const int u = blockIdx.x / a.nrt;
     const int rt = blockIdx.x - u * a.nrt;
     const WorkEntry we = a.wt[u];
     const int e = we.e, p0 = we.p0, p1 = we.p1;
     if (p0 >= p1) return;
-    const int nu = *a.nuniq;
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]) + a.down_off;
     const int kd = a.kd, S = kd >> 8;
@@ -1120,27 +1135,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
             const int tt = i >> 6, ln = i & 63;
             float sum = 0.f;
             for (int w = 0; w < nwv; w++) sum += part[w][tt][ln];
-            st_coh(a.osc + (size_t)(c0 + tt) * a.H + rt * 64 + ln, sum);
+            const int p = c0 + tt;
+            add_to(a.y + (size_t)a.ptok[p] * a.H + rt * 64 + ln, a.pw[p] * sum);
         }
-    }
-
-    // routing of every token, staged before the arrival so that the last
-    // workgroup only waits for the hand-over loads
-    const int kk = a.k + a.ns;
-    for (int i = threadIdx.x; i < a.T * kk; i += blockDim.x) sinv[i] = a.inv[i];
-    for (int i = threadIdx.x; i < a.T * a.k; i += blockDim.x) swt[i] = a.w[i];
-    if (!arrive(&a.cnt[rt], (unsigned)nu, &flag)) return;
-    for (int i = threadIdx.x; i < a.T * 64; i += blockDim.x) {
-        const int t = i >> 6, ln = i & 63;
-        const size_t row = (size_t)rt * 64 + ln;
-        float acc = a.accumulate ? a.y[(size_t)t * a.H + row] : 0.f;
-        for (int j = 0; j < a.k; j++) {
-            const int pj = sinv[t * kk + j];  // -1: dropped id, contributes zero
-            const float v = ld_coh(a.osc + (size_t)(pj < 0 ? 0 : pj) * a.H + row);
-            acc += (pj < 0 ? 0.f : swt[t * a.k + j]) * v;
-        }
-        for (int s = 0; s < a.ns; s++) acc += ld_coh(a.osc + (size_t)sinv[t * kk + a.k + s] * a.H + row);
-        a.y[(size_t)t * a.H + row] = acc;
     }
 }
 
@@ -1452,8 +1449,7 @@ __global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs 
 
 // k_down_mfma: workgroup (u, rt) = distinct expert u, down rows
 // [64rt, 64rt+64) (wave w: rows 32w..32w+31) against the expert's pairs'
-// SiLU(g)*u; hands each pair's rows over and the last expert of the tile
-// writes y, as k_down does.
+// SiLU(g)*u; adds each pair's weighted rows into y, as k_down does.
 struct DownMfmaArgs {
     const void *const *eptr;
     const void *const *sptr;
@@ -1463,23 +1459,16 @@ struct DownMfmaArgs {
     const float *hf;   // [P][kd]
     int H, I, kd;
     unsigned long long down_off;
-    float *osc;
-    unsigned *cnt;
     int nrt;
-    int T, k, ns;
-    const int *inv;
-    const float *w;
+    const int *ptok;
+    const float *pw;
     float *y;
-    int accumulate;
 };
 
 __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int lmax[kMfmaCols];
-    __shared__ int sinv[kMaxT * (kMaxK + kMaxShared)];
-    __shared__ float swt[kMaxT * kMaxK];
-    __shared__ int flag;
     const int u = blockIdx.x / a.nrt, rt = blockIdx.x - u * a.nrt;
     const int nu = uni(*a.nuniq);
     if (u >= nu) return;
@@ -1490,7 +1479,6 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
     const int wv = wave_id(), lane = lane_id();
     const int row64 = wv * 32 + (lane & 31), kh = lane >> 5;
     const int S = a.kd >> 8;
-    const int kk = a.k + a.ns;
     auto rowof = [&](int c) { return p0 + c; };
     if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;
     float acc[16];
@@ -1517,24 +1505,7 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const int t = 8 * (j >> 2) + 4 * kh + (j & 3);
-        if (t < n) st_coh(a.osc + (size_t)(p0 + t) * a.H + rt * 64 + row64, acc[j]);
-    }
-    // routing of every token, staged before the arrival
-    for (int i = threadIdx.x; i < a.T * kk; i += blockDim.x) sinv[i] = a.inv[i];
-    for (int i = threadIdx.x; i < a.T * a.k; i += blockDim.x) swt[i] = a.w[i];
-    if (!arrive(&a.cnt[rt], (unsigned)nu, &flag)) return;
-    // the last expert of row tile rt: weighted sum of every token's outputs
-    for (int i = threadIdx.x; i < a.T * 64; i += blockDim.x) {
-        const int t = i >> 6, ln = i & 63;
-        const size_t r = (size_t)rt * 64 + ln;
-        float acc2 = a.accumulate ? a.y[(size_t)t * a.H + r] : 0.f;
-        for (int j = 0; j < a.k; j++) {
-            const int pj = sinv[t * kk + j];
-            const float v = ld_coh(a.osc + (size_t)(pj < 0 ? 0 : pj) * a.H + r);
-            acc2 += (pj < 0 ? 0.f : swt[t * a.k + j]) * v;
-        }
-        for (int s2 = 0; s2 < a.ns; s2++) acc2 += ld_coh(a.osc + (size_t)sinv[t * kk + a.k + s2] * a.H + r);
-        a.y[(size_t)t * a.H + r] = acc2;
+        if (t < n) add_to(a.y + (size_t)a.ptok[p0 + t] * a.H + rt * 64 + row64, a.pw[p0 + t] * acc[j]);
     }
 }
 
@@ -1579,6 +1550,7 @@ struct Ws {
         g.Umax = L.U;
         g.ptok = at<int>(L.ptok);
         g.inv = at<int>(L.inv);
+        g.pw = at<float>(L.pw);
         return g;
     }
 };
@@ -1628,9 +1600,10 @@ bool use_mfma(const moe_expert_desc &d, int T)
     return T > kMfmaMinT && d.gate == MOE_Q4_K && d.up == MOE_Q4_K && d.down == MOE_Q4_K;
 }
 
-moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int k, int E, int ns,
-                           const void *const *eptr, const void *const *sptr, const float *src, const float *wts,
-                           float *y, int accumulate, float *act_out, hipStream_t s)
+// The FFN launches add into y (moe_expert_ffn clears it first when not
+// accumulating); the routing is the grouping in the workspace.
+moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int E, const void *const *eptr,
+                           const void *const *sptr, const float *src, float *y, float *act_out, hipStream_t s)
 {
     const WsLayout &L = ws.L;
     const size_t lds = 2 * kStageBytes;
@@ -1653,19 +1626,18 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     da.eptr = eptr; da.sptr = sptr; da.E = E;
     da.nuniq = ws.at<int>(L.nuniq); da.wt = ga.wt; da.hf = ga.hf;
     da.H = d.H; da.I = d.I; da.kd = g.kd; da.down_off = g.down_off;
-    da.osc = ws.at<float>(L.osc); da.cnt = ws.at<unsigned>(L.cnt_dn); da.nrt = d.H / 64;
-    da.T = T; da.k = k; da.ns = ns; da.inv = ws.at<int>(L.inv); da.w = wts; da.y = y; da.accumulate = accumulate;
+    da.nrt = d.H / 64;
+    da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
     k_down_mfma<<<L.U * da.nrt, kDnMfmaThreads, lds, s>>>(da);
     LAUNCH_OK("k_down_mfma");
     return MOE_OK;
 }
 
-moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int k, int E,
-                              int ns, const void *const *eptr, const void *const *sptr, const float *src,
-                              const float *wts, float *y, int accumulate, float *act_out, hipStream_t s)
+moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
+                              const void *const *eptr, const void *const *sptr, const float *src, float *y,
+                              float *act_out, hipStream_t s)
 {
-    if (use_mfma(d, T))
-        return launch_ffn_mfma(d, g, ws, T, k, E, ns, eptr, sptr, src, wts, y, accumulate, act_out, s);
+    if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, E, eptr, sptr, src, y, act_out, s);
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -1691,9 +1663,8 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     da.nuniq = ws.at<int>(L.nuniq); da.wt = ga.wt;
     da.h = ga.h;
     da.H = d.H; da.kd = g.kd; da.down_off = g.down_off;
-    da.osc = ws.at<float>(L.osc); da.cnt = ws.at<unsigned>(L.cnt_dn);
     da.nrt = d.H / 64;
-    da.T = T; da.k = k; da.ns = ns; da.inv = ws.at<int>(L.inv); da.w = wts; da.y = y; da.accumulate = accumulate;
+    da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
     const int S = g.kd / 256;
     da.tpass = (int)(kDnLds / enc_bytes(g.kd));
     if (da.tpass > kDnPass) da.tpass = kDnPass;
@@ -1781,13 +1752,13 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
     PrepArgs pa{};
-    pa.x = x; pa.T = T; pa.H = d->H; pa.k = k; pa.E = E; pa.ns = n_shared; pa.idx = idx;
+    pa.x = x; pa.T = T; pa.H = d->H; pa.k = k; pa.E = E; pa.ns = n_shared; pa.idx = idx; pa.w = w;
+    pa.yzero = accumulate ? nullptr : y;
     pa.xe = W.x(); pa.go = W.group(); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
-    return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, x, w, y, accumulate, act_out,
-                              s);
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, x, y, act_out, s);
 }
 
 moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, const float *w_router,
@@ -1830,8 +1801,7 @@ moe_status moe_layer_ffn(const moe_expert_desc *d, float *h, int32_t T, int32_t 
     if (!h || !expert_ptrs || (n_shared > 0 && !shared_ptrs)) { set_error("moe_layer_ffn: null pointer"); return MOE_ERR_ARG; }
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
-    return launch_ffn_kernels(*d, g, W, T, k, E, n_shared, expert_ptrs, shared_ptrs, W.at<float>(W.L.xhat),
-                              W.at<float>(W.L.w), h, 1, nullptr, s);
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, W.at<float>(W.L.xhat), h, nullptr, s);
 }
 
 moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, const float *w_router, const float *bias,
