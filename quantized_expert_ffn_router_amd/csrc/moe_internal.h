@@ -73,11 +73,12 @@ inline bool geom(const moe_expert_desc &d, ExpertGeom *g)
 }
 
 
-// The router's self-resetting arrival counter sits at a fixed offset at the
-// start of every workspace, whatever the batch size, so that calls of
-// different sizes can share one workspace.
-constexpr size_t kCntRoute = 0;
-constexpr size_t kCntBytes = 256;
+// The router's hand-over of logit keys sits at a fixed offset at the start of
+// every workspace, sized for the largest batch and expert count, so that calls
+// of different sizes can share one workspace: the route launch finds it zero
+// (as moe_workspace_init leaves it) and leaves it zero.
+constexpr size_t kKeys = 0;
+constexpr size_t kKeysBytes = (size_t)kMaxT * kMaxE * 4;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
@@ -89,7 +90,7 @@ constexpr size_t enc_bytes(int K) { return (size_t)4 * K; }
 
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U;
-    size_t xenc, xhat, logits, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, cnt_route, total;
+    size_t keys, xenc, xhat, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -101,11 +102,11 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.P = T * (k + ns);
     int ur = E < T * k ? E : T * k;
     L.U = ur + ns;
-    size_t o = kCntBytes;
+    L.keys = kKeys;
+    size_t o = kKeys + kKeysBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
     L.xhat = take((size_t)T * d.H * 4);
-    L.logits = take((size_t)T * E * 4);
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
     L.nuniq = take(4);
@@ -115,7 +116,6 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.pw = take((size_t)L.P * 4);
     L.henc = take((size_t)L.P * enc_bytes(L.kd));
     L.hf = take((size_t)L.P * L.kd * 4);
-    L.cnt_route = kCntRoute;
     L.total = o;
     return L;
 }

@@ -53,7 +53,7 @@ constexpr float kC1 = 1.0f / 254.0f;
 constexpr float kC2 = 1.0f / 64516.0f;
 constexpr int kChunk = 8;  // tokens per pass of the matvec kernels
 constexpr int kRouteThreads = 256;
-constexpr int kRouteRows = kRouteThreads / 64;  // router rows per workgroup
+constexpr int kRouteRows = 2;                   // router rows per workgroup
 constexpr int kEncThreads = 256;                // positions encoded per workgroup
 constexpr int kMaxK = 64;
 
@@ -138,23 +138,12 @@ __device__ __forceinline__ int dot4(uint32_t a, int b, int c) { return __builtin
 
 __device__ __forceinline__ void st_coh(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ float ld_coh(const float *p) { return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-
-// Arrival of a workgroup whose hand-over stores (st_coh) are issued: waits
-// for their completion, then counts the workgroup.  Returns true in every
-// thread of the last of `target` arriving workgroups, which also resets the
-// counter for the next launch.
-__device__ bool arrive(unsigned *cnt, unsigned target, int *flag)
+__device__ __forceinline__ uint32_t ld_coh_u(const uint32_t *p)
 {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *flag = old == target - 1;
-        if (*flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    return *flag != 0;
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Bound on the polls of a wait for other workgroups of the same launch.
+constexpr unsigned kSpinLimit = 1u << 20;
 
 __device__ float block_sum(float v, float *red)
 {
@@ -407,24 +396,31 @@ __device__ __forceinline__ int below(uint64_t m)
 }
 __device__ __forceinline__ int ballot_count(bool p) { return __popcll(__ballot(p)); }
 
-// Top-k of one token by one wave, E <= 64*NVL logits (lane l holds experts
-// l + 64i).  Order-preserving keys make the comparisons integer.  A radix
-// select finds the k-th largest key v from the most significant bit down
-// (bit b is kept when at least k keys are >= the candidate); the keys above
-// v and, among those equal to v, the lowest ids make up the selection.  A
-// selected key's rank is the number of keys above it plus the equal keys of
-// lower id (logit descending, ties to the lower id).  Lane j < k receives
-// selection j; *top is the largest logit.
-template <int NVL, bool LDS = false>
-__device__ __forceinline__ void topk_wave(const float *lg, int E, int k, float *mine, int *myid, float *top)
+// Routing key of a logit: its order-preserving bits.  Keys are never zero
+// (NaN is taken as the canonical positive NaN), so that zero can mark a
+// key not yet written.
+__device__ __forceinline__ uint32_t logit_key(float v)
+{
+    return ord_bits(v != v ? __uint_as_float(0x7fc00000u) : v);
+}
+
+// Top-k of one token by one wave, E <= 64*NVL keys (lane l holds experts
+// l + 64i), read from LDS or (GLOBAL) with coherent loads.  A radix select
+// finds the k-th largest key v from the most significant bit down (bit b is
+// kept when at least k keys are >= the candidate); the keys above v and,
+// among those equal to v, the lowest ids make up the selection.  A selected
+// key's rank is the number of keys above it plus the equal keys of lower id
+// (logit descending, ties to the lower id); selection j goes to sidx[j],
+// skey[j].
+template <int NVL, bool GLOBAL>
+__device__ __forceinline__ void topk_wave(const uint32_t *keys, int E, int k, int *sidx, uint32_t *skey)
 {
     const int lane = lane_id();
     uint32_t key[NVL];
 #pragma unroll
     for (int i = 0; i < NVL; i++) {
         const int e = lane + 64 * i;
-        const float v = e < E ? (LDS ? lg[e] : ld_coh(lg + e)) : 0.f;
-        key[i] = e < E ? ord_bits(v) : 0u;  // every valid key is above 0
+        key[i] = e >= E ? 0u : GLOBAL ? ld_coh_u(keys + e) : keys[e];
     }
     uint32_t thr = 0;
     for (int b = 31; b >= 0; b--) {
@@ -459,12 +455,75 @@ __device__ __forceinline__ void topk_wave(const float *lg, int E, int k, float *
             for (int i2 = 0; i2 < NVL; i2++)
                 r += ballot_count(key[i2] > kx || (key[i2] == kx && lane + 64 * i2 < id));
             if (lane == r) {
-                *mine = unord_bits(kx);
-                *myid = id;
+                sidx[r] = id;
+                skey[r] = kx;
             }
         }
     }
-    *top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(*mine), 0));
+}
+
+template <bool GLOBAL>
+__device__ __forceinline__ void topk_wave_any(const uint32_t *keys, int E, int k, int *sidx, uint32_t *skey)
+{
+    if (E <= 64) topk_wave<1, GLOBAL>(keys, E, k, sidx, skey);
+    else if (E <= 128) topk_wave<2, GLOBAL>(keys, E, k, sidx, skey);
+    else if (E <= 256) topk_wave<4, GLOBAL>(keys, E, k, sidx, skey);
+    else if (E <= 512) topk_wave<8, GLOBAL>(keys, E, k, sidx, skey);
+    else topk_wave<16, GLOBAL>(keys, E, k, sidx, skey);
+}
+
+// Top-k of every token by ranks, for T*E <= kRankKeys: key e of token t
+// becomes the 64-bit C = key << 32 | ~e (unique, ordered like the key with
+// ties to the lower id), its rank is the number of its token's C_j above
+// it, and a key of rank r < k is selection r of its token (same order and
+// ties as topk_wave).  Each thread compares one key with 32 of its token's
+// keys at a time (zero padding up to a multiple of 32 ranks below every key;
+// a thread's key and chunk are (w mod n, w div n) for work item w);
+// partial ranks are summed with LDS atomics.  lc: LDS of T*ep 64-bit slots,
+// ep = E rounded up to 32; rank: LDS of T*E ints; lk: the T*E keys.
+constexpr int kRankKeys = 256;
+
+// floor(i / d) for 0 <= i < 2^16, 1 <= d <= 2^16, with r = 1.0f/d: (i + 0.5)/d
+// is at least 0.5/d away from an integer, far more than the float error.
+__device__ __forceinline__ int fdiv(int i, float r) { return (int)(((float)i + 0.5f) * r); }
+
+__device__ __forceinline__ void topk_ranks(const uint32_t *lk, int T, int E, int k, int *sidx, uint32_t *skey,
+                                           uint64_t *lc, int *rank)
+{
+    const int tid = (int)threadIdx.x, n = T * E;
+    const int ep = (E + 31) & ~31, nch = ep >> 5;
+    const float rE = 1.0f / (float)E, rep = 1.0f / (float)ep, rn = 1.0f / (float)n;
+    for (int i = tid; i < T * ep; i += blockDim.x) {
+        const int t = fdiv(i, rep), e = i - t * ep;
+        lc[i] = e < E ? (uint64_t)lk[t * E + e] << 32 | (uint32_t)~e : 0ull;
+    }
+    for (int i = tid; i < n; i += blockDim.x) rank[i] = 0;
+    __syncthreads();
+    for (int w = tid; w < n * nch; w += blockDim.x) {
+        // consecutive threads take consecutive keys against the same chunk:
+        // a wave's LDS reads are broadcasts of one address
+        const int c = fdiv(w, rn), i = w - c * n;
+        const int t = fdiv(i, rE), e = i - t * E;
+        const uint64_t ci = lc[t * ep + e];
+        const ulonglong2 *row = (const ulonglong2 *)(lc + t * ep + 32 * c);
+        int r0 = 0, r1 = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const ulonglong2 v = row[j];
+            r0 += v.x > ci;
+            r1 += v.y > ci;
+        }
+        atomicAdd(&rank[i], r0 + r1);
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+        const int r = rank[i];
+        if (r < k) {
+            const int t = fdiv(i, rE);
+            sidx[t * k + r] = i - t * E;
+            skey[t * k + r] = lk[i];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -478,7 +537,7 @@ struct RouteArgs {
     int E, k;
     float eps;
     int normalize;          // scale logits (and the encoding) by 1/rms(h[t])
-    float *logits;          // [T][E] hand-over buffer
+    unsigned *keys;         // [T][E] hand-over of logit keys; zero = not yet written
     int *idx;               // [T][k]
     float *w;               // [T][k]
     int *idx2;              // optional copies
@@ -491,25 +550,138 @@ struct RouteArgs {
     GroupOut go;
     Enc hpad;               // [P] vectors of kd: padding blocks zeroed here
     int P, I, kd;
-    unsigned *counter;
-    int n_expert_blocks;    // router workgroups; the rest encode (T * H/256)
+    int n_expert_blocks;    // router workgroups; then T * H/256 encoding workgroups, then the tail
 };
 
-// Router workgroup: 4 router rows, one per wave, against all T tokens.
-// Encoding workgroup (t, c): RMS of token t, then positions [256c, 256c+256).
-// The last router workgroup to finish does top-k and grouping.
+// Grouping of one token's k distinct selections (T = 1), by wave 0: the
+// selection of the j-th smallest id is pair and distinct expert j.  Same
+// outputs as group_block.
+__device__ __forceinline__ void group_one(const int *sidx, int k, int E, int ns, GroupOut g, PrePtr pre)
+{
+    if (wave_id() != 0) return;
+    const int lane = lane_id();
+    const int e = lane < k ? sidx[lane] : 0;
+    // table entries of e from the lanes that loaded them (all lanes take part)
+    const long long q0 = __shfl((long long)pre.p0, e & 63, 64);
+    const long long q1 = __shfl((long long)pre.p1, e & 63, 64);
+    int pos = 0;
+    for (int q = 0; q < k; q++) pos += __shfl(e, q, 64) < e;
+    if (lane < k) {
+        WorkEntry we{};
+        we.e = e; we.p0 = pos; we.p1 = pos + 1;
+        we.ptr = !g.eptr                     ? nullptr
+                 : (pre.valid && e < 64)     ? (const void *)q0
+                 : (pre.valid && e < 128)    ? (const void *)q1
+                                             : g.eptr[e];
+        g.wt[pos] = we;  // tok[] all zero: token 0
+        g.ptok[pos] = 0;
+        g.inv[lane] = pos;
+        if (g.pw) g.pw[pos] = g.wsrc[lane];
+    }
+    if (lane < ns) {
+        WorkEntry we{};
+        we.e = E + lane; we.p0 = k + lane; we.p1 = k + lane + 1;
+        we.ptr = g.eptr ? g.sptr[lane] : nullptr;
+        g.wt[k + lane] = we;
+        g.ptok[k + lane] = 0;
+        g.inv[k + lane] = k + lane;
+        if (g.pw) g.pw[k + lane] = 1.0f;
+    }
+    for (int u = k + ns + lane; u < g.Umax; u += 64) g.wt[u] = WorkEntry{};
+    if (lane == 0) *g.nuniq = k + ns;
+}
+
+// The tail workgroup: polls the keys until every one is written, then top-k
+// (clearing the keys for the next launch), softmax and grouping.  A poll that
+// gives up after kSpinLimit rounds routes with NaN weights, which no caller
+// can miss.
+__device__ void route_tail(const RouteArgs &a)
+{
+    __shared__ uint32_t lk[kRankKeys];
+    __shared__ uint64_t lc[2 * kRankKeys];
+    __shared__ int lrank[kRankKeys];
+    __shared__ int sidx[kMaxT * kMaxK];
+    __shared__ uint32_t skey[kMaxT * kMaxK];
+    __shared__ float sw[kMaxT * kMaxK];
+    __shared__ int lstart[2 * kMaxE];
+    const int T = a.T, E = a.E, k = a.k, n = T * E;
+    const int tid = (int)threadIdx.x, lane = lane_id();
+    const bool ranks = n <= kRankKeys && T * ((E + 31) & ~31) <= 2 * kRankKeys;  // fits lk, lc
+
+    // pointer table entries lane + 64i for the grouping
+    PrePtr pre{nullptr, nullptr, a.go.eptr != nullptr};
+    if (a.go.eptr && wave_id() == 0) {
+        if (lane < E) pre.p0 = a.go.eptr[lane];
+        if (64 + lane < E) pre.p1 = a.go.eptr[64 + lane];
+    }
+    int ok = 1;
+    for (unsigned it = 0;; it++) {
+        int missing = 0;
+        for (int i = tid; i < n; i += kRouteThreads) {
+            const uint32_t v = ld_coh_u(a.keys + i);
+            if (ranks) lk[i] = v;
+            missing |= v == 0u;
+        }
+        if (!__syncthreads_or(missing)) break;
+        if (it >= kSpinLimit) {
+            ok = 0;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    if (ranks) {
+        topk_ranks(lk, T, E, k, sidx, skey, lc, lrank);
+    } else {
+        for (int t = wave_id(); t < T; t += kRouteThreads / 64)
+            topk_wave_any<true>(a.keys + (size_t)t * E, E, k, sidx + t * k, skey + t * k);
+    }
+    __syncthreads();
+    // clear the keys for the next launch (plain stores: the launch boundary
+    // makes them visible); nothing reads them again in this launch
+    for (int i = tid; i < n; i += kRouteThreads) a.keys[i] = 0u;
+    // softmax over the k selected logits of each token, lane j holding selection j
+    for (int t = wave_id(); t < T; t += kRouteThreads / 64) {
+        const float lg = lane < k ? unord_bits(skey[t * k + lane]) : 0.f;
+        const float top = __shfl(lg, 0, 64);
+        const float ex = lane < k ? expf(lg - top) : 0.f;
+        const float s = wave_sum(ex);
+        if (lane < k) {
+            const float wj = ok ? ex / s : __builtin_nanf("");
+            const int id = sidx[t * k + lane];
+            sw[t * k + lane] = wj;
+            a.idx[t * k + lane] = id;
+            a.w[t * k + lane] = wj;
+            if (a.idx2) a.idx2[t * k + lane] = id;
+            if (a.w2) a.w2[t * k + lane] = wj;
+        }
+    }
+    if (!a.group) return;
+    GroupOut go = a.go;
+    go.wsrc = sw;
+    if (T == 1) {
+        // wave 0 wrote its own token's sidx / sw above
+        group_one(sidx, k, E, a.ns, go, pre);
+    } else {
+        __syncthreads();
+        group_block(sidx, T, k, E, a.ns, go, lstart, pre);
+    }
+}
+
+// Router workgroup: 2 router rows against all T tokens, the 4 waves
+// splitting H; the logits go to the tail as keys.  Encoding workgroup (t, c): RMS of token t,
+// then positions [256c, 256c+256).  The last workgroup is the tail.
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
 {
     __shared__ float red[8];
-    __shared__ int sidx[kMaxT * kMaxK];
-    __shared__ float sw[kMaxT * kMaxK];
-    __shared__ int lstart[2 * kMaxE];
-    __shared__ int flag;
 
     const int H = a.H, T = a.T, E = a.E;
     const int blk = blockIdx.x;
     const int lane = lane_id();
     const int nv = H >> 8;  // float4 per lane per row
+    if (blk == (int)gridDim.x - 1) {
+        route_tail(a);
+        return;
+    }
     if (blk >= a.n_expert_blocks) {
         const int g = blk - a.n_expert_blocks;
         const int t = g / nv, c = g - t * nv;
@@ -537,98 +709,80 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         return;
     }
 
-    // pointer table entries lane + 64i, loaded early in case this workgroup ends last
-    PrePtr pre{nullptr, nullptr, a.go.eptr != nullptr};
-    if (a.go.eptr && wave_id() == 0) {
-        if (lane < E) pre.p0 = a.go.eptr[lane];
-        if (64 + lane < E) pre.p1 = a.go.eptr[64 + lane];
-    }
-    const int e = blk * kRouteRows + wave_id();
-    if (e < E) {
-        const float4 *wrow = (const float4 *)(a.wr + (size_t)e * H);
-        const float b = a.bias ? a.bias[e] : 0.f;
-        for (int t0 = 0; t0 < T; t0 += 4) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f}, ss[4] = {0.f, 0.f, 0.f, 0.f};
-            // (T=1 issues one row chunk and one state chunk; larger T four states per batch)
-            for (int i0 = 0; i0 < nv; i0 += 8) {
-                // issue the router row chunk and 4 tokens' state chunks together
-                float4 wv[8], hv[4][8];
+    // router rows [e0, e0 + kRouteRows) against all tokens; wave w takes the
+    // 256-column chunks w, w+4, ... of H, partial sums meet in LDS
+    __shared__ float part[kRouteThreads / 64][kRouteRows + 1][4];
+    const int e0 = blk * kRouteRows, w = wave_id();
+    const int nr = E - e0 < kRouteRows ? E - e0 : kRouteRows;
+    for (int t0 = 0; t0 < T; t0 += 4) {
+        float acc[kRouteRows][4], ss[4];
 #pragma unroll
-                for (int i = 0; i < 8; i++)
-                    if (i0 + i < nv) wv[i] = wrow[(i0 + i) * 64 + lane];
+        for (int tt = 0; tt < 4; tt++) {
+            ss[tt] = 0.f;
 #pragma unroll
-                for (int tt = 0; tt < 4; tt++)
+            for (int r = 0; r < kRouteRows; r++) acc[r][tt] = 0.f;
+        }
+#pragma unroll 2
+        for (int c = w; c < nv; c += kRouteThreads / 64) {
+            float4 wv[kRouteRows], hv[4];
 #pragma unroll
-                    for (int i = 0; i < 8; i++)
-                        if (t0 + tt < T && i0 + i < nv)
-                            hv[tt][i] = ((const float4 *)(a.h + (size_t)(t0 + tt) * H))[(i0 + i) * 64 + lane];
+            for (int r = 0; r < kRouteRows; r++)
+                if (r < nr) wv[r] = ((const float4 *)(a.wr + (size_t)(e0 + r) * H))[c * 64 + lane];
 #pragma unroll
-                for (int tt = 0; tt < 4; tt++)
+            for (int tt = 0; tt < 4; tt++)
+                if (t0 + tt < T) hv[tt] = ((const float4 *)(a.h + (size_t)(t0 + tt) * H))[c * 64 + lane];
 #pragma unroll
-                    for (int i = 0; i < 8; i++)
-                        if (t0 + tt < T && i0 + i < nv) {
-                            const float4 x = hv[tt][i];
-                            acc[tt] += wv[i].x * x.x + wv[i].y * x.y + wv[i].z * x.z + wv[i].w * x.w;
-                            ss[tt] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-                        }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 4; tt++) {
+            for (int tt = 0; tt < 4; tt++)
                 if (t0 + tt < T) {
-                    const float d = wave_sum(acc[tt]);
-                    const float q = wave_sum(ss[tt]);
-                    if (lane == 0) {
-                        const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
-                        const float lg = d * rr + b;
-                        st_coh(a.logits + (size_t)(t0 + tt) * E + e, lg);
-                        if (a.logits2) a.logits2[(size_t)(t0 + tt) * E + e] = lg;
-                    }
+                    const float4 x = hv[tt];
+                    ss[tt] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+#pragma unroll
+                    for (int r = 0; r < kRouteRows; r++)
+                        if (r < nr) acc[r][tt] += wv[r].x * x.x + wv[r].y * x.y + wv[r].z * x.z + wv[r].w * x.w;
                 }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) {
+            if (t0 + tt >= T) break;
+            const float q = wave_sum(ss[tt]);
+            if (lane == 0) part[w][kRouteRows][tt] = q;
+#pragma unroll
+            for (int r = 0; r < kRouteRows; r++) {
+                const float d = wave_sum(acc[r][tt]);
+                if (lane == 0) part[w][r][tt] = d;
             }
         }
-    }
-    if (!arrive(a.counter, (unsigned)a.n_expert_blocks, &flag)) return;
-
-    // last router workgroup: softmax top-k of every token (one wave per token)
-    const int k = a.k;
-    for (int t = wave_id(); t < T; t += kRouteThreads / 64) {
-        float top = 0.f, mine = 0.f;
-        int myid = 0;
-        const float *lg = a.logits + (size_t)t * E;
-        if (E <= 64) topk_wave<1>(lg, E, k, &mine, &myid, &top);
-        else if (E <= 128) topk_wave<2>(lg, E, k, &mine, &myid, &top);
-        else if (E <= 256) topk_wave<4>(lg, E, k, &mine, &myid, &top);
-        else if (E <= 512) topk_wave<8>(lg, E, k, &mine, &myid, &top);
-        else topk_wave<16>(lg, E, k, &mine, &myid, &top);
-        // softmax over the k selected logits, lane j holding selection j
-        const float ex = lane < k ? expf(mine - top) : 0.f;
-        const float s = wave_sum(ex);
-        if (lane < k) {
-            const float wj = ex / s;
-            sidx[t * k + lane] = myid;
-            sw[t * k + lane] = wj;
-            a.idx[t * k + lane] = myid;
-            a.w[t * k + lane] = wj;
-            if (a.idx2) a.idx2[t * k + lane] = myid;
-            if (a.w2) a.w2[t * k + lane] = wj;
+        __syncthreads();
+        if ((int)threadIdx.x < nr * 4) {
+            const int r = threadIdx.x >> 2, tt = threadIdx.x & 3, t = t0 + tt;
+            if (t < T) {
+                float d = 0.f, q = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kRouteThreads / 64; ww++) {
+                    d += part[ww][r][tt];
+                    q += part[ww][kRouteRows][tt];
+                }
+                const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
+                const float lg = d * rr + (a.bias ? a.bias[e0 + r] : 0.f);
+                __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (a.logits2) a.logits2[(size_t)t * E + e0 + r] = lg;
+            }
         }
-    }
-    __syncthreads();
-    if (a.group) {
-        GroupOut go = a.go;
-        go.wsrc = sw;
-        group_block(sidx, T, k, E, a.ns, go, lstart, pre);
+        __syncthreads();
     }
 }
 
 // k_route_token: stand-alone routing, one workgroup per token (16 waves
-// share the E router rows; the logits stay in LDS).
+// share the E router rows; the keys stay in LDS).
 constexpr int kRouteTokThreads = 1024;
 __global__ __launch_bounds__(kRouteTokThreads) void k_route_token(const float *x, int H, const float *wr,
                                                                   const float *bias, int E, int k, int *idx,
                                                                   float *w, float *logits)
 {
-    __shared__ float lg[kMaxE];
+    __shared__ uint32_t lk[kMaxE];
+    __shared__ int sidx[kMaxK];
+    __shared__ uint32_t skey[kMaxK];
     const int t = blockIdx.x, lane = lane_id();
     const float4 *xr = (const float4 *)(x + (size_t)t * H);
     const int nv = H >> 8;
@@ -642,24 +796,20 @@ __global__ __launch_bounds__(kRouteTokThreads) void k_route_token(const float *x
         acc = wave_sum(acc);
         if (lane == 0) {
             const float l = acc + (bias ? bias[e] : 0.f);
-            lg[e] = l;
+            lk[e] = logit_key(l);
             if (logits) logits[(size_t)t * E + e] = l;
         }
     }
     __syncthreads();
     if (wave_id() != 0) return;
-    float top = 0.f, mine = 0.f;
-    int myid = 0;
-    if (E <= 64) topk_wave<1, true>(lg, E, k, &mine, &myid, &top);
-    else if (E <= 128) topk_wave<2, true>(lg, E, k, &mine, &myid, &top);
-    else if (E <= 256) topk_wave<4, true>(lg, E, k, &mine, &myid, &top);
-    else if (E <= 512) topk_wave<8, true>(lg, E, k, &mine, &myid, &top);
-    else topk_wave<16, true>(lg, E, k, &mine, &myid, &top);
+    topk_wave_any<false>(lk, E, k, sidx, skey);
     // softmax over the k selected logits, lane j holding selection j
-    const float ex = lane < k ? expf(mine - top) : 0.f;
+    const float lg = lane < k ? unord_bits(skey[lane]) : 0.f;
+    const float top = __shfl(lg, 0, 64);
+    const float ex = lane < k ? expf(lg - top) : 0.f;
     const float sum = wave_sum(ex);
     if (lane < k) {
-        idx[t * k + lane] = myid;
+        idx[t * k + lane] = sidx[lane];
         w[t * k + lane] = ex / sum;
     }
 }
@@ -1776,16 +1926,15 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
     RouteArgs a{};
     a.h = h; a.T = T; a.H = d->H; a.wr = w_router; a.bias = bias; a.E = E; a.k = k; a.eps = eps; a.normalize = 1;
-    a.logits = W.at<float>(W.L.logits); a.idx = W.at<int>(W.L.idx); a.w = W.at<float>(W.L.w);
+    a.keys = W.at<unsigned>(W.L.keys); a.idx = W.at<int>(W.L.idx); a.w = W.at<float>(W.L.w);
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
     a.x = W.x();
     a.xhat = use_mfma(*d, T) ? W.at<float>(W.L.xhat) : nullptr;
     a.group = 1; a.ns = n_shared; a.go = W.group();
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
-    a.counter = W.at<unsigned>(W.L.cnt_route);
     a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows;
-    k_route<<<a.n_expert_blocks + T * (d->H / kEncThreads), kRouteThreads, 0, s>>>(a);
+    k_route<<<a.n_expert_blocks + T * (d->H / kEncThreads) + 1, kRouteThreads, 0, s>>>(a);
     LAUNCH_OK("k_route");
     return MOE_OK;
 }

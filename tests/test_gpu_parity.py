@@ -228,6 +228,13 @@ def test_layer_tiny_q8_0(seed):
     _run_stack_and_compare(W.tiny_q8_0(seed=seed), 1, 1)
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_layer_wide_router(T):
+    """E=200 experts: T=1 ranks the 200 keys (ids above 128 read from the
+    expert table in the grouping), T=2 takes the per-wave radix select."""
+    _run_stack_and_compare(W.tiny_q8_0(seed=6).with_(E=200, k=6), 1, T)
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_layer_qwen3_shape_q4k(T):
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T), 1, T)
