@@ -482,6 +482,7 @@ __device__ __forceinline__ void topk_wave_any(const uint32_t *keys, int E, int k
 // partial ranks are summed with LDS atomics.  lc: LDS of T*ep 64-bit slots,
 // ep = E rounded up to 32; rank: LDS of T*E ints; lk: the T*E keys.
 constexpr int kRankKeys = 256;
+constexpr int kStageKeys = 4096;  // keys the route tail keeps in LDS
 
 // floor(i / d) for 0 <= i < 2^16, 1 <= d <= 2^16, with r = 1.0f/d: (i + 0.5)/d
 // is at least 0.5/d away from an integer, far more than the float error.
@@ -597,7 +598,7 @@ __device__ __forceinline__ void group_one(const int *sidx, int k, int E, int ns,
 // can miss.
 __device__ void route_tail(const RouteArgs &a)
 {
-    __shared__ uint32_t lk[kRankKeys];
+    __shared__ uint32_t lk[kStageKeys];
     __shared__ uint64_t lc[2 * kRankKeys];
     __shared__ int lrank[kRankKeys];
     __shared__ int sidx[kMaxT * kMaxK];
@@ -607,6 +608,7 @@ __device__ void route_tail(const RouteArgs &a)
     const int T = a.T, E = a.E, k = a.k, n = T * E;
     const int tid = (int)threadIdx.x, lane = lane_id();
     const bool ranks = n <= kRankKeys && T * ((E + 31) & ~31) <= 2 * kRankKeys;  // fits lk, lc
+    const bool staged = n <= kStageKeys;  // keys kept in LDS by the poll
 
     // pointer table entries lane + 64i for the grouping
     PrePtr pre{nullptr, nullptr, a.go.eptr != nullptr};
@@ -619,7 +621,7 @@ __device__ void route_tail(const RouteArgs &a)
         int missing = 0;
         for (int i = tid; i < n; i += kRouteThreads) {
             const uint32_t v = ld_coh_u(a.keys + i);
-            if (ranks) lk[i] = v;
+            if (staged) lk[i] = v;
             missing |= v == 0u;
         }
         if (!__syncthreads_or(missing)) break;
@@ -631,6 +633,9 @@ __device__ void route_tail(const RouteArgs &a)
     }
     if (ranks) {
         topk_ranks(lk, T, E, k, sidx, skey, lc, lrank);
+    } else if (staged) {
+        for (int t = wave_id(); t < T; t += kRouteThreads / 64)
+            topk_wave_any<false>(lk + t * E, E, k, sidx + t * k, skey + t * k);
     } else {
         for (int t = wave_id(); t < T; t += kRouteThreads / 64)
             topk_wave_any<true>(a.keys + (size_t)t * E, E, k, sidx + t * k, skey + t * k);
@@ -901,32 +906,49 @@ __device__ __forceinline__ XL xl(const uint8_t *rec, int K, int s)
 
 __device__ __forceinline__ int w4(const int4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 struct Q4KRegs { uint4 meta; uint4 q[8]; };
 struct Q6KRegs { uint4 ql[8]; uint4 qh[4]; uint4 sc; uint32_t d; };
 struct Q80Regs { uint4 q[16]; uint4 d; };
 
+// Loads from expert slots.  Slot addresses come from tables in memory, whose
+// address space the compiler cannot infer; these loads name the global
+// space, so that they compile to global (not flat) loads, which need not
+// wait for LDS traffic (flat loads may address LDS).
+typedef const __attribute__((address_space(1))) uint8_t gbyte;
+template <class T> __device__ __forceinline__ T ldg(const uint8_t *p, int off)
+{
+    return *(const __attribute__((address_space(1))) T *)((gbyte *)p + off);
+}
+template <> __device__ __forceinline__ uint4 ldg<uint4>(const uint8_t *p, int off)
+{
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)((gbyte *)p + off);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void load_regs(Q4KRegs &r, const uint8_t *tile, int lt)
 {
-    r.meta = *(const uint4 *)(tile + lt * 16);
+    r.meta = ldg<uint4>(tile, lt * 16);
 #pragma unroll
-    for (int j = 0; j < 8; j++) r.q[j] = *(const uint4 *)(tile + 1024 + j * 1024 + lt * 16);
+    for (int j = 0; j < 8; j++) r.q[j] = ldg<uint4>(tile, 1024 + j * 1024 + lt * 16);
 }
 
 __device__ __forceinline__ void load_regs(Q6KRegs &r, const uint8_t *tile, int lt)
 {
 #pragma unroll
-    for (int j = 0; j < 8; j++) r.ql[j] = *(const uint4 *)(tile + j * 1024 + lt * 16);
+    for (int j = 0; j < 8; j++) r.ql[j] = ldg<uint4>(tile, j * 1024 + lt * 16);
 #pragma unroll
-    for (int j = 0; j < 4; j++) r.qh[j] = *(const uint4 *)(tile + 8192 + j * 1024 + lt * 16);
-    r.sc = *(const uint4 *)(tile + 12288 + lt * 16);
-    r.d = *(const unsigned short *)(tile + 13312 + lt * 2);
+    for (int j = 0; j < 4; j++) r.qh[j] = ldg<uint4>(tile, 8192 + j * 1024 + lt * 16);
+    r.sc = ldg<uint4>(tile, 12288 + lt * 16);
+    r.d = ldg<unsigned short>(tile, 13312 + lt * 2);
 }
 
 __device__ __forceinline__ void load_regs(Q80Regs &r, const uint8_t *tile, int lt)
 {
 #pragma unroll
-    for (int j = 0; j < 16; j++) r.q[j] = *(const uint4 *)(tile + j * 1024 + lt * 16);
-    r.d = *(const uint4 *)(tile + 16384 + lt * 16);
+    for (int j = 0; j < 16; j++) r.q[j] = ldg<uint4>(tile, j * 1024 + lt * 16);
+    r.d = ldg<uint4>(tile, 16384 + lt * 16);
 }
 
 __device__ __forceinline__ float fpieces(int a0, int a1, int a2)
@@ -1135,10 +1157,11 @@ struct GateUpArgs {
 };
 
 constexpr int kGUThreads = 512;
-constexpr int kTokPass = 4;
+constexpr int kTokPass = 4;  // <= kInlineTok
 constexpr int kGULds = 32768;   // staged token records per pass
 constexpr int kDnLds = 24576;   // staged pair records per pass
 constexpr int kDnPass = 8;
+constexpr int kDnPre = 4;       // record words per thread loaded before the weights
 
 template <int QT>
 __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gate_up(GateUpArgs a)
@@ -1161,16 +1184,43 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const int tile64 = row >> 6, lt = row & 63;
     const uint8_t *mat = base + (m ? a.up_off : 0);
 
-    typename RegsOf<QT>::T rg[1];
-    int loaded = -1;
-    if (slot < S) {  // issue the first K-group's weights before staging the tokens
-        load_regs(rg[0], mat + ((size_t)tile64 * S + slot) * kTileBytes<QT>, lt);
-        loaded = slot;
+    // The first pass's token records are loaded before the weights: loads
+    // complete in order, so the barrier after staging them does not wait for
+    // the weights, and each wave starts its dots as soon as its own weights
+    // arrive.
+    const int nt0 = p1 - p0 < a.tpass ? p1 - p0 : a.tpass;
+    const int q16 = (int)(RB / 16);  // 16-byte words per record
+    const float rq16 = 1.0f / (float)q16;
+    uint64_t toks;
+    __builtin_memcpy(&toks, we.tok, sizeof(toks));
+    u32x4 xr[kGULds / 16 / kGUThreads];
+#pragma unroll
+    for (int q = 0; q < kGULds / 16 / kGUThreads; q++) {
+        // unconditional loads (clamped index): no per-word branches, whose
+        // merges would wait for each load
+        const int i = min((int)threadIdx.x + q * kGUThreads, nt0 * q16 - 1);
+        const int tt = fdiv(i, rq16);  // < tpass <= kInlineTok: an inline token
+        const int tok = (int)((toks >> (8 * tt)) & 0xff);
+        xr[q] = ((const u32x4 *)rec_at(a.x, tok, H))[i - tt * q16];
     }
+    // the first K-group's weights, loaded unconditionally (slots past S
+    // load K-group 0 and leave it unused) so that the waits for the records
+    // above count these loads as still in flight
+    typename RegsOf<QT>::T rg[1];
+    load_regs(rg[0], mat + ((size_t)tile64 * S + (slot < S ? slot : 0)) * kTileBytes<QT>, lt);
+    int loaded = slot < S ? slot : -1;
     for (int c0 = p0; c0 < p1; c0 += a.tpass) {
         const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
-        if (c0 != p0) __syncthreads();  // the previous pass is done with xs
-        for (int tt = 0; tt < nt; tt++) stage16(xs + tt * RB, rec_at(a.x, token_of(we, a.ptok, c0 + tt), H), RB);
+        if (c0 == p0) {
+#pragma unroll
+            for (int q = 0; q < kGULds / 16 / kGUThreads; q++) {
+                const int i = (int)threadIdx.x + q * kGUThreads;
+                if (i < nt0 * q16) ((u32x4 *)xs)[i] = xr[q];
+            }
+        } else {
+            __syncthreads();  // the previous pass is done with xs
+            for (int tt = 0; tt < nt; tt++) stage16(xs + tt * RB, rec_at(a.x, token_of(we, a.ptok, c0 + tt), H), RB);
+        }
         __syncthreads();
         // each lane owns part[slot][*][r]: plain writes for its first K-group, sums after
         for (int s = slot; s < S; s += 8) {
@@ -1238,7 +1288,7 @@ __device__ __forceinline__ void add_to(float *p, float v)
 }
 
 template <int QT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_down(DownArgs a)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3))) void k_down(DownArgs a)
 {
     extern __shared__ __align__(16) uint8_t hsl[];
     __shared__ float part[8][kDnPass][64];
@@ -1255,16 +1305,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int nwv = (int)(blockDim.x >> 6);
     const int wv = wave_id(), lane = lane_id();
 
+    // The first pass's pair records (contiguous), up to kDnPre words per
+    // thread, are loaded before the weights, as in k_gate_up: the wait for
+    // them before the barrier then leaves the weights in flight, and each
+    // wave starts its dots as soon as its own weights arrive.  Words past
+    // kDnPre are staged after the barrier.
+    const int n16 = (int)((p1 - p0 < a.tpass ? p1 - p0 : a.tpass) * RB / 16);
+    const u32x4 *h16 = (const u32x4 *)rec_at(a.h, p0, kd);
+    u32x4 hr[kDnPre];
+#pragma unroll
+    for (int q = 0; q < kDnPre; q++) hr[q] = h16[min((int)threadIdx.x + q * (int)blockDim.x, n16 - 1)];
+    // blockDim = 64 * min(S, 8): every wave has a K-group (loaded
+    // unconditionally, for the same reason as in k_gate_up)
     typename RegsOf<QT>::T rg[1];
-    int loaded = -1;
-    if (wv < S) {
-        load_regs(rg[0], base + ((size_t)rt * S + wv) * kTileBytes<QT>, lane);
-        loaded = wv;
-    }
+    load_regs(rg[0], base + ((size_t)rt * S + wv) * kTileBytes<QT>, lane);
+    int loaded = wv;
     for (int c0 = p0; c0 < p1; c0 += a.tpass) {
         const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
-        if (c0 != p0) __syncthreads();
-        stage16(hsl, rec_at(a.h, c0, kd), nt * RB);  // the expert's pairs are contiguous
+        if (c0 == p0) {
+#pragma unroll
+            for (int q = 0; q < kDnPre; q++) {
+                const int i = (int)threadIdx.x + q * (int)blockDim.x;
+                if (i < n16) ((u32x4 *)hsl)[i] = hr[q];
+            }
+            for (int i = (int)threadIdx.x + kDnPre * (int)blockDim.x; i < n16; i += blockDim.x)
+                ((u32x4 *)hsl)[i] = h16[i];
+        } else {
+            __syncthreads();
+            stage16(hsl, rec_at(a.h, c0, kd), nt * RB);  // the expert's pairs are contiguous
+        }
         __syncthreads();
         for (int s = wv; s < S; s += nwv) {
             if (s != loaded) {
