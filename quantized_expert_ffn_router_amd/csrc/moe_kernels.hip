@@ -554,30 +554,109 @@ struct RouteArgs {
     int n_expert_blocks;    // router workgroups; then T * H/256 encoding workgroups, then the tail
 };
 
-// Grouping of one token's k distinct selections (T = 1), by wave 0: the
-// selection of the j-th smallest id is pair and distinct expert j.  Same
-// outputs as group_block.
-__device__ __forceinline__ void group_one(const int *sidx, int k, int E, int ns, GroupOut g, PrePtr pre)
+// Single-token routing tail, by wave 0 alone (no barriers).  The wave polls
+// the E keys into registers (lane l holds experts l + 64i), takes tau, the
+// k-th largest of the 64 per-lane maxima (bitonic sort across the lanes):
+// at least k keys are >= tau, so the top k are among the keys >= tau, and
+// usually only a few more.  Those candidates, as 64-bit C = key << 32 | ~e
+// (unique, ordered like the key with ties to the lower id), are ranked
+// against each other in LDS; rank r < k is selection r.  Softmax over the k
+// selected logits and the grouping (selection j is pair and distinct expert
+// pos_j, its position among the k ids in ascending order) follow in the same
+// wave.  cand: LDS of at least E + 8 64-bit slots.
+template <int NVL>
+__device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *cand, PrePtr pre)
 {
-    if (wave_id() != 0) return;
-    const int lane = lane_id();
-    const int e = lane < k ? sidx[lane] : 0;
-    // table entries of e from the lanes that loaded them (all lanes take part)
-    const long long q0 = __shfl((long long)pre.p0, e & 63, 64);
-    const long long q1 = __shfl((long long)pre.p1, e & 63, 64);
+    const int E = a.E, k = a.k, ns = a.ns, lane = lane_id();
+    uint32_t key[NVL];
+    int ok = 1;
+    for (unsigned it = 0;; it++) {
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? ld_coh_u(a.keys + e) : 0u;
+            missing |= e < E && key[i] == 0u;
+        }
+        if (!__ballot(missing)) break;
+        if (it >= kSpinLimit) {
+            ok = 0;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    // tau: the k-th largest lane maximum (bitonic sort, descending across lanes)
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; i++) v = max(v, key[i]);
+#pragma unroll
+    for (int k2 = 2; k2 <= 64; k2 <<= 1)
+#pragma unroll
+        for (int j = k2 >> 1; j > 0; j >>= 1) {
+            const uint32_t p = (uint32_t)__shfl_xor((int)v, j, 64);
+            v = (((lane & j) == 0) == ((lane & k2) == 0)) ? max(v, p) : min(v, p);
+        }
+    const uint32_t tau = (uint32_t)__shfl((int)v, k - 1, 64);
+    // candidates >= tau, compacted into cand[0, m), zero padding after
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; i++) {
+        const int e = lane + 64 * i;
+        const bool c = e < E && key[i] >= tau;
+        const uint64_t bal = __ballot(c);
+        if (c) cand[m + below(bal)] = (uint64_t)key[i] << 32 | (uint32_t)~e;
+        m += __popcll(bal);
+    }
+    if (lane < 8) cand[m + lane] = 0ull;
+    const int mp = (m + 7) & ~7;
+    // exact ranks among the candidates; lane r < k then holds selection r in sel
+    uint64_t *sel = cand + ((E + 8 + 1) & ~1);
+    for (int c = lane; c < m; c += 64) {
+        const uint64_t ci = cand[c];
+        int r0 = 0, r1 = 0;
+        for (int c2 = 0; c2 < mp; c2 += 8) {
+            const ulonglong2 *q = (const ulonglong2 *)(cand + c2);
+            const ulonglong2 x0 = q[0], x1 = q[1], x2 = q[2], x3 = q[3];
+            r0 += (x0.x > ci) + (x0.y > ci) + (x1.x > ci) + (x1.y > ci);
+            r1 += (x2.x > ci) + (x2.y > ci) + (x3.x > ci) + (x3.y > ci);
+        }
+        if (r0 + r1 < k) sel[r0 + r1] = ci;
+    }
+    const uint64_t cs = lane < k ? sel[lane] : 0ull;
+    const int id = (int)~(uint32_t)cs;
+    // softmax over the k selected logits
+    const float lg = lane < k ? unord_bits((uint32_t)(cs >> 32)) : 0.f;
+    const float top = __shfl(lg, 0, 64);
+    const float ex = lane < k ? expf(lg - top) : 0.f;
+    const float wsum = wave_sum(ex);
+    const float wj = ok ? ex / wsum : __builtin_nanf("");
+    // clear the keys for the next launch (plain stores: the launch boundary
+    // makes them visible)
+#pragma unroll
+    for (int i = 0; i < NVL; i++)
+        if (lane + 64 * i < E) a.keys[lane + 64 * i] = 0u;
+    // grouping: position of each id among the k ids in ascending order
+    const int idl = lane < k ? id : 0x7fffffff;
     int pos = 0;
-    for (int q = 0; q < k; q++) pos += __shfl(e, q, 64) < e;
+    for (int q = 0; q < k; q++) pos += __shfl(idl, q, 64) < idl;
+    const long long q0 = __shfl((long long)pre.p0, id & 63, 64);
+    const long long q1 = __shfl((long long)pre.p1, id & 63, 64);
+    GroupOut g = a.go;
     if (lane < k) {
+        a.idx[lane] = id;
+        a.w[lane] = wj;
+        if (a.idx2) a.idx2[lane] = id;
+        if (a.w2) a.w2[lane] = wj;
         WorkEntry we{};
-        we.e = e; we.p0 = pos; we.p1 = pos + 1;
-        we.ptr = !g.eptr                     ? nullptr
-                 : (pre.valid && e < 64)     ? (const void *)q0
-                 : (pre.valid && e < 128)    ? (const void *)q1
-                                             : g.eptr[e];
+        we.e = id; we.p0 = pos; we.p1 = pos + 1;
+        we.ptr = !g.eptr                 ? nullptr
+                 : (pre.valid && id < 64)  ? (const void *)q0
+                 : (pre.valid && id < 128) ? (const void *)q1
+                                           : g.eptr[id];
         g.wt[pos] = we;  // tok[] all zero: token 0
         g.ptok[pos] = 0;
         g.inv[lane] = pos;
-        if (g.pw) g.pw[pos] = g.wsrc[lane];
+        g.pw[pos] = wj;
     }
     if (lane < ns) {
         WorkEntry we{};
@@ -586,19 +665,20 @@ __device__ __forceinline__ void group_one(const int *sidx, int k, int E, int ns,
         g.wt[k + lane] = we;
         g.ptok[k + lane] = 0;
         g.inv[k + lane] = k + lane;
-        if (g.pw) g.pw[k + lane] = 1.0f;
+        g.pw[k + lane] = 1.0f;
     }
     for (int u = k + ns + lane; u < g.Umax; u += 64) g.wt[u] = WorkEntry{};
     if (lane == 0) *g.nuniq = k + ns;
 }
 
-// The tail workgroup: polls the keys until every one is written, then top-k
-// (clearing the keys for the next launch), softmax and grouping.  A poll that
+// The tail workgroup: a single token goes to route_tail_one; otherwise the
+// workgroup polls the keys until every one is written, then top-k (clearing
+// the keys for the next launch), softmax and grouping.  A poll that
 // gives up after kSpinLimit rounds routes with NaN weights, which no caller
 // can miss.
-__device__ void route_tail(const RouteArgs &a)
+__device__ __forceinline__ void route_tail(const RouteArgs &a)
 {
-    __shared__ uint32_t lk[kStageKeys];
+    __shared__ __align__(16) uint32_t lk[kStageKeys];
     __shared__ uint64_t lc[2 * kRankKeys];
     __shared__ int lrank[kRankKeys];
     __shared__ int sidx[kMaxT * kMaxK];
@@ -615,6 +695,17 @@ __device__ void route_tail(const RouteArgs &a)
     if (a.go.eptr && wave_id() == 0) {
         if (lane < E) pre.p0 = a.go.eptr[lane];
         if (64 + lane < E) pre.p1 = a.go.eptr[64 + lane];
+    }
+    if (T == 1 && a.group) {
+        if (wave_id() != 0) return;
+        static_assert(kMaxE + 9 + kMaxK <= kStageKeys / 2, "candidate slots");
+        uint64_t *cand = (uint64_t *)lk;  // E + 9 + k slots
+        if (E <= 64) route_tail_one<1>(a, cand, pre);
+        else if (E <= 128) route_tail_one<2>(a, cand, pre);
+        else if (E <= 256) route_tail_one<4>(a, cand, pre);
+        else if (E <= 512) route_tail_one<8>(a, cand, pre);
+        else route_tail_one<16>(a, cand, pre);
+        return;
     }
     int ok = 1;
     for (unsigned it = 0;; it++) {
@@ -663,13 +754,8 @@ __device__ void route_tail(const RouteArgs &a)
     if (!a.group) return;
     GroupOut go = a.go;
     go.wsrc = sw;
-    if (T == 1) {
-        // wave 0 wrote its own token's sidx / sw above
-        group_one(sidx, k, E, a.ns, go, pre);
-    } else {
-        __syncthreads();
-        group_block(sidx, T, k, E, a.ns, go, lstart, pre);
-    }
+    __syncthreads();
+    group_block(sidx, T, k, E, a.ns, go, lstart, pre);
 }
 
 // Router workgroup: 2 router rows against all T tokens, the 4 waves
