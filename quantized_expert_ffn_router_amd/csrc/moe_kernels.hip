@@ -1059,38 +1059,31 @@ __device__ __forceinline__ void kgroup_dot(const Q4KRegs (&r)[NM], const XL &X, 
         accm[m] = 0.f;
     }
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-        // words 16c..16c+7 (sub-block 2c) and 16c+8..16c+15 (sub-block 2c+1) of each piece
-        const int4 x0a = X.q0[4 * c], x0b = X.q0[4 * c + 1], x0c = X.q0[4 * c + 2], x0d = X.q0[4 * c + 3];
-        const int4 x1a = X.q1[4 * c], x1b = X.q1[4 * c + 1], x1c = X.q1[4 * c + 2], x1d = X.q1[4 * c + 3];
-        const int4 x2a = X.q2[4 * c], x2b = X.q2[4 * c + 1], x2c = X.q2[4 * c + 2], x2d = X.q2[4 * c + 3];
-        const float bs0 = X.bs[2 * c], bs1 = X.bs[2 * c + 1];
-        const float bm0 = X.bsum[2 * c], bm1 = X.bsum[2 * c + 1];
+    for (int sb = 0; sb < 8; sb++) {
+        // sub-block sb: the low (even sb) or high (odd sb) nibbles of q words
+        // 8(sb/2) .. 8(sb/2)+7, against words 8sb .. 8sb+7 of each piece
+        const int c = sb >> 1;
+        const int4 x0a = X.q0[2 * sb], x0b = X.q0[2 * sb + 1];
+        const int4 x1a = X.q1[2 * sb], x1b = X.q1[2 * sb + 1];
+        const int4 x2a = X.q2[2 * sb], x2b = X.q2[2 * sb + 1];
+        const float bsv = X.bs[sb], bmv = X.bsum[sb];
 #pragma unroll
         for (int m = 0; m < NM; m++) {
             const uint32_t scw = c < 2 ? sclo[m] : schi[m];
             const uint32_t mw = c < 2 ? mlo[m] : mhi[m];
-            const int sh0 = 8 * ((2 * c) & 3), sh1 = 8 * ((2 * c + 1) & 3);
-            const int sc0 = (scw >> sh0) & 0xff, sc1 = (scw >> sh1) & 0xff;
-            const int m0 = (mw >> sh0) & 0xff, m1 = (mw >> sh1) & 0xff;
-            int a0 = 0, a1 = 0, a2 = 0, b0 = 0, b1 = 0, b2 = 0;
+            const int sh = 8 * (sb & 3);
+            const int sc = (scw >> sh) & 0xff, mn = (mw >> sh) & 0xff;
+            int a0 = 0, a1 = 0, a2 = 0;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const uint32_t qd = comp(r[m].q[2 * c + (i >> 2)], i & 3);
-                const uint32_t lo = qd & 0x0F0F0F0Fu;
-                const uint32_t hi = (qd >> 4) & 0x0F0F0F0Fu;
-                const int xl0 = i < 4 ? w4(x0a, i) : w4(x0b, i - 4), xh0 = i < 4 ? w4(x0c, i) : w4(x0d, i - 4);
-                const int xl1 = i < 4 ? w4(x1a, i) : w4(x1b, i - 4), xh1 = i < 4 ? w4(x1c, i) : w4(x1d, i - 4);
-                const int xl2 = i < 4 ? w4(x2a, i) : w4(x2b, i - 4), xh2 = i < 4 ? w4(x2c, i) : w4(x2d, i - 4);
-                a0 = dot4(lo, xl0, a0);
-                a1 = dot4(lo, xl1, a1);
-                a2 = dot4(lo, xl2, a2);
-                b0 = dot4(hi, xh0, b0);
-                b1 = dot4(hi, xh1, b1);
-                b2 = dot4(hi, xh2, b2);
+                const uint32_t nib = (sb & 1) ? (qd >> 4) & 0x0F0F0F0Fu : qd & 0x0F0F0F0Fu;
+                a0 = dot4(nib, i < 4 ? w4(x0a, i) : w4(x0b, i - 4), a0);
+                a1 = dot4(nib, i < 4 ? w4(x1a, i) : w4(x1b, i - 4), a1);
+                a2 = dot4(nib, i < 4 ? w4(x2a, i) : w4(x2b, i - 4), a2);
             }
-            acc[m] += (float)sc0 * (bs0 * fpieces(a0, a1, a2)) + (float)sc1 * (bs1 * fpieces(b0, b1, b2));
-            accm[m] += (float)m0 * bm0 + (float)m1 * bm1;
+            acc[m] += (float)sc * (bsv * fpieces(a0, a1, a2));
+            accm[m] += (float)mn * bmv;
         }
     }
 #pragma unroll
@@ -1244,13 +1237,14 @@ struct GateUpArgs {
 
 constexpr int kGUThreads = 512;
 constexpr int kTokPass = 4;  // <= kInlineTok
+constexpr int kGUPre = 2;     // record words per thread loaded before the weights
 constexpr int kGULds = 32768;   // staged token records per pass
 constexpr int kDnLds = 24576;   // staged pair records per pass
 constexpr int kDnPass = 8;
 constexpr int kDnPre = 4;       // record words per thread loaded before the weights
 
 template <int QT>
-__global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gate_up(GateUpArgs a)
+__global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 2))) void k_gate_up(GateUpArgs a)
 {
     extern __shared__ __align__(16) uint8_t xs[];
     __shared__ float part[8][kTokPass][32][2];
@@ -1270,18 +1264,18 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const int tile64 = row >> 6, lt = row & 63;
     const uint8_t *mat = base + (m ? a.up_off : 0);
 
-    // The first pass's token records are loaded before the weights: loads
-    // complete in order, so the barrier after staging them does not wait for
-    // the weights, and each wave starts its dots as soon as its own weights
-    // arrive.
+    // The first pass's token records (up to kGUPre words per thread, the
+    // rest after) are loaded before the weights: loads complete in order, so
+    // the barrier after staging them does not wait for the weights, and each
+    // wave starts its dots as soon as its own weights arrive.
     const int nt0 = p1 - p0 < a.tpass ? p1 - p0 : a.tpass;
     const int q16 = (int)(RB / 16);  // 16-byte words per record
     const float rq16 = 1.0f / (float)q16;
     uint64_t toks;
     __builtin_memcpy(&toks, we.tok, sizeof(toks));
-    u32x4 xr[kGULds / 16 / kGUThreads];
+    u32x4 xr[kGUPre];
 #pragma unroll
-    for (int q = 0; q < kGULds / 16 / kGUThreads; q++) {
+    for (int q = 0; q < kGUPre; q++) {
         // unconditional loads (clamped index): no per-word branches, whose
         // merges would wait for each load
         const int i = min((int)threadIdx.x + q * kGUThreads, nt0 * q16 - 1);
@@ -1299,9 +1293,13 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(2)))
         const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
         if (c0 == p0) {
 #pragma unroll
-            for (int q = 0; q < kGULds / 16 / kGUThreads; q++) {
+            for (int q = 0; q < kGUPre; q++) {
                 const int i = (int)threadIdx.x + q * kGUThreads;
                 if (i < nt0 * q16) ((u32x4 *)xs)[i] = xr[q];
+            }
+            for (int i = (int)threadIdx.x + kGUPre * kGUThreads; i < nt0 * q16; i += kGUThreads) {
+                const int tt = fdiv(i, rq16);
+                ((u32x4 *)xs)[i] = ((const u32x4 *)rec_at(a.x, (int)((toks >> (8 * tt)) & 0xff), H))[i - tt * q16];
             }
         } else {
             __syncthreads();  // the previous pass is done with xs
@@ -1374,7 +1372,7 @@ __device__ __forceinline__ void add_to(float *p, float v)
 }
 
 template <int QT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(3))) void k_down(DownArgs a)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 3))) void k_down(DownArgs a)
 {
     extern __shared__ __align__(16) uint8_t hsl[];
     __shared__ float part[8][kDnPass][64];
