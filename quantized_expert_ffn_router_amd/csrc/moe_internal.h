@@ -88,8 +88,13 @@ constexpr size_t kKeysBytes = (size_t)kMaxT * kMaxE * 4;
 // per-16-position integer sums of each piece ps[3][K/16] (int32).
 constexpr size_t enc_bytes(int K) { return (size_t)4 * K; }
 
+// Pairs per work item of the VALU FFN kernels: an expert with more pairs is
+// cut into several items, so that its row tiles' token passes run in
+// parallel workgroups.
+constexpr int kItemTok = 4;
+
 struct WsLayout {
-    int T, k, E, ns, H, kd, P, U;
+    int T, k, E, ns, H, kd, P, U, UI;  // U: distinct experts, UI: work items (both at most)
     size_t keys, xenc, xhat, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
 };
 
@@ -102,6 +107,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.P = T * (k + ns);
     int ur = E < T * k ? E : T * k;
     L.U = ur + ns;
+    L.UI = L.U + (L.P + kItemTok - 1) / kItemTok;
     L.keys = kKeys;
     size_t o = kKeys + kKeysBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -110,7 +116,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
     L.nuniq = take(4);
-    L.wt = take((size_t)L.U * 32);
+    L.wt = take((size_t)L.UI * 32);
     L.ptok = take((size_t)L.P * 4);
     L.inv = take((size_t)L.P * 4);
     L.pw = take((size_t)L.P * 4);

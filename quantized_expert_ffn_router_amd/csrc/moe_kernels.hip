@@ -235,7 +235,7 @@ struct WorkEntry {
 };
 
 struct GroupOut {
-    int *nuniq;           // distinct experts (workspace)
+    int *nuniq;           // work-table entries in use (workspace)
     WorkEntry *wt;        // [Umax]; entries past nuniq are empty (p0 == p1)
     int Umax;
     int *ptok;            // [P] token of each grouped pair
@@ -244,6 +244,7 @@ struct GroupOut {
     int *count, *offset, *pairs;  // moe_group_tokens outputs (may be null)
     float *pw;            // [P] combine weight of each grouped pair, or null
     const float *wsrc;    // [T][k] routing weights the pair weights are taken from
+    int chunk;            // > 0: work items of at most `chunk` pairs; 0: one entry per expert
 };
 
 // Expert-table entries lane and 64 + lane, which the router's wave 0 loads
@@ -279,31 +280,36 @@ __device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupO
             const int e = base + lane;
             const uint32_t m = e < E ? (uint32_t)lmask[e] : 0u;
             const int cnt = __popc(m);
+            const int chunk = g.chunk > 0 ? g.chunk : (cnt > 0 ? cnt : 1);
+            const int nit = (cnt + chunk - 1) / chunk;  // work items of the expert
             const int incl = wave_incl_scan(cnt);
-            const int uincl = wave_incl_scan(cnt > 0);
+            const int iincl = wave_incl_scan(nit);
             const int off = run + incl - cnt;
-            const int ui = nu + uincl - (cnt > 0);
+            const int ui = nu + iincl - nit;
             if (g.count && e < E) g.count[e] = cnt;
             if (g.offset && e < E) g.offset[e] = off;
             if (cnt > 0 && g.wt) {
-                WorkEntry we{};
-                we.e = e; we.p0 = off; we.p1 = off + cnt;
-                we.ptr = !g.eptr                     ? nullptr
-                         : (pre.valid && base == 0)  ? pre.p0
-                         : (pre.valid && base == 64) ? pre.p1
-                                                     : g.eptr[e];
-                uint64_t toks = 0;
-                uint32_t mm = m;
-                for (int i = 0; i < kInlineTok && mm; i++) {
-                    const int t = __ffs(mm) - 1;
-                    toks |= (uint64_t)t << (8 * i);
-                    mm &= mm - 1;
+                const void *ptr = !g.eptr                     ? nullptr
+                                  : (pre.valid && base == 0)  ? pre.p0
+                                  : (pre.valid && base == 64) ? pre.p1
+                                                              : g.eptr[e];
+                uint32_t mm = m;  // the expert's tokens, ascending
+                for (int it = 0; it < nit; it++) {
+                    WorkEntry we{};
+                    we.e = e; we.p0 = off + it * chunk; we.p1 = min(off + (it + 1) * chunk, off + cnt);
+                    we.ptr = ptr;
+                    uint64_t toks = 0;
+                    for (int i = 0; i < chunk && mm; i++) {
+                        const int t = __ffs(mm) - 1;
+                        if (i < kInlineTok) toks |= (uint64_t)t << (8 * i);
+                        mm &= mm - 1;
+                    }
+                    __builtin_memcpy(we.tok, &toks, sizeof(toks));
+                    g.wt[ui + it] = we;
                 }
-                __builtin_memcpy(we.tok, &toks, sizeof(toks));
-                g.wt[ui] = we;
             }
             run += __shfl(incl, 63, 64);
-            nu += __shfl(uincl, 63, 64);
+            nu += __shfl(iincl, 63, 64);
             if (e < E) lmask[E + e] = off;
         }
         if (lane == 0) { s_nu = nu; s_valid = run; }
@@ -327,15 +333,19 @@ __device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupO
     }
     if (g.offset && threadIdx.x == 0) g.offset[E] = nvalid;
     if (g.wt) {
-        for (int s2 = threadIdx.x; s2 < ns; s2 += blockDim.x) {
+        // shared expert s2: pairs nvalid + s2*T + t, cut into items like the routed ones
+        const int sc = g.chunk > 0 ? g.chunk : T;
+        const int sit = (T + sc - 1) / sc;
+        for (int i = threadIdx.x; i < ns * sit; i += blockDim.x) {
+            const int s2 = i / sit, it = i - s2 * sit;
             WorkEntry we{};
-            we.e = E + s2; we.p0 = nvalid + s2 * T; we.p1 = nvalid + (s2 + 1) * T;
+            we.e = E + s2; we.p0 = nvalid + s2 * T + it * sc; we.p1 = nvalid + s2 * T + min((it + 1) * sc, T);
             we.ptr = g.eptr ? g.sptr[s2] : nullptr;
-            for (int i = 0; i < kInlineTok; i++) we.tok[i] = (uint8_t)i;
-            g.wt[nu + s2] = we;
+            for (int q = 0; q < kInlineTok; q++) we.tok[q] = (uint8_t)(it * sc + q);
+            g.wt[nu + i] = we;
         }
-        for (int u = nu + ns + threadIdx.x; u < g.Umax; u += blockDim.x) g.wt[u] = WorkEntry{};
-        if (threadIdx.x == 0) *g.nuniq = nu + ns;
+        for (int u = nu + ns * sit + threadIdx.x; u < g.Umax; u += blockDim.x) g.wt[u] = WorkEntry{};
+        if (threadIdx.x == 0) *g.nuniq = nu + ns * sit;
     }
     if (g.ptok) {
         for (int i = threadIdx.x; i < ns * T; i += blockDim.x) {
@@ -1845,12 +1855,15 @@ struct Ws {
     template <class T> T *at(size_t off) const { return (T *)(b + off); }
     Enc x() const { return Enc{at<uint8_t>(L.xenc)}; }
     Enc h() const { return Enc{at<uint8_t>(L.henc)}; }
-    GroupOut group() const
+    // items: the VALU FFN kernels' work items (kItemTok pairs at most),
+    // else one entry per distinct expert (MFMA kernels)
+    GroupOut group(bool items) const
     {
         GroupOut g{};
         g.nuniq = at<int>(L.nuniq);
         g.wt = at<WorkEntry>(L.wt);
-        g.Umax = L.U;
+        g.Umax = items ? L.UI : L.U;
+        g.chunk = items ? kItemTok : 0;
         g.ptok = at<int>(L.ptok);
         g.inv = at<int>(L.inv);
         g.pw = at<float>(L.pw);
@@ -1953,7 +1966,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     ga.tpass = (int)(kGULds / enc_bytes(d.H));
     if (ga.tpass > kTokPass) ga.tpass = kTokPass;
     const size_t glds = (size_t)ga.tpass * enc_bytes(d.H);
-    dim3 ggrid(L.U * ga.ntile);
+    dim3 ggrid(L.UI * ga.ntile);
     switch (d.gate) {
     case MOE_Q4_K: k_gate_up<MOE_Q4_K><<<ggrid, kGUThreads, glds, s>>>(ga); break;
     case MOE_Q6_K: k_gate_up<MOE_Q6_K><<<ggrid, kGUThreads, glds, s>>>(ga); break;
@@ -1972,7 +1985,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     da.tpass = (int)(kDnLds / enc_bytes(g.kd));
     if (da.tpass > kDnPass) da.tpass = kDnPass;
     const size_t dlds = (size_t)da.tpass * enc_bytes(g.kd);
-    dim3 dgrid(L.U * da.nrt), dblock(64 * (S < 8 ? S : 8));
+    dim3 dgrid(L.UI * da.nrt), dblock(64 * (S < 8 ? S : 8));
     switch (d.down) {
     case MOE_Q4_K: k_down<MOE_Q4_K><<<dgrid, dblock, dlds, s>>>(da); break;
     case MOE_Q6_K: k_down<MOE_Q6_K><<<dgrid, dblock, dlds, s>>>(da); break;
@@ -2057,7 +2070,7 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     PrepArgs pa{};
     pa.x = x; pa.T = T; pa.H = d->H; pa.k = k; pa.E = E; pa.ns = n_shared; pa.idx = idx; pa.w = w;
     pa.yzero = accumulate ? nullptr : y;
-    pa.xe = W.x(); pa.go = W.group(); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
+    pa.xe = W.x(); pa.go = W.group(!use_mfma(*d, T)); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
@@ -2083,7 +2096,7 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
     a.x = W.x();
     a.xhat = use_mfma(*d, T) ? W.at<float>(W.L.xhat) : nullptr;
-    a.group = 1; a.ns = n_shared; a.go = W.group();
+    a.group = 1; a.ns = n_shared; a.go = W.group(!use_mfma(*d, T));
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
     a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows;
