@@ -261,7 +261,7 @@ struct PrePtr { const void *p0, *p1; bool valid; };
 // A token that names one expert in two slots gets one pair, which both slots
 // point at (its output then carries the sum of their weights).
 // `lmask` is LDS of at least E ints; wave 0 scans.
-__device__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupOut g, int *lmask,
+__device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E, int ns, GroupOut g, int *lmask,
                             PrePtr pre /* this lane's table entries lane and 64 + lane, if valid */)
 {
     __shared__ int s_nu, s_valid;
@@ -482,60 +482,12 @@ __device__ __forceinline__ void topk_wave_any(const uint32_t *keys, int E, int k
     else topk_wave<16, GLOBAL>(keys, E, k, sidx, skey);
 }
 
-// Top-k of every token by ranks, for T*E <= kRankKeys: key e of token t
-// becomes the 64-bit C = key << 32 | ~e (unique, ordered like the key with
-// ties to the lower id), its rank is the number of its token's C_j above
-// it, and a key of rank r < k is selection r of its token (same order and
-// ties as topk_wave).  Each thread compares one key with 32 of its token's
-// keys at a time (zero padding up to a multiple of 32 ranks below every key;
-// a thread's key and chunk are (w mod n, w div n) for work item w);
-// partial ranks are summed with LDS atomics.  lc: LDS of T*ep 64-bit slots,
-// ep = E rounded up to 32; rank: LDS of T*E ints; lk: the T*E keys.
-constexpr int kRankKeys = 256;
 constexpr int kStageKeys = 4096;  // keys the route tail keeps in LDS
+constexpr int kWaveTopE = 256;    // experts for the per-wave topk_one (4 keys per lane)
 
 // floor(i / d) for 0 <= i < 2^16, 1 <= d <= 2^16, with r = 1.0f/d: (i + 0.5)/d
 // is at least 0.5/d away from an integer, far more than the float error.
 __device__ __forceinline__ int fdiv(int i, float r) { return (int)(((float)i + 0.5f) * r); }
-
-__device__ __forceinline__ void topk_ranks(const uint32_t *lk, int T, int E, int k, int *sidx, uint32_t *skey,
-                                           uint64_t *lc, int *rank)
-{
-    const int tid = (int)threadIdx.x, n = T * E;
-    const int ep = (E + 31) & ~31, nch = ep >> 5;
-    const float rE = 1.0f / (float)E, rep = 1.0f / (float)ep, rn = 1.0f / (float)n;
-    for (int i = tid; i < T * ep; i += blockDim.x) {
-        const int t = fdiv(i, rep), e = i - t * ep;
-        lc[i] = e < E ? (uint64_t)lk[t * E + e] << 32 | (uint32_t)~e : 0ull;
-    }
-    for (int i = tid; i < n; i += blockDim.x) rank[i] = 0;
-    __syncthreads();
-    for (int w = tid; w < n * nch; w += blockDim.x) {
-        // consecutive threads take consecutive keys against the same chunk:
-        // a wave's LDS reads are broadcasts of one address
-        const int c = fdiv(w, rn), i = w - c * n;
-        const int t = fdiv(i, rE), e = i - t * E;
-        const uint64_t ci = lc[t * ep + e];
-        const ulonglong2 *row = (const ulonglong2 *)(lc + t * ep + 32 * c);
-        int r0 = 0, r1 = 0;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            const ulonglong2 v = row[j];
-            r0 += v.x > ci;
-            r1 += v.y > ci;
-        }
-        atomicAdd(&rank[i], r0 + r1);
-    }
-    __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x) {
-        const int r = rank[i];
-        if (r < k) {
-            const int t = fdiv(i, rE);
-            sidx[t * k + r] = i - t * E;
-            skey[t * k + r] = lk[i];
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // k_route
@@ -564,38 +516,19 @@ struct RouteArgs {
     int n_expert_blocks;    // router workgroups; then T * H/256 encoding workgroups, then the tail
 };
 
-// Single-token routing tail, by wave 0 alone (no barriers).  The wave polls
-// the E keys into registers (lane l holds experts l + 64i), takes tau, the
-// k-th largest of the 64 per-lane maxima (bitonic sort across the lanes):
-// at least k keys are >= tau, so the top k are among the keys >= tau, and
+// Top-k of one token's E keys by one wave (no barriers), keys in registers
+// (lane l holds experts l + 64i, zero past E).  tau, the k-th largest of the
+// 64 per-lane maxima (bitonic sort across the lanes), bounds the top k from
+// below: at least k keys are >= tau, so the top k are among them, and
 // usually only a few more.  Those candidates, as 64-bit C = key << 32 | ~e
 // (unique, ordered like the key with ties to the lower id), are ranked
-// against each other in LDS; rank r < k is selection r.  Softmax over the k
-// selected logits and the grouping (selection j is pair and distinct expert
-// pos_j, its position among the k ids in ascending order) follow in the same
-// wave.  cand: LDS of at least E + 8 64-bit slots.
+// against each other in LDS.  Returns, in lane j < k, the C of selection j
+// (logit descending, ties to the lower id), 0 in the other lanes.
+// cand: LDS of at least E + 9 + k 64-bit slots, 16-byte aligned.
 template <int NVL>
-__device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *cand, PrePtr pre)
+__device__ __forceinline__ uint64_t topk_one(const uint32_t (&key)[NVL], int E, int k, uint64_t *cand)
 {
-    const int E = a.E, k = a.k, ns = a.ns, lane = lane_id();
-    uint32_t key[NVL];
-    int ok = 1;
-    for (unsigned it = 0;; it++) {
-        bool missing = false;
-#pragma unroll
-        for (int i = 0; i < NVL; i++) {
-            const int e = lane + 64 * i;
-            key[i] = e < E ? ld_coh_u(a.keys + e) : 0u;
-            missing |= e < E && key[i] == 0u;
-        }
-        if (!__ballot(missing)) break;
-        if (it >= kSpinLimit) {
-            ok = 0;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    // tau: the k-th largest lane maximum (bitonic sort, descending across lanes)
+    const int lane = lane_id();
     uint32_t v = 0;
 #pragma unroll
     for (int i = 0; i < NVL; i++) v = max(v, key[i]);
@@ -619,7 +552,7 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
     }
     if (lane < 8) cand[m + lane] = 0ull;
     const int mp = (m + 7) & ~7;
-    // exact ranks among the candidates; lane r < k then holds selection r in sel
+    // exact ranks among the candidates; selection r goes to sel[r]
     uint64_t *sel = cand + ((E + 8 + 1) & ~1);
     for (int c = lane; c < m; c += 64) {
         const uint64_t ci = cand[c];
@@ -632,7 +565,35 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
         }
         if (r0 + r1 < k) sel[r0 + r1] = ci;
     }
-    const uint64_t cs = lane < k ? sel[lane] : 0ull;
+    return lane < k ? sel[lane] : 0ull;
+}
+
+// Single-token routing tail, by wave 0 alone (no barriers): polls the keys
+// into registers, topk_one, softmax over the k selected logits, and the
+// grouping (selection j is pair and distinct expert pos_j, its position
+// among the k ids in ascending order).
+template <int NVL>
+__device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *cand, PrePtr pre)
+{
+    const int E = a.E, k = a.k, ns = a.ns, lane = lane_id();
+    uint32_t key[NVL];
+    int ok = 1;
+    for (unsigned it = 0;; it++) {
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? ld_coh_u(a.keys + e) : 0u;
+            missing |= e < E && key[i] == 0u;
+        }
+        if (!__ballot(missing)) break;
+        if (it >= kSpinLimit) {
+            ok = 0;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    const uint64_t cs = topk_one<NVL>(key, E, k, cand);
     const int id = (int)~(uint32_t)cs;
     // softmax over the k selected logits
     const float lg = lane < k ? unord_bits((uint32_t)(cs >> 32)) : 0.f;
@@ -689,15 +650,16 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
 __device__ __forceinline__ void route_tail(const RouteArgs &a)
 {
     __shared__ __align__(16) uint32_t lk[kStageKeys];
-    __shared__ uint64_t lc[2 * kRankKeys];
-    __shared__ int lrank[kRankKeys];
+    __shared__ union {
+        uint64_t cand[kRouteThreads / 64][kWaveTopE + 9 + kMaxK];  // top-k, per wave
+        int lstart[2 * kMaxE];                                     // grouping, after the top-k
+    } u;
+    int *lstart = u.lstart;
     __shared__ int sidx[kMaxT * kMaxK];
     __shared__ uint32_t skey[kMaxT * kMaxK];
     __shared__ float sw[kMaxT * kMaxK];
-    __shared__ int lstart[2 * kMaxE];
     const int T = a.T, E = a.E, k = a.k, n = T * E;
     const int tid = (int)threadIdx.x, lane = lane_id();
-    const bool ranks = n <= kRankKeys && T * ((E + 31) & ~31) <= 2 * kRankKeys;  // fits lk, lc
     const bool staged = n <= kStageKeys;  // keys kept in LDS by the poll
 
     // pointer table entries lane + 64i for the grouping
@@ -732,8 +694,21 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    if (ranks) {
-        topk_ranks(lk, T, E, k, sidx, skey, lc, lrank);
+    if (staged && E <= kWaveTopE) {
+        // a wave per token: topk_one on the token's staged keys
+        for (int t = wave_id(); t < T; t += kRouteThreads / 64) {
+            uint32_t key[kWaveTopE / 64];
+#pragma unroll
+            for (int i = 0; i < kWaveTopE / 64; i++) {
+                const int e = lane + 64 * i;
+                key[i] = e < E ? lk[t * E + e] : 0u;
+            }
+            const uint64_t cs = topk_one<kWaveTopE / 64>(key, E, k, u.cand[wave_id()]);
+            if (lane < k) {
+                sidx[t * k + lane] = (int)~(uint32_t)cs;
+                skey[t * k + lane] = (uint32_t)(cs >> 32);
+            }
+        }
     } else if (staged) {
         for (int t = wave_id(); t < T; t += kRouteThreads / 64)
             topk_wave_any<false>(lk + t * E, E, k, sidx + t * k, skey + t * k);
