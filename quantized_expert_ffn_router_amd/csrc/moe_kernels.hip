@@ -234,6 +234,21 @@ struct WorkEntry {
     uint8_t tok[kInlineTok];     // tokens of the first kInlineTok pairs
 };
 
+// A work-table entry read whole by one scalar load: the table is written by
+// an earlier launch and only read in this one, so it may be read as
+// constant memory (a uniform index then gives one s_load_dwordx8 instead of
+// two loads split around the early exit for an empty entry).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ WorkEntry load_entry(const WorkEntry *wt, int u)
+{
+    typedef const __attribute__((address_space(4))) uint8_t cbyte;
+    const i32x8 v = *(const __attribute__((address_space(4))) i32x8 *)((cbyte *)wt + (size_t)u * sizeof(WorkEntry));
+    WorkEntry we;
+    static_assert(sizeof(WorkEntry) == sizeof(i32x8), "work entry size");
+    __builtin_memcpy(&we, &v, sizeof(we));
+    return we;
+}
+
 struct GroupOut {
     int *nuniq;           // work-table entries in use (workspace)
     WorkEntry *wt;        // [Umax]; entries past nuniq are empty (p0 == p1)
@@ -1169,6 +1184,10 @@ __device__ __forceinline__ void kgroup_dot(const Q80Regs (&r)[NM], const XL &X, 
 // An empty asm that claims to modify the weight registers: the nibble
 // unpacking then stays inside each dot product instead of being hoisted out
 // of the token loop, where its unpacked copies would not fit in registers.
+// Uses v, so that a load into it stays ahead of the branch it is issued
+// before (the compiler would otherwise sink it into the one path using it).
+__device__ __forceinline__ void use(const u32x4 &v) { asm volatile("" ::"v"(v)); }
+
 template <class R> __device__ __forceinline__ void opaque(R &r)
 {
     uint32_t *w = reinterpret_cast<uint32_t *>(&r);
@@ -1218,6 +1237,7 @@ struct GateUpArgs {
     float *act_out;   // [P][kd] or null
     int ntile;        // I/32
     int tpass;        // tokens staged per pass
+    int T;            // tokens (records of x)
 };
 
 constexpr int kGUThreads = 512;
@@ -1228,7 +1248,10 @@ constexpr int kDnLds = 24576;   // staged pair records per pass
 constexpr int kDnPass = 8;
 constexpr int kDnPre = 4;       // record words per thread loaded before the weights
 
-template <int QT>
+// ALL: every token's record fits the first pass and the prefetch words
+// (T <= tpass, T * RB <= kGUPre * kGUThreads * 16); the records are then
+// loaded before the work entry arrives, token t to LDS slot t.
+template <int QT, bool ALL>
 __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 2))) void k_gate_up(GateUpArgs a)
 {
     extern __shared__ __align__(16) uint8_t xs[];
@@ -1236,12 +1259,25 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
 
     const int u = blockIdx.x / a.ntile;
     const int rt = blockIdx.x - u * a.ntile;
-    const WorkEntry we = a.wt[u];
-    const int e = we.e, p0 = we.p0, p1 = we.p1;
-    if (p0 >= p1) return;
-    const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
     const int H = a.H, S = H >> 8;
     const size_t RB = enc_bytes(H);
+    const int q16 = (int)(RB / 16);  // 16-byte words per record
+    u32x4 xr[kGUPre];
+    if (ALL) {
+        // the records are back to back: word i is word i % q16 of token i / q16
+#pragma unroll
+        for (int q = 0; q < kGUPre; q++)
+            xr[q] = ((const u32x4 *)a.x.base)[min((int)threadIdx.x + q * kGUThreads, a.T * q16 - 1)];
+    }
+    const WorkEntry we = load_entry(a.wt, u);
+    const int e = we.e, p0 = we.p0, p1 = we.p1;
+    if (p0 >= p1) {
+        if (ALL)
+#pragma unroll
+            for (int q = 0; q < kGUPre; q++) use(xr[q]);
+        return;
+    }
+    const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
     const int lane = lane_id();
     const int m = (int)(threadIdx.x >> 8);              // 0: gate, 1: up
     const int slot = (int)((threadIdx.x >> 5) & 7), r = lane & 31;
@@ -1254,19 +1290,19 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     // the barrier after staging them does not wait for the weights, and each
     // wave starts its dots as soon as its own weights arrive.
     const int nt0 = p1 - p0 < a.tpass ? p1 - p0 : a.tpass;
-    const int q16 = (int)(RB / 16);  // 16-byte words per record
     const float rq16 = 1.0f / (float)q16;
     uint64_t toks;
     __builtin_memcpy(&toks, we.tok, sizeof(toks));
-    u32x4 xr[kGUPre];
+    if (!ALL) {
 #pragma unroll
-    for (int q = 0; q < kGUPre; q++) {
-        // unconditional loads (clamped index): no per-word branches, whose
-        // merges would wait for each load
-        const int i = min((int)threadIdx.x + q * kGUThreads, nt0 * q16 - 1);
-        const int tt = fdiv(i, rq16);  // < tpass <= kInlineTok: an inline token
-        const int tok = (int)((toks >> (8 * tt)) & 0xff);
-        xr[q] = ((const u32x4 *)rec_at(a.x, tok, H))[i - tt * q16];
+        for (int q = 0; q < kGUPre; q++) {
+            // unconditional loads (clamped index): no per-word branches, whose
+            // merges would wait for each load
+            const int i = min((int)threadIdx.x + q * kGUThreads, nt0 * q16 - 1);
+            const int tt = fdiv(i, rq16);  // < tpass <= kInlineTok: an inline token
+            const int tok = (int)((toks >> (8 * tt)) & 0xff);
+            xr[q] = ((const u32x4 *)rec_at(a.x, tok, H))[i - tt * q16];
+        }
     }
     // the first K-group's weights, loaded unconditionally (slots past S
     // load K-group 0 and leave it unused) so that the waits for the records
@@ -1277,11 +1313,13 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     for (int c0 = p0; c0 < p1; c0 += a.tpass) {
         const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
         if (c0 == p0) {
+            const int n16 = (ALL ? a.T : nt0) * q16;
 #pragma unroll
             for (int q = 0; q < kGUPre; q++) {
                 const int i = (int)threadIdx.x + q * kGUThreads;
-                if (i < nt0 * q16) ((u32x4 *)xs)[i] = xr[q];
+                if (i < n16) ((u32x4 *)xs)[i] = xr[q];
             }
+            if (!ALL)
             for (int i = (int)threadIdx.x + kGUPre * kGUThreads; i < nt0 * q16; i += kGUThreads) {
                 const int tt = fdiv(i, rq16);
                 ((u32x4 *)xs)[i] = ((const u32x4 *)rec_at(a.x, (int)((toks >> (8 * tt)) & 0xff), H))[i - tt * q16];
@@ -1301,7 +1339,9 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             for (int tt = 0; tt < nt; tt++) {
                 float o[1];
                 opaque(rg[0]);
-                kgroup_dot<1>(rg, xl(xs + tt * RB, H, s), o);
+                // ALL: a single pass, its tokens inline
+                const int xslot = ALL ? (int)((toks >> (8 * tt)) & 0xff) : tt;
+                kgroup_dot<1>(rg, xl(xs + xslot * RB, H, s), o);
                 if (s == slot) part[slot][tt][r][m] = o[0];
                 else part[slot][tt][r][m] += o[0];
             }
@@ -1348,6 +1388,7 @@ struct DownArgs {
     const float *pw; // [P] combine weight of each grouped pair
     float *y;        // [T][H], added into
     int tpass;
+    int P;           // pair records in h
 };
 
 // y[t][row] += v, relaxed agent-scope float atomic (no return value).
@@ -1356,7 +1397,10 @@ __device__ __forceinline__ void add_to(float *p, float v)
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT>
+// ONE: a single token, whose work item u is pair u (one pair per item, in
+// pair order); the pair's record is then loaded before the work entry
+// arrives (it must fit the prefetch words).
+template <int QT, bool ONE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 3))) void k_down(DownArgs a)
 {
     extern __shared__ __align__(16) uint8_t hsl[];
@@ -1364,9 +1408,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
 
     const int u = blockIdx.x / a.nrt;
     const int rt = blockIdx.x - u * a.nrt;
-    const WorkEntry we = a.wt[u];
+    u32x4 hr[kDnPre];
+    if (ONE) {
+        const u32x4 *h16 = (const u32x4 *)rec_at(a.h, min(u, a.P - 1), a.kd);
+        const int n16 = (int)(enc_bytes(a.kd) / 16);
+#pragma unroll
+        for (int q = 0; q < kDnPre; q++) hr[q] = h16[min((int)threadIdx.x + q * (int)blockDim.x, n16 - 1)];
+    }
+    const WorkEntry we = load_entry(a.wt, u);
     const int e = we.e, p0 = we.p0, p1 = we.p1;
-    if (p0 >= p1) return;
+    if (p0 >= p1) {
+        if (ONE)
+#pragma unroll
+            for (int q = 0; q < kDnPre; q++) use(hr[q]);
+        return;
+    }
+    if (ONE && (p0 != u || p1 != u + 1)) {
+        // not the one-pair-per-item grouping the records were loaded for
+        for (int i = threadIdx.x; i < (p1 - p0) * 64; i += blockDim.x)
+            add_to(a.y + (size_t)a.ptok[p0 + (i >> 6)] * a.H + rt * 64 + (i & 63), __builtin_nanf(""));
+        return;
+    }
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]) + a.down_off;
     const int kd = a.kd, S = kd >> 8;
@@ -1381,9 +1443,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
     // kDnPre are staged after the barrier.
     const int n16 = (int)((p1 - p0 < a.tpass ? p1 - p0 : a.tpass) * RB / 16);
     const u32x4 *h16 = (const u32x4 *)rec_at(a.h, p0, kd);
-    u32x4 hr[kDnPre];
+    if (!ONE) {
 #pragma unroll
-    for (int q = 0; q < kDnPre; q++) hr[q] = h16[min((int)threadIdx.x + q * (int)blockDim.x, n16 - 1)];
+        for (int q = 0; q < kDnPre; q++) hr[q] = h16[min((int)threadIdx.x + q * (int)blockDim.x, n16 - 1)];
+    }
     // blockDim = 64 * min(S, 8): every wave has a K-group (loaded
     // unconditionally, for the same reason as in k_gate_up)
     typename RegsOf<QT>::T rg[1];
@@ -1687,7 +1750,7 @@ __global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs 
     // number of distinct experts, and workgroups past the actual ones leave
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int u = item / a.nrb, rb = item - u * a.nrb;
-        const WorkEntry we = a.wt[u];
+        const WorkEntry we = load_entry(a.wt, u);
         const int p0 = we.p0, n = we.p1 - we.p0;
         const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]);
         const int row64 = hr * 32 + (lane & 31), row = rb * 64 + row64;
@@ -1760,7 +1823,7 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
     const int u = blockIdx.x / a.nrt, rt = blockIdx.x - u * a.nrt;
     const int nu = uni(*a.nuniq);
     if (u >= nu) return;
-    const WorkEntry we = a.wt[u];
+    const WorkEntry we = load_entry(a.wt, u);
     const int p0 = we.p0, n = we.p1 - we.p0;
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]) + a.down_off;
@@ -1940,13 +2003,20 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     ga.ntile = d.I / 32;
     ga.tpass = (int)(kGULds / enc_bytes(d.H));
     if (ga.tpass > kTokPass) ga.tpass = kTokPass;
+    ga.T = T;
     const size_t glds = (size_t)ga.tpass * enc_bytes(d.H);
     dim3 ggrid(L.UI * ga.ntile);
+    // every token's record staged up front when they all fit the first pass
+    const bool all = T <= ga.tpass && (size_t)T * enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16;
+#define GATE_UP(Q)                                                                        \
+    (all ? k_gate_up<Q, true><<<ggrid, kGUThreads, glds, s>>>(ga)                        \
+         : k_gate_up<Q, false><<<ggrid, kGUThreads, glds, s>>>(ga))
     switch (d.gate) {
-    case MOE_Q4_K: k_gate_up<MOE_Q4_K><<<ggrid, kGUThreads, glds, s>>>(ga); break;
-    case MOE_Q6_K: k_gate_up<MOE_Q6_K><<<ggrid, kGUThreads, glds, s>>>(ga); break;
-    case MOE_Q8_0: k_gate_up<MOE_Q8_0><<<ggrid, kGUThreads, glds, s>>>(ga); break;
+    case MOE_Q4_K: GATE_UP(MOE_Q4_K); break;
+    case MOE_Q6_K: GATE_UP(MOE_Q6_K); break;
+    case MOE_Q8_0: GATE_UP(MOE_Q8_0); break;
     }
+#undef GATE_UP
     LAUNCH_OK("k_gate_up");
 
     DownArgs da;
@@ -1956,16 +2026,21 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     da.H = d.H; da.kd = g.kd; da.down_off = g.down_off;
     da.nrt = d.H / 64;
     da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
+    da.P = L.P;
     const int S = g.kd / 256;
     da.tpass = (int)(kDnLds / enc_bytes(g.kd));
     if (da.tpass > kDnPass) da.tpass = kDnPass;
     const size_t dlds = (size_t)da.tpass * enc_bytes(g.kd);
     dim3 dgrid(L.UI * da.nrt), dblock(64 * (S < 8 ? S : 8));
+    // one token: item u is pair u, whose record is loaded up front when it fits
+    const bool one = T == 1 && enc_bytes(g.kd) <= (size_t)kDnPre * dblock.x * 16;
+#define DOWN(Q) (one ? k_down<Q, true><<<dgrid, dblock, dlds, s>>>(da) : k_down<Q, false><<<dgrid, dblock, dlds, s>>>(da))
     switch (d.down) {
-    case MOE_Q4_K: k_down<MOE_Q4_K><<<dgrid, dblock, dlds, s>>>(da); break;
-    case MOE_Q6_K: k_down<MOE_Q6_K><<<dgrid, dblock, dlds, s>>>(da); break;
-    case MOE_Q8_0: k_down<MOE_Q8_0><<<dgrid, dblock, dlds, s>>>(da); break;
+    case MOE_Q4_K: DOWN(MOE_Q4_K); break;
+    case MOE_Q6_K: DOWN(MOE_Q6_K); break;
+    case MOE_Q8_0: DOWN(MOE_Q8_0); break;
     }
+#undef DOWN
     LAUNCH_OK("k_down");
     return MOE_OK;
 }
