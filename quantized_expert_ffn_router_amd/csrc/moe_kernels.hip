@@ -54,6 +54,7 @@ constexpr float kC2 = 1.0f / 64516.0f;
 constexpr int kChunk = 8;  // tokens per pass of the matvec kernels
 constexpr int kRouteThreads = 256;
 constexpr int kRouteRows = 2;                   // router rows per workgroup
+constexpr int kRouteTok = 8;                    // tokens per pass of a router workgroup
 constexpr int kEncThreads = 256;                // positions encoded per workgroup
 constexpr int kMaxK = 64;
 
@@ -498,7 +499,8 @@ __device__ __forceinline__ void topk_wave_any(const uint32_t *keys, int E, int k
 }
 
 constexpr int kStageKeys = 4096;  // keys the route tail keeps in LDS
-constexpr int kWaveTopE = 256;    // experts for the per-wave topk_one (4 keys per lane)
+constexpr int kWaveTopE = 256;    // experts for the per-wave topk_multi (4 keys per lane)
+constexpr int kCandSlots = kWaveTopE + 9 + kMaxK + 1;  // candidate slots of one token
 
 // floor(i / d) for 0 <= i < 2^16, 1 <= d <= 2^16, with r = 1.0f/d: (i + 0.5)/d
 // is at least 0.5/d away from an integer, far more than the float error.
@@ -531,56 +533,90 @@ struct RouteArgs {
     int n_expert_blocks;    // router workgroups; then T * H/256 encoding workgroups, then the tail
 };
 
-// Top-k of one token's E keys by one wave (no barriers), keys in registers
-// (lane l holds experts l + 64i, zero past E).  tau, the k-th largest of the
-// 64 per-lane maxima (bitonic sort across the lanes), bounds the top k from
-// below: at least k keys are >= tau, so the top k are among them, and
-// usually only a few more.  Those candidates, as 64-bit C = key << 32 | ~e
-// (unique, ordered like the key with ties to the lower id), are ranked
-// against each other in LDS.  Returns, in lane j < k, the C of selection j
-// (logit descending, ties to the lower id), 0 in the other lanes.
-// cand: LDS of at least E + 9 + k 64-bit slots, 16-byte aligned.
-template <int NVL>
-__device__ __forceinline__ uint64_t topk_one(const uint32_t (&key)[NVL], int E, int k, uint64_t *cand)
+// Top-k of NT tokens' E keys each by one wave (no barriers), keys in
+// registers (lane l holds experts l + 64i of token t in key[t][i], zero past
+// E); the NT tokens' steps are interleaved, so that their latencies overlap.
+// tau, the k-th largest of the 64 per-lane maxima (bitonic sort across the
+// lanes), bounds the top k from below: at least k keys are >= tau, so the
+// top k are among them, and usually only a few more.  Those candidates, as
+// 64-bit C = key << 32 | ~e (unique, ordered like the key with ties to the
+// lower id), are ranked against each other in LDS.  Returns in out[t], in
+// lane j < k, the C of token t's selection j (logit descending, ties to the
+// lower id), 0 in the other lanes.
+// cand: LDS of NT regions of cstride >= E + 9 + k + ... 64-bit slots (see
+// kCandSlots), 16-byte aligned.
+template <int NVL, int NT>
+__device__ __forceinline__ void topk_multi(const uint32_t (&key)[NT][NVL], int E, int k, uint64_t *cand, int cstride,
+                                           uint64_t (&out)[NT])
 {
     const int lane = lane_id();
-    uint32_t v = 0;
+    uint32_t v[NT];
 #pragma unroll
-    for (int i = 0; i < NVL; i++) v = max(v, key[i]);
+    for (int t = 0; t < NT; t++) {
+        v[t] = 0;
+#pragma unroll
+        for (int i = 0; i < NVL; i++) v[t] = max(v[t], key[t][i]);
+    }
 #pragma unroll
     for (int k2 = 2; k2 <= 64; k2 <<= 1)
 #pragma unroll
         for (int j = k2 >> 1; j > 0; j >>= 1) {
-            const uint32_t p = (uint32_t)__shfl_xor((int)v, j, 64);
-            v = (((lane & j) == 0) == ((lane & k2) == 0)) ? max(v, p) : min(v, p);
-        }
-    const uint32_t tau = (uint32_t)__shfl((int)v, k - 1, 64);
-    // candidates >= tau, compacted into cand[0, m), zero padding after
-    int m = 0;
+            const bool up = ((lane & j) == 0) == ((lane & k2) == 0);
 #pragma unroll
-    for (int i = 0; i < NVL; i++) {
-        const int e = lane + 64 * i;
-        const bool c = e < E && key[i] >= tau;
-        const uint64_t bal = __ballot(c);
-        if (c) cand[m + below(bal)] = (uint64_t)key[i] << 32 | (uint32_t)~e;
-        m += __popcll(bal);
-    }
-    if (lane < 8) cand[m + lane] = 0ull;
-    const int mp = (m + 7) & ~7;
-    // exact ranks among the candidates; selection r goes to sel[r]
-    uint64_t *sel = cand + ((E + 8 + 1) & ~1);
-    for (int c = lane; c < m; c += 64) {
-        const uint64_t ci = cand[c];
-        int r0 = 0, r1 = 0;
-        for (int c2 = 0; c2 < mp; c2 += 8) {
-            const ulonglong2 *q = (const ulonglong2 *)(cand + c2);
-            const ulonglong2 x0 = q[0], x1 = q[1], x2 = q[2], x3 = q[3];
-            r0 += (x0.x > ci) + (x0.y > ci) + (x1.x > ci) + (x1.y > ci);
-            r1 += (x2.x > ci) + (x2.y > ci) + (x3.x > ci) + (x3.y > ci);
+            for (int t = 0; t < NT; t++) {
+                const uint32_t p = (uint32_t)__shfl_xor((int)v[t], j, 64);
+                v[t] = up ? max(v[t], p) : min(v[t], p);
+            }
         }
-        if (r0 + r1 < k) sel[r0 + r1] = ci;
+    // candidates >= tau, compacted into the token's cand[0, m), zero padding after
+    int m[NT], mp[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const uint32_t tau = (uint32_t)__shfl((int)v[t], k - 1, 64);
+        uint64_t *ct = cand + t * cstride;
+        m[t] = 0;
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+            const int e = lane + 64 * i;
+            const bool c = e < E && key[t][i] >= tau;
+            const uint64_t bal = __ballot(c);
+            if (c) ct[m[t] + below(bal)] = (uint64_t)key[t][i] << 32 | (uint32_t)~e;
+            m[t] += __popcll(bal);
+        }
+        if (lane < 8) ct[m[t] + lane] = 0ull;
+        mp[t] = (m[t] + 7) & ~7;
     }
-    return lane < k ? sel[lane] : 0ull;
+    // exact ranks among the candidates; selection r goes to sel[r]
+    const int soff = (E + 8 + 1) & ~1;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        uint64_t *ct = cand + t * cstride;
+        for (int c = lane; c < m[t]; c += 64) {
+            const uint64_t ci = ct[c];
+            int r0 = 0, r1 = 0;
+            for (int c2 = 0; c2 < mp[t]; c2 += 8) {
+                const ulonglong2 *q = (const ulonglong2 *)(ct + c2);
+                const ulonglong2 x0 = q[0], x1 = q[1], x2 = q[2], x3 = q[3];
+                r0 += (x0.x > ci) + (x0.y > ci) + (x1.x > ci) + (x1.y > ci);
+                r1 += (x2.x > ci) + (x2.y > ci) + (x3.x > ci) + (x3.y > ci);
+            }
+            if (r0 + r1 < k) ct[soff + r0 + r1] = ci;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) out[t] = lane < k ? cand[t * cstride + soff + lane] : 0ull;
+}
+
+// topk_multi for a single token.  cand: E + 9 + k + 1 slots.
+template <int NVL>
+__device__ __forceinline__ uint64_t topk_one(const uint32_t (&key)[NVL], int E, int k, uint64_t *cand)
+{
+    uint32_t kk[1][NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; i++) kk[0][i] = key[i];
+    uint64_t out[1];
+    topk_multi<NVL, 1>(kk, E, k, cand, 0, out);
+    return out[0];
 }
 
 // Single-token routing tail, by wave 0 alone (no barriers): polls the keys
@@ -665,9 +701,9 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
 __device__ __forceinline__ void route_tail(const RouteArgs &a)
 {
     __shared__ __align__(16) uint32_t lk[kStageKeys];
-    __shared__ union {
-        uint64_t cand[kRouteThreads / 64][kWaveTopE + 9 + kMaxK];  // top-k, per wave
-        int lstart[2 * kMaxE];                                     // grouping, after the top-k
+    __shared__ __align__(16) union {
+        uint64_t cand[kRouteThreads / 64][2][kCandSlots];  // top-k, per wave, two tokens at a time
+        int lstart[2 * kMaxE];                             // grouping, after the top-k
     } u;
     int *lstart = u.lstart;
     __shared__ int sidx[kMaxT * kMaxK];
@@ -694,6 +730,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         else route_tail_one<16>(a, cand, pre);
         return;
     }
+    // each wave polls its own share of the keys, then the workgroup meets once
     int ok = 1;
     for (unsigned it = 0;; it++) {
         int missing = 0;
@@ -702,27 +739,34 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
             if (staged) lk[i] = v;
             missing |= v == 0u;
         }
-        if (!__syncthreads_or(missing)) break;
+        if (!__ballot(missing)) break;
         if (it >= kSpinLimit) {
             ok = 0;
             break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
+    ok = __syncthreads_and(ok);
     if (staged && E <= kWaveTopE) {
-        // a wave per token: topk_one on the token's staged keys
-        for (int t = wave_id(); t < T; t += kRouteThreads / 64) {
-            uint32_t key[kWaveTopE / 64];
+        // a wave per pair of tokens: topk_multi on the tokens' staged keys
+        constexpr int NVL = kWaveTopE / 64;
+        for (int t0 = 2 * wave_id(); t0 < T; t0 += 2 * (kRouteThreads / 64)) {
+            uint32_t key[2][NVL];
 #pragma unroll
-            for (int i = 0; i < kWaveTopE / 64; i++) {
-                const int e = lane + 64 * i;
-                key[i] = e < E ? lk[t * E + e] : 0u;
-            }
-            const uint64_t cs = topk_one<kWaveTopE / 64>(key, E, k, u.cand[wave_id()]);
-            if (lane < k) {
-                sidx[t * k + lane] = (int)~(uint32_t)cs;
-                skey[t * k + lane] = (uint32_t)(cs >> 32);
-            }
+            for (int q = 0; q < 2; q++)
+#pragma unroll
+                for (int i = 0; i < NVL; i++) {
+                    const int e = lane + 64 * i, t = min(t0 + q, T - 1);
+                    key[q][i] = e < E ? lk[t * E + e] : 0u;
+                }
+            uint64_t cs[2];
+            topk_multi<NVL, 2>(key, E, k, &u.cand[wave_id()][0][0], kCandSlots, cs);
+#pragma unroll
+            for (int q = 0; q < 2; q++)
+                if (lane < k && t0 + q < T) {
+                    sidx[(t0 + q) * k + lane] = (int)~(uint32_t)cs[q];
+                    skey[(t0 + q) * k + lane] = (uint32_t)(cs[q] >> 32);
+                }
         }
     } else if (staged) {
         for (int t = wave_id(); t < T; t += kRouteThreads / 64)
@@ -756,6 +800,78 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
     go.wsrc = sw;
     __syncthreads();
     group_block(sidx, T, k, E, a.ns, go, lstart, pre);
+}
+
+// Router rows [e0, e0 + nr) against all tokens, NT tokens per pass; wave w
+// takes the 256-column chunks w, w+4, ... of H, and the partial sums meet in
+// LDS.  Loads are unconditional (row and token indices clamped; results for
+// clamped tokens are dropped), so that each pass issues all of its loads at
+// once.
+template <int NT>
+__device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
+{
+    __shared__ float part[kRouteThreads / 64][kRouteRows + 1][NT];
+    const int H = a.H, T = a.T, E = a.E, nv = H >> 8;
+    const int w = wave_id(), lane = lane_id();
+    const float4 *wrow[kRouteRows];
+#pragma unroll
+    for (int r = 0; r < kRouteRows; r++) wrow[r] = (const float4 *)(a.wr + (size_t)(r < nr ? e0 + r : e0) * H);
+    for (int t0 = 0; t0 < T; t0 += NT) {
+        const float4 *hrow[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) hrow[tt] = (const float4 *)(a.h + (size_t)min(t0 + tt, T - 1) * H);
+        float acc[kRouteRows][NT], ss[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+            ss[tt] = 0.f;
+#pragma unroll
+            for (int r = 0; r < kRouteRows; r++) acc[r][tt] = 0.f;
+        }
+#pragma unroll 2
+        for (int c = w; c < nv; c += kRouteThreads / 64) {
+            float4 wv[kRouteRows], hv[NT];
+#pragma unroll
+            for (int r = 0; r < kRouteRows; r++) wv[r] = wrow[r][c * 64 + lane];
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) hv[tt] = hrow[tt][c * 64 + lane];
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) {
+                const float4 x = hv[tt];
+                ss[tt] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+#pragma unroll
+                for (int r = 0; r < kRouteRows; r++)
+                    acc[r][tt] += wv[r].x * x.x + wv[r].y * x.y + wv[r].z * x.z + wv[r].w * x.w;
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+            const float q = wave_sum(ss[tt]);
+            if (lane == 0) part[w][kRouteRows][tt] = q;
+#pragma unroll
+            for (int r = 0; r < kRouteRows; r++) {
+                const float d = wave_sum(acc[r][tt]);
+                if (lane == 0) part[w][r][tt] = d;
+            }
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < nr * NT) {
+            const int r = threadIdx.x / NT, tt = threadIdx.x % NT, t = t0 + tt;
+            if (t < T) {
+                float d = 0.f, q = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kRouteThreads / 64; ww++) {
+                    d += part[ww][r][tt];
+                    q += part[ww][kRouteRows][tt];
+                }
+                const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
+                const float lg = d * rr + (a.bias ? a.bias[e0 + r] : 0.f);
+                __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (a.logits2) a.logits2[(size_t)t * E + e0 + r] = lg;
+            }
+        }
+        __syncthreads();
+    }
 }
 
 // Router workgroup: 2 router rows against all T tokens, the 4 waves
@@ -800,68 +916,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         return;
     }
 
-    // router rows [e0, e0 + kRouteRows) against all tokens; wave w takes the
-    // 256-column chunks w, w+4, ... of H, partial sums meet in LDS
-    __shared__ float part[kRouteThreads / 64][kRouteRows + 1][4];
-    const int e0 = blk * kRouteRows, w = wave_id();
+    const int e0 = blk * kRouteRows;
     const int nr = E - e0 < kRouteRows ? E - e0 : kRouteRows;
-    for (int t0 = 0; t0 < T; t0 += 4) {
-        float acc[kRouteRows][4], ss[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            ss[tt] = 0.f;
-#pragma unroll
-            for (int r = 0; r < kRouteRows; r++) acc[r][tt] = 0.f;
-        }
-#pragma unroll 2
-        for (int c = w; c < nv; c += kRouteThreads / 64) {
-            float4 wv[kRouteRows], hv[4];
-#pragma unroll
-            for (int r = 0; r < kRouteRows; r++)
-                if (r < nr) wv[r] = ((const float4 *)(a.wr + (size_t)(e0 + r) * H))[c * 64 + lane];
-#pragma unroll
-            for (int tt = 0; tt < 4; tt++)
-                if (t0 + tt < T) hv[tt] = ((const float4 *)(a.h + (size_t)(t0 + tt) * H))[c * 64 + lane];
-#pragma unroll
-            for (int tt = 0; tt < 4; tt++)
-                if (t0 + tt < T) {
-                    const float4 x = hv[tt];
-                    ss[tt] += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-#pragma unroll
-                    for (int r = 0; r < kRouteRows; r++)
-                        if (r < nr) acc[r][tt] += wv[r].x * x.x + wv[r].y * x.y + wv[r].z * x.z + wv[r].w * x.w;
-                }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            if (t0 + tt >= T) break;
-            const float q = wave_sum(ss[tt]);
-            if (lane == 0) part[w][kRouteRows][tt] = q;
-#pragma unroll
-            for (int r = 0; r < kRouteRows; r++) {
-                const float d = wave_sum(acc[r][tt]);
-                if (lane == 0) part[w][r][tt] = d;
-            }
-        }
-        __syncthreads();
-        if ((int)threadIdx.x < nr * 4) {
-            const int r = threadIdx.x >> 2, tt = threadIdx.x & 3, t = t0 + tt;
-            if (t < T) {
-                float d = 0.f, q = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < kRouteThreads / 64; ww++) {
-                    d += part[ww][r][tt];
-                    q += part[ww][kRouteRows][tt];
-                }
-                const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
-                const float lg = d * rr + (a.bias ? a.bias[e0 + r] : 0.f);
-                __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                if (a.logits2) a.logits2[(size_t)t * E + e0 + r] = lg;
-            }
-        }
-        __syncthreads();
-    }
+    if (T == 1) router_rows<1>(a, e0, nr);
+    else if (T == 2) router_rows<2>(a, e0, nr);
+    else if (T <= 4) router_rows<4>(a, e0, nr);
+    else router_rows<kRouteTok>(a, e0, nr);
 }
 
 // k_route_token: stand-alone routing, one workgroup per token (16 waves
