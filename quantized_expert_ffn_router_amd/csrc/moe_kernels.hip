@@ -260,12 +260,18 @@ struct GroupOut {
     int *count, *offset, *pairs;  // moe_group_tokens outputs (may be null)
     float *pw;            // [P] combine weight of each grouped pair, or null
     const float *wsrc;    // [T][k] routing weights the pair weights are taken from
-    int chunk;            // > 0: work items of at most `chunk` pairs; 0: one entry per expert
+    int chunk;            // kItemTok: work items of at most kItemTok pairs; 0: one entry per expert
 };
 
-// Expert-table entries lane and 64 + lane, which the router's wave 0 loads
-// before the top-k so that the grouping does not wait on them.
+// Expert-table entries that the route tail's wave 0 loads before the top-k,
+// so that the grouping does not wait on them: for a single token, entries
+// lane and 64 + lane; for group_block, entries EPL*lane and EPL*lane + 1,
+// EPL = ceil(E / 64) (the first two experts of the lane).
 struct PrePtr { const void *p0, *p1; bool valid; };
+
+// Waits for the loads of pre here, before the caller issues stores: a later
+// wait for them would also wait for those stores (one counter for both).
+__device__ __forceinline__ void settle(const PrePtr &pre) { asm volatile("" ::"v"(pre.p0), "v"(pre.p1)); }
 
 // Grouping by token masks.  Ids are distinct within a token, so an expert
 // is chosen at most once per token and its pairs, in (token, slot) order,
@@ -281,6 +287,7 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
                             PrePtr pre /* this lane's table entries lane and 64 + lane, if valid */)
 {
     __shared__ int s_nu, s_valid;
+    __shared__ const void *lptr[kMaxE];  // slot addresses of the chosen experts
     const int P = T * k;
     for (int e = threadIdx.x; e < E; e += blockDim.x) lmask[e] = 0;
     __syncthreads();
@@ -290,25 +297,39 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
     }
     __syncthreads();
     if (threadIdx.x < 64) {
+        // lane l takes experts [EPL*l, EPL*l + EPL): one scan of the lanes' totals
         const int lane = lane_id();
-        int run = 0, nu = 0;
-        for (int base = 0; base < E; base += 64) {
-            const int e = base + lane;
-            const uint32_t m = e < E ? (uint32_t)lmask[e] : 0u;
+        const int EPL = (E + 63) >> 6;
+        const int eb = lane * EPL;
+        // Counts, and the slot addresses of the chosen experts into LDS: the
+        // table loads stay in this loop, so that the store loop below has no
+        // load to wait for (a wait for a load also waits for every store
+        // issued before it).
+        int lc = 0, li = 0;
+        for (int j = 0; j < EPL; j++) {
+            const int e = eb + j;
+            const int cnt = e < E ? __popc((uint32_t)lmask[e]) : 0;
+            lc += cnt;
+            li += g.chunk > 0 ? (cnt + kItemTok - 1) / kItemTok : cnt > 0;
+            if (cnt > 0 && g.wt && g.eptr) {
+                if (pre.valid && j < 2) lptr[e] = j == 0 ? pre.p0 : pre.p1;
+                else lptr[e] = g.eptr[e];
+            }
+        }
+        const int incl = wave_incl_scan(lc);
+        const int iincl = wave_incl_scan(li);
+        int off = incl - lc, ui = iincl - li;
+        for (int j = 0; j < EPL; j++) {
+            const int e = eb + j;
+            if (e >= E) break;
+            const uint32_t m = (uint32_t)lmask[e];
             const int cnt = __popc(m);
-            const int chunk = g.chunk > 0 ? g.chunk : (cnt > 0 ? cnt : 1);
-            const int nit = (cnt + chunk - 1) / chunk;  // work items of the expert
-            const int incl = wave_incl_scan(cnt);
-            const int iincl = wave_incl_scan(nit);
-            const int off = run + incl - cnt;
-            const int ui = nu + iincl - nit;
-            if (g.count && e < E) g.count[e] = cnt;
-            if (g.offset && e < E) g.offset[e] = off;
+            const int chunk = g.chunk > 0 ? kItemTok : (cnt > 0 ? cnt : 1);
+            const int nit = g.chunk > 0 ? (cnt + kItemTok - 1) / kItemTok : cnt > 0;  // work items of the expert
+            if (g.count) g.count[e] = cnt;
+            if (g.offset) g.offset[e] = off;
             if (cnt > 0 && g.wt) {
-                const void *ptr = !g.eptr                     ? nullptr
-                                  : (pre.valid && base == 0)  ? pre.p0
-                                  : (pre.valid && base == 64) ? pre.p1
-                                                              : g.eptr[e];
+                const void *ptr = g.eptr ? lptr[e] : nullptr;
                 uint32_t mm = m;  // the expert's tokens, ascending
                 for (int it = 0; it < nit; it++) {
                     WorkEntry we{};
@@ -324,11 +345,11 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
                     g.wt[ui + it] = we;
                 }
             }
-            run += __shfl(incl, 63, 64);
-            nu += __shfl(iincl, 63, 64);
-            if (e < E) lmask[E + e] = off;
+            lmask[E + e] = off;
+            off += cnt;
+            ui += nit;
         }
-        if (lane == 0) { s_nu = nu; s_valid = run; }
+        if (lane == 63) { s_nu = ui; s_valid = off; }
     }
     __syncthreads();
     const int nu = s_nu, nvalid = s_valid;
@@ -350,7 +371,7 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
     if (g.offset && threadIdx.x == 0) g.offset[E] = nvalid;
     if (g.wt) {
         // shared expert s2: pairs nvalid + s2*T + t, cut into items like the routed ones
-        const int sc = g.chunk > 0 ? g.chunk : T;
+        const int sc = g.chunk > 0 ? kItemTok : T;
         const int sit = (T + sc - 1) / sc;
         for (int i = threadIdx.x; i < ns * sit; i += blockDim.x) {
             const int s2 = i / sit, it = i - s2 * sit;
@@ -645,6 +666,7 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
         __builtin_amdgcn_s_sleep(1);
     }
     const uint64_t cs = topk_one<NVL>(key, E, k, cand);
+    settle(pre);
     const int id = (int)~(uint32_t)cs;
     // softmax over the k selected logits
     const float lg = lane < k ? unord_bits((uint32_t)(cs >> 32)) : 0.f;
@@ -713,11 +735,13 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
     const int tid = (int)threadIdx.x, lane = lane_id();
     const bool staged = n <= kStageKeys;  // keys kept in LDS by the poll
 
-    // pointer table entries lane + 64i for the grouping
+    // pointer table entries for the grouping (layouts: see PrePtr)
     PrePtr pre{nullptr, nullptr, a.go.eptr != nullptr};
     if (a.go.eptr && wave_id() == 0) {
-        if (lane < E) pre.p0 = a.go.eptr[lane];
-        if (64 + lane < E) pre.p1 = a.go.eptr[64 + lane];
+        const int EPL = (E + 63) >> 6;
+        const int i0 = T == 1 ? lane : EPL * lane, i1 = T == 1 ? 64 + lane : (EPL > 1 ? EPL * lane + 1 : E);
+        if (i0 < E) pre.p0 = a.go.eptr[i0];
+        if (i1 < E) pre.p1 = a.go.eptr[i1];
     }
     if (T == 1 && a.group) {
         if (wave_id() != 0) return;
@@ -775,24 +799,30 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         for (int t = wave_id(); t < T; t += kRouteThreads / 64)
             topk_wave_any<true>(a.keys + (size_t)t * E, E, k, sidx + t * k, skey + t * k);
     }
+    settle(pre);
     __syncthreads();
     // clear the keys for the next launch (plain stores: the launch boundary
     // makes them visible); nothing reads them again in this launch
     for (int i = tid; i < n; i += kRouteThreads) a.keys[i] = 0u;
-    // softmax over the k selected logits of each token, lane j holding selection j
-    for (int t = wave_id(); t < T; t += kRouteThreads / 64) {
-        const float lg = lane < k ? unord_bits(skey[t * k + lane]) : 0.f;
-        const float top = __shfl(lg, 0, 64);
-        const float ex = lane < k ? expf(lg - top) : 0.f;
-        const float s = wave_sum(ex);
-        if (lane < k) {
+    // softmax over the k selected logits of each token (selection 0 is the
+    // largest): for k <= 8, eight tokens per wave, lane 8q + j holding
+    // selection j of token 8w + q; else a token per wave, lane j selection j
+    const bool narrow = k <= 8;
+    for (int t0 = narrow ? 8 * wave_id() : wave_id(); t0 < T; t0 += narrow ? 8 * (kRouteThreads / 64) : kRouteThreads / 64) {
+        const int t = narrow ? t0 + (lane >> 3) : t0, j = narrow ? lane & 7 : lane;
+        const bool live = j < k && t < T;
+        const float lg = live ? unord_bits(skey[t * k + j]) : 0.f;
+        const float top = __shfl(lg, narrow ? lane & ~7 : 0, 64);
+        const float ex = live ? expf(lg - top) : 0.f;
+        const float s = narrow ? group_sum<8>(ex) : wave_sum(ex);
+        if (live) {
             const float wj = ok ? ex / s : __builtin_nanf("");
-            const int id = sidx[t * k + lane];
-            sw[t * k + lane] = wj;
-            a.idx[t * k + lane] = id;
-            a.w[t * k + lane] = wj;
-            if (a.idx2) a.idx2[t * k + lane] = id;
-            if (a.w2) a.w2[t * k + lane] = wj;
+            const int id = sidx[t * k + j];
+            sw[t * k + j] = wj;
+            a.idx[t * k + j] = id;
+            a.w[t * k + j] = wj;
+            if (a.idx2) a.idx2[t * k + j] = id;
+            if (a.w2) a.w2[t * k + j] = wj;
         }
     }
     if (!a.group) return;
@@ -1345,10 +1375,11 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     const int tile64 = row >> 6, lt = row & 63;
     const uint8_t *mat = base + (m ? a.up_off : 0);
 
-    // The first pass's token records (up to kGUPre words per thread, the
-    // rest after) are loaded before the weights: loads complete in order, so
-    // the barrier after staging them does not wait for the weights, and each
-    // wave starts its dots as soon as its own weights arrive.
+    // The first pass's token records (kGUPre words per thread into registers,
+    // the rest by LDS DMA) are loaded before the weights: loads complete in
+    // order, so when the registers suffice the barrier after staging them
+    // does not wait for the weights, and each wave starts its dots as soon as
+    // its own weights arrive.
     const int nt0 = p1 - p0 < a.tpass ? p1 - p0 : a.tpass;
     const float rq16 = 1.0f / (float)q16;
     uint64_t toks;
@@ -1362,6 +1393,22 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             const int tt = fdiv(i, rq16);  // < tpass <= kInlineTok: an inline token
             const int tok = (int)((toks >> (8 * tt)) & 0xff);
             xr[q] = ((const u32x4 *)rec_at(a.x, tok, H))[i - tt * q16];
+        }
+        // Words past the prefetch go straight to LDS (a 16-byte LDS DMA per
+        // lane, 64 consecutive words per wave, which never straddle two
+        // records: q16 is a multiple of 64).  Their wait then also waits for
+        // the weights issued below, which the dots need first anyway.
+        const int w0 = (int)(threadIdx.x & ~63u);
+#pragma unroll
+        for (int q = kGUPre; q < kGULds / 16 / kGUThreads; q++) {
+            const int i0 = w0 + q * kGUThreads;  // wave-uniform
+            if (i0 < nt0 * q16) {
+                const int tt = fdiv(i0, rq16);
+                const int tok = (int)((toks >> (8 * tt)) & 0xff);
+                const uint8_t *src = rec_at(a.x, tok, H) + (size_t)(i0 + lane - tt * q16) * 16;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                                 (__attribute__((address_space(3))) void *)(xs + (size_t)i0 * 16), 16, 0, 0);
+            }
         }
     }
     // the first K-group's weights, loaded unconditionally (slots past S
@@ -1378,11 +1425,6 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             for (int q = 0; q < kGUPre; q++) {
                 const int i = (int)threadIdx.x + q * kGUThreads;
                 if (i < n16) ((u32x4 *)xs)[i] = xr[q];
-            }
-            if (!ALL)
-            for (int i = (int)threadIdx.x + kGUPre * kGUThreads; i < nt0 * q16; i += kGUThreads) {
-                const int tt = fdiv(i, rq16);
-                ((u32x4 *)xs)[i] = ((const u32x4 *)rec_at(a.x, (int)((toks >> (8 * tt)) & 0xff), H))[i - tt * q16];
             }
         } else {
             __syncthreads();  // the previous pass is done with xs
