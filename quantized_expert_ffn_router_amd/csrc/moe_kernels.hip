@@ -305,20 +305,39 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
         // table loads stay in this loop, so that the store loop below has no
         // load to wait for (a wait for a load also waits for every store
         // issued before it).
-        int lc = 0, li = 0;
+        // Work items go to the table largest first (items of kItemTok pairs,
+        // then kItemTok-1, ...), so that the FFN launches, which take them in
+        // table order, start the long ones first; pairs stay in expert order.
+        // nb[c]: this lane's items of class c (class c holds items of
+        // kItemTok - c pairs; with one entry per expert, class 0 only).
+        int lc = 0, nb[kItemTok];
+#pragma unroll
+        for (int c = 0; c < kItemTok; c++) nb[c] = 0;
         for (int j = 0; j < EPL; j++) {
             const int e = eb + j;
             const int cnt = e < E ? __popc((uint32_t)lmask[e]) : 0;
             lc += cnt;
-            li += g.chunk > 0 ? (cnt + kItemTok - 1) / kItemTok : cnt > 0;
+            if (g.chunk > 0) {
+                nb[0] += cnt / kItemTok;
+                const int rem = cnt % kItemTok;
+#pragma unroll
+                for (int c = 1; c < kItemTok; c++) nb[c] += rem == kItemTok - c;
+            } else {
+                nb[0] += cnt > 0;
+            }
             if (cnt > 0 && g.wt && g.eptr) {
                 if (pre.valid && j < 2) lptr[e] = j == 0 ? pre.p0 : pre.p1;
                 else lptr[e] = g.eptr[e];
             }
         }
         const int incl = wave_incl_scan(lc);
-        const int iincl = wave_incl_scan(li);
-        int off = incl - lc, ui = iincl - li;
+        int off = incl - lc, ui[kItemTok], nu = 0;
+#pragma unroll
+        for (int c = 0; c < kItemTok; c++) {
+            const int ic = wave_incl_scan(nb[c]);
+            ui[c] = nu + ic - nb[c];
+            nu += __shfl(ic, 63, 64);
+        }
         for (int j = 0; j < EPL; j++) {
             const int e = eb + j;
             if (e >= E) break;
@@ -342,14 +361,20 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
                         mm &= mm - 1;
                     }
                     __builtin_memcpy(we.tok, &toks, sizeof(toks));
-                    g.wt[ui + it] = we;
+                    // the item's class: full items class 0, the last one by its size
+                    const int c = g.chunk > 0 ? kItemTok - (we.p1 - we.p0) : 0;
+                    int at = ui[0];
+#pragma unroll
+                    for (int c2 = 1; c2 < kItemTok; c2++) at = c == c2 ? ui[c2] : at;
+                    g.wt[at] = we;
+#pragma unroll
+                    for (int c2 = 0; c2 < kItemTok; c2++) ui[c2] += c == c2;
                 }
             }
             lmask[E + e] = off;
             off += cnt;
-            ui += nit;
         }
-        if (lane == 63) { s_nu = ui; s_valid = off; }
+        if (lane == 63) { s_nu = nu; s_valid = off; }
     }
     __syncthreads();
     const int nu = s_nu, nvalid = s_valid;
