@@ -1205,6 +1205,51 @@ __device__ __forceinline__ void kgroup_dot(const Q4KRegs (&r)[NM], const XL &X, 
     for (int m = 0; m < NM; m++) out[m] = half_lo(r[m].meta.x) * acc[m] - half_hi(r[m].meta.x) * accm[m];
 }
 
+// Q4_K against nt <= NT vectors at once: each sub-block's nibbles and
+// scales are unpacked once for all of them.
+template <int NT>
+__device__ __forceinline__ void kgroup_dot_n(const Q4KRegs &r, const XL (&X)[NT], int nt, float (&out)[NT])
+{
+    const uint32_t W0 = r.meta.y, W1 = r.meta.z, W2 = r.meta.w;
+    const uint32_t sclo = W0 & 0x3F3F3F3Fu, mlo = W1 & 0x3F3F3F3Fu;
+    const uint32_t schi = (W2 & 0x0F0F0F0Fu) | ((W0 >> 2) & 0x30303030u);
+    const uint32_t mhi = ((W2 >> 4) & 0x0F0F0F0Fu) | ((W1 >> 2) & 0x30303030u);
+    float acc[NT], accm[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = accm[t] = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 8; sb++) {
+        const int c = sb >> 1, sh = 8 * (sb & 3);
+        const float fsc = (float)(((c < 2 ? sclo : schi) >> sh) & 0xff);
+        const float fmn = (float)(((c < 2 ? mlo : mhi) >> sh) & 0xff);
+        uint32_t nib[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t qd = comp(r.q[2 * c + (i >> 2)], i & 3);
+            nib[i] = (sb & 1) ? (qd >> 4) & 0x0F0F0F0Fu : qd & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (t >= nt) break;
+            const int4 x0a = X[t].q0[2 * sb], x0b = X[t].q0[2 * sb + 1];
+            const int4 x1a = X[t].q1[2 * sb], x1b = X[t].q1[2 * sb + 1];
+            const int4 x2a = X[t].q2[2 * sb], x2b = X[t].q2[2 * sb + 1];
+            int a0 = 0, a1 = 0, a2 = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                a0 = dot4(nib[i], i < 4 ? w4(x0a, i) : w4(x0b, i - 4), a0);
+                a1 = dot4(nib[i], i < 4 ? w4(x1a, i) : w4(x1b, i - 4), a1);
+                a2 = dot4(nib[i], i < 4 ? w4(x2a, i) : w4(x2b, i - 4), a2);
+            }
+            acc[t] += fsc * (X[t].bs[sb] * fpieces(a0, a1, a2));
+            accm[t] += fmn * X[t].bsum[sb];
+        }
+    }
+    const float d = half_lo(r.meta.x), dmin = half_hi(r.meta.x);
+#pragma unroll
+    for (int t = 0; t < NT; t++) out[t] = d * acc[t] - dmin * accm[t];
+}
+
 // Q6_K: d * sum_b bs_b * sum_{j in b} sc_j * (Q_j - 32*S_j), Q_j / S_j piece dots / sums of sub-block j.
 template <int NM>
 __device__ __forceinline__ void kgroup_dot(const Q6KRegs (&r)[NM], const XL &X, float (&out)[NM])
@@ -1360,17 +1405,18 @@ constexpr int kTokPass = 4;  // <= kInlineTok
 constexpr int kGUPre = 2;     // record words per thread loaded before the weights
 constexpr int kGULds = 32768;   // staged token records per pass
 constexpr int kDnLds = 24576;   // staged pair records per pass
-constexpr int kDnPass = 8;
 constexpr int kDnPre = 4;       // record words per thread loaded before the weights
 
-// ALL: every token's record fits the first pass and the prefetch words
-// (T <= tpass, T * RB <= kGUPre * kGUThreads * 16); the records are then
-// loaded before the work entry arrives, token t to LDS slot t.
-template <int QT, bool ALL>
+// NTOK: tokens per pass at most (1, 2 or kTokPass).  NTOK <= 2 (ALL):
+// every token's record fits the first pass and the prefetch words (T <= 2,
+// T * RB <= kGUPre * kGUThreads * 16); the records are then loaded before
+// the work entry arrives, token t to LDS slot t.
+template <int QT, int NTOK>
 __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 2))) void k_gate_up(GateUpArgs a)
 {
     extern __shared__ __align__(16) uint8_t xs[];
     __shared__ float part[8][kTokPass][32][2];
+    constexpr bool ALL = NTOK <= 2;
 
     const int u = blockIdx.x / a.ntile;
     const int rt = blockIdx.x - u * a.ntile;
@@ -1462,15 +1508,42 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 load_regs(rg[0], mat + ((size_t)tile64 * S + s) * kTileBytes<QT>, lt);
                 loaded = s;
             }
-#pragma unroll 1
-            for (int tt = 0; tt < nt; tt++) {
-                float o[1];
+            if constexpr (QT == MOE_Q4_K) {
+                // all nt <= kTokPass tokens of the pass at once (ALL: a
+                // single pass, its tokens inline)
+                XL X[kTokPass];
+#pragma unroll
+                for (int tt = 0; tt < kTokPass; tt++)
+                    X[tt] = xl(xs + (ALL ? (int)((toks >> (8 * tt)) & 0xff) : tt) * RB, H, s);
+                float o[kTokPass];
                 opaque(rg[0]);
-                // ALL: a single pass, its tokens inline
-                const int xslot = ALL ? (int)((toks >> (8 * tt)) & 0xff) : tt;
-                kgroup_dot<1>(rg, xl(xs + xslot * RB, H, s), o);
-                if (s == slot) part[slot][tt][r][m] = o[0];
-                else part[slot][tt][r][m] += o[0];
+                if constexpr (NTOK < kTokPass) {
+                    XL Xn[NTOK];
+                    float on[NTOK];
+#pragma unroll
+                    for (int tt = 0; tt < NTOK; tt++) Xn[tt] = X[tt];
+                    kgroup_dot_n<NTOK>(rg[0], Xn, nt, on);
+#pragma unroll
+                    for (int tt = 0; tt < NTOK; tt++) o[tt] = on[tt];
+                } else {
+                    kgroup_dot_n<kTokPass>(rg[0], X, nt, o);
+                }
+#pragma unroll
+                for (int tt = 0; tt < kTokPass; tt++)
+                    if (tt < nt) {
+                        if (s == slot) part[slot][tt][r][m] = o[tt];
+                        else part[slot][tt][r][m] += o[tt];
+                    }
+            } else {
+#pragma unroll 1
+                for (int tt = 0; tt < nt; tt++) {
+                    float o[1];
+                    opaque(rg[0]);
+                    const int xslot = ALL ? (int)((toks >> (8 * tt)) & 0xff) : tt;
+                    kgroup_dot<1>(rg, xl(xs + xslot * RB, H, s), o);
+                    if (s == slot) part[slot][tt][r][m] = o[0];
+                    else part[slot][tt][r][m] += o[0];
+                }
             }
         }
         if (slot >= S)
@@ -1531,7 +1604,7 @@ template <int QT, bool ONE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 3))) void k_down(DownArgs a)
 {
     extern __shared__ __align__(16) uint8_t hsl[];
-    __shared__ float part[8][kDnPass][64];
+    __shared__ float part[8][kItemTok][64];
 
     const int u = blockIdx.x / a.nrt;
     const int rt = blockIdx.x - u * a.nrt;
@@ -1599,13 +1672,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
                 load_regs(rg[0], base + ((size_t)rt * S + s) * kTileBytes<QT>, lane);
                 loaded = s;
             }
-#pragma unroll 1
-            for (int tt = 0; tt < nt; tt++) {
-                float v[1];
+            if constexpr (QT == MOE_Q4_K) {
+                // all nt <= kItemTok pairs of the pass at once (tpass <= kItemTok)
+                XL X[kItemTok];
+#pragma unroll
+                for (int tt = 0; tt < kItemTok; tt++) X[tt] = xl(hsl + tt * RB, kd, s);
+                float v[kItemTok];
                 opaque(rg[0]);
-                kgroup_dot<1>(rg, xl(hsl + tt * RB, kd, s), v);
-                if (s == wv) part[wv][tt][lane] = v[0];
-                else part[wv][tt][lane] += v[0];
+                if constexpr (ONE) {
+                    XL X1[1] = {X[0]};
+                    float v1[1];
+                    kgroup_dot_n<1>(rg[0], X1, 1, v1);
+                    v[0] = v1[0];
+                } else {
+                    kgroup_dot_n<kItemTok>(rg[0], X, nt, v);
+                }
+#pragma unroll
+                for (int tt = 0; tt < kItemTok; tt++)
+                    if (tt < nt) {
+                        if (s == wv) part[wv][tt][lane] = v[tt];
+                        else part[wv][tt][lane] += v[tt];
+                    }
+            } else {
+#pragma unroll 1
+                for (int tt = 0; tt < nt; tt++) {
+                    float v[1];
+                    opaque(rg[0]);
+                    kgroup_dot<1>(rg, xl(hsl + tt * RB, kd, s), v);
+                    if (s == wv) part[wv][tt][lane] = v[0];
+                    else part[wv][tt][lane] += v[0];
+                }
             }
         }
         __syncthreads();
@@ -2134,10 +2230,11 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     const size_t glds = (size_t)ga.tpass * enc_bytes(d.H);
     dim3 ggrid(L.UI * ga.ntile);
     // every token's record staged up front when they all fit the first pass
-    const bool all = T <= ga.tpass && (size_t)T * enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16;
+    const bool all = T <= 2 && T <= ga.tpass && (size_t)T * enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16;
 #define GATE_UP(Q)                                                                        \
-    (all ? k_gate_up<Q, true><<<ggrid, kGUThreads, glds, s>>>(ga)                        \
-         : k_gate_up<Q, false><<<ggrid, kGUThreads, glds, s>>>(ga))
+    (all ? (T == 1 ? k_gate_up<Q, 1><<<ggrid, kGUThreads, glds, s>>>(ga)                 \
+                   : k_gate_up<Q, 2><<<ggrid, kGUThreads, glds, s>>>(ga))                \
+         : k_gate_up<Q, kTokPass><<<ggrid, kGUThreads, glds, s>>>(ga))
     switch (d.gate) {
     case MOE_Q4_K: GATE_UP(MOE_Q4_K); break;
     case MOE_Q6_K: GATE_UP(MOE_Q6_K); break;
@@ -2156,7 +2253,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     da.P = L.P;
     const int S = g.kd / 256;
     da.tpass = (int)(kDnLds / enc_bytes(g.kd));
-    if (da.tpass > kDnPass) da.tpass = kDnPass;
+    if (da.tpass > kItemTok) da.tpass = kItemTok;  // a work item has at most kItemTok pairs
     const size_t dlds = (size_t)da.tpass * enc_bytes(g.kd);
     dim3 dgrid(L.UI * da.nrt), dblock(64 * (S < 8 ? S : 8));
     // one token: item u is pair u, whose record is loaded up front when it fits
