@@ -355,10 +355,20 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
                     we.e = e; we.p0 = off + it * chunk; we.p1 = min(off + (it + 1) * chunk, off + cnt);
                     we.ptr = ptr;
                     uint64_t toks = 0;
-                    for (int i = 0; i < chunk && mm; i++) {
-                        const int t = __ffs(mm) - 1;
-                        if (i < kInlineTok) toks |= (uint64_t)t << (8 * i);
-                        mm &= mm - 1;
+                    if (g.chunk > 0) {
+                        // the item's (at most kItemTok) tokens, a fixed count of steps
+#pragma unroll
+                        for (int i = 0; i < kItemTok; i++) {
+                            const uint32_t t = (uint32_t)__builtin_ctz(mm | 0x80000000u);  // 31 once empty
+                            toks |= (uint64_t)(mm ? t : 0u) << (8 * i);
+                            mm &= mm - 1;
+                        }
+                    } else {
+                        for (int i = 0; i < chunk && mm; i++) {
+                            const int t = __ffs(mm) - 1;
+                            if (i < kInlineTok) toks |= (uint64_t)t << (8 * i);
+                            mm &= mm - 1;
+                        }
                     }
                     __builtin_memcpy(we.tok, &toks, sizeof(toks));
                     // the item's class: full items class 0, the last one by its size
