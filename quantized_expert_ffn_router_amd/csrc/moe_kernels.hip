@@ -55,7 +55,8 @@ constexpr int kChunk = 8;  // tokens per pass of the matvec kernels
 constexpr int kRouteThreads = 256;
 constexpr int kRouteRows = 2;                   // router rows per workgroup
 constexpr int kRouteTok = 8;                    // tokens per pass of a router workgroup
-constexpr int kEncThreads = 256;                // positions encoded per workgroup
+constexpr int kRouteWG = 512;                   // threads of a k_route workgroup
+constexpr int kEncPos = 512;                    // positions encoded per k_route encoding workgroup
 constexpr int kMaxK = 64;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -586,7 +587,7 @@ struct RouteArgs {
     GroupOut go;
     Enc hpad;               // [P] vectors of kd: padding blocks zeroed here
     int P, I, kd;
-    int n_expert_blocks;    // router workgroups; then T * H/256 encoding workgroups, then the tail
+    int n_expert_blocks;    // router workgroups; then T * ceil(H/kEncPos) encoding workgroups, then the tail
 };
 
 // Top-k of NT tokens' E keys each by one wave (no barriers), keys in
@@ -759,7 +760,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
 {
     __shared__ __align__(16) uint32_t lk[kStageKeys];
     __shared__ __align__(16) union {
-        uint64_t cand[kRouteThreads / 64][2][kCandSlots];  // top-k, per wave, two tokens at a time
+        uint64_t cand[kRouteWG / 64][2][kCandSlots];  // top-k, per wave, up to two tokens at a time
         int lstart[2 * kMaxE];                             // grouping, after the top-k
     } u;
     int *lstart = u.lstart;
@@ -793,7 +794,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
     int ok = 1;
     for (unsigned it = 0;; it++) {
         int missing = 0;
-        for (int i = tid; i < n; i += kRouteThreads) {
+        for (int i = tid; i < n; i += kRouteWG) {
             const uint32_t v = ld_coh_u(a.keys + i);
             if (staged) lk[i] = v;
             missing |= v == 0u;
@@ -806,10 +807,28 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         __builtin_amdgcn_s_sleep(1);
     }
     ok = __syncthreads_and(ok);
-    if (staged && E <= kWaveTopE) {
+    if (staged && E <= kWaveTopE && T <= kRouteWG / 64) {
+        // a wave per token: topk_multi on the token's staged keys
+        constexpr int NVL = kWaveTopE / 64;
+        const int t = wave_id();
+        if (t < T) {
+            uint32_t key[1][NVL];
+#pragma unroll
+            for (int i = 0; i < NVL; i++) {
+                const int e = lane + 64 * i;
+                key[0][i] = e < E ? lk[t * E + e] : 0u;
+            }
+            uint64_t cs[1];
+            topk_multi<NVL, 1>(key, E, k, &u.cand[t][0][0], kCandSlots, cs);
+            if (lane < k) {
+                sidx[t * k + lane] = (int)~(uint32_t)cs[0];
+                skey[t * k + lane] = (uint32_t)(cs[0] >> 32);
+            }
+        }
+    } else if (staged && E <= kWaveTopE) {
         // a wave per pair of tokens: topk_multi on the tokens' staged keys
         constexpr int NVL = kWaveTopE / 64;
-        for (int t0 = 2 * wave_id(); t0 < T; t0 += 2 * (kRouteThreads / 64)) {
+        for (int t0 = 2 * wave_id(); t0 < T; t0 += 2 * (kRouteWG / 64)) {
             uint32_t key[2][NVL];
 #pragma unroll
             for (int q = 0; q < 2; q++)
@@ -828,22 +847,22 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
                 }
         }
     } else if (staged) {
-        for (int t = wave_id(); t < T; t += kRouteThreads / 64)
+        for (int t = wave_id(); t < T; t += kRouteWG / 64)
             topk_wave_any<false>(lk + t * E, E, k, sidx + t * k, skey + t * k);
     } else {
-        for (int t = wave_id(); t < T; t += kRouteThreads / 64)
+        for (int t = wave_id(); t < T; t += kRouteWG / 64)
             topk_wave_any<true>(a.keys + (size_t)t * E, E, k, sidx + t * k, skey + t * k);
     }
     settle(pre);
     __syncthreads();
     // clear the keys for the next launch (plain stores: the launch boundary
     // makes them visible); nothing reads them again in this launch
-    for (int i = tid; i < n; i += kRouteThreads) a.keys[i] = 0u;
+    for (int i = tid; i < n; i += kRouteWG) a.keys[i] = 0u;
     // softmax over the k selected logits of each token (selection 0 is the
     // largest): for k <= 8, eight tokens per wave, lane 8q + j holding
     // selection j of token 8w + q; else a token per wave, lane j selection j
     const bool narrow = k <= 8;
-    for (int t0 = narrow ? 8 * wave_id() : wave_id(); t0 < T; t0 += narrow ? 8 * (kRouteThreads / 64) : kRouteThreads / 64) {
+    for (int t0 = narrow ? 8 * wave_id() : wave_id(); t0 < T; t0 += narrow ? 8 * (kRouteWG / 64) : kRouteWG / 64) {
         const int t = narrow ? t0 + (lane >> 3) : t0, j = narrow ? lane & 7 : lane;
         const bool live = j < k && t < T;
         const float lg = live ? unord_bits(skey[t * k + j]) : 0.f;
@@ -868,14 +887,14 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
 }
 
 // Router rows [e0, e0 + nr) against all tokens, NT tokens per pass; wave w
-// takes the 256-column chunks w, w+4, ... of H, and the partial sums meet in
+// takes the 256-column chunks w, w+8, ... of H, and the partial sums meet in
 // LDS.  Loads are unconditional (row and token indices clamped; results for
 // clamped tokens are dropped), so that each pass issues all of its loads at
 // once.
 template <int NT>
 __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
 {
-    __shared__ float part[kRouteThreads / 64][kRouteRows + 1][NT];
+    __shared__ float part[kRouteWG / 64][kRouteRows + 1][NT];
     const int H = a.H, T = a.T, E = a.E, nv = H >> 8;
     const int w = wave_id(), lane = lane_id();
     const float4 *wrow[kRouteRows];
@@ -893,7 +912,7 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
             for (int r = 0; r < kRouteRows; r++) acc[r][tt] = 0.f;
         }
 #pragma unroll 2
-        for (int c = w; c < nv; c += kRouteThreads / 64) {
+        for (int c = w; c < nv; c += kRouteWG / 64) {
             float4 wv[kRouteRows], hv[NT];
 #pragma unroll
             for (int r = 0; r < kRouteRows; r++) wv[r] = wrow[r][c * 64 + lane];
@@ -924,7 +943,7 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
             if (t < T) {
                 float d = 0.f, q = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < kRouteThreads / 64; ww++) {
+                for (int ww = 0; ww < kRouteWG / 64; ww++) {
                     d += part[ww][r][tt];
                     q += part[ww][kRouteRows][tt];
                 }
@@ -939,24 +958,26 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
     }
 }
 
-// Router workgroup: 2 router rows against all T tokens, the 4 waves
-// splitting H; the logits go to the tail as keys.  Encoding workgroup (t, c): RMS of token t,
-// then positions [256c, 256c+256).  The last workgroup is the tail.
-__global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
+// Router workgroup: 2 router rows against all T tokens, the 8 waves
+// splitting H; the logits go to the tail as keys.  Encoding workgroup (t, c):
+// RMS of token t, then positions [kEncPos c, kEncPos c + kEncPos).  The last
+// workgroup is the tail.
+__global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
 {
-    __shared__ float red[8];
+    __shared__ float red[kRouteWG / 64];
 
     const int H = a.H, T = a.T, E = a.E;
     const int blk = blockIdx.x;
     const int lane = lane_id();
-    const int nv = H >> 8;  // float4 per lane per row
     if (blk == (int)gridDim.x - 1) {
         route_tail(a);
         return;
     }
     if (blk >= a.n_expert_blocks) {
+        // encoding workgroup (t, c): positions [kEncPos c, kEncPos c + kEncPos) of token t
+        const int ne = (H + kEncPos - 1) / kEncPos;
         const int g = blk - a.n_expert_blocks;
-        const int t = g / nv, c = g - t * nv;
+        const int t = g / ne, c = g - t * ne;
         const float4 *hr = (const float4 *)(a.h + (size_t)t * H);
         float ss = 0.f;
         for (int i = threadIdx.x; i < H / 4; i += blockDim.x) {
@@ -967,14 +988,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         if (lane == 0) red[wave_id()] = ss;
         __syncthreads();
         ss = 0.f;
-        for (int i = 0; i < kRouteThreads / 64; i++) ss += red[i];
+        for (int i = 0; i < kRouteWG / 64; i++) ss += red[i];
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
-        const int pos = c * 256 + threadIdx.x;
-        const float xv = a.h[(size_t)t * H + pos] * r;
-        encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
-        if (a.xhat) a.xhat[(size_t)t * H + pos] = xv;
+        const int pos = c * kEncPos + threadIdx.x;
+        if (pos < H) {  // whole waves (H is a multiple of 256)
+            const float xv = a.h[(size_t)t * H + pos] * r;
+            encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
+            if (a.xhat) a.xhat[(size_t)t * H + pos] = xv;
+        }
         if (a.kd > a.I) {
-            const int nenc = T * nv;
+            const int nenc = T * ne;
             for (int p = g; p < a.P; p += nenc)
                 zero_blocks(rec_at(a.hpad, p, a.kd), a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
         }
@@ -2384,7 +2407,7 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
     a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows;
-    k_route<<<a.n_expert_blocks + T * (d->H / kEncThreads) + 1, kRouteThreads, 0, s>>>(a);
+    k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + 1, kRouteWG, 0, s>>>(a);
     LAUNCH_OK("k_route");
     return MOE_OK;
 }
