@@ -365,9 +365,10 @@ __device__ __forceinline__ void group_block(const int *sidx, int T, int k, int E
                             mm &= mm - 1;
                         }
                     } else {
-                        for (int i = 0; i < chunk && mm; i++) {
+                        // the first kInlineTok tokens inline; the rest are read from ptok
+                        for (int i = 0; i < kInlineTok && mm; i++) {
                             const int t = __ffs(mm) - 1;
-                            if (i < kInlineTok) toks |= (uint64_t)t << (8 * i);
+                            toks |= (uint64_t)t << (8 * i);
                             mm &= mm - 1;
                         }
                     }
@@ -587,7 +588,7 @@ struct RouteArgs {
     GroupOut go;
     Enc hpad;               // [P] vectors of kd: padding blocks zeroed here
     int P, I, kd;
-    int n_expert_blocks;    // router workgroups; then T * ceil(H/kEncPos) encoding workgroups, then the tail
+    int n_expert_blocks;    // router workgroups (row pair, token group); then T * ceil(H/kEncPos) encoding workgroups, then the tail
 };
 
 // Top-k of NT tokens' E keys each by one wave (no barriers), keys in
@@ -760,7 +761,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
 {
     __shared__ __align__(16) uint32_t lk[kStageKeys];
     __shared__ __align__(16) union {
-        uint64_t cand[kRouteWG / 64][2][kCandSlots];  // top-k, per wave, up to two tokens at a time
+        uint64_t cand[kRouteWG / 64][kCandSlots];  // top-k, per wave
         int lstart[2 * kMaxE];                             // grouping, after the top-k
     } u;
     int *lstart = u.lstart;
@@ -807,11 +808,10 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         __builtin_amdgcn_s_sleep(1);
     }
     ok = __syncthreads_and(ok);
-    if (staged && E <= kWaveTopE && T <= kRouteWG / 64) {
+    if (staged && E <= kWaveTopE) {
         // a wave per token: topk_multi on the token's staged keys
         constexpr int NVL = kWaveTopE / 64;
-        const int t = wave_id();
-        if (t < T) {
+        for (int t = wave_id(); t < T; t += kRouteWG / 64) {
             uint32_t key[1][NVL];
 #pragma unroll
             for (int i = 0; i < NVL; i++) {
@@ -819,32 +819,11 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
                 key[0][i] = e < E ? lk[t * E + e] : 0u;
             }
             uint64_t cs[1];
-            topk_multi<NVL, 1>(key, E, k, &u.cand[t][0][0], kCandSlots, cs);
+            topk_multi<NVL, 1>(key, E, k, u.cand[wave_id()], kCandSlots, cs);
             if (lane < k) {
                 sidx[t * k + lane] = (int)~(uint32_t)cs[0];
                 skey[t * k + lane] = (uint32_t)(cs[0] >> 32);
             }
-        }
-    } else if (staged && E <= kWaveTopE) {
-        // a wave per pair of tokens: topk_multi on the tokens' staged keys
-        constexpr int NVL = kWaveTopE / 64;
-        for (int t0 = 2 * wave_id(); t0 < T; t0 += 2 * (kRouteWG / 64)) {
-            uint32_t key[2][NVL];
-#pragma unroll
-            for (int q = 0; q < 2; q++)
-#pragma unroll
-                for (int i = 0; i < NVL; i++) {
-                    const int e = lane + 64 * i, t = min(t0 + q, T - 1);
-                    key[q][i] = e < E ? lk[t * E + e] : 0u;
-                }
-            uint64_t cs[2];
-            topk_multi<NVL, 2>(key, E, k, &u.cand[wave_id()][0][0], kCandSlots, cs);
-#pragma unroll
-            for (int q = 0; q < 2; q++)
-                if (lane < k && t0 + q < T) {
-                    sidx[(t0 + q) * k + lane] = (int)~(uint32_t)cs[q];
-                    skey[(t0 + q) * k + lane] = (uint32_t)(cs[q] >> 32);
-                }
         }
     } else if (staged) {
         for (int t = wave_id(); t < T; t += kRouteWG / 64)
@@ -892,7 +871,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
 // clamped tokens are dropped), so that each pass issues all of its loads at
 // once.
 template <int NT>
-__device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
+__device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr, int tb, int te)
 {
     __shared__ float part[kRouteWG / 64][kRouteRows + 1][NT];
     const int H = a.H, T = a.T, E = a.E, nv = H >> 8;
@@ -900,7 +879,7 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr)
     const float4 *wrow[kRouteRows];
 #pragma unroll
     for (int r = 0; r < kRouteRows; r++) wrow[r] = (const float4 *)(a.wr + (size_t)(r < nr ? e0 + r : e0) * H);
-    for (int t0 = 0; t0 < T; t0 += NT) {
+    for (int t0 = tb; t0 < te; t0 += NT) {
         const float4 *hrow[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) hrow[tt] = (const float4 *)(a.h + (size_t)min(t0 + tt, T - 1) * H);
@@ -1004,12 +983,15 @@ __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
         return;
     }
 
-    const int e0 = blk * kRouteRows;
+    // router workgroup (row pair, token group of kRouteTok)
+    const int npair = (E + kRouteRows - 1) / kRouteRows;
+    const int grp = blk / npair;
+    const int e0 = (blk - grp * npair) * kRouteRows;
     const int nr = E - e0 < kRouteRows ? E - e0 : kRouteRows;
-    if (T == 1) router_rows<1>(a, e0, nr);
-    else if (T == 2) router_rows<2>(a, e0, nr);
-    else if (T <= 4) router_rows<4>(a, e0, nr);
-    else router_rows<kRouteTok>(a, e0, nr);
+    if (T == 1) router_rows<1>(a, e0, nr, 0, 1);
+    else if (T == 2) router_rows<2>(a, e0, nr, 0, 2);
+    else if (T <= 4) router_rows<4>(a, e0, nr, 0, T);
+    else router_rows<kRouteTok>(a, e0, nr, grp * kRouteTok, min(T, grp * kRouteTok + kRouteTok));
 }
 
 // k_route_token: stand-alone routing, one workgroup per token (16 waves
@@ -2406,7 +2388,8 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.group = 1; a.ns = n_shared; a.go = W.group(!use_mfma(*d, T));
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
-    a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows;
+    // router workgroups: row pairs x token groups of kRouteTok
+    a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows * ((T + kRouteTok - 1) / kRouteTok);
     k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + 1, kRouteWG, 0, s>>>(a);
     LAUNCH_OK("k_route");
     return MOE_OK;
