@@ -93,9 +93,16 @@ constexpr size_t enc_bytes(int K) { return (size_t)4 * K; }
 // parallel workgroups.
 constexpr int kItemTok = 4;
 
+// Half-precision records of the MFMA path, one per (vector, 256-position
+// super-block): the positions times 2^e (e brings the super-block's largest
+// magnitude to [0.5, 1)) split into fp16 hi + lo, [hi 256][lo 256] halves,
+// the 32-position block sums of the scaled values as fp16 hi [8] and lo [8],
+// then 2^-e as fp32 and padding.
+constexpr int kX16Bytes = 1072;
+
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U, UI;  // U: distinct experts, UI: work items (both at most)
-    size_t keys, xenc, xhat, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
+    size_t keys, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -112,7 +119,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     size_t o = kKeys + kKeysBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
-    L.xhat = take((size_t)T * d.H * 4);
+    L.x16 = take((size_t)T * (d.H / 256) * kX16Bytes);
     L.idx = take((size_t)T * k * 4);
     L.w = take((size_t)T * k * 4);
     L.nuniq = take(4);

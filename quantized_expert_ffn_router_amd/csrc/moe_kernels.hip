@@ -207,6 +207,35 @@ __device__ __forceinline__ void encode32(float v, int r, uint8_t *rec, int K, in
     }
 }
 
+// One position of a half-precision (MFMA) record: 256 consecutive threads
+// (a quarter or half of the workgroup, whole waves) hold positions p =
+// 0..255 of one super-block, v their value (0 past the vector's end); rec is
+// the super-block's record (kX16Bytes).  The largest magnitude comes from
+// the group's waves through redm (LDS, one float per wave); every thread of
+// the workgroup calls this (it holds barriers).
+__device__ __forceinline__ void encode_x16(float v, uint8_t *rec, int p, bool live, float *redm)
+{
+    const float am = group_max<64>(fabsf(v));
+    if (lane_id() == 0) redm[wave_id()] = am;
+    __syncthreads();
+    const int g0 = wave_id() & ~3;
+    const float cm = fmaxf(fmaxf(redm[g0], redm[g0 + 1]), fmaxf(redm[g0 + 2], redm[g0 + 3]));
+    __syncthreads();  // redm is free again
+    if (!live) return;
+    const int e = cm > 0.f ? -ilogbf(cm) - 1 : 0;  // cm * 2^e in [0.5, 1)
+    const float x = v * ldexpf(1.0f, e);           // exact (power of two)
+    const _Float16 xh = (_Float16)x;
+    ((_Float16 *)rec)[p] = xh;
+    ((_Float16 *)(rec + 512))[p] = (_Float16)(x - (float)xh);
+    const float s32 = group_sum<32>(x);
+    if ((p & 31) == 0) {
+        const _Float16 sh = (_Float16)s32;
+        ((_Float16 *)(rec + 1024))[p >> 5] = sh;
+        ((_Float16 *)(rec + 1040))[p >> 5] = (_Float16)(s32 - (float)sh);
+    }
+    if (p == 0) *(float *)(rec + 1056) = ldexpf(1.0f, -e);
+}
+
 // Zero blocks [b0, b1) of a record (padding columns of the down rows).
 __device__ void zero_blocks(uint8_t *rec, int K, int b0, int b1, int tid, int nthr)
 {
@@ -582,7 +611,7 @@ struct RouteArgs {
     float *w2;
     float *logits2;
     Enc x;                  // [T] vectors of H
-    float *xhat;            // [T][H] normalised states (fp32), or null
+    uint8_t *x16;           // [T][H/256] half-precision records of the normalised states, or null
     int group;
     int ns;
     GroupOut go;
@@ -943,7 +972,7 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr, 
 // workgroup is the tail.
 __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
 {
-    __shared__ float red[kRouteWG / 64];
+    __shared__ float red[kRouteWG / 64], redx[kRouteWG / 64];
 
     const int H = a.H, T = a.T, E = a.E;
     const int blk = blockIdx.x;
@@ -970,11 +999,12 @@ __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
         for (int i = 0; i < kRouteWG / 64; i++) ss += red[i];
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
         const int pos = c * kEncPos + threadIdx.x;
+        const float xv = pos < H ? a.h[(size_t)t * H + pos] * r : 0.f;
         if (pos < H) {  // whole waves (H is a multiple of 256)
-            const float xv = a.h[(size_t)t * H + pos] * r;
             encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
-            if (a.xhat) a.xhat[(size_t)t * H + pos] = xv;
         }
+        if (a.x16)
+            encode_x16(xv, a.x16 + ((size_t)t * (H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, pos < H, redx);
         if (a.kd > a.I) {
             const int nenc = T * ne;
             for (int p = g; p < a.P; p += nenc)
@@ -1045,6 +1075,7 @@ struct PrepArgs {
     const float *w;  // [T][k] routing weights
     float *yzero;    // [T][H] cleared here (the FFN adds into it), or null
     Enc xe;
+    uint8_t *x16;    // [T][H/256] half-precision records of x, or null
     GroupOut go;
     Enc hpad;
     int P, I, kd;
@@ -1054,10 +1085,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
 {
     __shared__ int sidx[kMaxT * kMaxK];
     __shared__ int lstart[2 * kMaxE];
+    __shared__ float redm[kRouteThreads / 64];
     const int t = blockIdx.x;
     for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x) {
-        encode32(a.x[(size_t)t * a.H + pos], threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31);
+        const float v = a.x[(size_t)t * a.H + pos];
+        encode32(v, threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31);
         if (a.yzero) a.yzero[(size_t)t * a.H + pos] = 0.f;
+        // blockDim = 256: one super-block per pass (H is a multiple of 256)
+        if (a.x16) encode_x16(v, a.x16 + ((size_t)t * (a.H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, true, redm);
     }
     if (a.kd > a.I)
         for (int p = t; p < a.P; p += a.T)
@@ -1136,6 +1171,12 @@ typedef const __attribute__((address_space(1))) uint8_t gbyte;
 template <class T> __device__ __forceinline__ T ldg(const uint8_t *p, int off)
 {
     return *(const __attribute__((address_space(1))) T *)((gbyte *)p + off);
+}
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <> __device__ __forceinline__ uint2 ldg<uint2>(const uint8_t *p, int off)
+{
+    const u32x2 v = *(const __attribute__((address_space(1))) u32x2 *)((gbyte *)p + off);
+    return make_uint2(v.x, v.y);
 }
 template <> __device__ __forceinline__ uint4 ldg<uint4>(const uint8_t *p, int off)
 {
@@ -1755,14 +1796,16 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMfmaCols = 32;  // columns (tokens or pairs) per expert
-// LDS of one staged super-block: hi and lo [16 K-steps][2 halves][32 cols][8],
-// block sums hi and lo [2][32][4], column scales [32].
-constexpr int kStageHalf = 16 * 2 * kMfmaCols * 8;       // halves per part
-constexpr int kStageSum = 2 * kMfmaCols * 4;            // halves per part
-constexpr size_t kStageBytes = (size_t)(2 * kStageHalf + 2 * kStageSum) * 2 + kMfmaCols * 4;
+// LDS of one staged super-block: hi and lo [16 K-steps][2 halves][32 cols][8]
+// (for one column, its 256 positions in order, in 32 chunks of 8 that lie
+// 32 columns apart), block sums [hi, lo][32 cols][8 blocks], column scales
+// [32] (+32 unused, the second half-wave's target when staged by DMA).
+constexpr int kStageHalf = 16 * 2 * kMfmaCols * 8;  // halves per part
+constexpr int kStageSum = 2 * kMfmaCols * 8;       // halves
+constexpr size_t kStageBytes = (size_t)(2 * kStageHalf + kStageSum) * 2 + 2 * kMfmaCols * 4;
 
 struct Stage {
-    _Float16 *hi, *lo, *shi, *slo;
+    _Float16 *hi, *lo, *sum;
     float *esc;
 };
 __device__ __forceinline__ Stage stage_at(uint8_t *base)
@@ -1770,9 +1813,8 @@ __device__ __forceinline__ Stage stage_at(uint8_t *base)
     Stage st;
     st.hi = (_Float16 *)base;
     st.lo = st.hi + kStageHalf;
-    st.shi = st.lo + kStageHalf;
-    st.slo = st.shi + kStageSum;
-    st.esc = (float *)(st.slo + kStageSum);
+    st.sum = st.lo + kStageHalf;
+    st.esc = (float *)(st.sum + kStageSum);
     return st;
 }
 
@@ -1861,11 +1903,36 @@ __device__ __forceinline__ void stage_store(const StageRegs<NT> &r, Stage st, in
             *(f16x8 *)(st.hi + ((s * 2 + kh) * kMfmaCols + c) * 8) = h;
             *(f16x8 *)(st.lo + ((s * 2 + kh) * kMfmaCols + c) * 8) = l;
         }
-        // block sums: A'' lane l holds column l%32, blocks (l/32)*4 + [0,4)
+        // block sums
         const _Float16 sh = (_Float16)sum;
-        st.shi[((b >> 2) * kMfmaCols + c) * 4 + (b & 3)] = sh;
-        st.slo[((b >> 2) * kMfmaCols + c) * 4 + (b & 3)] = (_Float16)(sum - (float)sh);
+        st.sum[c * 8 + b] = sh;
+        st.sum[(kMfmaCols + c) * 8 + b] = (_Float16)(sum - (float)sh);
         if (b == 0) st.esc[c] = ldexpf(1.0f, -e);
+    }
+}
+
+// Staging of one super-block of up to 32 columns from their half-precision
+// records by LDS DMA (16 bytes per lane, 34 wave instructions spread over
+// the workgroup's nw waves).  rec: this lane's column's record of the
+// super-block (column lane%32).  Instruction i < 32 copies chunks 2i' and
+// 2i'+1 (i' = i%16) of hi (i < 16) or lo: lane l takes chunk 2i' + l/32 of
+// column l%32, which lies at LDS offset 1024i' + 16l; instruction 32 the
+// block sums (lane l: part l/32 of column l%32), 33 the column scales.
+__device__ __forceinline__ void stage_dma(const uint8_t *rec, Stage st, int nw)
+{
+    typedef const __attribute__((address_space(1))) void *gsrc;
+    typedef __attribute__((address_space(3))) void *ldst;
+    const int wv = wave_id(), half = lane_id() >> 5;
+    for (int job = wv; job < 34; job += nw) {
+        if (job < 32) {
+            const int part = job >> 4, i = job & 15;
+            __builtin_amdgcn_global_load_lds((gsrc)(rec + part * 512 + (2 * i + half) * 16),
+                                             (ldst)((part ? st.lo : st.hi) + i * 2 * kMfmaCols * 8), 16, 0, 0);
+        } else if (job == 32) {
+            __builtin_amdgcn_global_load_lds((gsrc)(rec + 1024 + half * 16), (ldst)st.sum, 16, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds((gsrc)(rec + 1056), (ldst)st.esc, 4, 0, 0);
+        }
     }
 }
 
@@ -1879,9 +1946,9 @@ struct Q4KRow {
 };
 __device__ __forceinline__ void load_q4k_row(Q4KRow &w, const uint8_t *tile, int row64, int kh)
 {
-    w.meta = *(const uint4 *)(tile + row64 * 16);
+    w.meta = ldg<uint4>(tile, row64 * 16);
 #pragma unroll
-    for (int g = 0; g < 8; g++) w.q[g] = *(const uint2 *)(tile + 1024 + g * 1024 + row64 * 16 + kh * 8);
+    for (int g = 0; g < 8; g++) w.q[g] = ldg<uint2>(tile, 1024 + g * 1024 + row64 * 16 + kh * 8);
 }
 
 // 4 bytes of quants -> 4 fp16 (sc * q), q the low (HI=false) or high nibbles.
@@ -1934,12 +2001,13 @@ __device__ __forceinline__ void mfma_super(const Q4KRow &w, Stage st, int lane, 
             }
         }
     }
-    // min term: A'' = block sums (columns x 8 blocks), B'' = m_b (blocks x rows)
+    // min term: A'' = block sums (columns x 8 blocks; lane l holds column
+    // l%32, blocks (l/32)*4 + [0,4)), B'' = m_b (blocks x rows)
     const uint32_t mw = kh ? mhi : mlo;
     const f16x4 bm = {(_Float16)(float)(mw & 0xff), (_Float16)(float)((mw >> 8) & 0xff),
                       (_Float16)(float)((mw >> 16) & 0xff), (_Float16)(float)(mw >> 24)};
-    const f16x4 sh = *(const f16x4 *)(st.shi + (kh * kMfmaCols + col) * 4);
-    const f16x4 sl = *(const f16x4 *)(st.slo + (kh * kMfmaCols + col) * 4);
+    const f16x4 sh = *(const f16x4 *)(st.sum + col * 8 + kh * 4);
+    const f16x4 sl = *(const f16x4 *)(st.sum + (kMfmaCols + col) * 8 + kh * 4);
     f32x16 c2 = {};
     c2 = __builtin_amdgcn_mfma_f32_32x32x8f16(sh, bm, c2, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_f32_32x32x8f16(sl, bm, c2, 0, 0, 0);
@@ -1962,7 +2030,7 @@ struct GateUpMfmaArgs {
     const WorkEntry *wt;
     const int *nuniq;
     const int *ptok;
-    const float *x;     // [T][H] normalised states
+    const uint8_t *x16; // [T][H/256] half-precision records of the normalised states
     int H, I, kd;
     unsigned long long up_off;
     float *hf;          // [P][kd] SiLU(g)*u
@@ -1976,9 +2044,7 @@ constexpr int kDnMfmaThreads = 128;
 __global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ int lmax[kMfmaCols];
     __shared__ float xg[2][kMfmaCols][33];
-    if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;
     const int nitems = uni(*a.nuniq) * a.nrb;
     const int wv = wave_id(), lane = lane_id();
     const int hr = wv & 1;  // 32-row half of the 64-row block
@@ -1993,27 +2059,28 @@ __global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs 
         const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]);
         const int row64 = hr * 32 + (lane & 31), row = rb * 64 + row64;
         const uint8_t *mat = base + (wv >= 2 ? a.up_off : 0);
-        auto rowof = [&](int c) { return token_of(we, a.ptok, p0 + c); };
+        // this lane's column's records (columns past the item's repeat its
+        // last token; their results are dropped)
+        const uint8_t *rec =
+            a.x16 + (size_t)token_of(we, a.ptok, p0 + min(lane & 31, n - 1)) * S * kX16Bytes;
         float acc[16];
 #pragma unroll
         for (int j = 0; j < 16; j++) acc[j] = 0.f;
-        StageRegs<kGUMfmaThreads> sr;
-        stage_load<kGUMfmaThreads>(sr, a.x, a.H, a.H, 0, n, rowof);
+        __syncthreads();  // the previous item is done with the staging buffers and xg
+        stage_dma(rec, stage_at(smem), kGUMfmaThreads / 64);
         Q4KRow w;
         load_q4k_row(w, mat + ((size_t)rb * S) * kTileBytes<MOE_Q4_K>, row64, kh);
-        __syncthreads();  // the previous item is done with the staging buffers and xg
-        stage_store<kGUMfmaThreads>(sr, stage_at(smem), lmax);
         for (int sb = 0; sb < S; sb++) {
+            __syncthreads();  // stage sb has landed; buffer (sb+1)&1 is free
             Q4KRow wn;
-            if (sb + 1 < S) load_q4k_row(wn, mat + ((size_t)rb * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
-            __syncthreads();  // stage sb is complete
+            if (sb + 1 < S) {  // the next super-block's records and weights, in flight during this one's MFMAs
+                stage_dma(rec + (size_t)(sb + 1) * kX16Bytes, stage_at(smem + ((sb + 1) & 1) * kStageBytes),
+                          kGUMfmaThreads / 64);
+                load_q4k_row(wn, mat + ((size_t)rb * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
+            }
             opaque(w);
             mfma_super(w, stage_at(smem + (sb & 1) * kStageBytes), lane, acc);
-            if (sb + 1 < S) {  // stage the next super-block while the other buffer is in use
-                stage_load<kGUMfmaThreads>(sr, a.x, a.H, a.H, sb + 1, n, rowof);
-                stage_store<kGUMfmaThreads>(sr, stage_at(smem + ((sb + 1) & 1) * kStageBytes), lmax);
-                w = wn;
-            }
+            if (sb + 1 < S) w = wn;
         }
         // SiLU(g) * u: the gate waves hand their values over through LDS
         if (wv < 2) {
@@ -2195,7 +2262,7 @@ bool use_mfma(const moe_expert_desc &d, int T)
 // The FFN launches add into y (moe_expert_ffn clears it first when not
 // accumulating); the routing is the grouping in the workspace.
 moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int E, const void *const *eptr,
-                           const void *const *sptr, const float *src, float *y, float *act_out, hipStream_t s)
+                           const void *const *sptr, float *y, float *act_out, hipStream_t s)
 {
     const WsLayout &L = ws.L;
     const size_t lds = 2 * kStageBytes;
@@ -2208,7 +2275,7 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     GateUpMfmaArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
     ga.wt = ws.at<WorkEntry>(L.wt); ga.ptok = ws.at<int>(L.ptok);
-    ga.x = src; ga.H = d.H; ga.I = d.I; ga.kd = g.kd; ga.up_off = g.up_off;
+    ga.x16 = ws.at<uint8_t>(L.x16); ga.H = d.H; ga.I = d.I; ga.kd = g.kd; ga.up_off = g.up_off;
     ga.hf = ws.at<float>(L.hf); ga.act_out = act_out;
     ga.nrb = d.I / 64;
     ga.nuniq = ws.at<int>(L.nuniq);
@@ -2226,10 +2293,10 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
 }
 
 moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
-                              const void *const *eptr, const void *const *sptr, const float *src, float *y,
+                              const void *const *eptr, const void *const *sptr, float *y,
                               float *act_out, hipStream_t s)
 {
-    if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, E, eptr, sptr, src, y, act_out, s);
+    if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, E, eptr, sptr, y, act_out, s);
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -2360,10 +2427,11 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     pa.x = x; pa.T = T; pa.H = d->H; pa.k = k; pa.E = E; pa.ns = n_shared; pa.idx = idx; pa.w = w;
     pa.yzero = accumulate ? nullptr : y;
     pa.xe = W.x(); pa.go = W.group(!use_mfma(*d, T)); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
+    pa.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
-    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, x, y, act_out, s);
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, y, act_out, s);
 }
 
 moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, const float *w_router,
@@ -2384,7 +2452,7 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.keys = W.at<unsigned>(W.L.keys); a.idx = W.at<int>(W.L.idx); a.w = W.at<float>(W.L.w);
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
     a.x = W.x();
-    a.xhat = use_mfma(*d, T) ? W.at<float>(W.L.xhat) : nullptr;
+    a.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
     a.group = 1; a.ns = n_shared; a.go = W.group(!use_mfma(*d, T));
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
@@ -2406,7 +2474,7 @@ moe_status moe_layer_ffn(const moe_expert_desc *d, float *h, int32_t T, int32_t 
     if (!h || !expert_ptrs || (n_shared > 0 && !shared_ptrs)) { set_error("moe_layer_ffn: null pointer"); return MOE_ERR_ARG; }
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
-    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, W.at<float>(W.L.xhat), h, nullptr, s);
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, h, nullptr, s);
 }
 
 moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, const float *w_router, const float *bias,
