@@ -2148,12 +2148,14 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
     stage_store<kDnMfmaThreads>(sr, stage_at(smem), lmax);
     for (int sb = 0; sb < S; sb++) {
         Q4KRow wn;
-        if (sb + 1 < S) load_q4k_row(wn, base + ((size_t)rt * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
+        if (sb + 1 < S) {  // the next super-block's weights and h, in flight during this one's MFMAs
+            load_q4k_row(wn, base + ((size_t)rt * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
+            stage_load<kDnMfmaThreads>(sr, a.hf, a.kd, a.I, sb + 1, n, rowof);
+        }
         __syncthreads();  // stage sb is complete
         opaque(w);
         mfma_super(w, stage_at(smem + (sb & 1) * kStageBytes), lane, acc);
-        if (sb + 1 < S) {  // stage the next super-block while the other buffer is in use
-            stage_load<kDnMfmaThreads>(sr, a.hf, a.kd, a.I, sb + 1, n, rowof);
+        if (sb + 1 < S) {  // convert the next super-block into the other buffer
             stage_store<kDnMfmaThreads>(sr, stage_at(smem + ((sb + 1) & 1) * kStageBytes), lmax);
             w = wn;
         }
