@@ -114,6 +114,31 @@ template <int N> __device__ __forceinline__ float group_max(float v)
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// Wave sums of N values at once (N a multiple of 8), written to dst[0, nv):
+// three exchange steps across lanes 32, 16 and 8 apart each keep half of
+// the values per lane (the half given away is added into the partner's),
+// then an 8-lane sum finishes the N/8 values each lane group holds.
+// 1.25 N exchanges instead of the 6 N of N separate wave sums.
+template <int N> __device__ __forceinline__ void wave_sums_to(const float (&v)[N], float *dst, int nv)
+{
+    static_assert(N % 8 == 0, "N must be a multiple of 8");
+    const int lane = lane_id();
+    float a[N / 2], b[N / 4], c[N / 8];
+    const bool u5 = lane & 32, u4 = lane & 16, u3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < N / 2; i++) a[i] = (u5 ? v[i + N / 2] : v[i]) + xchg<32>(u5 ? v[i] : v[i + N / 2]);
+#pragma unroll
+    for (int i = 0; i < N / 4; i++) b[i] = (u4 ? a[i + N / 4] : a[i]) + xchg<16>(u4 ? a[i] : a[i + N / 4]);
+#pragma unroll
+    for (int i = 0; i < N / 8; i++) c[i] = group_sum<8>((u3 ? b[i + N / 8] : b[i]) + xchg<8>(u3 ? b[i] : b[i + N / 8]));
+    if ((lane & 7) == 0) {
+        const int base = (u5 ? N / 2 : 0) + (u4 ? N / 4 : 0) + (u3 ? N / 8 : 0);
+#pragma unroll
+        for (int i = 0; i < N / 8; i++)
+            if (base + i < nv) dst[base + i] = c[i];
+    }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele steps
 // inside 16-lane rows (row_shr 1, 2, 4, 8), then the row totals carried
 // across rows with row_bcast:15 and row_bcast:31.
@@ -935,16 +960,18 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr, 
                     acc[r][tt] += wv[r].x * x.x + wv[r].y * x.y + wv[r].z * x.z + wv[r].w * x.w;
             }
         }
+        // the wave's partial dots and sums of squares, all reduced at once
+        constexpr int NV = (kRouteRows + 1) * NT, N8 = (NV + 7) / 8 * 8;
+        float vals[N8];
+#pragma unroll
+        for (int i = 0; i < N8; i++) vals[i] = 0.f;
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) {
-            const float q = wave_sum(ss[tt]);
-            if (lane == 0) part[w][kRouteRows][tt] = q;
 #pragma unroll
-            for (int r = 0; r < kRouteRows; r++) {
-                const float d = wave_sum(acc[r][tt]);
-                if (lane == 0) part[w][r][tt] = d;
-            }
+            for (int r = 0; r < kRouteRows; r++) vals[r * NT + tt] = acc[r][tt];
+            vals[kRouteRows * NT + tt] = ss[tt];
         }
+        wave_sums_to<N8>(vals, &part[w][0][0], NV);
         __syncthreads();
         if ((int)threadIdx.x < nr * NT) {
             const int r = threadIdx.x / NT, tt = threadIdx.x % NT, t = t0 + tt;
