@@ -228,17 +228,49 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int):
         stats = cs.cache.stats()
         copy_s = cs.copy_ms() * 1e-3
         cs.close()
-        legs.append({
+        leg = {
             "pool_fraction": f, "slots": int(slots[0]), "tokens_per_s": round(steps / el, 2),
             "hit_rate": round(stats["hits"] / stats["lookups"], 4),
             "hit_rate_le8": round(stats["hits_le8"] / max(1, stats["lookups_le8"]), 4),
             "misses_per_token": round(stats["misses"] / steps, 2),
             "upload_bytes": int(stats["upload_bytes"]),
             "upload_GBps": round(stats["upload_bytes"] / copy_s / 1e9, 2) if copy_s > 0 else None,
-        })
+        }
+        # the same trace with the LRU on the device: eager steps, then replays
+        # of one captured step (input copied in before each replay); each run
+        # starts from a cold pool and must reproduce the host run's counts
+        for mode in ("eager", "graph"):
+            cs = CachedStack(zspecs, packed, slots, T_max=1, device_lookup=True)
+            hb = xs[0].clone()
+            if mode == "graph":
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    cs.step(hb)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s_ in range(steps):
+                hb.copy_(xs[s_])
+                if mode == "graph":
+                    graph.replay()
+                else:
+                    cs.step(hb)
+            torch.cuda.synchronize()
+            el_d = time.perf_counter() - t0
+            ds = cs.cache.stats()
+            if mode == "graph":
+                del graph
+            cs.close()
+            same = all(ds[k_] == stats[k_] for k_ in ("lookups", "hits", "misses", "evictions", "upload_bytes"))
+            if not same:
+                raise RuntimeError(f"device LRU counts {ds} differ from the host LRU's {stats}")
+            leg[f"device_lru_{mode}_tokens_per_s"] = round(steps / el_d, 2)
+        legs.append(leg)
         log(f"cache {f:.0%}: {legs[-1]}")
     return {"workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
-                        f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K)",
+                        f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
+                        f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
+                        f"copies on the device, eager and as a captured HIP graph",
             "legs": legs}
 
 

@@ -277,6 +277,39 @@ moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out);
 /* Reset statistics (not the cache contents). */
 moe_status moe_cache_reset_stats(moe_cache *c);
 
+/* Switch the cache to lookups on the device (before any host lookup): the
+ * LRU state moves to device memory (a last-use stamp and a key per slot per
+ * group, from one clock, and the key->slot map), so that a layer-step's
+ * lookup and miss uploads run on a stream with no host synchronization (and
+ * can be captured in a HIP graph).  Same policy as moe_cache_lookup (T4
+ * MoE-cache report, sections "What the MoE cache caches" and "Size your
+ * experts before configuring"): the distinct selected ids in ascending
+ * order; a hit refreshes its slot; a miss takes the group's next never-used
+ * slot, else the least recently used one (smallest stamp).  The host
+ * copies must be pinned memory the device can read (hipHostMalloc; torch
+ * pin_memory); their device addresses are taken here.  trace_capacity > 0
+ * keeps the first trace_capacity lookups (see moe_cache_trace_read).  After
+ * this call moe_cache_lookup and moe_cache_upload return MOE_ERR_STATE;
+ * moe_cache_stats and moe_cache_reset_stats synchronize the device.
+ * Returns MOE_ERR_CAPACITY when a group has more than 16384 slots. */
+moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity);
+
+/* Device lookup of one layer-step on `stream`: idx (device int32 [T][k],
+ * the layer's selected ids as moe_layer_route writes them) -> the LRU
+ * update, the layer's row of moe_cache_expert_ptrs, and the misses' copies
+ * from pinned host memory into their slots (a kernel reading the host
+ * memory over the bus).  Work on `stream` after this call sees the
+ * experts in their slots.  Calls on one cache must be ordered (one stream,
+ * or the caller's events).  MOE_ERR_CAPACITY when T*k exceeds the layer's
+ * group's slots, MOE_ERR_BATCH when T > 32. */
+moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
+                                   hipStream_t stream);
+
+/* Copy the device trace (synchronizes): records of 4 int32 (layer, expert,
+ * hit 1/0, evicted key layer*E+expert or -1), in lookup order; *n gets the
+ * number of lookups made (the device keeps the first trace_capacity). */
+moe_status moe_cache_trace_read(moe_cache *c, int32_t *out, int32_t capacity, int32_t *n);
+
 /* Drain outstanding copies and free the pools and tables. */
 void moe_cache_destroy(moe_cache *c);
 

@@ -18,6 +18,7 @@ EXPORTED = [
     "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
     "moe_cache_plan", "moe_cache_create", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
+    "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_trace_read",
 ]
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_QTYPE",
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
         "moe_cache_expert_ptrs": (P, [P, i32]),
         "moe_cache_stats": (i32, [P, ctypes.POINTER(CacheStats)]),
         "moe_cache_reset_stats": (i32, [P]),
+        "moe_cache_device_enable": (i32, [P, i32]),
+        "moe_cache_lookup_device": (i32, [P, i32, P, i32, i32, P]),
+        "moe_cache_trace_read": (i32, [P, P, i32, P]),
         "moe_cache_destroy": (None, [P]),
     }
     for name, (res, args) in sig.items():
@@ -254,6 +258,25 @@ class Cache:
     def upload(self, layer: int, copy_stream, done_event=None):
         ev = None if done_event is None else done_event.cuda_event if hasattr(done_event, "cuda_event") else done_event
         _check(lib().moe_cache_upload(self.h, layer, _stream(copy_stream), ev))
+
+    def enable_device(self, trace_capacity: int = 0):
+        """Move the LRU state to the device (moe_cache_device_enable)."""
+        _check(lib().moe_cache_device_enable(self.h, int(trace_capacity)))
+
+    def lookup_device(self, layer: int, idx, T: int, k: int, stream=None):
+        """Device lookup + miss uploads of one layer-step (moe_cache_lookup_device);
+        idx: int32 [T, k] contiguous, on the device."""
+        import torch
+        if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous() or idx.numel() < T * k:
+            raise ValueError("idx must be a contiguous int32 device tensor of T*k ids")
+        _check(lib().moe_cache_lookup_device(self.h, layer, idx.data_ptr(), T, k, _stream(stream)))
+
+    def trace_read(self, capacity: int) -> np.ndarray:
+        """The device trace: int32 [n, 4] (layer, expert, hit, evicted key or -1)."""
+        out = np.empty((max(capacity, 0), 4), np.int32)
+        n = ctypes.c_int32()
+        _check(lib().moe_cache_trace_read(self.h, out.ctypes.data, out.shape[0], ctypes.byref(n)))
+        return out[:min(n.value, out.shape[0])]
 
     def expert_ptrs(self, layer: int) -> int:
         p = lib().moe_cache_expert_ptrs(self.h, layer)

@@ -166,6 +166,18 @@ struct moe_cache {
     std::vector<std::vector<Pending>> pending;  // per layer
     std::vector<char> looked_up;
     moe_cache_stats_t st{};
+    // device-side lookup (moe_cache_device_enable): the LRU state in device
+    // memory, one stamp and key per slot per group
+    bool dev = false;
+    struct DevGroup { uint32_t *stamp = nullptr; int32_t *key = nullptr; };
+    std::vector<DevGroup> dgroups;
+    int32_t *d_where = nullptr;       // [L*E]
+    const void **d_src = nullptr;     // [L*E] device addresses of the host copies
+    int32_t *d_counters = nullptr;    // [n_groups] next_free, then clock, njobs, ntrace
+    CacheJob *d_jobs = nullptr;       // [E]
+    unsigned long long *d_stats = nullptr;  // 9 counters
+    int32_t *d_trace = nullptr;
+    int trace_cap = 0;
 };
 
 namespace {
@@ -198,6 +210,13 @@ void destroy(moe_cache *c)
     if (c->htab) (void)hipHostFree((void *)c->htab);
     for (auto ev : c->table_done)
         if (ev) (void)hipEventDestroy(ev);
+    for (auto &dg : c->dgroups) {
+        if (dg.stamp) (void)hipFree(dg.stamp);
+        if (dg.key) (void)hipFree(dg.key);
+    }
+    for (void *p : {(void *)c->d_where, (void *)c->d_src, (void *)c->d_counters, (void *)c->d_jobs,
+                    (void *)c->d_stats, (void *)c->d_trace})
+        if (p) (void)hipFree(p);
     delete c;
 }
 
@@ -283,6 +302,7 @@ moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, const int32_
         set_error("moe_cache_lookup: bad argument");
         return MOE_ERR_ARG;
     }
+    if (c->dev) { set_error("moe_cache_lookup: the cache looks up on the device (moe_cache_lookup_device)"); return MOE_ERR_STATE; }
     if (T < 1 || T > kMaxT) { set_error("moe_cache_lookup: T=%d outside [1, 32]; larger batches bypass the cache", T); return MOE_ERR_BATCH; }
     for (int i = 0; i < n; i++) {
         if (experts[i] < 0 || experts[i] >= c->E || (i > 0 && experts[i] <= experts[i - 1])) {
@@ -345,6 +365,7 @@ moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, const int32_
 moe_status moe_cache_upload(moe_cache *c, int32_t layer, hipStream_t copy_stream, hipEvent_t done)
 {
     if (!c || layer < 0 || layer >= c->n_layers) { set_error("moe_cache_upload: bad argument"); return MOE_ERR_ARG; }
+    if (c->dev) { set_error("moe_cache_upload: the cache looks up on the device (moe_cache_lookup_device)"); return MOE_ERR_STATE; }
     if (!c->looked_up[layer]) { set_error("moe_cache_upload: layer %d has no lookup", layer); return MOE_ERR_STATE; }
     auto &G = c->groups[c->layer_group[layer]];
     for (const auto &p : c->pending[layer]) {
@@ -374,6 +395,15 @@ const void *const *moe_cache_expert_ptrs(moe_cache *c, int32_t layer)
 moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out)
 {
     if (!c || !out) { set_error("moe_cache_stats: null argument"); return MOE_ERR_ARG; }
+    if (c->dev) {
+        static_assert(sizeof(moe_cache_stats_t) == 9 * sizeof(uint64_t), "stats layout");
+        if (hipSetDevice(c->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipMemcpy(out, c->d_stats, sizeof *out, hipMemcpyDeviceToHost) != hipSuccess) {
+            set_error("moe_cache_stats: reading the device counters failed");
+            return MOE_ERR_HIP;
+        }
+        return MOE_OK;
+    }
     *out = c->st;
     return MOE_OK;
 }
@@ -381,7 +411,116 @@ moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out)
 moe_status moe_cache_reset_stats(moe_cache *c)
 {
     if (!c) { set_error("moe_cache_reset_stats: null cache"); return MOE_ERR_ARG; }
+    if (c->dev) {
+        if (hipSetDevice(c->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipMemset(c->d_stats, 0, sizeof(moe_cache_stats_t)) != hipSuccess) {
+            set_error("moe_cache_reset_stats: clearing the device counters failed");
+            return MOE_ERR_HIP;
+        }
+        return MOE_OK;
+    }
     c->st = moe_cache_stats_t{};
+    return MOE_OK;
+}
+
+moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
+{
+    if (!c || trace_capacity < 0) { set_error("moe_cache_device_enable: bad argument"); return MOE_ERR_ARG; }
+    if (c->dev) { set_error("moe_cache_device_enable: already enabled"); return MOE_ERR_STATE; }
+    if (c->st.lookups) { set_error("moe_cache_device_enable: the cache has host lookups already"); return MOE_ERR_STATE; }
+    for (size_t g = 0; g < c->groups.size(); g++)
+        if (c->groups[g].n_slots > kCacheMaxSlots) {
+            set_error("moe_cache_device_enable: group %zu has %d slots, above the %d the device lookup holds", g,
+                      c->groups[g].n_slots, kCacheMaxSlots);
+            return MOE_ERR_CAPACITY;
+        }
+    if (hipSetDevice(c->device) != hipSuccess) { set_error("hipSetDevice failed"); return MOE_ERR_HIP; }
+    const size_t LE = (size_t)c->n_layers * c->E, ng = c->groups.size();
+    std::vector<const void *> src(LE);
+    for (size_t i = 0; i < LE; i++) {
+        void *dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, const_cast<void *>(c->host[i]), 0) != hipSuccess || !dp) {
+            set_error("moe_cache_device_enable: host expert %zu is not pinned memory the device can read", i);
+            return MOE_ERR_ARG;
+        }
+        src[i] = dp;
+    }
+    std::vector<int32_t> minus1(LE, -1);
+    bool ok = hipMalloc((void **)&c->d_where, LE * 4) == hipSuccess &&
+              hipMalloc((void **)&c->d_src, LE * sizeof(void *)) == hipSuccess &&
+              hipMalloc((void **)&c->d_counters, (ng + 3) * 4) == hipSuccess &&
+              hipMalloc((void **)&c->d_jobs, (size_t)c->E * sizeof(CacheJob)) == hipSuccess &&
+              hipMalloc((void **)&c->d_stats, sizeof(moe_cache_stats_t)) == hipSuccess &&
+              hipMemcpy(c->d_where, minus1.data(), LE * 4, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(c->d_src, src.data(), LE * sizeof(void *), hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemset(c->d_counters, 0, (ng + 3) * 4) == hipSuccess &&
+              hipMemset(c->d_stats, 0, sizeof(moe_cache_stats_t)) == hipSuccess;
+    if (ok && trace_capacity > 0)
+        ok = hipMalloc((void **)&c->d_trace, (size_t)trace_capacity * 16) == hipSuccess;
+    c->dgroups.assign(ng, {});
+    for (size_t g = 0; ok && g < ng; g++) {
+        const int n = c->groups[g].n_slots;
+        std::vector<int32_t> keys(n, -1);
+        ok = hipMalloc((void **)&c->dgroups[g].stamp, (size_t)n * 4) == hipSuccess &&
+             hipMalloc((void **)&c->dgroups[g].key, (size_t)n * 4) == hipSuccess &&
+             hipMemset(c->dgroups[g].stamp, 0, (size_t)n * 4) == hipSuccess &&
+             hipMemcpy(c->dgroups[g].key, keys.data(), (size_t)n * 4, hipMemcpyHostToDevice) == hipSuccess;
+    }
+    if (!ok) { set_error("moe_cache_device_enable: device allocation failed"); return MOE_ERR_HIP; }
+    // the host table is no longer refreshed; the device lookup writes dtab
+    c->trace_cap = trace_capacity;
+    c->dev = true;
+    return MOE_OK;
+}
+
+moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
+                                   hipStream_t stream)
+{
+    if (!c || !idx || layer < 0 || layer >= c->n_layers || k < 1 || k > c->E) {
+        set_error("moe_cache_lookup_device: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (!c->dev) { set_error("moe_cache_lookup_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
+    if (T < 1 || T > kMaxT) { set_error("moe_cache_lookup_device: T=%d outside [1, 32]", T); return MOE_ERR_BATCH; }
+    const int g = c->layer_group[layer];
+    auto &G = c->groups[g];
+    if (T * k > G.n_slots) {
+        set_error("moe_cache_lookup_device: %d selections may exceed the %d slots of the group", T * k, G.n_slots);
+        return MOE_ERR_CAPACITY;
+    }
+    const int ng = (int)c->groups.size();
+    CacheDevArgs a{};
+    a.idx = idx; a.T = T; a.k = k; a.layer = layer; a.E = c->E;
+    a.where = c->d_where; a.src = c->d_src; a.dtab = c->dtab;
+    a.stamp = c->dgroups[g].stamp; a.key = c->dgroups[g].key;
+    a.next_free = c->d_counters + g;
+    a.clock = (uint32_t *)(c->d_counters + ng);
+    a.njobs = c->d_counters + ng + 1;
+    a.pool = G.pool; a.slot_bytes = G.slot_bytes; a.n_slots = G.n_slots;
+    a.jobs = c->d_jobs;
+    a.stats = c->d_stats;
+    a.trace = c->d_trace; a.ntrace = c->d_counters + ng + 2; a.trace_cap = c->trace_cap;
+    return launch_cache_device(a, stream);
+}
+
+moe_status moe_cache_trace_read(moe_cache *c, int32_t *out, int32_t capacity, int32_t *n)
+{
+    if (!c || !n || capacity < 0 || (capacity && !out)) { set_error("moe_cache_trace_read: bad argument"); return MOE_ERR_ARG; }
+    if (!c->dev || !c->d_trace) { set_error("moe_cache_trace_read: no device trace (moe_cache_device_enable with a capacity)"); return MOE_ERR_STATE; }
+    const int ng = (int)c->groups.size();
+    int32_t total = 0;
+    if (hipSetDevice(c->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&total, c->d_counters + ng + 2, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+        set_error("moe_cache_trace_read: reading the trace failed");
+        return MOE_ERR_HIP;
+    }
+    *n = total;
+    const int m = total < c->trace_cap ? total : c->trace_cap;
+    const int cp = m < capacity ? m : capacity;
+    if (cp > 0 && hipMemcpy(out, c->d_trace, (size_t)cp * 16, hipMemcpyDeviceToHost) != hipSuccess) {
+        set_error("moe_cache_trace_read: reading the trace failed");
+        return MOE_ERR_HIP;
+    }
     return MOE_OK;
 }
 

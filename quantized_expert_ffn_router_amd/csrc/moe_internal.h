@@ -73,6 +73,35 @@ inline bool geom(const moe_expert_desc &d, ExpertGeom *g)
 }
 
 
+// Device-side slot-pool lookup (see k_cache_lookup): the LRU state of one
+// group, the layer's selected ids, and where the results go.
+struct CacheJob {
+    uint8_t *dst;        // slot
+    const uint8_t *src;  // device address of the expert's pinned host copy
+};
+struct CacheDevArgs {
+    const int32_t *idx;  // [T][k] selected ids of the layer-step (device)
+    int T, k, layer, E;
+    int32_t *where;              // [L*E] slot of each key, -1 absent
+    const void *const *src;      // [L*E] device addresses of the host copies
+    void **dtab;                 // [L*E] slot addresses (the layer's row is written)
+    uint32_t *stamp;             // [n_slots] last use of each slot (group)
+    int32_t *key;                // [n_slots] key held by each slot, -1 free (group)
+    int32_t *next_free;          // group's first never-used slot
+    uint32_t *clock;             // last stamp handed out (all groups)
+    uint8_t *pool;
+    unsigned long long slot_bytes;
+    int n_slots;
+    CacheJob *jobs;              // [E] misses of this call
+    int32_t *njobs;
+    unsigned long long *stats;   // moe_cache_stats_t fields, in order
+    int32_t *trace;              // [trace_cap][4] (layer, expert, hit, victim key) or null
+    int32_t *ntrace;
+    int trace_cap;
+};
+constexpr int kCacheMaxSlots = 16384;  // slots per group that the device lookup holds in LDS
+moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s);
+
 // The router's hand-over of logit keys sits at a fixed offset at the start of
 // every workspace, sized for the largest batch and expert count, so that calls
 // of different sizes can share one workspace: the route launch finds it zero

@@ -2194,6 +2194,170 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Slot-pool lookup on the device (the same LRU as the host lookup, T4
+// MoE-cache report, sections "What the MoE cache caches" and "Size your
+// experts before configuring"): the layer-step's distinct selected experts
+// are looked up in ascending id; a hit refreshes its slot's recency; a miss
+// takes the group's next never-used slot, else the least recently used one.
+// Recency is a stamp per slot from one increasing clock, so the least
+// recently used slot is the occupied slot with the smallest stamp (the tail
+// of the host's recency list).  One workgroup; the group's stamps and keys
+// are copied to LDS only when this step can evict.  Misses are written as
+// copy jobs for k_cache_copy.
+
+constexpr int kCacheThreads = 1024;
+
+__global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
+{
+    __shared__ int sel[kMaxE];
+    __shared__ int list[kMaxE];
+    __shared__ int wh[kMaxE];
+    __shared__ int s_nd, s_absent;
+    __shared__ uint32_t rmin[kCacheThreads / 64];
+    __shared__ int rslot[kCacheThreads / 64];
+    extern __shared__ uint32_t dyn[];  // lstamp[n_slots], lkey[n_slots]
+    uint32_t *lstamp = dyn;
+    int *lkey = (int *)(dyn + a.n_slots);
+    const int tid = (int)threadIdx.x, lane = lane_id(), E = a.E, P = a.T * a.k;
+    for (int e = tid; e < E; e += kCacheThreads) sel[e] = 0;
+    if (tid == 0) s_absent = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kCacheThreads) {
+        const int e = a.idx[p];
+        if ((unsigned)e < (unsigned)E) sel[e] = 1;
+    }
+    __syncthreads();
+    // ascending list of the distinct ids: wave 0, EPL consecutive ids per lane
+    if (tid < 64) {
+        const int EPL = (E + 63) >> 6, e0 = lane * EPL;
+        int c = 0;
+        for (int j = 0; j < EPL; j++) c += (e0 + j < E) ? sel[e0 + j] : 0;
+        int off = wave_incl_scan(c) - c;
+        for (int j = 0; j < EPL; j++)
+            if (e0 + j < E && sel[e0 + j]) list[off++] = e0 + j;
+        if (lane == 63) s_nd = off;
+    }
+    __syncthreads();
+    const int nd = s_nd;
+    const int64_t kbase = (int64_t)a.layer * E;
+    for (int i = tid; i < nd; i += kCacheThreads) {
+        wh[i] = a.where[kbase + list[i]];
+        if (wh[i] < 0) atomicAdd(&s_absent, 1);
+    }
+    __syncthreads();
+    int nf = *a.next_free;
+    uint32_t clk = *a.clock;
+    // no eviction can happen unless the absent ids outnumber the free slots
+    const bool evict = s_absent > a.n_slots - nf;
+    if (evict)
+        for (int sl = tid; sl < a.n_slots; sl += kCacheThreads) {
+            lstamp[sl] = a.stamp[sl];
+            lkey[sl] = a.key[sl];
+        }
+    __syncthreads();
+    int nj = 0, nh = 0, nev = 0;
+    // every thread walks the ids with the same (uniform) decisions; thread 0
+    // writes the state, all threads take part in the minimum search
+    for (int i = 0; i < nd; i++) {
+        const int e = list[i];
+        const int key = (int)(kbase + e);
+        int s = wh[i];
+        const bool hit = s >= 0 && (!evict || lkey[s] == key);
+        int victim = -1;
+        if (!hit) {
+            if (nf < a.n_slots) {
+                s = nf++;
+            } else {
+                // least recently used: the smallest stamp (all slots are in use)
+                uint32_t best = 0xffffffffu;
+                int bs = 0x7fffffff;
+                for (int sl = tid; sl < a.n_slots; sl += kCacheThreads) {
+                    const uint32_t v = lstamp[sl];
+                    if (v < best) { best = v; bs = sl; }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const uint32_t ov = (uint32_t)__shfl_xor((int)best, o, 64);
+                    const int os = __shfl_xor(bs, o, 64);
+                    if (ov < best || (ov == best && os < bs)) { best = ov; bs = os; }
+                }
+                if (lane == 0) { rmin[tid >> 6] = best; rslot[tid >> 6] = bs; }
+                __syncthreads();
+                best = rmin[0];
+                bs = rslot[0];
+                for (int w = 1; w < kCacheThreads / 64; w++)
+                    if (rmin[w] < best || (rmin[w] == best && rslot[w] < bs)) { best = rmin[w]; bs = rslot[w]; }
+                s = bs;
+                victim = lkey[s];
+                nev++;
+            }
+        } else {
+            nh++;
+        }
+        ++clk;
+        if (tid == 0) {
+            if (evict) { lstamp[s] = clk; lkey[s] = key; }
+            a.stamp[s] = clk;
+            uint8_t *slot = a.pool + (size_t)s * a.slot_bytes;
+            a.dtab[key] = slot;
+            if (!hit) {
+                if (victim >= 0) a.where[victim] = -1;
+                a.where[key] = s;
+                a.key[s] = key;
+                a.jobs[nj] = CacheJob{slot, (const uint8_t *)a.src[key]};
+            }
+            if (a.trace) {
+                const int t = a.ntrace[0] + i;
+                if (t < a.trace_cap) {
+                    a.trace[4 * t] = a.layer;
+                    a.trace[4 * t + 1] = e;
+                    a.trace[4 * t + 2] = hit ? 1 : 0;
+                    a.trace[4 * t + 3] = victim;
+                }
+            }
+        }
+        if (!hit) nj++;
+        __syncthreads();  // the state thread 0 wrote (LDS) before the next id
+    }
+    if (tid == 0) {
+        *a.next_free = nf;
+        *a.clock = clk;
+        *a.njobs = nj;
+        if (a.trace) a.ntrace[0] += nd;
+        unsigned long long *st = a.stats;
+        st[0] += nd;                    // lookups
+        st[1] += nh;                    // hits
+        st[2] += nd - nh;               // misses
+        st[3] += nev;                   // evictions
+        st[4] += (unsigned long long)nj * a.slot_bytes;
+        if (a.T <= 8) { st[5] += nd; st[6] += nh; }
+        else { st[7] += nd; st[8] += nh; }
+    }
+}
+
+// The misses' copies from pinned host memory (read over the bus) into their
+// slots: every workgroup takes a share of each job's 16-byte words.
+constexpr int kCacheCopyThreads = 256;
+__global__ __launch_bounds__(kCacheCopyThreads) void k_cache_copy(const CacheJob *jobs, const int32_t *njobs,
+                                                                  unsigned long long slot_bytes)
+{
+    const int nj = *njobs;
+    const size_t n16 = slot_bytes / 16, stride = (size_t)gridDim.x * kCacheCopyThreads;
+    for (int j = 0; j < nj; j++) {
+        const CacheJob jb = jobs[j];
+        const uint4 *src = (const uint4 *)jb.src;
+        uint4 *dst = (uint4 *)jb.dst;
+        size_t i = (size_t)blockIdx.x * kCacheCopyThreads + threadIdx.x;
+        // four words in flight per thread
+        for (; i + 3 * stride < n16; i += 4 * stride) {
+            const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+            dst[i] = v0; dst[i + stride] = v1; dst[i + 2 * stride] = v2; dst[i + 3 * stride] = v3;
+        }
+        for (; i < n16; i += stride) dst[i] = src[i];
+    }
+}
+
 __global__ void k_fill_zero(uint4 *p, size_t n16)
 {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
@@ -2381,6 +2545,23 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
 }
 
 }  // namespace
+
+moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s)
+{
+    const size_t lds = (size_t)a.n_slots * 8;
+    static bool attr = false;
+    if (!attr) {
+        HIP_OK(hipFuncSetAttribute((const void *)k_cache_lookup, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)((size_t)kCacheMaxSlots * 8)));
+        attr = true;
+    }
+    k_cache_lookup<<<1, kCacheThreads, lds, s>>>(a);
+    LAUNCH_OK("k_cache_lookup");
+    k_cache_copy<<<512, kCacheCopyThreads, 0, s>>>(a.jobs, a.njobs, a.slot_bytes);
+    LAUNCH_OK("k_cache_copy");
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;

@@ -122,10 +122,18 @@ class CachedStack:
     used slot); the misses are uploaded on a side stream, which the compute
     stream then waits for; moe_layer_ffn reads the experts through the
     cache's slot table of the layer.
+
+    device_lookup=True keeps the LRU state on the device instead
+    (moe_cache_device_enable): each layer is then moe_layer_route,
+    moe_cache_lookup_device (lookup and miss copies) and moe_layer_ffn on the
+    current stream, with no host synchronization, so a whole step can be
+    captured in a HIP graph.  trace_capacity > 0 keeps the device's lookup
+    trace (device_trace).
     """
 
     def __init__(self, layers: Sequence[LayerSpec], packed: Sequence[torch.Tensor], slots: Sequence[int],
-                 T_max: int = 8, device: str = "cuda", eps: float = 1e-6):
+                 T_max: int = 8, device: str = "cuda", eps: float = 1e-6, device_lookup: bool = False,
+                 trace_capacity: int = 0):
         self.layers = list(layers)
         self.device = torch.device(device)
         self.eps = eps
@@ -174,8 +182,13 @@ class CachedStack:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         L.moe_workspace_init(self.ws, self.ws_bytes)
         kmax = max(s.k for s in self.layers)
-        self.idx_dev = torch.empty((T_max, kmax), dtype=torch.int32, device=self.device)
-        self.idx_host = torch.empty((T_max, kmax), dtype=torch.int32, pin_memory=True)
+        # ids of a layer-step: the first T*k entries, contiguous [T, k]
+        self.idx_dev = torch.empty(T_max * kmax, dtype=torch.int32, device=self.device)
+        self.idx_host = torch.empty(T_max * kmax, dtype=torch.int32, pin_memory=True)
+        self.device_lookup = device_lookup
+        self.trace_capacity = trace_capacity
+        if device_lookup:
+            self.cache.enable_device(trace_capacity)
         self.copy_stream = torch.cuda.Stream(device=self.device)
         self.trace: Optional[list] = None
         self.time_copies = False       # record events around each layer's uploads
@@ -189,10 +202,15 @@ class CachedStack:
         s = self.layers[layer]
         T = h.shape[0]
         d = self.descs[layer]
-        idx = self.idx_dev[:T, :s.k]
+        idx = self.idx_dev[:T * s.k].view(T, s.k)
         L.moe_layer_route(d, h, T, self.routers[layer], self.biases[layer], s.E, s.k, None, self.shared_ptrs(layer),
                           s.n_shared, self.eps, idx, None, self.ws, self.ws_bytes)
-        ih = self.idx_host[:T, :s.k]
+        if self.device_lookup:
+            self.cache.lookup_device(layer, idx, T, s.k)
+            L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
+                            self.ws, self.ws_bytes)
+            return
+        ih = self.idx_host[:T * s.k].view(T, s.k)
         ih.copy_(idx, non_blocking=True)
         torch.cuda.current_stream(self.device).synchronize()
         experts = np.unique(ih.numpy())
@@ -216,6 +234,15 @@ class CachedStack:
         """One decode step through every layer; h [T, H] fp32 is updated in place."""
         for li in range(len(self.layers)):
             self.layer_forward(li, h)
+
+    def device_trace(self):
+        """The device lookups so far as (layer, expert, hit, victim_layer,
+        victim_expert) int32 arrays (device_lookup with a trace_capacity)."""
+        t = self.cache.trace_read(self.trace_capacity)
+        vk = t[:, 3]
+        vl = np.where(vk >= 0, vk // self.E, -1).astype(np.int32)
+        ve = np.where(vk >= 0, vk % self.E, -1).astype(np.int32)
+        return t[:, 0].copy(), t[:, 1].copy(), t[:, 2].astype(np.uint8), vl, ve
 
     def copy_ms(self) -> float:
         """Sum of the timed upload intervals (after a synchronisation)."""

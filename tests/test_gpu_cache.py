@@ -37,7 +37,7 @@ def _groups(cfg, n_layers):
     return descs, ebytes, per_group, layer_group
 
 
-def _run(cfg, n_layers, steps, fraction, T):
+def _run(cfg, n_layers, steps, fraction, T, device_lookup=False):
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts, n_layers)
     specs = layer_specs(cfg, n_layers)
@@ -47,9 +47,10 @@ def _run(cfg, n_layers, steps, fraction, T):
     st, slots = moe.moe_cache_plan(descs, per_group, budget, cfg.k)
     rc, oslots = oracle.cache_plan(ebytes, per_group, budget, cfg.k)
     assert st == 0 and rc == 0 and np.array_equal(slots, oslots), (slots, oslots)
-    _say(cfg.name, dict(layers=n_layers, steps=steps, T=T, fraction=fraction, slots=list(slots)))
+    _say(cfg.name, dict(layers=n_layers, steps=steps, T=T, fraction=fraction, slots=list(slots), device=device_lookup))
     packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
-    cs = CachedStack(specs, packed, slots, T_max=T)
+    cap = steps * n_layers * T * cfg.k
+    cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=device_lookup, trace_capacity=cap)
     cs.trace = []
     ids = np.empty((steps, n_layers, T * cfg.k), np.int32)
     try:
@@ -67,14 +68,17 @@ def _run(cfg, n_layers, steps, fraction, T):
             assert centered_rel_l2(hg - x, href - x) <= REL_L2_BAR, f"step {step}"
         # the GPU's lookups are the oracle routing's distinct experts ...
         LL, EE = oracle.lookup_sequence(ids)
-        gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in cs.trace])
-        ge = np.concatenate([e for _, e, *_ in cs.trace]).astype(np.int32)
+        if device_lookup:
+            gl, ge, hit, vl, ve = cs.device_trace()
+        else:
+            gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in cs.trace])
+            ge = np.concatenate([e for _, e, *_ in cs.trace]).astype(np.int32)
+            hit = np.concatenate([t[2] for t in cs.trace])
+            vl = np.concatenate([t[3] for t in cs.trace])
+            ve = np.concatenate([t[4] for t in cs.trace])
         assert np.array_equal(gl, LL) and np.array_equal(ge, EE)
         # ... and its hit/miss/victim trace is the oracle LRU's, bit for bit
         ref = oracle.lru(slots, layer_group, LL, EE)
-        hit = np.concatenate([t[2] for t in cs.trace])
-        vl = np.concatenate([t[3] for t in cs.trace])
-        ve = np.concatenate([t[4] for t in cs.trace])
         assert np.array_equal(hit, ref.hit)
         assert np.array_equal(vl, ref.victim_layer)
         assert np.array_equal(ve, ref.victim_expert)
@@ -89,19 +93,21 @@ def _run(cfg, n_layers, steps, fraction, T):
         cs.close()
 
 
+@pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
 @pytest.mark.parametrize("fraction", [0.1, 0.6])
-def test_cache_zipf_qwen3_shape(fraction):
+def test_cache_zipf_qwen3_shape(fraction, device_lookup):
     """Zipf-biased routing over a 4-layer Qwen3-30B-A3B-shaped Q4_K stack,
     pool at 10 % / 60 % of the routed expert bytes, 24 decode steps."""
-    _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1)
+    _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, device_lookup)
 
 
-def test_cache_two_groups_mixed_shared():
+@pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
+def test_cache_two_groups_mixed_shared(device_lookup):
     """Q4_K and Q6_K layers (two pools), 2 shared experts kept resident, T=4."""
     cfg = W.mixed_shared_q4k_q6k(T=4)
     Q4, Q6 = W.Q4_K, W.Q6_K
     sub = cfg.with_(n_layers=4, layer_qtypes=((Q4,) * 3, (Q4,) * 3, (Q6,) * 3, (Q6,) * 3))
-    s = _run(sub, 4, 6, 0.25, 4)
+    s = _run(sub, 4, 6, 0.25, 4, device_lookup)
     assert s["lookups_le8"] == s["lookups"] and s["lookups_9_32"] == 0
 
 
@@ -123,5 +129,37 @@ def test_cache_errors():
         assert not hit.any() and (vl == -1).all() and sorted(slot.tolist()) == [0, 1, 2]
         cs.cache.upload(0, cs.copy_stream)
         torch.cuda.synchronize()
+    finally:
+        cs.close()
+
+
+def test_cache_device_errors():
+    """Device-mode refusals: host lookups after the switch, a second switch,
+    more selections than slots, batches over 32 tokens."""
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=1).with_(E=16, k=4, seed=9)
+    experts = ExpertCache(cfg)
+    specs = layer_specs(cfg, 1)
+    packed = [pack_layer(specs[0], 0, experts)]
+    cs = CachedStack(specs, packed, [5], T_max=2, device_lookup=True, trace_capacity=64)
+    try:
+        with pytest.raises(moe.MoeError):  # the LRU state now lives on the device
+            cs.cache.lookup(0, 1, np.array([1, 2], np.int32))
+        with pytest.raises(moe.MoeError):
+            cs.cache.enable_device(0)
+        idx = torch.tensor([[1, 2, 3, 4], [5, 6, 7, 8]], dtype=torch.int32, device=DEV)
+        with pytest.raises(moe.MoeError):  # 8 selections may exceed 5 slots
+            cs.cache.lookup_device(0, idx, 2, 4)
+        with pytest.raises(moe.MoeError):  # batches over 32 tokens bypass the cache
+            cs.cache.lookup_device(0, torch.zeros(33 * 4, dtype=torch.int32, device=DEV), 33, 4)
+        cs.cache.lookup_device(0, idx[:1], 1, 4)   # 4 misses into free slots
+        cs.cache.lookup_device(0, idx[1:], 1, 4)   # 1 free slot, then 3 evictions
+        cs.cache.lookup_device(0, idx[:1], 1, 4)   # 1 (still resident?) of the first four
+        torch.cuda.synchronize()
+        gl, ge, hit, vl, ve = cs.device_trace()
+        ref = oracle.lru([5], [0], gl, ge)
+        assert np.array_equal(ge, [1, 2, 3, 4, 5, 6, 7, 8, 1, 2, 3, 4])
+        assert np.array_equal(hit, ref.hit) and np.array_equal(vl, ref.victim_layer) and np.array_equal(ve, ref.victim_expert)
+        s = cs.cache.stats()
+        assert s["lookups"] == 12 and s["hits"] == int(ref.hit.sum()) and s["evictions"] == int((ref.victim_layer >= 0).sum())
     finally:
         cs.close()
