@@ -845,14 +845,25 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         else route_tail_one<16>(a, cand, pre);
         return;
     }
-    // each wave polls its own share of the keys, then the workgroup meets once
+    // each wave polls its own share of the keys, then the workgroup meets
+    // once; a thread's keys of a round are all loaded before any is checked
+    // (one round trip per round, not one per key)
     int ok = 1;
+    constexpr int kPollQ = 8;
     for (unsigned it = 0;; it++) {
         int missing = 0;
-        for (int i = tid; i < n; i += kRouteWG) {
-            const uint32_t v = ld_coh_u(a.keys + i);
-            if (staged) lk[i] = v;
-            missing |= v == 0u;
+        for (int i0 = tid; i0 < n; i0 += kPollQ * kRouteWG) {
+            uint32_t v[kPollQ];
+#pragma unroll
+            for (int q = 0; q < kPollQ; q++) v[q] = ld_coh_u(a.keys + min(i0 + q * kRouteWG, n - 1));
+#pragma unroll
+            for (int q = 0; q < kPollQ; q++) {
+                const int i = i0 + q * kRouteWG;
+                if (i < n) {
+                    if (staged) lk[i] = v[q];
+                    missing |= v[q] == 0u;
+                }
+            }
         }
         if (!__ballot(missing)) break;
         if (it >= kSpinLimit) {
