@@ -1699,22 +1699,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
 {
     extern __shared__ __align__(16) uint8_t hsl[];
     __shared__ float part[8][kItemTok][64];
+    __shared__ int lptok[kItemTok];   // the item's pairs' tokens and combine weights
+    __shared__ float lpw[kItemTok];
 
     const int u = blockIdx.x / a.nrt;
     const int rt = blockIdx.x - u * a.nrt;
     u32x4 hr[kDnPre];
+    int tok1 = 0;
+    float pw1 = 0.f;
     if (ONE) {
-        const u32x4 *h16 = (const u32x4 *)rec_at(a.h, min(u, a.P - 1), a.kd);
+        // item u is pair u: its record, token and weight are loaded before
+        // the work entry arrives (their addresses do not depend on it)
+        const int pp = min(u, a.P - 1);
+        const u32x4 *h16 = (const u32x4 *)rec_at(a.h, pp, a.kd);
         const int n16 = (int)(enc_bytes(a.kd) / 16);
 #pragma unroll
         for (int q = 0; q < kDnPre; q++) hr[q] = h16[min((int)threadIdx.x + q * (int)blockDim.x, n16 - 1)];
+        tok1 = a.ptok[pp];
+        pw1 = a.pw[pp];
     }
     const WorkEntry we = load_entry(a.wt, u);
     const int e = we.e, p0 = we.p0, p1 = we.p1;
     if (p0 >= p1) {
-        if (ONE)
+        if (ONE) {
 #pragma unroll
             for (int q = 0; q < kDnPre; q++) use(hr[q]);
+            asm volatile("" ::"v"(tok1), "v"(pw1));
+        }
         return;
     }
     if (ONE && (p0 != u || p1 != u + 1)) {
@@ -1740,6 +1751,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
     if (!ONE) {
 #pragma unroll
         for (int q = 0; q < kDnPre; q++) hr[q] = h16[min((int)threadIdx.x + q * (int)blockDim.x, n16 - 1)];
+        // an item has at most kItemTok pairs
+        if ((int)threadIdx.x < p1 - p0) {
+            lptok[threadIdx.x] = a.ptok[p0 + threadIdx.x];
+            lpw[threadIdx.x] = a.pw[p0 + threadIdx.x];
+        }
     }
     // blockDim = 64 * min(S, 8): every wave has a K-group (loaded
     // unconditionally, for the same reason as in k_gate_up)
@@ -1803,8 +1819,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
             const int tt = i >> 6, ln = i & 63;
             float sum = 0.f;
             for (int w = 0; w < nwv; w++) sum += part[w][tt][ln];
-            const int p = c0 + tt;
-            add_to(a.y + (size_t)a.ptok[p] * a.H + rt * 64 + ln, a.pw[p] * sum);
+            const int q = c0 - p0 + tt;  // < kItemTok
+            const int tok = ONE ? tok1 : lptok[q];
+            const float pw = ONE ? pw1 : lpw[q];
+            add_to(a.y + (size_t)tok * a.H + rt * 64 + ln, pw * sum);
         }
     }
 }
@@ -2163,11 +2181,17 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int lmax[kMfmaCols];
+    __shared__ int lptok[kMfmaCols];  // the expert's pairs' tokens and combine weights
+    __shared__ float lpw[kMfmaCols];
     const int u = blockIdx.x / a.nrt, rt = blockIdx.x - u * a.nrt;
     const int nu = uni(*a.nuniq);
     if (u >= nu) return;
     const WorkEntry we = load_entry(a.wt, u);
     const int p0 = we.p0, n = we.p1 - we.p0;
+    if ((int)threadIdx.x < n) {  // read in the epilogue, after the loop's barriers
+        lptok[threadIdx.x] = a.ptok[p0 + threadIdx.x];
+        lpw[threadIdx.x] = a.pw[p0 + threadIdx.x];
+    }
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]) + a.down_off;
     const int wv = wave_id(), lane = lane_id();
@@ -2201,7 +2225,7 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const int t = 8 * (j >> 2) + 4 * kh + (j & 3);
-        if (t < n) add_to(a.y + (size_t)a.ptok[p0 + t] * a.H + rt * 64 + row64, a.pw[p0 + t] * acc[j]);
+        if (t < n) add_to(a.y + (size_t)lptok[t] * a.H + rt * 64 + row64, lpw[t] * acc[j]);
     }
 }
 
