@@ -2095,7 +2095,7 @@ struct GateUpMfmaArgs {
 };
 
 constexpr int kGUMfmaThreads = 256;
-constexpr int kDnMfmaThreads = 128;
+constexpr int kDnMfmaThreads = 256;  // 4 waves: 128 down rows share one staging
 
 __global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs a)
 {
@@ -2160,8 +2160,9 @@ __global__ __launch_bounds__(kGUMfmaThreads) void k_gate_up_mfma(GateUpMfmaArgs 
 }
 
 // k_down_mfma: workgroup (u, rt) = distinct expert u, down rows
-// [64rt, 64rt+64) (wave w: rows 32w..32w+31) against the expert's pairs'
-// SiLU(g)*u; adds each pair's weighted rows into y, as k_down does.
+// [128rt, 128rt+128) (wave w: rows 32w..32w+31) against the expert's pairs'
+// SiLU(g)*u, staged once for the four waves; adds each pair's weighted rows
+// into y, as k_down does.
 struct DownMfmaArgs {
     const void *const *eptr;
     const void *const *sptr;
@@ -2195,7 +2196,10 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]) + a.down_off;
     const int wv = wave_id(), lane = lane_id();
-    const int row64 = wv * 32 + (lane & 31), kh = lane >> 5;
+    // wave wv: rows 32wv..32wv+31 of the 128-row block rt, in 64-row tile
+    // 2rt + wv/2
+    const int row64 = (wv & 1) * 32 + (lane & 31), kh = lane >> 5;
+    const size_t tile0 = (size_t)(2 * rt + (wv >> 1));
     const int S = a.kd >> 8;
     auto rowof = [&](int c) { return p0 + c; };
     if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;
@@ -2205,13 +2209,13 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
     StageRegs<kDnMfmaThreads> sr;
     stage_load<kDnMfmaThreads>(sr, a.hf, a.kd, a.I, 0, n, rowof);
     Q4KRow w;
-    load_q4k_row(w, base + ((size_t)rt * S) * kTileBytes<MOE_Q4_K>, row64, kh);
+    load_q4k_row(w, base + (tile0 * S) * kTileBytes<MOE_Q4_K>, row64, kh);
     __syncthreads();  // lmax cleared
     stage_store<kDnMfmaThreads>(sr, stage_at(smem), lmax);
     for (int sb = 0; sb < S; sb++) {
         Q4KRow wn;
         if (sb + 1 < S) {  // the next super-block's weights and h, in flight during this one's MFMAs
-            load_q4k_row(wn, base + ((size_t)rt * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
+            load_q4k_row(wn, base + (tile0 * S + sb + 1) * kTileBytes<MOE_Q4_K>, row64, kh);
             stage_load<kDnMfmaThreads>(sr, a.hf, a.kd, a.I, sb + 1, n, rowof);
         }
         __syncthreads();  // stage sb is complete
@@ -2225,7 +2229,7 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         const int t = 8 * (j >> 2) + 4 * kh + (j & 3);
-        if (t < n) add_to(a.y + (size_t)lptok[t] * a.H + rt * 64 + row64, lpw[t] * acc[j]);
+        if (t < n) add_to(a.y + (size_t)lptok[t] * a.H + rt * 128 + wv * 32 + (lane & 31), lpw[t] * acc[j]);
     }
 }
 
@@ -2480,11 +2484,11 @@ moe_status check_ws(const moe_expert_desc &d, void *ws, size_t ws_bytes, int T, 
 }
 
 // The MFMA path takes batches of more than kMfmaMinT tokens whose expert
-// matrices are all Q4_K.
+// matrices are all Q4_K (and H a multiple of 128).
 constexpr int kMfmaMinT = 8;
 bool use_mfma(const moe_expert_desc &d, int T)
 {
-    return T > kMfmaMinT && d.gate == MOE_Q4_K && d.up == MOE_Q4_K && d.down == MOE_Q4_K;
+    return T > kMfmaMinT && d.gate == MOE_Q4_K && d.up == MOE_Q4_K && d.down == MOE_Q4_K && d.H % 128 == 0;
 }
 
 // The FFN launches add into y (moe_expert_ffn clears it first when not
@@ -2513,7 +2517,7 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     da.eptr = eptr; da.sptr = sptr; da.E = E;
     da.nuniq = ws.at<int>(L.nuniq); da.wt = ga.wt; da.hf = ga.hf;
     da.H = d.H; da.I = d.I; da.kd = g.kd; da.down_off = g.down_off;
-    da.nrt = d.H / 64;
+    da.nrt = d.H / 128;
     da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
     k_down_mfma<<<L.U * da.nrt, kDnMfmaThreads, lds, s>>>(da);
     LAUNCH_OK("k_down_mfma");
