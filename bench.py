@@ -188,10 +188,12 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
                 bytes_per_launch=tot_bytes / n_ffn, gbps=tot_bytes / (tot_ffn_ms * 1e-3) / 1e9, launches=n_ffn)
 
 
-def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int):
+def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int = 4):
     """The same stack with its routed experts in pinned host memory behind an
     HBM slot pool of `fraction` of the routed expert bytes, Zipf(1.1)-biased
-    routing, `steps` single-token decode steps from a cold pool."""
+    routing, `steps` single-token decode steps from a cold pool.  Then n_req
+    concurrent requests sharing the pool, decoded as one n_req-token batch
+    per step (the device LRU as a HIP graph)."""
     import torch
     import workloads as W
     import quantized_expert_ffn_router_amd as moe
@@ -265,12 +267,39 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int):
             if not same:
                 raise RuntimeError(f"device LRU counts {ds} differ from the host LRU's {stats}")
             leg[f"device_lru_{mode}_tokens_per_s"] = round(steps / el_d, 2)
+        # n_req concurrent requests: one n_req-token batch per step, fresh
+        # tokens each step, from a cold pool
+        if n_req > 1:
+            xr = torch.randn((steps, n_req, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+            cs = CachedStack(zspecs, packed, slots, T_max=n_req, device_lookup=True)
+            hb = xr[0].clone()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                cs.step(hb)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s_ in range(steps):
+                hb.copy_(xr[s_])
+                graph.replay()
+            torch.cuda.synchronize()
+            el_r = time.perf_counter() - t0
+            rs = cs.cache.stats()
+            del graph
+            cs.close()
+            leg[f"requests_{n_req}"] = {
+                "tokens_per_s": round(n_req * steps / el_r, 2),
+                "hit_rate": round(rs["hits"] / rs["lookups"], 4),
+                "misses_per_step": round(rs["misses"] / steps, 2),
+            }
         legs.append(leg)
         log(f"cache {f:.0%}: {legs[-1]}")
     return {"workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
                         f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
                         f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
-                        f"copies on the device, eager and as a captured HIP graph",
+                        f"copies on the device, eager and as a captured HIP graph; requests_N: N concurrent requests "
+                        f"sharing the pool, one N-token batch per step (device LRU, graph; hit rate over the "
+                        f"step's distinct experts per layer)",
             "legs": legs}
 
 

@@ -101,6 +101,15 @@ def test_cache_zipf_qwen3_shape(fraction, device_lookup):
     _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, device_lookup)
 
 
+def test_cache_four_requests_thrash_device_lru():
+    """Four concurrent requests decoded as one 4-token batch on a 10 % pool of
+    the Qwen3-30B-A3B-shaped stack: each step's distinct experts outgrow
+    the pool, so nearly every lookup evicts; the device LRU's trace must
+    still be the oracle LRU's, bit for bit."""
+    s = _run(W.qwen3_30b_a3b_q4k_zipf(T=4, n_layers=4), 4, 10, 0.1, 4, True)
+    assert s["evictions"] > 0 and s["lookups_le8"] == s["lookups"]
+
+
 @pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
 def test_cache_two_groups_mixed_shared(device_lookup):
     """Q4_K and Q6_K layers (two pools), 2 shared experts kept resident, T=4."""
