@@ -23,7 +23,8 @@ namespace moe {
 
 constexpr int kTileRows = 64;
 constexpr int kTileCols = 256;
-constexpr int kMaxT = 32;
+constexpr int kMaxT = 32;        // batch of the layer path and the slot-pool cache
+constexpr int kMaxTLarge = 256;  // batch of moe_route_topk and moe_expert_ffn (prompt-sized batches)
 constexpr int kMaxE = 1024;
 constexpr int kMaxShared = 8;
 constexpr int kMaxH = 8192;

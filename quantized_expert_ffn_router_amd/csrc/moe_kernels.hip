@@ -1135,12 +1135,133 @@ __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
     if (a.kd > a.I)
         for (int p = t; p < a.P; p += a.T)
             zero_blocks(rec_at(a.hpad, p, a.kd), a.kd, a.I / 32, a.kd / 32, threadIdx.x, blockDim.x);
-    if (t != 0) return;
+    if (t != 0 || a.T > kMaxT) return;  // larger batches are grouped by k_group_large
     for (int p = threadIdx.x; p < a.T * a.k; p += blockDim.x) sidx[p] = a.idx[p];
     __syncthreads();
     GroupOut go = a.go;
     go.wsrc = a.w;
     group_block(sidx, a.T, a.k, a.E, a.ns, go, lstart, PrePtr{nullptr, nullptr, false});
+}
+
+// k_group_large: the grouping of group_block for batches of up to
+// kMaxTLarge tokens (one workgroup of 1024 threads), with a bitmap of
+// tokens per expert instead of one 32-bit mask: ids are distinct per token,
+// so pair (t, j) of expert e sits at offset[e] + (tokens below t that chose
+// e).  Work entries cover at most `chunk` consecutive pairs of one expert
+// (kItemTok for the dot-product kernels, kMfmaCols for the MFMA ones),
+// in expert order, then the shared experts' pairs (token order) in the same
+// chunks; entries past them are cleared.
+constexpr int kGroupLargeThreads = 1024;
+constexpr int kBmWords = kMaxTLarge / 32;
+
+struct GroupLargeArgs {
+    const int *idx;
+    const float *w;
+    int T, k, E, ns, chunk;
+    GroupOut go;
+};
+
+// Exclusive scans of two values over the 1024 threads; totals in tot[2].
+__device__ __forceinline__ void block_excl_scan2(int &a, int &b, int *lds /* 2 * 16 */, int *tot)
+{
+    const int lane = lane_id(), wv = wave_id();
+    const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    if (lane == 63) { lds[wv] = ia; lds[16 + wv] = ib; }
+    __syncthreads();
+    int pa = 0, pb = 0, ta = 0, tb = 0;
+    for (int w = 0; w < kGroupLargeThreads / 64; w++) {
+        if (w < wv) { pa += lds[w]; pb += lds[16 + w]; }
+        ta += lds[w];
+        tb += lds[16 + w];
+    }
+    a = pa + ia - a;
+    b = pb + ib - b;
+    if (threadIdx.x == 0) { tot[0] = ta; tot[1] = tb; }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kGroupLargeThreads) void k_group_large(GroupLargeArgs a)
+{
+    __shared__ uint32_t bm[kMaxE * kBmWords];  // tokens of each expert
+    __shared__ int cnt[kMaxE], off[kMaxE], iof[kMaxE];
+    __shared__ int scan[32], tot[2];
+    const int tid = (int)threadIdx.x, T = a.T, k = a.k, E = a.E, ns = a.ns, P = T * k, chunk = a.chunk;
+    const int nw = (T + 31) >> 5;
+    GroupOut g = a.go;
+    for (int i = tid; i < E * kBmWords; i += kGroupLargeThreads) bm[i] = 0u;
+    for (int e = tid; e < E; e += kGroupLargeThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kGroupLargeThreads) {
+        const int e = a.idx[p], t = p / k;
+        if ((unsigned)e < (unsigned)E) {
+            atomicOr(&bm[e * kBmWords + (t >> 5)], 1u << (t & 31));
+            atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    // pair offsets and entry offsets by expert (E <= kMaxE = 1024: one per thread)
+    int c = tid < E ? cnt[tid] : 0;
+    int it = (c + chunk - 1) / chunk;
+    block_excl_scan2(c, it, scan, tot);
+    if (tid < E) { off[tid] = c; iof[tid] = it; }
+    __syncthreads();
+    const int nvalid = tot[0], nitems = tot[1];
+    for (int p = tid; p < P; p += kGroupLargeThreads) {
+        const int e = a.idx[p], t = p / k, j = p - t * k;
+        if ((unsigned)e >= (unsigned)E) {
+            g.inv[t * (k + ns) + j] = -1;
+            continue;
+        }
+        const uint32_t *row = bm + e * kBmWords;
+        int r = __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+        for (int wd = 0; wd < (t >> 5); wd++) r += __popc(row[wd]);
+        const int pos = off[e] + r;
+        g.ptok[pos] = t;
+        g.inv[t * (k + ns) + j] = pos;
+        if (g.pw) g.pw[pos] = a.w[p];
+    }
+    for (int i = tid; i < ns * T; i += kGroupLargeThreads) {
+        const int s2 = i / T, t = i - s2 * T, pos = nvalid + s2 * T + t;
+        g.ptok[pos] = t;
+        g.inv[t * (k + ns) + k + s2] = pos;
+        if (g.pw) g.pw[pos] = 1.0f;  // shared experts have weight one
+    }
+    // routed entries: expert e's pairs [off, off + cnt) in chunks; the first
+    // kInlineTok tokens of each chunk inline (the set bits of the bitmap from
+    // rank it*chunk on)
+    for (int e = tid; e < E; e += kGroupLargeThreads) {
+        const int ce = cnt[e];
+        if (ce == 0) continue;
+        const uint32_t *row = bm + e * kBmWords;
+        int wd = 0;
+        uint32_t m = row[0];
+        for (int i0 = 0, u = iof[e]; i0 < ce; i0 += chunk, u++) {
+            WorkEntry we{};
+            we.e = e; we.p0 = off[e] + i0; we.p1 = off[e] + min(i0 + chunk, ce);
+            we.ptr = g.eptr ? g.eptr[e] : nullptr;
+            // walk the bitmap to the chunk's tokens (bits consumed in order)
+            for (int q = 0; q < chunk && i0 + q < ce; q++) {
+                while (m == 0u && wd + 1 < nw) m = row[++wd];
+                const int t = wd * 32 + __builtin_ctz(m);
+                m &= m - 1u;
+                if (q < kInlineTok) we.tok[q] = (uint8_t)t;  // t < kMaxTLarge = 256
+            }
+            g.wt[u] = we;
+        }
+    }
+    const int sit = (T + chunk - 1) / chunk;
+    for (int i = tid; i < ns * sit; i += kGroupLargeThreads) {
+        const int s2 = i / sit, itn = i - s2 * sit;
+        WorkEntry we{};
+        we.e = E + s2;
+        we.p0 = nvalid + s2 * T + itn * chunk;
+        we.p1 = nvalid + s2 * T + min((itn + 1) * chunk, T);
+        we.ptr = g.eptr ? g.sptr[s2] : nullptr;
+        for (int q = 0; q < kInlineTok; q++) we.tok[q] = (uint8_t)(itn * chunk + q);
+        g.wt[nitems + i] = we;
+    }
+    for (int u = nitems + ns * sit + tid; u < g.Umax; u += kGroupLargeThreads) g.wt[u] = WorkEntry{};
+    if (tid == 0) *g.nuniq = nitems + ns * sit;
 }
 
 // k_group: moe_group_tokens (one workgroup).
@@ -2462,9 +2583,9 @@ moe_status check_desc(const moe_expert_desc *d, ExpertGeom *g)
     return MOE_OK;
 }
 
-moe_status check_tke(int T, int k, int E, int ns)
+moe_status check_tke(int T, int k, int E, int ns, int tmax = kMaxT)
 {
-    if (T < 1 || T > kMaxT) { set_error("T=%d outside [1, %d]", T, kMaxT); return MOE_ERR_BATCH; }
+    if (T < 1 || T > tmax) { set_error("T=%d outside [1, %d]", T, tmax); return MOE_ERR_BATCH; }
     if (E < 1 || E > kMaxE) { set_error("E=%d outside [1, %d]", E, kMaxE); return MOE_ERR_ARG; }
     if (k < 1 || k > E || k > kMaxK) { set_error("k=%d outside [1, min(E=%d, %d)]", k, E, kMaxK); return MOE_ERR_ARG; }
     if (ns < 0 || ns > kMaxShared) { set_error("n_shared=%d outside [0, %d]", ns, kMaxShared); return MOE_ERR_ARG; }
@@ -2493,10 +2614,13 @@ bool use_mfma(const moe_expert_desc &d, int T)
 
 // The FFN launches add into y (moe_expert_ffn clears it first when not
 // accumulating); the routing is the grouping in the workspace.
-moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int E, const void *const *eptr,
-                           const void *const *sptr, float *y, float *act_out, hipStream_t s)
+moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
+                           const void *const *eptr, const void *const *sptr, float *y, float *act_out, hipStream_t s)
 {
     const WsLayout &L = ws.L;
+    // entries: one per distinct expert up to kMaxT tokens; chunks of
+    // kMfmaCols pairs for larger batches (k_group_large)
+    const int nent = T > kMaxT ? L.UI : L.U;
     const size_t lds = 2 * kStageBytes;
     static bool attr = false;
     if (!attr) {
@@ -2511,7 +2635,7 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     ga.hf = ws.at<float>(L.hf); ga.act_out = act_out;
     ga.nrb = d.I / 64;
     ga.nuniq = ws.at<int>(L.nuniq);
-    k_gate_up_mfma<<<L.U * ga.nrb, kGUMfmaThreads, lds, s>>>(ga);
+    k_gate_up_mfma<<<nent * ga.nrb, kGUMfmaThreads, lds, s>>>(ga);
     LAUNCH_OK("k_gate_up_mfma");
     DownMfmaArgs da;
     da.eptr = eptr; da.sptr = sptr; da.E = E;
@@ -2519,7 +2643,7 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     da.H = d.H; da.I = d.I; da.kd = g.kd; da.down_off = g.down_off;
     da.nrt = d.H / 128;
     da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
-    k_down_mfma<<<L.U * da.nrt, kDnMfmaThreads, lds, s>>>(da);
+    k_down_mfma<<<nent * da.nrt, kDnMfmaThreads, lds, s>>>(da);
     LAUNCH_OK("k_down_mfma");
     return MOE_OK;
 }
@@ -2528,7 +2652,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
                               const void *const *eptr, const void *const *sptr, float *y,
                               float *act_out, hipStream_t s)
 {
-    if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, E, eptr, sptr, y, act_out, s);
+    if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, T, E, eptr, sptr, y, act_out, s);
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -2618,7 +2742,7 @@ moe_status moe_rmsnorm(const float *h, int32_t T, int32_t H, float eps, float *x
 moe_status moe_route_topk(const float *x, int32_t T, int32_t H, const float *w_router, const float *bias, int32_t E,
                           int32_t k, int32_t *idx, float *w, float *logits, hipStream_t s)
 {
-    moe_status st = check_tke(T, k, E, 0);
+    moe_status st = check_tke(T, k, E, 0, kMaxTLarge);
     if (st != MOE_OK) return st;
     if (!x || !w_router || !idx || !w) { set_error("moe_route_topk: null pointer"); return MOE_ERR_ARG; }
     if (H < 256 || H % 256 || H > kMaxH) { set_error("moe_route_topk: H=%d must be a multiple of 256 up to %d", H, kMaxH); return MOE_ERR_SHAPE; }
@@ -2641,7 +2765,7 @@ moe_status moe_group_tokens(const int32_t *idx, int32_t T, int32_t k, int32_t E,
 size_t moe_workspace_bytes(const moe_expert_desc *d, int32_t T, int32_t k, int32_t E, int32_t n_shared)
 {
     ExpertGeom g;
-    if (!d || !geom(*d, &g) || check_tke(T, k, E, n_shared) != MOE_OK) return 0;
+    if (!d || !geom(*d, &g) || check_tke(T, k, E, n_shared, kMaxTLarge) != MOE_OK) return 0;
     return ws_layout(*d, T, k, E, n_shared).total;
 }
 
@@ -2665,7 +2789,7 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     ExpertGeom g;
     moe_status st = check_desc(d, &g);
     if (st != MOE_OK) return st;
-    if ((st = check_tke(T, k, E, n_shared)) != MOE_OK) return st;
+    if ((st = check_tke(T, k, E, n_shared, kMaxTLarge)) != MOE_OK) return st;
     if (!x || !idx || !w || !expert_ptrs || !y || (n_shared > 0 && !shared_ptrs)) {
         set_error("moe_expert_ffn: null pointer");
         return MOE_ERR_ARG;
@@ -2680,6 +2804,17 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
+    if (T > kMaxT) {
+        // prompt-sized batch: work entries of at most kItemTok (dot-product
+        // kernels) or kMfmaCols (MFMA) pairs, from per-expert token bitmaps
+        GroupLargeArgs ga{};
+        ga.idx = idx; ga.w = w; ga.T = T; ga.k = k; ga.E = E; ga.ns = n_shared;
+        ga.chunk = use_mfma(*d, T) ? kMfmaCols : kItemTok;
+        ga.go = pa.go;
+        ga.go.Umax = W.L.UI;
+        k_group_large<<<1, kGroupLargeThreads, 0, s>>>(ga);
+        LAUNCH_OK("k_group_large");
+    }
     return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, y, act_out, s);
 }
 

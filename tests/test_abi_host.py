@@ -51,9 +51,13 @@ def test_argument_errors_are_host_side():
     assert st(h=None) == -1 and st(ns=1) == -1
     assert st(wsb=ws_need - 1) == -1
     assert b"workspace too small" in L.moe_last_error()
-    with pytest.raises(moe.MoeError) as ei:
-        moe.moe_route_topk(fake, 40, 2048, fake, None, 128, 8, fake, fake, None, stream=0)
+    with pytest.raises(moe.MoeError) as ei:  # the stand-alone router takes up to 256 tokens
+        moe.moe_route_topk(fake, 257, 2048, fake, None, 128, 8, fake, fake, None, stream=0)
     assert ei.value.name == "MOE_ERR_BATCH"
+    # moe_expert_ffn takes up to 256 tokens, the layer calls up to 32
+    assert moe.moe_workspace_bytes(d, 256, 8, 128, 0) > moe.moe_workspace_bytes(d, 32, 8, 128, 0) > 0
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_bytes(d, 257, 8, 128, 0)
     with pytest.raises(moe.MoeError):
         moe.moe_group_tokens(fake, 4, 9, 8, fake, fake, fake, stream=0)
 

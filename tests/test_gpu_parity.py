@@ -57,6 +57,9 @@ ROUTE_CASES = [
     (5, 512, 5, 5, False, 4),        # k == E, E not a multiple of 4
     (3, 768, 61, 7, False, 5),
     (2, 1024, 1000, 16, False, 6),
+    # prompt-sized batches (moe_route_topk takes up to 256 tokens)
+    (64, 512, 64, 6, False, 7),
+    (256, 256, 16, 4, True, 8),
 ]
 
 
@@ -142,6 +145,11 @@ FFN_CASES = [
     ((W.Q4_K,) * 3, 1024, 320, 8, 8, 0, 32, False),     # every token on every expert: 32 columns; ragged I
     ((W.Q4_K,) * 3, 2048, 768, 128, 8, 2, 16, True),    # shared experts, zero-mean weights
     ((W.Q4_K,) * 3, 2048, 768, 16, 8, 0, 32, False),    # the Qwen3-30B-A3B shape at T=32
+    # prompt-sized batches (T > 32): entries of at most 32 pairs per expert on the
+    # MFMA path (every expert here has more), of at most 4 on the dot-product path
+    ((W.Q4_K,) * 3, 512, 192, 8, 8, 0, 64, False),      # 64 pairs per expert: two entries each
+    ((W.Q4_K,) * 3, 1024, 320, 16, 4, 1, 256, True),    # 256 tokens, a shared expert of 8 entries
+    ((W.Q6_K, W.Q6_K, W.Q8_0), 512, 128, 6, 2, 1, 48, False),
 ]
 
 
