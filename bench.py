@@ -303,6 +303,39 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
             "legs": legs}
 
 
+def prompt_leg(st, cfg, T: int, steps: int, seed: int):
+    """A prompt-sized batch of T tokens through the resident stack
+    (ResidentStack.prompt_step: moe_rmsnorm, moe_route_topk, moe_expert_ffn
+    per layer, eager launches), fresh N(0,1) states each step; the distinct
+    experts per layer-step are counted from the routing of one step."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    xs = torch.randn((steps + 2, T, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+    idx = torch.empty((cfg.n_layers, T, cfg.k), dtype=torch.int32, device="cuda")
+    for s_ in range(2):
+        h = xs[steps + s_].clone()
+        st.prompt_step(h, idx if s_ == 1 else None)
+    torch.cuda.synchronize()
+    uniq = float(np.mean([len(np.unique(idx[l].cpu().numpy())) for l in range(cfg.n_layers)]))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    hs = [xs[s_].clone() for s_ in range(steps)]
+    torch.cuda.synchronize()
+    e0.record()
+    for s_ in range(steps):
+        st.prompt_step(hs[s_])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    eb = cfg.expert_bytes(0)
+    return {"batch": T, "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "distinct_experts_per_layer": round(uniq, 1),
+            "expert_GBps": round(uniq * eb * cfg.n_layers / (ms * 1e-3) / 1e9, 1),
+            "workload": f"{T} fresh tokens per step through the {cfg.n_layers}-layer stack (moe_rmsnorm, "
+                        f"moe_route_topk, moe_expert_ffn per layer; MFMA FFN in work entries of at most "
+                        f"32 pairs); expert_GBps = distinct experts x expert bytes x layers / step time"}
+
+
 def cpu_baseline(cfg, experts: dict, n_tokens: int, n_layers: int):
     """The oracle as it stands, on a bounded sample (n_tokens single-token
     decodes through the first n_layers layers), scaled to the whole stack."""
@@ -338,6 +371,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--cpu-layers", type=int, default=8)
     ap.add_argument("--cache-steps", type=int, default=512, help="decode steps of each slot-pool leg (0: none)")
+    ap.add_argument("--prompt-batch", type=int, default=128, help="tokens of the prompt-sized batch leg (0: none)")
+    ap.add_argument("--prompt-steps", type=int, default=10)
     ap.add_argument("--zipf", action="store_true", help="Zipf(1.1) router bias on the resident stack "
                                                          "(the skewed T=32 workload)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -385,6 +420,11 @@ def main():
         log(f"T={T}: {tps:.1f} tok/s, {ms:.3f} ms/step; FFN {tm['ffn_us']:.2f} us/launch "
             f"{tm['gbps']:.0f} GB/s ({tm['bytes_per_launch'] / 1e6:.2f} MB), route {tm['route_us']:.2f} us")
 
+    prompt = None
+    if args.prompt_batch:
+        prompt = prompt_leg(st, cfg, args.prompt_batch, args.prompt_steps, seed=7)
+        log(f"prompt: {prompt}")
+
     cache = None
     if args.cache_steps:
         cache = cache_leg(cfg, specs, packed, (0.1, 0.6), args.cache_steps, seed=4)
@@ -415,6 +455,7 @@ def main():
         "route_us_per_layer": round(tm["route_us"], 3),
         "cpu_baseline": cpu,
         "cache": cache,
+        "prompt": prompt,
     }
     if args.also_batch and args.also_batch in res and args.also_batch != T:
         t2, m2, tm2 = res[args.also_batch]

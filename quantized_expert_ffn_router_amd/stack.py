@@ -111,6 +111,31 @@ class ResidentStack:
             self.layer_forward(li, h, None if idx_out is None else idx_out[li],
                                None if w_out is None else w_out[li], stream, split)
 
+    def prompt_step(self, h: torch.Tensor, idx_out: Optional[torch.Tensor] = None,
+                    w_out: Optional[torch.Tensor] = None, stream=None):
+        """The same layer stack for a prompt-sized batch (up to 256 tokens, past
+        the layer calls' 32): per layer moe_rmsnorm, moe_route_topk and
+        moe_expert_ffn adding into h.  idx_out / w_out, if given, are [L, T, k]."""
+        T, H = h.shape
+        key = (T, H)
+        if getattr(self, "_prompt_key", None) != key:
+            kmax = max(s.k for s in self.layers)
+            self._pxhat = torch.empty((T, H), dtype=torch.float32, device=self.device)
+            self._pidx = torch.empty(T * kmax, dtype=torch.int32, device=self.device)
+            self._pw = torch.empty(T * kmax, dtype=torch.float32, device=self.device)
+            self._pws_bytes = max(L.moe_workspace_bytes(d, T, s.k, s.E, s.n_shared)
+                                  for d, s in zip(self.descs, self.layers))
+            self._pws = torch.empty(self._pws_bytes, dtype=torch.uint8, device=self.device)
+            L.moe_workspace_init(self._pws, self._pws_bytes)
+            self._prompt_key = key
+        for li, s in enumerate(self.layers):
+            idx = self._pidx[:T * s.k].view(T, s.k) if idx_out is None else idx_out[li]
+            w = self._pw[:T * s.k].view(T, s.k) if w_out is None else w_out[li]
+            L.moe_rmsnorm(h, T, H, self.eps, self._pxhat, stream)
+            L.moe_route_topk(self._pxhat, T, H, self.routers[li], self.biases[li], s.E, s.k, idx, w, None, stream)
+            L.moe_expert_ffn(self.descs[li], self._pxhat, T, s.k, s.E, idx, w, self.expert_ptrs(li),
+                             self.shared_ptrs(li), s.n_shared, h, 1, None, self._pws, self._pws_bytes, stream)
+
 
 class CachedStack:
     """A decode-time MoE stack whose routed experts live in pinned host memory

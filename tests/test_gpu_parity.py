@@ -204,7 +204,7 @@ def test_expert_ffn(qt, H, I, E, k, ns, T, zm, accumulate):
 
 
 # ---------------------------------------------------------------- fused layer and stack
-def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False):
+def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False, prompt=False):
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts, n_layers)
     x, att = W.tie_free_tokens(cfg, step, T, chain_min_gap(olayers))
@@ -213,7 +213,10 @@ def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False):
     h = _dev(x)
     idx = torch.empty((n_layers, T, cfg.k), dtype=torch.int32, device=DEV)
     wts = torch.empty((n_layers, T, cfg.k), dtype=torch.float32, device=DEV)
-    st.step(h, idx, wts, split=split)
+    if prompt:
+        st.prompt_step(h, idx, wts)
+    else:
+        st.step(h, idx, wts, split=split)
     torch.cuda.synchronize()
     hg, ig, wg = h.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy()
     href = []
@@ -281,6 +284,15 @@ def test_stack_mixed_shared_6_layers_t4():
 def test_stack_split_route_then_ffn(T):
     """moe_layer_route followed by moe_layer_ffn, the two halves of a layer."""
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T, n_layers=2).with_(seed=5), 2, T, split=True)
+
+
+def test_stack_prompt_batch_t96():
+    """A prompt-sized batch (96 tokens, past the layer calls' 32) through two
+    all-Q4_K layers by moe_rmsnorm + moe_route_topk + moe_expert_ffn: 8
+    experts at top-4, so each expert takes about 48 tokens, two MFMA work
+    entries of at most 32."""
+    cfg = W.qwen3_30b_a3b_q4k(T=96, n_layers=2).with_(H=512, I=192, E=8, k=4, seed=11)
+    _run_stack_and_compare(cfg, 2, 96, T_max=8, prompt=True)
 
 
 def test_mixed_shared_split():
