@@ -60,6 +60,8 @@ ROUTE_CASES = [
     # prompt-sized batches (moe_route_topk takes up to 256 tokens)
     (64, 512, 64, 6, False, 7),
     (256, 256, 16, 4, True, 8),
+    # limits: E = 1024 experts, k = 64
+    (3, 512, 1024, 64, False, 9),
 ]
 
 
@@ -150,6 +152,11 @@ FFN_CASES = [
     ((W.Q4_K,) * 3, 512, 192, 8, 8, 0, 64, False),      # 64 pairs per expert: two entries each
     ((W.Q4_K,) * 3, 1024, 320, 16, 4, 1, 256, True),    # 256 tokens, a shared expert of 8 entries
     ((W.Q6_K, W.Q6_K, W.Q8_0), 512, 128, 6, 2, 1, 48, False),
+    # limits and degenerate cases: H = 8192 (the largest), k = 64 (the largest),
+    # a single expert (E = k = 1: weight one)
+    ((W.Q8_0,) * 3, 8192, 64, 4, 2, 0, 2, False),
+    ((W.Q4_K,) * 3, 256, 64, 64, 64, 0, 2, False),
+    ((W.Q4_K,) * 3, 512, 128, 1, 1, 0, 3, False),
 ]
 
 
