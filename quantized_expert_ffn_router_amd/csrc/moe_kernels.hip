@@ -2417,6 +2417,38 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
         }
     __syncthreads();
     int nj = 0, nh = 0, nev = 0;
+    if (!evict) {
+        // no miss can evict: every decision is a hit or the next free slot,
+        // so thread 0 walks the ids alone, with no barrier between them
+        if (tid == 0) {
+            for (int i = 0; i < nd; i++) {
+                const int e = list[i];
+                const int key = (int)(kbase + e);
+                int s = wh[i];
+                const bool hit = s >= 0;
+                if (hit) nh++;
+                else s = nf++;
+                ++clk;
+                a.stamp[s] = clk;
+                uint8_t *slot = a.pool + (size_t)s * a.slot_bytes;
+                a.dtab[key] = slot;
+                if (!hit) {
+                    a.where[key] = s;
+                    a.key[s] = key;
+                    a.jobs[nj++] = CacheJob{slot, (const uint8_t *)a.src[key]};
+                }
+                if (a.trace) {
+                    const int t = a.ntrace[0] + i;
+                    if (t < a.trace_cap) {
+                        a.trace[4 * t] = a.layer;
+                        a.trace[4 * t + 1] = e;
+                        a.trace[4 * t + 2] = hit ? 1 : 0;
+                        a.trace[4 * t + 3] = -1;
+                    }
+                }
+            }
+        }
+    } else
     // every thread walks the ids with the same (uniform) decisions; thread 0
     // writes the state, all threads take part in the minimum search
     for (int i = 0; i < nd; i++) {
