@@ -2752,7 +2752,7 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s)
     }
     k_cache_lookup<<<1, kCacheThreads, lds, s>>>(a);
     LAUNCH_OK("k_cache_lookup");
-    k_cache_copy<<<512, kCacheCopyThreads, 0, s>>>(a.jobs, a.njobs, a.slot_bytes);
+    k_cache_copy<<<128, kCacheCopyThreads, 0, s>>>(a.jobs, a.njobs, a.slot_bytes);
     LAUNCH_OK("k_cache_copy");
     return MOE_OK;
 }
