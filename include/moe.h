@@ -2,7 +2,9 @@
  * moe.h -- C ABI of libmoe, the MI355X (gfx950) decode-time MoE expert FFN.
  *
  * The library computes one Mixture-of-Experts FFN layer for a small decode
- * batch (T <= 32 tokens) whose experts are stored as GGUF-style quantized
+ * batch (T <= 32 tokens for the fused layer calls and the cache; the
+ * stand-alone router and FFN calls also take prompt-sized batches of up to
+ * 256) whose experts are stored as GGUF-style quantized
  * blocks: router GEMV, softmax top-k with renormalised weights, grouping of
  * (token, expert) pairs, gate/up quantized matvecs with SiLU(gate)*up, the
  * down matvec and the weighted combine (plus always-active shared experts
@@ -114,7 +116,8 @@ moe_status moe_rmsnorm(const float *h, int32_t T, int32_t H, float eps, float *x
  *   w        device fp32 [T, k]: softmax over the k selected logits (equal
  *            to the full softmax renormalised over the k winners)
  *   logits   device fp32 [T, E] or NULL
- * 1 <= T <= 32, 1 <= k <= E <= 1024, H a multiple of 256. */
+ * 1 <= T <= 256 (prompt-sized batches too), 1 <= k <= E <= 1024, k <= 64,
+ * H a multiple of 256. */
 moe_status moe_route_topk(const float *x, int32_t T, int32_t H, const float *w_router,
                           const float *bias, int32_t E, int32_t k, int32_t *idx, float *w,
                           float *logits, hipStream_t s);
@@ -158,7 +161,9 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s);
  *               [I, Ipad) are not written
  *   ws          workspace from moe_workspace_bytes(d, >=T, >=k, >=E, >=n_shared),
  *               initialised once with moe_workspace_init
- * 1 <= T <= 32.  The experts' contributions are added into y with float
+ * 1 <= T <= 256 (batches above 32 tokens, prompt-sized, are grouped by a
+ * one-workgroup kernel into work entries of at most 32 pairs on the MFMA
+ * path, 4 otherwise).  The experts' contributions are added into y with float
  * atomics, so the order of the sum over a token's experts follows the
  * order in which workgroups finish: results agree with any fixed order to
  * fp32 rounding, but their last bits can differ from run to run.  The same
