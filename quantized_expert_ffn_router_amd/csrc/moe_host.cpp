@@ -466,7 +466,21 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
              hipMemset(c->dgroups[g].stamp, 0, (size_t)n * 4) == hipSuccess &&
              hipMemcpy(c->dgroups[g].key, keys.data(), (size_t)n * 4, hipMemcpyHostToDevice) == hipSuccess;
     }
-    if (!ok) { set_error("moe_cache_device_enable: device allocation failed"); return MOE_ERR_HIP; }
+    if (!ok) {
+        // leave the cache as it was (host lookups, nothing allocated)
+        for (auto &dg : c->dgroups) {
+            if (dg.stamp) (void)hipFree(dg.stamp);
+            if (dg.key) (void)hipFree(dg.key);
+        }
+        c->dgroups.clear();
+        for (void **pp : {(void **)&c->d_where, (void **)&c->d_src, (void **)&c->d_counters, (void **)&c->d_jobs,
+                          (void **)&c->d_stats, (void **)&c->d_trace}) {
+            if (*pp) (void)hipFree(*pp);
+            *pp = nullptr;
+        }
+        set_error("moe_cache_device_enable: device allocation failed");
+        return MOE_ERR_HIP;
+    }
     // the host table is no longer refreshed; the device lookup writes dtab
     c->trace_cap = trace_capacity;
     c->dev = true;
