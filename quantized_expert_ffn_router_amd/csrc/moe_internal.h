@@ -109,6 +109,9 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s);
 // (as moe_workspace_init leaves it) and leaves it zero.
 constexpr size_t kKeys = 0;
 constexpr size_t kKeysBytes = (size_t)kMaxT * kMaxE * 4;
+// After them, the per-token top-k workgroups' hand-over of each token's k
+// selections to the route tail (64-bit, never zero), same protocol.
+constexpr size_t kTkBytes = (size_t)kMaxT * 64 * 8;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
@@ -132,7 +135,7 @@ constexpr int kX16Bytes = 1072;
 
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U, UI;  // U: distinct experts, UI: work items (both at most)
-    size_t keys, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
+    size_t keys, tk, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -146,7 +149,8 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.U = ur + ns;
     L.UI = L.U + (L.P + kItemTok - 1) / kItemTok;
     L.keys = kKeys;
-    size_t o = kKeys + kKeysBytes;
+    L.tk = kKeys + kKeysBytes;
+    size_t o = L.tk + kTkBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
     L.x16 = take((size_t)T * (d.H / 256) * kX16Bytes);

@@ -613,6 +613,7 @@ __device__ __forceinline__ void topk_wave_any(const uint32_t *keys, int E, int k
 constexpr int kStageKeys = 4096;  // keys the route tail keeps in LDS
 constexpr int kWaveTopE = 256;    // experts for the per-wave topk_multi (4 keys per lane)
 constexpr int kCandSlots = kWaveTopE + 9 + kMaxK + 1;  // candidate slots of one token
+constexpr int kTopkBlocksMinT = 16;  // batches above this rank their tokens in top-k workgroups
 
 // floor(i / d) for 0 <= i < 2^16, 1 <= d <= 2^16, with r = 1.0f/d: (i + 0.5)/d
 // is at least 0.5/d away from an integer, far more than the float error.
@@ -642,7 +643,10 @@ struct RouteArgs {
     GroupOut go;
     Enc hpad;               // [P] vectors of kd: padding blocks zeroed here
     int P, I, kd;
-    int n_expert_blocks;    // router workgroups (row pair, token group); then T * ceil(H/kEncPos) encoding workgroups, then the tail
+    int n_expert_blocks;    // router workgroups (row pair, token group); then T * ceil(H/kEncPos) encoding workgroups,
+                            // then topk_blocks top-k workgroups, then the tail
+    int topk_blocks;        // 0, or T: a workgroup per token ranks its keys and hands them to the tail
+    unsigned long long *tk; // [T][k] hand-over of those selections (key << 32 | ~id, never zero)
 };
 
 // Top-k of NT tokens' E keys each by one wave (no barriers), keys in
@@ -806,6 +810,49 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
     if (lane == 0) *g.nuniq = k + ns;
 }
 
+// Top-k workgroup of token t (batches with topk_blocks): wave 0 polls the
+// token's E keys into registers (bounded, as the tail does), ranks them with
+// topk_one and hands the k selections to the tail with coherent 64-bit
+// stores (key << 32 | ~id: the key half is never zero).  A poll that gives
+// up hands over selections with a zero key half, which the tail never
+// accepts: it gives up too and routes with NaN weights.
+template <int NVL>
+__device__ __forceinline__ void route_topk_token(const RouteArgs &a, int t, uint64_t *cand)
+{
+    const int E = a.E, k = a.k, lane = lane_id();
+    const unsigned *kt = a.keys + (size_t)t * E;
+    uint32_t key[NVL];
+    bool ok = true;
+    for (unsigned it = 0;; it++) {
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < NVL; i++) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? ld_coh_u(kt + e) : 0u;
+            missing |= e < E && key[i] == 0u;
+        }
+        if (!__ballot(missing)) break;
+        if (it >= kSpinLimit) {
+            ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    uint64_t cs = topk_one<NVL>(key, E, k, cand);
+    if (!ok) cs = 0xffffffffull;  // zero key half: never accepted
+    if (lane < k)
+        __hip_atomic_store(a.tk + (size_t)t * k + lane, (unsigned long long)cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void route_topk_role(const RouteArgs &a, int t)
+{
+    __shared__ __align__(16) uint64_t tcand[kCandSlots];
+    if (wave_id() != 0) return;
+    if (a.E <= 64) route_topk_token<1>(a, t, tcand);
+    else if (a.E <= 128) route_topk_token<2>(a, t, tcand);
+    else route_topk_token<4>(a, t, tcand);  // E <= kWaveTopE (the host's condition)
+}
+
 // The tail workgroup: a single token goes to route_tail_one; otherwise the
 // workgroup polls the keys until every one is written, then top-k (clearing
 // the keys for the next launch), softmax and grouping.  A poll that
@@ -845,11 +892,37 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         else route_tail_one<16>(a, cand, pre);
         return;
     }
+    int ok = 1;
+    constexpr int kPollQ = 8;
+    if (a.topk_blocks) {
+        // the top-k workgroups' selections, polled like the keys
+        const int nk = T * k;
+        for (unsigned it = 0;; it++) {
+            int missing = 0;
+            for (int i = tid; i < nk; i += kRouteWG) {
+                const unsigned long long c = __hip_atomic_load(a.tk + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sidx[i] = (int)~(uint32_t)c;
+                skey[i] = (uint32_t)(c >> 32);
+                missing |= (c >> 32) == 0ull;  // not yet written (or given up on)
+            }
+            if (!__ballot(missing)) break;
+            if (it >= kSpinLimit) {
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        ok = __syncthreads_and(ok);
+        // clear both hand-overs for the next launch (the top-k workgroups are
+        // done with the keys once their selections are all here)
+        for (int i = tid; i < n; i += kRouteWG) a.keys[i] = 0u;
+        for (int i = tid; i < nk; i += kRouteWG) a.tk[i] = 0ull;
+        settle(pre);
+        __syncthreads();
+    } else {
     // each wave polls its own share of the keys, then the workgroup meets
     // once; a thread's keys of a round are all loaded before any is checked
     // (one round trip per round, not one per key)
-    int ok = 1;
-    constexpr int kPollQ = 8;
     for (unsigned it = 0;; it++) {
         int missing = 0;
         for (int i0 = tid; i0 < n; i0 += kPollQ * kRouteWG) {
@@ -902,6 +975,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
     // clear the keys for the next launch (plain stores: the launch boundary
     // makes them visible); nothing reads them again in this launch
     for (int i = tid; i < n; i += kRouteWG) a.keys[i] = 0u;
+    }
     // softmax over the k selected logits of each token (selection 0 is the
     // largest): for k <= 8, eight tokens per wave, lane 8q + j holding
     // selection j of token 8w + q; else a token per wave, lane j selection j
@@ -1017,6 +1091,10 @@ __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
     const int lane = lane_id();
     if (blk == (int)gridDim.x - 1) {
         route_tail(a);
+        return;
+    }
+    if (blk >= (int)gridDim.x - 1 - a.topk_blocks) {
+        route_topk_role(a, blk - ((int)gridDim.x - 1 - a.topk_blocks));
         return;
     }
     if (blk >= a.n_expert_blocks) {
@@ -2874,7 +2952,11 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
     // router workgroups: row pairs x token groups of kRouteTok
     a.n_expert_blocks = (E + kRouteRows - 1) / kRouteRows * ((T + kRouteTok - 1) / kRouteTok);
-    k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + 1, kRouteWG, 0, s>>>(a);
+    // above kTopkBlocksMinT tokens (the tail would rank them in several rounds
+    // of its 8 waves), a top-k workgroup per token
+    a.topk_blocks = T > kTopkBlocksMinT && E <= kWaveTopE ? T : 0;
+    a.tk = W.at<unsigned long long>(W.L.tk);
+    k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + a.topk_blocks + 1, kRouteWG, 0, s>>>(a);
     LAUNCH_OK("k_route");
     return MOE_OK;
 }

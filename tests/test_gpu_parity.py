@@ -253,6 +253,13 @@ def test_layer_wide_router(T):
     _run_stack_and_compare(W.tiny_q8_0(seed=6).with_(E=200, k=6), 1, T)
 
 
+@pytest.mark.parametrize("T,E,k", [(17, 200, 6), (24, 64, 1), (32, 128, 8)])
+def test_layer_per_token_topk(T, E, k):
+    """Batches above 16 tokens rank each token's router keys in a workgroup
+    of its own (4, 1 and 2 keys per lane for E=200, 64 and 128)."""
+    _run_stack_and_compare(W.tiny_q8_0(seed=8).with_(E=E, k=k), 1, T)
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_layer_qwen3_shape_q4k(T):
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T), 1, T)
@@ -287,7 +294,7 @@ def test_stack_mixed_shared_6_layers_t4():
     _run_stack_and_compare(sub, 6, 4)
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 8, 24])
 def test_stack_split_route_then_ffn(T):
     """moe_layer_route followed by moe_layer_ffn, the two halves of a layer."""
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T, n_layers=2).with_(seed=5), 2, T, split=True)
