@@ -310,6 +310,23 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity);
 moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
                                    hipStream_t stream);
 
+/* Cross-layer prefetch (Laptop post, section 2.3: the experts of the next
+ * layers are fetched while the current one computes).  idx (device int32
+ * [T][k]): the ids predicted for `layer`, e.g. its router applied to an
+ * earlier layer's state.  The lookup runs on `stream`, the stream of every
+ * other lookup of the cache, and counts in the statistics and the trace
+ * like any lookup; the misses' copies run on `copy_stream` (which must
+ * differ from `stream`) after the work queued on `stream` so far, so they
+ * overlap what `stream` does next.  The next moe_cache_lookup_device of
+ * `layer` makes its stream wait for those copies.  Because the copies are
+ * still running, the library refuses (MOE_ERR_CAPACITY) a lookup or
+ * prefetch that touches so many slots of the group that a prefetched slot
+ * could become the victim before that wait; MOE_ERR_STATE when `layer`
+ * already has a prefetch not yet taken by its lookup, MOE_ERR_BATCH when
+ * T > 32. */
+moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
+                                     hipStream_t stream, hipStream_t copy_stream);
+
 /* Copy the device trace (synchronizes): records of 4 int32 (layer, expert,
  * hit 1/0, evicted key layer*E+expert or -1), in lookup order; *n gets the
  * number of lookups made (the device keeps the first trace_capacity). */

@@ -255,6 +255,25 @@ def lookup_sequence(ids: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return np.asarray(L_, np.int32), np.asarray(E_, np.int32)
 
 
+def prefetch_lookup_sequence(ids: np.ndarray, pred: np.ndarray, targets: Sequence[Sequence[int]]
+                             ) -> Tuple[np.ndarray, np.ndarray]:
+    """Lookup order of a stack that prefetches the experts of later layers
+    while the current one computes (Laptop post, section 2.3).  ids, pred:
+    int [steps, layers, T*k], the routed ids and the ids predicted for each
+    layer; targets[l]: the layers whose predicted experts are looked up at
+    layer l, after layer l's own lookup.  Within each lookup the distinct
+    ids come once each in ascending order, as in lookup_sequence."""
+    L_, E_ = [], []
+    steps, layers = ids.shape[:2]
+    for s in range(steps):
+        for l in range(layers):
+            for m, row in [(l, ids[s, l])] + [(m, pred[s, m]) for m in targets[l]]:
+                for e in np.unique(row):
+                    L_.append(m)
+                    E_.append(int(e))
+    return np.asarray(L_, np.int32), np.asarray(E_, np.int32)
+
+
 # ---------------------------------------------------------------------------
 # layer and stack composition (per token; tokens are independent)
 

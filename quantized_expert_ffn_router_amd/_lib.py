@@ -18,7 +18,7 @@ EXPORTED = [
     "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
     "moe_cache_plan", "moe_cache_create", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
-    "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_trace_read",
+    "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_prefetch_device", "moe_cache_trace_read",
 ]
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_QTYPE",
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
         "moe_cache_reset_stats": (i32, [P]),
         "moe_cache_device_enable": (i32, [P, i32]),
         "moe_cache_lookup_device": (i32, [P, i32, P, i32, i32, P]),
+        "moe_cache_prefetch_device": (i32, [P, i32, P, i32, i32, P, P]),
         "moe_cache_trace_read": (i32, [P, P, i32, P]),
         "moe_cache_destroy": (None, [P]),
     }
@@ -270,6 +271,15 @@ class Cache:
         if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous() or idx.numel() < T * k:
             raise ValueError("idx must be a contiguous int32 device tensor of T*k ids")
         _check(lib().moe_cache_lookup_device(self.h, layer, idx.data_ptr(), T, k, _stream(stream)))
+
+    def prefetch_device(self, layer: int, idx, T: int, k: int, copy_stream, stream=None):
+        """Prefetch of predicted ids for `layer` (moe_cache_prefetch_device):
+        the lookup on `stream`, the miss copies on `copy_stream`."""
+        import torch
+        if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous() or idx.numel() < T * k:
+            raise ValueError("idx must be a contiguous int32 device tensor of T*k ids")
+        _check(lib().moe_cache_prefetch_device(self.h, layer, idx.data_ptr(), T, k, _stream(stream),
+                                               _stream(copy_stream)))
 
     def trace_read(self, capacity: int) -> np.ndarray:
         """The device trace: int32 [n, 4] (layer, expert, hit, evicted key or -1)."""

@@ -177,6 +177,14 @@ struct moe_cache {
     CacheJob *d_jobs = nullptr;       // [E]
     unsigned long long *d_stats = nullptr;  // 9 counters
     int32_t *d_trace = nullptr;
+    // prefetch (moe_cache_prefetch_device): per layer a list of miss copies
+    // run on the caller's copy stream and the event that ends them, and the
+    // slot touches of the layer's group since the prefetch (-1: none pending)
+    CacheJob *d_pjobs = nullptr;      // [L][E]
+    int32_t *d_pnjobs = nullptr;      // [L]
+    hipEvent_t ev_fork = nullptr;
+    std::vector<hipEvent_t> ev_pref;  // [L]
+    std::vector<int> pend_touch;      // [L]
     int trace_cap = 0;
 };
 
@@ -215,9 +223,52 @@ void destroy(moe_cache *c)
         if (dg.key) (void)hipFree(dg.key);
     }
     for (void *p : {(void *)c->d_where, (void *)c->d_src, (void *)c->d_counters, (void *)c->d_jobs,
-                    (void *)c->d_stats, (void *)c->d_trace})
+                    (void *)c->d_stats, (void *)c->d_trace, (void *)c->d_pjobs, (void *)c->d_pnjobs})
         if (p) (void)hipFree(p);
+    for (auto ev : c->ev_pref)
+        if (ev) (void)hipEventDestroy(ev);
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     delete c;
+}
+
+// A prefetch's copies run beside the lookups that follow it.  The slots it
+// filled were touched last by the prefetch, so a later lookup can take one
+// of them as its victim only once every other slot of the group has been
+// touched since.  A call that could reach that count while the prefetch may
+// still be copying is refused (`skip`: the layer whose own wait comes first).
+moe_status prefetch_guard(moe_cache *c, int g, int n, int skip, const char *who)
+{
+    for (int m = 0; m < c->n_layers; m++)
+        if (m != skip && c->pend_touch[m] >= 0 && c->layer_group[m] == g && c->pend_touch[m] + n >= c->groups[g].n_slots) {
+            set_error("%s: %d more slot touches could evict the experts prefetched for layer %d (group of %d slots)",
+                      who, n, m, c->groups[g].n_slots);
+            return MOE_ERR_CAPACITY;
+        }
+    return MOE_OK;
+}
+
+void prefetch_count(moe_cache *c, int g, int n)
+{
+    for (int m = 0; m < c->n_layers; m++)
+        if (c->pend_touch[m] >= 0 && c->layer_group[m] == g) c->pend_touch[m] += n;
+}
+
+CacheDevArgs device_args(moe_cache *c, int layer, const int32_t *idx, int T, int k)
+{
+    const int g = c->layer_group[layer], ng = (int)c->groups.size();
+    auto &G = c->groups[g];
+    CacheDevArgs a{};
+    a.idx = idx; a.T = T; a.k = k; a.layer = layer; a.E = c->E;
+    a.where = c->d_where; a.src = c->d_src; a.dtab = c->dtab;
+    a.stamp = c->dgroups[g].stamp; a.key = c->dgroups[g].key;
+    a.next_free = c->d_counters + g;
+    a.clock = (uint32_t *)(c->d_counters + ng);
+    a.njobs = c->d_counters + ng + 1;
+    a.pool = G.pool; a.slot_bytes = G.slot_bytes; a.n_slots = G.n_slots;
+    a.jobs = c->d_jobs;
+    a.stats = c->d_stats;
+    a.trace = c->d_trace; a.ntrace = c->d_counters + ng + 2; a.trace_cap = c->trace_cap;
+    return a;
 }
 
 }  // namespace
@@ -451,6 +502,9 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
               hipMalloc((void **)&c->d_counters, (ng + 3) * 4) == hipSuccess &&
               hipMalloc((void **)&c->d_jobs, (size_t)c->E * sizeof(CacheJob)) == hipSuccess &&
               hipMalloc((void **)&c->d_stats, sizeof(moe_cache_stats_t)) == hipSuccess &&
+              hipMalloc((void **)&c->d_pjobs, LE * sizeof(CacheJob)) == hipSuccess &&
+              hipMalloc((void **)&c->d_pnjobs, (size_t)c->n_layers * 4) == hipSuccess &&
+              hipMemset(c->d_pnjobs, 0, (size_t)c->n_layers * 4) == hipSuccess &&
               hipMemcpy(c->d_where, minus1.data(), LE * 4, hipMemcpyHostToDevice) == hipSuccess &&
               hipMemcpy(c->d_src, src.data(), LE * sizeof(void *), hipMemcpyHostToDevice) == hipSuccess &&
               hipMemset(c->d_counters, 0, (ng + 3) * 4) == hipSuccess &&
@@ -474,7 +528,7 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
         }
         c->dgroups.clear();
         for (void **pp : {(void **)&c->d_where, (void **)&c->d_src, (void **)&c->d_counters, (void **)&c->d_jobs,
-                          (void **)&c->d_stats, (void **)&c->d_trace}) {
+                          (void **)&c->d_stats, (void **)&c->d_trace, (void **)&c->d_pjobs, (void **)&c->d_pnjobs}) {
             if (*pp) (void)hipFree(*pp);
             *pp = nullptr;
         }
@@ -483,6 +537,8 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
     }
     // the host table is no longer refreshed; the device lookup writes dtab
     c->trace_cap = trace_capacity;
+    c->pend_touch.assign(c->n_layers, -1);
+    c->ev_pref.assign(c->n_layers, nullptr);
     c->dev = true;
     return MOE_OK;
 }
@@ -502,19 +558,57 @@ moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *i
         set_error("moe_cache_lookup_device: %d selections may exceed the %d slots of the group", T * k, G.n_slots);
         return MOE_ERR_CAPACITY;
     }
-    const int ng = (int)c->groups.size();
-    CacheDevArgs a{};
-    a.idx = idx; a.T = T; a.k = k; a.layer = layer; a.E = c->E;
-    a.where = c->d_where; a.src = c->d_src; a.dtab = c->dtab;
-    a.stamp = c->dgroups[g].stamp; a.key = c->dgroups[g].key;
-    a.next_free = c->d_counters + g;
-    a.clock = (uint32_t *)(c->d_counters + ng);
-    a.njobs = c->d_counters + ng + 1;
-    a.pool = G.pool; a.slot_bytes = G.slot_bytes; a.n_slots = G.n_slots;
-    a.jobs = c->d_jobs;
-    a.stats = c->d_stats;
-    a.trace = c->d_trace; a.ntrace = c->d_counters + ng + 2; a.trace_cap = c->trace_cap;
-    return launch_cache_device(a, stream);
+    if (moe_status st = prefetch_guard(c, g, T * k, layer, "moe_cache_lookup_device")) return st;
+    if (c->pend_touch[layer] >= 0) {
+        // the layer's prefetched copies end before its lookup
+        if (hipStreamWaitEvent(stream, c->ev_pref[layer], 0) != hipSuccess) {
+            set_error("moe_cache_lookup_device: hipStreamWaitEvent failed");
+            return MOE_ERR_HIP;
+        }
+        c->pend_touch[layer] = -1;
+    }
+    prefetch_count(c, g, T * k);
+    return launch_cache_device(device_args(c, layer, idx, T, k), stream);
+}
+
+moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
+                                     hipStream_t stream, hipStream_t copy_stream)
+{
+    if (!c || !idx || layer < 0 || layer >= c->n_layers || k < 1 || k > c->E || copy_stream == stream) {
+        set_error("moe_cache_prefetch_device: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (!c->dev) { set_error("moe_cache_prefetch_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
+    if (T < 1 || T > kMaxT) { set_error("moe_cache_prefetch_device: T=%d outside [1, 32]", T); return MOE_ERR_BATCH; }
+    if (c->pend_touch[layer] >= 0) {
+        set_error("moe_cache_prefetch_device: layer %d has a prefetch that its lookup has not taken yet", layer);
+        return MOE_ERR_STATE;
+    }
+    const int g = c->layer_group[layer];
+    if (T * k >= c->groups[g].n_slots) {
+        set_error("moe_cache_prefetch_device: %d selections need more than the %d slots of the group", T * k,
+                  c->groups[g].n_slots);
+        return MOE_ERR_CAPACITY;
+    }
+    if (moe_status st = prefetch_guard(c, g, T * k, -1, "moe_cache_prefetch_device")) return st;
+    if (!c->ev_fork && hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess) {
+        c->ev_fork = nullptr;
+        set_error("moe_cache_prefetch_device: hipEventCreate failed");
+        return MOE_ERR_HIP;
+    }
+    if (!c->ev_pref[layer] && hipEventCreateWithFlags(&c->ev_pref[layer], hipEventDisableTiming) != hipSuccess) {
+        c->ev_pref[layer] = nullptr;
+        set_error("moe_cache_prefetch_device: hipEventCreate failed");
+        return MOE_ERR_HIP;
+    }
+    CacheDevArgs a = device_args(c, layer, idx, T, k);
+    a.jobs = c->d_pjobs + (size_t)layer * c->E;
+    a.njobs = c->d_pnjobs + layer;
+    moe_status st = launch_cache_device(a, stream, copy_stream, c->ev_fork, c->ev_pref[layer]);
+    if (st != MOE_OK) return st;
+    prefetch_count(c, g, T * k);
+    c->pend_touch[layer] = T * k;
+    return MOE_OK;
 }
 
 moe_status moe_cache_trace_read(moe_cache *c, int32_t *out, int32_t capacity, int32_t *n)

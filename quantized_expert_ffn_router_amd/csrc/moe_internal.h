@@ -101,7 +101,10 @@ struct CacheDevArgs {
     int trace_cap;
 };
 constexpr int kCacheMaxSlots = 16384;  // slots per group that the device lookup holds in LDS
-moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s);
+// The lookup on s, then the miss copies: on s, or with a side stream cs on cs
+// after `fork` (recorded on s), recording `done` on cs after them.
+moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t cs = nullptr,
+                               hipEvent_t fork = nullptr, hipEvent_t done = nullptr);
 
 // The router's hand-over of logit keys sits at a fixed offset at the start of
 // every workspace, sized for the largest batch and expert count, so that calls

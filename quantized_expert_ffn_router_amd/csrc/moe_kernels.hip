@@ -2819,7 +2819,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
 
 }  // namespace
 
-moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s)
+moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t cs, hipEvent_t fork, hipEvent_t done)
 {
     const size_t lds = (size_t)a.n_slots * 8;
     static bool attr = false;
@@ -2830,8 +2830,14 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s)
     }
     k_cache_lookup<<<1, kCacheThreads, lds, s>>>(a);
     LAUNCH_OK("k_cache_lookup");
+    if (fork) {
+        HIP_OK(hipEventRecord(fork, s));
+        HIP_OK(hipStreamWaitEvent(cs, fork, 0));
+        s = cs;
+    }
     k_cache_copy<<<128, kCacheCopyThreads, 0, s>>>(a.jobs, a.njobs, a.slot_bytes);
     LAUNCH_OK("k_cache_copy");
+    if (done) HIP_OK(hipEventRecord(done, s));
     return MOE_OK;
 }
 

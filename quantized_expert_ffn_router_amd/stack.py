@@ -154,11 +154,21 @@ class CachedStack:
     current stream, with no host synchronization, so a whole step can be
     captured in a HIP graph.  trace_capacity > 0 keeps the device's lookup
     trace (device_trace).
+
+    prefetch_depth=d > 0 (device_lookup only) adds cross-layer prefetch: at
+    layer l, after its lookup, the layers up to l+d not prefetched yet in
+    this step (1..d at layer 0, then l+d) have their experts predicted by
+    applying their routers to layer l's input state (moe_rmsnorm +
+    moe_route_topk) and looked up with moe_cache_prefetch_device, whose
+    miss copies run on copy_stream beside the rest of the step.
     """
 
     def __init__(self, layers: Sequence[LayerSpec], packed: Sequence[torch.Tensor], slots: Sequence[int],
                  T_max: int = 8, device: str = "cuda", eps: float = 1e-6, device_lookup: bool = False,
-                 trace_capacity: int = 0):
+                 trace_capacity: int = 0, prefetch_depth: int = 0):
+        if prefetch_depth and not device_lookup:
+            raise ValueError("prefetch_depth needs device_lookup")
+        self.prefetch_depth = int(prefetch_depth)
         self.layers = list(layers)
         self.device = torch.device(device)
         self.eps = eps
@@ -210,6 +220,11 @@ class CachedStack:
         # ids of a layer-step: the first T*k entries, contiguous [T, k]
         self.idx_dev = torch.empty(T_max * kmax, dtype=torch.int32, device=self.device)
         self.idx_host = torch.empty(T_max * kmax, dtype=torch.int32, pin_memory=True)
+        if self.prefetch_depth:
+            H = self.layers[0].H
+            self._fxhat = torch.empty((T_max, H), dtype=torch.float32, device=self.device)
+            self._fidx = torch.empty(T_max * kmax, dtype=torch.int32, device=self.device)
+            self._fw = torch.empty(T_max * kmax, dtype=torch.float32, device=self.device)
         self.device_lookup = device_lookup
         self.trace_capacity = trace_capacity
         if device_lookup:
@@ -232,6 +247,8 @@ class CachedStack:
                           s.n_shared, self.eps, idx, None, self.ws, self.ws_bytes)
         if self.device_lookup:
             self.cache.lookup_device(layer, idx, T, s.k)
+            if self.prefetch_depth:
+                self._prefetch(layer, h)
             L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
                             self.ws, self.ws_bytes)
             return
@@ -254,6 +271,22 @@ class CachedStack:
         torch.cuda.current_stream(self.device).wait_stream(self.copy_stream)
         L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
                         self.ws, self.ws_bytes)
+
+    def prefetch_targets(self, layer: int) -> List[int]:
+        """Layers whose experts are prefetched at `layer` (before its FFN)."""
+        d, n = self.prefetch_depth, len(self.layers)
+        first = 1 if layer == 0 else layer + d
+        return [m for m in range(first, min(layer + d, n - 1) + 1)] if d else []
+
+    def _prefetch(self, layer: int, h: torch.Tensor):
+        T, H = h.shape
+        xh = self._fxhat[:T]
+        L.moe_rmsnorm(h, T, H, self.eps, xh)
+        for m in self.prefetch_targets(layer):
+            s = self.layers[m]
+            idx = self._fidx[:T * s.k].view(T, s.k)
+            L.moe_route_topk(xh, T, H, self.routers[m], self.biases[m], s.E, s.k, idx, self._fw[:T * s.k], None)
+            self.cache.prefetch_device(m, idx, T, s.k, self.copy_stream)
 
     def step(self, h: torch.Tensor):
         """One decode step through every layer; h [T, H] fp32 is updated in place."""

@@ -37,7 +37,7 @@ def _groups(cfg, n_layers):
     return descs, ebytes, per_group, layer_group
 
 
-def _run(cfg, n_layers, steps, fraction, T, device_lookup=False):
+def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0):
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts, n_layers)
     specs = layer_specs(cfg, n_layers)
@@ -49,8 +49,11 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False):
     assert st == 0 and rc == 0 and np.array_equal(slots, oslots), (slots, oslots)
     _say(cfg.name, dict(layers=n_layers, steps=steps, T=T, fraction=fraction, slots=list(slots), device=device_lookup))
     packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
-    cap = steps * n_layers * T * cfg.k
-    cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=device_lookup, trace_capacity=cap)
+    cap = steps * n_layers * T * cfg.k * (2 if prefetch_depth else 1)
+    cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=device_lookup, trace_capacity=cap,
+                     prefetch_depth=prefetch_depth)
+    targets = [cs.prefetch_targets(l) for l in range(n_layers)]
+    pred = np.zeros((steps, n_layers, T * cfg.k), np.int32)
     cs.trace = []
     ids = np.empty((steps, n_layers, T * cfg.k), np.int32)
     try:
@@ -62,12 +65,19 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False):
             outs = [oracle.stack_token(olayers, x[t]) for t in range(T)]
             for l in range(n_layers):
                 ids[step, l] = np.concatenate([outs[t][l].route.idx.ravel() for t in range(T)])
+                for m in targets[l]:  # layer m's router on layer l's input state
+                    rs = [oracle.route(oracle.rmsnorm(np.asarray(x[t] if l == 0 else outs[t][l - 1].h_next,
+                                                                 np.float32))[None, :],
+                                       olayers[m].router, olayers[m].bias, cfg.k) for t in range(T)]
+                    assert min(float(r.gap[0]) for r in rs) >= 1e-4, f"near-tie in the prediction of layer {m}"
+                    pred[step, m] = np.concatenate([r.idx.ravel() for r in rs])
             href = np.stack([outs[t][-1].h_next for t in range(T)])
             hg = h.cpu().numpy()
             assert oracle.rel_l2(hg, href) <= REL_L2_BAR, f"step {step}"
             assert centered_rel_l2(hg - x, href - x) <= REL_L2_BAR, f"step {step}"
         # the GPU's lookups are the oracle routing's distinct experts ...
-        LL, EE = oracle.lookup_sequence(ids)
+        LL, EE = (oracle.prefetch_lookup_sequence(ids, pred, targets) if prefetch_depth
+                  else oracle.lookup_sequence(ids))
         if device_lookup:
             gl, ge, hit, vl, ve = cs.device_trace()
         else:
@@ -99,6 +109,48 @@ def test_cache_zipf_qwen3_shape(fraction, device_lookup):
     """Zipf-biased routing over a 4-layer Qwen3-30B-A3B-shaped Q4_K stack,
     pool at 10 % / 60 % of the routed expert bytes, 24 decode steps."""
     _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, device_lookup)
+
+
+@pytest.mark.parametrize("fraction,depth", [(0.1, 2), (0.6, 1)])
+def test_cache_prefetch_device_lru(fraction, depth):
+    """Cross-layer prefetch on the 4-layer Zipf stack: the predicted experts
+    (each later layer's router on the current layer's input state) are looked
+    up beside the routed ones and copied on a side stream; the outputs stay
+    the oracle's and the trace is the oracle LRU's over the prefetching
+    lookup order, bit for bit."""
+    s = _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, True, prefetch_depth=depth)
+    assert s["misses"] > 0
+
+
+def test_cache_prefetch_errors():
+    """Prefetch refusals: the compute stream as copy stream, a second
+    prefetch of a layer before its lookup, and a lookup whose slot touches
+    could evict a prefetched slot still being copied; then the lookups that
+    take the prefetches, against the oracle LRU."""
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=2).with_(E=16, k=2, seed=9)
+    experts = ExpertCache(cfg)
+    specs = layer_specs(cfg, 2)
+    packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
+    cs = CachedStack(specs, packed, [5], T_max=2, device_lookup=True, trace_capacity=64)
+    try:
+        idx = torch.tensor([1, 2, 3, 4, 5, 6], dtype=torch.int32, device=DEV)
+        with pytest.raises(moe.MoeError):
+            cs.cache.prefetch_device(1, idx, 1, 2, torch.cuda.current_stream())
+        cs.cache.prefetch_device(1, idx, 1, 2, cs.copy_stream)       # layer 1: experts 1, 2
+        with pytest.raises(moe.MoeError):                            # layer 1 has one pending
+            cs.cache.prefetch_device(1, idx, 1, 2, cs.copy_stream)
+        with pytest.raises(moe.MoeError):                            # 2 + 3 touches reach the 5 slots
+            cs.cache.lookup_device(0, idx[2:], 1, 3)
+        cs.cache.lookup_device(0, idx[2:], 1, 2)                     # 2 + 2 < 5: layer 0 experts 3, 4
+        cs.cache.lookup_device(1, idx[:2], 1, 2)                     # waits for the copies: two hits
+        cs.cache.lookup_device(0, idx[2:], 1, 3)                     # nothing pending any more
+        torch.cuda.synchronize()
+        gl, ge, hit, vl, ve = cs.device_trace()
+        assert list(gl) == [1, 1, 0, 0, 1, 1, 0, 0, 0] and list(ge) == [1, 2, 3, 4, 1, 2, 3, 4, 5]
+        ref = oracle.lru([5], [0, 0], gl, ge)
+        assert np.array_equal(hit, ref.hit) and list(hit) == [0, 0, 0, 0, 1, 1, 1, 1, 0]
+    finally:
+        cs.close()
 
 
 def test_cache_four_requests_thrash_device_lru():

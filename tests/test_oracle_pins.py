@@ -459,6 +459,22 @@ def test_lru_large_capacity_gives_compulsory_misses_only():
     assert list(tr.hit) == first
 
 
+def test_prefetch_lookup_sequence_order():
+    """Worked by hand: at layer 0 the predicted experts of layers 1 and 2 are
+    looked up right after layer 0's own; an empty schedule is the plain
+    order; a perfect prediction on a pool that holds everything turns every
+    later lookup of the prefetched layers into hits."""
+    ids = np.array([[[3, 1], [2, 2], [0, 4]]], np.int32)
+    pred = np.array([[[9, 9], [5, 2], [4, 4]]], np.int32)
+    L, E = oracle.prefetch_lookup_sequence(ids, pred, [[1, 2], [], []])
+    assert list(L) == [0, 0, 1, 1, 2, 1, 2, 2] and list(E) == [1, 3, 2, 5, 4, 2, 0, 4]
+    L0, E0 = oracle.prefetch_lookup_sequence(ids, pred, [[], [], []])
+    L1, E1 = oracle.lookup_sequence(ids)
+    assert np.array_equal(L0, L1) and np.array_equal(E0, E1)
+    tr = oracle.lru([16], [0, 0, 0], *oracle.prefetch_lookup_sequence(ids, ids, [[1, 2], [], []]))
+    assert list(tr.hit) == [0, 0, 0, 0, 0, 1, 1, 1]
+
+
 def test_lookup_sequence_order():
     ids = np.array([[[3, 1, 3, 0], [2, 2, 2, 2]]], np.int32)
     L, E = oracle.lookup_sequence(ids)
