@@ -101,3 +101,20 @@ def test_repack_is_a_byte_permutation_with_documented_tiles(qt):
         at = 1 * tb + 5 * 16
     assert np.array_equal(out[at:at + 16], first16)
     assert S == 2
+
+
+def test_prefetch_schedule():
+    """Cross-layer prefetch schedule (host logic): at layer 0 the next d
+    layers, then l+d, never past the last layer; every layer after the
+    first is prefetched exactly once per step, before its own lookup."""
+    from types import SimpleNamespace
+    from quantized_expert_ffn_router_amd.stack import CachedStack
+    for n, d in [(4, 1), (4, 2), (48, 2), (3, 5), (1, 2)]:
+        obj = SimpleNamespace(prefetch_depth=d, layers=[None] * n)
+        sched = [CachedStack.prefetch_targets(obj, l) for l in range(n)]
+        flat = [m for t in sched for m in t]
+        assert sorted(flat) == list(range(1, n)) and len(flat) == len(set(flat))
+        assert all(l < m <= l + d for l, t in enumerate(sched) for m in t)
+    assert [CachedStack.prefetch_targets(SimpleNamespace(prefetch_depth=2, layers=[None] * 5), l)
+            for l in range(5)] == [[1, 2], [3], [4], [], []]
+    assert CachedStack.prefetch_targets(SimpleNamespace(prefetch_depth=0, layers=[None] * 5), 0) == []
