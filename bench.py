@@ -270,24 +270,29 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
         # cross-layer prefetch (device LRU, graph): at each layer the next
         # layers' routers on its input state predict their experts, whose
         # copies run on a side stream during the current layer
-        for depth in (2,):
+        for depth, mode in ((2, "eager"), (2, "graph")):
             cs = CachedStack(zspecs, packed, slots, T_max=1, device_lookup=True, prefetch_depth=depth)
             hb = xs[0].clone()
             torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                cs.step(hb)
-            torch.cuda.synchronize()
+            if mode == "graph":
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    cs.step(hb)
+                torch.cuda.synchronize()
             t0 = time.perf_counter()
             for s_ in range(steps):
                 hb.copy_(xs[s_])
-                graph.replay()
+                if mode == "graph":
+                    graph.replay()
+                else:
+                    cs.step(hb)
             torch.cuda.synchronize()
             el_p = time.perf_counter() - t0
             ps = cs.cache.stats()
-            del graph
+            if mode == "graph":
+                del graph
             cs.close()
-            leg[f"prefetch_{depth}_graph"] = {
+            leg[f"prefetch_{depth}_{mode}"] = {
                 "tokens_per_s": round(steps / el_p, 2),
                 "lookups": ps["lookups"], "misses": ps["misses"],
                 "misses_per_token": round(ps["misses"] / steps, 2),
@@ -323,7 +328,7 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
     return {"workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
                         f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
                         f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
-                        f"copies on the device, eager and as a captured HIP graph; prefetch_D_graph: the device LRU graph with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
+                        f"copies on the device, eager and as a captured HIP graph; prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
                         f"sharing the pool, one N-token batch per step (device LRU, graph; hit rate over the "
                         f"step's distinct experts per layer)",
             "legs": legs}
