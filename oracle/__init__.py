@@ -117,7 +117,9 @@ def qmatvec(qtype: int, w: np.ndarray, n: int, k: int, x: np.ndarray) -> np.ndar
 
 
 def rmsnorm(h: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
-    h = _c(h, np.float32)
+    """Weightless RMSNorm of the state as given (fp64; an fp32 state is
+    passed exactly)."""
+    h = _c(h, np.float64)
     out = np.empty(h.shape, np.float64)
     for t in range(h.shape[0]) if h.ndim == 2 else [None]:
         src = h[t] if t is not None else h
@@ -301,10 +303,10 @@ class LayerOut:
 
 
 def moe_layer_token(lw: LayerWeights, h: np.ndarray, keep: bool = False) -> LayerOut:
-    """One pre-norm residual MoE layer on one token.  h is the fp32-valued
-    residual state (fp64 array of fp32-representable values or fp32)."""
-    h32 = np.asarray(h, np.float32)
-    xhat = rmsnorm(h32)
+    """One pre-norm residual MoE layer on one token.  h is the residual
+    state, normalised and added to exactly as given (stack_token rounds it
+    to fp32 between layers, the state's storage type)."""
+    xhat = rmsnorm(np.asarray(h, np.float64))
     r = route(xhat[None, :], lw.router, lw.bias, lw.k)
     y = np.zeros(lw.H, np.float64)
     per = {}

@@ -197,14 +197,14 @@ int orc_qmatvec(int qtype, const uint8_t *w, int n, int k, const double *x, doub
 /* Layer-stack normalisation.  The pages give no composition for a stack of
  * MoE layers; the reading used here is a pre-norm residual block with a
  * weightless RMSNorm:  xhat = h / sqrt(mean(h^2) + eps). */
-void orc_rmsnorm(const float *h, int n, double eps, double *out)
+void orc_rmsnorm(const double *h, int n, double eps, double *out)
 {
     double ss = 0.0;
     for (int i = 0; i < n; i++)
-        ss += (double)h[i] * (double)h[i];
+        ss += h[i] * h[i];
     double r = 1.0 / sqrt(ss / n + eps);
     for (int i = 0; i < n; i++)
-        out[i] = (double)h[i] * r;
+        out[i] = h[i] * r;
 }
 
 /* Router for one token: logits, top-k ids ordered by (logit desc, id asc),

@@ -324,6 +324,77 @@ def test_shared_experts_are_added_with_weight_one():
     assert np.allclose(out.y, y, rtol=1e-13)
 
 
+# ---------------------------------------------------------------- layer stack
+def _dense_layer(cfg, layer, h):
+    """One pre-norm residual MoE layer written out densely in numpy from the
+    dequantized matrices (dequant_matrix is pinned above by hand-packed
+    blocks): RMSNorm, logits, top-k by a stable argsort, softmax over the
+    winners, SiLU(gate)*up, down, weighted sum, residual add."""
+    h = np.asarray(h, np.float64)
+    x = h / np.sqrt(np.mean(h * h) + oracle.RMS_EPS)
+    wr = W.router(cfg, layer).astype(np.float64)
+    b = W.zipf_bias(cfg, layer)
+    lg = wr @ x + (0.0 if b is None else b.astype(np.float64))
+    order = np.argsort(-lg, kind="stable")[:cfg.k]
+    p = np.exp(lg[order] - lg[order].max())
+    p /= p.sum()
+    qg, qu, qd = cfg.qtypes(layer)
+    y = np.zeros(cfg.H)
+    for wj, e in zip(p, order):
+        ex = W.expert(cfg, layer, int(e))
+        g = oracle.dequant_matrix(qg, ex.gate, cfg.I, cfg.H) @ x
+        u = oracle.dequant_matrix(qu, ex.up, cfg.I, cfg.H) @ x
+        a = np.zeros(cfg.down_k(layer))
+        a[:cfg.I] = g / (1 + np.exp(-g)) * u
+        y += wj * (oracle.dequant_matrix(qd, ex.down, cfg.H, cfg.down_k(layer)) @ a)
+    return sorted(int(e) for e in order), h + y
+
+
+def test_stack_token_chains_h_next_with_fp32_rounding():
+    """Two layers composed by hand from the dense definition: layer 1 must
+    see layer 0's h_next (state plus MoE output, not the MoE output alone),
+    rounded to fp32 between the layers; with the rounding switched off the
+    chain must follow the unrounded state instead, and the two differ."""
+    cfg = W.MoEConfig("pin2", 2, 256, 6, 2, 64, ((W.Q4_K, W.Q4_K, W.Q4_K), (W.Q6_K, W.Q6_K, W.Q8_0)),
+                      zipf_s=1.1, seed=33)
+    lw = [_layer(cfg, l) for l in range(2)]
+    h0 = W.token(cfg, 0, 0)
+    ids0, h1 = _dense_layer(cfg, 0, h0)
+    h1r = h1.astype(np.float32).astype(np.float64)
+    assert not np.array_equal(h1r, h1)  # the rounding is visible at this state
+    ids1r, h2r = _dense_layer(cfg, 1, h1r)
+    ids1u, h2u = _dense_layer(cfg, 1, h1)
+    outs = oracle.stack_token(lw, h0)
+    assert sorted(outs[0].route.idx[0].tolist()) == ids0
+    assert np.allclose(outs[0].h_next, h1, rtol=1e-12, atol=0)
+    assert sorted(outs[1].route.idx[0].tolist()) == ids1r
+    assert np.allclose(outs[1].xhat, h1r / np.sqrt(np.mean(h1r * h1r) + oracle.RMS_EPS), rtol=1e-13, atol=0)
+    assert np.allclose(outs[1].h_next, h2r, rtol=1e-12, atol=0)
+    outs_u = oracle.stack_token(lw, h0, round_state_to_fp32=False)
+    assert sorted(outs_u[1].route.idx[0].tolist()) == ids1u
+    assert np.allclose(outs_u[1].h_next, h2u, rtol=1e-12, atol=0)
+    # the rounded and unrounded chains part by far more than the 1e-12 bars above
+    assert np.max(np.abs(outs_u[1].xhat - outs[1].xhat)) > 1e-9 * np.max(np.abs(outs[1].xhat))
+
+
+@pytest.mark.parametrize("a,b,want", [
+    ([1.0, 0.0], [2.0, 0.0], 0.5),                      # the reference's norm is the denominator
+    ([2.0, 0.0], [1.0, 0.0], 1.0),
+    ([0.0, 5.0], [3.0, 4.0], math.sqrt(10.0) / 5.0),    # ||(-3, 1)|| / 5
+    ([[1.0, 0.0], [0.0, 0.0]], [[0.0, 0.0], [0.0, 2.0]], math.sqrt(5.0) / 2.0),  # whole array, not per row
+    ([3.0, 4.0], [0.0, 0.0], 5.0),                      # zero reference: the absolute norm
+    ([1.0, -2.0, 2.0], [1.0, -2.0, 2.0], 0.0),
+])
+def test_rel_l2_closed_forms(a, b, want):
+    assert math.isclose(oracle.rel_l2(np.array(a), np.array(b)), want, rel_tol=1e-15, abs_tol=0.0)
+
+
+def test_rel_l2_scale_invariant_and_relative():
+    b = np.random.default_rng(5).standard_normal(1000)
+    assert math.isclose(oracle.rel_l2(b * (1 + 1e-3), b), 1e-3, rel_tol=1e-9)
+    assert math.isclose(oracle.rel_l2(1e6 * b * (1 - 2e-4), 1e6 * b), 2e-4, rel_tol=1e-9)
+
+
 # ---------------------------------------------------------------- grouping
 def test_group_brute_force():
     rng = np.random.default_rng(2)
