@@ -236,45 +236,97 @@ moe_status moe_cache_plan(const moe_expert_desc *groups, const int32_t *layers_p
 typedef struct moe_cache moe_cache;
 
 /* Create a cache.
- *   groups [n_groups], slots [n_groups] (all >= 1; a disabled group is
- *   refused with MOE_ERR_BUDGET because this library has no host fallback
- *   for its experts), layer_group [n_layers] (group of each layer),
- *   host_experts [n_layers * E] pinned host addresses of each expert in the
- *   slot layout (the pinned memory stays owned by the caller and must
- *   outlive the cache).  Allocates one device pool per group (hipMalloc) and
- *   one device pointer table per layer. */
+ *   groups [n_groups], slots [n_groups] as moe_cache_plan gives them.  A
+ *   group with 0 slots is below the budget floor and is not cached: its
+ *   layers keep all of their experts resident in HBM (uploaded here, once),
+ *   their lookups are answered without touching any pool and count in no
+ *   statistic, and a warning goes to stderr and to moe_last_error() (the
+ *   T4 MoE-cache report, section "Size your experts before configuring":
+ *   a group below the floor is left out with a warning; only a budget that
+ *   disables every group is refused).  MOE_ERR_BUDGET when every group has 0
+ *   slots, MOE_ERR_ARG for a negative count.
+ *   layer_group [n_layers] (group of each layer), host_experts [n_layers * E]
+ *   pinned host addresses of each expert in the slot layout (the pinned
+ *   memory stays owned by the caller and must outlive the cache).  Allocates
+ *   one device pool per group (hipMalloc) and one device pointer table per
+ *   layer. */
 moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
                             const int32_t *layer_group, int32_t n_layers, int32_t E,
                             const void *const *host_experts, moe_cache **out);
 
-/* Look up the distinct experts of one layer-step (host int32 [n], strictly
- * ascending ids in [0, E)).  T is the batch size of the step (for the
- * per-batch-size hit statistics).  Updates the LRU state and records the
- * misses for the next moe_cache_upload of this layer.  Per expert: slot_out
- * (host int32 [n]), hit_out (host uint8 [n]), victim_layer/victim_expert
- * (host int32 [n], -1 when nothing was evicted; either may be NULL).
- * Returns MOE_ERR_CAPACITY when n exceeds the group's slots and
- * MOE_ERR_BATCH when T > 32 (state unchanged in both cases). */
-moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, const int32_t *experts, int32_t n,
-                            int32_t *slot_out, uint8_t *hit_out, int32_t *victim_layer,
-                            int32_t *victim_expert);
+/* Where a cache keeps its pools and how it fills them.  The default
+ * (moe_cache_create) is hipMalloc'd HBM and hipMemcpyAsync from pinned host
+ * memory on the caller's copy stream.  A caller-supplied backend is
+ * synchronous: alloc returns memory for the pools and the slot tables,
+ * copy must have read src and written dst when it returns, and a non-zero
+ * return from copy is an upload failure (moe_cache_upload then rolls the
+ * lookup back, see there).  Such a cache runs the host LRU only (no
+ * moe_cache_device_enable), makes no HIP call, and serves hit-rate
+ * simulation of a budget without a GPU and the failure tests of the LRU. */
+typedef struct {
+    void *user;
+    int32_t (*alloc)(void *user, size_t bytes, void **out); /* 0 on success */
+    void (*release)(void *user, void *p);
+    int32_t (*copy)(void *user, void *dst, const void *src, size_t bytes); /* 0 on success */
+} moe_cache_backend;
 
-/* Enqueue the misses recorded by the last lookup of `layer` as
- * hipMemcpyAsync host->device copies on copy_stream, then record `done` (may
- * be NULL) on copy_stream.  The compute stream waits on `done` before the
- * FFN reads the slots.  The layer's device pointer table is also refreshed
- * on copy_stream. */
+/* moe_cache_create with an explicit backend (NULL: the default). */
+moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
+                               const int32_t *layer_group, int32_t n_layers, int32_t E,
+                               const void *const *host_experts, const moe_cache_backend *backend,
+                               moe_cache **out);
+
+/* Look up one layer-step (T4 MoE-cache report, section "What the MoE cache
+ * caches": LRU over (layer, expert) keys in the group's pool).
+ *   idx        host int32 [T*k], the selected ids of the step's T tokens,
+ *              each in [0, E); repeats allowed
+ * The step's distinct ids are looked up once each in ascending order; they
+ * go to experts_out (host int32 [T*k]), their number to *n_out.  Per
+ * distinct expert: slot_out (host int32 [T*k]), hit_out (host uint8 [T*k]),
+ * victim_layer / victim_expert (host int32 [T*k], -1 when nothing was
+ * evicted; either may be NULL).  A hit refreshes the expert's recency; a
+ * miss takes the group's next never-used slot, else evicts the least
+ * recently used key of the group, whose entry in its layer's slot table
+ * becomes NULL (the cleared rows reach the device with the next
+ * moe_cache_upload).  The misses are recorded for the next moe_cache_upload
+ * of this layer.  For a layer of a group with 0 slots (resident, see
+ * moe_cache_create) every expert is reported as a hit in slot -1 and nothing
+ * is recorded.  Returns MOE_ERR_CAPACITY when the distinct ids exceed the
+ * group's slots and MOE_ERR_BATCH when T > 32 (state unchanged in both
+ * cases). */
+moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, int32_t k, const int32_t *idx,
+                            int32_t *experts_out, int32_t *n_out, int32_t *slot_out, uint8_t *hit_out,
+                            int32_t *victim_layer, int32_t *victim_expert);
+
+/* Enqueue the misses recorded by the last lookup of `layer` as copies from
+ * pinned host memory into their slots (hipMemcpyAsync on copy_stream), then
+ * the slot-table rows that changed since their last upload (this layer's
+ * and those of evicted keys), then record `done` (may be NULL; must be NULL
+ * with a caller-supplied backend, which ignores copy_stream) on copy_stream.
+ * The compute stream waits on `done` before the FFN reads the slots.  If a
+ * copy cannot be enqueued (or a backend's copy fails), the lookup is rolled
+ * back from that miss on: the misses already enqueued stay (their slots are
+ * being filled), and the rest of the lookup's decisions are undone in
+ * reverse order (keys, recency order, free-slot count, evicted keys put back
+ * in their untouched slots, table entries, statistics), as if the lookup had
+ * stopped before that miss; MOE_ERR_HIP is returned and the layer may be
+ * looked up again. */
 moe_status moe_cache_upload(moe_cache *c, int32_t layer, hipStream_t copy_stream, hipEvent_t done);
 
-/* Device array [E] of slot addresses of `layer` (entries of experts not
- * resident are NULL).  The array is owned by the cache and is valid after
- * the upload of the layer completes.  Pass it as expert_ptrs. */
+/* Device array [E] of slot addresses of `layer` (NULL for experts that are
+ * not resident: never looked up, or evicted).  The array is owned by the
+ * cache and is valid after the upload of the layer completes (with the
+ * device lookup: after moe_cache_lookup_device).  Pass it as expert_ptrs. */
 const void *const *moe_cache_expert_ptrs(moe_cache *c, int32_t layer);
 
 typedef struct {
     uint64_t lookups, hits, misses, evictions, upload_bytes;
     uint64_t lookups_le8, hits_le8;     /* steps with T <= 8 */
     uint64_t lookups_9_32, hits_9_32;   /* steps with 9 <= T <= 32 */
+    /* batches above 32 tokens (moe_cache_stage_large): experts copied from
+     * their slots into the caller's staging area, and experts uploaded there
+     * from host memory because no slot held them */
+    uint64_t large_copies, large_uploads;
 } moe_cache_stats_t;
 
 moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out);

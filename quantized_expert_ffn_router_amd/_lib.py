@@ -16,7 +16,7 @@ EXPORTED = [
     "moe_last_error", "moe_expert_bytes", "moe_down_k", "moe_repack_expert",
     "moe_rmsnorm", "moe_route_topk", "moe_group_tokens", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
-    "moe_cache_plan", "moe_cache_create", "moe_cache_lookup", "moe_cache_upload",
+    "moe_cache_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
     "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_prefetch_device", "moe_cache_trace_read",
 ]
@@ -45,10 +45,41 @@ class ExpertDesc(ctypes.Structure):
 class CacheStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "lookups", "hits", "misses", "evictions", "upload_bytes",
-        "lookups_le8", "hits_le8", "lookups_9_32", "hits_9_32")]
+        "lookups_le8", "hits_le8", "lookups_9_32", "hits_9_32", "large_copies", "large_uploads")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+BackendAlloc = ctypes.CFUNCTYPE(ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p))
+BackendRelease = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p)
+BackendCopy = ctypes.CFUNCTYPE(ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t)
+
+
+class CacheBackend(ctypes.Structure):
+    """moe_cache_backend: a synchronous pool allocator and copier (see moe.h)."""
+    _fields_ = [("user", ctypes.c_void_p), ("alloc", BackendAlloc), ("release", BackendRelease),
+                ("copy", BackendCopy)]
+
+    @classmethod
+    def of(cls, alloc, release, copy) -> "CacheBackend":
+        """Python callables alloc(nbytes) -> address (0 on failure), release(address),
+        copy(dst, src, nbytes) -> 0 on success.  The returned structure keeps the
+        ctypes thunks alive; keep it alive as long as the cache."""
+        def _alloc(_u, n, out):
+            a = int(alloc(int(n)) or 0)
+            out[0] = a
+            return 0 if a else 1
+
+        def _release(_u, p):
+            release(int(p or 0))
+
+        def _copy(_u, dst, src, n):
+            return int(copy(int(dst or 0), int(src or 0), int(n)))
+
+        b = cls(None, BackendAlloc(_alloc), BackendRelease(_release), BackendCopy(_copy))
+        b._keep = (_alloc, _release, _copy)
+        return b
 
 
 _lib = None
@@ -84,7 +115,8 @@ def lib() -> ctypes.CDLL:
         "moe_layer_forward": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_cache_plan": (i32, [D, P, i32, u64, i32, P]),
         "moe_cache_create": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(P)]),
-        "moe_cache_lookup": (i32, [P, i32, i32, P, i32, P, P, P, P]),
+        "moe_cache_create_ex": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(CacheBackend), ctypes.POINTER(P)]),
+        "moe_cache_lookup": (i32, [P, i32, i32, i32, P, P, P, P, P, P, P]),
         "moe_cache_upload": (i32, [P, i32, P, P]),
         "moe_cache_expert_ptrs": (P, [P, i32]),
         "moe_cache_stats": (i32, [P, ctypes.POINTER(CacheStats)]),
@@ -229,36 +261,52 @@ def moe_cache_plan(descs: Sequence, layers_per_group: Sequence[int], budget_byte
 
 
 class Cache:
-    """Owner of a moe_cache* (moe_cache_create / moe_cache_destroy)."""
+    """Owner of a moe_cache* (moe_cache_create / moe_cache_create_ex / moe_cache_destroy)."""
 
     def __init__(self, descs: Sequence, slots: Sequence[int], layer_group: Sequence[int], E: int,
-                 host_expert_ptrs: Sequence[int]):
+                 host_expert_ptrs: Sequence[int], backend: Optional[CacheBackend] = None):
         n = len(descs)
         self._descs = (ExpertDesc * n)(*[_desc(d) for d in descs])
         self._slots = np.asarray(slots, np.int32)
         self._lg = np.asarray(layer_group, np.int32)
         self._hp = np.asarray(host_expert_ptrs, np.uint64)
+        self._backend = backend
         self.n_layers = len(self._lg)
         self.E = E
         h = ctypes.c_void_p()
-        _check(lib().moe_cache_create(self._descs, n, self._slots.ctypes.data, self._lg.ctypes.data,
-                                      self.n_layers, E, self._hp.ctypes.data, ctypes.byref(h)))
+        self.h = None
+        if backend is None:
+            st = lib().moe_cache_create(self._descs, n, self._slots.ctypes.data, self._lg.ctypes.data,
+                                        self.n_layers, E, self._hp.ctypes.data, ctypes.byref(h))
+        else:
+            st = lib().moe_cache_create_ex(self._descs, n, self._slots.ctypes.data, self._lg.ctypes.data,
+                                           self.n_layers, E, self._hp.ctypes.data, ctypes.byref(backend),
+                                           ctypes.byref(h))
+        _check(st)
         self.h = h
 
-    def lookup(self, layer: int, T: int, experts: np.ndarray):
-        ex = np.ascontiguousarray(experts, np.int32)
-        n = ex.shape[0]
-        slot = np.empty(n, np.int32)
-        hit = np.empty(n, np.uint8)
-        vl = np.empty(n, np.int32)
-        ve = np.empty(n, np.int32)
-        _check(lib().moe_cache_lookup(self.h, layer, T, ex.ctypes.data, n, slot.ctypes.data, hit.ctypes.data,
-                                      vl.ctypes.data, ve.ctypes.data))
-        return slot, hit, vl, ve
+    def lookup(self, layer: int, T: int, k: int, idx: np.ndarray):
+        """Host LRU lookup of one layer-step from its raw selected ids (host
+        int32 [T*k]).  Returns (experts, slot, hit, victim_layer,
+        victim_expert) over the step's distinct experts, ascending."""
+        ids = np.ascontiguousarray(np.asarray(idx).reshape(-1)[:T * k], np.int32)
+        if ids.shape[0] != T * k:
+            raise ValueError("idx must hold T*k ids")
+        ex = np.empty(T * k, np.int32)
+        n = ctypes.c_int32()
+        slot = np.empty(T * k, np.int32)
+        hit = np.empty(T * k, np.uint8)
+        vl = np.empty(T * k, np.int32)
+        ve = np.empty(T * k, np.int32)
+        _check(lib().moe_cache_lookup(self.h, layer, T, k, ids.ctypes.data, ex.ctypes.data, ctypes.byref(n),
+                                      slot.ctypes.data, hit.ctypes.data, vl.ctypes.data, ve.ctypes.data))
+        m = n.value
+        return ex[:m], slot[:m], hit[:m], vl[:m], ve[:m]
 
     def upload(self, layer: int, copy_stream, done_event=None):
         ev = None if done_event is None else done_event.cuda_event if hasattr(done_event, "cuda_event") else done_event
-        _check(lib().moe_cache_upload(self.h, layer, _stream(copy_stream), ev))
+        cs = None if (copy_stream is None and self._backend is not None) else _stream(copy_stream)
+        _check(lib().moe_cache_upload(self.h, layer, cs, ev))
 
     def enable_device(self, trace_capacity: int = 0):
         """Move the LRU state to the device (moe_cache_device_enable)."""

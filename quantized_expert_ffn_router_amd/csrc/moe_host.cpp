@@ -15,6 +15,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -147,24 +148,38 @@ struct moe_cache {
     struct Group {
         moe_expert_desc desc;
         size_t slot_bytes = 0;
-        int n_slots = 0;
-        uint8_t *pool = nullptr;
+        int n_slots = 0;                // 0: below the budget floor, its layers resident
+        uint8_t *pool = nullptr;        // the slots; a resident group: its layers' experts, layer-major
         std::vector<int64_t> slot_key;  // key = layer*E + expert, -1 free
         std::vector<int> prev, next;    // recency list over slots, head = most recent
         int head = -1, tail = -1, next_free = 0;
     };
+    // One decision of a host lookup, kept until the layer's upload so that a
+    // failed upload can undo the lookup from a miss on (in reverse order).
+    struct Op {
+        int slot, old_prev;   // the slot, and its predecessor in the recency list before the decision
+        int64_t key, victim;  // the key looked up; the key evicted, or -1
+        uint8_t kind;         // 0 hit, 1 miss into a never-used slot, 2 miss with eviction
+    };
+    struct Pending { int slot; const void *src; int op; };
     int n_layers = 0, E = 0, device = 0;
+    bool custom = false;                 // caller-supplied (synchronous) backend
+    moe_cache_backend be{};
     std::vector<Group> groups;
     std::vector<int> layer_group;
+    std::vector<int> layer_rank;         // position of a layer among its group's layers
     std::vector<const void *> host;      // [L*E] pinned sources
     std::vector<int> where;              // [L*E] slot of a key, -1 absent
-    const void **htab = nullptr;         // pinned [L*E] slot addresses
+    const void **htab = nullptr;         // host [L*E] slot addresses (pinned with the default backend)
     void **dtab = nullptr;               // device [L*E]
-    std::vector<hipEvent_t> table_done;  // per layer: last table copy
-    std::vector<char> table_pending;
-    struct Pending { int slot; const void *src; };
-    std::vector<std::vector<Pending>> pending;  // per layer
+    std::vector<hipEvent_t> table_done;  // per layer: last copy of its table row
+    std::vector<char> table_pending;     // that copy may still be reading htab
+    std::vector<char> dirty;             // row changed since its last upload
+    std::vector<std::vector<Pending>> pending;  // per layer: misses of its last lookup
+    std::vector<std::vector<Op>> ops;           // per layer: decisions of its last lookup
+    std::vector<int> lookup_T;
     std::vector<char> looked_up;
+    int open_lookup = -1;                // layer whose lookup awaits its upload, -1 none
     moe_cache_stats_t st{};
     // device-side lookup (moe_cache_device_enable): the LRU state in device
     // memory, one stamp and key per slot per group
@@ -175,7 +190,7 @@ struct moe_cache {
     const void **d_src = nullptr;     // [L*E] device addresses of the host copies
     int32_t *d_counters = nullptr;    // [n_groups] next_free, then clock, njobs, ntrace
     CacheJob *d_jobs = nullptr;       // [E]
-    unsigned long long *d_stats = nullptr;  // 9 counters
+    unsigned long long *d_stats = nullptr;  // moe_cache_stats_t
     int32_t *d_trace = nullptr;
     // prefetch (moe_cache_prefetch_device): per layer a list of miss copies
     // run on the caller's copy stream and the event that ends them, and the
@@ -185,12 +200,17 @@ struct moe_cache {
     hipEvent_t ev_fork = nullptr;
     std::vector<hipEvent_t> ev_pref;  // [L]
     std::vector<int> pend_touch;      // [L]
+    // per group: slot touches since (and including) its latest device lookup,
+    // whose experts the FFN that follows is reading; -1 before the first
+    std::vector<int> recent_touch;
     int trace_cap = 0;
 };
 
 namespace {
 
-void unlink(moe_cache::Group &g, int s)
+using Group = moe_cache::Group;
+
+void unlink(Group &g, int s)
 {
     int p = g.prev[s], n = g.next[s];
     if (p >= 0) g.next[p] = n; else g.head = n;
@@ -198,7 +218,7 @@ void unlink(moe_cache::Group &g, int s)
     g.prev[s] = g.next[s] = -1;
 }
 
-void push_front(moe_cache::Group &g, int s)
+void push_front(Group &g, int s)
 {
     g.prev[s] = -1;
     g.next[s] = g.head;
@@ -207,15 +227,35 @@ void push_front(moe_cache::Group &g, int s)
     if (g.tail < 0) g.tail = s;
 }
 
+// Put s back right after p (p = -1: at the head).
+void insert_after(Group &g, int p, int s)
+{
+    if (p < 0) { push_front(g, s); return; }
+    const int n = g.next[p];
+    g.next[p] = s;
+    g.prev[s] = p;
+    g.next[s] = n;
+    if (n >= 0) g.prev[n] = s; else g.tail = s;
+}
+
+// The default backend: HBM from hipMalloc, copies by hipMemcpyAsync.
+int32_t hip_alloc(void *, size_t bytes, void **out) { return hipMalloc(out, bytes) == hipSuccess ? 0 : 1; }
+void hip_release(void *, void *p) { (void)hipFree(p); }
+
 void destroy(moe_cache *c)
 {
     if (!c) return;
-    (void)hipSetDevice(c->device);
-    (void)hipDeviceSynchronize();
+    if (!c->custom) {
+        (void)hipSetDevice(c->device);
+        (void)hipDeviceSynchronize();
+    }
     for (auto &g : c->groups)
-        if (g.pool) (void)hipFree(g.pool);
-    if (c->dtab) (void)hipFree(c->dtab);
-    if (c->htab) (void)hipHostFree((void *)c->htab);
+        if (g.pool) c->be.release(c->be.user, g.pool);
+    if (c->dtab) c->be.release(c->be.user, c->dtab);
+    if (c->htab) {
+        if (c->custom) free((void *)c->htab);
+        else (void)hipHostFree((void *)c->htab);
+    }
     for (auto ev : c->table_done)
         if (ev) (void)hipEventDestroy(ev);
     for (auto &dg : c->dgroups) {
@@ -230,6 +270,8 @@ void destroy(moe_cache *c)
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     delete c;
 }
+
+bool resident_layer(const moe_cache *c, int layer) { return c->groups[c->layer_group[layer]].n_slots == 0; }
 
 // A prefetch's copies run beside the lookups that follow it.  The slots it
 // filled were touched last by the prefetch, so a later lookup can take one
@@ -271,24 +313,93 @@ CacheDevArgs device_args(moe_cache *c, int layer, const int32_t *idx, int T, int
     return a;
 }
 
+void count_lookup(moe_cache_stats_t &st, int T, bool hit, int sign)
+{
+    const uint64_t d = (uint64_t)(int64_t)sign;  // +1 or -1 (mod 2^64)
+    st.lookups += d;
+    if (T <= 8) st.lookups_le8 += d; else st.lookups_9_32 += d;
+    if (hit) {
+        st.hits += d;
+        if (T <= 8) st.hits_le8 += d; else st.hits_9_32 += d;
+    } else {
+        st.misses += d;
+    }
+}
+
+// Undo one decision of a host lookup.  Called in reverse order over a suffix
+// of the lookup's decisions, with no other lookup since, so the decision's
+// slot is at the head of the recency list.
+void undo_op(moe_cache *c, Group &G, const moe_cache::Op &op, int T)
+{
+    const int s = op.slot;
+    const int64_t E = c->E;
+    unlink(G, s);
+    count_lookup(c->st, T, op.kind == 0, -1);
+    if (op.kind != 0) {
+        c->where[op.key] = -1;
+        c->htab[op.key] = nullptr;
+        c->dirty[op.key / E] = 1;
+        if (op.kind == 1) {  // the never-used slot is free again
+            G.slot_key[s] = -1;
+            G.next_free--;
+            return;
+        }
+        c->st.evictions--;
+        G.slot_key[s] = op.victim;
+        c->where[op.victim] = s;
+        c->htab[op.victim] = G.pool + (size_t)s * G.slot_bytes;
+        c->dirty[op.victim / E] = 1;
+    }
+    insert_after(G, op.old_prev, s);
+}
+
+// Copy one table row to the device (default backend: on `s`, recording the
+// row's event; a custom backend: synchronously).
+moe_status upload_row(moe_cache *c, int r, hipStream_t s)
+{
+    const size_t off = (size_t)r * c->E, bytes = sizeof(void *) * (size_t)c->E;
+    if (c->custom) {
+        if (c->be.copy(c->be.user, c->dtab + off, c->htab + off, bytes) != 0) {
+            set_error("slot table upload of layer %d failed (backend copy)", r);
+            return MOE_ERR_HIP;
+        }
+        c->dirty[r] = 0;
+        return MOE_OK;
+    }
+    hipError_t e = hipMemcpyAsync(c->dtab + off, c->htab + off, bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipEventRecord(c->table_done[r], s);
+    if (e != hipSuccess) { set_error("slot table upload of layer %d failed: %s", r, hipGetErrorString(e)); return MOE_ERR_HIP; }
+    c->table_pending[r] = 1;
+    c->dirty[r] = 0;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
-                            const int32_t *layer_group, int32_t n_layers, int32_t E,
-                            const void *const *host_experts, moe_cache **out)
+moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
+                               const int32_t *layer_group, int32_t n_layers, int32_t E,
+                               const void *const *host_experts, const moe_cache_backend *backend,
+                               moe_cache **out)
 {
     if (!groups || !slots || !layer_group || !host_experts || !out || n_groups < 1 || n_layers < 1 || E < 1) {
         set_error("moe_cache_create: bad argument");
         return MOE_ERR_ARG;
     }
+    if (backend && (!backend->alloc || !backend->release || !backend->copy)) {
+        set_error("moe_cache_create_ex: the backend needs alloc, release and copy");
+        return MOE_ERR_ARG;
+    }
     *out = nullptr;
+    bool any = false;
     for (int g = 0; g < n_groups; g++) {
-        if (slots[g] < 1) {
-            set_error("group %d has no slots (below the budget floor); its experts would have nowhere to run", g);
-            return MOE_ERR_BUDGET;
-        }
+        if (slots[g] < 0) { set_error("group %d: negative slot count %d", g, slots[g]); return MOE_ERR_ARG; }
+        any = any || slots[g] > 0;
+    }
+    if (!any) {
+        set_error("every group has 0 slots (the budget is below the floor of each)");
+        return MOE_ERR_BUDGET;
     }
     for (int l = 0; l < n_layers; l++) {
         if (layer_group[l] < 0 || layer_group[l] >= n_groups) { set_error("layer %d: bad group", l); return MOE_ERR_ARG; }
@@ -299,7 +410,13 @@ moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, con
     moe_cache *c = new moe_cache();
     c->n_layers = n_layers;
     c->E = E;
-    if (hipGetDevice(&c->device) != hipSuccess) { delete c; set_error("hipGetDevice failed"); return MOE_ERR_HIP; }
+    c->custom = backend != nullptr;
+    c->be = backend ? *backend : moe_cache_backend{nullptr, hip_alloc, hip_release, nullptr};
+    if (!c->custom && hipGetDevice(&c->device) != hipSuccess) { delete c; set_error("hipGetDevice failed"); return MOE_ERR_HIP; }
+    c->layer_group.assign(layer_group, layer_group + n_layers);
+    c->layer_rank.assign(n_layers, 0);
+    std::vector<int> per_group(n_groups, 0);
+    for (int l = 0; l < n_layers; l++) c->layer_rank[l] = per_group[layer_group[l]]++;
     c->groups.resize(n_groups);
     for (int g = 0; g < n_groups; g++) {
         ExpertGeom eg;
@@ -311,105 +428,186 @@ moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, con
         G.slot_key.assign(G.n_slots, -1);
         G.prev.assign(G.n_slots, -1);
         G.next.assign(G.n_slots, -1);
-        hipError_t e = hipMalloc((void **)&G.pool, G.slot_bytes * (size_t)G.n_slots);
-        if (e != hipSuccess) {
-            G.pool = nullptr;
+        const size_t n = G.n_slots > 0 ? (size_t)G.n_slots : (size_t)per_group[g] * E;
+        if (n == 0) continue;  // a resident group without layers
+        void *p = nullptr;
+        if (c->be.alloc(c->be.user, G.slot_bytes * n, &p) != 0 || !p) {
             destroy(c);
-            set_error("hipMalloc of %zu bytes for pool %d failed: %s", G.slot_bytes * (size_t)G.n_slots, g,
-                      hipGetErrorString(e));
+            set_error("allocation of %zu bytes for pool %d failed", G.slot_bytes * n, g);
             return MOE_ERR_HIP;
         }
+        G.pool = (uint8_t *)p;
     }
-    c->layer_group.assign(layer_group, layer_group + n_layers);
     c->host.assign(host_experts, host_experts + (size_t)n_layers * E);
     c->where.assign((size_t)n_layers * E, -1);
     size_t tb = sizeof(void *) * (size_t)n_layers * E;
-    if (hipHostMalloc((void **)&c->htab, tb, hipHostMallocDefault) != hipSuccess ||
-        hipMalloc((void **)&c->dtab, tb) != hipSuccess || hipMemset(c->dtab, 0, tb) != hipSuccess) {
+    void *dt = nullptr;
+    bool ok = c->be.alloc(c->be.user, tb, &dt) == 0 && dt;
+    c->dtab = (void **)dt;
+    if (ok) {
+        if (c->custom) ok = (c->htab = (const void **)calloc((size_t)n_layers * E, sizeof(void *))) != nullptr;
+        else ok = hipHostMalloc((void **)&c->htab, tb, hipHostMallocDefault) == hipSuccess;
+    }
+    if (!ok) {
         destroy(c);
         set_error("allocation of the slot tables failed");
         return MOE_ERR_HIP;
     }
     memset((void *)c->htab, 0, tb);
-    c->table_done.assign(n_layers, nullptr);
-    for (int l = 0; l < n_layers; l++) {
-        if (hipEventCreateWithFlags(&c->table_done[l], hipEventDisableTiming) != hipSuccess) {
-            destroy(c);
-            set_error("hipEventCreate failed");
-            return MOE_ERR_HIP;
+    if (!c->custom) {
+        c->table_done.assign(n_layers, nullptr);
+        for (int l = 0; l < n_layers; l++) {
+            if (hipEventCreateWithFlags(&c->table_done[l], hipEventDisableTiming) != hipSuccess) {
+                destroy(c);
+                set_error("hipEventCreate failed");
+                return MOE_ERR_HIP;
+            }
         }
     }
     c->table_pending.assign(n_layers, 0);
+    c->dirty.assign(n_layers, 1);  // every row goes up once (resident rows are final)
     c->pending.assign(n_layers, {});
+    c->ops.assign(n_layers, {});
+    c->lookup_T.assign(n_layers, 0);
     c->looked_up.assign(n_layers, 0);
+    // groups below the floor: their layers' experts resident, uploaded once
+    int n_res = 0;
+    size_t res_bytes = 0;
+    for (int l = 0; l < n_layers; l++) {
+        auto &G = c->groups[layer_group[l]];
+        if (G.n_slots > 0) continue;
+        n_res++;
+        for (int e = 0; e < E; e++) {
+            uint8_t *dst = G.pool + ((size_t)c->layer_rank[l] * E + e) * G.slot_bytes;
+            const void *src = c->host[(size_t)l * E + e];
+            const bool cp = c->custom ? c->be.copy(c->be.user, dst, src, G.slot_bytes) == 0
+                                      : hipMemcpy(dst, src, G.slot_bytes, hipMemcpyHostToDevice) == hipSuccess;
+            if (!cp) { destroy(c); set_error("upload of resident expert (%d, %d) failed", l, e); return MOE_ERR_HIP; }
+            c->htab[(size_t)l * E + e] = dst;
+            res_bytes += G.slot_bytes;
+        }
+    }
+    for (int l = 0; l < n_layers; l++) {
+        const size_t off = (size_t)l * E;
+        const bool cp = c->custom ? c->be.copy(c->be.user, c->dtab + off, c->htab + off, sizeof(void *) * (size_t)E) == 0
+                                  : hipMemcpy(c->dtab + off, c->htab + off, sizeof(void *) * (size_t)E,
+                                              hipMemcpyHostToDevice) == hipSuccess;
+        if (!cp) { destroy(c); set_error("upload of the slot tables failed"); return MOE_ERR_HIP; }
+        c->dirty[l] = 0;
+    }
+    if (n_res) {
+        char msg[256];
+        snprintf(msg, sizeof msg,
+                 "moe cache: %d of %d layers belong to groups below the budget floor; their experts stay resident "
+                 "(%zu bytes) and are not cached", n_res, n_layers, res_bytes);
+        fprintf(stderr, "%s\n", msg);
+        set_error("%s", msg);
+    }
     *out = c;
     return MOE_OK;
 }
 
-moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, const int32_t *experts, int32_t n,
-                            int32_t *slot_out, uint8_t *hit_out, int32_t *victim_layer, int32_t *victim_expert)
+moe_status moe_cache_create(const moe_expert_desc *groups, int32_t n_groups, const int32_t *slots,
+                            const int32_t *layer_group, int32_t n_layers, int32_t E,
+                            const void *const *host_experts, moe_cache **out)
 {
-    if (!c || !experts || !slot_out || !hit_out || n < 0 || layer < 0 || layer >= c->n_layers) {
+    return moe_cache_create_ex(groups, n_groups, slots, layer_group, n_layers, E, host_experts, nullptr, out);
+}
+
+moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, int32_t k, const int32_t *idx,
+                            int32_t *experts_out, int32_t *n_out, int32_t *slot_out, uint8_t *hit_out,
+                            int32_t *victim_layer, int32_t *victim_expert)
+{
+    if (!c || !idx || !experts_out || !n_out || !slot_out || !hit_out || k < 1 || layer < 0 || layer >= c->n_layers) {
         set_error("moe_cache_lookup: bad argument");
         return MOE_ERR_ARG;
     }
     if (c->dev) { set_error("moe_cache_lookup: the cache looks up on the device (moe_cache_lookup_device)"); return MOE_ERR_STATE; }
-    if (T < 1 || T > kMaxT) { set_error("moe_cache_lookup: T=%d outside [1, 32]; larger batches bypass the cache", T); return MOE_ERR_BATCH; }
-    for (int i = 0; i < n; i++) {
-        if (experts[i] < 0 || experts[i] >= c->E || (i > 0 && experts[i] <= experts[i - 1])) {
-            set_error("moe_cache_lookup: experts must be distinct, ascending and in [0, %d)", c->E);
-            return MOE_ERR_ARG;
-        }
+    if (T < 1 || T > kMaxT) { set_error("moe_cache_lookup: T=%d outside [1, 32]; larger batches bypass the slots", T); return MOE_ERR_BATCH; }
+    const int64_t E = c->E;
+    std::vector<char> sel((size_t)E, 0);
+    for (int p = 0; p < T * k; p++) {
+        if (idx[p] < 0 || idx[p] >= E) { set_error("moe_cache_lookup: id %d outside [0, %d)", idx[p], (int)E); return MOE_ERR_ARG; }
+        sel[idx[p]] = 1;
     }
+    int n = 0;
+    for (int e = 0; e < E; e++)
+        if (sel[e]) experts_out[n++] = e;
+    *n_out = n;
     auto &G = c->groups[c->layer_group[layer]];
+    if (G.n_slots == 0) {  // resident layer
+        for (int i = 0; i < n; i++) {
+            slot_out[i] = -1;
+            hit_out[i] = 1;
+            if (victim_layer) victim_layer[i] = -1;
+            if (victim_expert) victim_expert[i] = -1;
+        }
+        return MOE_OK;
+    }
     if (n > G.n_slots) {
         set_error("moe_cache_lookup: %d distinct experts exceed the %d slots of the group", n, G.n_slots);
         return MOE_ERR_CAPACITY;
     }
-    if (c->pending[layer].size()) { set_error("moe_cache_lookup: previous misses of layer %d not uploaded", layer); return MOE_ERR_STATE; }
-    // the previous table copy of this layer must have read the pinned table
-    if (c->table_pending[layer]) {
-        if (hipEventSynchronize(c->table_done[layer]) != hipSuccess) { set_error("hipEventSynchronize failed"); return MOE_ERR_HIP; }
-        c->table_pending[layer] = 0;
+    if (c->open_lookup >= 0) {
+        set_error("moe_cache_lookup: the lookup of layer %d has not been uploaded", c->open_lookup);
+        return MOE_ERR_STATE;
     }
-    const int64_t E = c->E;
-    for (int i = 0; i < n; i++) {
-        const int64_t key = layer * E + experts[i];
-        int s = c->where[key];
-        int vl = -1, ve = -1;
-        c->st.lookups++;
-        if (T <= 8) c->st.lookups_le8++; else c->st.lookups_9_32++;
-        if (s >= 0) {
-            hit_out[i] = 1;
-            c->st.hits++;
-            if (T <= 8) c->st.hits_le8++; else c->st.hits_9_32++;
-            unlink(G, s);
-            push_front(G, s);
-        } else {
-            hit_out[i] = 0;
-            c->st.misses++;
-            if (G.next_free < G.n_slots) {
-                s = G.next_free++;
-            } else {
-                s = G.tail;
-                const int64_t vk = G.slot_key[s];
-                vl = (int)(vk / E);
-                ve = (int)(vk % E);
-                c->where[vk] = -1;
-                unlink(G, s);
-                c->st.evictions++;
+    // table rows of this group still being copied must be read before this
+    // lookup rewrites them (in the usual flow they finished long ago)
+    if (!c->custom)
+        for (int l = 0; l < c->n_layers; l++)
+            if (c->table_pending[l] && c->layer_group[l] == c->layer_group[layer]) {
+                if (hipEventSynchronize(c->table_done[l]) != hipSuccess) { set_error("hipEventSynchronize failed"); return MOE_ERR_HIP; }
+                c->table_pending[l] = 0;
             }
+    auto &ops = c->ops[layer];
+    auto &pend = c->pending[layer];
+    ops.clear();
+    pend.clear();
+    for (int i = 0; i < n; i++) {
+        const int64_t key = layer * E + experts_out[i];
+        int s = c->where[key];
+        moe_cache::Op op{};
+        op.key = key;
+        op.victim = -1;
+        if (s >= 0) {
+            op.kind = 0;
+            op.old_prev = G.prev[s];
+            unlink(G, s);
+        } else if (G.next_free < G.n_slots) {
+            op.kind = 1;
+            op.old_prev = -1;
+            s = G.next_free++;
+        } else {
+            op.kind = 2;
+            s = G.tail;
+            op.old_prev = G.prev[s];
+            op.victim = G.slot_key[s];
+            c->where[op.victim] = -1;
+            c->htab[op.victim] = nullptr;  // the evicted expert is no longer resident
+            c->dirty[op.victim / E] = 1;
+            unlink(G, s);
+            c->st.evictions++;
+        }
+        op.slot = s;
+        count_lookup(c->st, T, op.kind == 0, +1);
+        if (op.kind != 0) {
             G.slot_key[s] = key;
             c->where[key] = s;
-            push_front(G, s);
-            c->pending[layer].push_back({s, c->host[key]});
+            c->htab[key] = G.pool + (size_t)s * G.slot_bytes;
+            c->dirty[layer] = 1;
+            pend.push_back({s, c->host[key], (int)ops.size()});
         }
-        c->htab[key] = G.pool + (size_t)s * G.slot_bytes;
+        push_front(G, s);
+        ops.push_back(op);
         slot_out[i] = s;
-        if (victim_layer) victim_layer[i] = vl;
-        if (victim_expert) victim_expert[i] = ve;
+        hit_out[i] = op.kind == 0;
+        if (victim_layer) victim_layer[i] = op.victim >= 0 ? (int)(op.victim / E) : -1;
+        if (victim_expert) victim_expert[i] = op.victim >= 0 ? (int)(op.victim % E) : -1;
     }
+    c->lookup_T[layer] = T;
     c->looked_up[layer] = 1;
+    c->open_lookup = layer;
     return MOE_OK;
 }
 
@@ -417,23 +615,49 @@ moe_status moe_cache_upload(moe_cache *c, int32_t layer, hipStream_t copy_stream
 {
     if (!c || layer < 0 || layer >= c->n_layers) { set_error("moe_cache_upload: bad argument"); return MOE_ERR_ARG; }
     if (c->dev) { set_error("moe_cache_upload: the cache looks up on the device (moe_cache_lookup_device)"); return MOE_ERR_STATE; }
+    if (c->custom && done) { set_error("moe_cache_upload: a backend cache has no events (done must be NULL)"); return MOE_ERR_ARG; }
+    if (resident_layer(c, layer)) {
+        if (done && hipEventRecord(done, copy_stream) != hipSuccess) { set_error("hipEventRecord failed"); return MOE_ERR_HIP; }
+        return MOE_OK;
+    }
     if (!c->looked_up[layer]) { set_error("moe_cache_upload: layer %d has no lookup", layer); return MOE_ERR_STATE; }
     auto &G = c->groups[c->layer_group[layer]];
-    for (const auto &p : c->pending[layer]) {
-        hipError_t e = hipMemcpyAsync(G.pool + (size_t)p.slot * G.slot_bytes, p.src, G.slot_bytes,
-                                      hipMemcpyHostToDevice, copy_stream);
-        if (e != hipSuccess) { set_error("expert upload failed: %s", hipGetErrorString(e)); return MOE_ERR_HIP; }
+    auto &pend = c->pending[layer];
+    for (size_t j = 0; j < pend.size(); j++) {
+        uint8_t *dst = G.pool + (size_t)pend[j].slot * G.slot_bytes;
+        bool ok;
+        char why[160] = "";
+        if (c->custom) {
+            ok = c->be.copy(c->be.user, dst, pend[j].src, G.slot_bytes) == 0;
+            if (!ok) snprintf(why, sizeof why, "the backend's copy failed");
+        } else {
+            hipError_t e = hipMemcpyAsync(dst, pend[j].src, G.slot_bytes, hipMemcpyHostToDevice, copy_stream);
+            ok = e == hipSuccess;
+            if (!ok) snprintf(why, sizeof why, "%s", hipGetErrorString(e));
+        }
+        if (!ok) {
+            // undo the lookup from this miss on, newest decision first
+            auto &ops = c->ops[layer];
+            const int from = pend[j].op;
+            for (int o = (int)ops.size() - 1; o >= from; o--) undo_op(c, G, ops[o], c->lookup_T[layer]);
+            ops.resize(from);
+            pend.clear();
+            c->looked_up[layer] = 0;
+            c->open_lookup = -1;
+            set_error("expert upload %zu of layer %d failed (%s); the lookup was rolled back to its first %d decisions",
+                      j, layer, why, from);
+            return MOE_ERR_HIP;
+        }
         c->st.upload_bytes += G.slot_bytes;
     }
-    c->pending[layer].clear();
-    const size_t off = (size_t)layer * c->E;
-    hipError_t e = hipMemcpyAsync(c->dtab + off, c->htab + off, sizeof(void *) * (size_t)c->E,
-                                  hipMemcpyHostToDevice, copy_stream);
-    if (e == hipSuccess) e = hipEventRecord(c->table_done[layer], copy_stream);
-    if (e == hipSuccess && done) e = hipEventRecord(done, copy_stream);
-    if (e != hipSuccess) { set_error("slot table upload failed: %s", hipGetErrorString(e)); return MOE_ERR_HIP; }
-    c->table_pending[layer] = 1;
+    pend.clear();
+    c->ops[layer].clear();
     c->looked_up[layer] = 0;
+    c->open_lookup = -1;
+    for (int r = 0; r < c->n_layers; r++)
+        if (c->dirty[r])
+            if (moe_status st = upload_row(c, r, copy_stream)) return st;
+    if (done && hipEventRecord(done, copy_stream) != hipSuccess) { set_error("hipEventRecord failed"); return MOE_ERR_HIP; }
     return MOE_OK;
 }
 
@@ -447,7 +671,6 @@ moe_status moe_cache_stats(const moe_cache *c, moe_cache_stats_t *out)
 {
     if (!c || !out) { set_error("moe_cache_stats: null argument"); return MOE_ERR_ARG; }
     if (c->dev) {
-        static_assert(sizeof(moe_cache_stats_t) == 9 * sizeof(uint64_t), "stats layout");
         if (hipSetDevice(c->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
             hipMemcpy(out, c->d_stats, sizeof *out, hipMemcpyDeviceToHost) != hipSuccess) {
             set_error("moe_cache_stats: reading the device counters failed");
@@ -477,8 +700,9 @@ moe_status moe_cache_reset_stats(moe_cache *c)
 moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
 {
     if (!c || trace_capacity < 0) { set_error("moe_cache_device_enable: bad argument"); return MOE_ERR_ARG; }
+    if (c->custom) { set_error("moe_cache_device_enable: a cache with a caller-supplied backend looks up on the host"); return MOE_ERR_STATE; }
     if (c->dev) { set_error("moe_cache_device_enable: already enabled"); return MOE_ERR_STATE; }
-    if (c->st.lookups) { set_error("moe_cache_device_enable: the cache has host lookups already"); return MOE_ERR_STATE; }
+    if (c->st.lookups || c->open_lookup >= 0) { set_error("moe_cache_device_enable: the cache has host lookups already"); return MOE_ERR_STATE; }
     for (size_t g = 0; g < c->groups.size(); g++)
         if (c->groups[g].n_slots > kCacheMaxSlots) {
             set_error("moe_cache_device_enable: group %zu has %d slots, above the %d the device lookup holds", g,
@@ -514,6 +738,7 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
     c->dgroups.assign(ng, {});
     for (size_t g = 0; ok && g < ng; g++) {
         const int n = c->groups[g].n_slots;
+        if (n == 0) continue;  // resident group: no LRU state
         std::vector<int32_t> keys(n, -1);
         ok = hipMalloc((void **)&c->dgroups[g].stamp, (size_t)n * 4) == hipSuccess &&
              hipMalloc((void **)&c->dgroups[g].key, (size_t)n * 4) == hipSuccess &&
@@ -539,6 +764,7 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
     c->trace_cap = trace_capacity;
     c->pend_touch.assign(c->n_layers, -1);
     c->ev_pref.assign(c->n_layers, nullptr);
+    c->recent_touch.assign(ng, -1);
     c->dev = true;
     return MOE_OK;
 }
@@ -552,6 +778,7 @@ moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *i
     }
     if (!c->dev) { set_error("moe_cache_lookup_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
     if (T < 1 || T > kMaxT) { set_error("moe_cache_lookup_device: T=%d outside [1, 32]", T); return MOE_ERR_BATCH; }
+    if (resident_layer(c, layer)) return MOE_OK;  // its table row is final
     const int g = c->layer_group[layer];
     auto &G = c->groups[g];
     if (T * k > G.n_slots) {
@@ -567,8 +794,11 @@ moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *i
         }
         c->pend_touch[layer] = -1;
     }
+    moe_status st = launch_cache_device(device_args(c, layer, idx, T, k), stream);
+    if (st != MOE_OK) return st;
     prefetch_count(c, g, T * k);
-    return launch_cache_device(device_args(c, layer, idx, T, k), stream);
+    c->recent_touch[g] = T * k;  // the slots the FFN after this lookup reads
+    return MOE_OK;
 }
 
 moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
@@ -580,14 +810,24 @@ moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t 
     }
     if (!c->dev) { set_error("moe_cache_prefetch_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
     if (T < 1 || T > kMaxT) { set_error("moe_cache_prefetch_device: T=%d outside [1, 32]", T); return MOE_ERR_BATCH; }
+    if (resident_layer(c, layer)) return MOE_OK;  // nothing to fetch
     if (c->pend_touch[layer] >= 0) {
         set_error("moe_cache_prefetch_device: layer %d has a prefetch that its lookup has not taken yet", layer);
         return MOE_ERR_STATE;
     }
     const int g = c->layer_group[layer];
-    if (T * k >= c->groups[g].n_slots) {
-        set_error("moe_cache_prefetch_device: %d selections need more than the %d slots of the group", T * k,
-                  c->groups[g].n_slots);
+    const int n_slots = c->groups[g].n_slots;
+    if (T * k >= n_slots) {
+        set_error("moe_cache_prefetch_device: %d selections need more than the %d slots of the group", T * k, n_slots);
+        return MOE_ERR_CAPACITY;
+    }
+    // The copies overlap the FFN that follows the group's latest lookup.  A
+    // miss can evict one of that lookup's slots only once every slot of the
+    // group has been touched since the lookup, so the prefetch is refused
+    // when the touches since it plus this prefetch's could reach the slots.
+    if (c->recent_touch[g] >= 0 && c->recent_touch[g] + T * k >= n_slots) {
+        set_error("moe_cache_prefetch_device: %d slot touches since the group's latest lookup plus %d more could evict "
+                  "experts that its FFN is reading (group of %d slots)", c->recent_touch[g], T * k, n_slots);
         return MOE_ERR_CAPACITY;
     }
     if (moe_status st = prefetch_guard(c, g, T * k, -1, "moe_cache_prefetch_device")) return st;
@@ -607,6 +847,7 @@ moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t 
     moe_status st = launch_cache_device(a, stream, copy_stream, c->ev_fork, c->ev_pref[layer]);
     if (st != MOE_OK) return st;
     prefetch_count(c, g, T * k);
+    if (c->recent_touch[g] >= 0) c->recent_touch[g] += T * k;
     c->pend_touch[layer] = T * k;
     return MOE_OK;
 }

@@ -2,16 +2,26 @@
 //
 // Decode path of one MoE layer (T <= 32 tokens), three launches:
 //
-//   k_route    router GEMV (+ RMSNorm and bias) by 8 expert rows per
-//              workgroup; the last of those workgroups does softmax top-k and
-//              the grouping of (token, expert) pairs into a work table;
-//              T more workgroups encode each token's normalised state.
-//   k_gate_up  one workgroup per (distinct expert, 32-row tile): the gate
-//              and up rows of the expert against all of its tokens,
-//              SiLU(g)*u, and the encoding of those 32 values.
-//   k_down     one workgroup per (distinct expert, 64-row tile): down rows
-//              against SiLU(g)*u; the last expert to finish a row tile adds
-//              the weighted outputs of every token (and the residual).
+//   k_route    router GEMV, 2 router rows per workgroup against a group of up
+//              to 8 tokens (the 8 waves split H; the sum of squares of the
+//              state rides along for the RMSNorm), each logit handed to the
+//              tail as an order-preserving 32-bit key; encoding workgroups
+//              write each token's normalised state as activation records;
+//              above 16 tokens one top-k workgroup per token; the last
+//              workgroup (the tail) polls the keys (bounded), takes the
+//              softmax top-k and groups the (token, expert) pairs into a work
+//              table of items of at most 4 pairs, largest first.
+//   k_gate_up  one workgroup per (work item, 32-row tile): the gate and up
+//              rows of the item's expert against its tokens, SiLU(g)*u, and
+//              the encoding of those 32 values as one activation block.
+//   k_down     one workgroup per (work item, 64-row tile): down rows against
+//              SiLU(g)*u; each pair's rows, times its combine weight, are
+//              added into the token's rows of y with float atomics (y holds
+//              the residual already, so no combine pass follows).
+// Batches of more than 8 tokens on all-Q4_K experts use k_gate_up_mfma /
+// k_down_mfma instead (fp16 MFMA on the exact integer weights sc*q and a
+// two-part split of the activations).  The slot-pool cache's device lookup
+// and miss copies are k_cache_lookup and k_cache_copy.
 //
 // Gating follows the MoE offload blog (mhpn.cn, section 3.1: router logits,
 // softmax, top-k; section 5.2: the batched form); matvecs that keep the
@@ -29,17 +39,18 @@
 // (v_dot4 on 4 int8 lanes) and a few fp32 operations per block.  This keeps
 // the matvec near 1.3 VALU operations per weight, well under the ~2.7 that
 // 8 TB/s of Q4_K leaves on 256 CUs, while the result stays within fp32
-// rounding of the exact product.  The pieces live in global memory and every
-// lane of a wavefront reads the same words (a lane owns a weight row), so
-// the compiler loads them with scalar loads into SGPRs and feeds them
-// straight to v_dot4.
+// rounding of the exact product.  The records are staged in LDS and read by
+// broadcast (every lane of a wave owns a weight row and reads the same
+// activation words).
 //
-// Cross-workgroup hand-off (route -> top-k, down -> combine) uses relaxed
-// agent-scope atomic stores/loads for the handed-over data (coherent across
-// the XCDs' L2 caches without whole-cache write-back or invalidation), a
-// wait for their completion, and a relaxed arrival counter.
+// Cross-workgroup hand-off (router -> tail, top-k workgroups -> tail) uses
+// relaxed agent-scope atomic stores and loads of words that are never zero
+// once written (coherent across the XCDs' L2 caches without whole-cache
+// write-back or invalidation); the tail polls them with a bounded loop and
+// clears them for the next launch.  There is no arrival counter.
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <atomic>
 #include <hip/hip_fp16.h>
 #include <math.h>
 #include <stdint.h>
@@ -2572,7 +2583,10 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
             uint8_t *slot = a.pool + (size_t)s * a.slot_bytes;
             a.dtab[key] = slot;
             if (!hit) {
-                if (victim >= 0) a.where[victim] = -1;
+                if (victim >= 0) {
+                    a.where[victim] = -1;
+                    a.dtab[victim] = nullptr;  // the evicted expert is no longer resident
+                }
                 a.where[key] = s;
                 a.key[s] = key;
                 a.jobs[nj] = CacheJob{slot, (const uint8_t *)a.src[key]};
@@ -2732,11 +2746,14 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     // kMfmaCols pairs for larger batches (k_group_large)
     const int nent = T > kMaxT ? L.UI : L.U;
     const size_t lds = 2 * kStageBytes;
-    static bool attr = false;
-    if (!attr) {
+    static std::atomic<uint64_t> attr_set{0};  // one bit per device
+    int dev = 0;
+    HIP_OK(hipGetDevice(&dev));
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(attr_set.load() & bit)) {
         HIP_OK(hipFuncSetAttribute((const void *)k_gate_up_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
         HIP_OK(hipFuncSetAttribute((const void *)k_down_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-        attr = true;
+        attr_set.fetch_or(bit);
     }
     GateUpMfmaArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -2822,11 +2839,14 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
 moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t cs, hipEvent_t fork, hipEvent_t done)
 {
     const size_t lds = (size_t)a.n_slots * 8;
-    static bool attr = false;
-    if (!attr) {
+    static std::atomic<uint64_t> attr_set{0};  // one bit per device
+    int dev = 0;
+    HIP_OK(hipGetDevice(&dev));
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(attr_set.load() & bit)) {
         HIP_OK(hipFuncSetAttribute((const void *)k_cache_lookup, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)((size_t)kCacheMaxSlots * 8)));
-        attr = true;
+        attr_set.fetch_or(bit);
     }
     k_cache_lookup<<<1, kCacheThreads, lds, s>>>(a);
     LAUNCH_OK("k_cache_lookup");

@@ -146,7 +146,8 @@ class CachedStack:
     (hits refresh their recency, misses take a free or the least recently
     used slot); the misses are uploaded on a side stream, which the compute
     stream then waits for; moe_layer_ffn reads the experts through the
-    cache's slot table of the layer.
+    cache's slot table of the layer.  Layers of a group that the plan left
+    with 0 slots (below the budget floor) keep their experts resident.
 
     device_lookup=True keeps the LRU state on the device instead
     (moe_cache_device_enable): each layer is then moe_layer_route,
@@ -255,8 +256,7 @@ class CachedStack:
         ih = self.idx_host[:T * s.k].view(T, s.k)
         ih.copy_(idx, non_blocking=True)
         torch.cuda.current_stream(self.device).synchronize()
-        experts = np.unique(ih.numpy())
-        slot, hit, vl, ve = self.cache.lookup(layer, T, experts)
+        experts, slot, hit, vl, ve = self.cache.lookup(layer, T, s.k, ih.numpy())
         if self.trace is not None:
             self.trace.append((layer, experts.copy(), hit.copy(), vl.copy(), ve.copy()))
         timed = self.time_copies and not hit.all()

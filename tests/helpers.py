@@ -75,3 +75,27 @@ def weights_close(gi, gw, ri, rw, rel=W_REL_BAR) -> bool:
             if abs(da[e] - db[e]) > rel * abs(db[e]):
                 return False
     return True
+
+
+def dev_read(addr: int, nbytes: int) -> np.ndarray:
+    """Copy nbytes of device memory at a raw address to the host (hipMemcpy
+    of the HIP runtime that torch and libmoe share)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    out = np.empty(nbytes, np.uint8)
+    rc = hip.hipMemcpy(ctypes.c_void_p(out.ctypes.data), ctypes.c_void_p(addr), ctypes.c_size_t(nbytes),
+                       ctypes.c_int(2))  # hipMemcpyDeviceToHost
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed ({rc})")
+    return out
+
+
+def resident_keys(slots, layer_group, LL, EE):
+    """(layer, expert) keys in the pools after the oracle LRU runs over (LL, EE)."""
+    ref = oracle.lru(slots, layer_group, LL, EE)
+    res = set()
+    for l, e, v_l, v_e in zip(LL, EE, ref.victim_layer, ref.victim_expert):
+        if v_l >= 0:
+            res.discard((int(v_l), int(v_e)))
+        res.add((int(l), int(e)))
+    return ref, res

@@ -13,7 +13,8 @@ import torch
 import oracle
 import workloads as W
 import quantized_expert_ffn_router_amd as moe
-from helpers import ExpertCache, REL_L2_BAR, centered_rel_l2, chain_min_gap, layer_specs, oracle_layers, sets_equal
+from helpers import (ExpertCache, REL_L2_BAR, centered_rel_l2, chain_min_gap, dev_read, layer_specs, oracle_layers,
+                     resident_keys, sets_equal)
 from quantized_expert_ffn_router_amd.stack import CachedStack, pack_layer
 
 pytestmark = pytest.mark.gpu
@@ -37,16 +38,22 @@ def _groups(cfg, n_layers):
     return descs, ebytes, per_group, layer_group
 
 
-def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0):
+def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0, slots=None):
+    """slots=None: the planner's slots for `fraction` of the routed expert
+    bytes (checked against the oracle planner); else the given slots, where
+    a group at 0 slots keeps its layers resident."""
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts, n_layers)
     specs = layer_specs(cfg, n_layers)
     descs, ebytes, per_group, layer_group = _groups(cfg, n_layers)
-    total = sum(cfg.E * ebytes[g] for g in layer_group)
-    budget = int(fraction * total)
-    st, slots = moe.moe_cache_plan(descs, per_group, budget, cfg.k)
-    rc, oslots = oracle.cache_plan(ebytes, per_group, budget, cfg.k)
-    assert st == 0 and rc == 0 and np.array_equal(slots, oslots), (slots, oslots)
+    if slots is None:
+        total = sum(cfg.E * ebytes[g] for g in layer_group)
+        budget = int(fraction * total)
+        st, slots = moe.moe_cache_plan(descs, per_group, budget, cfg.k)
+        rc, oslots = oracle.cache_plan(ebytes, per_group, budget, cfg.k)
+        assert st == 0 and rc == 0 and np.array_equal(slots, oslots), (slots, oslots)
+    slots = np.asarray(slots, np.int32)
+    cached = [slots[layer_group[l]] > 0 for l in range(n_layers)]
     _say(cfg.name, dict(layers=n_layers, steps=steps, T=T, fraction=fraction, slots=list(slots), device=device_lookup))
     packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
     cap = steps * n_layers * T * cfg.k * (2 if prefetch_depth else 1)
@@ -78,6 +85,8 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
         # the GPU's lookups are the oracle routing's distinct experts ...
         LL, EE = (oracle.prefetch_lookup_sequence(ids, pred, targets) if prefetch_depth
                   else oracle.lookup_sequence(ids))
+        keep = np.array([cached[l] for l in LL], bool)  # resident layers make no lookups
+        LL, EE = LL[keep], EE[keep]
         if device_lookup:
             gl, ge, hit, vl, ve = cs.device_trace()
         else:
@@ -98,6 +107,20 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
         assert s["evictions"] == int((ref.victim_layer >= 0).sum())
         assert s["upload_bytes"] == sum(ebytes[layer_group[l]] for l, m in zip(LL, ref.hit) if not m)
         _say("hit rate %.3f over %d lookups, %d evictions" % (n_hit / len(LL), len(LL), s["evictions"]))
+        # the device slot tables: an entry per resident expert (its slot holds
+        # that expert's bytes), NULL for every evicted or never-used expert
+        _, resident = resident_keys(slots, layer_group, LL, EE)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            tab = dev_read(cs.cache.expert_ptrs(l), 8 * cfg.E).view(np.uint64)
+            eb = ebytes[layer_group[l]]
+            for e in range(cfg.E):
+                if not cached[l] or (l, e) in resident:
+                    assert tab[e] != 0, (l, e)
+                    if e % 7 == 0:  # a sample of the slots' bytes
+                        assert np.array_equal(dev_read(int(tab[e]), eb), packed[l][e * eb:(e + 1) * eb].numpy()), (l, e)
+                else:
+                    assert tab[e] == 0, (l, e)
         return s
     finally:
         cs.close()
@@ -180,13 +203,14 @@ def test_cache_errors():
     cs = CachedStack(specs, packed, [5], T_max=1)
     try:
         with pytest.raises(moe.MoeError):  # 6 distinct experts > 5 slots
-            cs.cache.lookup(0, 1, np.arange(6, dtype=np.int32))
+            cs.cache.lookup(0, 1, 6, np.arange(6, dtype=np.int32))
         with pytest.raises(moe.MoeError):  # batches over 32 tokens bypass the cache
-            cs.cache.lookup(0, 33, np.arange(2, dtype=np.int32))
-        with pytest.raises(moe.MoeError):  # not ascending
-            cs.cache.lookup(0, 1, np.array([3, 1], np.int32))
+            cs.cache.lookup(0, 33, 1, np.arange(33, dtype=np.int32) % 16)
+        with pytest.raises(moe.MoeError):  # an id outside [0, E)
+            cs.cache.lookup(0, 1, 2, np.array([3, 16], np.int32))
         assert cs.cache.stats()["lookups"] == 0  # refused lookups leave the state unchanged
-        slot, hit, vl, ve = cs.cache.lookup(0, 1, np.array([1, 2, 3], np.int32))
+        ex, slot, hit, vl, ve = cs.cache.lookup(0, 1, 4, np.array([3, 1, 2, 1], np.int32))
+        assert ex.tolist() == [1, 2, 3]
         assert not hit.any() and (vl == -1).all() and sorted(slot.tolist()) == [0, 1, 2]
         cs.cache.upload(0, cs.copy_stream)
         torch.cuda.synchronize()
@@ -224,3 +248,103 @@ def test_cache_device_errors():
         assert s["lookups"] == 12 and s["hits"] == int(ref.hit.sum()) and s["evictions"] == int((ref.victim_layer >= 0).sum())
     finally:
         cs.close()
+
+
+@pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
+def test_cache_group_below_floor_stays_resident(device_lookup):
+    """A plan whose Q4_K group got 0 slots (below the floor): its layers keep
+    their experts resident and make no lookups, the Q6_K group caches; the
+    outputs stay the oracle's and the trace is the oracle LRU's over the
+    cached layers' lookups (T4 MoE-cache report, "Size your experts before
+    configuring": a group below the floor is left out with a warning)."""
+    cfg = W.mixed_shared_q4k_q6k(T=4)
+    Q4, Q6 = W.Q4_K, W.Q6_K
+    sub = cfg.with_(n_layers=4, layer_qtypes=((Q4,) * 3, (Q6,) * 3, (Q4,) * 3, (Q6,) * 3))
+    s = _run(sub, 4, 5, None, 4, device_lookup, slots=[0, 12])
+    assert s["lookups"] > 0 and s["evictions"] > 0
+
+
+def test_cache_prefetch_refused_while_lookup_slots_in_use():
+    """A prefetch whose misses could evict a slot that the FFN after the
+    group's latest lookup is still reading is refused: a pool of 6 slots, a
+    lookup of 4 experts, then a prefetch of 4 more (4 + 4 touches reach the 6
+    slots).  Through CachedStack with prefetch depth 1 the first step fails
+    the same way."""
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=2).with_(E=16, k=4, seed=9)
+    experts = ExpertCache(cfg)
+    specs = layer_specs(cfg, 2)
+    packed = [pack_layer(s_, l, experts) for l, s_ in enumerate(specs)]
+    cs = CachedStack(specs, packed, [6], T_max=1, device_lookup=True, trace_capacity=64)
+    try:
+        a = torch.tensor([1, 2, 3, 4], dtype=torch.int32, device=DEV)
+        b = torch.tensor([5, 6, 7, 8], dtype=torch.int32, device=DEV)
+        cs.cache.lookup_device(0, a, 1, 4)
+        with pytest.raises(moe.MoeError) as ei:
+            cs.cache.prefetch_device(1, b, 1, 4, cs.copy_stream)
+        assert ei.value.name == "MOE_ERR_CAPACITY"
+        cs.cache.prefetch_device(1, b[:1], 1, 1, cs.copy_stream)  # 4 + 1 < 6 touches: allowed
+        cs.cache.lookup_device(1, b[:1], 1, 1)
+        torch.cuda.synchronize()
+        gl, ge, hit, vl, ve = cs.device_trace()
+        assert list(gl) == [0, 0, 0, 0, 1, 1] and list(hit) == [0, 0, 0, 0, 0, 1]
+    finally:
+        cs.close()
+    cs = CachedStack(specs, packed, [6], T_max=1, device_lookup=True, prefetch_depth=1)
+    try:
+        with pytest.raises(moe.MoeError) as ei:
+            cs.step(torch.from_numpy(W.token(cfg, 0, 0)[None]).to(DEV))
+        assert ei.value.name == "MOE_ERR_CAPACITY"
+        torch.cuda.synchronize()
+    finally:
+        cs.close()
+
+
+def test_cache_device_lru_evicts_beyond_1024_slots():
+    """The device lookup's eviction path with more slots than the lookup
+    workgroup has threads (2,100 slots, not a multiple of 1,024, so each
+    thread scans several stamps and the last pass is partial): 8 steps over
+    6 layers of 512 experts, 384 selections per layer-step drawn with a mild
+    skew, 3,072 keys against 2,100 slots.  The trace must be the oracle LRU's
+    bit for bit; the slot tables and a sample of slot bytes are checked."""
+    desc = moe.ExpertDesc.of((W.Q4_K,) * 3, 256, 64)
+    eb = moe.moe_expert_bytes(desc)
+    L, E, T, k, n_slots, steps = 6, 512, 16, 24, 2100, 8
+    rng = np.random.default_rng(11)
+    host = [torch.from_numpy(rng.integers(0, 256, E * eb, dtype=np.uint8)).pin_memory() for _ in range(L)]
+    ptrs = [host[l].data_ptr() + e * eb for l in range(L) for e in range(E)]
+    cache = moe.Cache([desc], [n_slots], [0] * L, E, ptrs)
+    cap = steps * L * T * k
+    try:
+        cache.enable_device(cap)
+        p = np.arange(1, E + 1, dtype=np.float64) ** -0.6
+        p /= p.sum()
+        ids = np.empty((steps, L, T * k), np.int32)
+        for s_ in range(steps):
+            for l in range(L):
+                ids[s_, l] = np.concatenate([rng.choice(E, k, replace=False, p=p) for _ in range(T)])
+                cache.lookup_device(l, torch.from_numpy(ids[s_, l]).to(DEV), T, k)
+        torch.cuda.synchronize()
+        t = cache.trace_read(cap)
+        LL, EE = oracle.lookup_sequence(ids)
+        assert np.array_equal(t[:, 0], LL) and np.array_equal(t[:, 1], EE)
+        ref, resident = resident_keys([n_slots], [0] * L, LL, EE)
+        vk = t[:, 3]
+        assert np.array_equal(t[:, 2].astype(np.uint8), ref.hit)
+        assert np.array_equal(np.where(vk >= 0, vk // E, -1), ref.victim_layer)
+        assert np.array_equal(np.where(vk >= 0, vk % E, -1), ref.victim_expert)
+        n_ev = int((ref.victim_layer >= 0).sum())
+        _say(f"{len(LL)} lookups, {int(ref.hit.sum())} hits, {n_ev} evictions")
+        assert n_ev > 2000
+        st = cache.stats()
+        assert st["lookups"] == len(LL) and st["evictions"] == n_ev and st["hits"] == int(ref.hit.sum())
+        for l in range(L):
+            tab = dev_read(cache.expert_ptrs(l), 8 * E).view(np.uint64)
+            for e in range(E):
+                if (l, e) in resident:
+                    assert tab[e] != 0, (l, e)
+                    if e % 37 == 0:
+                        assert np.array_equal(dev_read(int(tab[e]), eb), host[l][e * eb:(e + 1) * eb].numpy()), (l, e)
+                else:
+                    assert tab[e] == 0, (l, e)
+    finally:
+        cache.close()
