@@ -90,11 +90,12 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
         if device_lookup:
             gl, ge, hit, vl, ve = cs.device_trace()
         else:
-            gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in cs.trace])
-            ge = np.concatenate([e for _, e, *_ in cs.trace]).astype(np.int32)
-            hit = np.concatenate([t[2] for t in cs.trace])
-            vl = np.concatenate([t[3] for t in cs.trace])
-            ve = np.concatenate([t[4] for t in cs.trace])
+            tr = [t for t in cs.trace if cached[t[0]]]
+            gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in tr])
+            ge = np.concatenate([e for _, e, *_ in tr]).astype(np.int32)
+            hit = np.concatenate([t[2] for t in tr])
+            vl = np.concatenate([t[3] for t in tr])
+            ve = np.concatenate([t[4] for t in tr])
         assert np.array_equal(gl, LL) and np.array_equal(ge, EE)
         # ... and its hit/miss/victim trace is the oracle LRU's, bit for bit
         ref = oracle.lru(slots, layer_group, LL, EE)
@@ -228,7 +229,7 @@ def test_cache_device_errors():
     cs = CachedStack(specs, packed, [5], T_max=2, device_lookup=True, trace_capacity=64)
     try:
         with pytest.raises(moe.MoeError):  # the LRU state now lives on the device
-            cs.cache.lookup(0, 1, np.array([1, 2], np.int32))
+            cs.cache.lookup(0, 1, 2, np.array([1, 2], np.int32))
         with pytest.raises(moe.MoeError):
             cs.cache.enable_device(0)
         idx = torch.tensor([[1, 2, 3, 4], [5, 6, 7, 8]], dtype=torch.int32, device=DEV)
