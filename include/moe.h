@@ -209,6 +209,22 @@ moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, cons
                              int32_t n_shared, float eps, int32_t *idx_out, float *w_out,
                              void *ws, size_t ws_bytes, hipStream_t s);
 
+/* moe_layer_forward without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the layer runs in a library-owned static scratch array of 8 MiB per GPU,
+ * held from the first call on that GPU until the process ends (the first
+ * call also clears it on stream s).  Arguments as for moe_layer_forward.
+ * MOE_ERR_CAPACITY (nothing enqueued) when the layer needs more scratch than
+ * the array holds (moe_workspace_bytes of the same sizes; every
+ * configuration of up to 32 tokens with H, I <= 4096 and E <= 256 fits).  Every call on
+ * a GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams without ordering) race. */
+moe_status moe_layer_forward_noalloc(const moe_expert_desc *d, float *h, int32_t T, const float *w_router,
+                                     const float *bias, int32_t E, int32_t k, const void *const *expert_ptrs,
+                                     const void *const *shared_ptrs, int32_t n_shared, float eps,
+                                     int32_t *idx_out, float *w_out, hipStream_t s);
+
 /* ---------------------------------------------------------------------- */
 /* Expert slot-pool cache (T4 MoE-cache report, sections "What the MoE cache
  * caches" and "Size your experts before configuring").  Experts are grouped

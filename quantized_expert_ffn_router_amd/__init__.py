@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     moe_group_tokens,
     moe_layer_ffn,
     moe_layer_forward,
+    moe_layer_forward_noalloc,
     moe_layer_route,
     moe_repack_expert,
     moe_rmsnorm,

@@ -16,6 +16,7 @@ EXPORTED = [
     "moe_last_error", "moe_expert_bytes", "moe_down_k", "moe_repack_expert",
     "moe_rmsnorm", "moe_route_topk", "moe_group_tokens", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
+    "moe_layer_forward_noalloc",
     "moe_cache_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
     "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_prefetch_device", "moe_cache_trace_read",
@@ -113,6 +114,7 @@ def lib() -> ctypes.CDLL:
         "moe_layer_route": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_layer_ffn": (i32, [D, P, i32, i32, i32, P, P, i32, P, sz, P]),
         "moe_layer_forward": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
+        "moe_layer_forward_noalloc": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P]),
         "moe_cache_plan": (i32, [D, P, i32, u64, i32, P]),
         "moe_cache_create": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(P)]),
         "moe_cache_create_ex": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(CacheBackend), ctypes.POINTER(P)]),
@@ -231,6 +233,13 @@ def moe_layer_forward(desc, h, T: int, w_router, bias, E: int, k: int, expert_pt
     _check(lib().moe_layer_forward(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k,
                                    _ptr(expert_ptrs), _ptr(shared_ptrs), n_shared, eps, _ptr(idx_out),
                                    _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_forward_noalloc(desc, h, T: int, w_router, bias, E: int, k: int, expert_ptrs, shared_ptrs,
+                              n_shared: int, eps: float, idx_out, w_out, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k,
+                                           _ptr(expert_ptrs), _ptr(shared_ptrs), n_shared, eps, _ptr(idx_out),
+                                           _ptr(w_out), _stream(stream)))
 
 
 def moe_layer_route(desc, h, T: int, w_router, bias, E: int, k: int, expert_ptrs, shared_ptrs, n_shared: int,

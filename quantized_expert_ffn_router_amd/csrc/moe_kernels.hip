@@ -51,6 +51,7 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <hip/hip_fp16.h>
 #include <math.h>
 #include <stdint.h>
@@ -2648,6 +2649,19 @@ __global__ void k_fill_zero(uint4 *p, size_t n16)
         p[i] = make_uint4(0, 0, 0, 0);
 }
 
+}  // namespace
+}  // namespace moe
+
+// Scratch of moe_layer_forward_noalloc, for callers that cannot allocate:
+// one array per GPU, held from the library's first use on that GPU until
+// the process ends.  Host code never uses its name as an address; it takes
+// the device address from hipGetSymbolAddress once per device.
+static constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace moe {
+namespace {
+
 // ---------------------------------------------------------------------------
 // host side
 
@@ -3011,6 +3025,74 @@ moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, cons
                                     w_out, ws, ws_bytes, s);
     if (st != MOE_OK) return st;
     return moe_layer_ffn(d, h, T, E, k, expert_ptrs, shared_ptrs, n_shared, ws, ws_bytes, s);
+}
+
+
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch array: taken once per device
+// (with that device current) and kept; the first call also clears the
+// whole array on s, since the routing hand-over words must start at zero
+// (the kernels leave them at zero when they finish).
+moe_status static_scratch(hipStream_t s, void **out)
+{
+    int dev = 0;
+    HIP_OK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device %d outside the %d devices the static scratch tracks", dev, kMaxDevices);
+        return MOE_ERR_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_error("hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+            return MOE_ERR_HIP;
+        }
+        k_fill_zero<<<1024, 256, 0, s>>>((uint4 *)p, kStaticScratchBytes / 16);
+        LAUNCH_OK("k_fill_zero");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const moe_expert_desc *d, float *h, int32_t T, const float *w_router,
+                                     const float *bias, int32_t E, int32_t k, const void *const *expert_ptrs,
+                                     const void *const *shared_ptrs, int32_t n_shared, float eps, int32_t *idx_out,
+                                     float *w_out, hipStream_t s)
+{
+    ExpertGeom g;
+    moe_status st = check_desc(d, &g);
+    if (st != MOE_OK) return st;
+    if ((st = check_tke(T, k, E, n_shared)) != MOE_OK) return st;
+    if (!h || !w_router || !expert_ptrs || (n_shared > 0 && !shared_ptrs)) {
+        set_error("moe_layer_forward_noalloc: null pointer");
+        return MOE_ERR_ARG;
+    }
+    const size_t need = ws_layout(*d, T, k, E, n_shared).total;
+    if (need > kStaticScratchBytes) {
+        set_error("moe_layer_forward_noalloc: this layer needs %zu bytes of scratch, the static array holds %zu "
+                  "(use moe_layer_forward with a workspace)", need, kStaticScratchBytes);
+        return MOE_ERR_CAPACITY;
+    }
+    void *ws = nullptr;
+    if ((st = static_scratch(s, &ws)) != MOE_OK) return st;
+    return moe_layer_forward(d, h, T, w_router, bias, E, k, expert_ptrs, shared_ptrs, n_shared, eps, idx_out, w_out,
+                             ws, kStaticScratchBytes, s);
 }
 
 }  // extern "C"
