@@ -170,8 +170,12 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
         for l in range(nl):
             sp = st.layers[l]
             ev[l][0].record()
+            # a single token's ids are distinct, so U = k; not asking for them
+            # lets the route launch leave the routing to the FFN's workgroups,
+            # as moe_layer_forward does in the timed graph
             moe.moe_layer_route(st.descs[l], h, T, st.routers[l], st.biases[l], sp.E, sp.k, st.expert_ptrs(l),
-                                st.shared_ptrs(l), sp.n_shared, st.eps, idx[l], None, st.ws, st.ws_bytes)
+                                st.shared_ptrs(l), sp.n_shared, st.eps, idx[l] if T > 1 else None, None, st.ws,
+                                st.ws_bytes)
             ev[l][1].record()
             moe.moe_layer_ffn(st.descs[l], h, T, sp.E, sp.k, st.expert_ptrs(l), st.shared_ptrs(l), sp.n_shared,
                               st.ws, st.ws_bytes)
@@ -179,7 +183,7 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
         torch.cuda.synchronize()
         ids = idx.cpu().numpy()
         for l in range(nl):
-            U = len(np.unique(ids[l]))
+            U = len(np.unique(ids[l])) if T > 1 else k
             tot_bytes += U * eb
             tot_ffn_ms += ev[l][1].elapsed_time(ev[l][2])
             tot_route_ms += ev[l][0].elapsed_time(ev[l][1])

@@ -138,7 +138,7 @@ constexpr int kX16Bytes = 1072;
 
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U, UI;  // U: distinct experts, UI: work items (both at most)
-    size_t keys, tk, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, total;
+    size_t keys, tk, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, dlog, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -166,6 +166,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.pw = take((size_t)L.P * 4);
     L.henc = take((size_t)L.P * enc_bytes(L.kd));
     L.hf = take((size_t)L.P * L.kd * 4);
+    L.dlog = take((size_t)E * 4);  // a single token's logit keys, for routing in the FFN
     L.total = o;
     return L;
 }

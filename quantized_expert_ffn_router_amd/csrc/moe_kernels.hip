@@ -659,6 +659,8 @@ struct RouteArgs {
                             // then topk_blocks top-k workgroups, then the tail
     int topk_blocks;        // 0, or T: a workgroup per token ranks its keys and hands them to the tail
     unsigned long long *tk; // [T][k] hand-over of those selections (key << 32 | ~id, never zero)
+    int tail;               // 1: the last workgroup routes (keys handed over); 0: no tail
+    uint32_t *dlog;         // [E] (T = 1) the logit keys for routing in the FFN (plain stores), or null
 };
 
 // Top-k of NT tokens' E keys each by one wave (no barriers), keys in
@@ -1081,8 +1083,10 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr, 
                 }
                 const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
                 const float lg = d * rr + (a.bias ? a.bias[e0 + r] : 0.f);
-                __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (a.dlog) a.dlog[e0 + r] = logit_key(lg);  // read after the launch boundary
+                if (a.tail)
+                    __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
                 if (a.logits2) a.logits2[(size_t)t * E + e0 + r] = lg;
             }
         }
@@ -1101,11 +1105,11 @@ __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
     const int H = a.H, T = a.T, E = a.E;
     const int blk = blockIdx.x;
     const int lane = lane_id();
-    if (blk == (int)gridDim.x - 1) {
+    if (a.tail && blk == (int)gridDim.x - 1) {
         route_tail(a);
         return;
     }
-    if (blk >= (int)gridDim.x - 1 - a.topk_blocks) {
+    if (a.tail && blk >= (int)gridDim.x - 1 - a.topk_blocks) {
         route_topk_role(a, blk - ((int)gridDim.x - 1 - a.topk_blocks));
         return;
     }
@@ -1703,7 +1707,44 @@ struct GateUpArgs {
     int ntile;        // I/32
     int tpass;        // tokens staged per pass
     int T;            // tokens (records of x)
+    // single-token routing done here (DEFER): the router's logit keys [E],
+    // and the grouping that workgroup (0, 0) records for k_down
+    const uint32_t *dlog;
+    int k, ns, Umax;
+    WorkEntry *wt_out;
+    int *ptok_out, *inv, *nuniq;
+    float *pw;
 };
+
+// Ranks of one token's E <= 128 logit keys by a whole 512-thread workgroup:
+// key i's rank is the number of keys that beat it (a larger key, or an equal
+// key of lower id), i.e. of larger 64-bit composites key << 32 | ~id.  The
+// lane quad 4i..4i+3 counts for key i, lane q over the quarter q of the
+// composites (ids 32q .. 32q+31), all 16 reads issued at once, and the quad
+// sums its counts with DPP.  The quarters sit 272 bytes apart in LDS, so that
+// the four quarters' 16-byte reads of one instruction fall in different
+// banks.  key: the composite of id tid/4 in lanes with tid % 4 == 0.
+// Returns the rank of id tid/4 in every lane of its quad (ids past E: more
+// than any k).  Holds one barrier.
+constexpr int kRankStride = 34;  // 64-bit keys per quarter in LDS, with padding (272 B)
+__device__ __forceinline__ int rank_keys_128(uint64_t key, int E, uint64_t *lk)
+{
+    const int tid = (int)threadIdx.x, i = tid >> 2, q = tid & 3;
+    const int at = (i >> 5) * kRankStride + (i & 31);
+    if (q == 0) lk[at] = i < E ? key : 0ull;
+    __syncthreads();
+    const uint64_t ki = lk[at];
+    const ulonglong2 *src = (const ulonglong2 *)(lk + kRankStride * q);
+    ulonglong2 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) v[j] = src[j];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) cnt += (v[j].x > ki) + (v[j].y > ki);
+    cnt += xchg<1>(cnt);
+    cnt += xchg<2>(cnt);
+    return i < E ? cnt : 0x7fffffff;
+}
 
 constexpr int kGUThreads = 512;
 constexpr int kTokPass = 4;  // <= kInlineTok
@@ -1716,18 +1757,27 @@ constexpr int kDnPre = 4;       // record words per thread loaded before the wei
 // every token's record fits the first pass and the prefetch words (T <= 2,
 // T * RB <= kGUPre * kGUThreads * 16); the records are then loaded before
 // the work entry arrives, token t to LDS slot t.
-template <int QT, int NTOK>
+template <int QT, int NTOK, bool DEFER>
 __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 2))) void k_gate_up(GateUpArgs a)
 {
     extern __shared__ __align__(16) uint8_t xs[];
     __shared__ float part[8][kTokPass][32][2];
     constexpr bool ALL = NTOK <= 2;
+    static_assert(!DEFER || NTOK == 1, "routing in the FFN is for a single token");
 
     const int u = blockIdx.x / a.ntile;
     const int rt = blockIdx.x - u * a.ntile;
     const int H = a.H, S = H >> 8;
     const size_t RB = enc_bytes(H);
     const int q16 = (int)(RB / 16);  // 16-byte words per record
+    // DEFER: the logit key and expert address of id tid/4, loaded first by
+    // lane 0 of each quad
+    uint32_t dkey = 0;
+    const void *dptr = nullptr;
+    if (DEFER && u < a.k && (threadIdx.x & 3) == 0 && (int)(threadIdx.x >> 2) < a.E) {
+        dkey = a.dlog[threadIdx.x >> 2];
+        dptr = a.eptr[threadIdx.x >> 2];
+    }
     u32x4 xr[kGUPre];
     if (ALL) {
         // the records are back to back: word i is word i % q16 of token i / q16
@@ -1735,15 +1785,84 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
         for (int q = 0; q < kGUPre; q++)
             xr[q] = ((const u32x4 *)a.x.base)[min((int)threadIdx.x + q * kGUThreads, a.T * q16 - 1)];
     }
-    const WorkEntry we = load_entry(a.wt, u);
-    const int e = we.e, p0 = we.p0, p1 = we.p1;
-    if (p0 >= p1) {
-        if (ALL)
+    int e, p0, p1;
+    const uint8_t *base;
+    uint64_t toks = 0;
+    if constexpr (DEFER) {
+        // Routing of the single token from the router's logit keys, in every
+        // workgroup (E <= 128): the ranks of the keys; the expert of rank u is
+        // work item and pair u (ranks order the pairs here: the layer calls
+        // never expose the grouped order).  Workgroup (0, 0) records the
+        // grouping and the softmax weights for k_down.  Items k .. k+ns-1 are
+        // the shared experts, items past them are empty.
+        __shared__ __align__(16) uint64_t lk[4 * kRankStride];
+        __shared__ int lsel_e[kMaxK];
+        __shared__ const void *lsel_p[kMaxK];
+        __shared__ uint32_t lkey_r[kMaxK];
+        const int k = a.k, ns = a.ns, tid = (int)threadIdx.x;
+        if (u >= k + ns) {
 #pragma unroll
             for (int q = 0; q < kGUPre; q++) use(xr[q]);
-        return;
+            return;
+        }
+        if (u >= k) {
+            e = a.E + (u - k);
+            base = (const uint8_t *)a.sptr[u - k];
+        } else {
+            const int r = rank_keys_128((uint64_t)dkey << 32 | (uint32_t)~(threadIdx.x >> 2), a.E, lk);
+            if (r < k && (tid & 3) == 0) {
+                lsel_e[r] = tid >> 2;
+                lsel_p[r] = dptr;
+                lkey_r[r] = dkey;
+            }
+            __syncthreads();
+            e = lsel_e[u];
+            base = (const uint8_t *)lsel_p[u];
+        }
+        p0 = u;
+        p1 = u + 1;
+        if (u == 0 && rt == 0 && tid < 64) {
+            // softmax over the k selected logits (selection j = rank j) and
+            // the grouping: pair j = selection j
+            const int lane = tid;
+            const float lg = lane < k ? unord_bits(lkey_r[lane]) : 0.f;
+            const float top = unord_bits(lkey_r[0]);
+            const float ex = lane < k ? expf(lg - top) : 0.f;
+            const float wsum = wave_sum(ex);
+            if (lane < k) {
+                WorkEntry we{};
+                we.e = lsel_e[lane]; we.p0 = lane; we.p1 = lane + 1;
+                we.ptr = lsel_p[lane];
+                a.wt_out[lane] = we;
+                a.ptok_out[lane] = 0;
+                a.inv[lane] = lane;
+                a.pw[lane] = ex / wsum;
+            }
+            if (lane < ns) {
+                WorkEntry we{};
+                we.e = a.E + lane; we.p0 = k + lane; we.p1 = k + lane + 1;
+                we.ptr = a.sptr[lane];
+                a.wt_out[k + lane] = we;
+                a.ptok_out[k + lane] = 0;
+                a.inv[k + lane] = k + lane;
+                a.pw[k + lane] = 1.0f;
+            }
+            for (int u2 = k + ns + lane; u2 < a.Umax; u2 += 64) a.wt_out[u2] = WorkEntry{};
+            if (lane == 0) *a.nuniq = k + ns;
+        }
+    } else {
+        const WorkEntry we = load_entry(a.wt, u);
+        e = we.e; p0 = we.p0; p1 = we.p1;
+        if (p0 >= p1) {
+            if (ALL)
+#pragma unroll
+                for (int q = 0; q < kGUPre; q++) use(xr[q]);
+            return;
+        }
+        base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
+        __builtin_memcpy(&toks, we.tok, sizeof(toks));
     }
-    const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
+    (void)e;
     const int lane = lane_id();
     const int m = (int)(threadIdx.x >> 8);              // 0: gate, 1: up
     const int slot = (int)((threadIdx.x >> 5) & 7), r = lane & 31;
@@ -1758,8 +1877,6 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     // its own weights arrive.
     const int nt0 = p1 - p0 < a.tpass ? p1 - p0 : a.tpass;
     const float rq16 = 1.0f / (float)q16;
-    uint64_t toks;
-    __builtin_memcpy(&toks, we.tok, sizeof(toks));
     if (!ALL) {
 #pragma unroll
         for (int q = 0; q < kGUPre; q++) {
@@ -1804,7 +1921,11 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             }
         } else {
             __syncthreads();  // the previous pass is done with xs
-            for (int tt = 0; tt < nt; tt++) stage16(xs + tt * RB, rec_at(a.x, token_of(we, a.ptok, c0 + tt), H), RB);
+            for (int tt = 0; tt < nt; tt++) {
+                const int i = c0 + tt - p0;
+                const int tok = i < kInlineTok ? (int)((toks >> (8 * i)) & 0xff) : a.ptok[c0 + tt];
+                stage16(xs + tt * RB, rec_at(a.x, tok, H), RB);
+            }
         }
         __syncthreads();
         // each lane owns part[slot][*][r]: plain writes for its first K-group, sums after
@@ -2789,9 +2910,19 @@ moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const 
     return MOE_OK;
 }
 
+// A single token's routing moves from the route launch's tail into the
+// gate/up workgroups when the experts are few enough for their rank count
+// (E <= 128) and the token's record fits the prefetch words.  The layer
+// calls use it: moe_layer_route then only writes the logit keys (and runs
+// its tail only when the caller asks for the routing), moe_layer_ffn routes.
+bool defer_routing(const moe_expert_desc &d, int T, int E)
+{
+    return T == 1 && E <= 128 && enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16 && !use_mfma(d, T);
+}
+
 moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
                               const void *const *eptr, const void *const *sptr, float *y,
-                              float *act_out, hipStream_t s)
+                              float *act_out, hipStream_t s, bool defer = false)
 {
     if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, T, E, eptr, sptr, y, act_out, s);
     const WsLayout &L = ws.L;
@@ -2810,10 +2941,17 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     dim3 ggrid(L.UI * ga.ntile);
     // every token's record staged up front when they all fit the first pass
     const bool all = T <= 2 && T <= ga.tpass && (size_t)T * enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16;
+    // a single token routed by the gate/up workgroups themselves (the layer's
+    // route launch left its logit keys in the workspace)
+    ga.dlog = defer ? ws.at<uint32_t>(L.dlog) : nullptr;
+    ga.k = L.k; ga.ns = L.ns; ga.Umax = L.UI;
+    ga.wt_out = ws.at<WorkEntry>(L.wt); ga.ptok_out = ws.at<int>(L.ptok); ga.inv = ws.at<int>(L.inv);
+    ga.nuniq = ws.at<int>(L.nuniq); ga.pw = ws.at<float>(L.pw);
 #define GATE_UP(Q)                                                                        \
-    (all ? (T == 1 ? k_gate_up<Q, 1><<<ggrid, kGUThreads, glds, s>>>(ga)                 \
-                   : k_gate_up<Q, 2><<<ggrid, kGUThreads, glds, s>>>(ga))                \
-         : k_gate_up<Q, kTokPass><<<ggrid, kGUThreads, glds, s>>>(ga))
+    (defer ? k_gate_up<Q, 1, true><<<ggrid, kGUThreads, glds, s>>>(ga)                   \
+     : all ? (T == 1 ? k_gate_up<Q, 1, false><<<ggrid, kGUThreads, glds, s>>>(ga)        \
+                     : k_gate_up<Q, 2, false><<<ggrid, kGUThreads, glds, s>>>(ga))       \
+           : k_gate_up<Q, kTokPass, false><<<ggrid, kGUThreads, glds, s>>>(ga))
     switch (d.gate) {
     case MOE_Q4_K: GATE_UP(MOE_Q4_K); break;
     case MOE_Q6_K: GATE_UP(MOE_Q6_K); break;
@@ -2996,7 +3134,14 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     // of its 8 waves), a top-k workgroup per token
     a.topk_blocks = T > kTopkBlocksMinT && E <= kWaveTopE ? T : 0;
     a.tk = W.at<unsigned long long>(W.L.tk);
-    k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + a.topk_blocks + 1, kRouteWG, 0, s>>>(a);
+    // a single token is routed by moe_layer_ffn's gate/up workgroups from the
+    // logit keys; the tail runs only when the caller wants the routing now
+    const bool defer = defer_routing(*d, T, E);
+    a.dlog = defer ? W.at<uint32_t>(W.L.dlog) : nullptr;
+    a.tail = !defer || idx_out || w_out;
+    if (!a.tail) a.topk_blocks = 0;
+    k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + a.topk_blocks + (a.tail ? 1 : 0), kRouteWG, 0,
+              s>>>(a);
     LAUNCH_OK("k_route");
     return MOE_OK;
 }
@@ -3012,7 +3157,7 @@ moe_status moe_layer_ffn(const moe_expert_desc *d, float *h, int32_t T, int32_t 
     if (!h || !expert_ptrs || (n_shared > 0 && !shared_ptrs)) { set_error("moe_layer_ffn: null pointer"); return MOE_ERR_ARG; }
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
-    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, h, nullptr, s);
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, h, nullptr, s, defer_routing(*d, T, E));
 }
 
 moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, const float *w_router, const float *bias,
