@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE decode tokens/s (layer stack) + achieved HBM GB/s on expert bytes read"
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_ffn_qwen3_30b_q4k_hbm_traffic.md")
 KERNEL_SOURCES = ("moe_kernels.hip", "moe_internal.h")
 
@@ -138,13 +139,18 @@ def throughput(st, T: int, K: int, Wm: int, H: int, seed: int):
         h.copy_(xs[s])
         graph.replay()
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     t0 = time.perf_counter()
     for s in range(K):
+        evs[s].record()
         h.copy_(xs[Wm + s])
         graph.replay()
+    evs[K].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    return T * K / el, el / K * 1e3
+    per = np.array([evs[s].elapsed_time(evs[s + 1]) for s in range(K)])
+    pct = {f"p{q}": round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)}
+    return T * K / el, el / K * 1e3, pct
 
 
 def ffn_timing(st, T: int, steps: int, H: int, seed: int):
@@ -158,10 +164,11 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
     xs = torch.randn((steps, T, H), generator=g, dtype=torch.float32).to(dev)
     idx = torch.empty((nl, T, k), dtype=torch.int32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nl)]
-    eb = st.expert_bytes[0]
     tot_bytes = 0.0
     tot_ffn_ms = 0.0
     tot_route_ms = 0.0
+    tot_pairs = 0
+    tot_flop = 0.0
     n_ffn = 0
     for s in range(steps):
         h = xs[s]
@@ -183,13 +190,17 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
         torch.cuda.synchronize()
         ids = idx.cpu().numpy()
         for l in range(nl):
-            U = len(np.unique(ids[l])) if T > 1 else k
-            tot_bytes += U * eb
+            # distinct routed experts plus the always-read shared experts
+            U = (len(np.unique(ids[l])) if T > 1 else k) + st.layers[l].n_shared
+            tot_bytes += U * st.expert_bytes[l]
+            tot_pairs += T * (st.layers[l].k + st.layers[l].n_shared)
+            tot_flop += 2.0 * T * (st.layers[l].k + st.layers[l].n_shared) * 3 * st.layers[l].H * st.layers[l].I
             tot_ffn_ms += ev[l][1].elapsed_time(ev[l][2])
             tot_route_ms += ev[l][0].elapsed_time(ev[l][1])
             n_ffn += 1
     return dict(ffn_us=tot_ffn_ms / n_ffn * 1e3, route_us=tot_route_ms / n_ffn * 1e3,
-                bytes_per_launch=tot_bytes / n_ffn, gbps=tot_bytes / (tot_ffn_ms * 1e-3) / 1e9, launches=n_ffn)
+                bytes_per_launch=tot_bytes / n_ffn, gbps=tot_bytes / (tot_ffn_ms * 1e-3) / 1e9, launches=n_ffn,
+                tflops=tot_flop / (tot_ffn_ms * 1e-3) / 1e12, flop_per_launch=tot_flop / n_ffn)
 
 
 def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int = 4):
@@ -371,25 +382,180 @@ def prompt_leg(st, cfg, T: int, steps: int, seed: int):
                         f"32 pairs); expert_GBps = distinct experts x expert bytes x layers / step time"}
 
 
-def cpu_baseline(cfg, experts: dict, n_tokens: int, n_layers: int):
-    """The oracle as it stands, on a bounded sample (n_tokens single-token
-    decodes through the first n_layers layers), scaled to the whole stack."""
+def cache_leg_groups(cfg, specs, packed, fractions, steps: int, T: int, seed: int):
+    """A stack of several (type, shape) groups (the mixed Q4_K / Q6_K stack)
+    with its routed experts in pinned host memory behind one slot pool per
+    group (the planner splits the budget), shared experts resident, `steps`
+    decode steps of T fresh tokens from a cold pool, the device LRU replayed
+    as a HIP graph: tokens/s, hit rate, misses per step."""
+    import torch
+    import quantized_expert_ffn_router_amd as moe
+    from quantized_expert_ffn_router_amd.stack import CachedStack
+
+    keys, lg = [], []
+    for l in range(cfg.n_layers):
+        if cfg.qtypes(l) not in keys:
+            keys.append(cfg.qtypes(l))
+        lg.append(keys.index(cfg.qtypes(l)))
+    descs = [moe.ExpertDesc.of(q, cfg.H, cfg.I) for q in keys]
+    eb = [moe.moe_expert_bytes(d) for d in descs]
+    per_group = [lg.count(g) for g in range(len(keys))]
+    total = sum(cfg.E * eb[g] for g in lg)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    xs = torch.randn((steps, T, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+    legs = []
+    for f in fractions:
+        st_, slots = moe.moe_cache_plan(descs, per_group, int(f * total), cfg.k)
+        cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=True)
+        hb = xs[0].clone()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs.step(hb)
+        torch.cuda.synchronize()
+        cs.cache.reset_stats()
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            hb.copy_(xs[s_])
+            graph.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        rs = cs.cache.stats()
+        del graph
+        cs.close()
+        legs.append({"pool_fraction": f, "slots": [int(x) for x in slots], "tokens_per_s": round(T * steps / el, 2),
+                     "hit_rate": round(rs["hits"] / max(1, rs["lookups"]), 4),
+                     "misses_per_step": round(rs["misses"] / steps, 2)})
+        log(f"cache (groups) {f:.0%}: {legs[-1]}")
+    return {"workload": f"{cfg.n_layers}-layer mixed Q4_K/Q6_K stack, two slot pools (one per type), shared experts "
+                        f"resident, {steps} steps of {T} fresh tokens, device LRU as a HIP graph; the pools start "
+                        f"with the capture step's experts", "legs": legs}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_CPU_SNIPPET = r"""
+import sys, time, json
+sys.path.insert(0, {root!r})
+import oracle, workloads as W
+import numpy as np
+def layers(cfg, n):
+    ex = {{}}
+    def fn(l):
+        def g(e):
+            if (l, e) not in ex:
+                ex[(l, e)] = W.expert(cfg, l, e)
+            return ex[(l, e)]
+        return g
+    return [oracle.LayerWeights(cfg.qtypes(l), cfg.H, cfg.I, cfg.down_k(l), cfg.E, cfg.k, W.router(cfg, l),
+                                W.zipf_bias(cfg, l), fn(l), cfg.n_shared) for l in range(n)], ex
+out = {{}}
+# C1: the tiny single Q8_0 layer, per token
+c1 = W.tiny_q8_0(seed=1)
+lw, _ = layers(c1, 1)
+xs = [W.token(c1, 99, t) for t in range(64)]
+oracle.stack_token(lw, xs[0])
+t0 = time.perf_counter()
+for x in xs:
+    oracle.stack_token(lw, x)
+out["c1_tokens_per_s"] = len(xs) / (time.perf_counter() - t0)
+# the 48-layer Qwen3-30B-A3B-shaped stack: {n_tok} tokens through {n_lay} layers (experts generated outside the timing)
+c2 = W.qwen3_30b_a3b_q4k(T=1)
+lw, ex = layers(c2, {n_lay})
+xs = [W.token(c2, 99, t) for t in range({n_tok})]
+for x in xs:
+    oracle.stack_token(lw, x)  # generates the routed experts (untimed)
+t0 = time.perf_counter()
+for x in xs:
+    oracle.stack_token(lw, x)
+el = time.perf_counter() - t0
+out["c2_s_per_token_layer"] = el / (len(xs) * {n_lay})
+print(json.dumps(out))
+"""
+
+
+def cpu_baseline(n_tokens: int, n_layers: int, threads: int):
+    """The oracle as it stands, timed on the host on bounded samples, in child
+    processes with OMP_NUM_THREADS = 1 and = all cores: C1 (one layer) per
+    token, and the 48-layer stack per token from n_tokens tokens through
+    n_layers layers (scaled to 48; the oracle handles each token on its own,
+    so a batch of 8 costs 8 tokens); and the exact LRU simulation of a
+    512-step x 48-layer lookup trace (Zipf-skewed ids drawn on the host) at
+    the 10 % and 60 % pools."""
+    import subprocess
     import oracle
-    import workloads as W
-    lw = [oracle.LayerWeights(cfg.qtypes(l), cfg.H, cfg.I, cfg.down_k(l), cfg.E, cfg.k, W.router(cfg, l),
-                              W.zipf_bias(cfg, l), (lambda l_: (lambda e: experts[(l_, e)]))(l), cfg.n_shared)
-          for l in range(n_layers)]
-    xs = [W.token(cfg, 99, t) for t in range(n_tokens)]
-    t0 = time.perf_counter()
-    for x in xs:
-        oracle.stack_token(lw, x)
-    el = time.perf_counter() - t0
-    per_token_layer = el / (n_tokens * n_layers)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=round(1.0 / (per_token_layer * cfg.n_layers), 4), unit="tokens/s", cores=threads,
-                kind="oracle",
-                sample=f"{n_tokens} single-token decodes through {n_layers} of {cfg.n_layers} layers "
-                       f"(fp64 oracle, {el:.1f} s), scaled to {cfg.n_layers} layers")
+    res = {}
+    for nth in (1, threads):
+        env = dict(os.environ, OMP_NUM_THREADS=str(nth))
+        code = _CPU_SNIPPET.format(root=ROOT, n_tok=n_tokens if nth > 1 else max(2, n_tokens // 16),
+                                   n_lay=n_layers)
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=900)
+        if r.returncode != 0:
+            raise RuntimeError(f"oracle timing failed: {r.stderr[-2000:]}")
+        res[nth] = json.loads(r.stdout.strip().splitlines()[-1])
+    # LRU simulation over a trace of the C4 size
+    rng = np.random.default_rng(4)
+    p = np.arange(1, 129, dtype=np.float64) ** -1.1
+    p /= p.sum()
+    perms = [rng.permutation(128) for _ in range(48)]
+    LL, EE = [], []
+    for s_ in range(512):
+        for l in range(48):
+            e = np.unique(perms[l][rng.choice(128, 8, replace=False, p=p)])
+            LL.append(np.full(len(e), l, np.int32))
+            EE.append(e.astype(np.int32))
+    LL, EE = np.concatenate(LL), np.concatenate(EE)
+    lru_s = {}
+    for name, slots in (("pool_10pct_613_slots", 613), ("pool_60pct_3685_slots", 3685)):
+        t0 = time.perf_counter()
+        oracle.lru([slots], [0] * 48, LL, EE)
+        lru_s[name] = round(time.perf_counter() - t0, 3)
+    all_c = res[threads]
+    tps = 1.0 / (all_c["c2_s_per_token_layer"] * 48)
+    return dict(value=round(tps, 4), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{n_tokens} single-token decodes through {n_layers} of the 48 layers of the Qwen3-30B-A3B-"
+                       f"shaped Q4_K stack (fp64 oracle, {threads} threads), scaled to 48 layers; the oracle "
+                       f"handles each token on its own, so T=8 costs 8 tokens",
+                cpu_model=_cpu_model(), nproc=os.cpu_count(),
+                single_thread_tokens_per_s=round(1.0 / (res[1]["c2_s_per_token_layer"] * 48), 4),
+                batch8_tokens_per_s=round(tps, 4),
+                c1_tokens_per_s={"all_cores": round(all_c["c1_tokens_per_s"], 1),
+                                 "single_thread": round(res[1]["c1_tokens_per_s"], 1)},
+                lru_simulation_s={"lookups": int(len(LL)), **lru_s})
+
+
+def roof_hbm(tm, traffic=None, kernel="expert FFN (k_gate_up + k_down of moe_layer_ffn)"):
+    return {"bound": "hbm", "achieved": round(tm["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(tm["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
+            "bytes_per_launch": round(tm["bytes_per_launch"]), "us_per_launch": round(tm["ffn_us"], 3),
+            "launches": tm["launches"]}
+
+
+def resident_leg(st, T: int, args, seed: int, traffic=None, mfma=False):
+    """Throughput (graph replays) and the per-layer FFN roofline of one stack at batch T."""
+    tps, ms, pct = throughput(st, T, args.steps, args.warmup, st.layers[0].H, seed=seed)
+    tm = ffn_timing(st, T, args.timing_steps, st.layers[0].H, seed=seed)
+    leg = {"value": round(tps, 2), "unit": "tokens/s", "ms_per_step": round(ms, 4), "step_ms_percentiles": pct,
+           "roofline": roof_hbm(tm, traffic, "expert FFN (k_gate_up_mfma + k_down_mfma)" if mfma else
+                                "expert FFN (k_gate_up + k_down of moe_layer_ffn)"),
+           "route_us_per_layer": round(tm["route_us"], 3)}
+    if mfma:
+        # the matrix cores: the pairs' algorithmic flops (2 per multiply-add of gate, up and
+        # down) per FFN launch, against the fp16 dense peak the kernels issue on
+        leg["mfma"] = {"bound": "mfma", "achieved": round(tm["tflops"], 2), "peak": MFMA_FP16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tm["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4),
+                       "flop_per_launch": round(tm["flop_per_launch"])}
+    log(f"T={T}: {tps:.1f} tok/s, {ms:.3f} ms/step {pct}; FFN {tm['ffn_us']:.2f} us/launch "
+        f"{tm['gbps']:.0f} GB/s ({tm['bytes_per_launch'] / 1e6:.2f} MB), route {tm['route_us']:.2f} us")
+    return leg, tm
 
 
 def main():
@@ -403,13 +569,15 @@ def main():
     ap.add_argument("--timing-steps", type=int, default=10)
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--cpu-layers", type=int, default=8)
     ap.add_argument("--cache-steps", type=int, default=512, help="decode steps of each slot-pool leg (0: none)")
     ap.add_argument("--prompt-batch", type=int, default=128, help="tokens of the prompt-sized batch leg (0: none)")
     ap.add_argument("--prompt-steps", type=int, default=10)
-    ap.add_argument("--zipf", action="store_true", help="Zipf(1.1) router bias on the resident stack "
-                                                         "(the skewed T=32 workload)")
+    ap.add_argument("--zipf-t32", type=int, default=1, help="the Zipf-biased T=32 leg (MFMA path); 0: none")
+    ap.add_argument("--zero-mean", type=int, default=1, help="the zero-mean-field stack at T=8; 0: none")
+    ap.add_argument("--mixed", type=int, default=1, help="the mixed Q4_K/Q6_K shared-expert stack legs; 0: none")
+    ap.add_argument("--zipf", action="store_true", help="Zipf(1.1) router bias on the headline stack")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB three times (reads and writes MIB MiB "
                          "each), the reference dispatch for scaling HBM byte counters")
@@ -443,17 +611,24 @@ def main():
         cfg = cfg.with_(zipf_s=1.1)
     log(f"building {cfg.name}: {cfg.n_layers} layers x {cfg.E} experts x {cfg.expert_bytes(0)} B")
     t0 = time.time()
-    st, kept, specs, packed = build_stack(cfg, args.threads, args.cpu_layers if args.cpu_baseline else 0,
-                                          T_max=max(8, args.batch, args.also_batch))
+    Tmax = max(8, args.batch, args.also_batch, 32 if args.zipf_t32 else 0)
+    st, kept, specs, packed = build_stack(cfg, args.threads, 0, T_max=Tmax)
     log(f"stack resident in {time.time() - t0:.1f} s")
 
     res = {}
     for T in [args.batch] + ([args.also_batch] if args.also_batch and args.also_batch != args.batch else []):
-        tps, ms = throughput(st, T, args.steps, args.warmup, cfg.H, seed=T)
-        tm = ffn_timing(st, T, args.timing_steps, cfg.H, seed=T)
-        res[T] = (tps, ms, tm)
-        log(f"T={T}: {tps:.1f} tok/s, {ms:.3f} ms/step; FFN {tm['ffn_us']:.2f} us/launch "
-            f"{tm['gbps']:.0f} GB/s ({tm['bytes_per_launch'] / 1e6:.2f} MB), route {tm['route_us']:.2f} us")
+        res[T] = resident_leg(st, T, args, seed=T, traffic=measured_traffic(T))
+
+    zipf32 = None
+    if args.zipf_t32:
+        # the same stack at T=32 with the Zipf(1.1) router bias (skewed expert loads, MFMA path)
+        zc = cfg.with_(zipf_s=1.1, T=32)
+        saved = st.biases
+        st.biases = [torch.from_numpy(W.zipf_bias(zc, l)).to(st.device) for l in range(cfg.n_layers)]
+        zipf32, _ = resident_leg(st, 32, args, seed=32, mfma=True)
+        zipf32["config"] = {"workload": f"the same {cfg.n_layers}-layer Q4_K stack at T=32, Zipf(1.1) router bias "
+                                        f"(per-layer permutation), fresh N(0,1) states every step"}
+        st.biases = saved
 
     prompt = None
     if args.prompt_batch:
@@ -463,40 +638,67 @@ def main():
     cache = None
     if args.cache_steps:
         cache = cache_leg(cfg, specs, packed, (0.1, 0.6), args.cache_steps, seed=4)
+    del st, packed, specs
+    torch.cuda.empty_cache()
+
+    zero_mean = None
+    if args.zero_mean:
+        zcfg = W.qwen3_30b_a3b_q4k(T=8, n_layers=args.layers).with_(zero_mean=True)
+        log(f"building {zcfg.name} (zero-mean fields)")
+        zst, _, _, zpacked = build_stack(zcfg, args.threads, 0, T_max=8)
+        del zpacked
+        zero_mean, _ = resident_leg(zst, 8, args, seed=88)
+        zero_mean["config"] = {"workload": f"{zcfg.n_layers}-layer Qwen3-30B-A3B-shaped Q4_K stack with zero-mean "
+                                           f"weights (dmin = 7.5 d), T=8: states keep no common offset, so the "
+                                           f"8 tokens route apart"}
+        del zst
+        torch.cuda.empty_cache()
+
+    mixed = None
+    if args.mixed:
+        mcfg = W.mixed_shared_q4k_q6k(T=1)
+        log(f"building {mcfg.name}")
+        mst, _, mspecs, mpacked = build_stack(mcfg, args.threads, 0, T_max=8)
+        mixed = {}
+        for T in (1, 4):
+            mixed[f"t{T}"], _ = resident_leg(mst, T, args, seed=100 + T)
+        mixed["config"] = {"workload": f"{mcfg.n_layers} layers, H=2048, 64 routed (top-2) + 2 shared experts, "
+                                       f"I=1408 (down rows padded to 1536), layers 0-11 Q4_K, 12-23 Q6_K, all "
+                                       f"resident; FFN bytes per launch include the two shared experts"}
+        del mst
+        torch.cuda.empty_cache()
+        if args.cache_steps:
+            mixed["cache"] = cache_leg_groups(mcfg, mspecs, mpacked, (0.1, 0.6), min(args.cache_steps, 256), 4,
+                                              seed=9)
+        del mpacked
 
     cpu = None
     if args.cpu_baseline:
-        cpu = cpu_baseline(cfg, kept, args.cpu_tokens, args.cpu_layers)
+        cpu = cpu_baseline(args.cpu_tokens, args.cpu_layers, args.threads)
         log(f"cpu baseline {cpu['value']:.4f} tok/s ({cpu['sample']})")
 
-    def roof(tm, T):
-        return {"bound": "hbm", "achieved": round(tm["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(tm["gbps"] / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(T),
-                "kernel": "expert FFN (k_gate_up + k_down of moe_layer_ffn)",
-                "bytes_per_launch": round(tm["bytes_per_launch"]), "us_per_launch": round(tm["ffn_us"], 3),
-                "launches": tm["launches"]}
-
     T = args.batch
-    tps, ms, tm = res[T]
+    head, tm = res[T]
     out = {
-        "metric": METRIC, "value": round(tps, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "step_ms_percentiles": head["step_ms_percentiles"],
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "q4_k weights x int8-piece activations, fp32 scales/accumulate",
         "data": "synthetic (seeded Q4_K fields, N(0,1) states, N(0,0.02^2) router)",
         "config": {"workload": f"qwen3-30b-a3b-shaped Q4_K MoE stack: {cfg.n_layers} layers, H=2048, E=128, "
                                f"top-8, I=768, T={T}, all experts resident",
                    "layers": cfg.n_layers, "batch": T, "expert_bytes": cfg.expert_bytes(0)},
-        "roofline": roof(tm, T),
-        "route_us_per_layer": round(tm["route_us"], 3),
+        "roofline": head["roofline"],
+        "route_us_per_layer": head["route_us_per_layer"],
         "cpu_baseline": cpu,
-        "cache": cache,
-        "prompt": prompt,
     }
     if args.also_batch and args.also_batch in res and args.also_batch != T:
-        t2, m2, tm2 = res[args.also_batch]
-        out[f"batch{args.also_batch}"] = {"value": round(t2, 2), "unit": "tokens/s", "ms_per_step": round(m2, 4),
-                                          "roofline": roof(tm2, args.also_batch),
-                                          "route_us_per_layer": round(tm2["route_us"], 3)}
+        out[f"batch{args.also_batch}"] = res[args.also_batch][0]
+    out["zero_mean_batch8"] = zero_mean
+    out["zipf_batch32"] = zipf32
+    out["mixed_shared"] = mixed
+    out["prompt"] = prompt
+    out["cache"] = cache
     print(json.dumps(out), flush=True)
 
 
