@@ -340,7 +340,37 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
             }
         legs.append(leg)
         log(f"cache {f:.0%}: {legs[-1]}")
-    return {"workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
+    # placement (T4 report, "Two ways to run"): the 60 % budget spent FIT-style,
+    # whole layers resident and a pool of 10 % of the expert bytes for the
+    # rest, against the 60 % pool above (every layer cached)
+    fit = None
+    st_, state, slots = moe.moe_placement_plan([desc], [0] * cfg.n_layers, cfg.E, int(0.6 * total), int(0.1 * total),
+                                               cfg.k, moe.MOE_PLACE_FIT)
+    if st_ == 0:
+        cs = CachedStack(zspecs, packed, slots, T_max=1, device_lookup=True, resident=[x < 0 for x in state])
+        hb = xs[0].clone()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs.step(hb)
+        torch.cuda.synchronize()
+        cs.cache.reset_stats()
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            hb.copy_(xs[s_])
+            graph.replay()
+        torch.cuda.synchronize()
+        el_f = time.perf_counter() - t0
+        fs = cs.cache.stats()
+        del graph
+        cs.close()
+        fit = {"vram_fraction": 0.6, "cache_fraction": 0.1, "resident_layers": int((state < 0).sum()),
+               "slots": int(slots[0]), "tokens_per_s": round(steps / el_f, 2),
+               "hit_rate_cached_layers": round(fs["hits"] / max(1, fs["lookups"]), 4),
+               "misses_per_token": round(fs["misses"] / steps, 2)}
+        log(f"placement FIT: {fit}")
+    return {"placement_fit": fit,
+            "workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
                         f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
                         f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
                         f"copies on the device, eager and as a captured HIP graph; prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "

@@ -249,6 +249,34 @@ moe_status moe_cache_plan(const moe_expert_desc *groups, const int32_t *layers_p
                           int32_t n_groups, uint64_t budget_bytes, int32_t top_k,
                           int32_t *slots_out);
 
+/* Placement of a stack's experts in a VRAM budget (T4 MoE-cache report,
+ * section "Two ways to run: automatic placement vs manual takeover"):
+ *   MOE_PLACE_FIT         layer granularity, as --fit with a cache: the
+ *                         cache reserves cache_bytes, layers are made
+ *                         resident whole in layer order while they fit in
+ *                         the rest of vram_bytes (a layer that does not fit
+ *                         is skipped, a later smaller one may still fit), and
+ *                         the layers left over are served by the cache, whose
+ *                         slots are planned over them alone;
+ *   MOE_PLACE_ALL_CACHED  expert granularity, as --cpu-moe with a cache:
+ *                         no layer resident, all of vram_bytes to the cache.
+ *   groups [n_groups]; layer_group [n_layers] the group of each layer (>= 0);
+ *   E experts per layer; vram_bytes the budget for expert bytes (resident
+ *   layers plus pools); cache_bytes the pool budget (FIT only); top_k the
+ *   slot floor per group.
+ *   layer_state [n_layers] out: the group g of a cached layer, or -(g+1) for
+ *   a resident one -- the layer_group argument of moe_cache_create;
+ *   slots_out [n_groups] out (0 for a group with no cached layer).
+ * MOE_ERR_BUDGET when a group with cached layers gets fewer than top_k
+ * slots (the outputs are still filled); MOE_ERR_ARG for bad arguments.
+ * (Computing missed experts on the host CPU, as --cpu-moe without a cache
+ * does, is not offered: every step of the path runs in this library's GPU
+ * kernels.)  Pure host function. */
+enum { MOE_PLACE_FIT = 1, MOE_PLACE_ALL_CACHED = 2 };
+moe_status moe_placement_plan(const moe_expert_desc *groups, int32_t n_groups, const int32_t *layer_group,
+                              int32_t n_layers, int32_t E, uint64_t vram_bytes, uint64_t cache_bytes,
+                              int32_t top_k, int32_t mode, int32_t *layer_state, int32_t *slots_out);
+
 typedef struct moe_cache moe_cache;
 
 /* Create a cache.
@@ -260,8 +288,11 @@ typedef struct moe_cache moe_cache;
  *   T4 MoE-cache report, section "Size your experts before configuring":
  *   a group below the floor is left out with a warning; only a budget that
  *   disables every group is refused).  MOE_ERR_BUDGET when every group has 0
- *   slots, MOE_ERR_ARG for a negative count.
- *   layer_group [n_layers] (group of each layer), host_experts [n_layers * E]
+ *   slots while some layer asks for caching, MOE_ERR_ARG for a negative
+ *   count.
+ *   layer_group [n_layers]: the group g of each layer, or -(g+1) for a
+ *   layer whose experts stay resident (shape of group g; see
+ *   moe_placement_plan), host_experts [n_layers * E]
  *   pinned host addresses of each expert in the slot layout (the pinned
  *   memory stays owned by the caller and must outlive the cache).  Allocates
  *   one device pool per group (hipMalloc) and one device pointer table per

@@ -16,7 +16,10 @@ from ._lib import (  # noqa: F401
     MoeError,
     lib,
     lib_path,
+    MOE_PLACE_ALL_CACHED,
+    MOE_PLACE_FIT,
     moe_cache_plan,
+    moe_placement_plan,
     moe_down_k,
     moe_expert_bytes,
     moe_expert_ffn,

@@ -17,7 +17,7 @@ EXPORTED = [
     "moe_rmsnorm", "moe_route_topk", "moe_group_tokens", "moe_workspace_bytes",
     "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
     "moe_layer_forward_noalloc",
-    "moe_cache_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
+    "moe_cache_plan", "moe_placement_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
     "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_prefetch_device", "moe_cache_trace_read",
 ]
@@ -116,6 +116,7 @@ def lib() -> ctypes.CDLL:
         "moe_layer_forward": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_layer_forward_noalloc": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P]),
         "moe_cache_plan": (i32, [D, P, i32, u64, i32, P]),
+        "moe_placement_plan": (i32, [D, i32, P, i32, i32, u64, u64, i32, i32, P, P]),
         "moe_cache_create": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(P)]),
         "moe_cache_create_ex": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(CacheBackend), ctypes.POINTER(P)]),
         "moe_cache_lookup": (i32, [P, i32, i32, i32, P, P, P, P, P, P, P]),
@@ -267,6 +268,25 @@ def moe_cache_plan(descs: Sequence, layers_per_group: Sequence[int], budget_byte
     if st not in (0, -4):
         _check(st)
     return st, slots
+
+
+MOE_PLACE_FIT, MOE_PLACE_ALL_CACHED = 1, 2
+
+
+def moe_placement_plan(descs: Sequence, layer_group: Sequence[int], E: int, vram_bytes: int, cache_bytes: int,
+                       top_k: int, mode: int):
+    """Returns (status, layer_state, slots); status is 0 or the MOE_ERR_BUDGET
+    code.  layer_state[l] = g (cached) or -(g+1) (resident)."""
+    n = len(descs)
+    arr = (ExpertDesc * n)(*[_desc(d) for d in descs])
+    lg = np.ascontiguousarray(layer_group, np.int32)
+    state = np.zeros(lg.shape[0], np.int32)
+    slots = np.zeros(n, np.int32)
+    st = lib().moe_placement_plan(arr, n, lg.ctypes.data, lg.shape[0], E, int(vram_bytes), int(cache_bytes), top_k,
+                                  mode, state.ctypes.data, slots.ctypes.data)
+    if st not in (0, -4):
+        _check(st)
+    return st, state, slots
 
 
 class Cache:

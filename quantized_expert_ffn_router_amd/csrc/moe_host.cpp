@@ -142,6 +142,67 @@ moe_status moe_cache_plan(const moe_expert_desc *groups, const int32_t *layers_p
     return MOE_OK;
 }
 
+moe_status moe_placement_plan(const moe_expert_desc *groups, int32_t n_groups, const int32_t *layer_group,
+                              int32_t n_layers, int32_t E, uint64_t vram_bytes, uint64_t cache_bytes,
+                              int32_t top_k, int32_t mode, int32_t *layer_state, int32_t *slots_out)
+{
+    if (!groups || !layer_group || !layer_state || !slots_out || n_groups < 1 || n_layers < 1 || E < 1 || top_k < 1 ||
+        (mode != MOE_PLACE_FIT && mode != MOE_PLACE_ALL_CACHED) || (mode == MOE_PLACE_FIT && cache_bytes > vram_bytes)) {
+        set_error("moe_placement_plan: bad argument");
+        return MOE_ERR_ARG;
+    }
+    std::vector<uint64_t> layer_bytes(n_layers);
+    for (int l = 0; l < n_layers; l++) {
+        ExpertGeom eg;
+        const int g = layer_group[l];
+        if (g < 0 || g >= n_groups || !geom(groups[g], &eg)) {
+            set_error("moe_placement_plan: layer %d has a bad group", l);
+            return MOE_ERR_ARG;
+        }
+        layer_bytes[l] = (uint64_t)eg.bytes * (uint64_t)E;
+    }
+    // resident layers first (FIT: whole layers, in layer order, first fit)
+    uint64_t avail = mode == MOE_PLACE_FIT ? vram_bytes - cache_bytes : 0;
+    const uint64_t pool = mode == MOE_PLACE_FIT ? cache_bytes : vram_bytes;
+    std::vector<int32_t> cached(n_groups, 0);
+    for (int l = 0; l < n_layers; l++) {
+        const int g = layer_group[l];
+        if (mode == MOE_PLACE_FIT && layer_bytes[l] <= avail) {
+            avail -= layer_bytes[l];
+            layer_state[l] = -(g + 1);
+        } else {
+            layer_state[l] = g;
+            cached[g]++;
+        }
+    }
+    // the cache's slots over the cached layers alone (the planner's formula)
+    unsigned __int128 denom = 0;
+    for (int g = 0; g < n_groups; g++) {
+        ExpertGeom eg;
+        geom(groups[g], &eg);
+        denom += (unsigned __int128)eg.bytes * (uint64_t)cached[g];
+    }
+    int short_group = -1;
+    for (int g = 0; g < n_groups; g++) {
+        long long sl = 0;
+        if (cached[g] > 0) {
+            sl = (long long)(((unsigned __int128)pool * (uint64_t)cached[g]) / denom) - 1;
+            if (sl < top_k) {
+                sl = 0;
+                short_group = g;
+            }
+            if (sl > 0x7fffffff) sl = 0x7fffffff;
+        }
+        slots_out[g] = (int32_t)sl;
+    }
+    if (short_group >= 0) {
+        set_error("moe_placement_plan: a pool of %llu bytes leaves group %d (%d cached layers) below %d slots",
+                  (unsigned long long)pool, short_group, cached[short_group], top_k);
+        return MOE_ERR_BUDGET;
+    }
+    return MOE_OK;
+}
+
 }  // extern "C"
 
 struct moe_cache {
@@ -149,7 +210,8 @@ struct moe_cache {
         moe_expert_desc desc;
         size_t slot_bytes = 0;
         int n_slots = 0;                // 0: below the budget floor, its layers resident
-        uint8_t *pool = nullptr;        // the slots; a resident group: its layers' experts, layer-major
+        uint8_t *pool = nullptr;        // the slots
+        uint8_t *res = nullptr;         // the group's resident layers' experts, layer-major
         std::vector<int64_t> slot_key;  // key = layer*E + expert, -1 free
         std::vector<int> prev, next;    // recency list over slots, head = most recent
         int head = -1, tail = -1, next_free = 0;
@@ -166,8 +228,9 @@ struct moe_cache {
     bool custom = false;                 // caller-supplied (synchronous) backend
     moe_cache_backend be{};
     std::vector<Group> groups;
-    std::vector<int> layer_group;
-    std::vector<int> layer_rank;         // position of a layer among its group's layers
+    std::vector<int> layer_group;        // group of each layer (its shape, resident or not)
+    std::vector<char> resident;          // the layer's experts stay resident, no lookups
+    std::vector<int> layer_rank;         // position of a resident layer among its group's resident layers
     std::vector<const void *> host;      // [L*E] pinned sources
     std::vector<int> where;              // [L*E] slot of a key, -1 absent
     const void **htab = nullptr;         // host [L*E] slot addresses (pinned with the default backend)
@@ -249,8 +312,10 @@ void destroy(moe_cache *c)
         (void)hipSetDevice(c->device);
         (void)hipDeviceSynchronize();
     }
-    for (auto &g : c->groups)
+    for (auto &g : c->groups) {
         if (g.pool) c->be.release(c->be.user, g.pool);
+        if (g.res) c->be.release(c->be.user, g.res);
+    }
     if (c->dtab) c->be.release(c->be.user, c->dtab);
     if (c->htab) {
         if (c->custom) free((void *)c->htab);
@@ -271,7 +336,7 @@ void destroy(moe_cache *c)
     delete c;
 }
 
-bool resident_layer(const moe_cache *c, int layer) { return c->groups[c->layer_group[layer]].n_slots == 0; }
+bool resident_layer(const moe_cache *c, int layer) { return c->resident[layer] != 0; }
 
 // A prefetch's copies run beside the lookups that follow it.  The slots it
 // filled were touched last by the prefetch, so a later lookup can take one
@@ -392,17 +457,19 @@ moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, 
         return MOE_ERR_ARG;
     }
     *out = nullptr;
-    bool any = false;
+    bool any = false, wants_cache = false;
     for (int g = 0; g < n_groups; g++) {
         if (slots[g] < 0) { set_error("group %d: negative slot count %d", g, slots[g]); return MOE_ERR_ARG; }
         any = any || slots[g] > 0;
     }
-    if (!any) {
+    for (int l = 0; l < n_layers; l++) {
+        const int g = layer_group[l] < 0 ? -layer_group[l] - 1 : layer_group[l];
+        if (g < 0 || g >= n_groups) { set_error("layer %d: bad group", l); return MOE_ERR_ARG; }
+        wants_cache = wants_cache || layer_group[l] >= 0;
+    }
+    if (!any && wants_cache) {
         set_error("every group has 0 slots (the budget is below the floor of each)");
         return MOE_ERR_BUDGET;
-    }
-    for (int l = 0; l < n_layers; l++) {
-        if (layer_group[l] < 0 || layer_group[l] >= n_groups) { set_error("layer %d: bad group", l); return MOE_ERR_ARG; }
     }
     for (size_t i = 0; i < (size_t)n_layers * E; i++) {
         if (!host_experts[i]) { set_error("host expert %zu is null", i); return MOE_ERR_ARG; }
@@ -413,10 +480,18 @@ moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, 
     c->custom = backend != nullptr;
     c->be = backend ? *backend : moe_cache_backend{nullptr, hip_alloc, hip_release, nullptr};
     if (!c->custom && hipGetDevice(&c->device) != hipSuccess) { delete c; set_error("hipGetDevice failed"); return MOE_ERR_HIP; }
-    c->layer_group.assign(layer_group, layer_group + n_layers);
+    // a layer is resident when asked to be (negative group) or when its group
+    // has no slots; layer_rank: its position among its group's resident layers
+    c->layer_group.assign(n_layers, 0);
+    c->resident.assign(n_layers, 0);
     c->layer_rank.assign(n_layers, 0);
     std::vector<int> per_group(n_groups, 0);
-    for (int l = 0; l < n_layers; l++) c->layer_rank[l] = per_group[layer_group[l]]++;
+    for (int l = 0; l < n_layers; l++) {
+        const int g = layer_group[l] < 0 ? -layer_group[l] - 1 : layer_group[l];
+        c->layer_group[l] = g;
+        c->resident[l] = layer_group[l] < 0 || slots[g] == 0;
+        if (c->resident[l]) c->layer_rank[l] = per_group[g]++;
+    }
     c->groups.resize(n_groups);
     for (int g = 0; g < n_groups; g++) {
         ExpertGeom eg;
@@ -428,15 +503,18 @@ moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, 
         G.slot_key.assign(G.n_slots, -1);
         G.prev.assign(G.n_slots, -1);
         G.next.assign(G.n_slots, -1);
-        const size_t n = G.n_slots > 0 ? (size_t)G.n_slots : (size_t)per_group[g] * E;
-        if (n == 0) continue;  // a resident group without layers
-        void *p = nullptr;
-        if (c->be.alloc(c->be.user, G.slot_bytes * n, &p) != 0 || !p) {
-            destroy(c);
-            set_error("allocation of %zu bytes for pool %d failed", G.slot_bytes * n, g);
-            return MOE_ERR_HIP;
+        for (int pass = 0; pass < 2; pass++) {
+            // the slots, then the group's resident layers' experts
+            const size_t n = pass == 0 ? (size_t)G.n_slots : (size_t)per_group[g] * E;
+            if (n == 0) continue;
+            void *p = nullptr;
+            if (c->be.alloc(c->be.user, G.slot_bytes * n, &p) != 0 || !p) {
+                destroy(c);
+                set_error("allocation of %zu bytes for group %d failed", G.slot_bytes * n, g);
+                return MOE_ERR_HIP;
+            }
+            (pass == 0 ? G.pool : G.res) = (uint8_t *)p;
         }
-        G.pool = (uint8_t *)p;
     }
     c->host.assign(host_experts, host_experts + (size_t)n_layers * E);
     c->where.assign((size_t)n_layers * E, -1);
@@ -474,11 +552,11 @@ moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, 
     int n_res = 0;
     size_t res_bytes = 0;
     for (int l = 0; l < n_layers; l++) {
-        auto &G = c->groups[layer_group[l]];
-        if (G.n_slots > 0) continue;
+        auto &G = c->groups[c->layer_group[l]];
+        if (!c->resident[l]) continue;
         n_res++;
         for (int e = 0; e < E; e++) {
-            uint8_t *dst = G.pool + ((size_t)c->layer_rank[l] * E + e) * G.slot_bytes;
+            uint8_t *dst = G.res + ((size_t)c->layer_rank[l] * E + e) * G.slot_bytes;
             const void *src = c->host[(size_t)l * E + e];
             const bool cp = c->custom ? c->be.copy(c->be.user, dst, src, G.slot_bytes) == 0
                                       : hipMemcpy(dst, src, G.slot_bytes, hipMemcpyHostToDevice) == hipSuccess;
@@ -498,8 +576,8 @@ moe_status moe_cache_create_ex(const moe_expert_desc *groups, int32_t n_groups, 
     if (n_res) {
         char msg[256];
         snprintf(msg, sizeof msg,
-                 "moe cache: %d of %d layers belong to groups below the budget floor; their experts stay resident "
-                 "(%zu bytes) and are not cached", n_res, n_layers, res_bytes);
+                 "moe cache: %d of %d layers keep their experts resident (%zu bytes) and are not cached (placed "
+                 "resident, or their group is below the budget floor)", n_res, n_layers, res_bytes);
         fprintf(stderr, "%s\n", msg);
         set_error("%s", msg);
     }
@@ -535,7 +613,7 @@ moe_status moe_cache_lookup(moe_cache *c, int32_t layer, int32_t T, int32_t k, c
         if (sel[e]) experts_out[n++] = e;
     *n_out = n;
     auto &G = c->groups[c->layer_group[layer]];
-    if (G.n_slots == 0) {  // resident layer
+    if (resident_layer(c, layer)) {
         for (int i = 0; i < n; i++) {
             slot_out[i] = -1;
             hit_out[i] = 1;

@@ -166,7 +166,9 @@ class CachedStack:
 
     def __init__(self, layers: Sequence[LayerSpec], packed: Sequence[torch.Tensor], slots: Sequence[int],
                  T_max: int = 8, device: str = "cuda", eps: float = 1e-6, device_lookup: bool = False,
-                 trace_capacity: int = 0, prefetch_depth: int = 0):
+                 trace_capacity: int = 0, prefetch_depth: int = 0, resident: Optional[Sequence[bool]] = None):
+        """resident[l] (e.g. from moe_placement_plan) keeps layer l's experts
+        resident in HBM, outside the cache."""
         if prefetch_depth and not device_lookup:
             raise ValueError("prefetch_depth needs device_lookup")
         self.prefetch_depth = int(prefetch_depth)
@@ -194,7 +196,9 @@ class CachedStack:
             base = self.packed[li].data_ptr()
             host_ptrs += [base + e * self.expert_bytes[li] for e in range(s.E)]
         self.slots = list(slots)
-        self.cache = L.Cache(self.group_descs, self.slots, self.layer_group, self.E, host_ptrs)
+        self.resident = [bool(r) for r in resident] if resident is not None else [False] * len(self.layers)
+        state = [-(g + 1) if r else g for g, r in zip(self.layer_group, self.resident)]
+        self.cache = L.Cache(self.group_descs, self.slots, state, self.E, host_ptrs)
         # shared experts, routers and biases resident
         self.shared: List[Optional[torch.Tensor]] = []
         self.shared_tabs: List[Optional[torch.Tensor]] = []

@@ -240,3 +240,64 @@ def test_failed_upload_rolls_back_from_the_failing_miss(fail_at):
     ref, resident = _oracle_state(s.slots, lg, np.array(LL, np.int32), np.array(EE, np.int32))
     assert np.array_equal(np.concatenate(got), ref.hit)
     s.check_tables(resident)
+
+
+def test_placement_plan_fit_and_all_cached():
+    """The placement planner (T4 MoE-cache report, "Two ways to run"): FIT
+    reserves the cache budget, makes whole layers resident in layer order
+    while they fit (first fit), and plans the slots over the layers left;
+    ALL_CACHED gives every layer to the cache, as moe_cache_plan does."""
+    descs = [moe.ExpertDesc.of((Q8_0,) * 3, 256, 64), moe.ExpertDesc.of((Q4_K,) * 3, 256, 64)]
+    eb = [moe.moe_expert_bytes(d) for d in descs]
+    assert eb == [104448, 55296]
+    lg = [0, 1, 0, 1, 1]
+    E, k = 8, 2
+    layer = [E * eb[g] for g in lg]  # 835,584 / 442,368 bytes per layer
+    # FIT: 2,000,000 bytes of VRAM, 400,000 for the cache: 1,600,000 left for layers.
+    # layer 0 (835,584) fits -> 764,416 left; layer 1 (442,368) fits -> 322,048;
+    # layer 2 (835,584) no; layer 3 (442,368) no; layer 4 no.
+    # cached: group 0 one layer, group 1 two layers; denominator 104,448 + 2 * 55,296 = 215,040
+    # group 0: floor(400,000 * 1 / 215,040) - 1 = 0 -> below k=2: refused (outputs still filled);
+    # group 1: floor(400,000 * 2 / 215,040) - 1 = 3 - 1 = 2
+    st, state, slots = moe.moe_placement_plan(descs, lg, E, 2_000_000, 400_000, k, moe.MOE_PLACE_FIT)
+    assert st == -4 and state.tolist() == [-1, -2, 0, 1, 1] and slots.tolist() == [0, 2]
+    st, state, slots = moe.moe_placement_plan(descs, lg, E, 3_000_000, 1_500_000, k, moe.MOE_PLACE_FIT)
+    # 1,500,000 for layers: layer 0 fits (664,416 left), layer 1 fits (222,048), the rest no
+    assert st == 0 and state.tolist() == [-1, -2, 0, 1, 1]
+    # group 0: floor(1,500,000 / 215,040) - 1 = 6 - 1 = 5; group 1: floor(3,000,000 / 215,040) - 1 = 13 - 1 = 12
+    assert slots.tolist() == [5, 12]
+    # every layer fits: all resident, no slots
+    st, state, slots = moe.moe_placement_plan(descs, lg, E, 10_000_000, 100, k, moe.MOE_PLACE_FIT)
+    assert st == 0 and (state < 0).all() and slots.tolist() == [0, 0]
+    # ALL_CACHED: the plain planner over all layers
+    st, state, slots = moe.moe_placement_plan(descs, lg, E, 3_000_000, 0, k, moe.MOE_PLACE_ALL_CACHED)
+    st_p, slots_p = moe.moe_cache_plan(descs, [2, 3], 3_000_000, k)
+    assert st == 0 and state.tolist() == lg and slots.tolist() == slots_p.tolist()
+    with pytest.raises(moe.MoeError):
+        moe.moe_placement_plan(descs, lg, E, 100, 200, k, moe.MOE_PLACE_FIT)  # cache above the budget
+
+
+def test_resident_layers_beside_cached_layers():
+    """Layers placed resident (group entry -(g+1)) keep all their experts and
+    make no lookups; the cached layers of the same group follow the oracle
+    LRU over their own lookups."""
+    rng = np.random.default_rng(3)
+    lg = [0, 0, 0, 0]
+    E, T, k = 10, 2, 2
+    s = Setup([(Q4_K, 256, 64)], [-1, 0, -1, 0], E, [5], seed=5)
+    LL, EE, got = [], [], []
+    for l, ids in _random_steps(rng, 8, 4, E, T, k):
+        ex, slot, hit, vl, ve = s.cache.lookup(l, T, k, ids.ravel())
+        s.cache.upload(l, None)
+        if l in (0, 2):
+            assert hit.all() and (slot == -1).all()
+            continue
+        LL += [l] * len(ex)
+        EE += ex.tolist()
+        got.append(hit)
+    ref, resident = _oracle_state([5], lg, np.array(LL, np.int32), np.array(EE, np.int32))
+    assert np.array_equal(np.concatenate(got), ref.hit)
+    st = s.cache.stats()
+    assert st["lookups"] == len(LL) and st["hits"] == int(ref.hit.sum())
+    resident |= {(l, e) for l in (0, 2) for e in range(E)}
+    s.check_tables(resident)

@@ -38,7 +38,7 @@ def _groups(cfg, n_layers):
     return descs, ebytes, per_group, layer_group
 
 
-def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0, slots=None):
+def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0, slots=None, resident=None):
     """slots=None: the planner's slots for `fraction` of the routed expert
     bytes (checked against the oracle planner); else the given slots, where
     a group at 0 slots keeps its layers resident."""
@@ -53,12 +53,13 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
         rc, oslots = oracle.cache_plan(ebytes, per_group, budget, cfg.k)
         assert st == 0 and rc == 0 and np.array_equal(slots, oslots), (slots, oslots)
     slots = np.asarray(slots, np.int32)
-    cached = [slots[layer_group[l]] > 0 for l in range(n_layers)]
+    resident = list(resident) if resident is not None else [False] * n_layers
+    cached = [slots[layer_group[l]] > 0 and not resident[l] for l in range(n_layers)]
     _say(cfg.name, dict(layers=n_layers, steps=steps, T=T, fraction=fraction, slots=list(slots), device=device_lookup))
     packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
     cap = steps * n_layers * T * cfg.k * (2 if prefetch_depth else 1)
     cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=device_lookup, trace_capacity=cap,
-                     prefetch_depth=prefetch_depth)
+                     prefetch_depth=prefetch_depth, resident=resident)
     targets = [cs.prefetch_targets(l) for l in range(n_layers)]
     pred = np.zeros((steps, n_layers, T * cfg.k), np.int32)
     cs.trace = []
@@ -349,3 +350,20 @@ def test_cache_device_lru_evicts_beyond_1024_slots():
                     assert tab[e] == 0, (l, e)
     finally:
         cache.close()
+
+
+@pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
+def test_cache_fit_placement_resident_and_cached_layers(device_lookup):
+    """The placement planner's FIT mode on the 4-layer Zipf Qwen3-30B-A3B-shaped
+    stack (T4 MoE-cache report, "Two ways to run"): a VRAM budget of 1.75
+    layers of experts with a quarter layer's worth reserved for the cache
+    (31 slots) makes layer 0 resident and caches layers 1-3; outputs stay the
+    oracle's and the cached layers' trace is the oracle LRU's."""
+    cfg = W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4)
+    desc = moe.ExpertDesc.of(cfg.qtypes(0), cfg.H, cfg.I)
+    layer_bytes = cfg.E * moe.moe_expert_bytes(desc)
+    st, state, slots = moe.moe_placement_plan([desc], [0] * 4, cfg.E, int(1.75 * layer_bytes), int(0.25 * layer_bytes),
+                                              cfg.k, moe.MOE_PLACE_FIT)
+    assert st == 0 and state.tolist() == [-1, 0, 0, 0], state
+    s = _run(cfg, 4, 16, None, 1, device_lookup, slots=slots, resident=[x < 0 for x in state])
+    assert s["lookups"] > 0 and s["evictions"] > 0
