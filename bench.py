@@ -313,6 +313,26 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
                 "misses_per_token": round(ps["misses"] / steps, 2),
                 "upload_GB": round(ps["upload_bytes"] / 1e9, 3),
             }
+        # a prompt-sized batch through the cache: 64 single-token steps fill
+        # the pool, then 128-token batches stage their experts (copied from
+        # the slots that hold them, else read from host memory), LRU untouched
+        cs = CachedStack(zspecs, packed, slots, T_max=1, device_lookup=True)
+        for s_ in range(64):
+            cs.step(xs[s_].clone())
+        xp = torch.randn((4, 128, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+        cs.prompt_step(xp[0].clone())
+        torch.cuda.synchronize()
+        cs.cache.reset_stats()
+        t0 = time.perf_counter()
+        for s_ in range(1, 4):
+            cs.prompt_step(xp[s_].clone())
+        torch.cuda.synchronize()
+        el_p = time.perf_counter() - t0
+        ps = cs.cache.stats()
+        cs.close()
+        leg["prompt_128"] = {"tokens_per_s": round(3 * 128 / el_p, 1),
+                             "experts_copied_from_slots_per_step": round(ps["large_copies"] / 3, 1),
+                             "experts_uploaded_per_step": round(ps["large_uploads"] / 3, 1)}
         # n_req concurrent requests: one n_req-token batch per step, fresh
         # tokens each step, from a cold pool
         if n_req > 1:
@@ -373,7 +393,8 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
             "workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
                         f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
                         f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
-                        f"copies on the device, eager and as a captured HIP graph; prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
+                        f"copies on the device, eager and as a captured HIP graph; prompt_128: 128-token batches after 64 steps, "
+                        f"staged beside the slots (device LRU, eager); prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
                         f"sharing the pool, one N-token batch per step (device LRU, graph; hit rate over the "
                         f"step's distinct experts per layer)",
             "legs": legs}

@@ -431,6 +431,36 @@ moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t 
  * number of lookups made (the device keeps the first trace_capacity). */
 moe_status moe_cache_trace_read(moe_cache *c, int32_t *out, int32_t capacity, int32_t *n);
 
+/* Batches above 32 tokens (prompt processing) leave the slots alone (T4
+ * MoE-cache report, section "What the MoE cache caches": larger batches do
+ * not go through the cache; the experts they need that the cache holds are
+ * copied from it, its log counts them).  The layer's distinct selected
+ * experts are staged in a caller-owned device area instead: an expert that a
+ * slot holds is copied from the slot device to device (statistic
+ * large_copies), any other is read from its pinned host copy
+ * (large_uploads).  The LRU state, its statistics and its trace are not
+ * touched.  A resident layer stages nothing: its table is its own.
+ *   idx          host int32 [T*k] (moe_cache_stage_large) or device int32
+ *                [T*k] (moe_cache_stage_large_device), ids in [0, E)
+ *   staging      device area of at least min(E, T*k) * expert bytes of the
+ *                layer's group; the u-th distinct id (ascending) lands at
+ *                staging + u * expert bytes
+ *   table_out    device array [E] (caller-owned): the staged address of each
+ *                selected expert, NULL for the others; pass it as the
+ *                expert_ptrs of moe_expert_ffn
+ *   s            the stream of the FFN; work queued on it after this call sees
+ *                the staged experts.  With the host LRU, s must already be
+ *                ordered after the uploads of earlier lookups (their slots are
+ *                read); with a caller-supplied backend the copies are done on
+ *                return and s is ignored.
+ * 33 <= T <= 256 (MOE_ERR_BATCH otherwise), MOE_ERR_ARG when staging is too
+ * small.  moe_cache_stage_large needs the host LRU, moe_cache_stage_large_device
+ * the device one (MOE_ERR_STATE otherwise). */
+moe_status moe_cache_stage_large(moe_cache *c, int32_t layer, int32_t T, int32_t k, const int32_t *idx,
+                                 void *staging, size_t staging_bytes, void **table_out, hipStream_t s);
+moe_status moe_cache_stage_large_device(moe_cache *c, int32_t layer, int32_t T, int32_t k, const int32_t *idx,
+                                        void *staging, size_t staging_bytes, void **table_out, hipStream_t s);
+
 /* Drain outstanding copies and free the pools and tables. */
 void moe_cache_destroy(moe_cache *c);
 

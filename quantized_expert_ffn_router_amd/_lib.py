@@ -20,6 +20,7 @@ EXPORTED = [
     "moe_cache_plan", "moe_placement_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
     "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_prefetch_device", "moe_cache_trace_read",
+    "moe_cache_stage_large", "moe_cache_stage_large_device",
 ]
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_QTYPE",
@@ -128,6 +129,8 @@ def lib() -> ctypes.CDLL:
         "moe_cache_lookup_device": (i32, [P, i32, P, i32, i32, P]),
         "moe_cache_prefetch_device": (i32, [P, i32, P, i32, i32, P, P]),
         "moe_cache_trace_read": (i32, [P, P, i32, P]),
+        "moe_cache_stage_large": (i32, [P, i32, i32, i32, P, P, sz, P, P]),
+        "moe_cache_stage_large_device": (i32, [P, i32, i32, i32, P, P, sz, P, P]),
         "moe_cache_destroy": (None, [P]),
     }
     for name, (res, args) in sig.items():
@@ -357,6 +360,19 @@ class Cache:
             raise ValueError("idx must be a contiguous int32 device tensor of T*k ids")
         _check(lib().moe_cache_prefetch_device(self.h, layer, idx.data_ptr(), T, k, _stream(stream),
                                                _stream(copy_stream)))
+
+    def stage_large(self, layer: int, T: int, k: int, idx, staging, staging_bytes: int, table_out, stream=None):
+        """Stage a large batch's experts (moe_cache_stage_large): idx host
+        int32 [T*k] (numpy), staging / table_out device addresses or tensors."""
+        ids = np.ascontiguousarray(np.asarray(idx).reshape(-1)[:T * k], np.int32)
+        cs = None if (stream is None and self._backend is not None) else _stream(stream)
+        _check(lib().moe_cache_stage_large(self.h, layer, T, k, ids.ctypes.data, _ptr(staging), int(staging_bytes),
+                                           _ptr(table_out), cs))
+
+    def stage_large_device(self, layer: int, T: int, k: int, idx, staging, staging_bytes: int, table_out, stream=None):
+        """moe_cache_stage_large_device: idx a device int32 tensor of T*k ids."""
+        _check(lib().moe_cache_stage_large_device(self.h, layer, T, k, _ptr(idx), _ptr(staging), int(staging_bytes),
+                                                  _ptr(table_out), _stream(stream)))
 
     def trace_read(self, capacity: int) -> np.ndarray:
         """The device trace: int32 [n, 4] (layer, expert, hit, evicted key or -1)."""

@@ -18,6 +18,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "moe_internal.h"
@@ -267,6 +268,13 @@ struct moe_cache {
     // whose experts the FFN that follows is reading; -1 before the first
     std::vector<int> recent_touch;
     int trace_cap = 0;
+    // large-batch staging: the host-LRU path's table row (pinned; its last copy
+    // ends at stage_done), the device path's copy jobs
+    const void **stage_row = nullptr;
+    hipEvent_t stage_done = nullptr;
+    bool stage_pending = false;
+    CacheJob *d_sjobs = nullptr;     // [E]
+    int32_t *d_snjobs = nullptr;
 };
 
 namespace {
@@ -333,6 +341,13 @@ void destroy(moe_cache *c)
     for (auto ev : c->ev_pref)
         if (ev) (void)hipEventDestroy(ev);
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    if (c->stage_row) {
+        if (c->custom) free((void *)c->stage_row);
+        else (void)hipHostFree((void *)c->stage_row);
+    }
+    if (c->stage_done) (void)hipEventDestroy(c->stage_done);
+    if (c->d_sjobs) (void)hipFree(c->d_sjobs);
+    if (c->d_snjobs) (void)hipFree(c->d_snjobs);
     delete c;
 }
 
@@ -949,6 +964,110 @@ moe_status moe_cache_trace_read(moe_cache *c, int32_t *out, int32_t capacity, in
         return MOE_ERR_HIP;
     }
     return MOE_OK;
+}
+
+moe_status moe_cache_stage_large(moe_cache *c, int32_t layer, int32_t T, int32_t k, const int32_t *idx,
+                                 void *staging, size_t staging_bytes, void **table_out, hipStream_t s)
+{
+    if (!c || !idx || !table_out || k < 1 || layer < 0 || layer >= c->n_layers) {
+        set_error("moe_cache_stage_large: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (c->dev) { set_error("moe_cache_stage_large: the cache looks up on the device (moe_cache_stage_large_device)"); return MOE_ERR_STATE; }
+    if (T <= kMaxT || T > kMaxTLarge) { set_error("moe_cache_stage_large: T=%d outside [33, %d]", T, kMaxTLarge); return MOE_ERR_BATCH; }
+    if (c->open_lookup >= 0) {
+        set_error("moe_cache_stage_large: the lookup of layer %d has not been uploaded (its slots are not filled)", c->open_lookup);
+        return MOE_ERR_STATE;
+    }
+    const int E = c->E;
+    auto &G = c->groups[c->layer_group[layer]];
+    const size_t need = (size_t)std::min(E, T * k) * G.slot_bytes;
+    if (!resident_layer(c, layer) && (!staging || staging_bytes < need)) {
+        set_error("moe_cache_stage_large: staging of %zu bytes, %zu needed", staging_bytes, need);
+        return MOE_ERR_ARG;
+    }
+    std::vector<char> sel(E, 0);
+    for (int p = 0; p < T * k; p++) {
+        if (idx[p] < 0 || idx[p] >= E) { set_error("moe_cache_stage_large: id %d outside [0, %d)", idx[p], E); return MOE_ERR_ARG; }
+        sel[idx[p]] = 1;
+    }
+    if (!c->stage_row) {
+        if (c->custom) c->stage_row = (const void **)calloc(E, sizeof(void *));
+        else if (hipHostMalloc((void **)&c->stage_row, sizeof(void *) * E, hipHostMallocDefault) != hipSuccess) c->stage_row = nullptr;
+        if (!c->stage_row || (!c->custom && hipEventCreateWithFlags(&c->stage_done, hipEventDisableTiming) != hipSuccess)) {
+            set_error("moe_cache_stage_large: allocation failed");
+            return MOE_ERR_HIP;
+        }
+    }
+    if (c->stage_pending) {  // the previous call's table copy must have read the row
+        if (hipEventSynchronize(c->stage_done) != hipSuccess) { set_error("hipEventSynchronize failed"); return MOE_ERR_HIP; }
+        c->stage_pending = false;
+    }
+    const size_t off = (size_t)layer * E;
+    int u = 0, copies = 0;
+    for (int e = 0; e < E; e++) {
+        if (resident_layer(c, layer)) { c->stage_row[e] = c->htab[off + e]; continue; }
+        if (!sel[e]) { c->stage_row[e] = nullptr; continue; }
+        uint8_t *dst = (uint8_t *)staging + (size_t)u * G.slot_bytes;
+        const int sl = c->where[off + e];
+        const void *src = sl >= 0 ? (const void *)(G.pool + (size_t)sl * G.slot_bytes) : c->host[off + e];
+        bool ok;
+        if (c->custom) ok = c->be.copy(c->be.user, dst, src, G.slot_bytes) == 0;
+        else ok = hipMemcpyAsync(dst, src, G.slot_bytes, sl >= 0 ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s) == hipSuccess;
+        if (!ok) { set_error("moe_cache_stage_large: copy of expert %d failed", e); return MOE_ERR_HIP; }
+        c->stage_row[e] = dst;
+        copies += sl >= 0;
+        u++;
+    }
+    bool ok;
+    if (c->custom) ok = c->be.copy(c->be.user, table_out, c->stage_row, sizeof(void *) * E) == 0;
+    else ok = hipMemcpyAsync(table_out, c->stage_row, sizeof(void *) * E, hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipEventRecord(c->stage_done, s) == hipSuccess;
+    if (!ok) { set_error("moe_cache_stage_large: table copy failed"); return MOE_ERR_HIP; }
+    c->stage_pending = !c->custom;
+    c->st.large_copies += copies;
+    c->st.large_uploads += u - copies;
+    return MOE_OK;
+}
+
+moe_status moe_cache_stage_large_device(moe_cache *c, int32_t layer, int32_t T, int32_t k, const int32_t *idx,
+                                        void *staging, size_t staging_bytes, void **table_out, hipStream_t s)
+{
+    if (!c || !idx || !table_out || k < 1 || k > (c ? c->E : 0) || layer < 0 || layer >= c->n_layers) {
+        set_error("moe_cache_stage_large_device: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (!c->dev) { set_error("moe_cache_stage_large_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
+    if (T <= kMaxT || T > kMaxTLarge) { set_error("moe_cache_stage_large_device: T=%d outside [33, %d]", T, kMaxTLarge); return MOE_ERR_BATCH; }
+    const int E = c->E;
+    auto &G = c->groups[c->layer_group[layer]];
+    if (resident_layer(c, layer)) {
+        if (hipMemcpyAsync(table_out, c->dtab + (size_t)layer * E, sizeof(void *) * E, hipMemcpyDeviceToDevice, s) != hipSuccess) {
+            set_error("moe_cache_stage_large_device: table copy failed");
+            return MOE_ERR_HIP;
+        }
+        return MOE_OK;
+    }
+    const size_t need = (size_t)std::min(E, T * k) * G.slot_bytes;
+    if (!staging || staging_bytes < need) {
+        set_error("moe_cache_stage_large_device: staging of %zu bytes, %zu needed", staging_bytes, need);
+        return MOE_ERR_ARG;
+    }
+    if (!c->d_sjobs && (hipMalloc((void **)&c->d_sjobs, sizeof(CacheJob) * (size_t)E) != hipSuccess ||
+                        hipMalloc((void **)&c->d_snjobs, 4) != hipSuccess)) {
+        set_error("moe_cache_stage_large_device: allocation failed");
+        return MOE_ERR_HIP;
+    }
+    if (c->pend_touch[layer] >= 0 && hipStreamWaitEvent(s, c->ev_pref[layer], 0) != hipSuccess) {
+        set_error("moe_cache_stage_large_device: hipStreamWaitEvent failed");  // a prefetch into this layer's slots
+        return MOE_ERR_HIP;
+    }
+    StageDevArgs a{};
+    a.idx = idx; a.T = T; a.k = k; a.layer = layer; a.E = E;
+    a.where = c->d_where; a.src = c->d_src; a.pool = G.pool; a.slot_bytes = G.slot_bytes;
+    a.staging = (uint8_t *)staging; a.table = table_out;
+    a.jobs = c->d_sjobs; a.njobs = c->d_snjobs; a.stats = c->d_stats;
+    return launch_stage_device(a, s);
 }
 
 void moe_cache_destroy(moe_cache *c) { destroy(c); }

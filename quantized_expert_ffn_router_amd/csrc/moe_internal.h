@@ -106,6 +106,23 @@ constexpr int kCacheMaxSlots = 16384;  // slots per group that the device lookup
 moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t cs = nullptr,
                                hipEvent_t fork = nullptr, hipEvent_t done = nullptr);
 
+// Staging of a large batch's experts on the device (moe_cache_stage_large_device):
+// the layer's distinct ids, each copied from its slot or its host copy.
+struct StageDevArgs {
+    const int32_t *idx;          // [T][k] (device)
+    int T, k, layer, E;
+    const int32_t *where;        // [L*E] slot of each key, -1 absent
+    const void *const *src;      // [L*E] device addresses of the host copies
+    const uint8_t *pool;
+    unsigned long long slot_bytes;
+    uint8_t *staging;
+    void **table;                // [E] out
+    CacheJob *jobs;              // [E]
+    int32_t *njobs;
+    unsigned long long *stats;   // moe_cache_stats_t fields, in order
+};
+moe_status launch_stage_device(const StageDevArgs &a, hipStream_t s);
+
 // The router's hand-over of logit keys sits at a fixed offset at the start of
 // every workspace, sized for the largest batch and expert count, so that calls
 // of different sizes can share one workspace: the route launch finds it zero

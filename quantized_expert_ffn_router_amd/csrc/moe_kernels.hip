@@ -2764,6 +2764,57 @@ __global__ __launch_bounds__(kCacheCopyThreads) void k_cache_copy(const CacheJob
     }
 }
 
+// Large-batch staging (T4 MoE-cache report, "What the MoE cache caches":
+// batches above 32 tokens bypass the slots, taking the experts the cache
+// holds from it): the layer's distinct selected ids in ascending order, the
+// u-th staged at staging + u * slot_bytes, copied from its slot when the
+// group holds it (large_copies) or from its pinned host copy (large_uploads);
+// the table gets the staged addresses, NULL elsewhere.  One workgroup; the
+// copies are k_cache_copy's jobs.  The LRU state is only read.
+__global__ __launch_bounds__(kCacheThreads) void k_cache_stage(StageDevArgs a)
+{
+    __shared__ int sel[kMaxE];
+    __shared__ int list[kMaxE];
+    __shared__ int s_nd, s_cp;
+    const int tid = (int)threadIdx.x, lane = lane_id(), E = a.E, P = a.T * a.k;
+    for (int e = tid; e < E; e += kCacheThreads) sel[e] = 0;
+    if (tid == 0) s_cp = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kCacheThreads) {
+        const int e = a.idx[p];
+        if ((unsigned)e < (unsigned)E) sel[e] = 1;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int EPL = (E + 63) >> 6, e0 = lane * EPL;
+        int c = 0;
+        for (int j = 0; j < EPL; j++) c += (e0 + j < E) ? sel[e0 + j] : 0;
+        int off = wave_incl_scan(c) - c;
+        for (int j = 0; j < EPL; j++)
+            if (e0 + j < E && sel[e0 + j]) list[off++] = e0 + j;
+        if (lane == 63) s_nd = off;
+    }
+    __syncthreads();
+    const int nd = s_nd;
+    const int64_t kbase = (int64_t)a.layer * E;
+    for (int e = tid; e < E; e += kCacheThreads)
+        if (!sel[e]) a.table[e] = nullptr;
+    for (int u = tid; u < nd; u += kCacheThreads) {
+        const int e = list[u];
+        const int s = a.where[kbase + e];
+        uint8_t *dst = a.staging + (size_t)u * a.slot_bytes;
+        a.table[e] = dst;
+        a.jobs[u] = CacheJob{dst, s >= 0 ? a.pool + (size_t)s * a.slot_bytes : (const uint8_t *)a.src[kbase + e]};
+        if (s >= 0) atomicAdd(&s_cp, 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        *a.njobs = nd;
+        a.stats[9] += s_cp;        // large_copies
+        a.stats[10] += nd - s_cp;  // large_uploads
+    }
+}
+
 __global__ void k_fill_zero(uint4 *p, size_t n16)
 {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
@@ -3010,6 +3061,15 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t
     k_cache_copy<<<128, kCacheCopyThreads, 0, s>>>(a.jobs, a.njobs, a.slot_bytes);
     LAUNCH_OK("k_cache_copy");
     if (done) HIP_OK(hipEventRecord(done, s));
+    return MOE_OK;
+}
+
+moe_status launch_stage_device(const StageDevArgs &a, hipStream_t s)
+{
+    k_cache_stage<<<1, kCacheThreads, 0, s>>>(a);
+    LAUNCH_OK("k_cache_stage");
+    k_cache_copy<<<128, kCacheCopyThreads, 0, s>>>(a.jobs, a.njobs, a.slot_bytes);
+    LAUNCH_OK("k_cache_copy");
     return MOE_OK;
 }
 

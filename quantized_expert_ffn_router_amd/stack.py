@@ -276,6 +276,44 @@ class CachedStack:
         L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
                         self.ws, self.ws_bytes)
 
+    def prompt_step(self, h: torch.Tensor, idx_out: Optional[torch.Tensor] = None):
+        """A prompt-sized batch (33..256 tokens) through the cached stack: such
+        batches leave the slots alone (T4 MoE-cache report, "What the MoE cache
+        caches"); per layer moe_rmsnorm, moe_route_topk, the staging of the
+        selected experts (copied from their slots when cached, else read from
+        host memory; moe_cache_stage_large or _device) and moe_expert_ffn over
+        the staged table, adding into h.  idx_out, if given, is [L, T, k]."""
+        T, H = h.shape
+        key = (T, H)
+        if getattr(self, "_prompt_key", None) != key:
+            kmax = max(s.k for s in self.layers)
+            self._pxhat = torch.empty((T, H), dtype=torch.float32, device=self.device)
+            self._pidx = torch.empty(T * kmax, dtype=torch.int32, device=self.device)
+            self._pw = torch.empty(T * kmax, dtype=torch.float32, device=self.device)
+            self._pws_bytes = max(L.moe_workspace_bytes(d, T, s.k, s.E, s.n_shared)
+                                  for d, s in zip(self.descs, self.layers))
+            self._pws = torch.empty(self._pws_bytes, dtype=torch.uint8, device=self.device)
+            L.moe_workspace_init(self._pws, self._pws_bytes)
+            self._stage_bytes = max(min(s.E, T * s.k) * eb for s, eb in zip(self.layers, self.expert_bytes))
+            self._staging = torch.empty(self._stage_bytes, dtype=torch.uint8, device=self.device)
+            self._stab = torch.zeros(self.E, dtype=torch.int64, device=self.device)
+            self._pidx_host = torch.empty(T * kmax, dtype=torch.int32, pin_memory=True)
+            self._prompt_key = key
+        for li, s in enumerate(self.layers):
+            idx = self._pidx[:T * s.k].view(T, s.k) if idx_out is None else idx_out[li]
+            w = self._pw[:T * s.k].view(T, s.k)
+            L.moe_rmsnorm(h, T, H, self.eps, self._pxhat)
+            L.moe_route_topk(self._pxhat, T, H, self.routers[li], self.biases[li], s.E, s.k, idx, w, None)
+            if self.device_lookup:
+                self.cache.stage_large_device(li, T, s.k, idx, self._staging, self._stage_bytes, self._stab)
+            else:
+                ih = self._pidx_host[:T * s.k]
+                ih.copy_(idx.reshape(-1), non_blocking=True)
+                torch.cuda.current_stream(self.device).synchronize()
+                self.cache.stage_large(li, T, s.k, ih.numpy(), self._staging, self._stage_bytes, self._stab)
+            L.moe_expert_ffn(self.descs[li], self._pxhat, T, s.k, s.E, idx, w, self._stab, self.shared_ptrs(li),
+                             s.n_shared, h, 1, None, self._pws, self._pws_bytes)
+
     def prefetch_targets(self, layer: int) -> List[int]:
         """Layers whose experts are prefetched at `layer` (before its FFN)."""
         d, n = self.prefetch_depth, len(self.layers)

@@ -301,3 +301,56 @@ def test_resident_layers_beside_cached_layers():
     assert st["lookups"] == len(LL) and st["hits"] == int(ref.hit.sum())
     resident |= {(l, e) for l in (0, 2) for e in range(E)}
     s.check_tables(resident)
+
+
+def test_large_batch_staging_copies_cached_experts_and_leaves_the_lru():
+    """Batches above 32 tokens bypass the slots (T4 MoE-cache report, "What
+    the MoE cache caches"): the layer's distinct experts are staged in a
+    caller area, copied from their slots when cached (large_copies) or from
+    host memory (large_uploads).  The staged bytes are the experts' bytes,
+    the table names them, the counts follow the oracle LRU's resident set at
+    that point, and the LRU afterwards still follows the oracle over the
+    small-batch lookups alone."""
+    rng = np.random.default_rng(9)
+    lg = [0, 0, 0]
+    E, T, k = 12, 2, 2
+    s = Setup([(Q4_K, 256, 64)], lg, E, [6], seed=2)
+    eb = s.eb[0]
+    staging = s.pools.alloc(E * eb)
+    table = s.pools.alloc(8 * E)
+    LL, EE, got = [], [], []
+    copies = uploads = 0
+    for i, (l, ids) in enumerate(_random_steps(rng, 10, 3, E, T, k)):
+        ex, slot, hit, vl, ve = s.cache.lookup(l, T, k, ids.ravel())
+        s.cache.upload(l, None)
+        LL += [l] * len(ex)
+        EE += ex.tolist()
+        got.append(hit)
+        if i % 7 == 6:
+            big = rng.integers(0, E, 40 * 3).astype(np.int32)  # a 40-token batch, top-3
+            m = l  # the layer just looked up: some of its experts are in slots
+            _, resident = _oracle_state([6], lg, np.array(LL, np.int32), np.array(EE, np.int32))
+            s.cache.stage_large(m, 40, 3, big, staging, E * eb, table)
+            want = sorted(set(big.tolist()))
+            tab = [v or 0 for v in (ctypes.c_void_p * E).from_address(table)]
+            for u, e in enumerate(want):
+                assert tab[e] == staging + u * eb
+                assert np.array_equal(s.read(tab[e], eb), s.expert_bytes(m, e))
+            assert all(tab[e] == 0 for e in range(E) if e not in want)
+            c = sum((m, e) in resident for e in want)
+            copies += c
+            uploads += len(want) - c
+            st = s.cache.stats()
+            assert st["large_copies"] == copies and st["large_uploads"] == uploads
+    ref, resident = _oracle_state([6], lg, np.array(LL, np.int32), np.array(EE, np.int32))
+    assert np.array_equal(np.concatenate(got), ref.hit)
+    assert copies > 0 and uploads > 0
+    st = s.cache.stats()
+    assert st["lookups"] == len(LL)
+    with pytest.raises(moe.MoeError) as ei:
+        s.cache.stage_large(0, 32, 2, np.zeros(64, np.int32), staging, E * eb, table)
+    assert ei.value.name == "MOE_ERR_BATCH"
+    with pytest.raises(moe.MoeError) as ei:
+        s.cache.stage_large(0, 40, 3, np.arange(120, dtype=np.int32) % E, staging, eb, table)
+    assert ei.value.name == "MOE_ERR_ARG"
+    s.check_tables(resident)

@@ -367,3 +367,72 @@ def test_cache_fit_placement_resident_and_cached_layers(device_lookup):
     assert st == 0 and state.tolist() == [-1, 0, 0, 0], state
     s = _run(cfg, 4, 16, None, 1, device_lookup, slots=slots, resident=[x < 0 for x in state])
     assert s["lookups"] > 0 and s["evictions"] > 0
+
+
+@pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
+def test_cache_prompt_batch_stages_experts_beside_the_lru(device_lookup):
+    """A 40-token prompt batch through the cached stack (T4 MoE-cache report,
+    "What the MoE cache caches": batches above 32 tokens bypass the slots,
+    copying the cached experts they need): outputs and routing are the
+    oracle's, the copies counted from slots follow the oracle LRU's resident
+    set, and the single-token steps around the prompt keep the oracle LRU's
+    trace bit for bit (the prompt does not touch the LRU)."""
+    cfg = W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=2)
+    experts = ExpertCache(cfg)
+    olayers = oracle_layers(cfg, experts, 2)
+    specs = layer_specs(cfg, 2)
+    packed = [pack_layer(s_, l, experts) for l, s_ in enumerate(specs)]
+    cs = CachedStack(specs, packed, [40], T_max=1, device_lookup=device_lookup, trace_capacity=4096)
+    cs.trace = []
+    ids = []
+    try:
+        def decode(step):
+            x, _ = W.tie_free_tokens(cfg, step, 1, chain_min_gap(olayers))
+            h = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+            cs.step(h)
+            outs = oracle.stack_token(olayers, x[0])
+            ids.append([o.route.idx.ravel() for o in outs])
+            torch.cuda.synchronize()
+            assert oracle.rel_l2(h.cpu().numpy()[0], outs[-1].h_next) <= REL_L2_BAR
+
+        for step in range(6):
+            decode(step)
+        LL, EE = oracle.lookup_sequence(np.array(ids, np.int32))
+        _, resident = resident_keys([40], [0, 0], LL, EE)
+        Tp = 40
+        x, _ = W.tie_free_tokens(cfg, 100, Tp, chain_min_gap(olayers))
+        h = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+        idx = torch.empty((2, Tp, cfg.k), dtype=torch.int32, device=DEV)
+        cs.prompt_step(h, idx)
+        torch.cuda.synchronize()
+        hg, ig = h.cpu().numpy(), idx.cpu().numpy()
+        want_copies = want_uploads = 0
+        outs = [oracle.stack_token(olayers, x[t]) for t in range(Tp)]
+        for l in range(2):
+            sel = sorted(set(np.concatenate([outs[t][l].route.idx.ravel() for t in range(Tp)]).tolist()))
+            c = sum((l, e) in resident for e in sel)
+            want_copies += c
+            want_uploads += len(sel) - c
+        for t in range(Tp):
+            for l in range(2):
+                assert sets_equal(ig[l, t][None], outs[t][l].route.idx), (t, l)
+            assert oracle.rel_l2(hg[t], outs[t][-1].h_next) <= REL_L2_BAR, t
+        st = cs.cache.stats()
+        _say(f"prompt staging: {st['large_copies']} copied from slots, {st['large_uploads']} uploaded")
+        assert st["large_copies"] == want_copies and st["large_uploads"] == want_uploads
+        assert want_copies > 0 and want_uploads > 0
+        for step in range(6, 10):
+            decode(step)
+        LL, EE = oracle.lookup_sequence(np.array(ids, np.int32))
+        ref = oracle.lru([40], [0, 0], LL, EE)
+        if device_lookup:
+            gl, ge, hit, vl, ve = cs.device_trace()
+        else:
+            gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in cs.trace])
+            ge = np.concatenate([e for _, e, *_ in cs.trace]).astype(np.int32)
+            hit = np.concatenate([t_[2] for t_ in cs.trace])
+            vl = np.concatenate([t_[3] for t_ in cs.trace])
+        assert np.array_equal(gl, LL) and np.array_equal(ge, EE)
+        assert np.array_equal(hit, ref.hit) and np.array_equal(vl, ref.victim_layer)
+    finally:
+        cs.close()
