@@ -358,6 +358,35 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
                 "hit_rate": round(rs["hits"] / rs["lookups"], 4),
                 "misses_per_step": round(rs["misses"] / steps, 2),
             }
+        # hit rate and throughput against concurrency (T4 report, "When the
+        # cache hurts": N requests decode as one N-token batch, or a
+        # speculative verification of N-1 drafts): device LRU as a graph,
+        # cold pool, max(16, 256/N) steps of N fresh tokens
+        curve = {}
+        for nq in (1, 2, 4, 8, 16, 32):
+            nsteps = max(16, 256 // nq)
+            xq = torch.randn((nsteps, nq, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+            cs = CachedStack(zspecs, packed, slots, T_max=nq, device_lookup=True)
+            hb = xq[0].clone()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                cs.step(hb)
+            torch.cuda.synchronize()
+            cs.cache.reset_stats()
+            t0 = time.perf_counter()
+            for s_ in range(nsteps):
+                hb.copy_(xq[s_])
+                graph.replay()
+            torch.cuda.synchronize()
+            el_q = time.perf_counter() - t0
+            qs = cs.cache.stats()
+            del graph
+            cs.close()
+            curve[str(nq)] = {"tokens_per_s": round(nq * nsteps / el_q, 1),
+                              "hit_rate": round(qs["hits"] / max(1, qs["lookups"]), 4),
+                              "misses_per_step": round(qs["misses"] / nsteps, 1), "steps": nsteps}
+        leg["concurrency_curve"] = curve
         legs.append(leg)
         log(f"cache {f:.0%}: {legs[-1]}")
     # placement (T4 report, "Two ways to run"): the 60 % budget spent FIT-style,
@@ -394,7 +423,8 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
                         f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
                         f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
                         f"copies on the device, eager and as a captured HIP graph; prompt_128: 128-token batches after 64 steps, "
-                        f"staged beside the slots (device LRU, eager); prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
+                        f"staged beside the slots (device LRU, eager); concurrency_curve: N fresh tokens per step (N requests, or "
+                        f"a speculative verification of N-1 drafts), device LRU graph, cold pool; prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
                         f"sharing the pool, one N-token batch per step (device LRU, graph; hit rate over the "
                         f"step's distinct experts per layer)",
             "legs": legs}

@@ -436,3 +436,52 @@ def test_cache_prompt_batch_stages_experts_beside_the_lru(device_lookup):
         assert np.array_equal(hit, ref.hit) and np.array_equal(vl, ref.victim_layer)
     finally:
         cs.close()
+
+
+@pytest.mark.parametrize("device_lookup", [False, True], ids=["host_lru", "device_lru"])
+def test_cache_speculative_replay_and_batch_buckets(device_lookup):
+    """Speculative decoding widens the batch (T4 MoE-cache report, "When the
+    cache hurts": verifying a draft feeds several tokens at once): single-token
+    steps interleaved with verification batches of 5 and 12 tokens on one
+    pool.  The trace is the oracle LRU's over the mixed lookups, and the hit
+    counts per batch-size bucket (<= 8 and 9-32 tokens, as the report's log
+    splits them) are the oracle trace's, bucketed by each step's batch."""
+    cfg = W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4)
+    experts = ExpertCache(cfg)
+    olayers = oracle_layers(cfg, experts, 4)
+    specs = layer_specs(cfg, 4)
+    packed = [pack_layer(s_, l, experts) for l, s_ in enumerate(specs)]
+    cs = CachedStack(specs, packed, [100], T_max=12, device_lookup=device_lookup, trace_capacity=8192)
+    cs.trace = []
+    LL, EE, TT = [], [], []
+    try:
+        for step, T in enumerate([1, 1, 5, 1, 12, 1, 1, 5, 12, 1]):
+            x, _ = W.tie_free_tokens(cfg, 200 + step, T, chain_min_gap(olayers))
+            h = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+            cs.step(h)
+            torch.cuda.synchronize()
+            outs = [oracle.stack_token(olayers, x[t]) for t in range(T)]
+            for l in range(4):
+                e = np.unique(np.concatenate([outs[t][l].route.idx.ravel() for t in range(T)]))
+                LL += [l] * len(e)
+                EE += e.tolist()
+                TT += [T] * len(e)
+            href = np.stack([outs[t][-1].h_next for t in range(T)])
+            assert oracle.rel_l2(h.cpu().numpy(), href) <= REL_L2_BAR, step
+        LL, EE, TT = np.array(LL, np.int32), np.array(EE, np.int32), np.array(TT)
+        ref = oracle.lru([100], [0] * 4, LL, EE)
+        if device_lookup:
+            gl, ge, hit, vl, ve = cs.device_trace()
+        else:
+            gl = np.concatenate([np.full(len(e), l, np.int32) for l, e, *_ in cs.trace])
+            ge = np.concatenate([e for _, e, *_ in cs.trace]).astype(np.int32)
+            hit = np.concatenate([t_[2] for t_ in cs.trace])
+        assert np.array_equal(gl, LL) and np.array_equal(ge, EE) and np.array_equal(hit, ref.hit)
+        st = cs.cache.stats()
+        small, big = TT <= 8, TT > 8
+        assert st["lookups_le8"] == int(small.sum()) and st["hits_le8"] == int(ref.hit[small].sum())
+        assert st["lookups_9_32"] == int(big.sum()) and st["hits_9_32"] == int(ref.hit[big].sum())
+        assert st["lookups_9_32"] > 0 and st["evictions"] > 0
+        _say("buckets: <=8 %d/%d, 9-32 %d/%d" % (st["hits_le8"], st["lookups_le8"], st["hits_9_32"], st["lookups_9_32"]))
+    finally:
+        cs.close()
