@@ -138,8 +138,51 @@ size_t moe_workspace_bytes(const moe_expert_desc *d, int32_t T, int32_t k, int32
 /* Zero a workspace (a fill kernel on stream s, no hipMemset) before its
  * first use.  The kernels leave their counters at zero when they finish, so
  * a workspace is reusable by any later call of the same or smaller sizes.
- * Calls that share one workspace must be ordered (same stream or events). */
+ * Calls that share one workspace must be ordered (same stream or events).
+ * ws == NULL (ws_bytes ignored) clears the static scratch array of
+ * moe_layer_forward_noalloc on the current device instead (no allocation).
+ * This is also the one way to clear a workspace's status word (below). */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s);
+
+/* Status word of a workspace.  The route launch of moe_layer_route,
+ * moe_layer_forward and moe_layer_forward_noalloc hands logit keys (and,
+ * above 16 tokens, each token's top-k) between its workgroups through the
+ * workspace, and the receiving workgroup waits for them with a bounded poll.
+ * A poll that gives up -- never seen in normal operation: it means the
+ * sending workgroups were not scheduled within about a million polling
+ * rounds -- sets a bit here and routes that launch with NaN weights (idx_out
+ * ids stay in [0, E)), so the routing outputs and the updated state are NaN
+ * and no caller can miss it.  The bits are sticky: since late senders may
+ * still write into the hand-off arrays, every later route launch on the
+ * workspace that would read them routes with NaN weights too (without
+ * waiting) until moe_workspace_init clears the workspace.  Exception: a
+ * single token on the dot-product path with E <= 128 and H <= 4096 is ranked
+ * again inside moe_layer_ffn's gate/up kernel from plainly stored logits, not
+ * from the hand-off: its updated state stays exact (only idx_out / w_out, when
+ * requested, show the NaN weights). */
+enum {
+    MOE_WS_KEYS_TIMEOUT = 1, /* the wait for the router's logit keys gave up */
+    MOE_WS_TOPK_TIMEOUT = 2  /* a wait on the per-token top-k hand-off gave up */
+};
+/* Byte offset of the status word (uint32) in every workspace, for callers
+ * that check it on the device or from a captured graph. */
+#define MOE_WS_STATUS_OFFSET 147456u
+
+/* Read a workspace's status word (0: no wait has given up).  Waits for the
+ * work queued on s (stream-synchronous).  ws == NULL reads the static scratch
+ * array of moe_layer_forward_noalloc on the current device (0 if no call has
+ * used it yet).  MOE_ERR_ARG for a null status or a workspace too small to
+ * hold the word; MOE_ERR_HIP if the copy fails. */
+moe_status moe_workspace_status(const void *ws, size_t ws_bytes, uint32_t *status, hipStream_t s);
+
+/* Test hook for the give-up path above, for the route launches that follow
+ * this call in the process.  rounds: polling rounds after which a wait gives
+ * up (0 restores the default of 2^20; 1 makes a give-up likely whenever a
+ * sender is late).  withhold_keys != 0: the router workgroups store no logit
+ * keys into the hand-off, so every wait for them gives up after `rounds`
+ * (the plainly stored single-token logits are still written).  Production
+ * code never calls this; (0, 0) restores normal operation. */
+void moe_set_spin_limit(uint32_t rounds, int32_t withhold_keys);
 
 /* Expert FFN and weighted combine for one layer:
  *   y[t] = (accumulate ? y[t] : 0) + sum_j w[t,j] * FFN_{idx[t,j]}(x[t]) + sum_s FFN_shared_s(x[t])

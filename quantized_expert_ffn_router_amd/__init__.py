@@ -33,5 +33,10 @@ from ._lib import (  # noqa: F401
     moe_route_topk,
     moe_workspace_bytes,
     moe_workspace_init,
+    moe_workspace_status,
+    moe_set_spin_limit,
+    MOE_WS_KEYS_TIMEOUT,
+    MOE_WS_TOPK_TIMEOUT,
+    MOE_WS_STATUS_OFFSET,
     EXPORTED,
 )

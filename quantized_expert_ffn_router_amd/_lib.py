@@ -15,7 +15,7 @@ MOE_Q8_0, MOE_Q4_K, MOE_Q6_K = 1, 2, 3
 EXPORTED = [
     "moe_last_error", "moe_expert_bytes", "moe_down_k", "moe_repack_expert",
     "moe_rmsnorm", "moe_route_topk", "moe_group_tokens", "moe_workspace_bytes",
-    "moe_workspace_init", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
+    "moe_workspace_init", "moe_workspace_status", "moe_set_spin_limit", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
     "moe_layer_forward_noalloc",
     "moe_cache_plan", "moe_placement_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
         "moe_group_tokens": (i32, [P, i32, i32, i32, P, P, P, P]),
         "moe_workspace_bytes": (sz, [D, i32, i32, i32, i32]),
         "moe_workspace_init": (i32, [P, sz, P]),
+        "moe_workspace_status": (i32, [P, sz, P, P]),
+        "moe_set_spin_limit": (None, [ctypes.c_uint32, i32]),
         "moe_expert_ffn": (i32, [D, P, i32, i32, i32, P, P, P, P, i32, P, i32, P, P, sz, P]),
         "moe_layer_route": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_layer_ffn": (i32, [D, P, i32, i32, i32, P, P, i32, P, sz, P]),
@@ -222,7 +224,26 @@ def moe_workspace_bytes(desc, T: int, k: int, E: int, n_shared: int = 0) -> int:
 
 
 def moe_workspace_init(ws, nbytes: int, stream=None):
+    """ws None: the static scratch of moe_layer_forward_noalloc on the current device."""
     _check(lib().moe_workspace_init(_ptr(ws), nbytes, _stream(stream)))
+
+
+MOE_WS_KEYS_TIMEOUT, MOE_WS_TOPK_TIMEOUT = 1, 2
+MOE_WS_STATUS_OFFSET = 147456  # byte offset of the status word in every workspace
+
+
+def moe_workspace_status(ws, nbytes: int, stream=None) -> int:
+    """The workspace's status word (MOE_WS_* bits; 0 = no wait gave up).
+    Stream-synchronous.  ws None: the static scratch of the current device."""
+    out = ctypes.c_uint32(0)
+    _check(lib().moe_workspace_status(_ptr(ws), nbytes, ctypes.byref(out), _stream(stream)))
+    return int(out.value)
+
+
+def moe_set_spin_limit(rounds: int, withhold_keys: bool = False):
+    """Test hook: polling rounds before the route launch's waits give up
+    (0: default); withhold_keys makes every wait for the keys give up."""
+    lib().moe_set_spin_limit(int(rounds), 1 if withhold_keys else 0)
 
 
 def moe_expert_ffn(desc, x, T: int, k: int, E: int, idx, w, expert_ptrs, shared_ptrs, n_shared: int, y,

@@ -132,6 +132,12 @@ constexpr size_t kKeysBytes = (size_t)kMaxT * kMaxE * 4;
 // After them, the per-token top-k workgroups' hand-over of each token's k
 // selections to the route tail (64-bit, never zero), same protocol.
 constexpr size_t kTkBytes = (size_t)kMaxT * 64 * 8;
+// Then the workspace's status word (a 256-byte region): bits that the route
+// launch sets when a bounded wait gives up (MOE_WS_* in moe.h), sticky until
+// moe_workspace_init clears the workspace.
+constexpr size_t kStatus = kKeys + kKeysBytes + kTkBytes;
+constexpr size_t kStatusBytes = 256;
+static_assert(kStatus == MOE_WS_STATUS_OFFSET, "status word offset published in moe.h");
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
@@ -155,7 +161,7 @@ constexpr int kX16Bytes = 1072;
 
 struct WsLayout {
     int T, k, E, ns, H, kd, P, U, UI;  // U: distinct experts, UI: work items (both at most)
-    size_t keys, tk, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, dlog, total;
+    size_t keys, tk, status, xenc, x16, idx, w, nuniq, wt, ptok, inv, pw, henc, hf, dlog, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -170,7 +176,8 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.UI = L.U + (L.P + kItemTok - 1) / kItemTok;
     L.keys = kKeys;
     L.tk = kKeys + kKeysBytes;
-    size_t o = L.tk + kTkBytes;
+    L.status = kStatus;
+    size_t o = kStatus + kStatusBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
     L.x16 = take((size_t)T * (d.H / 256) * kX16Bytes);

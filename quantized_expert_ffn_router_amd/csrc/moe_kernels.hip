@@ -47,7 +47,8 @@
 // relaxed agent-scope atomic stores and loads of words that are never zero
 // once written (coherent across the XCDs' L2 caches without whole-cache
 // write-back or invalidation); the tail polls them with a bounded loop and
-// clears them for the next launch.  There is no arrival counter.
+// clears them for the next launch.  There is no arrival counter.  A wait that
+// gives up sets a sticky bit in the workspace's status word (see RouteArgs).
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
@@ -181,7 +182,8 @@ __device__ __forceinline__ uint32_t ld_coh_u(const uint32_t *p)
 {
     return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Bound on the polls of a wait for other workgroups of the same launch.
+// Default bound on the polls of a wait for other workgroups of the same
+// launch (moe_set_spin_limit overrides it for tests of the give-up path).
 constexpr unsigned kSpinLimit = 1u << 20;
 
 __device__ float block_sum(float v, float *red)
@@ -661,7 +663,16 @@ struct RouteArgs {
     unsigned long long *tk; // [T][k] hand-over of those selections (key << 32 | ~id, never zero)
     int tail;               // 1: the last workgroup routes (keys handed over); 0: no tail
     uint32_t *dlog;         // [E] (T = 1) the logit keys for routing in the FFN (plain stores), or null
+    uint32_t *status;       // the workspace's status word: nonzero = a wait gave up earlier (sticky)
+    unsigned spin;          // polling rounds before a wait gives up
+    int withhold;           // 1: the router workgroups store no keys (forced give-up, for tests)
 };
+
+// Sets bit b of the status word (a vector atomic; lane 0 of the calling wave).
+__device__ __forceinline__ void flag_status(uint32_t *status, uint32_t b)
+{
+    if (lane_id() == 0) __hip_atomic_fetch_or(status, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Top-k of NT tokens' E keys each by one wave (no barriers), keys in
 // registers (lane l holds experts l + 64i of token t in key[t][i], zero past
@@ -758,7 +769,9 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
 {
     const int E = a.E, k = a.k, ns = a.ns, lane = lane_id();
     uint32_t key[NVL];
-    int ok = 1;
+    // a workspace whose status word is set may hold stale keys: no wait
+    const bool dead = *a.status != 0u;
+    int ok = !dead;
     for (unsigned it = 0;; it++) {
         bool missing = false;
 #pragma unroll
@@ -768,7 +781,8 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
             missing |= e < E && key[i] == 0u;
         }
         if (!__ballot(missing)) break;
-        if (it >= kSpinLimit) {
+        if (dead || it >= a.spin) {
+            if (!dead) flag_status(a.status, MOE_WS_KEYS_TIMEOUT);
             ok = 0;
             break;
         }
@@ -828,15 +842,16 @@ __device__ __forceinline__ void route_tail_one(const RouteArgs &a, uint64_t *can
 // token's E keys into registers (bounded, as the tail does), ranks them with
 // topk_one and hands the k selections to the tail with coherent 64-bit
 // stores (key << 32 | ~id: the key half is never zero).  A poll that gives
-// up hands over selections with a zero key half, which the tail never
-// accepts: it gives up too and routes with NaN weights.
+// up sets the status word and hands over selections with a zero key half,
+// which the tail never accepts: it gives up too and routes with NaN weights.
 template <int NVL>
 __device__ __forceinline__ void route_topk_token(const RouteArgs &a, int t, uint64_t *cand)
 {
     const int E = a.E, k = a.k, lane = lane_id();
     const unsigned *kt = a.keys + (size_t)t * E;
     uint32_t key[NVL];
-    bool ok = true;
+    const bool dead = *a.status != 0u;
+    bool ok = !dead;
     for (unsigned it = 0;; it++) {
         bool missing = false;
 #pragma unroll
@@ -846,7 +861,8 @@ __device__ __forceinline__ void route_topk_token(const RouteArgs &a, int t, uint
             missing |= e < E && key[i] == 0u;
         }
         if (!__ballot(missing)) break;
-        if (it >= kSpinLimit) {
+        if (dead || it >= a.spin) {
+            if (!dead) flag_status(a.status, MOE_WS_TOPK_TIMEOUT);
             ok = false;
             break;
         }
@@ -870,8 +886,10 @@ __device__ __forceinline__ void route_topk_role(const RouteArgs &a, int t)
 // The tail workgroup: a single token goes to route_tail_one; otherwise the
 // workgroup polls the keys until every one is written, then top-k (clearing
 // the keys for the next launch), softmax and grouping.  A poll that
-// gives up after kSpinLimit rounds routes with NaN weights, which no caller
-// can miss.
+// gives up after a.spin rounds sets the status word and routes with NaN
+// weights, which no caller can miss; a set status word (from an earlier
+// launch) means no wait at all and NaN weights again, since senders that came
+// late may have left stale words behind.
 __device__ __forceinline__ void route_tail(const RouteArgs &a)
 {
     __shared__ __align__(16) uint32_t lk[kStageKeys];
@@ -906,7 +924,9 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
         else route_tail_one<16>(a, cand, pre);
         return;
     }
-    int ok = 1;
+    // a workspace whose status word is set may hold stale hand-offs: no wait
+    const bool dead = *a.status != 0u;
+    int ok = !dead;
     constexpr int kPollQ = 8;
     if (a.topk_blocks) {
         // the top-k workgroups' selections, polled like the keys
@@ -920,13 +940,21 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
                 missing |= (c >> 32) == 0ull;  // not yet written (or given up on)
             }
             if (!__ballot(missing)) break;
-            if (it >= kSpinLimit) {
+            if (dead || it >= a.spin) {
+                if (!dead) flag_status(a.status, MOE_WS_TOPK_TIMEOUT);
                 ok = 0;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
         ok = __syncthreads_and(ok);
+        // selections that never arrived (zero) or were given up on carry no
+        // valid id: route with ids 0..k-1 (distinct, in range; NaN weights)
+        if (!ok)
+            for (int i = tid; i < nk; i += kRouteWG) {
+                sidx[i] = i % k;
+                skey[i] = 0u;
+            }
         // clear both hand-overs for the next launch (the top-k workgroups are
         // done with the keys once their selections are all here)
         for (int i = tid; i < n; i += kRouteWG) a.keys[i] = 0u;
@@ -953,7 +981,8 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
             }
         }
         if (!__ballot(missing)) break;
-        if (it >= kSpinLimit) {
+        if (dead || it >= a.spin) {
+            if (!dead) flag_status(a.status, MOE_WS_KEYS_TIMEOUT);
             ok = 0;
             break;
         }
@@ -1084,7 +1113,7 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr, 
                 const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
                 const float lg = d * rr + (a.bias ? a.bias[e0 + r] : 0.f);
                 if (a.dlog) a.dlog[e0 + r] = logit_key(lg);  // read after the launch boundary
-                if (a.tail)
+                if (a.tail && !a.withhold)
                     __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
                 if (a.logits2) a.logits2[(size_t)t * E + e0 + r] = lg;
@@ -2837,6 +2866,10 @@ namespace {
 // ---------------------------------------------------------------------------
 // host side
 
+std::atomic<unsigned> g_spin{kSpinLimit};
+std::atomic<int> g_withhold{0};
+unsigned spin_limit() { return g_spin.load(std::memory_order_relaxed); }
+
 #define HIP_OK(expr)                                                                     \
     do {                                                                                 \
         hipError_t e_ = (expr);                                                          \
@@ -3117,17 +3150,6 @@ size_t moe_workspace_bytes(const moe_expert_desc *d, int32_t T, int32_t k, int32
     return ws_layout(*d, T, k, E, n_shared).total;
 }
 
-moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s)
-{
-    if (!ws || (ws_bytes & 15)) { set_error("moe_workspace_init: null or size not a multiple of 16"); return MOE_ERR_ARG; }
-    const size_t n16 = ws_bytes / 16;
-    int blocks = (int)((n16 + 255) / 256);
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    k_fill_zero<<<blocks, 256, 0, s>>>((uint4 *)ws, n16);
-    LAUNCH_OK("k_fill_zero");
-    return MOE_OK;
-}
 
 moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, int32_t k, int32_t E,
                           const int32_t *idx, const float *w, const void *const *expert_ptrs,
@@ -3200,6 +3222,9 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.dlog = defer ? W.at<uint32_t>(W.L.dlog) : nullptr;
     a.tail = !defer || idx_out || w_out;
     if (!a.tail) a.topk_blocks = 0;
+    a.status = W.at<uint32_t>(W.L.status);
+    a.spin = spin_limit();
+    a.withhold = g_withhold.load(std::memory_order_relaxed);
     k_route<<<a.n_expert_blocks + T * ((d->H + kEncPos - 1) / kEncPos) + a.topk_blocks + (a.tail ? 1 : 0), kRouteWG, 0,
               s>>>(a);
     LAUNCH_OK("k_route");
@@ -3242,11 +3267,23 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
 
+moe_status fill_zero(void *ws, size_t bytes, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    int blocks = (int)((n16 + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    k_fill_zero<<<blocks, 256, 0, s>>>((uint4 *)ws, n16);
+    LAUNCH_OK("k_fill_zero");
+    return MOE_OK;
+}
+
 // The device address of this GPU's scratch array: taken once per device
 // (with that device current) and kept; the first call also clears the
 // whole array on s, since the routing hand-over words must start at zero
-// (the kernels leave them at zero when they finish).
-moe_status static_scratch(hipStream_t s, void **out)
+// (the kernels leave them at zero when they finish).  With setup == false
+// no address is taken: *out is null if no call has taken it yet.
+moe_status static_scratch(hipStream_t s, void **out, bool setup = true)
 {
     int dev = 0;
     HIP_OK(hipGetDevice(&dev));
@@ -3255,15 +3292,15 @@ moe_status static_scratch(hipStream_t s, void **out)
         return MOE_ERR_ARG;
     }
     std::lock_guard<std::mutex> lock(g_scratch_mu);
-    if (!g_scratch_ptr[dev]) {
+    if (!g_scratch_ptr[dev] && setup) {
         void *p = nullptr;
         hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
         if (e != hipSuccess || !p) {
             set_error("hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
             return MOE_ERR_HIP;
         }
-        k_fill_zero<<<1024, 256, 0, s>>>((uint4 *)p, kStaticScratchBytes / 16);
-        LAUNCH_OK("k_fill_zero");
+        moe_status st = fill_zero(p, kStaticScratchBytes, s);
+        if (st != MOE_OK) return st;
         g_scratch_ptr[dev] = p;
     }
     *out = g_scratch_ptr[dev];
@@ -3298,6 +3335,47 @@ moe_status moe_layer_forward_noalloc(const moe_expert_desc *d, float *h, int32_t
     if ((st = static_scratch(s, &ws)) != MOE_OK) return st;
     return moe_layer_forward(d, h, T, w_router, bias, E, k, expert_ptrs, shared_ptrs, n_shared, eps, idx_out, w_out,
                              ws, kStaticScratchBytes, s);
+}
+
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s)
+{
+    if (!ws) {
+        // the static scratch of the current device
+        void *p = nullptr;
+        moe_status st = static_scratch(s, &p, false);
+        if (st != MOE_OK) return st;
+        if (!p) return static_scratch(s, &p);  // taken now, and cleared
+        return fill_zero(p, kStaticScratchBytes, s);
+    }
+    if (ws_bytes & 15) { set_error("moe_workspace_init: size not a multiple of 16"); return MOE_ERR_ARG; }
+    return fill_zero(ws, ws_bytes, s);
+}
+
+moe_status moe_workspace_status(const void *ws, size_t ws_bytes, uint32_t *status, hipStream_t s)
+{
+    if (!status) { set_error("moe_workspace_status: null status"); return MOE_ERR_ARG; }
+    *status = 0;
+    if (!ws) {
+        void *p = nullptr;
+        moe_status st = static_scratch(s, &p, false);
+        if (st != MOE_OK) return st;
+        if (!p) return MOE_OK;  // never used on this device
+        ws = p;
+        ws_bytes = kStaticScratchBytes;
+    }
+    if (ws_bytes < kStatus + 4) {
+        set_error("moe_workspace_status: %zu bytes cannot hold the status word at offset %zu", ws_bytes, kStatus);
+        return MOE_ERR_ARG;
+    }
+    HIP_OK(hipMemcpyAsync(status, (const uint8_t *)ws + kStatus, 4, hipMemcpyDeviceToHost, s));
+    HIP_OK(hipStreamSynchronize(s));
+    return MOE_OK;
+}
+
+void moe_set_spin_limit(uint32_t rounds, int32_t withhold_keys)
+{
+    g_spin.store(rounds ? rounds : kSpinLimit, std::memory_order_relaxed);
+    g_withhold.store(withhold_keys ? 1 : 0, std::memory_order_relaxed);
 }
 
 }  // extern "C"

@@ -118,3 +118,14 @@ def test_prefetch_schedule():
     assert [CachedStack.prefetch_targets(SimpleNamespace(prefetch_depth=2, layers=[None] * 5), l)
             for l in range(5)] == [[1, 2], [3], [4], [], []]
     assert CachedStack.prefetch_targets(SimpleNamespace(prefetch_depth=0, layers=[None] * 5), 0) == []
+
+
+def test_workspace_status_argument_checks_without_gpu():
+    """moe_workspace_status rejects a null status or a workspace too small to
+    hold the word on the host, before any HIP call."""
+    import ctypes
+    L = moe.lib()
+    out = ctypes.c_uint32(7)
+    assert L.moe_workspace_status(ctypes.c_void_p(4096), 1 << 20, None, None) == -1
+    assert L.moe_workspace_status(ctypes.c_void_p(4096), moe.MOE_WS_STATUS_OFFSET, ctypes.byref(out), None) == -1
+    assert b"status word" in L.moe_last_error()
