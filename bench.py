@@ -214,14 +214,16 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
     import quantized_expert_ffn_router_amd as moe
     from quantized_expert_ffn_router_amd.stack import CachedStack, LayerSpec
 
-    zcfg = cfg.with_(zipf_s=1.1)
+    zcfg = W.qwen3_cache_trace(cfg.n_layers)  # the same experts and routers, Zipf(1.1) bias
     zspecs = [LayerSpec(s.qtypes, s.H, s.I, s.E, s.k, s.n_shared, s.router, W.zipf_bias(zcfg, l))
               for l, s in enumerate(specs)]
     desc = moe.ExpertDesc.of(cfg.qtypes(0), cfg.H, cfg.I)
     eb = moe.moe_expert_bytes(desc)
     total = cfg.n_layers * cfg.E * eb
     g = torch.Generator(device="cpu").manual_seed(seed)
-    xs = torch.randn((steps + 2, 1, cfg.H), generator=g, dtype=torch.float32).to("cuda")
+    # the decode trace: token s of the trace's seeded stream at step s (the
+    # parity test replays the same stream, redrawing the few near-tie tokens)
+    xs = torch.from_numpy(np.stack([W.token(zcfg, s_, 0) for s_ in range(steps + 2)])[:, None, :]).to("cuda")
     legs = []
     for f in fractions:
         st, slots = moe.moe_cache_plan([desc], [cfg.n_layers], int(f * total), cfg.k)

@@ -109,6 +109,14 @@ def qwen3_30b_a3b_q4k_zipf(T: int = 32, seed: int = 3, n_layers: int = 48) -> Mo
                      _uniform_layers(n_layers, Q4_K), zipf_s=1.1, seed=seed, T=T)
 
 
+def qwen3_cache_trace(n_layers: int = 48) -> MoEConfig:
+    """The slot-pool cache's decode trace stack: the Qwen3-30B-A3B-shaped
+    Q4_K stack (same experts and routers, seed 2) with a Zipf(s=1.1) router
+    bias; each decode step is one fresh N(0, 1) token."""
+    return qwen3_30b_a3b_q4k(T=1, n_layers=n_layers).with_(
+        zipf_s=1.1, name=f"qwen3-30b-a3b-shaped-q4k-zipf-cache-trace-L{n_layers}")
+
+
 def mixed_shared_q4k_q6k(T: int = 1, seed: int = 5, n_layers: int = 24) -> MoEConfig:
     """24 layers, H=2048, 64 routed (top-2) + 2 shared experts, I=1408;
     layers 0-11 Q4_K, 12-23 Q6_K (down rows padded to 1536)."""
