@@ -18,10 +18,12 @@
 //              SiLU(g)*u; each pair's rows, times its combine weight, are
 //              added into the token's rows of y with float atomics (y holds
 //              the residual already, so no combine pass follows).
-// Batches of more than 8 tokens on all-Q4_K experts use k_gate_up_mfma /
-// k_down_mfma instead (fp16 MFMA on the exact integer weights sc*q and a
-// two-part split of the activations).  The slot-pool cache's device lookup
-// and miss copies are k_cache_lookup and k_cache_copy.
+// Batches of 2 to 8 tokens on all-Q4_K experts use k_gate_up_i8 / k_down_i8
+// instead (integer MFMA on the int8 activation pieces and the weights' sc*q
+// split into two int8 parts), batches of more than 8 k_gate_up_mfma /
+// k_down_mfma (fp16 MFMA on the exact integer weights sc*q and a two-part
+// split of the activations).  The slot-pool cache's device lookup and miss
+// copies are k_cache_lookup and k_cache_copy.
 //
 // Gating follows the MoE offload blog (mhpn.cn, section 3.1: router logits,
 // softmax, top-k; section 5.2: the batched form); matvecs that keep the
@@ -31,9 +33,12 @@
 // the MoE cache caches").
 //
 // Activation encoding.  Each block of 32 consecutive activation values v is
-// stored as three int8 pieces with one fp32 scale s = max|v|/127:
+// stored as three int8 pieces with one fp32 scale s = m/127:
 //     v ~= s * (x0 + x1/254 + x2/254^2),   |xi| <= 127,
-// an error below s * 7.8e-6 = max|v| * 6.1e-8, i.e. fp32 class.  Quantized
+// an error below s * 7.8e-6 = m * 6.1e-8, i.e. fp32 class.  m is the largest
+// magnitude of the 256-position super-block for the normalised input states
+// (one scale per Q4_K super-block, as the integer-MFMA kernels need) and of
+// the 32-value block itself for SiLU(g)*u.  Quantized
 // weights are small integers times per-block scales, so the product of a
 // weight block with an activation block is three exact integer dot products
 // (v_dot4 on 4 int8 lanes) and a few fp32 operations per block.  This keeps
@@ -212,10 +217,13 @@ struct Enc {
 __device__ __forceinline__ uint8_t *rec_at(const Enc &e, int vec, int K) { return e.base + (size_t)vec * 4 * K; }
 
 // Encode one 32-value block held by 32 consecutive lanes (lane r of the
-// group holds position pos0 + r) into record `rec`.
-__device__ __forceinline__ void encode32(float v, int r, uint8_t *rec, int K, int pos0)
+// group holds position pos0 + r) into record `rec`, with the scale a/127:
+// a = the block's own largest magnitude (amax < 0), or amax, a bound on it
+// shared by more blocks (the input states' records share one scale per
+// 256-position super-block, which the integer-MFMA kernels need).
+__device__ __forceinline__ void encode32(float v, int r, uint8_t *rec, int K, int pos0, float amax = -1.f)
 {
-    const float a = group_max<32>(fabsf(v));
+    const float a = amax >= 0.f ? amax : group_max<32>(fabsf(v));
     const float sm = group_sum<32>(v);
     const float inv = a > 0.f ? 127.0f / a : 0.f;
     const float r0 = v * inv, f0 = rintf(r0);
@@ -246,20 +254,27 @@ __device__ __forceinline__ void encode32(float v, int r, uint8_t *rec, int K, in
     }
 }
 
-// One position of a half-precision (MFMA) record: 256 consecutive threads
-// (a quarter or half of the workgroup, whole waves) hold positions p =
-// 0..255 of one super-block, v their value (0 past the vector's end); rec is
-// the super-block's record (kX16Bytes).  The largest magnitude comes from
-// the group's waves through redm (LDS, one float per wave); every thread of
-// the workgroup calls this (it holds barriers).
-__device__ __forceinline__ void encode_x16(float v, uint8_t *rec, int p, bool live, float *redm)
+// Largest of v over the 256 consecutive threads (4 whole waves: the waves
+// 4g .. 4g+3 of the caller's group g) of a workgroup; every thread calls it
+// (barriers inside).  redm: LDS of one float per wave.
+__device__ __forceinline__ float group256_max(float v, float *redm)
 {
-    const float am = group_max<64>(fabsf(v));
+    const float am = group_max<64>(v);
     if (lane_id() == 0) redm[wave_id()] = am;
     __syncthreads();
     const int g0 = wave_id() & ~3;
     const float cm = fmaxf(fmaxf(redm[g0], redm[g0 + 1]), fmaxf(redm[g0 + 2], redm[g0 + 3]));
     __syncthreads();  // redm is free again
+    return cm;
+}
+
+// One position of a half-precision (MFMA) record: 256 consecutive threads
+// (a quarter or half of the workgroup, whole waves) hold positions p =
+// 0..255 of one super-block, v their value (0 past the vector's end); rec is
+// the super-block's record (kX16Bytes), cm the super-block's largest
+// magnitude (group256_max).
+__device__ __forceinline__ void encode_x16(float v, uint8_t *rec, int p, bool live, float cm)
+{
     if (!live) return;
     const int e = cm > 0.f ? -ilogbf(cm) - 1 : 0;  // cm * 2^e in [0.5, 1)
     const float x = v * ldexpf(1.0f, e);           // exact (power of two)
@@ -1161,11 +1176,13 @@ __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
         const int pos = c * kEncPos + threadIdx.x;
         const float xv = pos < H ? a.h[(size_t)t * H + pos] * r : 0.f;
+        // one scale per 256-position super-block (4 whole waves)
+        const float sbmax = group256_max(fabsf(xv), redx);
         if (pos < H) {  // whole waves (H is a multiple of 256)
-            encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31);
+            encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31, sbmax);
         }
         if (a.x16)
-            encode_x16(xv, a.x16 + ((size_t)t * (H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, pos < H, redx);
+            encode_x16(xv, a.x16 + ((size_t)t * (H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, pos < H, sbmax);
         if (a.kd > a.I) {
             const int nenc = T * ne;
             for (int p = g; p < a.P; p += nenc)
@@ -1250,10 +1267,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
     const int t = blockIdx.x;
     for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x) {
         const float v = a.x[(size_t)t * a.H + pos];
-        encode32(v, threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31);
-        if (a.yzero) a.yzero[(size_t)t * a.H + pos] = 0.f;
         // blockDim = 256: one super-block per pass (H is a multiple of 256)
-        if (a.x16) encode_x16(v, a.x16 + ((size_t)t * (a.H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, true, redm);
+        const float sbmax = group256_max(fabsf(v), redm);
+        encode32(v, threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31, sbmax);
+        if (a.yzero) a.yzero[(size_t)t * a.H + pos] = 0.f;
+        if (a.x16) encode_x16(v, a.x16 + ((size_t)t * (a.H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, true, sbmax);
     }
     if (a.kd > a.I)
         for (int p = t; p < a.P; p += a.T)
@@ -2595,6 +2613,458 @@ __global__ __launch_bounds__(kDnMfmaThreads) void k_down_mfma(DownMfmaArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Integer-MFMA path: batches of 2..8 tokens on all-Q4_K experts.
+//
+// A Q4_K weight is w_i = d sc_j q_i - dmin m_j (sub-block j of 32 weights,
+// 6-bit sc_j and m_j, 4-bit q_i); an input activation is stored as
+// x_i = b (p0_i + p1_i/254 + p2_i/254^2) with int8 pieces p and one scale b
+// per 256-position super-block, plus the exact sums X_j of each 32-block.
+// Over one super-block,
+//     sum_i w_i x_i = d b sum_p 254^-p A_p - dmin sum_j m_j X_j,
+//     A_p = sum_i (sc_j q_i) p_{p,i}   (exact integers).
+// sc_j q_i (<= 945) does not fit int8, but sc_j = 8 sh_j + sl_j with
+// sh_j, sl_j <= 7 gives two int8 weight operands (sh q, sl q <= 105) and
+// A_p = 8 A_p^h + A_p^l: two v_mfma_i32_32x32x32_i8 per sub-block, whose 32
+// K positions are exactly one sub-block.  The 32 rows of the activation
+// operand are (token slot t, piece p) = (2 (c >> 3) + ((c >> 2) & 1), c & 3)
+// for row c (piece 3 is zero), so each lane of the result holds, for its
+// weight row, all pieces of tokens kh, kh+2, kh+4, kh+6 (kh = lane / 32).
+// The min term sum_j m_j X_j = b sum_j m_j (X_j / b) is one
+// v_mfma_f32_32x32x8_f16 per super-block (K = the 8 sub-blocks, X_j / b <=
+// 32 * 127 split into two fp16 parts in the rows of pieces 0 and 1, m_j
+// exact in fp16), so that large activations cannot overflow fp16.  Per super-block and lane: 5 weight
+// loads, 8 activation loads, 16 integer MFMAs, one fp16 MFMA and about 200
+// VALU operations (the nibble masks, 2 packed 16-bit multiplies per 4
+// weights, the epilogue) -- against the dot-product kernels' 3 v_dot4 per
+// weight per 4 tokens.
+//
+// MFMA lane layouts (for both operands, lane l: operand row/column l % 32,
+// the K half l / 32 holding K positions 16 (l/32) + [0, 16) for the i8 form
+// and 4 (l/32) + [0, 4) for the fp16 K=8 form); result element e of lane l:
+// row 8 (e >> 2) + 4 (l >> 5) + (e & 3) of the activation operand, column
+// l % 32 (the weight row).
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kI8Tok = 8;      // tokens (pairs) per work entry
+constexpr int kI8DnKG = 3;     // down K-groups
+constexpr int kI8DnRW = 2;     // down 32-row blocks per workgroup
+constexpr float kInv254 = 1.0f / 254.0f, kInv254sq = 1.0f / 64516.0f;
+
+// sc and m of the 8 sub-blocks of one Q4_K row (meta = d|dmin, 12 scale bytes)
+struct Q4KMeta {
+    float d, dmin;
+    uint32_t sc03, sc47, m03, m47;  // byte j: sub-block j (and 4 + j)
+};
+__device__ __forceinline__ Q4KMeta q4k_meta(const uint4 &meta)
+{
+    Q4KMeta r;
+    r.d = half_lo(meta.x);
+    r.dmin = half_hi(meta.x);
+    const uint32_t W0 = meta.y, W1 = meta.z, W2 = meta.w;
+    r.sc03 = W0 & 0x3F3F3F3Fu;
+    r.m03 = W1 & 0x3F3F3F3Fu;
+    r.sc47 = (W2 & 0x0F0F0F0Fu) | ((W0 >> 2) & 0x30303030u);
+    r.m47 = ((W2 >> 4) & 0x0F0F0F0Fu) | ((W1 >> 2) & 0x30303030u);
+    return r;
+}
+
+// (v, v) in the two 16-bit halves, v = byte b of w
+template <int B> __device__ __forceinline__ uint32_t bcast16(uint32_t w)
+{
+    return __builtin_amdgcn_perm(0u, w, (0x0c0c0c0cu & ~0x00ff00ffu) | ((uint32_t)B << 16) | (uint32_t)B);
+}
+
+// 16 nibbles (one u32 per 4 K positions, in K order) times an int8 scale
+// (s, s) in both 16-bit halves: q * s <= 105 stays in its byte.
+__device__ __forceinline__ i32x4 qscale(const uint32_t (&q)[4], uint32_t ss)
+{
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    i32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        r[i] = (int)__builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, q[i]) * __builtin_bit_cast(s16x2, ss));
+    return r;
+}
+
+// The activation operand's source for one lane: token slot t and piece p of
+// operand row lane % 32; invalid rows read a zero block (stride 0).
+struct I8Src {
+    const uint8_t *rec;  // the token's record (or the zero block)
+    int pstride;         // piece offset (K of the record) or 0
+    int valid;           // 1 if this row is (token < n, piece < 3)
+    int pcol;            // piece of this row (0..3)
+};
+
+// One super-block of one 32-row block: y[jj] += b_t (d sum_p 254^-p A_p -
+// dmin M_t) for token slots t = 2 jj + kh.  `aop(s)` returns the activation
+// operand of K-step s (sub-block s of the super-block), `sums()` this lane's
+// 4 block sums (sub-blocks 4 kh + [0, 4)) of its row's token divided by that
+// token's super-block scale b, `scale(jj)` the scale b of token slot 2 jj + kh.
+template <class AOp, class Sums, class Scale>
+__device__ __forceinline__ void i8_super(const uint4 &meta, const uint4 (&qp)[4], int kh, int prow, AOp aop,
+                                         Sums sums, Scale scale, float (&y)[4], int n)
+{
+    const Q4KMeta mt = q4k_meta(meta);
+    const uint32_t sh03 = (mt.sc03 >> 3) & 0x07070707u, sl03 = mt.sc03 & 0x07070707u;
+    const uint32_t sh47 = (mt.sc47 >> 3) & 0x07070707u, sl47 = mt.sc47 & 0x07070707u;
+    i32x16 ah = {}, al = {};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        // plane 2c + kh: bytes 16 kh + [0, 16) of quant chunk c; low nibbles
+        // are sub-block 2c, high nibbles sub-block 2c + 1
+        const uint32_t w[4] = {qp[c].x, qp[c].y, qp[c].z, qp[c].w};
+#pragma unroll
+        for (int nib = 0; nib < 2; nib++) {
+            const int sbk = 2 * c + nib;
+            uint32_t q[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) q[i] = (nib ? w[i] >> 4 : w[i]) & 0x0F0F0F0Fu;
+            uint32_t hs, ls;
+            switch (sbk) {  // compile-time after unrolling
+            case 0: hs = bcast16<0>(sh03); ls = bcast16<0>(sl03); break;
+            case 1: hs = bcast16<1>(sh03); ls = bcast16<1>(sl03); break;
+            case 2: hs = bcast16<2>(sh03); ls = bcast16<2>(sl03); break;
+            case 3: hs = bcast16<3>(sh03); ls = bcast16<3>(sl03); break;
+            case 4: hs = bcast16<0>(sh47); ls = bcast16<0>(sl47); break;
+            case 5: hs = bcast16<1>(sh47); ls = bcast16<1>(sl47); break;
+            case 6: hs = bcast16<2>(sh47); ls = bcast16<2>(sl47); break;
+            default: hs = bcast16<3>(sh47); ls = bcast16<3>(sl47); break;
+            }
+            const i32x4 a = aop(sbk);
+            ah = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qscale(q, hs), ah, 0, 0, 0);
+            al = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qscale(q, ls), al, 0, 0, 0);
+        }
+    }
+    // min term: rows of piece 0 / 1 carry the high / low fp16 part of X_j
+    const float4 xs = sums();
+    f16x4 am;
+    {
+        const float v[4] = {xs.x, xs.y, xs.z, xs.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const _Float16 h = (_Float16)v[i];
+            am[i] = prow == 0 ? h : prow == 1 ? (_Float16)(v[i] - (float)h) : (_Float16)0.f;
+        }
+    }
+    const uint32_t mw = kh ? mt.m47 : mt.m03;
+    const f16x4 bm = {(_Float16)(float)(mw & 0xff), (_Float16)(float)((mw >> 8) & 0xff),
+                      (_Float16)(float)((mw >> 16) & 0xff), (_Float16)(float)(mw >> 24)};
+    f32x16 cm = {};
+    cm = __builtin_amdgcn_mfma_f32_32x32x8f16(am, bm, cm, 0, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+        if (2 * jj + kh < n) {
+            const float A0 = (float)(8 * ah[4 * jj] + al[4 * jj]);
+            const float A1 = (float)(8 * ah[4 * jj + 1] + al[4 * jj + 1]);
+            const float A2 = (float)(8 * ah[4 * jj + 2] + al[4 * jj + 2]);
+            const float v = fmaf(A2, kInv254sq, fmaf(A1, kInv254, A0));
+            y[jj] = fmaf(scale(jj), fmaf(mt.d, v, -mt.dmin * (cm[4 * jj] + cm[4 * jj + 1])), y[jj]);
+        }
+    }
+}
+
+// This lane's activation-operand row: token slot and piece of row lane % 32.
+__device__ __forceinline__ void i8_row(int lane, int &tslot, int &piece)
+{
+    const int c = lane & 31;
+    tslot = 2 * (c >> 3) + ((c >> 2) & 1);
+    piece = c & 3;
+}
+
+// k_gate_up_i8: workgroup (u, rb) = distinct expert u, rows [64 rb, 64 rb +
+// 64) of gate and up (one 64-row tile of each): wave w takes matrix w & 1,
+// 32-row block (w >> 1) & 1 and the super-blocks g, g + kI8GUKG, ... (g =
+// w >> 2).
+// The entry's token records (pieces, scales, block sums) are first staged in
+// LDS (rows of H + 16 bytes, so that the 24 operand rows of one MFMA read
+// fall in different banks), while each wave's first weights are in flight;
+// the next super-block's weights are loaded during the current one's MFMAs.
+// The K-groups' partial sums meet in LDS (over the staged records, once every
+// wave is done with them); SiLU(g)*u of each pair goes to hf (fp32).
+struct GateUpI8Args {
+    const void *const *eptr;
+    const void *const *sptr;
+    int E;
+    const WorkEntry *wt;
+    const int *nuniq;
+    Enc x;              // [T] input records of H
+    int H, I, kd;
+    unsigned long long up_off;
+    float *hf;          // [P][kd]
+    float *act_out;     // [P][kd] or null
+    int nrb;            // I / 64
+};
+
+constexpr int kI8GUKG = 4;  // gate/up K-groups
+constexpr int kGUI8Threads = 2 * 2 * kI8GUKG * 64;
+constexpr int kI8MaxH = 2048;  // LDS-staged records of up to this many positions
+// dynamic LDS of k_gate_up_i8: 3 kI8Tok piece rows of H + 16 bytes, then
+// scales and block sums (kI8Tok x H/32 floats each), then 16 zero bytes
+__host__ __device__ constexpr size_t i8_gu_lds(int H)
+{
+    const size_t st = (size_t)3 * kI8Tok * (H + 16) + (size_t)2 * kI8Tok * (H / 32) * 4 + 16;
+    const size_t pt = (size_t)kI8GUKG * 2 * 2 * kI8Tok * 33 * 4;  // the partial sums, after the staging
+    return st > pt ? st : pt;
+}
+
+__device__ __forceinline__ void load_q4k_plane_row(uint4 &meta, uint4 (&qp)[4], const uint8_t *tile, int row64, int kh)
+{
+    meta = ldg<uint4>(tile, row64 * 16);
+#pragma unroll
+    for (int c = 0; c < 4; c++) qp[c] = ldg<uint4>(tile, 1024 + (2 * c + kh) * 1024 + row64 * 16);
+}
+
+__global__ __launch_bounds__(kGUI8Threads) __attribute__((amdgpu_waves_per_eu(4))) void k_gate_up_i8(GateUpI8Args a)
+{
+    extern __shared__ __align__(16) uint8_t lx[];
+    const int u = blockIdx.x / a.nrb, rb = blockIdx.x - u * a.nrb;
+    if (u >= uni(*a.nuniq)) return;
+    const WorkEntry we = load_entry(a.wt, u);
+    const int p0 = we.p0, n = we.p1 - we.p0;
+    const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]);
+    const int wv = wave_id(), lane = lane_id(), kh = lane >> 5, r = lane & 31;
+    const int m = wv & 1, rb2 = (wv >> 1) & 1, kg = wv >> 2;
+    const int H = a.H, S = H >> 8, RS = H + 16, NB = H / 32;
+    const uint8_t *mat = base + (m ? a.up_off : 0);
+    const int row64 = rb2 * 32 + r;
+    const size_t tile0 = (size_t)rb * S;
+    // this wave's first super-block's weights, in flight during the staging
+    uint4 meta = make_uint4(0, 0, 0, 0), qp[4] = {};
+    if (kg < S) load_q4k_plane_row(meta, qp, mat + (tile0 + kg) * kTileBytes<MOE_Q4_K>, row64, kh);
+    uint64_t toks;  // byte t = the entry's token slot t (shifts: no indexed private array)
+    __builtin_memcpy(&toks, we.tok, sizeof(toks));
+    // staging: piece rows (16-byte chunks), then scales and block sums
+    float *lbs = (float *)(lx + (size_t)3 * kI8Tok * RS);
+    float *lsum = lbs + kI8Tok * NB;
+    uint8_t *lzero = (uint8_t *)(lsum + kI8Tok * NB);
+    {
+        const int cpr = H / 16;  // chunks per piece row
+        const int nrow = 3 * n, nch = nrow * cpr;
+        constexpr int kMaxCh = (3 * kI8Tok * kI8MaxH / 16 + kGUI8Threads - 1) / kGUI8Threads;
+        u32x4 v[kMaxCh];
+#pragma unroll
+        for (int i = 0; i < kMaxCh; i++) {
+            const int c = (int)threadIdx.x + i * kGUI8Threads;
+            const int row = c / cpr, w = c - row * cpr;
+            const int t = row / 3, p = row - 3 * t;
+            if (c < nch) v[i] = *(const u32x4 *)(rec_at(a.x, (int)((toks >> (8 * t)) & 0xff), H) + (size_t)p * H + 16 * w);
+        }
+        const int nsc = n * NB;  // scales and sums: one float each
+        constexpr int kMaxSc = (2 * kI8Tok * kI8MaxH / 32 + kGUI8Threads - 1) / kGUI8Threads;
+        float sv[kMaxSc];
+        int si[kMaxSc];
+#pragma unroll
+        for (int i = 0; i < kMaxSc; i++) {
+            si[i] = -1;
+            sv[i] = 0.f;
+            const int c = (int)threadIdx.x + i * kGUI8Threads;
+            if (c < 2 * nsc) {
+                const int which = c >= nsc, cc = c - which * nsc, t = cc / NB, b = cc - t * NB;
+                const float *src = (const float *)(rec_at(a.x, (int)((toks >> (8 * t)) & 0xff), H) + 3 * (size_t)H);
+                sv[i] = src[which * NB + b];
+                si[i] = which * kI8Tok * NB + t * NB + b;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxCh; i++) {
+            const int c = (int)threadIdx.x + i * kGUI8Threads;
+            const int row = c / cpr, w = c - row * cpr;
+            if (c < nch) *(u32x4 *)(lx + (size_t)row * RS + 16 * w) = v[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxSc; i++)
+            if (si[i] >= 0) lbs[si[i]] = sv[i];
+        if (threadIdx.x < 4) ((uint32_t *)lzero)[threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    int tslot, piece;
+    i8_row(lane, tslot, piece);
+    const bool valid = tslot < n && piece < 3;
+    const uint8_t *asrc = valid ? lx + (size_t)(tslot * 3 + piece) * RS + 16 * kh : lzero;
+    const int astep = valid ? 32 : 0;
+    const bool svalid = tslot < n && piece < 2;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sb = kg; sb < S; sb += kI8GUKG) {
+        uint4 nmeta = make_uint4(0, 0, 0, 0), nqp[4] = {};
+        if (sb + kI8GUKG < S)
+            load_q4k_plane_row(nmeta, nqp, mat + (tile0 + sb + kI8GUKG) * kTileBytes<MOE_Q4_K>, row64, kh);
+        const uint8_t *ab = asrc + (valid ? sb * 256 : 0);
+        float4 xs = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (svalid) {
+            xs = *(const float4 *)(lsum + tslot * NB + sb * 8 + 4 * kh);
+            const float b = lbs[tslot * NB + sb * 8];
+            const float ib = b > 0.f ? 1.0f / b : 0.f;
+            xs.x *= ib; xs.y *= ib; xs.z *= ib; xs.w *= ib;
+        }
+        i8_super(meta, qp, kh, piece, [&](int s) { return *(const i32x4 *)(ab + s * astep); }, [&]() { return xs; },
+                 [&](int jj) {
+                     const int t = 2 * jj + kh;
+                     return lbs[(t < n ? t : 0) * NB + sb * 8];
+                 },
+                 y, n);
+        meta = nmeta;
+#pragma unroll
+        for (int c = 0; c < 4; c++) qp[c] = nqp[c];
+    }
+    __syncthreads();  // every wave is done with the staged records
+    float(*part)[2][2][kI8Tok][33] = (float(*)[2][2][kI8Tok][33])lx;  // [K-group][matrix][32-row block][token][row]
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) part[kg][m][rb2][2 * jj + kh][r] = y[jj];
+    __syncthreads();
+    for (int i = threadIdx.x; i < n * 64; i += blockDim.x) {
+        const int t = i >> 6, rr = i & 63, b2 = rr >> 5, r5 = rr & 31;
+        float g = 0.f, uu = 0.f;
+#pragma unroll
+        for (int q = 0; q < kI8GUKG; q++) {
+            g += part[q][0][b2][t][r5];
+            uu += part[q][1][b2][t][r5];
+        }
+        const float hv = g / (1.0f + expf(-g)) * uu;
+        const size_t o = (size_t)(p0 + t) * a.kd + rb * 64 + rr;
+        a.hf[o] = hv;
+        if (a.act_out) a.act_out[o] = hv;
+    }
+}
+
+// k_down_i8: workgroup (u, rt) = distinct expert u, down rows [64 rt, 64 rt
+// + 64) (kI8DnRW blocks of 32) x kI8DnKG K-groups.  The pairs' SiLU(g)*u
+// (fp32, positions >= I zero) are first encoded in LDS with one scale per
+// super-block (a wave per (pair, super-block): 4 positions per lane; piece
+// rows of kd + 16 bytes, then scales and block sums); then the MFMA loop as
+// in k_gate_up_i8; the K-groups' partial sums meet in LDS and each pair's
+// rows, times its combine weight, are added into y.
+struct DownI8Args {
+    const void *const *eptr;
+    const void *const *sptr;
+    int E;
+    const int *nuniq;
+    const WorkEntry *wt;
+    const float *hf;   // [P][kd]
+    int H, I, kd;
+    unsigned long long down_off;
+    int nrt;           // H / 64
+    const int *ptok;
+    const float *pw;
+    float *y;
+};
+
+constexpr int kDnI8Threads = kI8DnRW * kI8DnKG * 64;
+constexpr int kDnI8MaxKd = 1536;  // LDS records of up to this many positions
+// one pair's LDS record: 3 piece rows of K + 16 bytes, scales and block sums
+__host__ __device__ constexpr int i8_dn_rec(int K) { return 3 * (K + 16) + 2 * (K / 32) * 4; }
+
+__global__ __launch_bounds__(kDnI8Threads) __attribute__((amdgpu_waves_per_eu(5))) void k_down_i8(DownI8Args a)
+{
+    extern __shared__ __align__(16) uint8_t lrec_base[];  // kI8Tok records of i8_dn_rec(kd) bytes
+    __shared__ __align__(16) uint8_t lzero[16];
+    __shared__ float part[kI8DnRW][kI8DnKG][kI8Tok][33];
+    const int u = blockIdx.x / a.nrt, rt = blockIdx.x - u * a.nrt;
+    if (u >= uni(*a.nuniq)) return;
+    const WorkEntry we = load_entry(a.wt, u);
+    const int p0 = we.p0, n = we.p1 - we.p0;
+    const uint8_t *base =
+        (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]) + a.down_off;
+    const int wv = wave_id(), lane = lane_id(), kh = lane >> 5, r = lane & 31;
+    const int rw = wv / kI8DnKG, q = wv - rw * kI8DnKG;
+    const int K = a.kd, S = K >> 8, RS = K + 16, RR = i8_dn_rec(K);
+    const int row64 = rw * 32 + r;
+    const size_t tile0 = (size_t)rt * S;
+    // this wave's first super-block's weights, in flight during the encoding
+    uint4 meta = make_uint4(0, 0, 0, 0), qp[4];
+    if (q < S) {
+        const uint8_t *tile = base + (tile0 + q) * kTileBytes<MOE_Q4_K>;
+        meta = ldg<uint4>(tile, row64 * 16);
+#pragma unroll
+        for (int c = 0; c < 4; c++) qp[c] = ldg<uint4>(tile, 1024 + (2 * c + kh) * 1024 + row64 * 16);
+    }
+    // encode (pair, super-block) units, a wave's units loaded at once
+    if (threadIdx.x < 4) ((uint32_t *)lzero)[threadIdx.x] = 0u;
+    constexpr int kUnits = 4;  // units per wave per round (loaded at once)
+    for (int u0 = wv; u0 < n * S; u0 += kUnits * (kDnI8Threads / 64)) {
+    float4 uv[kUnits];
+#pragma unroll
+    for (int i = 0; i < kUnits; i++) {
+        const int unit = u0 + i * (kDnI8Threads / 64);
+        const int t = unit / S, pos = (unit - t * S) * 256 + 4 * lane;
+        uv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (unit < n * S && pos < a.I) uv[i] = *(const float4 *)(a.hf + (size_t)(p0 + t) * K + pos);  // I: multiple of 32
+    }
+#pragma unroll
+    for (int i = 0; i < kUnits; i++) {
+        const int unit = u0 + i * (kDnI8Threads / 64);
+        if (unit >= n * S) break;
+        const int t = unit / S, sb = unit - t * S;
+        const int pos = sb * 256 + 4 * lane;
+        const float4 v = uv[i];
+        const float am = group_max<64>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        const float inv = am > 0.f ? 127.0f / am : 0.f;
+        uint32_t w0 = 0, w1 = 0, w2 = 0;
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float r0 = vv[i] * inv, f0 = rintf(r0);
+            const float r1 = (r0 - f0) * 254.0f, f1 = rintf(r1);
+            const float r2 = (r1 - f1) * 254.0f, f2 = rintf(r2);
+            w0 |= ((uint32_t)(int)f0 & 0xffu) << (8 * i);
+            w1 |= ((uint32_t)(int)f1 & 0xffu) << (8 * i);
+            w2 |= ((uint32_t)(int)f2 & 0xffu) << (8 * i);
+        }
+        uint8_t *rec = lrec_base + (size_t)t * RR;
+        *(uint32_t *)(rec + pos) = w0;
+        *(uint32_t *)(rec + RS + pos) = w1;
+        *(uint32_t *)(rec + 2 * RS + pos) = w2;
+        const float bs = group_sum<8>(v.x + v.y + v.z + v.w);  // 32 positions = 8 lanes
+        if ((lane & 7) == 0) ((float *)(rec + 3 * RS + K / 8))[sb * 8 + (lane >> 3)] = bs;
+        if (lane < 8) ((float *)(rec + 3 * RS))[sb * 8 + lane] = am / 127.0f;
+    }
+    }
+    __syncthreads();
+    int tslot, piece;
+    i8_row(lane, tslot, piece);
+    const bool valid = tslot < n && piece < 3;
+    const uint8_t *trec = lrec_base + (size_t)(tslot < n ? tslot : 0) * RR;
+    const uint8_t *asrc = valid ? trec + (size_t)piece * RS + 16 * kh : lzero;
+    const int astep = valid ? 32 : 0;
+    const bool svalid = tslot < n && piece < 2;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sb = q; sb < S; sb += kI8DnKG) {
+        if (sb != q) {
+            const uint8_t *tile = base + (tile0 + sb) * kTileBytes<MOE_Q4_K>;
+            meta = ldg<uint4>(tile, row64 * 16);
+#pragma unroll
+            for (int c = 0; c < 4; c++) qp[c] = ldg<uint4>(tile, 1024 + (2 * c + kh) * 1024 + row64 * 16);
+        }
+        const uint8_t *ab = asrc + (valid ? sb * 256 : 0);
+        float4 xs = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (svalid) {
+            xs = *(const float4 *)(trec + 3 * RS + K / 8 + 4 * (sb * 8 + 4 * kh));
+            const float b = ((const float *)(trec + 3 * RS))[sb * 8];
+            const float ib = b > 0.f ? 1.0f / b : 0.f;
+            xs.x *= ib; xs.y *= ib; xs.z *= ib; xs.w *= ib;
+        }
+        i8_super(meta, qp, kh, piece, [&](int s) { return *(const i32x4 *)(ab + s * astep); },
+                 [&]() { return xs; },
+                 [&](int jj) {
+                     const int t = 2 * jj + kh;
+                     return ((const float *)(lrec_base + (size_t)(t < n ? t : 0) * RR + 3 * RS))[sb * 8];
+                 },
+                 y, n);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) part[rw][q][2 * jj + kh][r] = y[jj];
+    __syncthreads();
+    for (int i = threadIdx.x; i < n * kI8DnRW * 32; i += blockDim.x) {
+        const int t = i / (kI8DnRW * 32), rr = i - t * (kI8DnRW * 32);
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < kI8DnKG; k++) v += part[rr >> 5][k][t][rr & 31];
+        add_to(a.y + (size_t)a.ptok[p0 + t] * a.H + rt * 64 + rr, a.pw[p0 + t] * v);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Slot-pool lookup on the device (the same LRU as the host lookup, T4
 // MoE-cache report, sections "What the MoE cache caches" and "Size your
 // experts before configuring"): the layer-step's distinct selected experts
@@ -2955,6 +3425,42 @@ bool use_mfma(const moe_expert_desc &d, int T)
     return T > kMfmaMinT && d.gate == MOE_Q4_K && d.up == MOE_Q4_K && d.down == MOE_Q4_K && d.H % 128 == 0;
 }
 
+// The integer-MFMA path takes batches of 2 .. kI8Tok tokens on all-Q4_K
+// experts (one work entry per distinct expert, at most kI8Tok pairs each).
+bool use_i8(const moe_expert_desc &d, int T)
+{
+    return T >= 2 && T <= kI8Tok && d.gate == MOE_Q4_K && d.up == MOE_Q4_K && d.down == MOE_Q4_K && d.I % 64 == 0 &&
+           down_k(d) <= kDnI8MaxKd && d.H <= kI8MaxH;
+}
+
+// Work items of at most kItemTok pairs for the dot-product kernels; one
+// entry per distinct expert for the MFMA kernels.
+bool dot_items(const moe_expert_desc &d, int T) { return !use_mfma(d, T) && !use_i8(d, T); }
+
+moe_status launch_ffn_i8(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int E, const void *const *eptr,
+                         const void *const *sptr, float *y, float *act_out, hipStream_t s)
+{
+    const WsLayout &L = ws.L;
+    GateUpI8Args ga;
+    ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
+    ga.wt = ws.at<WorkEntry>(L.wt); ga.nuniq = ws.at<int>(L.nuniq);
+    ga.x = ws.x();
+    ga.H = d.H; ga.I = d.I; ga.kd = g.kd; ga.up_off = g.up_off;
+    ga.hf = ws.at<float>(L.hf); ga.act_out = act_out;
+    ga.nrb = d.I / 64;
+    k_gate_up_i8<<<L.U * ga.nrb, kGUI8Threads, i8_gu_lds(d.H), s>>>(ga);
+    LAUNCH_OK("k_gate_up_i8");
+    DownI8Args da;
+    da.eptr = eptr; da.sptr = sptr; da.E = E;
+    da.nuniq = ga.nuniq; da.wt = ga.wt; da.hf = ga.hf;
+    da.H = d.H; da.I = d.I; da.kd = g.kd; da.down_off = g.down_off;
+    da.nrt = d.H / 64;
+    da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
+    k_down_i8<<<L.U * da.nrt, kDnI8Threads, (size_t)kI8Tok * i8_dn_rec(g.kd), s>>>(da);
+    LAUNCH_OK("k_down_i8");
+    return MOE_OK;
+}
+
 // The FFN launches add into y (moe_expert_ffn clears it first when not
 // accumulating); the routing is the grouping in the workspace.
 moe_status launch_ffn_mfma(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
@@ -3009,6 +3515,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
                               float *act_out, hipStream_t s, bool defer = false)
 {
     if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, T, E, eptr, sptr, y, act_out, s);
+    if (use_i8(d, T)) return launch_ffn_i8(d, g, ws, E, eptr, sptr, y, act_out, s);
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -3169,7 +3676,7 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     PrepArgs pa{};
     pa.x = x; pa.T = T; pa.H = d->H; pa.k = k; pa.E = E; pa.ns = n_shared; pa.idx = idx; pa.w = w;
     pa.yzero = accumulate ? nullptr : y;
-    pa.xe = W.x(); pa.go = W.group(!use_mfma(*d, T)); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
+    pa.xe = W.x(); pa.go = W.group(dot_items(*d, T)); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
     pa.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
@@ -3207,7 +3714,7 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
     a.x = W.x();
     a.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
-    a.group = 1; a.ns = n_shared; a.go = W.group(!use_mfma(*d, T));
+    a.group = 1; a.ns = n_shared; a.go = W.group(dot_items(*d, T));
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
     // router workgroups: row pairs x token groups of kRouteTok

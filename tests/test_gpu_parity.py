@@ -142,6 +142,10 @@ FFN_CASES = [
     ((W.Q4_K, W.Q4_K, W.Q6_K), 768, 256, 9, 4, 2, 11, False),
     ((W.Q8_0, W.Q8_0, W.Q4_K), 1024, 128, 4, 4, 0, 32, False),
     ((W.Q4_K,) * 3, 2048, 768, 16, 8, 0, 8, True),
+    # all-Q4_K experts with 2..8 tokens take the integer-MFMA path
+    ((W.Q4_K,) * 3, 1024, 320, 8, 4, 2, 5, False),      # shared experts, ragged I (down rows padded to 512)
+    ((W.Q4_K,) * 3, 8192, 256, 8, 2, 0, 8, False),      # H = 8192: 32 super-blocks per gate/up row
+    ((W.Q4_K,) * 3, 2048, 1408, 64, 2, 2, 4, True),     # the mixed stack's Q4_K shape: I = 1408, 1536 down columns
     # all-Q4_K experts with more than 8 tokens take the MFMA path
     ((W.Q4_K,) * 3, 512, 192, 6, 2, 0, 9, False),       # just above the threshold; down rows padded
     ((W.Q4_K,) * 3, 1024, 320, 8, 8, 0, 32, False),     # every token on every expert: 32 columns; ragged I
