@@ -37,8 +37,8 @@
 //     v ~= s * (x0 + x1/254 + x2/254^2),   |xi| <= 127,
 // an error below s * 7.8e-6 = m * 6.1e-8, i.e. fp32 class.  m is the largest
 // magnitude of the 256-position super-block for the normalised input states
-// (one scale per Q4_K super-block, as the integer-MFMA kernels need) and of
-// the 32-value block itself for SiLU(g)*u.  Quantized
+// of batches on the integer-MFMA path (one scale per Q4_K super-block) and of
+// the 32-value block itself otherwise.  Quantized
 // weights are small integers times per-block scales, so the product of a
 // weight block with an activation block is three exact integer dot products
 // (v_dot4 on 4 int8 lanes) and a few fp32 operations per block.  This keeps
@@ -678,6 +678,7 @@ struct RouteArgs {
     unsigned long long *tk; // [T][k] hand-over of those selections (key << 32 | ~id, never zero)
     int tail;               // 1: the last workgroup routes (keys handed over); 0: no tail
     uint32_t *dlog;         // [E] (T = 1) the logit keys for routing in the FFN (plain stores), or null
+    int sb_scale;           // 1: the input records share one scale per 256-position super-block
     uint32_t *status;       // the workspace's status word: nonzero = a wait gave up earlier (sticky)
     unsigned spin;          // polling rounds before a wait gives up
     int withhold;           // 1: the router workgroups store no keys (forced give-up, for tests)
@@ -1176,10 +1177,11 @@ __global__ __launch_bounds__(kRouteWG) void k_route(RouteArgs a)
         const float r = a.normalize ? 1.0f / sqrtf(ss / (float)H + a.eps) : 1.0f;
         const int pos = c * kEncPos + threadIdx.x;
         const float xv = pos < H ? a.h[(size_t)t * H + pos] * r : 0.f;
-        // one scale per 256-position super-block (4 whole waves)
-        const float sbmax = group256_max(fabsf(xv), redx);
+        // one scale per 256-position super-block (4 whole waves) when the
+        // integer-MFMA or half-precision records need it, else per block
+        const float sbmax = a.sb_scale || a.x16 ? group256_max(fabsf(xv), redx) : -1.f;
         if (pos < H) {  // whole waves (H is a multiple of 256)
-            encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31, sbmax);
+            encode32(xv, threadIdx.x & 31, rec_at(a.x, t, H), H, pos & ~31, a.sb_scale ? sbmax : -1.f);
         }
         if (a.x16)
             encode_x16(xv, a.x16 + ((size_t)t * (H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, pos < H, sbmax);
@@ -1254,6 +1256,7 @@ struct PrepArgs {
     float *yzero;    // [T][H] cleared here (the FFN adds into it), or null
     Enc xe;
     uint8_t *x16;    // [T][H/256] half-precision records of x, or null
+    int sb_scale;    // 1: one record scale per 256-position super-block
     GroupOut go;
     Enc hpad;
     int P, I, kd;
@@ -1268,8 +1271,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_prep(PrepArgs a)
     for (int pos = threadIdx.x; pos < a.H; pos += blockDim.x) {
         const float v = a.x[(size_t)t * a.H + pos];
         // blockDim = 256: one super-block per pass (H is a multiple of 256)
-        const float sbmax = group256_max(fabsf(v), redm);
-        encode32(v, threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31, sbmax);
+        const float sbmax = a.sb_scale || a.x16 ? group256_max(fabsf(v), redm) : -1.f;
+        encode32(v, threadIdx.x & 31, rec_at(a.xe, t, a.H), a.H, pos & ~31, a.sb_scale ? sbmax : -1.f);
         if (a.yzero) a.yzero[(size_t)t * a.H + pos] = 0.f;
         if (a.x16) encode_x16(v, a.x16 + ((size_t)t * (a.H >> 8) + (pos >> 8)) * kX16Bytes, pos & 255, true, sbmax);
     }
@@ -3678,6 +3681,7 @@ moe_status moe_expert_ffn(const moe_expert_desc *d, const float *x, int32_t T, i
     pa.yzero = accumulate ? nullptr : y;
     pa.xe = W.x(); pa.go = W.group(dot_items(*d, T)); pa.hpad = W.h(); pa.P = W.L.P; pa.I = d->I; pa.kd = g.kd;
     pa.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
+    pa.sb_scale = use_i8(*d, T);
     pa.go.eptr = expert_ptrs; pa.go.sptr = shared_ptrs;
     k_prep<<<T, kRouteThreads, 0, s>>>(pa);
     LAUNCH_OK("k_prep");
@@ -3714,6 +3718,7 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.idx2 = idx_out; a.w2 = w_out; a.logits2 = nullptr;
     a.x = W.x();
     a.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
+    a.sb_scale = use_i8(*d, T);
     a.group = 1; a.ns = n_shared; a.go = W.group(dot_items(*d, T));
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
