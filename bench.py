@@ -50,6 +50,19 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode tokens/s (layer stack) + achieved HBM GB/s on expert bytes read"
 HBM_PEAK_GBPS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+MFMA_I8_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix peak
+
+# the FFN kernels each batch size runs on (the library's choice for all-Q4_K
+# experts: dot products at T=1, integer MFMA at T=2..8, fp16 MFMA above)
+FFN_KERNELS = {
+    "dot": "expert FFN (k_gate_up + k_down of moe_layer_ffn)",
+    "i8": "expert FFN (k_gate_up_i8 + k_down_i8: integer MFMA)",
+    "f16": "expert FFN (k_gate_up_mfma + k_down_mfma: fp16 MFMA)",
+}
+
+
+def ffn_path(T: int) -> str:
+    return "dot" if T == 1 else "i8" if T <= 8 else "f16"
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "expert_ffn_qwen3_30b_q4k_hbm_traffic.md")
 KERNEL_SOURCES = ("moe_kernels.hip", "moe_internal.h")
 
@@ -622,20 +635,21 @@ def roof_hbm(tm, traffic=None, kernel="expert FFN (k_gate_up + k_down of moe_lay
             "launches": tm["launches"]}
 
 
-def resident_leg(st, T: int, args, seed: int, traffic=None, mfma=False):
+def resident_leg(st, T: int, args, seed: int, traffic=None, kernel=None):
     """Throughput (graph replays) and the per-layer FFN roofline of one stack at batch T."""
     tps, ms, pct = throughput(st, T, args.steps, args.warmup, st.layers[0].H, seed=seed)
     tm = ffn_timing(st, T, args.timing_steps, st.layers[0].H, seed=seed)
+    path = ffn_path(T)
     leg = {"value": round(tps, 2), "unit": "tokens/s", "ms_per_step": round(ms, 4), "step_ms_percentiles": pct,
-           "roofline": roof_hbm(tm, traffic, "expert FFN (k_gate_up_mfma + k_down_mfma)" if mfma else
-                                "expert FFN (k_gate_up + k_down of moe_layer_ffn)"),
+           "roofline": roof_hbm(tm, traffic, kernel or FFN_KERNELS[path]),
            "route_us_per_layer": round(tm["route_us"], 3)}
-    if mfma:
-        # the matrix cores: the pairs' algorithmic flops (2 per multiply-add of gate, up and
-        # down) per FFN launch, against the fp16 dense peak the kernels issue on
-        leg["mfma"] = {"bound": "mfma", "achieved": round(tm["tflops"], 2), "peak": MFMA_FP16_PEAK_TFLOPS,
-                       "unit": "TFLOP/s", "frac": round(tm["tflops"] / MFMA_FP16_PEAK_TFLOPS, 4),
-                       "flop_per_launch": round(tm["flop_per_launch"])}
+    if path != "dot" and kernel is None:
+        # the matrix cores: the pairs' algorithmic operations (2 per multiply-add of gate, up
+        # and down) per FFN launch, against the dense peak of the type the kernels issue on
+        peak = MFMA_I8_PEAK_TOPS if path == "i8" else MFMA_FP16_PEAK_TFLOPS
+        leg["mfma"] = {"bound": "mfma", "achieved": round(tm["tflops"], 2), "peak": peak,
+                       "unit": "TOP/s (int8)" if path == "i8" else "TFLOP/s",
+                       "frac": round(tm["tflops"] / peak, 4), "flop_per_launch": round(tm["flop_per_launch"])}
     log(f"T={T}: {tps:.1f} tok/s, {ms:.3f} ms/step {pct}; FFN {tm['ffn_us']:.2f} us/launch "
         f"{tm['gbps']:.0f} GB/s ({tm['bytes_per_launch'] / 1e6:.2f} MB), route {tm['route_us']:.2f} us")
     return leg, tm
@@ -708,7 +722,7 @@ def main():
         zc = cfg.with_(zipf_s=1.1, T=32)
         saved = st.biases
         st.biases = [torch.from_numpy(W.zipf_bias(zc, l)).to(st.device) for l in range(cfg.n_layers)]
-        zipf32, _ = resident_leg(st, 32, args, seed=32, mfma=True)
+        zipf32, _ = resident_leg(st, 32, args, seed=32)
         zipf32["config"] = {"workload": f"the same {cfg.n_layers}-layer Q4_K stack at T=32, Zipf(1.1) router bias "
                                         f"(per-layer permutation), fresh N(0,1) states every step"}
         st.biases = saved
@@ -744,7 +758,10 @@ def main():
         mst, _, mspecs, mpacked = build_stack(mcfg, args.threads, 0, T_max=8)
         mixed = {}
         for T in (1, 4):
-            mixed[f"t{T}"], _ = resident_leg(mst, T, args, seed=100 + T)
+            mixed[f"t{T}"], _ = resident_leg(
+                mst, T, args, seed=100 + T,
+                kernel=None if T == 1 else "expert FFN (k_gate_up_i8 + k_down_i8 on the Q4_K layers, "
+                                           "k_gate_up + k_down on the Q6_K layers)")
         mixed["config"] = {"workload": f"{mcfg.n_layers} layers, H=2048, 64 routed (top-2) + 2 shared experts, "
                                        f"I=1408 (down rows padded to 1536), layers 0-11 Q4_K, 12-23 Q6_K, all "
                                        f"resident; FFN bytes per launch include the two shared experts"}
