@@ -2798,6 +2798,14 @@ struct GateUpI8Args {
     float *hf;          // [P][kd]
     float *act_out;     // [P][kd] or null
     int nrb;            // I / 64
+    // grouping in these workgroups (idx_in non-null): the routing's ids and weights
+    const int *idx_in;     // [T][k]
+    const float *w_in;     // [T][k]
+    int T, k, ns, Umax;
+    WorkEntry *wt_out;  // the down kernel's work table (pair indices inline), its length,
+    int *nuniq_out;     // each pair's token and weight, (token, slot) -> pair
+    int *ptok_out, *inv_out;
+    float *pw_out;
 };
 
 constexpr int kI8GUKG = 4;  // gate/up K-groups
@@ -2819,14 +2827,148 @@ __device__ __forceinline__ void load_q4k_plane_row(uint4 &meta, uint4 (&qp)[4], 
     for (int c = 0; c < 4; c++) qp[c] = ldg<uint4>(tile, 1024 + (2 * c + kh) * 1024 + row64 * 16);
 }
 
+// Grouping of T <= 8 tokens' routing in every workgroup of the integer-MFMA
+// gate/up kernel, from the ids and weights the route launch wrote (its tail
+// skips the grouping): workgroup u takes the u-th selected expert in
+// ascending id (then the shared experts) with the tokens that selected it
+// (ascending) and their pair indices t k + j (j the slot of the expert in
+// token t's selection) for routed pairs, T k + s T + t for shared ones: the
+// pairs are in (token, slot) order, which the layer calls never expose.
+// Workgroup 0 also writes what the down kernel reads: each pair's token and
+// combine weight, the (token, slot) -> pair map, the work table (pair
+// indices inline) and its length.  Returns the entry's pair count (0: no
+// entry u).  lw: LDS of i8_group_lds(T, E) bytes.
+__device__ __forceinline__ int i8_group(const GateUpI8Args &a, int u, int &e, uint64_t &toks, uint64_t &pairs,
+                                        uint32_t *lw)
+{
+    const int T = a.T, E = a.E, k = a.k, ns = a.ns, P = T * k, tid = (int)threadIdx.x, lane = lane_id();
+    uint32_t *lmask = lw;                       // [E] tokens selecting each expert
+    uint8_t *lslot = (uint8_t *)(lw + E);       // [E][kI8Tok] slot of the expert in each token
+    int *lsel = (int *)(lslot + E * kI8Tok);    // [2] the u-th selected expert, selected count
+    for (int j = tid; j < E; j += blockDim.x) lmask[j] = 0u;
+    __syncthreads();
+    if (tid < P) {
+        const int id = a.idx_in[tid], t = tid / k;
+        if ((unsigned)id < (unsigned)E) {
+            atomicOr(&lmask[id], 1u << t);
+            lslot[id * kI8Tok + t] = (uint8_t)(tid - t * k);
+        }
+    }
+    __syncthreads();
+    const bool w0 = blockIdx.x == 0;
+    if (wave_id() == 0) {
+        // the selected experts in ascending id: the u-th one (and, in
+        // workgroup 0, the work table entries of all of them)
+        int base = 0, found = -1;
+        for (int j0 = 0; j0 < E; j0 += 64) {
+            const int j = j0 + lane;
+            const uint32_t mk = j < E ? lmask[j] : 0u;
+            const uint64_t b = __ballot(mk != 0u);
+            const int r = base + __popcll(b & ((1ull << lane) - 1ull));
+            if (mk && r == u) found = j;
+            if (w0 && mk) {
+                WorkEntry we{};
+                we.e = j; we.p0 = 0; we.p1 = __popc(mk);
+                we.ptr = a.eptr[j];
+                uint64_t pl = 0;
+                uint32_t mm = mk;
+                for (int q = 0; mm; q++) {
+                    const int t = __ffs(mm) - 1;
+                    mm &= mm - 1;
+                    pl |= (uint64_t)(t * k + lslot[j * kI8Tok + t]) << (8 * q);
+                }
+                __builtin_memcpy(we.tok, &pl, sizeof(pl));
+                a.wt_out[r] = we;
+            }
+            base += __popcll(b);
+        }
+        const uint64_t fb = __ballot(found >= 0);
+        const int fj = __shfl(found, fb ? __ffsll((long long)fb) - 1 : 0, 64);
+        if (lane == 0) {
+            lsel[0] = fb ? fj : -1;
+            lsel[1] = base;
+        }
+    }
+    __syncthreads();
+    const int nsel = lsel[1];
+    if (w0) {
+        for (int p = tid; p < P; p += blockDim.x) {
+            const int t = p / k;
+            a.pw_out[p] = a.w_in[p];
+            a.ptok_out[p] = t;
+            a.inv_out[t * (k + ns) + (p - t * k)] = (unsigned)a.idx_in[p] < (unsigned)E ? p : -1;
+        }
+        for (int i = tid; i < ns * T; i += blockDim.x) {
+            const int s2 = i / T, t = i - s2 * T, p = P + s2 * T + t;
+            a.pw_out[p] = 1.0f;
+            a.ptok_out[p] = t;
+            a.inv_out[t * (k + ns) + k + s2] = p;
+        }
+        for (int s2 = tid; s2 < ns; s2 += blockDim.x) {
+            WorkEntry we{};
+            we.e = E + s2; we.p0 = 0; we.p1 = T;
+            we.ptr = a.sptr[s2];
+            uint64_t pl = 0;
+            for (int t = 0; t < T; t++) pl |= (uint64_t)(P + s2 * T + t) << (8 * t);
+            __builtin_memcpy(we.tok, &pl, sizeof(pl));
+            a.wt_out[nsel + s2] = we;
+        }
+        for (int v = nsel + ns + tid; v < a.Umax; v += blockDim.x) a.wt_out[v] = WorkEntry{};
+        if (tid == 0) *a.nuniq_out = nsel + ns;
+    }
+    int n = 0;
+    toks = 0;
+    pairs = 0;
+    e = -1;
+    if (u < nsel) {
+        e = lsel[0];
+        uint32_t mm = lmask[e];
+        for (; mm; n++) {
+            const int t = __ffs(mm) - 1;
+            mm &= mm - 1;
+            toks |= (uint64_t)t << (8 * n);
+            pairs |= (uint64_t)(t * k + lslot[e * kI8Tok + t]) << (8 * n);
+        }
+    } else if (u < nsel + ns) {
+        e = E + (u - nsel);
+        for (int t = 0; t < T; t++) {
+            toks |= (uint64_t)t << (8 * t);
+            pairs |= (uint64_t)(P + (u - nsel) * T + t) << (8 * t);
+        }
+        n = T;
+    }
+    __syncthreads();  // lw is reused by the caller
+    return n;
+}
+
+// LDS bytes of i8_group
+__host__ __device__ constexpr size_t i8_group_lds(int E)
+{
+    return (size_t)E * 4 + (size_t)E * kI8Tok + 16;
+}
+
+template <bool DEFER>
 __global__ __launch_bounds__(kGUI8Threads) __attribute__((amdgpu_waves_per_eu(4))) void k_gate_up_i8(GateUpI8Args a)
 {
     extern __shared__ __align__(16) uint8_t lx[];
     const int u = blockIdx.x / a.nrb, rb = blockIdx.x - u * a.nrb;
-    if (u >= uni(*a.nuniq)) return;
-    const WorkEntry we = load_entry(a.wt, u);
-    const int p0 = we.p0, n = we.p1 - we.p0;
-    const uint8_t *base = (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]);
+    uint64_t toks;   // byte t = the token of the entry's slot t (shifts: no indexed private array)
+    uint64_t pairs = 0;  // routing here: byte t = the pair of slot t; else the pairs are p0 + t
+    int n, p0 = 0;
+    const uint8_t *base;
+    if constexpr (DEFER) {
+        int e;
+        n = i8_group(a, u, e, toks, pairs, (uint32_t *)lx);
+        if (n == 0) return;
+        base = (const uint8_t *)(e < a.E ? a.eptr[e] : a.sptr[e - a.E]);
+    } else {
+        if (u >= uni(*a.nuniq)) return;
+        const WorkEntry we = load_entry(a.wt, u);
+        n = we.p1 - we.p0;
+        p0 = we.p0;
+        __builtin_memcpy(&toks, we.tok, sizeof(toks));
+        base = (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]);
+    }
     const int wv = wave_id(), lane = lane_id(), kh = lane >> 5, r = lane & 31;
     const int m = wv & 1, rb2 = (wv >> 1) & 1, kg = wv >> 2;
     const int H = a.H, S = H >> 8, RS = H + 16, NB = H / 32;
@@ -2836,8 +2978,6 @@ __global__ __launch_bounds__(kGUI8Threads) __attribute__((amdgpu_waves_per_eu(4)
     // this wave's first super-block's weights, in flight during the staging
     uint4 meta = make_uint4(0, 0, 0, 0), qp[4] = {};
     if (kg < S) load_q4k_plane_row(meta, qp, mat + (tile0 + kg) * kTileBytes<MOE_Q4_K>, row64, kh);
-    uint64_t toks;  // byte t = the entry's token slot t (shifts: no indexed private array)
-    __builtin_memcpy(&toks, we.tok, sizeof(toks));
     // staging: piece rows (16-byte chunks), then scales and block sums
     float *lbs = (float *)(lx + (size_t)3 * kI8Tok * RS);
     float *lsum = lbs + kI8Tok * NB;
@@ -2925,7 +3065,8 @@ __global__ __launch_bounds__(kGUI8Threads) __attribute__((amdgpu_waves_per_eu(4)
             uu += part[q][1][b2][t][r5];
         }
         const float hv = g / (1.0f + expf(-g)) * uu;
-        const size_t o = (size_t)(p0 + t) * a.kd + rb * 64 + rr;
+        const int pr = DEFER ? (int)((pairs >> (8 * t)) & 0xff) : p0 + t;
+        const size_t o = (size_t)pr * a.kd + rb * 64 + rr;
         a.hf[o] = hv;
         if (a.act_out) a.act_out[o] = hv;
     }
@@ -2951,6 +3092,7 @@ struct DownI8Args {
     const int *ptok;
     const float *pw;
     float *y;
+    int pairlist;      // 1: the entries' tok[] hold their pair indices (routing in the gate/up kernel)
 };
 
 constexpr int kDnI8Threads = kI8DnRW * kI8DnKG * 64;
@@ -2967,6 +3109,9 @@ __global__ __launch_bounds__(kDnI8Threads) __attribute__((amdgpu_waves_per_eu(5)
     if (u >= uni(*a.nuniq)) return;
     const WorkEntry we = load_entry(a.wt, u);
     const int p0 = we.p0, n = we.p1 - we.p0;
+    uint64_t pl;
+    __builtin_memcpy(&pl, we.tok, sizeof(pl));
+    auto pair_of = [&](int t) { return a.pairlist ? (int)((pl >> (8 * t)) & 0xff) : p0 + t; };
     const uint8_t *base =
         (const uint8_t *)(we.ptr ? we.ptr : we.e < a.E ? a.eptr[we.e] : a.sptr[we.e - a.E]) + a.down_off;
     const int wv = wave_id(), lane = lane_id(), kh = lane >> 5, r = lane & 31;
@@ -2992,7 +3137,7 @@ __global__ __launch_bounds__(kDnI8Threads) __attribute__((amdgpu_waves_per_eu(5)
         const int unit = u0 + i * (kDnI8Threads / 64);
         const int t = unit / S, pos = (unit - t * S) * 256 + 4 * lane;
         uv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (unit < n * S && pos < a.I) uv[i] = *(const float4 *)(a.hf + (size_t)(p0 + t) * K + pos);  // I: multiple of 32
+        if (unit < n * S && pos < a.I) uv[i] = *(const float4 *)(a.hf + (size_t)pair_of(t) * K + pos);  // I: multiple of 32
     }
 #pragma unroll
     for (int i = 0; i < kUnits; i++) {
@@ -3063,7 +3208,8 @@ __global__ __launch_bounds__(kDnI8Threads) __attribute__((amdgpu_waves_per_eu(5)
         float v = 0.f;
 #pragma unroll
         for (int k = 0; k < kI8DnKG; k++) v += part[rr >> 5][k][t][rr & 31];
-        add_to(a.y + (size_t)a.ptok[p0 + t] * a.H + rt * 64 + rr, a.pw[p0 + t] * v);
+        const int pr = pair_of(t);
+        add_to(a.y + (size_t)a.ptok[pr] * a.H + rt * 64 + rr, a.pw[pr] * v);
     }
 }
 
@@ -3440,8 +3586,9 @@ bool use_i8(const moe_expert_desc &d, int T)
 // entry per distinct expert for the MFMA kernels.
 bool dot_items(const moe_expert_desc &d, int T) { return !use_mfma(d, T) && !use_i8(d, T); }
 
-moe_status launch_ffn_i8(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int E, const void *const *eptr,
-                         const void *const *sptr, float *y, float *act_out, hipStream_t s)
+moe_status launch_ffn_i8(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
+                         const void *const *eptr, const void *const *sptr, float *y, float *act_out, hipStream_t s,
+                         bool defer)
 {
     const WsLayout &L = ws.L;
     GateUpI8Args ga;
@@ -3451,7 +3598,17 @@ moe_status launch_ffn_i8(const moe_expert_desc &d, const ExpertGeom &g, const Ws
     ga.H = d.H; ga.I = d.I; ga.kd = g.kd; ga.up_off = g.up_off;
     ga.hf = ws.at<float>(L.hf); ga.act_out = act_out;
     ga.nrb = d.I / 64;
-    k_gate_up_i8<<<L.U * ga.nrb, kGUI8Threads, i8_gu_lds(d.H), s>>>(ga);
+    ga.idx_in = defer ? ws.at<int>(L.idx) : nullptr;
+    ga.w_in = ws.at<float>(L.w);
+    ga.T = T; ga.k = L.k; ga.ns = L.ns; ga.Umax = L.U;
+    ga.wt_out = ws.at<WorkEntry>(L.wt); ga.nuniq_out = ws.at<int>(L.nuniq);
+    ga.ptok_out = ws.at<int>(L.ptok); ga.inv_out = ws.at<int>(L.inv); ga.pw_out = ws.at<float>(L.pw);
+    if (defer) {
+        const size_t lds = std::max(i8_gu_lds(d.H), i8_group_lds(E));
+        k_gate_up_i8<true><<<L.U * ga.nrb, kGUI8Threads, lds, s>>>(ga);
+    } else {
+        k_gate_up_i8<false><<<L.U * ga.nrb, kGUI8Threads, i8_gu_lds(d.H), s>>>(ga);
+    }
     LAUNCH_OK("k_gate_up_i8");
     DownI8Args da;
     da.eptr = eptr; da.sptr = sptr; da.E = E;
@@ -3459,6 +3616,7 @@ moe_status launch_ffn_i8(const moe_expert_desc &d, const ExpertGeom &g, const Ws
     da.H = d.H; da.I = d.I; da.kd = g.kd; da.down_off = g.down_off;
     da.nrt = d.H / 64;
     da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
+    da.pairlist = defer;
     k_down_i8<<<L.U * da.nrt, kDnI8Threads, (size_t)kI8Tok * i8_dn_rec(g.kd), s>>>(da);
     LAUNCH_OK("k_down_i8");
     return MOE_OK;
@@ -3513,12 +3671,20 @@ bool defer_routing(const moe_expert_desc &d, int T, int E)
     return T == 1 && E <= 128 && enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16 && !use_mfma(d, T);
 }
 
+// For 2 .. 8 tokens on the integer-MFMA kernels the grouping moves from the
+// route launch's tail (which keeps the top-k and softmax) into the gate/up
+// workgroups, when the pair indices fit a byte.
+bool defer_grouping(const moe_expert_desc &d, int T, int k, int ns)
+{
+    return use_i8(d, T) && T * k <= kGUI8Threads && T * (k + ns) <= 256;
+}
+
 moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
                               const void *const *eptr, const void *const *sptr, float *y,
                               float *act_out, hipStream_t s, bool defer = false)
 {
     if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, T, E, eptr, sptr, y, act_out, s);
-    if (use_i8(d, T)) return launch_ffn_i8(d, g, ws, E, eptr, sptr, y, act_out, s);
+    if (use_i8(d, T)) return launch_ffn_i8(d, g, ws, T, E, eptr, sptr, y, act_out, s, defer && T > 1);
     const WsLayout &L = ws.L;
     GateUpArgs ga;
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
@@ -3719,7 +3885,9 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     a.x = W.x();
     a.x16 = use_mfma(*d, T) ? W.at<uint8_t>(W.L.x16) : nullptr;
     a.sb_scale = use_i8(*d, T);
-    a.group = 1; a.ns = n_shared; a.go = W.group(dot_items(*d, T));
+    // for 2 .. 8 tokens on the integer-MFMA kernels the tail stops after the
+    // top-k and softmax: moe_layer_ffn's gate/up workgroups group the pairs
+    a.group = !defer_grouping(*d, T, k, n_shared); a.ns = n_shared; a.go = W.group(dot_items(*d, T));
     a.go.eptr = expert_ptrs; a.go.sptr = shared_ptrs;
     a.hpad = W.h(); a.P = W.L.P; a.I = d->I; a.kd = g.kd;
     // router workgroups: row pairs x token groups of kRouteTok
@@ -3754,7 +3922,8 @@ moe_status moe_layer_ffn(const moe_expert_desc *d, float *h, int32_t T, int32_t 
     if (!h || !expert_ptrs || (n_shared > 0 && !shared_ptrs)) { set_error("moe_layer_ffn: null pointer"); return MOE_ERR_ARG; }
     Ws W;
     if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
-    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, h, nullptr, s, defer_routing(*d, T, E));
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, h, nullptr, s,
+                              defer_routing(*d, T, E) || defer_grouping(*d, T, k, n_shared));
 }
 
 moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, const float *w_router, const float *bias,
