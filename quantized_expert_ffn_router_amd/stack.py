@@ -159,8 +159,8 @@ class CachedStack:
     prefetch_depth=d > 0 (device_lookup only) adds cross-layer prefetch: at
     layer l, after its lookup, the layers up to l+d not prefetched yet in
     this step (1..d at layer 0, then l+d) have their experts predicted by
-    applying their routers to layer l's input state (moe_rmsnorm +
-    moe_route_topk) and looked up with moe_cache_prefetch_device, whose
+    applying their routers to layer l's input state (moe_layer_route on a
+    workspace of their own) and looked up with moe_cache_prefetch_device, whose
     miss copies run on copy_stream beside the rest of the step.
     """
 
@@ -227,9 +227,13 @@ class CachedStack:
         self.idx_host = torch.empty(T_max * kmax, dtype=torch.int32, pin_memory=True)
         if self.prefetch_depth:
             H = self.layers[0].H
-            self._fxhat = torch.empty((T_max, H), dtype=torch.float32, device=self.device)
             self._fidx = torch.empty(T_max * kmax, dtype=torch.int32, device=self.device)
             self._fw = torch.empty(T_max * kmax, dtype=torch.float32, device=self.device)
+            # the predictions' own workspace: the layer route kernel (router rows
+            # spread over many workgroups) computes them, and its grouping and
+            # records must not overwrite the current layer's
+            self._fws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+            L.moe_workspace_init(self._fws, self.ws_bytes)
         self.device_lookup = device_lookup
         self.trace_capacity = trace_capacity
         if device_lookup:
@@ -321,13 +325,13 @@ class CachedStack:
         return [m for m in range(first, min(layer + d, n - 1) + 1)] if d else []
 
     def _prefetch(self, layer: int, h: torch.Tensor):
-        T, H = h.shape
-        xh = self._fxhat[:T]
-        L.moe_rmsnorm(h, T, H, self.eps, xh)
+        T = h.shape[0]
         for m in self.prefetch_targets(layer):
             s = self.layers[m]
             idx = self._fidx[:T * s.k].view(T, s.k)
-            L.moe_route_topk(xh, T, H, self.routers[m], self.biases[m], s.E, s.k, idx, self._fw[:T * s.k], None)
+            L.moe_layer_route(self.descs[m], h, T, self.routers[m], self.biases[m], s.E, s.k, None,
+                              self.shared_ptrs(m), s.n_shared, self.eps, idx, self._fw[:T * s.k].view(T, s.k),
+                              self._fws, self.ws_bytes)
             self.cache.prefetch_device(m, idx, T, s.k, self.copy_stream)
 
     def step(self, h: torch.Tensor):
