@@ -166,6 +166,9 @@ def throughput(st, T: int, K: int, Wm: int, H: int, seed: int):
     return T * K / el, el / K * 1e3, pct
 
 
+U_LOG = {}  # batch size -> distinct experts (with shared) of each timed layer-step, in launch order
+
+
 def ffn_timing(st, T: int, steps: int, H: int, seed: int):
     """HIP events around each layer's moe_layer_ffn, launched behind a delay."""
     import torch
@@ -205,6 +208,7 @@ def ffn_timing(st, T: int, steps: int, H: int, seed: int):
         for l in range(nl):
             # distinct routed experts plus the always-read shared experts
             U = (len(np.unique(ids[l])) if T > 1 else k) + st.layers[l].n_shared
+            U_LOG.setdefault(T, []).append(int(U))
             tot_bytes += U * st.expert_bytes[l]
             tot_pairs += T * (st.layers[l].k + st.layers[l].n_shared)
             tot_flop += 2.0 * T * (st.layers[l].k + st.layers[l].n_shared) * 3 * st.layers[l].H * st.layers[l].I
@@ -675,6 +679,9 @@ def main():
     ap.add_argument("--zero-mean", type=int, default=1, help="the zero-mean-field stack at T=8; 0: none")
     ap.add_argument("--mixed", type=int, default=1, help="the mixed Q4_K/Q6_K shared-expert stack legs; 0: none")
     ap.add_argument("--zipf", action="store_true", help="Zipf(1.1) router bias on the headline stack")
+    ap.add_argument("--u-log", default="", metavar="PATH",
+                    help="write the distinct experts of every timed FFN launch (by batch size, in launch order) "
+                         "as JSON, to match per-dispatch counters against the algorithmic bytes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB three times (reads and writes MIB MiB "
                          "each), the reference dispatch for scaling HBM byte counters")
@@ -799,6 +806,9 @@ def main():
     out["mixed_shared"] = mixed
     out["prompt"] = prompt
     out["cache"] = cache
+    if args.u_log:
+        with open(args.u_log, "w") as f:
+            json.dump({str(k): v for k, v in U_LOG.items()}, f)
     print(json.dumps(out), flush=True)
 
 
