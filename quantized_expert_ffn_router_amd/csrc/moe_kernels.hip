@@ -2261,8 +2261,10 @@ __device__ __forceinline__ Stage stage_at(uint8_t *base)
 // that the loads of the next super-block are in flight during the MFMAs of
 // the current one: stage_load fills the registers, stage_store converts them
 // into LDS.  The 256 items (column c, 32-wide block b) go to the NT threads
-// in turn, NI = 256/NT each.  A column's scale is a power of two bringing its
-// largest magnitude in the super-block to [0.5, 1).
+// in turn, NI = 256/NT each, columns fastest (neighbouring threads store
+// neighbouring 16-byte chunks: no LDS bank conflicts).  A column's scale is
+// a power of two bringing its largest magnitude in the super-block to
+// [0.5, 1).
 template <int NT> struct StageRegs {
     float v[256 / NT][32];
 };
@@ -2274,7 +2276,7 @@ __device__ __forceinline__ void stage_load(StageRegs<NT> &r, const float *src, i
     constexpr int NI = 256 / NT;
 #pragma unroll
     for (int it = 0; it < NI; it++) {
-        const int item = threadIdx.x + it * NT, c = item >> 3, b = item & 7;
+        const int item = threadIdx.x + it * NT, c = item & (kMfmaCols - 1), b = item / kMfmaCols;
         const int pos0 = sb * 256 + b * 32;
         if (c < n) {
             const float *row = src + (size_t)rowof(c) * K;
@@ -2307,7 +2309,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<NT> &r, Stage st, in
     constexpr int NI = 256 / NT;
 #pragma unroll
     for (int it = 0; it < NI; it++) {
-        const int c = (threadIdx.x + it * NT) >> 3;
+        const int c = (threadIdx.x + it * NT) & (kMfmaCols - 1);
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i++) m = fmaxf(m, fabsf(r.v[it][i]));
@@ -2316,12 +2318,12 @@ __device__ __forceinline__ void stage_store(const StageRegs<NT> &r, Stage st, in
     __syncthreads();
     int cms[NI];
 #pragma unroll
-    for (int it = 0; it < NI; it++) cms[it] = lmax[(threadIdx.x + it * NT) >> 3];
+    for (int it = 0; it < NI; it++) cms[it] = lmax[(threadIdx.x + it * NT) & (kMfmaCols - 1)];
     __syncthreads();
     if (threadIdx.x < kMfmaCols) lmax[threadIdx.x] = 0;  // for the next call
 #pragma unroll
     for (int it = 0; it < NI; it++) {
-        const int item = threadIdx.x + it * NT, c = item >> 3, b = item & 7;
+        const int item = threadIdx.x + it * NT, c = item & (kMfmaCols - 1), b = item / kMfmaCols;
         const float cm = __int_as_float(cms[it]);
         const int e = cm > 0.f ? -ilogbf(cm) - 1 : 0;  // cm * 2^e in [0.5, 1)
         const float sc = ldexpf(1.0f, e);
