@@ -452,6 +452,18 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity);
 moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
                                    hipStream_t stream);
 
+/* moe_cache_lookup_device for a single token whose routing the layer calls
+ * leave to the FFN kernels: the lookup kernel itself selects the k largest
+ * of the logit keys that the moe_layer_route before it on `stream`, on
+ * workspace ws, wrote (called without idx_out / w_out, so that its launch
+ * has no routing tail), ties to the lower id, as moe_layer_route's top-k
+ * does; then as moe_cache_lookup_device with those ids.  This saves the
+ * route launch's tail on the cached decode path.  MOE_ERR_ARG when the
+ * layer's group would not leave the keys (its route launch routes itself:
+ * E > 128, or experts off the dot-product path at T=1). */
+moe_status moe_cache_lookup_device_route(moe_cache *c, int32_t layer, const void *ws, size_t ws_bytes, int32_t k,
+                                         hipStream_t stream);
+
 /* Cross-layer prefetch (Laptop post, section 2.3: the experts of the next
  * layers are fetched while the current one computes).  idx (device int32
  * [T][k]): the ids predicted for `layer`, e.g. its router applied to an

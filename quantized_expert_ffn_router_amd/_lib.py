@@ -19,7 +19,8 @@ EXPORTED = [
     "moe_layer_forward_noalloc",
     "moe_cache_plan", "moe_placement_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
-    "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_prefetch_device", "moe_cache_trace_read",
+    "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_lookup_device_route", "moe_cache_prefetch_device",
+    "moe_cache_trace_read",
     "moe_cache_stage_large", "moe_cache_stage_large_device",
 ]
 
@@ -129,6 +130,7 @@ def lib() -> ctypes.CDLL:
         "moe_cache_reset_stats": (i32, [P]),
         "moe_cache_device_enable": (i32, [P, i32]),
         "moe_cache_lookup_device": (i32, [P, i32, P, i32, i32, P]),
+        "moe_cache_lookup_device_route": (i32, [P, i32, P, sz, i32, P]),
         "moe_cache_prefetch_device": (i32, [P, i32, P, i32, i32, P, P]),
         "moe_cache_trace_read": (i32, [P, P, i32, P]),
         "moe_cache_stage_large": (i32, [P, i32, i32, i32, P, P, sz, P, P]),
@@ -372,6 +374,11 @@ class Cache:
         if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous() or idx.numel() < T * k:
             raise ValueError("idx must be a contiguous int32 device tensor of T*k ids")
         _check(lib().moe_cache_lookup_device(self.h, layer, idx.data_ptr(), T, k, _stream(stream)))
+
+    def lookup_device_route(self, layer: int, ws, ws_bytes: int, k: int, stream=None):
+        """Device lookup of a single token from the logit keys the preceding
+        moe_layer_route (without idx_out) left in ws (moe_cache_lookup_device_route)."""
+        _check(lib().moe_cache_lookup_device_route(self.h, layer, _ptr(ws), ws_bytes, k, _stream(stream)))
 
     def prefetch_device(self, layer: int, idx, T: int, k: int, copy_stream, stream=None):
         """Prefetch of predicted ids for `layer` (moe_cache_prefetch_device):

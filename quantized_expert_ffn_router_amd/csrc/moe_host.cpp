@@ -894,6 +894,43 @@ moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *i
     return MOE_OK;
 }
 
+moe_status moe_cache_lookup_device_route(moe_cache *c, int32_t layer, const void *ws, size_t ws_bytes, int32_t k,
+                                         hipStream_t stream)
+{
+    if (!c || !ws || layer < 0 || layer >= c->n_layers || k < 1 || k > c->E || ws_bytes < kDlog + (size_t)c->E * 4) {
+        set_error("moe_cache_lookup_device_route: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (!c->dev) { set_error("moe_cache_lookup_device_route: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
+    if (resident_layer(c, layer)) return MOE_OK;  // its table row is final
+    const int g = c->layer_group[layer];
+    auto &G = c->groups[g];
+    if (!route_defers(G.desc, 1, c->E)) {
+        set_error("moe_cache_lookup_device_route: this group's route launch does not leave the logit keys "
+                  "(E <= 128 and the dot-product path at T=1 are needed); use moe_cache_lookup_device");
+        return MOE_ERR_ARG;
+    }
+    if (k > G.n_slots) {
+        set_error("moe_cache_lookup_device_route: %d selections may exceed the %d slots of the group", k, G.n_slots);
+        return MOE_ERR_CAPACITY;
+    }
+    if (moe_status st = prefetch_guard(c, g, k, layer, "moe_cache_lookup_device_route")) return st;
+    if (c->pend_touch[layer] >= 0) {
+        if (hipStreamWaitEvent(stream, c->ev_pref[layer], 0) != hipSuccess) {
+            set_error("moe_cache_lookup_device_route: hipStreamWaitEvent failed");
+            return MOE_ERR_HIP;
+        }
+        c->pend_touch[layer] = -1;
+    }
+    CacheDevArgs a = device_args(c, layer, nullptr, 1, k);
+    a.keys = (const uint32_t *)((const uint8_t *)ws + kDlog);
+    moe_status st = launch_cache_device(a, stream);
+    if (st != MOE_OK) return st;
+    prefetch_count(c, g, k);
+    c->recent_touch[g] = k;
+    return MOE_OK;
+}
+
 moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,
                                      hipStream_t stream, hipStream_t copy_stream)
 {

@@ -81,7 +81,8 @@ struct CacheJob {
     const uint8_t *src;  // device address of the expert's pinned host copy
 };
 struct CacheDevArgs {
-    const int32_t *idx;  // [T][k] selected ids of the layer-step (device)
+    const int32_t *idx;  // [T][k] selected ids of the layer-step (device), or null:
+    const uint32_t *keys;  // [E] (T = 1) the route launch's logit keys, whose k largest are the ids
     int T, k, layer, E;
     int32_t *where;              // [L*E] slot of each key, -1 absent
     const void *const *src;      // [L*E] device addresses of the host copies
@@ -101,6 +102,9 @@ struct CacheDevArgs {
     int trace_cap;
 };
 constexpr int kCacheMaxSlots = 16384;  // slots per group that the device lookup holds in LDS
+// True when moe_layer_route leaves a single token's routing to the FFN (only
+// the logit keys at kDlog are written unless the caller asks for the ids).
+bool route_defers(const moe_expert_desc &d, int T, int E);
 // The lookup on s, then the miss copies: on s, or with a side stream cs on cs
 // after `fork` (recorded on s), recording `done` on cs after them.
 moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t cs = nullptr,
@@ -138,6 +142,10 @@ constexpr size_t kTkBytes = (size_t)kMaxT * 64 * 8;
 constexpr size_t kStatus = kKeys + kKeysBytes + kTkBytes;
 constexpr size_t kStatusBytes = 256;
 static_assert(kStatus == MOE_WS_STATUS_OFFSET, "status word offset published in moe.h");
+// Then a single token's logit keys, written by the route launch for routing
+// in the FFN kernels (or in the cache's device lookup), at a fixed offset.
+constexpr size_t kDlog = kStatus + kStatusBytes;
+constexpr size_t kDlogBytes = (size_t)kMaxE * 4;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
@@ -177,7 +185,8 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.keys = kKeys;
     L.tk = kKeys + kKeysBytes;
     L.status = kStatus;
-    size_t o = kStatus + kStatusBytes;
+    L.dlog = kDlog;
+    size_t o = kDlog + kDlogBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
     L.x16 = take((size_t)T * (d.H / 256) * kX16Bytes);
@@ -190,7 +199,6 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.pw = take((size_t)L.P * 4);
     L.henc = take((size_t)L.P * enc_bytes(L.kd));
     L.hf = take((size_t)L.P * L.kd * 4);
-    L.dlog = take((size_t)E * 4);  // a single token's logit keys, for routing in the FFN
     L.total = o;
     return L;
 }

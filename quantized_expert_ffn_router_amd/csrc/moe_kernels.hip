@@ -3243,10 +3243,20 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
     const int tid = (int)threadIdx.x, lane = lane_id(), E = a.E, P = a.T * a.k;
     for (int e = tid; e < E; e += kCacheThreads) sel[e] = 0;
     if (tid == 0) s_absent = 0;
-    __syncthreads();
-    for (int p = tid; p < P; p += kCacheThreads) {
-        const int e = a.idx[p];
-        if ((unsigned)e < (unsigned)E) sel[e] = 1;
+    if (a.keys) {
+        // a single token (E <= 128): the k largest logit keys, ties to the
+        // lower id (a lane quad ranks each key, as the gate/up kernel does)
+        __shared__ __align__(16) uint64_t lrk[(kCacheThreads / 128) * kRankStride];
+        const int i = tid >> 2;
+        const uint64_t key = i < E ? (uint64_t)a.keys[i] << 32 | (uint32_t)~i : 0ull;
+        const int r = rank_keys_128(key, E, lrk);
+        if ((tid & 3) == 0 && i < E) sel[i] = r < a.k;
+    } else {
+        __syncthreads();
+        for (int p = tid; p < P; p += kCacheThreads) {
+            const int e = a.idx[p];
+            if ((unsigned)e < (unsigned)E) sel[e] = 1;
+        }
     }
     __syncthreads();
     // ascending list of the distinct ids: wave 0, EPL consecutive ids per lane
@@ -3672,6 +3682,12 @@ bool defer_routing(const moe_expert_desc &d, int T, int E)
 {
     return T == 1 && E <= 128 && enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16 && !use_mfma(d, T);
 }
+
+}  // namespace
+
+bool route_defers(const moe_expert_desc &d, int T, int E) { return defer_routing(d, T, E); }
+
+namespace {
 
 // For 2 .. 8 tokens on the integer-MFMA kernels the grouping moves from the
 // route launch's tail (which keeps the top-k and softmax) into the gate/up

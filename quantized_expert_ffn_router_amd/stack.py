@@ -238,6 +238,9 @@ class CachedStack:
         self.trace_capacity = trace_capacity
         if device_lookup:
             self.cache.enable_device(trace_capacity)
+        # layers whose single-token route launch leaves the logit keys (E <= 128,
+        # the dot-product path): their device lookup selects from the keys
+        self._keys_lookup = [s.E <= 128 and s.H <= 4096 and not self.resident[li] for li, s in enumerate(self.layers)]
         self.copy_stream = torch.cuda.Stream(device=self.device)
         self.trace: Optional[list] = None
         self.time_copies = False       # record events around each layer's uploads
@@ -252,6 +255,17 @@ class CachedStack:
         T = h.shape[0]
         d = self.descs[layer]
         idx = self.idx_dev[:T * s.k].view(T, s.k)
+        if self.device_lookup and T == 1 and self._keys_lookup[layer]:
+            # a single token: the route launch only writes the logit keys, and
+            # the lookup kernel picks the top-k from them (no routing tail)
+            L.moe_layer_route(d, h, T, self.routers[layer], self.biases[layer], s.E, s.k, None,
+                              self.shared_ptrs(layer), s.n_shared, self.eps, None, None, self.ws, self.ws_bytes)
+            self.cache.lookup_device_route(layer, self.ws, self.ws_bytes, s.k)
+            if self.prefetch_depth:
+                self._prefetch(layer, h)
+            L.moe_layer_ffn(d, h, T, s.E, s.k, self.cache.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared,
+                            self.ws, self.ws_bytes)
+            return
         L.moe_layer_route(d, h, T, self.routers[layer], self.biases[layer], s.E, s.k, None, self.shared_ptrs(layer),
                           s.n_shared, self.eps, idx, None, self.ws, self.ws_bytes)
         if self.device_lookup:

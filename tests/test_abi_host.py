@@ -129,3 +129,12 @@ def test_workspace_status_argument_checks_without_gpu():
     assert L.moe_workspace_status(ctypes.c_void_p(4096), 1 << 20, None, None) == -1
     assert L.moe_workspace_status(ctypes.c_void_p(4096), moe.MOE_WS_STATUS_OFFSET, ctypes.byref(out), None) == -1
     assert b"status word" in L.moe_last_error()
+
+
+def test_cache_lookup_device_route_argument_checks_without_gpu():
+    """moe_cache_lookup_device_route refuses a null cache or workspace on the
+    host, before any HIP call."""
+    import ctypes
+    L = moe.lib()
+    assert L.moe_cache_lookup_device_route(None, 0, ctypes.c_void_p(4096), 1 << 20, 8, None) == -1
+    assert L.moe_cache_lookup_device_route(ctypes.c_void_p(8), 0, None, 1 << 20, 8, None) == -1
