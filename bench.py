@@ -729,7 +729,7 @@ def main():
         zc = cfg.with_(zipf_s=1.1, T=32)
         saved = st.biases
         st.biases = [torch.from_numpy(W.zipf_bias(zc, l)).to(st.device) for l in range(cfg.n_layers)]
-        zipf32, _ = resident_leg(st, 32, args, seed=32)
+        zipf32, _ = resident_leg(st, 32, args, seed=32, traffic=measured_traffic(32))
         zipf32["config"] = {"workload": f"the same {cfg.n_layers}-layer Q4_K stack at T=32, Zipf(1.1) router bias "
                                         f"(per-layer permutation), fresh N(0,1) states every step"}
         st.biases = saved

@@ -10,7 +10,12 @@
 //              above 16 tokens one top-k workgroup per token; the last
 //              workgroup (the tail) polls the keys (bounded), takes the
 //              softmax top-k and groups the (token, expert) pairs into a work
-//              table of items of at most 4 pairs, largest first.
+//              table of items of at most 4 pairs, largest first.  A single
+//              token has no tail (unless the caller asks for its routing):
+//              the router workgroups also store the keys plainly and every
+//              k_gate_up workgroup ranks them itself after the launch
+//              boundary.  For 2 .. 8 tokens on the integer-MFMA kernels the
+//              tail stops after the softmax and k_gate_up_i8 groups the pairs.
 //   k_gate_up  one workgroup per (work item, 32-row tile): the gate and up
 //              rows of the item's expert against its tokens, SiLU(g)*u, and
 //              the encoding of those 32 values as one activation block.

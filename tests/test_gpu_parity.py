@@ -285,6 +285,29 @@ def test_layer_mixed_shared_q6k(T, first):
     _run_stack_and_compare(sub, 1, T)
 
 
+# single tokens on Q4_K experts of several shapes (the route launch hands the
+# logit keys to k_gate_up, whose workgroups rank them; k_down follows)
+T1_SHAPES = [
+    # H, I, E, k, n_shared, seed
+    (1024, 512, 64, 4, 0, 31),    # four gate/up K-groups, down rows of 2
+    (512, 320, 37, 3, 1, 32),     # odd E (a one-row router workgroup), I padded 320 -> 512, a shared expert
+    (2048, 768, 128, 1, 0, 33),   # top-1 of 128
+    (256, 2048, 16, 12, 2, 34),   # one gate/up K-group, down rows of 8 K-groups, 14 work items
+]
+
+
+@pytest.mark.parametrize("H,I,E,k,ns,seed", T1_SHAPES)
+def test_layer_single_token_shapes(H, I, E, k, ns, seed):
+    """Two layers back to back (the second route launch finds the keys that
+    the first layer's kernels left)."""
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=2).with_(H=H, I=I, E=E, k=k, n_shared=ns, seed=seed)
+    _run_stack_and_compare(cfg, 2, 1)
+
+
+def test_stack_qwen3_shape_6_layers_t1():
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=1, n_layers=6).with_(seed=12), 6, 1)
+
+
 def test_stack_qwen3_shape_4_layers_t8():
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=8, n_layers=4), 4, 8)
 
