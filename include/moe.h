@@ -252,6 +252,43 @@ moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, cons
                              int32_t n_shared, float eps, int32_t *idx_out, float *w_out,
                              void *ws, size_t ws_bytes, hipStream_t s);
 
+/* moe_layer_forward for consecutive single-token layers of a stack (the
+ * decode step of the MoE offload blog, section 3.1, layer after layer):
+ * the same update of h, with the next layer's router dot products started
+ * in this layer's FFN kernels, so that the next layer needs no route launch
+ * (two kernels per layer instead of three).  The router logits are linear in
+ * the state, so the next router's dots with this layer's output are the
+ * dots with its input (computed by the gate/up kernel) plus the dots with
+ * each expert's weighted contribution (added by the down kernel's
+ * workgroups, 64 positions each, with float atomics); the next layer's
+ * gate/up kernel sums them, applies 1/RMS and the bias, ranks them and
+ * encodes the normalised state itself.
+ *   chain_in     nonzero: the previous call on this workspace and stream was
+ *                given this layer's router as next_router (w_router is then
+ *                not read; bias and eps are); zero: this call routes with a
+ *                route launch as moe_layer_forward does
+ *   next_router  NULL (last layer of the chain), or the next layer's router,
+ *                device fp32 [next_E, H]; the next call must use the same h
+ *   next_E       rows of next_router, 1 .. 128
+ *   parity       0 or 1: which of the workspace's two hand-off buffers this
+ *                call reads (chain_in); it writes the other one, so
+ *                consecutive calls alternate (the layer index mod 2)
+ * Chaining needs T == 1 on the single-token kernels: E <= 128, H <= 4096,
+ * the dot-product path (moe_layer_chain_supported); otherwise MOE_ERR_ARG
+ * (nothing enqueued).  With chain_in == 0 and next_router == NULL this is
+ * moe_layer_forward without idx_out / w_out.  The logits are the same sums in
+ * another order (fp32 rounding; the last bits vary from run to run, as the
+ * combine's do).  Other arguments as for moe_layer_forward. */
+moe_status moe_layer_forward_chain(const moe_expert_desc *d, float *h, int32_t T, const float *w_router,
+                                   const float *bias, int32_t E, int32_t k, const void *const *expert_ptrs,
+                                   const void *const *shared_ptrs, int32_t n_shared, float eps, int32_t chain_in,
+                                   const float *next_router, int32_t next_E, int32_t parity, void *ws,
+                                   size_t ws_bytes, hipStream_t s);
+
+/* 1 if a layer of this desc, T tokens and E experts can be chained with
+ * moe_layer_forward_chain, else 0.  Pure host function. */
+int32_t moe_layer_chain_supported(const moe_expert_desc *d, int32_t T, int32_t E);
+
 /* moe_layer_forward without a workspace argument and without any
  * allocation, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

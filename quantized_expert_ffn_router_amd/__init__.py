@@ -25,7 +25,9 @@ from ._lib import (  # noqa: F401
     moe_expert_ffn,
     moe_group_tokens,
     moe_layer_ffn,
+    moe_layer_chain_supported,
     moe_layer_forward,
+    moe_layer_forward_chain,
     moe_layer_forward_noalloc,
     moe_layer_route,
     moe_repack_expert,

@@ -16,7 +16,7 @@ EXPORTED = [
     "moe_last_error", "moe_expert_bytes", "moe_down_k", "moe_repack_expert",
     "moe_rmsnorm", "moe_route_topk", "moe_group_tokens", "moe_workspace_bytes",
     "moe_workspace_init", "moe_workspace_status", "moe_set_spin_limit", "moe_expert_ffn", "moe_layer_route", "moe_layer_ffn", "moe_layer_forward",
-    "moe_layer_forward_noalloc",
+    "moe_layer_forward_noalloc", "moe_layer_forward_chain", "moe_layer_chain_supported",
     "moe_cache_plan", "moe_placement_plan", "moe_cache_create", "moe_cache_create_ex", "moe_cache_lookup", "moe_cache_upload",
     "moe_cache_expert_ptrs", "moe_cache_stats", "moe_cache_reset_stats", "moe_cache_destroy",
     "moe_cache_device_enable", "moe_cache_lookup_device", "moe_cache_lookup_device_route", "moe_cache_prefetch_device",
@@ -119,6 +119,8 @@ def lib() -> ctypes.CDLL:
         "moe_layer_ffn": (i32, [D, P, i32, i32, i32, P, P, i32, P, sz, P]),
         "moe_layer_forward": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P, sz, P]),
         "moe_layer_forward_noalloc": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, P, P, P]),
+        "moe_layer_forward_chain": (i32, [D, P, i32, P, P, i32, i32, P, P, i32, f32, i32, P, i32, i32, P, sz, P]),
+        "moe_layer_chain_supported": (i32, [D, i32, i32]),
         "moe_cache_plan": (i32, [D, P, i32, u64, i32, P]),
         "moe_placement_plan": (i32, [D, i32, P, i32, i32, u64, u64, i32, i32, P, P]),
         "moe_cache_create": (i32, [D, i32, P, P, i32, i32, P, ctypes.POINTER(P)]),
@@ -267,6 +269,18 @@ def moe_layer_forward_noalloc(desc, h, T: int, w_router, bias, E: int, k: int, e
     _check(lib().moe_layer_forward_noalloc(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k,
                                            _ptr(expert_ptrs), _ptr(shared_ptrs), n_shared, eps, _ptr(idx_out),
                                            _ptr(w_out), _stream(stream)))
+
+
+def moe_layer_forward_chain(desc, h, T: int, w_router, bias, E: int, k: int, expert_ptrs, shared_ptrs,
+                            n_shared: int, eps: float, chain_in: bool, next_router, next_E: int, parity: int,
+                            ws, ws_bytes: int, stream=None):
+    _check(lib().moe_layer_forward_chain(ctypes.byref(_desc(desc)), _ptr(h), T, _ptr(w_router), _ptr(bias), E, k,
+                                         _ptr(expert_ptrs), _ptr(shared_ptrs), n_shared, eps, int(bool(chain_in)),
+                                         _ptr(next_router), next_E, parity, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_chain_supported(desc, T: int, E: int) -> bool:
+    return bool(lib().moe_layer_chain_supported(ctypes.byref(_desc(desc)), T, E))
 
 
 def moe_layer_route(desc, h, T: int, w_router, bias, E: int, k: int, expert_ptrs, shared_ptrs, n_shared: int,

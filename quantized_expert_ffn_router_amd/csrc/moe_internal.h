@@ -146,6 +146,15 @@ static_assert(kStatus == MOE_WS_STATUS_OFFSET, "status word offset published in 
 // in the FFN kernels (or in the cache's device lookup), at a fixed offset.
 constexpr size_t kDlog = kStatus + kStatusBytes;
 constexpr size_t kDlogBytes = (size_t)kMaxE * 4;
+// Then the router dot products that chained single-token layers hand on:
+// two buffers (the layer's parity picks the one it reads; it writes the
+// other) of partial sums over 64-position tiles of the state, [H/64][kChainE]
+// (E <= kChainE, H <= kChainMaxH).
+constexpr int kChainE = 128;
+constexpr int kChainMaxH = 4096;
+constexpr size_t kChainBufBytes = (size_t)(kChainMaxH / 64) * kChainE * 4;
+constexpr size_t kChain = kDlog + kDlogBytes;
+constexpr size_t kChainBytes = 2 * kChainBufBytes;
 
 // Workspace map (byte offsets, 256-aligned regions) for a batch of T tokens.
 //
@@ -186,7 +195,7 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.tk = kKeys + kKeysBytes;
     L.status = kStatus;
     L.dlog = kDlog;
-    size_t o = kDlog + kDlogBytes;
+    size_t o = kChain + kChainBytes;
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
     L.xenc = take((size_t)T * enc_bytes(d.H));
     L.x16 = take((size_t)T * (d.H / 256) * kX16Bytes);

@@ -1769,7 +1769,91 @@ struct GateUpArgs {
     WorkEntry *wt_out;
     int *ptok_out, *inv, *nuniq;
     float *pw;
+    // chained single-token layers (CH): this layer's router dots as partial
+    // sums over 64-position tiles of the state (rp_in [H/64][kChainE]; null:
+    // the route launch left its keys in dlog and its record in x), the state
+    // hs [H], the router's bias [E] (or null) and eps; the next layer's router
+    // wn [En][H], whose dots with the input state go to rp_out as tile
+    // partials (or null: no next layer) for the down launch to add to
+    const float *rp_in, *hs, *bias;
+    float eps;
+    const float *wn;
+    int En;
+    float *rp_out;
+    int P;  // pair records in h (with rp_in their padding blocks are cleared here)
 };
+
+// One item j of the next router's dots with the state (chained layers): the
+// 16 lanes of a 64-position tile of one router row each hold a float4 pair;
+// their sum is the tile's partial of that row, stored by the first of them.
+// Items past n4 (whole 16-lane groups) store nothing.
+__device__ __forceinline__ void chain_item(float4 w, float4 x, int j, int n4, int H, float *rp_out)
+{
+    float d = w.x * x.x + w.y * x.y + w.z * x.z + w.w * x.w;
+    d = group_sum<16>(d);
+    if ((lane_id() & 15) == 0 && j < n4) {
+        const int q4 = H >> 2, row = j / q4, c4 = j - row * q4;
+        rp_out[(c4 >> 4) * kChainE + row] = d;
+    }
+}
+
+// The items j0, j0 + stride, ... (stride a multiple of 16), four in flight
+__device__ void chain_dots(const float *wn, const float *hs, int En, int H, float *rp_out, int j0, int stride)
+{
+    const int n4 = En * (H >> 2), q4 = H >> 2;
+    for (int j = j0; j < n4; j += 4 * stride) {
+        float4 w[4], x[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int jj = min(j + i * stride, n4 - 1);
+            w[i] = ((const float4 *)wn)[jj];
+            x[i] = ((const float4 *)hs)[jj % q4];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) chain_item(w[i], x[i], j + i * stride, n4, H, rp_out);
+    }
+}
+
+// Encoding of positions pos .. pos+3 (v) of a record, the 8 consecutive
+// lanes of a 32-position block holding 4 positions each: the arithmetic of
+// encode32 (block scale a/127 from the block's largest magnitude, three
+// int8 pieces, exact block sum, per-16 piece sums) in that layout.
+__device__ __forceinline__ void encode32_x4(float4 v, uint8_t *rec, int K, int pos)
+{
+    const int r = lane_id() & 7;
+    const float a = group_max<8>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float sm = group_sum<8>((v.x + v.y) + (v.z + v.w));
+    const float inv = a > 0.f ? 127.0f / a : 0.f;
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w0 = 0, w1 = 0, w2 = 0;
+    int s0 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float r0 = vv[i] * inv, f0 = rintf(r0);
+        const float r1 = (r0 - f0) * 254.0f, f1 = rintf(r1);
+        const float r2 = (r1 - f1) * 254.0f, f2 = rintf(r2);
+        const int i0 = (int)f0, i1 = (int)f1, i2 = (int)f2;
+        w0 |= (uint32_t)(i0 & 0xff) << (8 * i);
+        w1 |= (uint32_t)(i1 & 0xff) << (8 * i);
+        w2 |= (uint32_t)(i2 & 0xff) << (8 * i);
+        s0 += i0; s1 += i1; s2 += i2;
+    }
+    *(uint32_t *)(rec + pos) = w0;
+    *(uint32_t *)(rec + K + pos) = w1;
+    *(uint32_t *)(rec + 2 * K + pos) = w2;
+    s0 = group_sum<4>(s0); s1 = group_sum<4>(s1); s2 = group_sum<4>(s2);
+    if ((r & 3) == 0) {
+        int *ps = (int *)(rec + 3 * K + K / 4) + pos / 16;
+        ps[0] = s0;
+        ps[K / 16] = s1;
+        ps[K / 8] = s2;
+    }
+    if (r == 0) {
+        float *bs = (float *)(rec + 3 * K);
+        bs[pos / 32] = a / 127.0f;
+        bs[K / 32 + pos / 32] = sm;
+    }
+}
 
 // Ranks of one token's E <= 128 logit keys by a whole 512-thread workgroup:
 // key i's rank is the number of keys that beat it (a larger key, or an equal
@@ -1812,29 +1896,47 @@ constexpr int kDnPre = 4;       // record words per thread loaded before the wei
 // every token's record fits the first pass and the prefetch words (T <= 2,
 // T * RB <= kGUPre * kGUThreads * 16); the records are then loaded before
 // the work entry arrives, token t to LDS slot t.
-template <int QT, int NTOK, bool DEFER>
-__global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 2))) void k_gate_up(GateUpArgs a)
+template <int QT, int NTOK, bool DEFER, bool CH = false>
+__global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K && !CH ? 4 : 2))) void k_gate_up(GateUpArgs a)
 {
     extern __shared__ __align__(16) uint8_t xs[];
     __shared__ float part[8][kTokPass][32][2];
     constexpr bool ALL = NTOK <= 2;
     static_assert(!DEFER || NTOK == 1, "routing in the FFN is for a single token");
+    static_assert(!CH || DEFER, "chained layers route in the FFN");
 
     const int u = blockIdx.x / a.ntile;
     const int rt = blockIdx.x - u * a.ntile;
     const int H = a.H, S = H >> 8;
     const size_t RB = enc_bytes(H);
     const int q16 = (int)(RB / 16);  // 16-byte words per record
-    // DEFER: the logit key and expert address of id tid/4, loaded first by
-    // lane 0 of each quad
+    // CH loads first: with rp_in, this layer's router partials (id tid/4:
+    // tiles tid%4, tid%4 + 4, ..., summed in the lane quad later), its bias
+    // and the state (positions 4 tid + 2048 q)
+    const bool cin = CH && a.rp_in;
+    float4 hst[kChainMaxH / 2048];
+    float dsum = 0.f, dbias = 0.f;
+    if constexpr (CH) {
+        if (cin) {
+            const int i = (int)(threadIdx.x >> 2), nct = H >> 6;
+#pragma unroll 8
+            for (int t = (int)(threadIdx.x & 3); t < nct; t += 4) dsum += a.rp_in[t * kChainE + i];
+            dbias = a.bias ? a.bias[min(i, a.E - 1)] : 0.f;
+#pragma unroll
+            for (int q = 0; q < kChainMaxH / 2048; q++)
+                hst[q] = ((const float4 *)a.hs)[min((int)threadIdx.x + kGUThreads * q, (H >> 2) - 1)];
+        }
+    }
+    // DEFER: the logit key (unless CH computes it) and expert address of id
+    // tid/4, loaded first by lane 0 of each quad
     uint32_t dkey = 0;
     const void *dptr = nullptr;
     if (DEFER && u < a.k && (threadIdx.x & 3) == 0 && (int)(threadIdx.x >> 2) < a.E) {
-        dkey = a.dlog[threadIdx.x >> 2];
+        if (!cin) dkey = a.dlog[threadIdx.x >> 2];
         dptr = a.eptr[threadIdx.x >> 2];
     }
-    u32x4 xr[kGUPre];
-    if (ALL) {
+    u32x4 xr[kGUPre] = {};
+    if (ALL && !cin) {
         // the records are back to back: word i is word i % q16 of token i / q16
 #pragma unroll
         for (int q = 0; q < kGUPre; q++)
@@ -1858,7 +1960,45 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
         if (u >= k + ns) {
 #pragma unroll
             for (int q = 0; q < kGUPre; q++) use(xr[q]);
+            if constexpr (CH) {
+                // the workgroups without a work item (the last ones) take
+                // the next router's dots with the input state
+                const int i0 = (k + ns) * a.ntile;
+                if (a.rp_out)
+                    chain_dots(a.wn, a.hs, a.En, H, a.rp_out, ((int)blockIdx.x - i0) * kGUThreads + tid,
+                               ((int)gridDim.x - i0) * kGUThreads);
+                // the route launch, which did not run, cleared the pair
+                // records' padding blocks
+                if (cin && u == k + ns && a.kd > a.I)
+                    for (int p = rt; p < a.P; p += a.ntile)
+                        zero_blocks(rec_at(a.h, p, a.kd), a.kd, a.I / 32, a.kd / 32, tid, kGUThreads);
+            }
             return;
+        }
+        if constexpr (CH) {
+            if (cin) {
+                // the RMS of the state, then the logit key of id tid/4
+                __shared__ float lred[kGUThreads / 64];
+                float ss = 0.f;
+#pragma unroll
+                for (int q = 0; q < kChainMaxH / 2048; q++)
+                    if (tid + kGUThreads * q < (H >> 2))
+                        ss += hst[q].x * hst[q].x + hst[q].y * hst[q].y + hst[q].z * hst[q].z + hst[q].w * hst[q].w;
+                ss = wave_sum(ss);
+                if (lane_id() == 0) lred[wave_id()] = ss;
+                __syncthreads();
+                ss = 0.f;
+#pragma unroll
+                for (int w = 0; w < kGUThreads / 64; w++) ss += lred[w];
+                const float rms = 1.0f / sqrtf(ss / (float)H + a.eps);
+#pragma unroll
+                for (int q = 0; q < kChainMaxH / 2048; q++) {
+                    hst[q].x *= rms; hst[q].y *= rms; hst[q].z *= rms; hst[q].w *= rms;
+                }
+                dsum += xchg<1>(dsum);
+                dsum += xchg<2>(dsum);
+                dkey = logit_key(dsum * rms + dbias);
+            }
         }
         if (u >= k) {
             e = a.E + (u - k);
@@ -1967,7 +2107,14 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     int loaded = slot < S ? slot : -1;
     for (int c0 = p0; c0 < p1; c0 += a.tpass) {
         const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
-        if (c0 == p0) {
+        if (cin && c0 == p0) {
+            // the state's record (normalised above), encoded here
+#pragma unroll
+            for (int q = 0; q < kChainMaxH / 2048; q++) {
+                const int pos = 4 * ((int)threadIdx.x + kGUThreads * q);
+                if (pos < H) encode32_x4(hst[q], xs, H, pos);  // whole waves
+            }
+        } else if (c0 == p0) {
             const int n16 = (ALL ? a.T : nt0) * q16;
 #pragma unroll
             for (int q = 0; q < kGUPre; q++) {
@@ -2070,7 +2217,17 @@ struct DownArgs {
     float *y;        // [T][H], added into
     int tpass;
     int P;           // pair records in h
+    // chained single-token layers (CH): the next layer's router wn [En][H];
+    // each workgroup adds the dots of its rows' contribution with wn's
+    // columns of the tile to rp_out [H/64][kChainE]
+    const float *wn;
+    int En;
+    float *rp_out;
 };
+
+// next-router float4 per thread held through the dots (CH; fewer for the
+// types whose dots need more registers)
+template <int QT> constexpr int kDnChainPre = QT == MOE_Q4_K ? 12 : 6;
 
 // y[t][row] += v, relaxed agent-scope float atomic (no return value).
 __device__ __forceinline__ void add_to(float *p, float v)
@@ -2081,11 +2238,12 @@ __device__ __forceinline__ void add_to(float *p, float v)
 // ONE: a single token, whose work item u is pair u (one pair per item, in
 // pair order); the pair's record is then loaded before the work entry
 // arrives (it must fit the prefetch words).
-template <int QT, bool ONE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K ? 4 : 3))) void k_down(DownArgs a)
+template <int QT, bool ONE, bool CH = false>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(CH ? 2 : QT == MOE_Q4_K ? 4 : 3))) void k_down(DownArgs a)
 {
+    static_assert(!CH || ONE, "chained layers carry a single token");
     extern __shared__ __align__(16) uint8_t hsl[];
-    __shared__ float part[8][kItemTok][64];
+    __shared__ __align__(16) float part[8][kItemTok][64];
     __shared__ int lptok[kItemTok];   // the item's pairs' tokens and combine weights
     __shared__ float lpw[kItemTok];
 
@@ -2149,6 +2307,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
     typename RegsOf<QT>::T rg[1];
     load_regs(rg[0], base + ((size_t)rt * S + wv) * kTileBytes<QT>, lane);
     int loaded = wv;
+    // CH: the next router's columns of this tile (item j: row j/16, float4
+    // j%16 of the 64 positions), issued after the weights, so that the dots'
+    // waits for those do not wait for these
+    float4 cwv[kDnChainPre<QT>];
+    int cn4 = 0;
+    if constexpr (CH) {
+        cn4 = a.En * 16;
+#pragma unroll
+        for (int q = 0; q < kDnChainPre<QT>; q++) {
+            const int j = min((int)threadIdx.x + q * (int)blockDim.x, cn4 - 1);
+            cwv[q] = ((const float4 *)(a.wn + (size_t)(j >> 4) * a.H + rt * 64))[j & 15];
+        }
+    }
     for (int c0 = p0; c0 < p1; c0 += a.tpass) {
         const int nt = p1 - c0 < a.tpass ? p1 - c0 : a.tpass;
         if (c0 == p0) {
@@ -2210,6 +2381,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q
             const int tok = ONE ? tok1 : lptok[q];
             const float pw = ONE ? pw1 : lpw[q];
             add_to(a.y + (size_t)tok * a.H + rt * 64 + ln, pw * sum);
+        }
+    }
+    if constexpr (CH) {
+        // The dots of the tile's contribution with the next router's rows,
+        // without a barrier: every wave forms the contribution's columns
+        // 4(lane%16) .. +3 from the waves' partial sums (complete since the
+        // barrier before the sums above, and summed in the same order), 16
+        // lanes take a row, and the wave's row sums are gathered into lanes
+        // 4q + i (row 4w + q*blockDim/16 + i) for one atomic instruction.
+        const int c4 = 4 * (lane & 15);
+        float4 cv = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int w = 0; w < nwv; w++) {
+            cv.x += part[w][0][c4];
+            cv.y += part[w][0][c4 + 1];
+            cv.z += part[w][0][c4 + 2];
+            cv.w += part[w][0][c4 + 3];
+        }
+        cv.x *= pw1; cv.y *= pw1; cv.z *= pw1; cv.w *= pw1;
+        float mine = 0.f;
+#pragma unroll
+        for (int q = 0; q < kDnChainPre<QT>; q++) {
+            const float d = group_sum<16>(cwv[q].x * cv.x + cwv[q].y * cv.y + cwv[q].z * cv.z + cwv[q].w * cv.w);
+            const float v = __shfl(d, 16 * (lane & 3), 64);
+            if ((lane >> 2) == q) mine = v;
+        }
+        {
+            const int q = lane >> 2, i = lane & 3;
+            const int j = 64 * wv + q * (int)blockDim.x + 16 * i;
+            if (q < kDnChainPre<QT> && j < cn4) add_to(a.rp_out + rt * kChainE + (j >> 4), mine);
+        }
+        // rows past the held ones (small workgroups, or types holding fewer)
+        for (int j = (int)threadIdx.x + kDnChainPre<QT> * (int)blockDim.x; j < cn4; j += blockDim.x) {
+            const float4 w = ((const float4 *)(a.wn + (size_t)(j >> 4) * a.H + rt * 64))[j & 15];
+            const float d = group_sum<16>(w.x * cv.x + w.y * cv.y + w.z * cv.z + w.w * cv.w);
+            if ((lane & 15) == 0) add_to(a.rp_out + rt * kChainE + (j >> 4), d);
         }
     }
 }
@@ -3702,14 +3908,34 @@ bool defer_grouping(const moe_expert_desc &d, int T, int k, int ns)
     return use_i8(d, T) && T * k <= kGUI8Threads && T * (k + ns) <= 256;
 }
 
+// Chained single-token layers: where this layer's router dots come from
+// (rp_in, or null: the route launch ran) and where the next layer's go.
+struct Chain {
+    const float *rp_in;
+    float *rp_out;
+    const float *wn;  // the next layer's router [En][H]
+    int En;
+    const float *bias;
+    float eps;
+};
+
+// The down kernel's block for a single token, and whether the pair's record
+// fits its registers (the one-pair-per-item kernel)
+int down_block(const ExpertGeom &g)
+{
+    const int S = g.kd / 256;
+    return 64 * (S < 8 ? S : 8);
+}
+bool down_one(const ExpertGeom &g, int T) { return T == 1 && enc_bytes(g.kd) <= (size_t)kDnPre * down_block(g) * 16; }
+
 moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
                               const void *const *eptr, const void *const *sptr, float *y,
-                              float *act_out, hipStream_t s, bool defer = false)
+                              float *act_out, hipStream_t s, bool defer = false, const Chain *ch = nullptr)
 {
     if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, T, E, eptr, sptr, y, act_out, s);
     if (use_i8(d, T)) return launch_ffn_i8(d, g, ws, T, E, eptr, sptr, y, act_out, s, defer && T > 1);
     const WsLayout &L = ws.L;
-    GateUpArgs ga;
+    GateUpArgs ga{};
     ga.eptr = eptr; ga.sptr = sptr; ga.E = E;
     ga.wt = ws.at<WorkEntry>(L.wt); ga.ptok = ws.at<int>(L.ptok);
     ga.x = ws.x();
@@ -3730,8 +3956,13 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     ga.k = L.k; ga.ns = L.ns; ga.Umax = L.UI;
     ga.wt_out = ws.at<WorkEntry>(L.wt); ga.ptok_out = ws.at<int>(L.ptok); ga.inv = ws.at<int>(L.inv);
     ga.nuniq = ws.at<int>(L.nuniq); ga.pw = ws.at<float>(L.pw);
+    if (ch) {
+        ga.rp_in = ch->rp_in; ga.hs = y; ga.bias = ch->bias; ga.eps = ch->eps;
+        ga.wn = ch->wn; ga.En = ch->En; ga.rp_out = ch->rp_out; ga.P = L.P;
+    }
 #define GATE_UP(Q)                                                                        \
-    (defer ? k_gate_up<Q, 1, true><<<ggrid, kGUThreads, glds, s>>>(ga)                   \
+    (ch ? k_gate_up<Q, 1, true, true><<<ggrid, kGUThreads, glds, s>>>(ga)                \
+     : defer ? k_gate_up<Q, 1, true><<<ggrid, kGUThreads, glds, s>>>(ga)                 \
      : all ? (T == 1 ? k_gate_up<Q, 1, false><<<ggrid, kGUThreads, glds, s>>>(ga)        \
                      : k_gate_up<Q, 2, false><<<ggrid, kGUThreads, glds, s>>>(ga))       \
            : k_gate_up<Q, kTokPass, false><<<ggrid, kGUThreads, glds, s>>>(ga))
@@ -3743,7 +3974,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
 #undef GATE_UP
     LAUNCH_OK("k_gate_up");
 
-    DownArgs da;
+    DownArgs da{};
     da.eptr = eptr; da.sptr = sptr; da.E = E;
     da.nuniq = ws.at<int>(L.nuniq); da.wt = ga.wt;
     da.h = ga.h;
@@ -3751,14 +3982,17 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     da.nrt = d.H / 64;
     da.ptok = ws.at<int>(L.ptok); da.pw = ws.at<float>(L.pw); da.y = y;
     da.P = L.P;
-    const int S = g.kd / 256;
     da.tpass = (int)(kDnLds / enc_bytes(g.kd));
     if (da.tpass > kItemTok) da.tpass = kItemTok;  // a work item has at most kItemTok pairs
     const size_t dlds = (size_t)da.tpass * enc_bytes(g.kd);
-    dim3 dgrid(L.UI * da.nrt), dblock(64 * (S < 8 ? S : 8));
+    dim3 dgrid(L.UI * da.nrt), dblock(down_block(g));
     // one token: item u is pair u, whose record is loaded up front when it fits
-    const bool one = T == 1 && enc_bytes(g.kd) <= (size_t)kDnPre * dblock.x * 16;
-#define DOWN(Q) (one ? k_down<Q, true><<<dgrid, dblock, dlds, s>>>(da) : k_down<Q, false><<<dgrid, dblock, dlds, s>>>(da))
+    const bool one = down_one(g, T);
+    const bool dch = ch && ch->rp_out;
+    if (dch) { da.wn = ch->wn; da.En = ch->En; da.rp_out = ch->rp_out; }
+#define DOWN(Q)                                                                                   \
+    (dch ? k_down<Q, true, true><<<dgrid, dblock, dlds, s>>>(da)                                  \
+     : one ? k_down<Q, true><<<dgrid, dblock, dlds, s>>>(da) : k_down<Q, false><<<dgrid, dblock, dlds, s>>>(da))
     switch (d.down) {
     case MOE_Q4_K: DOWN(MOE_Q4_K); break;
     case MOE_Q6_K: DOWN(MOE_Q6_K); break;
@@ -3959,6 +4193,61 @@ moe_status moe_layer_forward(const moe_expert_desc *d, float *h, int32_t T, cons
                                     w_out, ws, ws_bytes, s);
     if (st != MOE_OK) return st;
     return moe_layer_ffn(d, h, T, E, k, expert_ptrs, shared_ptrs, n_shared, ws, ws_bytes, s);
+}
+
+moe_status moe_layer_forward_chain(const moe_expert_desc *d, float *h, int32_t T, const float *w_router,
+                                   const float *bias, int32_t E, int32_t k, const void *const *expert_ptrs,
+                                   const void *const *shared_ptrs, int32_t n_shared, float eps, int32_t chain_in,
+                                   const float *next_router, int32_t next_E, int32_t parity, void *ws,
+                                   size_t ws_bytes, hipStream_t s)
+{
+    if (!chain_in && !next_router)
+        return moe_layer_forward(d, h, T, w_router, bias, E, k, expert_ptrs, shared_ptrs, n_shared, eps, nullptr,
+                                 nullptr, ws, ws_bytes, s);
+    ExpertGeom g;
+    moe_status st = check_desc(d, &g);
+    if (st != MOE_OK) return st;
+    if ((st = check_tke(T, k, E, n_shared)) != MOE_OK) return st;
+    if (!h || !expert_ptrs || (n_shared > 0 && !shared_ptrs) || (!chain_in && !w_router)) {
+        set_error("moe_layer_forward_chain: null pointer");
+        return MOE_ERR_ARG;
+    }
+    if (!moe_layer_chain_supported(d, T, E)) {
+        set_error("moe_layer_forward_chain: chaining takes one token, E <= %d, H <= %d and the single-token kernels "
+                  "(T=%d E=%d H=%d I=%d)", kChainE, kChainMaxH, T, E, d->H, d->I);
+        return MOE_ERR_ARG;
+    }
+    if (next_router && (next_E < 1 || next_E > kChainE)) {
+        set_error("moe_layer_forward_chain: next_E=%d outside [1, %d]", next_E, kChainE);
+        return MOE_ERR_ARG;
+    }
+    if (parity != 0 && parity != 1) {
+        set_error("moe_layer_forward_chain: parity=%d (0 or 1)", parity);
+        return MOE_ERR_ARG;
+    }
+    Ws W;
+    if ((st = check_ws(*d, ws, ws_bytes, T, k, E, n_shared, &W)) != MOE_OK) return st;
+    if (!chain_in) {
+        st = moe_layer_route(d, h, T, w_router, bias, E, k, expert_ptrs, shared_ptrs, n_shared, eps, nullptr, nullptr,
+                             ws, ws_bytes, s);
+        if (st != MOE_OK) return st;
+    }
+    float *buf = W.at<float>(kChain);
+    Chain c{};
+    c.rp_in = chain_in ? buf + (size_t)parity * (kChainBufBytes / 4) : nullptr;
+    c.rp_out = next_router ? buf + (size_t)(parity ^ 1) * (kChainBufBytes / 4) : nullptr;
+    c.wn = next_router;
+    c.En = next_E;
+    c.bias = bias;
+    c.eps = eps;
+    return launch_ffn_kernels(*d, g, W, T, E, expert_ptrs, shared_ptrs, h, nullptr, s, true, &c);
+}
+
+int32_t moe_layer_chain_supported(const moe_expert_desc *d, int32_t T, int32_t E)
+{
+    ExpertGeom g;
+    if (!d || !qtype_ok(d->gate) || !qtype_ok(d->up) || !qtype_ok(d->down) || !geom(*d, &g)) return 0;
+    return defer_routing(*d, T, E) && down_one(g, T) && d->H <= kChainMaxH && E >= 1 && E <= kChainE;
 }
 
 

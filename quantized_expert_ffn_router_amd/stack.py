@@ -103,10 +103,29 @@ class ResidentStack:
                             self.expert_ptrs(layer), self.shared_ptrs(layer), s.n_shared, self.eps,
                             idx_out, w_out, self.ws, self.ws_bytes, stream)
 
+    def chainable(self, T: int) -> bool:
+        """Whether a step of T tokens can chain its layers (moe_layer_forward_chain)."""
+        return all(L.moe_layer_chain_supported(d, T, s.E) for d, s in zip(self.descs, self.layers))
+
     def step(self, h: torch.Tensor, idx_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None,
-             stream=None, split=False):
+             stream=None, split=False, chain: Optional[bool] = None):
         """One decode step through every layer; h [T, H] fp32 is updated in place.
-        idx_out / w_out, if given, are [L, T, k] and receive each layer's routing."""
+        idx_out / w_out, if given, are [L, T, k] and receive each layer's routing.
+        chain: layers through moe_layer_forward_chain (each layer's FFN starts
+        the next layer's router dots; no route launch after the first layer);
+        None chains whenever the step allows it (no routing outputs, no split)."""
+        T = h.shape[0]
+        if chain is None:
+            chain = idx_out is None and w_out is None and not split and self.chainable(T)
+        if chain:
+            n = len(self.layers)
+            for li, s in enumerate(self.layers):
+                nxt = self.layers[li + 1] if li + 1 < n else None
+                L.moe_layer_forward_chain(self.descs[li], h, T, self.routers[li], self.biases[li], s.E, s.k,
+                                          self.expert_ptrs(li), self.shared_ptrs(li), s.n_shared, self.eps,
+                                          li > 0, None if nxt is None else self.routers[li + 1],
+                                          0 if nxt is None else nxt.E, li & 1, self.ws, self.ws_bytes, stream)
+            return
         for li in range(len(self.layers)):
             self.layer_forward(li, h, None if idx_out is None else idx_out[li],
                                None if w_out is None else w_out[li], stream, split)

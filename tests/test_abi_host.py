@@ -62,6 +62,33 @@ def test_argument_errors_are_host_side():
         moe.moe_group_tokens(fake, 4, 9, 8, fake, fake, fake, stream=0)
 
 
+def test_layer_chain_support_and_argument_checks():
+    """moe_layer_chain_supported is a host rule (one token on the single-token
+    kernels, E <= 128, H <= 4096); moe_layer_forward_chain refuses what the
+    rule refuses, and bad next_E / parity, before anything is enqueued."""
+    import ctypes
+    L = moe.lib()
+    q4 = moe.ExpertDesc.of((W.Q4_K,) * 3, 2048, 768)
+    assert moe.moe_layer_chain_supported(q4, 1, 128)
+    assert not moe.moe_layer_chain_supported(q4, 2, 128)
+    assert not moe.moe_layer_chain_supported(q4, 1, 129)
+    assert moe.moe_layer_chain_supported(moe.ExpertDesc.of((W.Q8_0,) * 3, 4096, 512), 1, 48)
+    assert not moe.moe_layer_chain_supported(moe.ExpertDesc.of((W.Q4_K,) * 3, 8192, 512), 1, 64)
+    assert not moe.moe_layer_chain_supported(moe.ExpertDesc.of((7, 2, 2), 2048, 768), 1, 64)
+    fake = 0x1000
+    wsb = moe.moe_workspace_bytes(q4, 1, 8, 128, 0)
+
+    def st(T=1, E=128, chain_in=1, nxt=fake, nE=128, parity=0):
+        return L.moe_layer_forward_chain(ctypes.byref(q4), fake, T, fake, None, E, 8, fake, None, 0, 1e-6,
+                                         chain_in, nxt, nE, parity, fake, wsb, 0)
+
+    assert st(T=2) == -1 and b"chaining takes one token" in L.moe_last_error()
+    assert st(E=200) == -1
+    assert st(nE=129) == -1 and st(nE=0) == -1
+    assert st(parity=2) == -1 and b"parity" in L.moe_last_error()
+    assert st(T=40) == -7  # the layer calls' own batch limit comes first
+
+
 def test_cache_plan_through_abi_reproduces_page_example():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "t4_cache_plan_example.json")))
     pr = g["printed"]

@@ -93,20 +93,28 @@ def _tie_free_chains(cfg, olayers, step, T):
     return np.stack([r[0] for r in res]), [r[1] for r in res]
 
 
-def _graph_step_parity(cfg, st, T, step):
+def _graph_step_parity(cfg, st, T, step, chain=False):
+    """chain: the layers through moe_layer_forward_chain (no routing outputs:
+    the final states against the oracle chains)."""
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts)
     x, ref = _tie_free_chains(cfg, olayers, step, T)
-    _say(cfg.name, "T", T, "oracle chains done")
+    _say(cfg.name, "T", T, "chain" if chain else "", "oracle chains done")
     h = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
     idx = torch.empty((cfg.n_layers, T, cfg.k), dtype=torch.int32, device="cuda")
+    if chain:
+        assert st.chainable(T)
+        idx.fill_(-1)
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         h.copy_(torch.from_numpy(x))
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=stream):
-            st.step(h, idx)
+            if chain:
+                st.step(h, chain=True)
+            else:
+                st.step(h, idx)
     torch.cuda.synchronize()
     worst = 0.0
     for rep in range(2):  # replays with eager work between them
@@ -118,7 +126,8 @@ def _graph_step_parity(cfg, st, T, step):
         torch.cuda.synchronize()
         for t in range(T):
             for l, o in enumerate(ref[t]):
-                assert sets_equal(ig[l, t][None], o.route.idx), f"replay {rep} layer {l} token {t}"
+                if not chain:
+                    assert sets_equal(ig[l, t][None], o.route.idx), f"replay {rep} layer {l} token {t}"
             href = ref[t][-1].h_next
             e1 = oracle.rel_l2(hg[t], href)
             e2 = centered_rel_l2(hg[t] - x[t], href - x[t])
@@ -133,6 +142,13 @@ def test_fullsize_graph_step(qwen3, T):
     _graph_step_parity(cfg, st, T, 1000 + T)
 
 
+def test_fullsize_chain_graph_step(qwen3):
+    """48 chained single-token layers (one route launch, then each layer's
+    FFN kernels start the next layer's router dots) in a graph."""
+    cfg, st = qwen3
+    _graph_step_parity(cfg, st, 1, 1500, chain=True)
+
+
 def test_fullsize_zipf_t32_graph_step(qwen3_zipf):
     """48 layers at 32 tokens: every layer on the MFMA path."""
     cfg, st = qwen3_zipf
@@ -144,6 +160,13 @@ def test_fullsize_mixed_shared_graph_step(mixed, T):
     """24 layers, Q4_K then Q6_K, two shared experts."""
     cfg, st = mixed
     _graph_step_parity(cfg, st, T, 3000 + T)
+
+
+def test_fullsize_mixed_shared_chain_graph_step(mixed):
+    """The 24 mixed layers chained at one token (Q4_K then Q6_K kernels, two
+    shared experts' contributions to the next routers, down rows padded)."""
+    cfg, st = mixed
+    _graph_step_parity(cfg, st, 1, 3500, chain=True)
 
 
 # ---------------------------------------------------------------- the cache's whole trace

@@ -304,6 +304,76 @@ def test_layer_single_token_shapes(H, I, E, k, ns, seed):
     _run_stack_and_compare(cfg, 2, 1)
 
 
+def _run_chain_and_compare(cfg, n_layers, step=0):
+    """Chained single-token layers (moe_layer_forward_chain: one route launch,
+    then each layer's FFN kernels start the next layer's router dots): the
+    final state against the oracle chain, and against the same stack run
+    unchained (the same sums in another order)."""
+    experts = ExpertCache(cfg)
+    olayers = oracle_layers(cfg, experts, n_layers)
+    x, att = W.tie_free_tokens(cfg, step, 1, chain_min_gap(olayers))
+    _say("chain", cfg.name, dict(layers=n_layers, step=step, attempts=att))
+    st = ResidentStack(layer_specs(cfg, n_layers), experts, T_max=1)
+    assert st.chainable(1)
+    h = _dev(x)
+    st.step(h, chain=True)
+    hu = _dev(x)
+    st.step(hu, chain=False)
+    torch.cuda.synchronize()
+    hg, hun = h.cpu().numpy(), hu.cpu().numpy()
+    href = oracle.stack_token(olayers, x[0])[-1].h_next[None]
+    e1 = oracle.rel_l2(hg, href)
+    e2 = centered_rel_l2(hg - x, href - x)
+    e3 = centered_rel_l2(hg - x, hun - x)
+    print("rel-L2 h %.3g, centered update %.3g, against unchained %.3g" % (e1, e2, e3))
+    assert np.all(np.isfinite(hg))
+    assert e1 <= REL_L2_BAR and e2 <= REL_L2_BAR
+    # the same experts and fp32 sums in another order: far tighter than the
+    # oracle bar (a routing difference would move the update by >1e-2)
+    assert e3 <= 1e-4
+
+
+@pytest.mark.parametrize("H,I,E,k,ns,seed", T1_SHAPES)
+def test_chain_single_token_shapes(H, I, E, k, ns, seed):
+    """Three chained layers per shape: ragged I (down rows padded, cleared by
+    the gate/up launch when no route launch runs), odd E (partial 16-lane
+    groups of router rows never straddle), shared experts adding to the next
+    router's dots, H from 256 to 2048."""
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=3).with_(H=H, I=I, E=E, k=k, n_shared=ns, seed=seed + 100)
+    _run_chain_and_compare(cfg, 3)
+
+
+def test_chain_q8_0_and_wide_h():
+    """Q8_0 experts (their own gate/up and down instantiations) at H=4096, the
+    largest chained state (two state words per gate/up thread)."""
+    cfg = W.tiny_q8_0(seed=41).with_(H=4096, I=512, E=48, k=4, n_layers=3, layer_qtypes=((W.Q8_0,) * 3,) * 3)
+    _run_chain_and_compare(cfg, 3)
+
+
+def test_chain_qwen3_shape_6_layers():
+    _run_chain_and_compare(W.qwen3_30b_a3b_q4k(T=1, n_layers=6).with_(seed=13), 6)
+
+
+def test_chain_mixed_shared_q6k():
+    """Q4_K layers then Q6_K layers chained (the chain crosses the type
+    change), two shared experts, I=1408."""
+    cfg = W.mixed_shared_q4k_q6k(T=1)
+    Q4, Q6 = W.Q4_K, W.Q6_K
+    sub = cfg.with_(n_layers=4, layer_qtypes=((Q4,) * 3,) * 2 + ((Q6,) * 3,) * 2, seed=cfg.seed + 41)
+    _run_chain_and_compare(sub, 4)
+
+
+def test_chain_unsupported_is_refused():
+    """Two tokens, or E above 128, cannot chain: MOE_ERR_ARG, nothing run."""
+    cfg = W.qwen3_30b_a3b_q4k(T=2, n_layers=2).with_(seed=9)
+    experts = ExpertCache(cfg)
+    st = ResidentStack(layer_specs(cfg, 2), experts, T_max=2)
+    assert not st.chainable(2) and st.chainable(1)
+    h = _dev(W.tokens(cfg, 0, 2))
+    with pytest.raises(moe.MoeError, match="MOE_ERR_ARG"):
+        st.step(h, chain=True)
+
+
 def test_stack_qwen3_shape_6_layers_t1():
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=1, n_layers=6).with_(seed=12), 6, 1)
 
