@@ -14,11 +14,18 @@ Timed region: K replays of a HIP graph of one step (each preceded by a
 device copy of that step's input into the graph's state buffer), bracketed
 by synchronisation; value = T*K / elapsed.
 
+A single token's step chains its layers (moe_layer_forward_chain): one
+route launch, then per layer a gate/up and a down launch, which also start
+the next layer's router dot products.
+
 Roofline: the expert FFN (the gate/up and down kernels of moe_layer_ffn,
 which read the selected experts' bytes) timed with HIP events on the launch
 stream, layer by layer, in steps launched behind a delay kernel so that they
 run back to back.  achieved = sum over layer-steps of U * expert_bytes /
-sum of FFN durations, U = distinct experts of the layer-step.  traffic =
+sum of FFN durations, U = distinct experts of the layer-step.  For the
+chained single-token step the FFN is a chained layer's two launches (layers
+after the first), and their bytes also count the next router's E*H*4.
+traffic =
 HBM bytes per FFN launch measured with the FETCH_SIZE and WRITE_SIZE
 counters (scaled by a copy kernel of known size), read from the committed
 counter summary under profiles/ and reported only while the kernel sources
@@ -56,6 +63,8 @@ MFMA_I8_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix peak
 # experts: dot products at T=1, integer MFMA at T=2..8, fp16 MFMA above)
 FFN_KERNELS = {
     "dot": "expert FFN (k_gate_up + k_down of moe_layer_ffn)",
+    "chain": "expert FFN of a chained single-token layer (k_gate_up + k_down of moe_layer_forward_chain, "
+             "with the next layer's router dots)",
     "i8": "expert FFN (k_gate_up_i8 + k_down_i8: integer MFMA)",
     "f16": "expert FFN (k_gate_up_mfma + k_down_mfma: fp16 MFMA)",
 }
@@ -167,6 +176,58 @@ def throughput(st, T: int, K: int, Wm: int, H: int, seed: int):
 
 
 U_LOG = {}  # batch size -> distinct experts (with shared) of each timed layer-step, in launch order
+
+
+def chain_timing(st, steps: int, H: int, seed: int):
+    """A single token's chained step (as ResidentStack.step runs it), HIP
+    events around each layer's moe_layer_forward_chain, launched behind a
+    delay.  Layers after the first are their two FFN kernels only (the gate/up
+    launch also takes the next router's dots with the input state, the down
+    launch those of the experts' contributions), so their algorithmic bytes
+    are the k experts' bytes plus the next router's; the first layer's call
+    also holds the step's one route launch, whose time beyond an FFN launch
+    is spread over the layers as route_us."""
+    import torch
+    import quantized_expert_ffn_router_amd as moe
+    dev = st.device
+    nl = len(st.layers)
+    g = torch.Generator(device="cpu").manual_seed(seed + 7)
+    xs = torch.randn((steps, 1, H), generator=g, dtype=torch.float32).to(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nl)]
+    tot_bytes = tot_ffn_ms = tot_first_ms = tot_flop = 0.0
+    n_ffn = 0
+    for s in range(steps):
+        h = xs[s].clone()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(50_000_000)  # keep the GPU busy while the step is enqueued
+        for l in range(nl):
+            sp = st.layers[l]
+            nxt = st.layers[l + 1] if l + 1 < nl else None
+            ev[l][0].record()
+            moe.moe_layer_forward_chain(st.descs[l], h, 1, st.routers[l], st.biases[l], sp.E, sp.k,
+                                        st.expert_ptrs(l), st.shared_ptrs(l), sp.n_shared, st.eps, l > 0,
+                                        None if nxt is None else st.routers[l + 1], 0 if nxt is None else nxt.E,
+                                        l & 1, st.ws, st.ws_bytes)
+            ev[l][1].record()
+        torch.cuda.synchronize()
+        for l in range(nl):
+            ms = ev[l][0].elapsed_time(ev[l][1])
+            if l == 0:
+                tot_first_ms += ms
+                continue
+            sp = st.layers[l]
+            U = sp.k + sp.n_shared  # a single token's experts are distinct
+            U_LOG.setdefault(1, []).append(int(U))
+            nxt_bytes = st.layers[l + 1].E * sp.H * 4 if l + 1 < nl else 0
+            tot_bytes += U * st.expert_bytes[l] + nxt_bytes
+            tot_flop += 2.0 * U * 3 * sp.H * sp.I
+            tot_ffn_ms += ms
+            n_ffn += 1
+    ffn_ms = tot_ffn_ms / n_ffn
+    route_ms = max(0.0, tot_first_ms / steps - ffn_ms) / nl
+    return dict(ffn_us=ffn_ms * 1e3, route_us=route_ms * 1e3, bytes_per_launch=tot_bytes / n_ffn,
+                gbps=tot_bytes / (tot_ffn_ms * 1e-3) / 1e9, launches=n_ffn,
+                tflops=tot_flop / (tot_ffn_ms * 1e-3) / 1e12, flop_per_launch=tot_flop / n_ffn)
 
 
 def ffn_timing(st, T: int, steps: int, H: int, seed: int):
@@ -642,12 +703,16 @@ def roof_hbm(tm, traffic=None, kernel="expert FFN (k_gate_up + k_down of moe_lay
 def resident_leg(st, T: int, args, seed: int, traffic=None, kernel=None):
     """Throughput (graph replays) and the per-layer FFN roofline of one stack at batch T."""
     tps, ms, pct = throughput(st, T, args.steps, args.warmup, st.layers[0].H, seed=seed)
-    tm = ffn_timing(st, T, args.timing_steps, st.layers[0].H, seed=seed)
-    path = ffn_path(T)
+    chained = T == 1 and st.chainable(1)  # what st.step ran in the timed graph
+    if chained:
+        tm = chain_timing(st, args.timing_steps, st.layers[0].H, seed=seed)
+    else:
+        tm = ffn_timing(st, T, args.timing_steps, st.layers[0].H, seed=seed)
+    path = "chain" if chained else ffn_path(T)
     leg = {"value": round(tps, 2), "unit": "tokens/s", "ms_per_step": round(ms, 4), "step_ms_percentiles": pct,
            "roofline": roof_hbm(tm, traffic, kernel or FFN_KERNELS[path]),
            "route_us_per_layer": round(tm["route_us"], 3)}
-    if path != "dot" and kernel is None:
+    if path not in ("dot", "chain") and kernel is None:
         # the matrix cores: the pairs' algorithmic operations (2 per multiply-add of gate, up
         # and down) per FFN launch, against the dense peak of the type the kernels issue on
         peak = MFMA_I8_PEAK_TOPS if path == "i8" else MFMA_FP16_PEAK_TFLOPS

@@ -1915,16 +1915,19 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     // and the state (positions 4 tid + 2048 q)
     const bool cin = CH && a.rp_in;
     float4 hst[kChainMaxH / 2048];
+    float pv[kChainMaxH / 256];
     float dsum = 0.f, dbias = 0.f;
     if constexpr (CH) {
         if (cin) {
-            const int i = (int)(threadIdx.x >> 2), nct = H >> 6;
-#pragma unroll 8
-            for (int t = (int)(threadIdx.x & 3); t < nct; t += 4) dsum += a.rp_in[t * kChainE + i];
+            // every load issued before any is used (clamped indices; the
+            // partials past the state's tiles are loaded and dropped)
+            const int i = (int)(threadIdx.x >> 2), q4 = (int)(threadIdx.x & 3), nct = H >> 6;
             dbias = a.bias ? a.bias[min(i, a.E - 1)] : 0.f;
 #pragma unroll
             for (int q = 0; q < kChainMaxH / 2048; q++)
                 hst[q] = ((const float4 *)a.hs)[min((int)threadIdx.x + kGUThreads * q, (H >> 2) - 1)];
+#pragma unroll
+            for (int n = 0; n < kChainMaxH / 256; n++) pv[n] = a.rp_in[min(q4 + 4 * n, nct - 1) * kChainE + i];
         }
     }
     // DEFER: the logit key (unless CH computes it) and expert address of id
@@ -1995,6 +1998,8 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 for (int q = 0; q < kChainMaxH / 2048; q++) {
                     hst[q].x *= rms; hst[q].y *= rms; hst[q].z *= rms; hst[q].w *= rms;
                 }
+#pragma unroll
+                for (int n = 0; n < kChainMaxH / 256; n++) dsum += (tid & 3) + 4 * n < (H >> 6) ? pv[n] : 0.f;
                 dsum += xchg<1>(dsum);
                 dsum += xchg<2>(dsum);
                 dkey = logit_key(dsum * rms + dbias);
