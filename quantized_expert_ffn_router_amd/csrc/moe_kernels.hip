@@ -16,6 +16,12 @@
 //              k_gate_up workgroup ranks them itself after the launch
 //              boundary.  For 2 .. 8 tokens on the integer-MFMA kernels the
 //              tail stops after the softmax and k_gate_up_i8 groups the pairs.
+//              Consecutive single-token layers can be chained
+//              (moe_layer_forward_chain): only the first runs k_route; each
+//              layer's k_gate_up and k_down also leave the next layer's
+//              router dots as partial sums over 64-position tiles, and the
+//              next k_gate_up forms the logits, ranks them and encodes the
+//              normalised state itself.
 //   k_gate_up  one workgroup per (work item, 32-row tile): the gate and up
 //              rows of the item's expert against its tokens, SiLU(g)*u, and
 //              the encoding of those 32 values as one activation block.
