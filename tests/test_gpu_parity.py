@@ -350,6 +350,12 @@ def test_chain_q8_0_and_wide_h():
     _run_chain_and_compare(cfg, 3)
 
 
+def test_chain_biased_router():
+    """A router bias (Zipf(1.1) over the experts): the keys need 1/RMS before
+    the rank (without a bias the raw dot sums are ranked)."""
+    _run_chain_and_compare(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4).with_(seed=17), 4)
+
+
 def test_chain_qwen3_shape_6_layers():
     _run_chain_and_compare(W.qwen3_30b_a3b_q4k(T=1, n_layers=6).with_(seed=13), 6)
 
