@@ -336,10 +336,12 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
         # the same trace with the LRU on the device: eager steps, then replays
         # of one captured step (input copied in before each replay); each run
         # starts from a cold pool and must reproduce the host run's counts
-        for mode in ("eager", "graph"):
-            cs = CachedStack(zspecs, packed, slots, T_max=1, device_lookup=True)
+        # ("ffn_copies_graph": the misses copied inside the FFN launch, moe_cache_ffn_device)
+        for mode in ("eager", "graph", "ffn_copies_graph"):
+            cs = CachedStack(zspecs, packed, slots, T_max=1, device_lookup=True,
+                             ffn_copies=mode == "ffn_copies_graph")
             hb = xs[0].clone()
-            if mode == "graph":
+            if mode != "eager":
                 torch.cuda.synchronize()
                 graph = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(graph):
@@ -348,14 +350,14 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
             t0 = time.perf_counter()
             for s_ in range(steps):
                 hb.copy_(xs[s_])
-                if mode == "graph":
+                if mode != "eager":
                     graph.replay()
                 else:
                     cs.step(hb)
             torch.cuda.synchronize()
             el_d = time.perf_counter() - t0
             ds = cs.cache.stats()
-            if mode == "graph":
+            if mode != "eager":
                 del graph
             cs.close()
             same = all(ds[k_] == stats[k_] for k_ in ("lookups", "hits", "misses", "evictions", "upload_bytes"))
@@ -502,7 +504,7 @@ def cache_leg(cfg, specs, packed, fractions, steps: int, seed: int, n_req: int =
             "workload": f"same {cfg.n_layers}-layer stack, routed experts in pinned host memory, Zipf(1.1) router "
                         f"bias, {steps} single-token steps from a cold pool, one pool (all layers Q4_K); tokens_per_s: "
                         f"LRU on the host (per-layer id copy and synchronization); device_lru_*: LRU and miss "
-                        f"copies on the device, eager and as a captured HIP graph; prompt_128: 128-token batches after 64 steps, "
+                        f"copies on the device, eager and as a captured HIP graph (ffn_copies_graph: the misses copied by the FFN's gate/up launch, moe_cache_ffn_device); prompt_128: 128-token batches after 64 steps, "
                         f"staged beside the slots (device LRU, eager); concurrency_curve: N fresh tokens per step (N requests, or "
                         f"a speculative verification of N-1 drafts), device LRU graph, cold pool; prefetch_D_eager / prefetch_D_graph: the device LRU, eager and as a graph, with cross-layer prefetch of depth D (lookups include the prefetches); requests_N: N concurrent requests "
                         f"sharing the pool, one N-token batch per step (device LRU, graph; hit rate over the "

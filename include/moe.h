@@ -162,7 +162,8 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s);
  * requested, show the NaN weights). */
 enum {
     MOE_WS_KEYS_TIMEOUT = 1, /* the wait for the router's logit keys gave up */
-    MOE_WS_TOPK_TIMEOUT = 2  /* a wait on the per-token top-k hand-off gave up */
+    MOE_WS_TOPK_TIMEOUT = 2, /* a wait on the per-token top-k hand-off gave up */
+    MOE_WS_COPY_TIMEOUT = 4  /* moe_cache_ffn_device: a wait for a missed expert's copy gave up */
 };
 /* Byte offset of the status word (uint32) in every workspace, for callers
  * that check it on the device or from a captured graph. */
@@ -175,7 +176,8 @@ enum {
  * hold the word; MOE_ERR_HIP if the copy fails. */
 moe_status moe_workspace_status(const void *ws, size_t ws_bytes, uint32_t *status, hipStream_t s);
 
-/* Test hook for the give-up path above, for the route launches that follow
+/* Test hook for the give-up path above, for the route launches (and the
+ * waits for missed experts' copies of moe_cache_ffn_device) that follow
  * this call in the process.  rounds: polling rounds after which a wait gives
  * up (0 restores the default of 2^20; 1 makes a give-up likely whenever a
  * sender is late).  withhold_keys != 0: the router workgroups store no logit
@@ -500,6 +502,22 @@ moe_status moe_cache_lookup_device(moe_cache *c, int32_t layer, const int32_t *i
  * E > 128, or experts off the dot-product path at T=1). */
 moe_status moe_cache_lookup_device_route(moe_cache *c, int32_t layer, const void *ws, size_t ws_bytes, int32_t k,
                                          hipStream_t stream);
+
+/* moe_cache_lookup_device_route followed by the layer's FFN (moe_layer_ffn
+ * on the cache's table of the layer), with the misses copied inside the FFN's
+ * gate/up launch instead of by a launch of their own (Laptop post §2.3: the
+ * copies overlap the compute): that launch's first workgroups copy each
+ * missed expert from its pinned host copy into its slot, while the hit
+ * experts' workgroups start at once; a missed expert's workgroups wait for
+ * their copy (bounded; a wait that gives up sets MOE_WS_COPY_TIMEOUT in the
+ * workspace's status word and makes the layer's outputs NaN).  One token (T=1)
+ * after a moe_layer_route on the same stream and workspace, as for
+ * moe_cache_lookup_device_route; h, d, shared_ptrs, n_shared, ws as for
+ * moe_layer_ffn.  A layer kept resident runs its FFN alone.  Errors as for
+ * the two calls it replaces. */
+moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_desc *d, float *h, int32_t k,
+                                const void *const *shared_ptrs, int32_t n_shared, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /* Cross-layer prefetch (Laptop post, section 2.3: the experts of the next
  * layers are fetched while the current one computes).  idx (device int32

@@ -254,6 +254,8 @@ struct moe_cache {
     const void **d_src = nullptr;     // [L*E] device addresses of the host copies
     int32_t *d_counters = nullptr;    // [n_groups] next_free, then clock, njobs, ntrace
     CacheJob *d_jobs = nullptr;       // [E]
+    int32_t *d_jwait = nullptr;       // [E] moe_cache_ffn_device: each selected id's copy job + 1
+    uint32_t *d_done = nullptr;       // [E] its jobs' completion counts
     unsigned long long *d_stats = nullptr;  // moe_cache_stats_t
     int32_t *d_trace = nullptr;
     // prefetch (moe_cache_prefetch_device): per layer a list of miss copies
@@ -336,7 +338,8 @@ void destroy(moe_cache *c)
         if (dg.key) (void)hipFree(dg.key);
     }
     for (void *p : {(void *)c->d_where, (void *)c->d_src, (void *)c->d_counters, (void *)c->d_jobs,
-                    (void *)c->d_stats, (void *)c->d_trace, (void *)c->d_pjobs, (void *)c->d_pnjobs})
+                    (void *)c->d_stats, (void *)c->d_trace, (void *)c->d_pjobs, (void *)c->d_pnjobs,
+                    (void *)c->d_jwait, (void *)c->d_done})
         if (p) (void)hipFree(p);
     for (auto ev : c->ev_pref)
         if (ev) (void)hipEventDestroy(ev);
@@ -818,6 +821,8 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
               hipMalloc((void **)&c->d_src, LE * sizeof(void *)) == hipSuccess &&
               hipMalloc((void **)&c->d_counters, (ng + 3) * 4) == hipSuccess &&
               hipMalloc((void **)&c->d_jobs, (size_t)c->E * sizeof(CacheJob)) == hipSuccess &&
+              hipMalloc((void **)&c->d_jwait, (size_t)c->E * 4) == hipSuccess &&
+              hipMalloc((void **)&c->d_done, (size_t)c->E * 4) == hipSuccess &&
               hipMalloc((void **)&c->d_stats, sizeof(moe_cache_stats_t)) == hipSuccess &&
               hipMalloc((void **)&c->d_pjobs, LE * sizeof(CacheJob)) == hipSuccess &&
               hipMalloc((void **)&c->d_pnjobs, (size_t)c->n_layers * 4) == hipSuccess &&
@@ -846,7 +851,8 @@ moe_status moe_cache_device_enable(moe_cache *c, int32_t trace_capacity)
         }
         c->dgroups.clear();
         for (void **pp : {(void **)&c->d_where, (void **)&c->d_src, (void **)&c->d_counters, (void **)&c->d_jobs,
-                          (void **)&c->d_stats, (void **)&c->d_trace, (void **)&c->d_pjobs, (void **)&c->d_pnjobs}) {
+                          (void **)&c->d_stats, (void **)&c->d_trace, (void **)&c->d_pjobs, (void **)&c->d_pnjobs,
+                          (void **)&c->d_jwait, (void **)&c->d_done}) {
             if (*pp) (void)hipFree(*pp);
             *pp = nullptr;
         }
@@ -929,6 +935,50 @@ moe_status moe_cache_lookup_device_route(moe_cache *c, int32_t layer, const void
     prefetch_count(c, g, k);
     c->recent_touch[g] = k;
     return MOE_OK;
+}
+
+moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_desc *d, float *h, int32_t k,
+                                const void *const *shared_ptrs, int32_t n_shared, void *ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    if (!c || !d || !h || !ws || layer < 0 || layer >= c->n_layers || k < 1 || k > c->E ||
+        ws_bytes < kDlog + (size_t)c->E * 4 || (n_shared > 0 && !shared_ptrs)) {
+        set_error("moe_cache_ffn_device: bad argument");
+        return MOE_ERR_ARG;
+    }
+    if (!c->dev) { set_error("moe_cache_ffn_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
+    const void *const *table = moe_cache_expert_ptrs(c, layer);
+    if (resident_layer(c, layer))  // its table row is final: no lookup, nothing to copy
+        return moe_layer_ffn(d, h, 1, c->E, k, table, shared_ptrs, n_shared, ws, ws_bytes, stream);
+    const int g = c->layer_group[layer];
+    auto &G = c->groups[g];
+    if (!route_defers(G.desc, 1, c->E)) {
+        set_error("moe_cache_ffn_device: this group's route launch does not leave the logit keys "
+                  "(E <= 128 and the dot-product path at T=1 are needed)");
+        return MOE_ERR_ARG;
+    }
+    if (k > G.n_slots) {
+        set_error("moe_cache_ffn_device: %d selections may exceed the %d slots of the group", k, G.n_slots);
+        return MOE_ERR_CAPACITY;
+    }
+    if (moe_status st = prefetch_guard(c, g, k, layer, "moe_cache_ffn_device")) return st;
+    if (c->pend_touch[layer] >= 0) {
+        if (hipStreamWaitEvent(stream, c->ev_pref[layer], 0) != hipSuccess) {
+            set_error("moe_cache_ffn_device: hipStreamWaitEvent failed");
+            return MOE_ERR_HIP;
+        }
+        c->pend_touch[layer] = -1;
+    }
+    CacheDevArgs a = device_args(c, layer, nullptr, 1, k);
+    a.keys = (const uint32_t *)((const uint8_t *)ws + kDlog);
+    a.jwait = c->d_jwait;
+    a.done = c->d_done;
+    moe_status st = launch_cache_device(a, stream);  // the lookup alone
+    if (st != MOE_OK) return st;
+    prefetch_count(c, g, k);
+    c->recent_touch[g] = k;
+    CacheCopy cc{a.jobs, a.njobs, a.jwait, a.done, a.slot_bytes};
+    return launch_ffn_copy(d, h, c->E, k, table, shared_ptrs, n_shared, ws, ws_bytes, stream, cc);
 }
 
 moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,

@@ -100,6 +100,11 @@ struct CacheDevArgs {
     int32_t *trace;              // [trace_cap][4] (layer, expert, hit, victim key) or null
     int32_t *ntrace;
     int trace_cap;
+    // copies left to the FFN launch (moe_cache_ffn_device), or null: each
+    // selected id's job + 1 (0: a hit), and the jobs' completion counts
+    // (cleared here); no copy kernel is launched
+    int32_t *jwait;              // [E]
+    uint32_t *done;              // [E]
 };
 constexpr int kCacheMaxSlots = 16384;  // slots per group that the device lookup holds in LDS
 // True when moe_layer_route leaves a single token's routing to the FFN (only
@@ -109,6 +114,18 @@ bool route_defers(const moe_expert_desc &d, int T, int E);
 // after `fork` (recorded on s), recording `done` on cs after them.
 moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t cs = nullptr,
                                hipEvent_t fork = nullptr, hipEvent_t done = nullptr);
+// A cached single token's FFN whose gate/up launch also copies the misses
+// that a lookup with jwait/done left (moe_cache_ffn_device).
+struct CacheCopy {
+    const CacheJob *jobs;
+    const int32_t *njobs;
+    const int32_t *jwait;
+    uint32_t *done;
+    unsigned long long slot_bytes;
+};
+moe_status launch_ffn_copy(const moe_expert_desc *d, float *h, int E, int k, const void *const *eptr,
+                           const void *const *sptr, int n_shared, void *ws, size_t ws_bytes, hipStream_t s,
+                           const CacheCopy &cc);
 
 // Staging of a large batch's experts on the device (moe_cache_stage_large_device):
 // the layer's distinct ids, each copied from its slot or its host copy.

@@ -1787,7 +1787,48 @@ struct GateUpArgs {
     int En;
     float *rp_out;
     int P;  // pair records in h (with rp_in their padding blocks are cleared here)
+    // a cached single token whose missed experts are copied in this launch
+    // (ncopy > 0, DEFER): the first ncopy workgroups copy the jobs' experts
+    // from their pinned host copies into their slots, each adding its finished
+    // share of job j to done[j] (with release semantics); a routed workgroup
+    // whose expert e has jwait[e] = j + 1 (a miss) waits for done[j] = ncopy
+    // (bounded by spin; a give-up sets the status word and NaN outputs)
+    int ncopy;
+    const CacheJob *jobs;
+    const int32_t *njobs;
+    const int32_t *jwait;
+    uint32_t *done;
+    unsigned long long slot_bytes;
+    uint32_t *status;
+    unsigned spin;
 };
+
+constexpr int kGUThreadsC = 512;  // the gate/up kernels' workgroup size
+
+// One copying workgroup's share (16-byte words w*512 + tid, + ncopy*512, ...)
+// of every miss job of the call, then the count of that share in done[j]:
+// each thread's stores complete, the workgroup meets, and one release add
+// (which writes the workgroup's data back to the device level first).
+__device__ void cache_copy_share(const GateUpArgs &a, int w)
+{
+    const int nj = *a.njobs;
+    const size_t n16 = a.slot_bytes / 16, stride = (size_t)a.ncopy * kGUThreadsC;
+    for (int j = 0; j < nj; j++) {
+        const CacheJob jb = a.jobs[j];
+        const uint4 *src = (const uint4 *)jb.src;
+        uint4 *dst = (uint4 *)jb.dst;
+        size_t i = (size_t)w * kGUThreadsC + threadIdx.x;
+        // four words in flight per thread
+        for (; i + 3 * stride < n16; i += 4 * stride) {
+            const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+            dst[i] = v0; dst[i + stride] = v1; dst[i + 2 * stride] = v2; dst[i + 3 * stride] = v3;
+        }
+        for (; i < n16; i += stride) dst[i] = src[i];
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(a.done + j, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 // One item j of the next router's dots with the state (chained layers): the
 // 16 lanes of a 64-position tile of one router row each hold a float4 pair;
@@ -1891,7 +1932,7 @@ __device__ __forceinline__ int rank_keys_128(uint64_t key, int E, uint64_t *lk)
     return i < E ? cnt : 0x7fffffff;
 }
 
-constexpr int kGUThreads = 512;
+constexpr int kGUThreads = kGUThreadsC;
 constexpr int kTokPass = 4;  // <= kInlineTok
 constexpr int kGUPre = 2;     // record words per thread loaded before the weights
 constexpr int kGULds = 32768;   // staged token records per pass
@@ -1911,8 +1952,18 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     static_assert(!DEFER || NTOK == 1, "routing in the FFN is for a single token");
     static_assert(!CH || DEFER, "chained layers route in the FFN");
 
-    const int u = blockIdx.x / a.ntile;
-    const int rt = blockIdx.x - u * a.ntile;
+    int bid = (int)blockIdx.x;
+    if constexpr (DEFER && !CH) {
+        if (a.ncopy) {
+            if (bid < a.ncopy) {  // a copying workgroup (the first ones, dispatched first)
+                cache_copy_share(a, bid);
+                return;
+            }
+            bid -= a.ncopy;
+        }
+    }
+    const int u = bid / a.ntile;
+    const int rt = bid - u * a.ntile;
     const int H = a.H, S = H >> 8;
     const size_t RB = enc_bytes(H);
     const int q16 = (int)(RB / 16);  // 16-byte words per record
@@ -1940,9 +1991,11 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     // tid/4, loaded first by lane 0 of each quad
     uint32_t dkey = 0;
     const void *dptr = nullptr;
+    int djw = 0;  // ncopy: the id's copy job + 1 (0: no copy to wait for)
     if (DEFER && u < a.k && (threadIdx.x & 3) == 0 && (int)(threadIdx.x >> 2) < a.E) {
         if (!cin) dkey = a.dlog[threadIdx.x >> 2];
         dptr = a.eptr[threadIdx.x >> 2];
+        if (!CH && a.ncopy) djw = a.jwait[threadIdx.x >> 2];
     }
     u32x4 xr[kGUPre] = {};
     if (ALL && !cin) {
@@ -1954,6 +2007,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     int e, p0, p1;
     const uint8_t *base;
     uint64_t toks = 0;
+    bool gave = false;  // ncopy: the wait for this expert's copy gave up (NaN outputs)
     if constexpr (DEFER) {
         // Routing of the single token from the router's logit keys, in every
         // workgroup (E <= 128): the ranks of the keys; the expert of rank u is
@@ -1964,6 +2018,8 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
         __shared__ __align__(16) uint64_t lk[4 * kRankStride];
         __shared__ int lsel_e[kMaxK];
         __shared__ const void *lsel_p[kMaxK];
+        __shared__ int lsel_w[kMaxK];
+        __shared__ int lgave;
         __shared__ uint32_t lkey_r[kMaxK];
         const int k = a.k, ns = a.ns, tid = (int)threadIdx.x;
         if (u >= k + ns) {
@@ -1974,7 +2030,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 // the next router's dots with the input state
                 const int i0 = (k + ns) * a.ntile;
                 if (a.rp_out)
-                    chain_dots(a.wn, a.hs, a.En, H, a.rp_out, ((int)blockIdx.x - i0) * kGUThreads + tid,
+                    chain_dots(a.wn, a.hs, a.En, H, a.rp_out, (bid - i0) * kGUThreads + tid,
                                ((int)gridDim.x - i0) * kGUThreads);
                 // the route launch, which did not run, cleared the pair
                 // records' padding blocks
@@ -2019,11 +2075,37 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             if (r < k && (tid & 3) == 0) {
                 lsel_e[r] = tid >> 2;
                 lsel_p[r] = dptr;
+                lsel_w[r] = djw;
                 lkey_r[r] = dkey;
             }
             __syncthreads();
             e = lsel_e[u];
             base = (const uint8_t *)lsel_p[u];
+            if constexpr (!CH) {
+                const int jw = a.ncopy ? lsel_w[u] : 0;
+                if (jw > 0) {
+                    // a missed expert: thread 0 waits for its copy, then an
+                    // acquire, so that no line of the slot read before the
+                    // copy is used; the workgroup meets after it
+                    if (tid == 0) {
+                        int ok = 0;
+                        for (unsigned it = 0;; it++) {
+                            if (__hip_atomic_load(a.done + jw - 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                                (uint32_t)a.ncopy) {
+                                ok = 1;
+                                break;
+                            }
+                            if (it >= a.spin) break;
+                            __builtin_amdgcn_s_sleep(2);
+                        }
+                        if (!ok) flag_status(a.status, MOE_WS_COPY_TIMEOUT);
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        lgave = !ok;
+                    }
+                    __syncthreads();
+                    gave = lgave != 0;
+                }
+            }
         }
         p0 = u;
         p1 = u + 1;
@@ -2197,7 +2279,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 gs += part[sl][tt][rr][0];
                 us += part[sl][tt][rr][1];
             }
-            const float hv = gs / (1.0f + expf(-gs)) * us;
+            const float hv = gave ? __builtin_nanf("") : gs / (1.0f + expf(-gs)) * us;
             encode32(hv, rr, rec_at(a.h, c0 + tt, a.kd), a.kd, rt * 32);
             if (a.act_out) a.act_out[(size_t)(c0 + tt) * a.kd + rt * 32 + rr] = hv;
         }
@@ -3529,7 +3611,9 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
                     a.where[key] = s;
                     a.key[s] = key;
                     a.jobs[nj++] = CacheJob{slot, (const uint8_t *)a.src[key]};
+                    if (a.jwait) a.done[nj - 1] = 0u;
                 }
+                if (a.jwait) a.jwait[e] = hit ? 0 : nj;
                 if (a.trace) {
                     const int t = a.ntrace[0] + i;
                     if (t < a.trace_cap) {
@@ -3594,7 +3678,9 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
                 a.where[key] = s;
                 a.key[s] = key;
                 a.jobs[nj] = CacheJob{slot, (const uint8_t *)a.src[key]};
+                if (a.jwait) a.done[nj] = 0u;
             }
+            if (a.jwait) a.jwait[e] = hit ? 0 : nj + 1;
             if (a.trace) {
                 const int t = a.ntrace[0] + i;
                 if (t < a.trace_cap) {
@@ -3939,9 +4025,15 @@ int down_block(const ExpertGeom &g)
 }
 bool down_one(const ExpertGeom &g, int T) { return T == 1 && enc_bytes(g.kd) <= (size_t)kDnPre * down_block(g) * 16; }
 
+// workgroups of a single-token gate/up launch that copy a cached step's misses
+// (16 keep the bus busy; with 64, each one's release per job cost more than
+// the overlap gained)
+constexpr int kFfnCopyWGs = 16;
+
 moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, const Ws &ws, int T, int E,
                               const void *const *eptr, const void *const *sptr, float *y,
-                              float *act_out, hipStream_t s, bool defer = false, const Chain *ch = nullptr)
+                              float *act_out, hipStream_t s, bool defer = false, const Chain *ch = nullptr,
+                              const CacheCopy *cc = nullptr)
 {
     if (use_mfma(d, T)) return launch_ffn_mfma(d, g, ws, T, E, eptr, sptr, y, act_out, s);
     if (use_i8(d, T)) return launch_ffn_i8(d, g, ws, T, E, eptr, sptr, y, act_out, s, defer && T > 1);
@@ -3958,7 +4050,14 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     if (ga.tpass > kTokPass) ga.tpass = kTokPass;
     ga.T = T;
     const size_t glds = (size_t)ga.tpass * enc_bytes(d.H);
-    dim3 ggrid(L.UI * ga.ntile);
+    if (cc) {  // a cached single token: the first workgroups copy its misses
+        ga.ncopy = kFfnCopyWGs;
+        ga.jobs = cc->jobs; ga.njobs = cc->njobs; ga.jwait = cc->jwait; ga.done = cc->done;
+        ga.slot_bytes = cc->slot_bytes;
+        ga.status = ws.at<uint32_t>(L.status);
+        ga.spin = spin_limit();
+    }
+    dim3 ggrid(L.UI * ga.ntile + ga.ncopy);
     // every token's record staged up front when they all fit the first pass
     const bool all = T <= 2 && T <= ga.tpass && (size_t)T * enc_bytes(d.H) <= (size_t)kGUPre * kGUThreads * 16;
     // a single token routed by the gate/up workgroups themselves (the layer's
@@ -4030,6 +4129,7 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t
     }
     k_cache_lookup<<<1, kCacheThreads, lds, s>>>(a);
     LAUNCH_OK("k_cache_lookup");
+    if (a.jwait) return MOE_OK;  // the FFN launch copies the misses
     if (fork) {
         HIP_OK(hipEventRecord(fork, s));
         HIP_OK(hipStreamWaitEvent(cs, fork, 0));
@@ -4039,6 +4139,24 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t
     LAUNCH_OK("k_cache_copy");
     if (done) HIP_OK(hipEventRecord(done, s));
     return MOE_OK;
+}
+
+moe_status launch_ffn_copy(const moe_expert_desc *d, float *h, int E, int k, const void *const *eptr,
+                           const void *const *sptr, int n_shared, void *ws, size_t ws_bytes, hipStream_t s,
+                           const CacheCopy &cc)
+{
+    ExpertGeom g;
+    moe_status st = check_desc(d, &g);
+    if (st != MOE_OK) return st;
+    if ((st = check_tke(1, k, E, n_shared)) != MOE_OK) return st;
+    if (!h || !eptr || (n_shared > 0 && !sptr)) { set_error("moe_cache_ffn_device: null pointer"); return MOE_ERR_ARG; }
+    Ws W;
+    if ((st = check_ws(*d, ws, ws_bytes, 1, k, E, n_shared, &W)) != MOE_OK) return st;
+    if (!defer_routing(*d, 1, E)) {
+        set_error("moe_cache_ffn_device: the single-token kernels are needed (E <= 128, H <= 4096)");
+        return MOE_ERR_ARG;
+    }
+    return launch_ffn_kernels(*d, g, W, 1, E, eptr, sptr, h, nullptr, s, true, nullptr, &cc);
 }
 
 moe_status launch_stage_device(const StageDevArgs &a, hipStream_t s)

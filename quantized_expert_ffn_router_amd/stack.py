@@ -173,7 +173,10 @@ class CachedStack:
     moe_cache_lookup_device (lookup and miss copies) and moe_layer_ffn on the
     current stream, with no host synchronization, so a whole step can be
     captured in a HIP graph.  trace_capacity > 0 keeps the device's lookup
-    trace (device_trace).
+    trace (device_trace).  ffn_copies (the default; device lookup without
+    prefetch) copies a single token's misses inside the FFN's gate/up launch
+    (moe_cache_ffn_device), so that the hit experts' work overlaps the
+    copies and no copy launch runs; False keeps the copy launch.
 
     prefetch_depth=d > 0 (device_lookup only) adds cross-layer prefetch: at
     layer l, after its lookup, the layers up to l+d not prefetched yet in
@@ -185,7 +188,8 @@ class CachedStack:
 
     def __init__(self, layers: Sequence[LayerSpec], packed: Sequence[torch.Tensor], slots: Sequence[int],
                  T_max: int = 8, device: str = "cuda", eps: float = 1e-6, device_lookup: bool = False,
-                 trace_capacity: int = 0, prefetch_depth: int = 0, resident: Optional[Sequence[bool]] = None):
+                 trace_capacity: int = 0, prefetch_depth: int = 0, resident: Optional[Sequence[bool]] = None,
+                 ffn_copies: bool = True):
         """resident[l] (e.g. from moe_placement_plan) keeps layer l's experts
         resident in HBM, outside the cache."""
         if prefetch_depth and not device_lookup:
@@ -254,6 +258,9 @@ class CachedStack:
             self._fws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
             L.moe_workspace_init(self._fws, self.ws_bytes)
         self.device_lookup = device_lookup
+        # a single token's misses copied inside the FFN launch (moe_cache_ffn_device;
+        # device lookup without prefetch)
+        self.ffn_copies = bool(ffn_copies) and device_lookup and not self.prefetch_depth
         self.trace_capacity = trace_capacity
         if device_lookup:
             self.cache.enable_device(trace_capacity)
@@ -279,6 +286,9 @@ class CachedStack:
             # the lookup kernel picks the top-k from them (no routing tail)
             L.moe_layer_route(d, h, T, self.routers[layer], self.biases[layer], s.E, s.k, None,
                               self.shared_ptrs(layer), s.n_shared, self.eps, None, None, self.ws, self.ws_bytes)
+            if self.ffn_copies:
+                self.cache.ffn_device(layer, d, h, s.k, self.shared_ptrs(layer), s.n_shared, self.ws, self.ws_bytes)
+                return
             self.cache.lookup_device_route(layer, self.ws, self.ws_bytes, s.k)
             if self.prefetch_depth:
                 self._prefetch(layer, h)

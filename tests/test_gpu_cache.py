@@ -38,7 +38,8 @@ def _groups(cfg, n_layers):
     return descs, ebytes, per_group, layer_group
 
 
-def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0, slots=None, resident=None):
+def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0, slots=None, resident=None,
+         ffn_copies=False):
     """slots=None: the planner's slots for `fraction` of the routed expert
     bytes (checked against the oracle planner); else the given slots, where
     a group at 0 slots keeps its layers resident."""
@@ -59,7 +60,8 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
     packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
     cap = steps * n_layers * T * cfg.k * (2 if prefetch_depth else 1)
     cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=device_lookup, trace_capacity=cap,
-                     prefetch_depth=prefetch_depth, resident=resident)
+                     prefetch_depth=prefetch_depth, resident=resident, ffn_copies=ffn_copies)
+    assert cs.ffn_copies == (ffn_copies and device_lookup and not prefetch_depth)
     targets = [cs.prefetch_targets(l) for l in range(n_layers)]
     pred = np.zeros((steps, n_layers, T * cfg.k), np.int32)
     cs.trace = []
@@ -132,8 +134,52 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
 @pytest.mark.parametrize("fraction", [0.1, 0.6])
 def test_cache_zipf_qwen3_shape(fraction, device_lookup):
     """Zipf-biased routing over a 4-layer Qwen3-30B-A3B-shaped Q4_K stack,
-    pool at 10 % / 60 % of the routed expert bytes, 24 decode steps."""
-    _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, device_lookup)
+    pool at 10 % / 60 % of the routed expert bytes, 24 decode steps (device
+    LRU: the misses copied by a launch of their own)."""
+    _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, device_lookup, ffn_copies=False)
+
+
+@pytest.mark.parametrize("fraction", [0.1, 0.6])
+def test_cache_ffn_copies_device_lru(fraction):
+    """A single token's misses copied inside the FFN's gate/up launch
+    (moe_cache_ffn_device): every step's state, the hit/miss/victim trace and
+    the slot tables against the oracle, as with the copy launch."""
+    s = _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, True, ffn_copies=True)
+    assert s["misses"] > 0
+
+
+def test_cache_ffn_copies_mixed_shared():
+    """moe_cache_ffn_device on two pools (Q4_K and Q6_K layers), two resident
+    shared experts, I=1408 (down rows padded), one token per step."""
+    cfg = W.mixed_shared_q4k_q6k(T=1)
+    Q4, Q6 = W.Q4_K, W.Q6_K
+    sub = cfg.with_(n_layers=4, layer_qtypes=((Q4,) * 3, (Q4,) * 3, (Q6,) * 3, (Q6,) * 3), seed=cfg.seed + 50)
+    s = _run(sub, 4, 12, 0.1, 1, True, ffn_copies=True)
+    assert s["misses"] > 0 and s["evictions"] > 0
+
+
+def test_cache_ffn_copies_give_up_sets_status():
+    """A one-round bound on the wait for a miss's copy (the test hook): the
+    wait gives up long before a 2.65 MB expert crosses the bus, so the
+    status word gets MOE_WS_COPY_TIMEOUT and the state is NaN; the launch
+    itself still ends (its copying workgroups finish)."""
+    cfg = W.qwen3_30b_a3b_q4k(T=1, n_layers=1).with_(E=16, k=4, seed=19)
+    experts = ExpertCache(cfg)
+    specs = layer_specs(cfg, 1)
+    packed = [pack_layer(specs[0], 0, experts)]
+    cs = CachedStack(specs, packed, [8], T_max=1, device_lookup=True, ffn_copies=True)
+    try:
+        assert cs.ffn_copies
+        moe.moe_set_spin_limit(1)
+        h = torch.from_numpy(np.ascontiguousarray(W.tokens(cfg, 0, 1))).to(DEV)
+        cs.step(h)
+        torch.cuda.synchronize()
+        moe.moe_set_spin_limit(0)
+        assert moe.moe_workspace_status(cs.ws, cs.ws_bytes) & 4
+        assert np.isnan(h.cpu().numpy()).any()
+    finally:
+        moe.moe_set_spin_limit(0)
+        cs.close()
 
 
 @pytest.mark.parametrize("fraction,depth", [(0.1, 2), (0.6, 1)])
