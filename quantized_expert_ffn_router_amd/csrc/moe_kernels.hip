@@ -3545,8 +3545,16 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
     uint32_t *lstamp = dyn;
     int *lkey = (int *)(dyn + a.n_slots);
     const int tid = (int)threadIdx.x, lane = lane_id(), E = a.E, P = a.T * a.k;
+    const int64_t kbase = (int64_t)a.layer * E;
+    // the layer's slot of every id and the group's counters, loaded with the
+    // routing (one round trip; E <= kMaxE = kCacheThreads)
+    __shared__ int lwhere[kMaxE];
+    const int wpre = tid < E ? a.where[kbase + tid] : -1;
+    const int nf0 = *a.next_free;
+    const uint32_t clk0 = *a.clock;
     for (int e = tid; e < E; e += kCacheThreads) sel[e] = 0;
     if (tid == 0) s_absent = 0;
+    if (tid < E) lwhere[tid] = wpre;
     if (a.keys) {
         // a single token (E <= 128): the k largest logit keys, ties to the
         // lower id (a lane quad ranks each key, as the gate/up kernel does)
@@ -3575,14 +3583,13 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
     }
     __syncthreads();
     const int nd = s_nd;
-    const int64_t kbase = (int64_t)a.layer * E;
     for (int i = tid; i < nd; i += kCacheThreads) {
-        wh[i] = a.where[kbase + list[i]];
+        wh[i] = lwhere[list[i]];
         if (wh[i] < 0) atomicAdd(&s_absent, 1);
     }
     __syncthreads();
-    int nf = *a.next_free;
-    uint32_t clk = *a.clock;
+    int nf = nf0;
+    uint32_t clk = clk0;
     // no eviction can happen unless the absent ids outnumber the free slots
     const bool evict = s_absent > a.n_slots - nf;
     if (evict)
