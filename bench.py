@@ -151,9 +151,11 @@ def throughput(st, T: int, K: int, Wm: int, H: int, seed: int):
         h.copy_(xs[0])
         graph.replay()
         torch.cuda.synchronize()
-        # the experts' outputs are summed with float atomics: equal up to rounding order
+        # the experts' outputs are summed with float atomics: equal up to rounding order,
+        # which compounds over the layers (about 1e-5 after 48); a routing difference
+        # would move the state by 1e-2 or more
         err = (torch.linalg.vector_norm(h - ref) / torch.linalg.vector_norm(ref)).item()
-        if not err <= 1e-5:
+        if not err <= 1e-4:
             raise RuntimeError(f"graph replay differs from the eager step (rel-L2 {err:.3g})")
         st.step(h)  # eager work between replays
         torch.cuda.synchronize()
