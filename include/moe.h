@@ -513,11 +513,21 @@ moe_status moe_cache_lookup_device_route(moe_cache *c, int32_t layer, const void
  * workspace's status word and makes the layer's outputs NaN).  One token (T=1)
  * after a moe_layer_route on the same stream and workspace, as for
  * moe_cache_lookup_device_route; h, d, shared_ptrs, n_shared, ws as for
- * moe_layer_ffn.  A layer kept resident runs its FFN alone.  Errors as for
- * the two calls it replaces. */
+ * moe_layer_ffn.  A layer kept resident runs its FFN alone.
+ * Chained layers, as in moe_layer_forward_chain (single-token kernels: E <=
+ * 128, H <= 4096): next_router (NULL: none) [next_E, H] makes this call leave
+ * the next layer's router dots in the workspace's hand-off buffer parity^1;
+ * chain_in != 0 takes this layer's from buffer `parity` (left by the previous
+ * call, given this layer's router), so that no moe_layer_route precedes the
+ * call: the lookup forms the logit keys from them (with bias [E] or NULL and
+ * eps, the layer's RMSNorm) and stores them where the FFN ranks them.
+ * With chain_in == 0 and next_router == NULL, bias and eps are not read.
+ * Errors as for the two calls it replaces; MOE_ERR_ARG for a chain outside
+ * the single-token kernels or a bad next_E / parity. */
 moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_desc *d, float *h, int32_t k,
-                                const void *const *shared_ptrs, int32_t n_shared, void *ws, size_t ws_bytes,
-                                hipStream_t stream);
+                                const void *const *shared_ptrs, int32_t n_shared, const float *bias, float eps,
+                                int32_t chain_in, const float *next_router, int32_t next_E, int32_t parity,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Cross-layer prefetch (Laptop post, section 2.3: the experts of the next
  * layers are fetched while the current one computes).  idx (device int32

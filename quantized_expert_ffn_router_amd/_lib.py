@@ -134,7 +134,7 @@ def lib() -> ctypes.CDLL:
         "moe_cache_device_enable": (i32, [P, i32]),
         "moe_cache_lookup_device": (i32, [P, i32, P, i32, i32, P]),
         "moe_cache_lookup_device_route": (i32, [P, i32, P, sz, i32, P]),
-        "moe_cache_ffn_device": (i32, [P, i32, D, P, i32, P, i32, P, sz, P]),
+        "moe_cache_ffn_device": (i32, [P, i32, D, P, i32, P, i32, P, f32, i32, P, i32, i32, P, sz, P]),
         "moe_cache_prefetch_device": (i32, [P, i32, P, i32, i32, P, P]),
         "moe_cache_trace_read": (i32, [P, P, i32, P]),
         "moe_cache_stage_large": (i32, [P, i32, i32, i32, P, P, sz, P, P]),
@@ -396,11 +396,15 @@ class Cache:
         moe_layer_route (without idx_out) left in ws (moe_cache_lookup_device_route)."""
         _check(lib().moe_cache_lookup_device_route(self.h, layer, _ptr(ws), ws_bytes, k, _stream(stream)))
 
-    def ffn_device(self, layer: int, desc, h, k: int, shared_ptrs, n_shared: int, ws, ws_bytes: int, stream=None):
-        """A single token's device lookup from the route launch's keys and the
-        layer's FFN, the misses copied inside the FFN launch (moe_cache_ffn_device)."""
+    def ffn_device(self, layer: int, desc, h, k: int, shared_ptrs, n_shared: int, ws, ws_bytes: int,
+                   bias=None, eps: float = 0.0, chain_in: bool = False, next_router=None, next_E: int = 0,
+                   parity: int = 0, stream=None):
+        """A single token's device lookup and the layer's FFN, the misses copied
+        inside the FFN launch; chained layers as in moe_layer_forward_chain
+        (moe_cache_ffn_device)."""
         _check(lib().moe_cache_ffn_device(self.h, layer, ctypes.byref(_desc(desc)), _ptr(h), k, _ptr(shared_ptrs),
-                                          n_shared, _ptr(ws), ws_bytes, _stream(stream)))
+                                          n_shared, _ptr(bias), eps, int(bool(chain_in)), _ptr(next_router), next_E,
+                                          parity, _ptr(ws), ws_bytes, _stream(stream)))
 
     def prefetch_device(self, layer: int, idx, T: int, k: int, copy_stream, stream=None):
         """Prefetch of predicted ids for `layer` (moe_cache_prefetch_device):

@@ -938,8 +938,9 @@ moe_status moe_cache_lookup_device_route(moe_cache *c, int32_t layer, const void
 }
 
 moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_desc *d, float *h, int32_t k,
-                                const void *const *shared_ptrs, int32_t n_shared, void *ws, size_t ws_bytes,
-                                hipStream_t stream)
+                                const void *const *shared_ptrs, int32_t n_shared, const float *bias, float eps,
+                                int32_t chain_in, const float *next_router, int32_t next_E, int32_t parity,
+                                void *ws, size_t ws_bytes, hipStream_t stream)
 {
     if (!c || !d || !h || !ws || layer < 0 || layer >= c->n_layers || k < 1 || k > c->E ||
         ws_bytes < kDlog + (size_t)c->E * 4 || (n_shared > 0 && !shared_ptrs)) {
@@ -947,9 +948,29 @@ moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_de
         return MOE_ERR_ARG;
     }
     if (!c->dev) { set_error("moe_cache_ffn_device: moe_cache_device_enable was not called"); return MOE_ERR_STATE; }
+    const bool chain = chain_in || next_router;
+    if (chain) {
+        if (!moe_layer_chain_supported(d, 1, c->E)) {
+            set_error("moe_cache_ffn_device: chaining takes the single-token kernels (E <= %d, H <= %d)", kChainE,
+                      kChainMaxH);
+            return MOE_ERR_ARG;
+        }
+        if ((next_router && (next_E < 1 || next_E > kChainE)) || (parity != 0 && parity != 1)) {
+            set_error("moe_cache_ffn_device: next_E=%d or parity=%d out of range", next_E, parity);
+            return MOE_ERR_ARG;
+        }
+    }
+    Chain ch{};
+    ch.rp_in = chain_in ? chain_buf(ws, parity) : nullptr;
+    ch.rp_out = next_router ? chain_buf(ws, parity ^ 1) : nullptr;
+    ch.wn = next_router;
+    ch.En = next_E;
+    ch.bias = bias;
+    ch.eps = eps;
     const void *const *table = moe_cache_expert_ptrs(c, layer);
     if (resident_layer(c, layer))  // its table row is final: no lookup, nothing to copy
-        return moe_layer_ffn(d, h, 1, c->E, k, table, shared_ptrs, n_shared, ws, ws_bytes, stream);
+        return launch_ffn_copy(d, h, c->E, k, table, shared_ptrs, n_shared, ws, ws_bytes, stream, nullptr,
+                               chain ? &ch : nullptr);
     const int g = c->layer_group[layer];
     auto &G = c->groups[g];
     if (!route_defers(G.desc, 1, c->E)) {
@@ -969,8 +990,15 @@ moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_de
         }
         c->pend_touch[layer] = -1;
     }
+    uint32_t *keys = (uint32_t *)((uint8_t *)ws + kDlog);
     CacheDevArgs a = device_args(c, layer, nullptr, 1, k);
-    a.keys = (const uint32_t *)((const uint8_t *)ws + kDlog);
+    if (chain_in) {
+        // the keys are formed by the lookup from the previous layer's partials,
+        // and stored where the FFN launch ranks them
+        a.rp_in = ch.rp_in; a.hs = h; a.bias = bias; a.eps = eps; a.H = d->H; a.keys_out = keys;
+    } else {
+        a.keys = keys;
+    }
     a.jwait = c->d_jwait;
     a.done = c->d_done;
     moe_status st = launch_cache_device(a, stream);  // the lookup alone
@@ -978,7 +1006,9 @@ moe_status moe_cache_ffn_device(moe_cache *c, int32_t layer, const moe_expert_de
     prefetch_count(c, g, k);
     c->recent_touch[g] = k;
     CacheCopy cc{a.jobs, a.njobs, a.jwait, a.done, a.slot_bytes};
-    return launch_ffn_copy(d, h, c->E, k, table, shared_ptrs, n_shared, ws, ws_bytes, stream, cc);
+    ch.dlog_keys = true;  // the FFN ranks the keys the lookup ranked
+    return launch_ffn_copy(d, h, c->E, k, table, shared_ptrs, n_shared, ws, ws_bytes, stream, &cc,
+                           chain ? &ch : nullptr);
 }
 
 moe_status moe_cache_prefetch_device(moe_cache *c, int32_t layer, const int32_t *idx, int32_t T, int32_t k,

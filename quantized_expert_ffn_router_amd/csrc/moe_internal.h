@@ -105,6 +105,13 @@ struct CacheDevArgs {
     // (cleared here); no copy kernel is launched
     int32_t *jwait;              // [E]
     uint32_t *done;              // [E]
+    // T = 1 of a chained layer (keys null): the logits from the previous
+    // layer's tile partials rp_in [H/64][kChainE], the state hs [H], bias
+    // [E] (or null) and eps, as the chained gate/up kernel forms them
+    const float *rp_in, *hs, *bias;
+    float eps;
+    int H;
+    uint32_t *keys_out;          // [E] the keys formed from rp_in, for the FFN's rank
 };
 constexpr int kCacheMaxSlots = 16384;  // slots per group that the device lookup holds in LDS
 // True when moe_layer_route leaves a single token's routing to the FFN (only
@@ -123,9 +130,7 @@ struct CacheCopy {
     uint32_t *done;
     unsigned long long slot_bytes;
 };
-moe_status launch_ffn_copy(const moe_expert_desc *d, float *h, int E, int k, const void *const *eptr,
-                           const void *const *sptr, int n_shared, void *ws, size_t ws_bytes, hipStream_t s,
-                           const CacheCopy &cc);
+
 
 // Staging of a large batch's experts on the device (moe_cache_stage_large_device):
 // the layer's distinct ids, each copied from its slot or its host copy.
@@ -228,6 +233,27 @@ inline WsLayout ws_layout(const moe_expert_desc &d, int T, int k, int E, int ns)
     L.total = o;
     return L;
 }
+
+// Chained single-token layers (moe_layer_forward_chain, moe_cache_ffn_device):
+// where this layer's router dots come from (rp_in, or null: the route launch
+// ran) and where the next layer's go.
+struct Chain {
+    const float *rp_in;
+    float *rp_out;
+    const float *wn;  // the next layer's router [En][H]
+    int En;
+    const float *bias;
+    float eps;
+    bool dlog_keys;   // with rp_in: rank the keys at kDlog (formed by the cache lookup), not the partials
+};
+// The chain's hand-off buffer of the given parity in a workspace
+inline float *chain_buf(void *ws, int parity)
+{
+    return (float *)((uint8_t *)ws + kChain) + (size_t)parity * (kChainBufBytes / 4);
+}
+moe_status launch_ffn_copy(const moe_expert_desc *d, float *h, int E, int k, const void *const *eptr,
+                           const void *const *sptr, int n_shared, void *ws, size_t ws_bytes, hipStream_t s,
+                           const CacheCopy *cc, const Chain *ch);
 
 // Error reporting (thread-local message).
 void set_error(const char *fmt, ...);

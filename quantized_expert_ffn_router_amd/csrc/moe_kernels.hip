@@ -1787,6 +1787,7 @@ struct GateUpArgs {
     int En;
     float *rp_out;
     int P;  // pair records in h (with rp_in their padding blocks are cleared here)
+    int dlog_keys;  // with rp_in: rank the keys in dlog (a cache lookup formed them), not the partials
     // a cached single token whose missed experts are copied in this launch
     // (ncopy > 0, DEFER): the first ncopy workgroups copy the jobs' experts
     // from their pinned host copies into their slots, each adding its finished
@@ -1953,7 +1954,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     static_assert(!CH || DEFER, "chained layers route in the FFN");
 
     int bid = (int)blockIdx.x;
-    if constexpr (DEFER && !CH) {
+    if constexpr (DEFER) {
         if (a.ncopy) {
             if (bid < a.ncopy) {  // a copying workgroup (the first ones, dispatched first)
                 cache_copy_share(a, bid);
@@ -1971,6 +1972,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     // tiles tid%4, tid%4 + 4, ..., summed in the lane quad later), its bias
     // and the state (positions 4 tid + 2048 q)
     const bool cin = CH && a.rp_in;
+    const bool ckeys = cin && !a.dlog_keys;  // the keys formed here from the partials
     float4 hst[kChainMaxH / 2048];
     float pv[kChainMaxH / 256];
     float dsum = 0.f, dbias = 0.f;
@@ -1983,8 +1985,10 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
 #pragma unroll
             for (int q = 0; q < kChainMaxH / 2048; q++)
                 hst[q] = ((const float4 *)a.hs)[min((int)threadIdx.x + kGUThreads * q, (H >> 2) - 1)];
+            if (ckeys) {
 #pragma unroll
-            for (int n = 0; n < kChainMaxH / 256; n++) pv[n] = a.rp_in[min(q4 + 4 * n, nct - 1) * kChainE + i];
+                for (int n = 0; n < kChainMaxH / 256; n++) pv[n] = a.rp_in[min(q4 + 4 * n, nct - 1) * kChainE + i];
+            }
         }
     }
     // DEFER: the logit key (unless CH computes it) and expert address of id
@@ -1993,9 +1997,9 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     const void *dptr = nullptr;
     int djw = 0;  // ncopy: the id's copy job + 1 (0: no copy to wait for)
     if (DEFER && u < a.k && (threadIdx.x & 3) == 0 && (int)(threadIdx.x >> 2) < a.E) {
-        if (!cin) dkey = a.dlog[threadIdx.x >> 2];
+        if (!ckeys) dkey = a.dlog[threadIdx.x >> 2];
         dptr = a.eptr[threadIdx.x >> 2];
-        if (!CH && a.ncopy) djw = a.jwait[threadIdx.x >> 2];
+        if (a.ncopy) djw = a.jwait[threadIdx.x >> 2];
     }
     u32x4 xr[kGUPre] = {};
     if (ALL && !cin) {
@@ -2031,7 +2035,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 const int i0 = (k + ns) * a.ntile;
                 if (a.rp_out)
                     chain_dots(a.wn, a.hs, a.En, H, a.rp_out, (bid - i0) * kGUThreads + tid,
-                               ((int)gridDim.x - i0) * kGUThreads);
+                               ((int)gridDim.x - a.ncopy - i0) * kGUThreads);
                 // the route launch, which did not run, cleared the pair
                 // records' padding blocks
                 if (cin && u == k + ns && a.kd > a.I)
@@ -2060,11 +2064,13 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 for (int q = 0; q < kChainMaxH / 2048; q++) {
                     hst[q].x *= rms; hst[q].y *= rms; hst[q].z *= rms; hst[q].w *= rms;
                 }
+                if (ckeys) {
 #pragma unroll
-                for (int n = 0; n < kChainMaxH / 256; n++) dsum += (tid & 3) + 4 * n < (H >> 6) ? pv[n] : 0.f;
-                dsum += xchg<1>(dsum);
-                dsum += xchg<2>(dsum);
-                dkey = logit_key(dsum * rms + dbias);
+                    for (int n = 0; n < kChainMaxH / 256; n++) dsum += (tid & 3) + 4 * n < (H >> 6) ? pv[n] : 0.f;
+                    dsum += xchg<1>(dsum);
+                    dsum += xchg<2>(dsum);
+                    dkey = logit_key(dsum * rms + dbias);
+                }
             }
         }
         if (u >= k) {
@@ -2081,7 +2087,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             __syncthreads();
             e = lsel_e[u];
             base = (const uint8_t *)lsel_p[u];
-            if constexpr (!CH) {
+            {
                 const int jw = a.ncopy ? lsel_w[u] : 0;
                 if (jw > 0) {
                     // a missed expert: thread 0 waits for its copy, then an
@@ -3555,12 +3561,42 @@ __global__ __launch_bounds__(kCacheThreads) void k_cache_lookup(CacheDevArgs a)
     for (int e = tid; e < E; e += kCacheThreads) sel[e] = 0;
     if (tid == 0) s_absent = 0;
     if (tid < E) lwhere[tid] = wpre;
-    if (a.keys) {
+    if (a.keys || a.rp_in) {
         // a single token (E <= 128): the k largest logit keys, ties to the
         // lower id (a lane quad ranks each key, as the gate/up kernel does)
         __shared__ __align__(16) uint64_t lrk[(kCacheThreads / 128) * kRankStride];
         const int i = tid >> 2;
-        const uint64_t key = i < E ? (uint64_t)a.keys[i] << 32 | (uint32_t)~i : 0ull;
+        uint32_t kv = 0;
+        if (a.rp_in) {
+            // a chained layer: the router's dots with the state are the
+            // previous layer's tile partials (lane quad i sums tiles q,
+            // q+4, ...), times 1/RMS of the state, plus the bias; the keys
+            // are stored for the FFN launch, which ranks them as here
+            __shared__ float lss[kCacheThreads / 64];
+            const int q4 = tid & 3, nct = a.H >> 6, ic = min(i, kChainE - 1);
+            float pv[kChainMaxH / 256];
+#pragma unroll
+            for (int n = 0; n < kChainMaxH / 256; n++) pv[n] = a.rp_in[min(q4 + 4 * n, nct - 1) * kChainE + ic];
+            const float4 x = tid < (a.H >> 2) ? ((const float4 *)a.hs)[tid] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float bz = a.bias && i < E ? a.bias[i] : 0.f;
+            float ss = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+            ss = wave_sum(ss);
+            if (lane == 0) lss[tid >> 6] = ss;
+            float d = 0.f;
+#pragma unroll
+            for (int n = 0; n < kChainMaxH / 256; n++) d += q4 + 4 * n < nct ? pv[n] : 0.f;
+            d += xchg<1>(d);
+            d += xchg<2>(d);
+            __syncthreads();
+            ss = 0.f;
+#pragma unroll
+            for (int w = 0; w < kCacheThreads / 64; w++) ss += lss[w];
+            kv = logit_key(d * (1.0f / sqrtf(ss / (float)a.H + a.eps)) + bz);
+            if (q4 == 0 && i < E) a.keys_out[i] = kv;
+        } else if (i < E) {
+            kv = a.keys[i];
+        }
+        const uint64_t key = i < E ? (uint64_t)kv << 32 | (uint32_t)~i : 0ull;
         const int r = rank_keys_128(key, E, lrk);
         if ((tid & 3) == 0 && i < E) sel[i] = r < a.k;
     } else {
@@ -4012,17 +4048,6 @@ bool defer_grouping(const moe_expert_desc &d, int T, int k, int ns)
     return use_i8(d, T) && T * k <= kGUI8Threads && T * (k + ns) <= 256;
 }
 
-// Chained single-token layers: where this layer's router dots come from
-// (rp_in, or null: the route launch ran) and where the next layer's go.
-struct Chain {
-    const float *rp_in;
-    float *rp_out;
-    const float *wn;  // the next layer's router [En][H]
-    int En;
-    const float *bias;
-    float eps;
-};
-
 // The down kernel's block for a single token, and whether the pair's record
 // fits its registers (the one-pair-per-item kernel)
 int down_block(const ExpertGeom &g)
@@ -4076,6 +4101,7 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
     if (ch) {
         ga.rp_in = ch->rp_in; ga.hs = y; ga.bias = ch->bias; ga.eps = ch->eps;
         ga.wn = ch->wn; ga.En = ch->En; ga.rp_out = ch->rp_out; ga.P = L.P;
+        ga.dlog_keys = ch->dlog_keys ? 1 : 0;
     }
 #define GATE_UP(Q)                                                                        \
     (ch ? k_gate_up<Q, 1, true, true><<<ggrid, kGUThreads, glds, s>>>(ga)                \
@@ -4150,7 +4176,7 @@ moe_status launch_cache_device(const CacheDevArgs &a, hipStream_t s, hipStream_t
 
 moe_status launch_ffn_copy(const moe_expert_desc *d, float *h, int E, int k, const void *const *eptr,
                            const void *const *sptr, int n_shared, void *ws, size_t ws_bytes, hipStream_t s,
-                           const CacheCopy &cc)
+                           const CacheCopy *cc, const Chain *ch)
 {
     ExpertGeom g;
     moe_status st = check_desc(d, &g);
@@ -4163,7 +4189,7 @@ moe_status launch_ffn_copy(const moe_expert_desc *d, float *h, int E, int k, con
         set_error("moe_cache_ffn_device: the single-token kernels are needed (E <= 128, H <= 4096)");
         return MOE_ERR_ARG;
     }
-    return launch_ffn_kernels(*d, g, W, 1, E, eptr, sptr, h, nullptr, s, true, nullptr, &cc);
+    return launch_ffn_kernels(*d, g, W, 1, E, eptr, sptr, h, nullptr, s, true, ch, cc);
 }
 
 moe_status launch_stage_device(const StageDevArgs &a, hipStream_t s)
@@ -4368,10 +4394,9 @@ moe_status moe_layer_forward_chain(const moe_expert_desc *d, float *h, int32_t T
                              ws, ws_bytes, s);
         if (st != MOE_OK) return st;
     }
-    float *buf = W.at<float>(kChain);
     Chain c{};
-    c.rp_in = chain_in ? buf + (size_t)parity * (kChainBufBytes / 4) : nullptr;
-    c.rp_out = next_router ? buf + (size_t)(parity ^ 1) * (kChainBufBytes / 4) : nullptr;
+    c.rp_in = chain_in ? chain_buf(ws, parity) : nullptr;
+    c.rp_out = next_router ? chain_buf(ws, parity ^ 1) : nullptr;
     c.wn = next_router;
     c.En = next_E;
     c.bias = bias;

@@ -176,7 +176,11 @@ class CachedStack:
     trace (device_trace).  ffn_copies (the default; device lookup without
     prefetch) copies a single token's misses inside the FFN's gate/up launch
     (moe_cache_ffn_device), so that the hit experts' work overlaps the
-    copies and no copy launch runs; False keeps the copy launch.
+    copies and no copy launch runs; False keeps the copy launch.  chain=True
+    (with ffn_copies) chains single-token steps as ResidentStack.step does:
+    one route launch per step, each layer's FFN launches leaving the next
+    layer's router dots, from which the next lookup forms its keys (measured
+    no faster than the route launch it saves, so not the default).
 
     prefetch_depth=d > 0 (device_lookup only) adds cross-layer prefetch: at
     layer l, after its lookup, the layers up to l+d not prefetched yet in
@@ -189,7 +193,7 @@ class CachedStack:
     def __init__(self, layers: Sequence[LayerSpec], packed: Sequence[torch.Tensor], slots: Sequence[int],
                  T_max: int = 8, device: str = "cuda", eps: float = 1e-6, device_lookup: bool = False,
                  trace_capacity: int = 0, prefetch_depth: int = 0, resident: Optional[Sequence[bool]] = None,
-                 ffn_copies: bool = True):
+                 ffn_copies: bool = True, chain: bool = False):
         """resident[l] (e.g. from moe_placement_plan) keeps layer l's experts
         resident in HBM, outside the cache."""
         if prefetch_depth and not device_lookup:
@@ -261,6 +265,10 @@ class CachedStack:
         # a single token's misses copied inside the FFN launch (moe_cache_ffn_device;
         # device lookup without prefetch)
         self.ffn_copies = bool(ffn_copies) and device_lookup and not self.prefetch_depth
+        # single-token steps chained as ResidentStack.step chains them (one route
+        # launch per step; moe_cache_ffn_device with the hand-off of router dots)
+        self.chain = bool(chain) and self.ffn_copies and all(
+            L.moe_layer_chain_supported(dd, 1, s.E) for dd, s in zip(self.descs, self.layers))
         self.trace_capacity = trace_capacity
         if device_lookup:
             self.cache.enable_device(trace_capacity)
@@ -281,6 +289,16 @@ class CachedStack:
         T = h.shape[0]
         d = self.descs[layer]
         idx = self.idx_dev[:T * s.k].view(T, s.k)
+        if self.chain and T == 1:
+            nxt = self.layers[layer + 1] if layer + 1 < len(self.layers) else None
+            if layer == 0:  # the step's one route launch
+                L.moe_layer_route(d, h, T, self.routers[0], self.biases[0], s.E, s.k, None, self.shared_ptrs(0),
+                                  s.n_shared, self.eps, None, None, self.ws, self.ws_bytes)
+            self.cache.ffn_device(layer, d, h, s.k, self.shared_ptrs(layer), s.n_shared, self.ws, self.ws_bytes,
+                                  bias=self.biases[layer], eps=self.eps, chain_in=layer > 0,
+                                  next_router=None if nxt is None else self.routers[layer + 1],
+                                  next_E=0 if nxt is None else nxt.E, parity=layer & 1)
+            return
         if self.device_lookup and T == 1 and self._keys_lookup[layer]:
             # a single token: the route launch only writes the logit keys, and
             # the lookup kernel picks the top-k from them (no routing tail)

@@ -39,7 +39,7 @@ def _groups(cfg, n_layers):
 
 
 def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=0, slots=None, resident=None,
-         ffn_copies=False):
+         ffn_copies=False, chain=False):
     """slots=None: the planner's slots for `fraction` of the routed expert
     bytes (checked against the oracle planner); else the given slots, where
     a group at 0 slots keeps its layers resident."""
@@ -60,8 +60,9 @@ def _run(cfg, n_layers, steps, fraction, T, device_lookup=False, prefetch_depth=
     packed = [pack_layer(s, l, experts) for l, s in enumerate(specs)]
     cap = steps * n_layers * T * cfg.k * (2 if prefetch_depth else 1)
     cs = CachedStack(specs, packed, slots, T_max=T, device_lookup=device_lookup, trace_capacity=cap,
-                     prefetch_depth=prefetch_depth, resident=resident, ffn_copies=ffn_copies)
+                     prefetch_depth=prefetch_depth, resident=resident, ffn_copies=ffn_copies, chain=chain)
     assert cs.ffn_copies == (ffn_copies and device_lookup and not prefetch_depth)
+    assert cs.chain == (chain and cs.ffn_copies)
     targets = [cs.prefetch_targets(l) for l in range(n_layers)]
     pred = np.zeros((steps, n_layers, T * cfg.k), np.int32)
     cs.trace = []
@@ -139,12 +140,15 @@ def test_cache_zipf_qwen3_shape(fraction, device_lookup):
     _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, device_lookup, ffn_copies=False)
 
 
+@pytest.mark.parametrize("chain", [False, True], ids=["unchained", "chained"])
 @pytest.mark.parametrize("fraction", [0.1, 0.6])
-def test_cache_ffn_copies_device_lru(fraction):
+def test_cache_ffn_copies_device_lru(fraction, chain):
     """A single token's misses copied inside the FFN's gate/up launch
     (moe_cache_ffn_device): every step's state, the hit/miss/victim trace and
-    the slot tables against the oracle, as with the copy launch."""
-    s = _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, True, ffn_copies=True)
+    the slot tables against the oracle, as with the copy launch; chained, the
+    lookup forms the keys from the previous layer's router partials (one
+    route launch per step) with the Zipf bias."""
+    s = _run(W.qwen3_30b_a3b_q4k_zipf(T=1, n_layers=4), 4, 24, fraction, 1, True, ffn_copies=True, chain=chain)
     assert s["misses"] > 0
 
 
@@ -154,7 +158,7 @@ def test_cache_ffn_copies_mixed_shared():
     cfg = W.mixed_shared_q4k_q6k(T=1)
     Q4, Q6 = W.Q4_K, W.Q6_K
     sub = cfg.with_(n_layers=4, layer_qtypes=((Q4,) * 3, (Q4,) * 3, (Q6,) * 3, (Q6,) * 3), seed=cfg.seed + 50)
-    s = _run(sub, 4, 12, 0.1, 1, True, ffn_copies=True)
+    s = _run(sub, 4, 12, 0.1, 1, True, ffn_copies=True, chain=True)
     assert s["misses"] > 0 and s["evictions"] > 0
 
 
@@ -411,7 +415,10 @@ def test_cache_fit_placement_resident_and_cached_layers(device_lookup):
     st, state, slots = moe.moe_placement_plan([desc], [0] * 4, cfg.E, int(1.75 * layer_bytes), int(0.25 * layer_bytes),
                                               cfg.k, moe.MOE_PLACE_FIT)
     assert st == 0 and state.tolist() == [-1, 0, 0, 0], state
-    s = _run(cfg, 4, 16, None, 1, device_lookup, slots=slots, resident=[x < 0 for x in state])
+    # device LRU: chained with the misses copied in the FFN launch (the resident
+    # layer 0 takes the step's route launch and hands on its router dots)
+    s = _run(cfg, 4, 16, None, 1, device_lookup, slots=slots, resident=[x < 0 for x in state],
+             ffn_copies=device_lookup, chain=device_lookup)
     assert s["lookups"] > 0 and s["evictions"] > 0
 
 
