@@ -1944,7 +1944,9 @@ constexpr int kDnPre = 4;       // record words per thread loaded before the wei
 // every token's record fits the first pass and the prefetch words (T <= 2,
 // T * RB <= kGUPre * kGUThreads * 16); the records are then loaded before
 // the work entry arrives, token t to LDS slot t.
-template <int QT, int NTOK, bool DEFER, bool CH = false>
+// CP: a cached single token whose misses this launch copies (ncopy > 0); the
+// copy role and the waits are compiled only into these instantiations
+template <int QT, int NTOK, bool DEFER, bool CH = false, bool CP = false>
 __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT == MOE_Q4_K && !CH ? 4 : 2))) void k_gate_up(GateUpArgs a)
 {
     extern __shared__ __align__(16) uint8_t xs[];
@@ -1952,27 +1954,26 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     constexpr bool ALL = NTOK <= 2;
     static_assert(!DEFER || NTOK == 1, "routing in the FFN is for a single token");
     static_assert(!CH || DEFER, "chained layers route in the FFN");
+    static_assert(!CP || DEFER, "the copies are a single token's");
 
     int bid = (int)blockIdx.x;
-    if constexpr (DEFER) {
-        if (a.ncopy) {
-            if (bid < a.ncopy) {  // a copying workgroup (the first ones, dispatched first)
-                cache_copy_share(a, bid);
-                return;
-            }
-            bid -= a.ncopy;
+    if constexpr (CP) {
+        if (bid < a.ncopy) {  // a copying workgroup (the first ones, dispatched first)
+            cache_copy_share(a, bid);
+            return;
         }
+        bid -= a.ncopy;
     }
     const int u = bid / a.ntile;
     const int rt = bid - u * a.ntile;
     const int H = a.H, S = H >> 8;
     const size_t RB = enc_bytes(H);
     const int q16 = (int)(RB / 16);  // 16-byte words per record
+    const bool cin = CH && a.rp_in;
+    const bool ckeys = cin && !a.dlog_keys;  // the keys formed here from the partials
     // CH loads first: with rp_in, this layer's router partials (id tid/4:
     // tiles tid%4, tid%4 + 4, ..., summed in the lane quad later), its bias
     // and the state (positions 4 tid + 2048 q)
-    const bool cin = CH && a.rp_in;
-    const bool ckeys = cin && !a.dlog_keys;  // the keys formed here from the partials
     float4 hst[kChainMaxH / 2048];
     float pv[kChainMaxH / 256];
     float dsum = 0.f, dbias = 0.f;
@@ -1985,10 +1986,9 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
 #pragma unroll
             for (int q = 0; q < kChainMaxH / 2048; q++)
                 hst[q] = ((const float4 *)a.hs)[min((int)threadIdx.x + kGUThreads * q, (H >> 2) - 1)];
-            if (ckeys) {
+            // (loaded even when the keys come from dlog)
 #pragma unroll
-                for (int n = 0; n < kChainMaxH / 256; n++) pv[n] = a.rp_in[min(q4 + 4 * n, nct - 1) * kChainE + i];
-            }
+            for (int n = 0; n < kChainMaxH / 256; n++) pv[n] = a.rp_in[min(q4 + 4 * n, nct - 1) * kChainE + i];
         }
     }
     // DEFER: the logit key (unless CH computes it) and expert address of id
@@ -1999,7 +1999,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
     if (DEFER && u < a.k && (threadIdx.x & 3) == 0 && (int)(threadIdx.x >> 2) < a.E) {
         if (!ckeys) dkey = a.dlog[threadIdx.x >> 2];
         dptr = a.eptr[threadIdx.x >> 2];
-        if (a.ncopy) djw = a.jwait[threadIdx.x >> 2];
+        if (CP) djw = a.jwait[threadIdx.x >> 2];
     }
     u32x4 xr[kGUPre] = {};
     if (ALL && !cin) {
@@ -2035,7 +2035,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 const int i0 = (k + ns) * a.ntile;
                 if (a.rp_out)
                     chain_dots(a.wn, a.hs, a.En, H, a.rp_out, (bid - i0) * kGUThreads + tid,
-                               ((int)gridDim.x - a.ncopy - i0) * kGUThreads);
+                               ((int)gridDim.x - (CP ? a.ncopy : 0) - i0) * kGUThreads);
                 // the route launch, which did not run, cleared the pair
                 // records' padding blocks
                 if (cin && u == k + ns && a.kd > a.I)
@@ -2087,8 +2087,8 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
             __syncthreads();
             e = lsel_e[u];
             base = (const uint8_t *)lsel_p[u];
-            {
-                const int jw = a.ncopy ? lsel_w[u] : 0;
+            if constexpr (CP) {
+                const int jw = lsel_w[u];
                 if (jw > 0) {
                     // a missed expert: thread 0 waits for its copy, then an
                     // acquire, so that no line of the slot read before the
@@ -2285,7 +2285,7 @@ __global__ __launch_bounds__(kGUThreads) __attribute__((amdgpu_waves_per_eu(QT =
                 gs += part[sl][tt][rr][0];
                 us += part[sl][tt][rr][1];
             }
-            const float hv = gave ? __builtin_nanf("") : gs / (1.0f + expf(-gs)) * us;
+            const float hv = CP && gave ? __builtin_nanf("") : gs / (1.0f + expf(-gs)) * us;
             encode32(hv, rr, rec_at(a.h, c0 + tt, a.kd), a.kd, rt * 32);
             if (a.act_out) a.act_out[(size_t)(c0 + tt) * a.kd + rt * 32 + rr] = hv;
         }
@@ -4104,7 +4104,9 @@ moe_status launch_ffn_kernels(const moe_expert_desc &d, const ExpertGeom &g, con
         ga.dlog_keys = ch->dlog_keys ? 1 : 0;
     }
 #define GATE_UP(Q)                                                                        \
-    (ch ? k_gate_up<Q, 1, true, true><<<ggrid, kGUThreads, glds, s>>>(ga)                \
+    (ch && cc ? k_gate_up<Q, 1, true, true, true><<<ggrid, kGUThreads, glds, s>>>(ga)     \
+     : ch ? k_gate_up<Q, 1, true, true><<<ggrid, kGUThreads, glds, s>>>(ga)              \
+     : cc ? k_gate_up<Q, 1, true, false, true><<<ggrid, kGUThreads, glds, s>>>(ga)       \
      : defer ? k_gate_up<Q, 1, true><<<ggrid, kGUThreads, glds, s>>>(ga)                 \
      : all ? (T == 1 ? k_gate_up<Q, 1, false><<<ggrid, kGUThreads, glds, s>>>(ga)        \
                      : k_gate_up<Q, 2, false><<<ggrid, kGUThreads, glds, s>>>(ga))       \
