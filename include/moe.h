@@ -155,11 +155,15 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t s);
  * and no caller can miss it.  The bits are sticky: since late senders may
  * still write into the hand-off arrays, every later route launch on the
  * workspace that would read them routes with NaN weights too (without
- * waiting) until moe_workspace_init clears the workspace.  Exception: a
+ * waiting) until moe_workspace_init clears the workspace.  Exceptions: a
  * single token on the dot-product path with E <= 128 and H <= 4096 is ranked
  * again inside moe_layer_ffn's gate/up kernel from plainly stored logits, not
  * from the hand-off: its updated state stays exact (only idx_out / w_out, when
- * requested, show the NaN weights). */
+ * requested, show the NaN weights).  2 to 8 tokens on the integer-MFMA path
+ * (all-Q4_K experts) with E <= 256 are ranked there too; without idx_out and
+ * w_out the route launch then hands nothing over and waits for nothing, but
+ * that gate/up kernel still routes with NaN weights while a bit is set, as the
+ * route launch would. */
 enum {
     MOE_WS_KEYS_TIMEOUT = 1, /* the wait for the router's logit keys gave up */
     MOE_WS_TOPK_TIMEOUT = 2, /* a wait on the per-token top-k hand-off gave up */

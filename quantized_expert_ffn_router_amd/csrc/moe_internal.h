@@ -164,10 +164,12 @@ constexpr size_t kTkBytes = (size_t)kMaxT * 64 * 8;
 constexpr size_t kStatus = kKeys + kKeysBytes + kTkBytes;
 constexpr size_t kStatusBytes = 256;
 static_assert(kStatus == MOE_WS_STATUS_OFFSET, "status word offset published in moe.h");
-// Then a single token's logit keys, written by the route launch for routing
-// in the FFN kernels (or in the cache's device lookup), at a fixed offset.
+// Then the logit keys of up to kDlogTok tokens, [T][E], written by the route
+// launch for routing in the FFN kernels (or, for a single token, in the
+// cache's device lookup), at a fixed offset.
+constexpr int kDlogTok = 8;
 constexpr size_t kDlog = kStatus + kStatusBytes;
-constexpr size_t kDlogBytes = (size_t)kMaxE * 4;
+constexpr size_t kDlogBytes = (size_t)kDlogTok * kMaxE * 4;
 // Then the router dot products that chained single-token layers hand on:
 // two buffers (the layer's parity picks the one it reads; it writes the
 // other) of partial sums over 64-position tiles of the state, [H/64][kChainE]

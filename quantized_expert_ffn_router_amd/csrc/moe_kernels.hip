@@ -688,7 +688,7 @@ struct RouteArgs {
     int topk_blocks;        // 0, or T: a workgroup per token ranks its keys and hands them to the tail
     unsigned long long *tk; // [T][k] hand-over of those selections (key << 32 | ~id, never zero)
     int tail;               // 1: the last workgroup routes (keys handed over); 0: no tail
-    uint32_t *dlog;         // [E] (T = 1) the logit keys for routing in the FFN (plain stores), or null
+    uint32_t *dlog;         // [T][E] the logit keys for routing in the FFN (plain stores), or null
     int sb_scale;           // 1: the input records share one scale per 256-position super-block
     uint32_t *status;       // the workspace's status word: nonzero = a wait gave up earlier (sticky)
     unsigned spin;          // polling rounds before a wait gives up
@@ -775,10 +775,60 @@ __device__ __forceinline__ void topk_multi(const uint32_t (&key)[NT][NVL], int E
     for (int t = 0; t < NT; t++) out[t] = lane < k ? cand[t * cstride + soff + lane] : 0ull;
 }
 
-// topk_multi for a single token.  cand: E + 9 + k + 1 slots.
+// Top-k of one token's keys by one wave for k <= 8: lane l holds experts
+// l + 64 i in key[i] (zero past E).  tau, the smallest of the eight 8-lane
+// groups' largest keys, bounds the top k from below (each group holds a key
+// >= tau, so at least 8 >= k keys reach it); six lane exchanges find it,
+// where topk_multi sorts the 64 lane maxima.  The candidates >= tau, as
+// 64-bit C = key << 32 | ~e, are ranked against each other in LDS as there:
+// the same result, lane j < k returning selection j (key descending, ties to
+// the lower id), the other lanes 0.  cand: LDS of E + 23 64-bit slots,
+// 16-byte aligned.
+template <int NVL>
+__device__ __forceinline__ uint64_t topk_few(const uint32_t (&key)[NVL], int E, int k, uint64_t *cand)
+{
+    const int lane = lane_id();
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; i++) v = max(v, key[i]);
+    v = max(v, (uint32_t)xchg<1>((int)v));
+    v = max(v, (uint32_t)xchg<2>((int)v));
+    v = max(v, (uint32_t)xchg<4>((int)v));
+    v = min(v, (uint32_t)xchg<8>((int)v));
+    v = min(v, (uint32_t)xchg<16>((int)v));
+    v = min(v, (uint32_t)xchg<32>((int)v));
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; i++) {
+        const int e = lane + 64 * i;
+        const bool c = e < E && key[i] >= tau;
+        const uint64_t bal = __ballot(c);
+        if (c) cand[m + below(bal)] = (uint64_t)key[i] << 32 | (uint32_t)~e;
+        m += __popcll(bal);
+    }
+    if (lane < 8) cand[m + lane] = 0ull;
+    const int mp = (m + 7) & ~7, soff = mp + 8;
+    for (int c = lane; c < m; c += 64) {
+        const uint64_t ci = cand[c];
+        int r0 = 0, r1 = 0;
+        for (int c2 = 0; c2 < mp; c2 += 8) {
+            const ulonglong2 *q = (const ulonglong2 *)(cand + c2);
+            const ulonglong2 x0 = q[0], x1 = q[1], x2 = q[2], x3 = q[3];
+            r0 += (x0.x > ci) + (x0.y > ci) + (x1.x > ci) + (x1.y > ci);
+            r1 += (x2.x > ci) + (x2.y > ci) + (x3.x > ci) + (x3.y > ci);
+        }
+        if (r0 + r1 < k) cand[soff + r0 + r1] = ci;
+    }
+    return lane < k ? cand[soff + lane] : 0ull;
+}
+
+// Top-k of a single token: topk_few for k <= 8, else topk_multi.  cand:
+// E + 9 + k + 1 slots, and at least E + 23.
 template <int NVL>
 __device__ __forceinline__ uint64_t topk_one(const uint32_t (&key)[NVL], int E, int k, uint64_t *cand)
 {
+    if (k <= 8) return topk_few<NVL>(key, E, k, cand);
     uint32_t kk[1][NVL];
 #pragma unroll
     for (int i = 0; i < NVL; i++) kk[0][i] = key[i];
@@ -1027,7 +1077,7 @@ __device__ __forceinline__ void route_tail(const RouteArgs &a)
                 key[0][i] = e < E ? lk[t * E + e] : 0u;
             }
             uint64_t cs[1];
-            topk_multi<NVL, 1>(key, E, k, u.cand[wave_id()], kCandSlots, cs);
+            cs[0] = topk_one<NVL>(key[0], E, k, u.cand[wave_id()]);
             if (lane < k) {
                 sidx[t * k + lane] = (int)~(uint32_t)cs[0];
                 skey[t * k + lane] = (uint32_t)(cs[0] >> 32);
@@ -1139,7 +1189,7 @@ __device__ __forceinline__ void router_rows(const RouteArgs &a, int e0, int nr, 
                 }
                 const float rr = a.normalize ? 1.0f / sqrtf(q / (float)H + a.eps) : 1.0f;
                 const float lg = d * rr + (a.bias ? a.bias[e0 + r] : 0.f);
-                if (a.dlog) a.dlog[e0 + r] = logit_key(lg);  // read after the launch boundary
+                if (a.dlog) a.dlog[(size_t)t * E + e0 + r] = logit_key(lg);  // read after the launch boundary
                 if (a.tail && !a.withhold)
                     __hip_atomic_store(a.keys + (size_t)t * E + e0 + r, logit_key(lg), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -3110,9 +3160,13 @@ struct GateUpI8Args {
     float *hf;          // [P][kd]
     float *act_out;     // [P][kd] or null
     int nrb;            // I / 64
-    // grouping in these workgroups (idx_in non-null): the routing's ids and weights
+    // grouping in these workgroups (idx_in non-null): the routing's ids and
+    // weights, or (keys_in non-null) its top-k and softmax here too, from the
+    // logit keys, with NaN weights once the status word is set
     const int *idx_in;     // [T][k]
     const float *w_in;     // [T][k]
+    const uint32_t *keys_in;  // [T][E] or null
+    const uint32_t *status;
     int T, k, ns, Umax;
     WorkEntry *wt_out;  // the down kernel's work table (pair indices inline), its length,
     int *nuniq_out;     // each pair's token and weight, (token, slot) -> pair
@@ -3139,9 +3193,23 @@ __device__ __forceinline__ void load_q4k_plane_row(uint4 &meta, uint4 (&qp)[4], 
     for (int c = 0; c < 4; c++) qp[c] = ldg<uint4>(tile, 1024 + (2 * c + kh) * 1024 + row64 * 16);
 }
 
+// LDS bytes of i8_group: the grouping's arrays (i8_group_lds0, 16-byte
+// aligned), then the top-k's candidate slots and the ids and weights
+__host__ __device__ constexpr size_t i8_group_lds0(int E)
+{
+    return ((size_t)E * 4 + (size_t)E * kI8Tok + 16 + 15) / 16 * 16;
+}
+__host__ __device__ constexpr size_t i8_group_lds(int E)
+{
+    return i8_group_lds0(E) + (size_t)kI8Tok * kCandSlots * 8 + (size_t)2 * kI8Tok * kMaxK * 4;
+}
+
 // Grouping of T <= 8 tokens' routing in every workgroup of the integer-MFMA
-// gate/up kernel, from the ids and weights the route launch wrote (its tail
-// skips the grouping): workgroup u takes the u-th selected expert in
+// gate/up kernel, from the ids and weights the route launch's tail wrote (it
+// skips the grouping), or from the logit keys alone (the route launch has no
+// tail): then wave t < T first takes token t's top-k (topk_one, as the
+// tail's waves do) and its softmax over the k selected
+// logits, the same arithmetic in the same order as the tail's.  Workgroup u takes the u-th selected expert in
 // ascending id (then the shared experts) with the tokens that selected it
 // (ascending) and their pair indices t k + j (j the slot of the expert in
 // token t's selection) for routed pairs, T k + s T + t for shared ones: the
@@ -3149,7 +3217,7 @@ __device__ __forceinline__ void load_q4k_plane_row(uint4 &meta, uint4 (&qp)[4], 
 // Workgroup 0 also writes what the down kernel reads: each pair's token and
 // combine weight, the (token, slot) -> pair map, the work table (pair
 // indices inline) and its length.  Returns the entry's pair count (0: no
-// entry u).  lw: LDS of i8_group_lds(T, E) bytes.
+// entry u).  lw: LDS of i8_group_lds(E) bytes.
 __device__ __forceinline__ int i8_group(const GateUpI8Args &a, int u, int &e, uint64_t &toks, uint64_t &pairs,
                                         uint32_t *lw)
 {
@@ -3157,10 +3225,46 @@ __device__ __forceinline__ int i8_group(const GateUpI8Args &a, int u, int &e, ui
     uint32_t *lmask = lw;                       // [E] tokens selecting each expert
     uint8_t *lslot = (uint8_t *)(lw + E);       // [E][kI8Tok] slot of the expert in each token
     int *lsel = (int *)(lslot + E * kI8Tok);    // [2] the u-th selected expert, selected count
+    const int *ids = a.idx_in;
+    const float *wts = a.w_in;
+    if (a.keys_in) {
+        uint64_t *cand = (uint64_t *)((uint8_t *)lw + i8_group_lds0(E));  // [kI8Tok][kCandSlots]
+        int *lid = (int *)(cand + kI8Tok * kCandSlots);                     // [T][k]
+        float *lwt = (float *)(lid + kI8Tok * kMaxK);                       // [T][k]
+        const int w = wave_id();
+        if (w < T) {
+            const uint32_t *kt = a.keys_in + (size_t)w * E;
+            const bool dead = *a.status != 0u;
+            uint64_t *cw = cand + w * kCandSlots;
+            uint64_t cs;
+            if (E <= 128) {
+                uint32_t key[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) key[i] = lane + 64 * i < E ? kt[lane + 64 * i] : 0u;
+                cs = topk_one<2>(key, E, k, cw);
+            } else {
+                uint32_t key[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) key[i] = lane + 64 * i < E ? kt[lane + 64 * i] : 0u;
+                cs = topk_one<4>(key, E, k, cw);
+            }
+            const bool live = lane < k;
+            const float lg = live ? unord_bits((uint32_t)(cs >> 32)) : 0.f;
+            const float top = __shfl(lg, 0, 64);
+            const float ex = live ? expf(lg - top) : 0.f;
+            const float sum = k <= 8 ? group_sum<8>(ex) : wave_sum(ex);
+            if (live) {
+                lid[w * k + lane] = (int)~(uint32_t)cs;
+                lwt[w * k + lane] = dead ? __builtin_nanf("") : ex / sum;
+            }
+        }
+        ids = lid;
+        wts = lwt;
+    }
     for (int j = tid; j < E; j += blockDim.x) lmask[j] = 0u;
     __syncthreads();
     if (tid < P) {
-        const int id = a.idx_in[tid], t = tid / k;
+        const int id = ids[tid], t = tid / k;
         if ((unsigned)id < (unsigned)E) {
             atomicOr(&lmask[id], 1u << t);
             lslot[id * kI8Tok + t] = (uint8_t)(tid - t * k);
@@ -3206,9 +3310,9 @@ __device__ __forceinline__ int i8_group(const GateUpI8Args &a, int u, int &e, ui
     if (w0) {
         for (int p = tid; p < P; p += blockDim.x) {
             const int t = p / k;
-            a.pw_out[p] = a.w_in[p];
+            a.pw_out[p] = wts[p];
             a.ptok_out[p] = t;
-            a.inv_out[t * (k + ns) + (p - t * k)] = (unsigned)a.idx_in[p] < (unsigned)E ? p : -1;
+            a.inv_out[t * (k + ns) + (p - t * k)] = (unsigned)ids[p] < (unsigned)E ? p : -1;
         }
         for (int i = tid; i < ns * T; i += blockDim.x) {
             const int s2 = i / T, t = i - s2 * T, p = P + s2 * T + t;
@@ -3251,12 +3355,6 @@ __device__ __forceinline__ int i8_group(const GateUpI8Args &a, int u, int &e, ui
     }
     __syncthreads();  // lw is reused by the caller
     return n;
-}
-
-// LDS bytes of i8_group
-__host__ __device__ constexpr size_t i8_group_lds(int E)
-{
-    return (size_t)E * 4 + (size_t)E * kI8Tok + 16;
 }
 
 template <bool DEFER>
@@ -3963,6 +4061,8 @@ moe_status launch_ffn_i8(const moe_expert_desc &d, const ExpertGeom &g, const Ws
     ga.nrb = d.I / 64;
     ga.idx_in = defer ? ws.at<int>(L.idx) : nullptr;
     ga.w_in = ws.at<float>(L.w);
+    ga.keys_in = defer && E <= kWaveTopE ? ws.at<uint32_t>(L.dlog) : nullptr;
+    ga.status = ws.at<uint32_t>(L.status);
     ga.T = T; ga.k = L.k; ga.ns = L.ns; ga.Umax = L.U;
     ga.wt_out = ws.at<WorkEntry>(L.wt); ga.nuniq_out = ws.at<int>(L.nuniq);
     ga.ptok_out = ws.at<int>(L.ptok); ga.inv_out = ws.at<int>(L.inv); ga.pw_out = ws.at<float>(L.pw);
@@ -4046,6 +4146,15 @@ namespace {
 bool defer_grouping(const moe_expert_desc &d, int T, int k, int ns)
 {
     return use_i8(d, T) && T * k <= kGUI8Threads && T * (k + ns) <= 256;
+}
+
+// With E <= kWaveTopE the top-k and softmax move there as well: the route
+// launch leaves the logit keys and runs its tail only when the caller asks
+// for the routing.
+bool defer_topk(const moe_expert_desc &d, int T, int k, int ns, int E)
+{
+    static_assert(kI8Tok <= kDlogTok, "key region");
+    return defer_grouping(d, T, k, ns) && E <= kWaveTopE;
 }
 
 // The down kernel's block for a single token, and whether the pair's record
@@ -4317,9 +4426,10 @@ moe_status moe_layer_route(const moe_expert_desc *d, const float *h, int32_t T, 
     // of its 8 waves), a top-k workgroup per token
     a.topk_blocks = T > kTopkBlocksMinT && E <= kWaveTopE ? T : 0;
     a.tk = W.at<unsigned long long>(W.L.tk);
-    // a single token is routed by moe_layer_ffn's gate/up workgroups from the
-    // logit keys; the tail runs only when the caller wants the routing now
-    const bool defer = defer_routing(*d, T, E);
+    // a single token (and 2 .. 8 tokens on the integer-MFMA kernels) is
+    // routed by moe_layer_ffn's gate/up workgroups from the logit keys; the
+    // tail runs only when the caller wants the routing now
+    const bool defer = defer_routing(*d, T, E) || defer_topk(*d, T, k, n_shared, E);
     a.dlog = defer ? W.at<uint32_t>(W.L.dlog) : nullptr;
     a.tail = !defer || idx_out || w_out;
     if (!a.tail) a.topk_blocks = 0;
