@@ -215,7 +215,7 @@ def test_expert_ffn(qt, H, I, E, k, ns, T, zm, accumulate):
 
 
 # ---------------------------------------------------------------- fused layer and stack
-def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False, prompt=False):
+def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False, prompt=False, routing=True):
     experts = ExpertCache(cfg)
     olayers = oracle_layers(cfg, experts, n_layers)
     x, att = W.tie_free_tokens(cfg, step, T, chain_min_gap(olayers))
@@ -226,14 +226,18 @@ def _run_stack_and_compare(cfg, n_layers, T, step=0, T_max=None, split=False, pr
     wts = torch.empty((n_layers, T, cfg.k), dtype=torch.float32, device=DEV)
     if prompt:
         st.prompt_step(h, idx, wts)
-    else:
+    elif routing:
         st.step(h, idx, wts, split=split)
+    else:  # no routing outputs: no route tail where the FFN ranks the keys
+        st.step(h, None, None, split=split)
     torch.cuda.synchronize()
     hg, ig, wg = h.cpu().numpy(), idx.cpu().numpy(), wts.cpu().numpy()
     href = []
     for t in range(T):
         outs = oracle.stack_token(olayers, x[t])
         for l, o in enumerate(outs):
+            if not routing:
+                continue
             assert sets_equal(ig[l, t][None], o.route.idx), f"layer {l} token {t}"
             assert weights_close(ig[l, t][None], wg[l, t][None], o.route.idx, o.route.w), f"layer {l} token {t}"
         href.append(outs[-1].h_next)
@@ -267,6 +271,15 @@ def test_layer_per_token_topk(T, E, k):
 @pytest.mark.parametrize("T", [1, 8])
 def test_layer_qwen3_shape_q4k(T):
     _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T), 1, T)
+
+
+@pytest.mark.parametrize("T,E,k,routing", [(5, 200, 6, True), (3, 200, 10, False), (8, 128, 8, False), (2, 64, 4, False)])
+def test_layer_q4k_batch_ranked_in_ffn(T, E, k, routing):
+    """2..8 tokens on the integer-MFMA path: every gate/up workgroup ranks
+    each token's logit keys (the lane-group bound for k <= 8, the bitonic one
+    above; 4 keys per lane for E=200); without routing outputs the route
+    launch has no tail at all."""
+    _run_stack_and_compare(W.qwen3_30b_a3b_q4k(T=T).with_(E=E, k=k, seed=9), 1, T, routing=routing)
 
 
 def test_layer_qwen3_shape_q4k_zero_mean():
